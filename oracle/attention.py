@@ -1,0 +1,238 @@
+"""Forward and backward of the causal block-scaled attention call (oracle;
+test infrastructure).
+
+This is not exact attention: quantization is part of the result, so the
+algorithm is followed step by step -- the method's quantization rules, then
+attention on the dequantized operands.  Matrix products of dequantized E4M3
+operands are exact in fp64 (every product of two E4M3 values of one block pair
+is a multiple of 2**-18 of the pair's scale and the sums stay below 2**25 of it,
+well inside 53 bits); everything else is fp64 rounded once to the precision the
+method fixes.  Work is done per (document, head); nothing crosses a document.
+
+Readings of points the pages leave open (each a numbered reading in the
+design notes):
+
+* Scores ``S' = fp32(fp32(Q~ K~^T) * c)`` with ``c = fp32(softmax_scale *
+  log2 e)``; ``softmax_scale = 1/sqrt(d)`` by default.
+* Row-max scaling: the row maximum of S' is rounded up to an integer ``m``,
+  and ``P = fp32(exp2(S' - m))`` lies in (0, 1].  The backward must replay
+  the forward's tiling, diagonal decisions, exponential evaluation and
+  row-max scaling ([Summary, §3.3 Forward-Backward Numerical Consistency];
+  [Reading, 4.3]); with an integer maximum every online-softmax rescale is a
+  power of two, so the probabilities relative to the final maximum are the
+  ones both passes see.
+* The probability operand uses the fixed exponent -8 (the round-up rule
+  applied to P's bound of 1): ``P^ = E4M3(P * 2**8) * 2**-8``; it is a
+  constant, so one payload serves P^V and P^T dO.
+* Diagonal pairs are those whose query and key lie in the same doc-local
+  32-token block; there V uses per-key codes, and each key's exponent is
+  folded along the contraction (key) axis into P before P is quantized
+  ([Summary], opening paragraphs: per-key V scales with a K-fold on diagonal
+  tiles as a causal-leak limit; [News, "Key design choices"]: per-key scale
+  folding).  The fold is taken relative to the largest per-key exponent among
+  the keys the query may see in its block,
+  ``e_ref(i) = max{e_key(j) : blk(j) = blk(i), j <= i}``, so
+  ``f_ij = 2**(e_key(j) - e_ref(i)) <= 1`` and
+  ``P_eff = E4M3(P * f * 2**8) * 2**-8 / f``.  Nothing in this product then
+  depends on a later key.  (A fold relative to the block exponent, switch
+  ``fold="block"``, still depends on later keys of the block, because a
+  smaller ``f`` pushes more entries into E4M3's subnormal range.)  Defining
+  "diagonal" at block level makes the decision identical for every tiling.
+* The softmax denominator ``l`` and dS use the unquantized P; O and dV use
+  the quantized P^ ([Reading, 4.3] lists P^ as the replayed quantity).
+* D is built from the same quantized dO as dP and the bf16 output
+  ([Summary, §3.3]; [Reading, 4.3]).
+* dS gets one round-up exponent per doc-local 32 x 32 block from the block's
+  max-abs ([Summary, §3.3], second bullet; [Reading, 4.3]).
+* dQ and dK use the same token-block Q~ and K~ payloads as the forward.  With
+  the Hadamard rotation on, both are rotated back (the normalised matrix is
+  symmetric and orthogonal).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import formats
+from .hadamard import rotate_back_fp64
+from .quant import BLOCK, doc_bounds, fold_reference, quantize_qkv, quantize_token_blocks
+
+LOG2E = float(np.log2(np.e))
+P_EXP = -8          # fixed exponent of the probability operand
+
+
+@dataclass
+class Numerics:
+    """Switches of the oracle.  The defaults are the method."""
+    quantize_operands: bool = True   # E4M3 Q, K, V, dO (False: identity codecs)
+    quantize_p: bool = True          # E4M3 probability operand
+    quantize_ds: bool = True         # E4M3 dS with 32x32 block exponents
+    round_outputs: bool = True       # bf16 O, dQ, dK, dV
+    rule: str = "roundup"            # exponent rule: roundup | ceil | floor
+    granularity: str = "block"       # operand scales: block | tensor | token
+    hadamard: bool = False
+    causal: bool = True
+    path: str = "mxfp8"              # "mxfp8", or "mixed" (NVFP4 scores)
+    fold: str = "causal"             # diagonal V: causal | block | none (block codes)
+    softmax_scale: float | None = None
+
+
+def scale_constants(d: int, softmax_scale: float | None):
+    """fp32 softmax scale and fp32 ``c = softmax_scale * log2(e)``."""
+    s32 = np.float32(1.0 / np.sqrt(d)) if not softmax_scale or softmax_scale <= 0 \
+        else np.float32(softmax_scale)
+    c32 = np.float32(np.float64(s32) * LOG2E)
+    return s32, c32
+
+
+def _out(x, num: Numerics):
+    return formats.bf16_round(x) if num.round_outputs else np.asarray(x, dtype=np.float64)
+
+
+def _ds_quantize(ds: np.ndarray, valid: np.ndarray, rule: str):
+    """dS^ of one (document, head): one exponent per 32 x 32 block from the
+    block's max-abs over valid entries (masked entries count as 0)."""
+    L = ds.shape[0]
+    out = np.zeros_like(ds)
+    ex_rule = formats.EXPONENT_RULES[rule]
+    for i0 in range(0, L, BLOCK):
+        for j0 in range(0, L, BLOCK):
+            blk = ds[i0:i0 + BLOCK, j0:j0 + BLOCK]
+            v = valid[i0:i0 + BLOCK, j0:j0 + BLOCK]
+            if not v.any():
+                continue
+            e = ex_rule(np.max(np.abs(np.where(v, blk, 0.0))))
+            q = formats.e4m3_encode(np.ldexp(np.where(v, blk, 0.0), -e), saturate=(rule == "floor"))
+            out[i0:i0 + BLOCK, j0:j0 + BLOCK] = np.where(
+                v, np.ldexp(formats.e4m3_decode(q), e), 0.0)
+    return out
+
+
+def forward_doc(qd, kd, vblk, vkey, v_exp_blk, v_exp_key, c32, num: Numerics):
+    """Forward of one (document, head).
+
+    qd, kd: dequantized score operands ``[L, d]`` fp64 (E4M3 token-block, or
+    NVFP4 on the mixed path); vblk, vkey: dequantized V ``[L, d]`` fp64.  v_exp_blk, v_exp_key:
+    int ``[L]`` exponents of V's block and per-key scales.
+    Returns a dict with fp32 S', integer row max ``m``, fp32 P, fp32 ``l``,
+    the effective probability operand ``peff`` and the diagonal mask.
+    """
+    L = qd.shape[0]
+    i = np.arange(L)
+    valid = (i[None, :] <= i[:, None]) if num.causal else np.ones((L, L), bool)
+    s = formats.fp32_round(qd @ kd.T)                       # exact sum -> fp32
+    sp = (s.astype(np.float32) * c32).astype(np.float64)    # fp32 product
+    m = np.ceil(np.max(np.where(valid, sp, -np.inf), axis=1)) if L else np.zeros(0)
+    p = formats.fp32_round(np.exp2(np.where(valid, sp - m[:, None], -np.inf)))
+    l = formats.fp32_round(p.sum(axis=1))
+    blk = i // BLOCK
+    diag = (blk[:, None] == blk[None, :]) & valid
+    if num.fold == "none":               # block codes on the diagonal too
+        diag = np.zeros_like(diag)
+    e_ref = fold_reference(v_exp_key, num.causal)
+    if num.fold == "block":
+        e_ref = v_exp_blk
+    if num.quantize_p:
+        f = np.where(diag, np.ldexp(1.0, np.minimum(v_exp_key[None, :] - e_ref[:, None], 0)), 1.0)
+        p_off = np.ldexp(formats.e4m3_round(np.ldexp(p, -P_EXP)), P_EXP)
+        p_dia = np.ldexp(formats.e4m3_round(np.ldexp(p * f, -P_EXP)), P_EXP) / f
+        peff = np.where(diag, p_dia, p_off)
+    else:
+        peff = p
+    o = (np.where(diag, 0.0, peff) @ vblk + np.where(diag, peff, 0.0) @ vkey) / l[:, None]
+    return dict(sp=sp, m=m.astype(np.int64), p=p, l=l, peff=peff, diag=diag,
+                valid=valid, o=o)
+
+
+def backward_doc(fw, qd, kd, vblk, vkey, dod, o_out, s32, num: Numerics):
+    """Backward of one (document, head) given the forward record ``fw``,
+    the dequantized dO ``dod`` and the bf16 output ``o_out``."""
+    p, l, peff, diag, valid = fw["p"], fw["l"], fw["peff"], fw["diag"], fw["valid"]
+    D = np.sum(dod * o_out, axis=1)                                   # fp64
+    dp = np.where(diag, dod @ vkey.T, dod @ vblk.T)
+    ds = np.where(valid, (p / l[:, None]) * (dp - D[:, None]), 0.0)
+    dsq = _ds_quantize(ds, valid, num.rule) if num.quantize_ds else ds
+    dv = (peff / l[:, None]).T @ dod
+    dq = float(s32) * (dsq @ kd)
+    dk = float(s32) * (dsq.T @ qd)
+    nz = valid & (ds != 0)
+    zeroed = int(np.count_nonzero(nz & (dsq == 0)))
+    return dict(D=D, ds=ds, dsq=dsq, dq=dq, dk=dk, dv=dv,
+                ds_nonzero=int(np.count_nonzero(nz)), ds_zeroed=zeroed)
+
+
+def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
+    """Quantize, forward and backward of the whole packed call.
+
+    q, k, v, do: ``[T, H, d]`` arrays holding bf16 values.  Returns a dict
+    with the quantized payloads (codes and exponents, bit-comparable), the
+    forward statistics ``row_max`` (int) and ``row_sum`` (fp32) in ``[H, T]``,
+    ``D`` in ``[H, T]``, and the outputs O, dQ, dK, dV as fp64 arrays holding
+    bf16 values (or unrounded values when ``round_outputs`` is off).
+    """
+    num = num or Numerics()
+    q = np.asarray(q, dtype=np.float64)
+    T, H, d = q.shape
+    s32, c32 = scale_constants(d, num.softmax_scale)
+    if num.quantize_operands:
+        qt = quantize_qkv(q, k, v, cu_seqlens, num.hadamard, num.rule, num.granularity)
+        do_codes, do_exp, do_deq = quantize_token_blocks(do, cu_seqlens, num.rule, num.granularity)
+        qs_all, ks_all = qt["q"], qt["k"]
+        if num.path == "mixed":
+            from .nvfp4 import quantize_nvfp4
+            *_, qs_all = quantize_nvfp4(qt["q_rot"])
+            *_, ks_all = quantize_nvfp4(qt["k_rot"])
+        elif num.path != "mxfp8":
+            raise ValueError(num.path)
+    else:
+        from .hadamard import fwht_fp32
+        q32 = np.asarray(q, np.float32)
+        k32 = np.asarray(k, np.float32)
+        if num.hadamard:
+            q32, k32 = fwht_fp32(q32), fwht_fp32(k32)
+        z = np.zeros((H, T), dtype=np.int64)
+        v64 = np.asarray(v, dtype=np.float64)
+        qt = dict(q=q32.astype(np.float64), k=k32.astype(np.float64), v=v64, v_key=v64,
+                  v_exp=z, v_key_exp=z)
+        do_codes, do_exp, do_deq = None, z, np.asarray(do, dtype=np.float64)
+        qs_all, ks_all = qt["q"], qt["k"]
+
+    o = np.zeros((T, H, d))
+    dq = np.zeros((T, H, d))
+    dk = np.zeros((T, H, d))
+    dv = np.zeros((T, H, d))
+    row_max = np.zeros((H, T), dtype=np.int64)
+    row_sum = np.zeros((H, T), dtype=np.float64)
+    Dst = np.zeros((H, T))
+    ds_nonzero = ds_zeroed = 0
+    for s, e in doc_bounds(cu_seqlens):
+        if e == s:
+            continue
+        for h in range(H):
+            sl = slice(s, e)
+            fw = forward_doc(qs_all[sl, h], ks_all[sl, h], qt["v"][sl, h], qt["v_key"][sl, h],
+                             qt["v_exp"][h, sl], qt["v_key_exp"][h, sl], c32, num)
+            o_out = _out(fw["o"], num)
+            bw = backward_doc(fw, qt["q"][sl, h], qt["k"][sl, h], qt["v"][sl, h],
+                              qt["v_key"][sl, h], do_deq[sl, h], o_out, s32, num)
+            o[sl, h] = o_out
+            row_max[h, sl] = fw["m"]
+            row_sum[h, sl] = fw["l"]
+            Dst[h, sl] = bw["D"]
+            dqh, dkh = bw["dq"], bw["dk"]
+            if num.hadamard:
+                dqh, dkh = rotate_back_fp64(dqh), rotate_back_fp64(dkh)
+            dq[sl, h] = _out(dqh, num)
+            dk[sl, h] = _out(dkh, num)
+            dv[sl, h] = _out(bw["dv"], num)
+            ds_nonzero += bw["ds_nonzero"]
+            ds_zeroed += bw["ds_zeroed"]
+    res = dict(o=o, dq=dq, dk=dk, dv=dv, row_max=row_max, row_sum=row_sum, D=Dst,
+               do_codes=do_codes, do_exp=do_exp,
+               ds_zero_fraction=(ds_zeroed / ds_nonzero) if ds_nonzero else 0.0)
+    if num.quantize_operands:
+        res.update({k_: qt[k_] for k_ in ("q_codes", "q_exp", "k_codes", "k_exp", "v_codes",
+                                          "v_exp", "v_key_codes", "v_key_exp")})
+    return res

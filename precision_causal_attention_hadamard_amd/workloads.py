@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for the attention training call.
+
+This module only draws random numbers and rounds them to bf16; it holds none
+of the method's arithmetic, so both the HIP path and the CPU oracle can take
+their inputs from it.
+
+Recipe (the pages' kernel benchmarks use synthetic packed workloads with 16
+heads and head dim 128; no dataset is involved):
+
+* every tensor is drawn as fp32 N(0, 1) from ``numpy.random.default_rng(seed)``
+  (PCG64) and rounded to bf16 (round-to-nearest-even);
+* draw order: Q, K, V, dO, then structure (outlier channels, document
+  lengths);
+* layout ``[T, H, d]``, packed documents described by ``cu_seqlens``.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+SEED_BASE = 20261100
+
+
+@dataclass
+class Workload:
+    name: str
+    q: torch.Tensor            # bf16 [T, H, d] on the CPU
+    k: torch.Tensor
+    v: torch.Tensor
+    do: torch.Tensor
+    cu_seqlens: list
+    heads: int
+    head_dim: int
+    hadamard: bool = False
+    path: int = 0              # 0 = MXFP8, 1 = mixed NVFP4 scores
+    causal_dq_scale: bool = False
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def doc_lens(self) -> list:
+        return [b - a for a, b in zip(self.cu_seqlens, self.cu_seqlens[1:])]
+
+    def causal_pairs(self) -> int:
+        """Number of (query, key) pairs the causal call computes, all heads."""
+        return self.heads * sum(L * (L + 1) // 2 for L in self.doc_lens)
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs of forward (2 products) + backward (5 products),
+        each 2*d per causal pair: 14 * d * pairs."""
+        return 14 * self.head_dim * self.causal_pairs()
+
+
+def _bf16(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def draw_tensors(rng, T: int, H: int, d: int, outlier_scale: float = 0.0):
+    """Q, K, V, dO as bf16; optional outlier channels drawn after the tensors."""
+    raw = [rng.standard_normal((T, H, d), dtype=np.float32) for _ in range(4)]
+    if outlier_scale:
+        n_out = max(1, int(round(0.01 * d)))
+        for x in raw:
+            for h in range(H):
+                ch = rng.choice(d, size=n_out, replace=False)
+                x[:, h, ch] *= np.float32(outlier_scale)
+    return [_bf16(x) for x in raw]
+
+
+def lognormal_fill(rng, total: int, median: float = 1024.0, sigma: float = 1.0,
+                   lo: int = 17, hi: int = 8192) -> list:
+    """Document lengths filling ``total`` tokens: lengths
+    ``round(exp(N(ln median, sigma)))`` clipped to [lo, hi] are appended while
+    they fit; the remainder becomes the last document, merged into the
+    previous one when it is shorter than ``lo``."""
+    lens = []
+    left = total
+    while True:
+        L = int(np.clip(np.round(np.exp(rng.normal(np.log(median), sigma))), lo, hi))
+        if L > left:
+            break
+        lens.append(L)
+        left -= L
+    if left:
+        if left < lo and lens:
+            lens[-1] += left
+        else:
+            lens.append(left)
+    return lens
+
+
+def _cu(lens) -> list:
+    return [0] + list(np.cumsum(lens).astype(int).tolist())
+
+
+def config(k: int, seed: int | None = None) -> Workload:
+    """The five workloads of the call (k = 1..5)."""
+    seed = SEED_BASE + k if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if k == 1:   # tiny: one 256-token document, 2 heads, head dim 64
+        q, kk, v, do = draw_tensors(rng, 256, 2, 64)
+        return Workload("tiny_1x256_h2_d64", q, kk, v, do, [0, 256], 2, 64)
+    if k == 2:   # batch 2 x 4096, 16 heads, d 128, 1% outlier channels x20, Hadamard on
+        q, kk, v, do = draw_tensors(rng, 8192, 16, 128, outlier_scale=20.0)
+        return Workload("batched_2x4096_h16_d128_outliers_hadamard", q, kk, v, do,
+                        [0, 4096, 8192], 16, 128, hadamard=True)
+    if k == 3:   # packed 4 rows x 16384, lognormal documents
+        q, kk, v, do = draw_tensors(rng, 65536, 16, 128)
+        lens = []
+        for _ in range(4):
+            lens += lognormal_fill(rng, 16384)
+        return Workload("packed_4x16384_lognormal_h16_d128", q, kk, v, do, _cu(lens), 16, 128)
+    if k == 4:   # long context 32768: two 12288-token docs + lognormal shorts
+        q, kk, v, do = draw_tensors(rng, 32768, 16, 128)
+        lens = [12288, 12288] + lognormal_fill(rng, 8192)
+        return Workload("long_1x32768_h16_d128", q, kk, v, do, _cu(lens), 16, 128)
+    if k == 5:   # mixed path, shapes of config 2, no outliers
+        q, kk, v, do = draw_tensors(rng, 8192, 16, 128)
+        return Workload("mixed_2x4096_h16_d128", q, kk, v, do, [0, 4096, 8192], 16, 128,
+                        path=1)
+    raise ValueError(k)
+
+
+def small_packed(seed: int, doc_lens, heads: int = 2, head_dim: int = 64,
+                 outlier_scale: float = 0.0, hadamard: bool = False) -> Workload:
+    """A small packed workload for parity tests (documents off 32-alignment)."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(doc_lens))
+    q, kk, v, do = draw_tensors(rng, T, heads, head_dim, outlier_scale)
+    return Workload(f"packed_{'_'.join(map(str, doc_lens))}_h{heads}_d{head_dim}", q, kk, v, do,
+                    _cu(doc_lens), heads, head_dim, hadamard=hadamard)

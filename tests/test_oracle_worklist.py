@@ -1,0 +1,68 @@
+"""Pins of the oracle's work list and NVFP4 operands."""
+
+import numpy as np
+import pytest
+
+from oracle import formats, nvfp4, worklist
+from precision_causal_attention_hadamard_amd import workloads as W
+
+
+def touched_pairs_bruteforce(L, bq, bk):
+    """(q tile, k tile) pairs with at least one causal (j <= i) element."""
+    pairs = set()
+    for i in range(L):
+        for j in range(i + 1):
+            pairs.add((i // bq, j // bk))
+    return pairs
+
+
+@pytest.mark.parametrize("L", [1, 17, 64, 100, 129, 300])
+@pytest.mark.parametrize("bq,bk", [(128, 64), (64, 128), (64, 64), (32, 128)])
+def test_costs_equal_bruteforce_tile_counts(L, bq, bk):
+    pairs = touched_pairs_bruteforce(L, bq, bk)
+    for t in range(-(-L // bq)):
+        assert worklist.fwd_cost(t, L, bq, bk) == sum(1 for p in pairs if p[0] == t)
+    for u in range(-(-L // bk)):
+        assert worklist.bwd_cost(u, L, bq, bk) == sum(1 for p in pairs if p[1] == u)
+
+
+def test_worklist_is_sorted_permutation():
+    cu = [0, 17, 300, 300, 1500, 1600]
+    items = worklist.fwd_items(cu, 3, 128, 64)
+    costs = [it[3] for it in items]
+    assert costs == sorted(costs, reverse=True)
+    keys = {(d, t, h) for d, t, h, _ in items}
+    assert len(keys) == len(items) == 3 * (1 + 3 + 0 + 10 + 1)
+    b = worklist.bwd_items(cu, 3, 64, 128)
+    assert len(b) == 3 * (1 + 3 + 0 + 10 + 1)
+    assert [it[3] for it in b] == sorted((it[3] for it in b), reverse=True)
+
+
+def test_skew_rule():
+    assert worklist.is_skewed([0, 8192] + [8192 + 256 * (i + 1) for i in range(224)])
+    assert not worklist.is_skewed([0, 4096, 8192])
+
+
+def test_nvfp4_round_up_scale_and_exact_dequant():
+    wl = W.small_packed(12, [40], heads=2, head_dim=64)
+    x = wl.q.float().numpy()
+    codes, scales, t, deq = nvfp4.quantize_nvfp4(x)
+    assert t == np.float32(np.max(np.abs(x)) / 2688.0)
+    g = x.reshape(40, 2, 4, 16)
+    gmax = np.abs(g).max(-1)
+    # the scale is an E4M3 value, never below what the group needs, and the
+    # next smaller E4M3 value would be below it (round-up, tight)
+    need = (gmax.astype(np.float64) / np.float64(np.float32(6 * np.float64(t)))).astype(np.float32)
+    assert np.all(scales >= need)
+    np.testing.assert_array_equal(formats.e4m3_round(scales), scales)
+    vals = np.unique(formats.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+    for s, n in zip(scales.ravel()[:50], need.ravel()[:50]):
+        below = vals[vals < s]
+        assert below.size == 0 or below.max() < n
+    # dequantized = code value * s * t, and |x / (s t)| <= 6 (no clamp needed)
+    assert np.all(np.abs(x / (scales[..., None].repeat(16, -1).reshape(40, 2, 64) * t)) <= 6.0 + 1e-6)
+    # every code*scale product is an fp16-exact number (the GPU expands NVFP4
+    # into fp16 exactly): at most 6 significant bits
+    prod = formats.e2m1_decode(codes) * np.repeat(scales, 16, axis=-1)
+    np.testing.assert_array_equal(formats.fp16_round(prod), prod)
+    np.testing.assert_allclose(deq, prod * np.float64(t))
