@@ -1,0 +1,209 @@
+/*
+ * flamia.h -- C ABI of the causal block-scaled low-precision attention
+ * training call for AMD MI355X (gfx950).
+ *
+ * The call is three steps over packed variable-length documents:
+ *   flamia_quantize   fused quantization of Q, K, V (+ the work list),
+ *   flamia_attn_fwd   S = Q K^T, causal online softmax, O = P^ V,
+ *   flamia_attn_bwd   dO quantization + D, then dV, dP, dS, dQ, dK.
+ *
+ * Method (from the pages describing FLAMIA; page titles are cited in full
+ * once here and shortened after):
+ *   [Summary] "FLAMIA: FLAsh MIcroscaling Attention for Fast and Causally
+ *             Safe Training on Blackwell" (summary page; its bullets carry
+ *             the paper's section numbers, e.g. §3.1 Token-Block Scaling).
+ *   [Reading] "因果安全的低精度注意力——FLAMIA Blackwell 训练内核精读",
+ *             sections 4.1-4.4.
+ *   [News]    "FLAMIA Brings Causally Safe Low-Precision Attention to
+ *             Blackwell", "Key design choices".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts.  Per-token tensors are [T, H, d] row-major ("THD": packed tokens,
+ *   then heads, then the head dimension), no padding between documents.
+ *   Per-token metadata (exponent bytes, row statistics, D) is [H, T].
+ *   Documents are given by cu_seqlens (device int32[num_docs + 1],
+ *   0 = cu[0] <= cu[1] <= ... <= cu[num_docs] = T).
+ * Numbers.  q, k, v, dout, o, dq, dk, dv are bf16.  Codes are E4M3 (OCP FN:
+ *   bias 7, largest finite 448).  Exponent bytes are UE8M0 (value e + 127).
+ * Ownership.  Every pointer is caller-owned device memory; the library
+ *   never allocates, frees or keeps device memory, holds no state between
+ *   calls and never synchronises the host.  Each call only enqueues kernels
+ *   on `stream`, so a whole training call can be captured in a HIP graph.
+ * Errors.  Every function returns a flamia_status and never throws.  Only
+ *   host scalars and pointer non-nullness are validated (before anything is
+ *   launched); a malformed device-side cu_seqlens is undefined behaviour.
+ *   FLAMIA_ERR_HIP reports a failed kernel launch (hipGetLastError).
+ * Descriptor.  The same flamia_attn_desc (all fields equal) must be passed
+ *   to flamia_quantize, flamia_attn_fwd and flamia_attn_bwd of one call.
+ */
+#ifndef FLAMIA_H
+#define FLAMIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLAMIA_OK = 0,
+  FLAMIA_ERR_INVALID_ARG = 1,   /* bad host scalar or NULL pointer */
+  FLAMIA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  FLAMIA_ERR_WORKSPACE = 3,     /* a size exceeds what the library can index */
+  FLAMIA_ERR_HIP = 4            /* a kernel launch failed */
+} flamia_status;
+
+typedef struct flamia_attn_desc {
+  int32_t total_tokens;         /* T >= 0 */
+  int32_t num_docs;             /* >= 1 */
+  int32_t max_doc_len;          /* caller's upper bound of any document length, 1..T */
+  const int32_t* cu_seqlens;    /* device int32[num_docs + 1] */
+  int32_t num_heads;            /* H >= 1 */
+  int32_t head_dim;             /* d: 64 or 128 */
+  int32_t causal;               /* must be 1 */
+  int32_t path;                 /* 0 = MXFP8 (the only path this build runs) */
+  int32_t hadamard;             /* 1: rotate Q and K rows by the normalised Sylvester Hadamard matrix */
+  int32_t causal_dq_scale;      /* 1: dQ accumulator prescale from causally visible blocks only */
+  int32_t deterministic;        /* must be 0 (dQ is reduced with fp16 atomics) */
+  float softmax_scale;          /* <= 0 selects 1/sqrt(head_dim) */
+} flamia_attn_desc;
+
+/*
+ * Quantized operands and the GPU-built schedule: the forward-to-backward
+ * saved set together with o, row_max and row_sum.  All pointers point into
+ * one caller buffer of `qtensor_bytes` (flamia_buffer_sizes); fill them with
+ * flamia_qtensors_layout.
+ *
+ *  q_codes, k_codes   [T,H,d] E4M3 token-block codes of Q and K (after the
+ *                     optional Hadamard rotation) -- [Summary, §3.1 Token-Block
+ *                     Scaling]: one power-of-two exponent per 32 consecutive
+ *                     tokens of one document x the full head dimension.
+ *  v_codes            [T,H,d] token-block codes of V.
+ *  v_key_codes        [T,H,d] per-key codes of V, used on diagonal blocks.
+ *  q_exp, k_exp, v_exp  [H,T] UE8M0 block exponent, repeated for every token
+ *                     of the block (per-token scale metadata, [Summary, §3.6.2]).
+ *  v_key_exp          [H,T] per-key exponent of V.
+ *  v_ref_exp          [H,T] per query: largest v_key_exp among the keys of
+ *                     its own block it may see (the fold reference of the
+ *                     diagonal P^V product).
+ *  plan               opaque GPU-built longest-first work lists.
+ */
+typedef struct flamia_qtensors {
+  uint8_t* q_codes;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint8_t* v_key_codes;
+  uint8_t* q_exp;
+  uint8_t* k_exp;
+  uint8_t* v_exp;
+  uint8_t* v_key_exp;
+  uint8_t* v_ref_exp;
+  void* plan;
+} flamia_qtensors;
+
+/*
+ * flamia_buffer_sizes -- bytes the caller must provide.
+ *   qtensor_bytes : one buffer for flamia_qtensors (codes, exponents, plan).
+ *   fwd_ws_bytes  : workspace of flamia_attn_fwd (may be 0; pass NULL then).
+ *   bwd_ws_bytes  : workspace of flamia_attn_bwd (quantized dO, D, dO/l,
+ *                   fp16 dQ accumulator, fp32 dK staging, prescale exponents).
+ * Any output pointer may be NULL.  Host only; launches nothing.
+ */
+flamia_status flamia_buffer_sizes(const flamia_attn_desc* desc, size_t* qtensor_bytes,
+                                  size_t* fwd_ws_bytes, size_t* bwd_ws_bytes);
+
+/*
+ * flamia_qtensors_layout -- carve a qtensor buffer (device address `base`,
+ * at least qtensor_bytes long, 256-byte aligned) into the fields of `out`.
+ * Host only; writes no device memory.
+ */
+flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base,
+                                     flamia_qtensors* out);
+
+/*
+ * flamia_quantize -- fused forward-side quantization, [Reading, 4.4] first
+ * bullet (rotation, block statistics, codes and scales generated together)
+ * and [Summary, §4.3 Ablation Study]; plus the GPU-built work lists of
+ * [Summary, §3.6.2 Load-Balanced Scheduling] and [Reading, 4.4] last bullet.
+ *   q, k, v : bf16 [T,H,d] inputs (device).
+ *   out     : filled qtensors (device buffers, caller-owned).
+ * Per (document, 32-token block, head): optional fp32 Hadamard rotation of
+ * Q and K rows; amax over the 32 x d block; exponent e = the smallest
+ * integer with amax <= 448 * 2^e (rounded up so nothing clamps,
+ * [Summary, §3.2 Causally Safe Scales]); codes = RNE_E4M3(x * 2^-e).
+ * V also gets per-key exponents/codes and the per-query fold reference.
+ * Two kernel launches: the work-list builder and the quantizer.
+ */
+flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const void* k,
+                              const void* v, const flamia_qtensors* out, hipStream_t stream);
+
+/*
+ * flamia_attn_fwd -- forward pass, [Summary] opening paragraphs and
+ * [Reading, 4.1]/[Reading, 4.3]: S = Q~ K~^T on scaled FP8 matrix cores with
+ * the token-block exponents as operand scales (the factorisation
+ * S_ij = 2^(eQ(i)+eK(j)) x code dot product), causal mask within each
+ * document, online softmax with an integer (rounded-up, log2-domain) row
+ * maximum, P^ = E4M3(P * 2^8), per-key V scales folded into P on diagonal
+ * 32-token blocks, O = sum P^ V / l.
+ *   qt       : quantized operands from flamia_quantize.
+ *   o        : bf16 [T,H,d] output (device).
+ *   row_max  : int32 [H,T] integer row maximum m~ of S * softmax_scale * log2(e).
+ *   row_sum  : fp32 [H,T] softmax denominator l = sum_j exp2(S'_ij - m~_i).
+ *   ws       : fwd workspace (may be NULL when fwd_ws_bytes is 0).
+ */
+flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
+                              int32_t* row_max, float* row_sum, void* ws, hipStream_t stream);
+
+/*
+ * flamia_attn_bwd -- backward pass, [Summary, §3.3 Forward-Backward Numerical
+ * Consistency] and [Reading, 4.3]/[Reading, 4.4] third bullet: dO is
+ * token-block quantized and D = rowsum(dO~ * O) is built from that same
+ * payload; scores are recomputed from the same Q~/K~ codes with the same
+ * matrix-core sequence, mask, exponential evaluation, stored integer row
+ * maximum and diagonal fold as the forward, so the probability codes are
+ * the forward's; dV = P^T (dO~/l); dP = dO~ V~^T; dS = P/l (dP - D) gets one
+ * round-up exponent per 32x32 block; dK = dS^T Q~ and dQ = dS K~ (fp16
+ * partials with a data-dependent power-of-two prescale, reduced with
+ * atomics); with the rotation on, dQ and dK are rotated back.
+ *   o, row_max, row_sum : forward outputs.
+ *   dout                : bf16 [T,H,d] upstream gradient.
+ *   dq, dk, dv          : bf16 [T,H,d] gradients w.r.t. the unrotated q, k, v.
+ *   ws                  : bwd workspace of bwd_ws_bytes (device).
+ * Four kernel launches: dO quantizer, backward, two finalisers.
+ */
+flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensors* qt,
+                              const void* o, const int32_t* row_max, const float* row_sum,
+                              const void* dout, void* dq, void* dk, void* dv, void* ws,
+                              hipStream_t stream);
+
+/*
+ * flamia_tile_config -- tile sizes the kernels use for a head dim, i.e. the
+ * Bq/Bk of the work-list cost model.  Host only.
+ */
+flamia_status flamia_tile_config(int32_t head_dim, int32_t* fwd_bq, int32_t* fwd_bk,
+                                 int32_t* bwd_bq, int32_t* bwd_bk);
+
+/*
+ * flamia_plan_view -- where the work lists live inside qt->plan, so a caller
+ * (or a test) can copy them back.  Host only.  Layout of the plan:
+ *   int32 counts[4]   at byte 0: n_fwd_tiles, n_bwd_tiles, 0, 0
+ *   int32 fwd[cap_fwd][2] at fwd_offset: (doc, q tile), longest first
+ *   int32 bwd[cap_bwd][2] at bwd_offset: (doc, k tile), longest first
+ * Sort key: cost descending, then doc, then tile; each tile expands to
+ * num_heads consecutive items, head ascending.
+ */
+flamia_status flamia_plan_view(const flamia_attn_desc* desc, size_t* fwd_offset, int32_t* cap_fwd,
+                               size_t* bwd_offset, int32_t* cap_bwd);
+
+/* Static description of a status code; never NULL. */
+const char* flamia_status_string(flamia_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLAMIA_H */

@@ -234,5 +234,5 @@ def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
                ds_zero_fraction=(ds_zeroed / ds_nonzero) if ds_nonzero else 0.0)
     if num.quantize_operands:
         res.update({k_: qt[k_] for k_ in ("q_codes", "q_exp", "k_codes", "k_exp", "v_codes",
-                                          "v_exp", "v_key_codes", "v_key_exp")})
+                                          "v_exp", "v_key_codes", "v_key_exp", "v_ref_exp")})
     return res

@@ -1,0 +1,273 @@
+// Forward kernel of the causal block-scaled MXFP8 attention call.
+//
+// One workgroup (4 waves) per work item (document, 128-query tile, head),
+// items taken longest first from the GPU-built list.  Wave w owns the 32
+// queries of document-local block 4t + w.  The kernel steps over 64-key tiles
+// from the document start to the diagonal.  Per step:
+//   * K~ codes are staged token-major in LDS and V~ codes d-major (transposed
+//     while staging, tokens of each 32-block in pi order), plus the per-key
+//     V codes on the two diagonal key tiles;
+//   * S^T = K~ Q~^T on the scaled FP8 matrix cores: the token-block exponents
+//     are the operand scales, which realises the pages' factorisation
+//     S_ij = 2^(eQ(i) + eK(j)) x code dot product ([Reading, 4.1]);
+//   * each lane owns one query, so the row maximum is a lane-local max plus
+//     one cross-half exchange; it is rounded up to an integer m~ in the
+//     log2 domain and every rescale of the running output is a power of two;
+//   * P = 2^(n - m~) exp2(r) with n = floor(S'), r = S' - n, S' = S c, so P
+//     relative to the final m~ is exactly P relative to the running m~ times a
+//     power of two (the backward's replay relies on it);
+//   * P^ = E4M3(P 2^8) enters the P^V product with the constant scale 2^-8;
+//     on a query's own 32-token block V uses per-key codes and each key's
+//     exponent is folded into P relative to the largest visible per-key
+//     exponent of the block, which becomes that query's operand scale
+//     ([Summary], opening paragraphs: per-key V scales folded on diagonal
+//     tiles; [News, "Key design choices"]);
+//   * O^T += V~^T P^^T on the scaled FP8 matrix cores (P^^T is consumed
+//     straight from the S^T accumulator layout, no lane shuffles).
+// Epilogue: O = O_acc / l to bf16, integer row max and fp32 l stored.
+#include "flamia_device.hpp"
+#include "flamia_internal.hpp"
+
+namespace flamia {
+
+constexpr int FWD_THREADS = 256;
+
+struct FwdArgs {
+  Problem p;
+  const int* counts;
+  const int2* items;
+  const uint8_t *q_codes, *k_codes, *v_codes, *v_key_codes;
+  const uint8_t *q_exp, *k_exp, *v_exp, *v_key_exp, *v_ref_exp;
+  uint16_t* o;
+  int* row_max;
+  float* row_sum;
+};
+
+// Stage 64 tokens x D codes transposed into dst[D][stride], token t of the
+// tile at column (t / 32) * 32 + pi_pos(t % 32).  Rows past `valid` are zero.
+template <int D>
+__device__ __forceinline__ void stage_transposed64(uint8_t* __restrict__ dst, int stride,
+                                                   const uint8_t* __restrict__ src, size_t row_stride,
+                                                   int valid, int tid) {
+  constexpr int DG = D / 8;
+  for (int t = tid; t < 16 * DG; t += FWD_THREADS) {
+    const int g4 = t / DG, dg = t % DG;
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = 4 * g4 + r;
+      if (tok < valid) {
+        v2i w = *reinterpret_cast<const v2i*>(src + tok * row_stride + 8 * dg);
+        lo[r] = (uint32_t)w[0];
+        hi[r] = (uint32_t)w[1];
+      } else {
+        lo[r] = hi[r] = 0u;
+      }
+    }
+    uint32_t c[8];
+    transpose4x4_b8(lo[0], lo[1], lo[2], lo[3], c[0], c[1], c[2], c[3]);
+    transpose4x4_b8(hi[0], hi[1], hi[2], hi[3], c[4], c[5], c[6], c[7]);
+    const int pos = (g4 >> 3) * 32 + (g4 & 1) * 16 + ((g4 & 7) >> 1) * 4;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      *reinterpret_cast<uint32_t*>(dst + (8 * dg + k) * stride + pos) = c[k];
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
+  constexpr int KS = D + 16;      // token-major K row stride (bytes)
+  constexpr int VS = FWD_BK + 16; // d-major V row stride (bytes)
+  constexpr int NS = D / 64;      // K-steps of the S product
+  constexpr int ND = D / 32;      // d-blocks of the output
+  __shared__ __attribute__((aligned(16))) uint8_t sK[FWD_BK * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sVT[D * VS];
+  __shared__ __attribute__((aligned(16))) uint8_t sVkT[D * VS];
+  __shared__ uint8_t sKe[FWD_BK], sVe[FWD_BK], sVke[FWD_BK];
+
+  const Problem& p = a.p;
+  const int H = p.H, T = p.T;
+  const int tile_idx = blockIdx.x / H, head = blockIdx.x % H;
+  if (tile_idx >= a.counts[0]) return;
+  const int2 it = a.items[tile_idx];
+  const int doc = it.x, qt = it.y;
+  const int s_d = p.cu[doc];
+  const int L = p.cu[doc + 1] - s_d;
+  const int q0 = qt * FWD_BQ;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, hh = lane >> 5;
+  const int i = q0 + 32 * wave + n;          // this lane's query (document-local)
+  const bool iv = i < L;
+  const bool wave_active = q0 + 32 * wave < L;
+  const int QB = 4 * qt + wave;              // this wave's query block
+  const size_t rs = (size_t)H * D;           // token stride of [T,H,d] codes
+  const size_t hT = (size_t)head * T + s_d;  // base of [H,T] metadata of this doc/head
+
+  // Q~ as the B operand of S^T = K~ Q~^T (lane = query column)
+  v8i qa[NS];
+  int qe = E8M0_BIAS, vref = 0;
+  if (iv) {
+    const uint8_t* qrow = a.q_codes + (size_t)(s_d + i) * rs + (size_t)head * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qa[s] = cat8(ld16(qrow + 64 * s + 16 * hh), ld16(qrow + 64 * s + 32 + 16 * hh));
+    qe = a.q_exp[hT + i];
+    vref = (int)a.v_ref_exp[hT + i] - E8M0_BIAS;
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qa[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  v16f oacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) oacc[db] = v16f{};
+  float l_run = 0.f;
+  int m_run = M_NONE;
+  const float c = p.c_log2;
+
+  const int kt_last = (min(q0 + FWD_BQ, L) - 1) / FWD_BK;
+  for (int kt = 0; kt <= kt_last; ++kt) {
+    const int j0 = kt * FWD_BK;
+    const int nvalid = min(FWD_BK, L - j0);
+    const bool diag_tile = kt >= 2 * qt;
+    // ---- stage K (token-major), V (d-major), exponents
+    {
+      const uint8_t* kbase = a.k_codes + (size_t)(s_d + j0) * rs + (size_t)head * D;
+      for (int ch = tid; ch < FWD_BK * D / 16; ch += FWD_THREADS) {
+        const int r = ch / (D / 16), c16 = ch % (D / 16);
+        v4i w = r < nvalid ? ld16(kbase + r * rs + 16 * c16) : v4i{0, 0, 0, 0};
+        st16(sK + r * KS + 16 * c16, w);
+      }
+      stage_transposed64<D>(sVT, VS, a.v_codes + (size_t)(s_d + j0) * rs + (size_t)head * D, rs, nvalid, tid);
+      if (diag_tile)
+        stage_transposed64<D>(sVkT, VS, a.v_key_codes + (size_t)(s_d + j0) * rs + (size_t)head * D, rs,
+                              nvalid, tid);
+      if (tid < FWD_BK) {
+        const bool kv = tid < nvalid;
+        sKe[tid] = kv ? a.k_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
+        sVe[tid] = kv ? a.v_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
+        sVke[tid] = (kv && diag_tile) ? a.v_key_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
+      }
+    }
+    __syncthreads();
+
+    if (wave_active) {
+      bool act[2], dia[2];
+      v16f st[2];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int KB = 2 * kt + kb;
+        act[kb] = KB <= QB && j0 + 32 * kb < L;
+        dia[kb] = KB == QB;
+        st[kb] = v16f{};
+        if (act[kb]) {
+          const uint8_t* krow = sK + (32 * kb + n) * KS;
+          const int ske = sKe[32 * kb + n];
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            st[kb] = mfma_f8(cat8(ld16(krow + 64 * s + 16 * hh), ld16(krow + 64 * s + 32 + 16 * hh)), qa[s],
+                             st[kb], ske, qe);
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+            if (j <= i && j < L) tmax = fmaxf(tmax, st[kb][rr]);
+          }
+        }
+      }
+      if (act[0] || act[1]) {
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const int m_tile = tmax == -INFINITY ? M_NONE : (int)ceilf(tmax * c);
+        const int m_new = max(m_run, m_tile);
+        if (__any(m_new != m_run)) {
+          const int sh = m_run - m_new;   // <= 0
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) oacc[db][rr] = __builtin_amdgcn_ldexpf(oacc[db][rr], sh);
+          l_run = __builtin_amdgcn_ldexpf(l_run, sh);
+        }
+        m_run = m_new;
+
+        int pc[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int rr = 4 * g + r;
+              const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
+              const int j = j0 + 32 * kb + jj;
+              float pr = 0.f;
+              if (act[kb] && j <= i && j < L) {
+                const float x = st[kb][rr] * c;
+                const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
+                pr = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) - m_run);
+              }
+              l_run += pr;
+              const int sh = dia[kb] ? 8 + ((int)sVke[32 * kb + jj] - E8M0_BIAS) - vref : 8;
+              pv[r] = __builtin_amdgcn_ldexpf(pr, sh);
+            }
+            pc[kb][g] = cvt_fp8x4(pv[0], pv[1], pv[2], pv[3]);
+          }
+        }
+        const v8i pb = v8i{pc[0][0], pc[0][1], pc[0][2], pc[0][3], pc[1][0], pc[1][1], pc[1][2], pc[1][3]};
+        // lane half hh supplies the scales of key block hh
+        const int sb = dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP;
+        const int sa = dia[hh] ? E8M0_BIAS : (int)sVe[32 * hh];
+        const uint8_t* v0 = (dia[0] ? sVkT : sVT) + 16 * hh;
+        const uint8_t* v1 = (dia[1] ? sVkT : sVT) + 32 + 16 * hh;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const int drow = (32 * db + n) * VS;
+          oacc[db] = mfma_f8(cat8(ld16(v0 + drow), ld16(v1 + drow)), pb, oacc[db], sa, sb);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (wave_active) {
+    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    if (iv) {
+      const float inv = 1.0f / l;
+      uint16_t* orow = a.o + (size_t)(s_d + i) * rs + (size_t)head * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t b0 = f32_to_bf16_bits(oacc[db][4 * g] * inv);
+          const uint32_t b1 = f32_to_bf16_bits(oacc[db][4 * g + 1] * inv);
+          const uint32_t b2 = f32_to_bf16_bits(oacc[db][4 * g + 2] * inv);
+          const uint32_t b3 = f32_to_bf16_bits(oacc[db][4 * g + 3] * inv);
+          *reinterpret_cast<v2i*>(orow + 32 * db + 8 * g + 4 * hh) = v2i{(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
+        }
+      if (hh == 0) {
+        a.row_max[hT + i] = m_run;
+        a.row_sum[hT + i] = l;
+      }
+    }
+  }
+}
+
+hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout& pl,
+                           const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
+                           const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
+                           const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
+                           void* o, int* row_max, float* row_sum, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  const char* base = static_cast<const char*>(plan);
+  FwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.fwd_offset),
+            q_codes, k_codes, v_codes, v_key_codes, q_exp, k_exp, v_exp, v_key_exp, v_ref_exp,
+            static_cast<uint16_t*>(o), row_max, row_sum};
+  dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
+  if (p.D == 64)
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(FWD_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(FWD_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -1,0 +1,101 @@
+// Gradient finalisers of the backward pass.
+//
+// dQ: the fp16 accumulator holds dQ 2^-sigma (sigma per query block, chosen
+// so partial sums stay inside fp16); multiply back by 2^sigma and the
+// softmax scale.  dK: fp32 staging already carries the softmax scale.  With
+// the Hadamard option on, both are rotated back with the same normalised
+// Sylvester matrix as the forward rotation (it is symmetric and orthogonal):
+// fp32 butterflies h = 1, 2, ..., d/2 then one multiply by fp32(1/sqrt(d)).
+// Outputs are bf16 (round to nearest even).  One thread per (token, head) row.
+#include "flamia_device.hpp"
+#include "flamia_internal.hpp"
+
+namespace flamia {
+
+constexpr int FIN_THREADS = 256;
+
+template <int D>
+__device__ __forceinline__ void fwht_row(float (&x)[D]) {
+#pragma unroll
+  for (int h = 1; h < D; h <<= 1)
+#pragma unroll
+    for (int a = 0; a < D; ++a)
+      if ((a & h) == 0) {
+        const float lo = x[a], hi = x[a + h];
+        x[a] = lo + hi;
+        x[a + h] = lo - hi;
+      }
+  const float inv_sqrt_d = D == 64 ? 0.125f : __uint_as_float(0x3db504f3u);
+#pragma unroll
+  for (int a = 0; a < D; ++a) x[a] = x[a] * inv_sqrt_d;
+}
+
+template <int D>
+__device__ __forceinline__ void store_bf16_row(uint16_t* __restrict__ dst, const float (&x)[D]) {
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    v4i w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (int)((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k]) | ((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k + 1]) << 16));
+    st16(dst + 8 * c, w);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(FIN_THREADS)
+finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __restrict__ dq_sigma,
+                const float* __restrict__ dk_f32, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk) {
+  const size_t row = (size_t)blockIdx.x * FIN_THREADS + threadIdx.x;   // = t * H + h
+  const size_t rows = (size_t)p.T * p.H;
+  if (row >= rows) return;
+  const int t = (int)(row / p.H), h = (int)(row % p.H);
+  const size_t off = row * D;
+  {
+    float x[D];
+    const int sig = dq_sigma[(size_t)h * p.T + t];
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const v4i w = ld16(dq_acc + off + 8 * c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t u = (uint32_t)w[k];
+        _Float16 lo, hi;
+        uint16_t ul = (uint16_t)(u & 0xffffu), uh = (uint16_t)(u >> 16);
+        __builtin_memcpy(&lo, &ul, 2);
+        __builtin_memcpy(&hi, &uh, 2);
+        x[8 * c + 2 * k] = __builtin_amdgcn_ldexpf((float)lo, sig) * p.softmax_scale;
+        x[8 * c + 2 * k + 1] = __builtin_amdgcn_ldexpf((float)hi, sig) * p.softmax_scale;
+      }
+    }
+    if (p.hadamard) fwht_row<D>(x);
+    store_bf16_row<D>(dq + off, x);
+  }
+  {
+    float x[D];
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const v4f w = *reinterpret_cast<const v4f*>(dk_f32 + off + 4 * c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
+    }
+    if (p.hadamard) fwht_row<D>(x);
+    store_bf16_row<D>(dk + off, x);
+  }
+}
+
+hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
+                           const float* dk_f32, void* dq, void* dk, hipStream_t stream) {
+  const size_t rows = (size_t)p.T * p.H;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + FIN_THREADS - 1) / FIN_THREADS));
+  if (p.D == 64)
+    hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(FIN_THREADS), 0, stream, p,
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk);
+  else
+    hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(FIN_THREADS), 0, stream, p,
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk);
+  return hipGetLastError();
+}
+
+}  // namespace flamia

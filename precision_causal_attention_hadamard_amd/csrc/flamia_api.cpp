@@ -1,0 +1,220 @@
+// Host side of the flamia C ABI: argument validation, buffer layouts and
+// kernel launches.  Nothing here allocates, frees or synchronises.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/flamia.h"
+#include "flamia_internal.hpp"
+
+namespace {
+
+using namespace flamia;
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Tile sizes of the kernels (kept in step with flamia_device.hpp).
+constexpr int K_FWD_BQ = 128, K_FWD_BK = 64, K_BWD_BQ = 64, K_BWD_BK = 128;
+
+flamia_status validate(const flamia_attn_desc* d) {
+  if (!d || !d->cu_seqlens) return FLAMIA_ERR_INVALID_ARG;
+  if (d->total_tokens < 0 || d->num_docs < 1 || d->num_heads < 1) return FLAMIA_ERR_INVALID_ARG;
+  if (d->max_doc_len < 0 || d->max_doc_len > d->total_tokens) return FLAMIA_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return FLAMIA_ERR_INVALID_ARG;
+  if ((d->hadamard | d->causal_dq_scale | d->deterministic | d->causal) & ~1) return FLAMIA_ERR_INVALID_ARG;
+  if (d->path != 0 && d->path != 1) return FLAMIA_ERR_INVALID_ARG;
+  if (!std::isfinite(d->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
+  if (d->causal != 1 || d->path != 0 || d->deterministic != 0) return FLAMIA_ERR_UNSUPPORTED;
+  // index limits: documents and tiles are packed into 24 and 20 bits of the
+  // sort key, costs into 20 bits, grid x into 31 bits
+  if (d->num_docs >= (1 << 24) || d->total_tokens >= (1 << 24)) return FLAMIA_ERR_WORKSPACE;
+  const int cap = cdiv(d->total_tokens, 64) + d->num_docs;
+  if (cap > PLAN_MAX_TILES) return FLAMIA_ERR_UNSUPPORTED;
+  if ((int64_t)cap * d->num_heads >= (int64_t)1 << 31) return FLAMIA_ERR_WORKSPACE;
+  return FLAMIA_OK;
+}
+
+PlanLayout plan_layout(const flamia_attn_desc* d) {
+  PlanLayout pl{};
+  pl.cap_fwd = cdiv(d->total_tokens, K_FWD_BQ) + d->num_docs;
+  pl.cap_bwd = cdiv(d->total_tokens, K_BWD_BK) + d->num_docs;
+  pl.fwd_offset = ALIGN;
+  pl.bwd_offset = align_up(pl.fwd_offset + sizeof(int) * 2 * (size_t)pl.cap_fwd);
+  pl.bytes = align_up(pl.bwd_offset + sizeof(int) * 2 * (size_t)pl.cap_bwd);
+  return pl;
+}
+
+struct QLayout {
+  size_t codes[4], exps[5], plan, bytes;
+};
+
+QLayout q_layout(const flamia_attn_desc* d) {
+  QLayout q{};
+  const size_t E = (size_t)d->total_tokens * d->num_heads * d->head_dim;
+  const size_t M = (size_t)d->total_tokens * d->num_heads;
+  size_t off = 0;
+  for (int i = 0; i < 4; ++i) { q.codes[i] = off; off = align_up(off + E); }
+  for (int i = 0; i < 5; ++i) { q.exps[i] = off; off = align_up(off + M); }
+  q.plan = off;
+  q.bytes = off + plan_layout(d).bytes;
+  return q;
+}
+
+BwdLayout bwd_layout(const flamia_attn_desc* d) {
+  BwdLayout b{};
+  const size_t E = (size_t)d->total_tokens * d->num_heads * d->head_dim;
+  const size_t M = (size_t)d->total_tokens * d->num_heads;
+  size_t off = 0;
+  b.do_codes = off; off = align_up(off + E);
+  b.do_exp = off;   off = align_up(off + M);
+  b.delta = off;    off = align_up(off + 4 * M);
+  b.g = off;        off = align_up(off + 2 * E);
+  b.dq_sigma = off; off = align_up(off + 4 * M);
+  b.dq_acc = off;   off = align_up(off + 2 * E);
+  b.dk_f32 = off;   off = align_up(off + 4 * E);
+  b.bytes = off;
+  return b;
+}
+
+Problem problem(const flamia_attn_desc* d) {
+  Problem p{};
+  p.cu = d->cu_seqlens;
+  p.T = d->total_tokens;
+  p.ndocs = d->num_docs;
+  p.H = d->num_heads;
+  p.D = d->head_dim;
+  p.hadamard = d->hadamard;
+  p.causal_dq_scale = d->causal_dq_scale;
+  p.softmax_scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+  p.c_log2 = (float)((double)p.softmax_scale * 1.4426950408889634);
+  return p;
+}
+
+bool qt_complete(const flamia_qtensors* q) {
+  return q && q->q_codes && q->k_codes && q->v_codes && q->v_key_codes && q->q_exp && q->k_exp &&
+         q->v_exp && q->v_key_exp && q->v_ref_exp && q->plan;
+}
+
+flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+flamia_status flamia_buffer_sizes(const flamia_attn_desc* desc, size_t* qtensor_bytes,
+                                  size_t* fwd_ws_bytes, size_t* bwd_ws_bytes) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (qtensor_bytes) *qtensor_bytes = q_layout(desc).bytes;
+  if (fwd_ws_bytes) *fwd_ws_bytes = 0;
+  if (bwd_ws_bytes) *bwd_ws_bytes = bwd_layout(desc).bytes;
+  return FLAMIA_OK;
+}
+
+flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base, flamia_qtensors* out) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!base || !out || (reinterpret_cast<uintptr_t>(base) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
+  const QLayout q = q_layout(desc);
+  uint8_t* b = static_cast<uint8_t*>(base);
+  out->q_codes = b + q.codes[0];
+  out->k_codes = b + q.codes[1];
+  out->v_codes = b + q.codes[2];
+  out->v_key_codes = b + q.codes[3];
+  out->q_exp = b + q.exps[0];
+  out->k_exp = b + q.exps[1];
+  out->v_exp = b + q.exps[2];
+  out->v_key_exp = b + q.exps[3];
+  out->v_ref_exp = b + q.exps[4];
+  out->plan = b + q.plan;
+  return FLAMIA_OK;
+}
+
+flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const void* k, const void* v,
+                              const flamia_qtensors* out, hipStream_t stream) {
+  flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!q || !k || !v || !qt_complete(out)) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  const PlanLayout pl = plan_layout(desc);
+  s = hip_status(launch_plan(p.cu, p.ndocs, out->plan, pl, stream));
+  if (s != FLAMIA_OK) return s;
+  return hip_status(launch_quant_qkv(p, q, k, v, out->q_codes, out->k_codes, out->v_codes, out->v_key_codes,
+                                     out->q_exp, out->k_exp, out->v_exp, out->v_key_exp, out->v_ref_exp,
+                                     stream));
+}
+
+flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
+                              int32_t* row_max, float* row_sum, void* ws, hipStream_t stream) {
+  (void)ws;
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!qt_complete(qt) || !o || !row_max || !row_sum) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  return hip_status(launch_attn_fwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
+                                    qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp,
+                                    qt->v_ref_exp, o, row_max, row_sum, stream));
+}
+
+flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
+                              const int32_t* row_max, const float* row_sum, const void* dout, void* dq,
+                              void* dk, void* dv, void* ws, hipStream_t stream) {
+  flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!qt_complete(qt) || !o || !row_max || !row_sum || !dout || !dq || !dk || !dv || !ws)
+    return FLAMIA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  const BwdLayout b = bwd_layout(desc);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  s = hip_status(launch_quant_do(p, dout, o, row_sum, qt->k_exp, qt->v_exp, w + b.do_codes, w + b.do_exp,
+                                 reinterpret_cast<float*>(w + b.delta), w + b.g,
+                                 reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
+  if (s != FLAMIA_OK) return s;
+  s = hip_status(launch_attn_bwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
+                                 qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp, qt->v_ref_exp,
+                                 row_max, row_sum, w + b.do_codes, w + b.do_exp,
+                                 reinterpret_cast<const float*>(w + b.delta), w + b.g,
+                                 reinterpret_cast<const int*>(w + b.dq_sigma), w + b.dq_acc,
+                                 reinterpret_cast<float*>(w + b.dk_f32), dv, stream));
+  if (s != FLAMIA_OK) return s;
+  return hip_status(launch_finalize(p, w + b.dq_acc, reinterpret_cast<const int*>(w + b.dq_sigma),
+                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, stream));
+}
+
+flamia_status flamia_tile_config(int32_t head_dim, int32_t* fwd_bq, int32_t* fwd_bk, int32_t* bwd_bq,
+                                 int32_t* bwd_bk) {
+  if (head_dim != 64 && head_dim != 128) return FLAMIA_ERR_INVALID_ARG;
+  if (fwd_bq) *fwd_bq = K_FWD_BQ;
+  if (fwd_bk) *fwd_bk = K_FWD_BK;
+  if (bwd_bq) *bwd_bq = K_BWD_BQ;
+  if (bwd_bk) *bwd_bk = K_BWD_BK;
+  return FLAMIA_OK;
+}
+
+flamia_status flamia_plan_view(const flamia_attn_desc* desc, size_t* fwd_offset, int32_t* cap_fwd,
+                               size_t* bwd_offset, int32_t* cap_bwd) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  const PlanLayout pl = plan_layout(desc);
+  if (fwd_offset) *fwd_offset = pl.fwd_offset;
+  if (cap_fwd) *cap_fwd = pl.cap_fwd;
+  if (bwd_offset) *bwd_offset = pl.bwd_offset;
+  if (cap_bwd) *cap_bwd = pl.cap_bwd;
+  return FLAMIA_OK;
+}
+
+const char* flamia_status_string(flamia_status status) {
+  switch (status) {
+    case FLAMIA_OK: return "ok";
+    case FLAMIA_ERR_INVALID_ARG: return "invalid argument";
+    case FLAMIA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FLAMIA_ERR_WORKSPACE: return "size exceeds the library's index limits";
+    case FLAMIA_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// Device helpers shared by the flamia HIP kernels (gfx950 / CDNA4 only).
+//
+// Operand layouts of the gfx950 matrix-core instructions used here, as
+// measured on the hardware:
+//
+// * v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulate).  A is
+//   32 x 64 (M x K), B is 64 x 32 (K x N).  Lane l = 32*h + m holds, for A,
+//   row m and for B, column m: bytes 0..15 are 16 K-values of K-block 0
+//   (K 0..31) and bytes 16..31 are 16 K-values of K-block 1 (K 32..63); the
+//   two lane halves h = 0, 1 hold complementary halves of each K-block.
+//   Lane (m, h) supplies the UE8M0 scale of K-block h of its row (A) or
+//   column (B).  Which 16 K-values a lane half holds inside a block is free,
+//   provided A and B agree.  C is 32 x 32: lane (n, h) holds column n and,
+//   in accumulator register rr = 4q + r, row 8q + 4h + r.
+// * v_mfma_f32_32x32x16_bf16: same A/B/C arrangement with 8 bf16 per lane;
+//   no scales, so any K assignment shared by A and B is valid.
+// * Swapping A and B yields exactly the transposed C (bit for bit), which
+//   lets the forward compute S^T and the backward S from the same products.
+//
+// The index convention used for every 32-token block of tokens is the
+// "pi order": token t = 8q + 4h + r of the block (the row held by lane half h
+// in register 4q + r of a C tile) is stored at position 16h + 4q + r, so a
+// lane half's 16 tokens are contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flamia {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int TOKEN_BLOCK = 32;   // tokens per scale block
+constexpr int FWD_BQ = 128;       // queries per forward work item
+constexpr int FWD_BK = 64;        // keys per forward inner step
+constexpr int BWD_BQ = 64;        // queries per backward inner step
+constexpr int BWD_BK = 128;       // keys per backward work item
+constexpr int E8M0_BIAS = 127;
+constexpr int P_EXP = -8;         // fixed exponent of the probability operand
+constexpr int M_NONE = -(1 << 20);  // running row max before any visible key
+
+__device__ __forceinline__ int pi_pos(int t) {   // t in [0, 32)
+  return ((t >> 2) & 1) * 16 + (t >> 3) * 4 + (t & 3);
+}
+
+// ---------------------------------------------------------------- formats
+
+// Smallest integer e with amax <= 448 * 2^e, from the fp32 bits:
+// amax = m 2^k with m in [1, 2): e = k - 8 if m <= 1.75, else k - 7.
+// amax == 0 (or an fp32 subnormal) gives -127; clamped to [-127, 127].
+__device__ __forceinline__ int roundup_exp(float amax) {
+  uint32_t b = __float_as_uint(amax) & 0x7fffffffu;
+  int be = (int)(b >> 23);
+  if (be == 0) return -127;
+  int k = be - 127;
+  int e = (b & 0x7fffffu) <= 0x600000u ? k - 8 : k - 7;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Two fp32 values -> two E4M3 codes (round to nearest even; inputs must be
+// within +-464 in magnitude, which every caller guarantees).
+__device__ __forceinline__ int cvt_fp8x2(float a, float b) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffff;
+}
+__device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+__device__ __forceinline__ float fp8_value(int packed, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(packed, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(packed, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(packed, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(packed, 3);
+  }
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ __bf16 f32_to_bf16(float f) {
+  uint16_t b = f32_to_bf16_bits(f);
+  return *reinterpret_cast<__bf16*>(&b);
+}
+
+// ---------------------------------------------------------------- matrix cores
+
+__device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+__device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------- small loads
+
+__device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
+__device__ __forceinline__ void st16(void* p, v4i v) { *reinterpret_cast<v4i*>(p) = v; }
+
+__device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Transpose a 4 x 4 byte block held as four dwords (row i = dword i, byte j
+// = column j) into four dwords (dword j = column j, byte i = row i).
+__device__ __forceinline__ void transpose4x4_b8(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                                uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3) {
+  // interleave bytes of (r0, r1) and (r2, r3), then 16-bit halves
+  uint32_t a0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
+  uint32_t a1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
+  uint32_t b0 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+  uint32_t b1 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+  c0 = __builtin_amdgcn_perm(b0, a0, 0x05040100u);           // a0.lo16 b0.lo16
+  c1 = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+  c2 = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+  c3 = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+}
+
+}  // namespace flamia

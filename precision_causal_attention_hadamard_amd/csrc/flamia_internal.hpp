@@ -1,0 +1,64 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace flamia {
+
+constexpr int PLAN_MAX_TILES = 8192;      // LDS capacity of the work-list sort
+constexpr int COST_MAX = (1 << 20) - 1;   // costs must stay below this
+
+struct PlanLayout {
+  size_t fwd_offset;   // bytes from the plan base to the forward (doc, tile) list
+  size_t bwd_offset;
+  int cap_fwd;         // ceil(T / FWD_BQ) + num_docs
+  int cap_bwd;         // ceil(T / BWD_BK) + num_docs
+  size_t bytes;
+};
+
+// Byte offsets of the backward workspace.
+struct BwdLayout {
+  size_t do_codes, do_exp, delta, g, dq_sigma, dq_acc, dk_f32, bytes;
+};
+
+struct Problem {
+  const int* cu;
+  int T, ndocs, H, D;
+  int hadamard, causal_dq_scale;
+  float softmax_scale;     // fp32 softmax scale
+  float c_log2;            // fp32(softmax_scale * log2(e))
+};
+
+hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, hipStream_t stream);
+
+hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, const void* v,
+                            uint8_t* q_codes, uint8_t* k_codes, uint8_t* v_codes, uint8_t* v_key_codes,
+                            uint8_t* q_exp, uint8_t* k_exp, uint8_t* v_exp, uint8_t* v_key_exp,
+                            uint8_t* v_ref_exp, hipStream_t stream);
+
+hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const float* row_sum,
+                           const uint8_t* k_exp, const uint8_t* v_exp, uint8_t* do_codes,
+                           uint8_t* do_exp, float* delta, void* g, int* dq_sigma, void* dq_acc,
+                           hipStream_t stream);
+
+hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout& pl,
+                           const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
+                           const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
+                           const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
+                           void* o, int* row_max, float* row_sum, hipStream_t stream);
+
+hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl,
+                           const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
+                           const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
+                           const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
+                           const int* row_max, const float* row_sum, const uint8_t* do_codes,
+                           const uint8_t* do_exp, const float* delta, const void* g,
+                           const int* dq_sigma, void* dq_acc, float* dk_f32, void* dv,
+                           hipStream_t stream);
+
+hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
+                           const float* dk_f32, void* dq, void* dk, hipStream_t stream);
+
+}  // namespace flamia

@@ -1,0 +1,301 @@
+// Fused quantizers of the training call (HBM-bound).
+//
+// quant_qkv_kernel: one workgroup per (32-token chunk of the packed array,
+// tensor in {Q, K, V}); it quantizes every document-local 32-token block
+// that STARTS in its chunk, for all heads (wave w takes heads w, w+4, ...).
+// A block never crosses a document, so a document boundary may fall
+// anywhere inside a chunk and a block may run past the chunk's end.
+// Per (block, head): load 32 rows x d bf16 (lane = (row, half-row)),
+// optional fp32 Hadamard butterflies on Q and K, amax over the block, the
+// round-up exponent, E4M3 codes; for V also the per-key exponents, per-key
+// codes and the per-query fold reference (prefix max of the per-key
+// exponents inside the block).  [Summary, §3.1 Token-Block Scaling; §3.2
+// Causally Safe Scales; §4.3 Ablation Study]; [Reading, 4.4] first bullet.
+//
+// quant_do_kernel: the backward's preparation, per block and head: token-block
+// codes of dO, D_i = sum_d dO~_id O_id from the same codes ([Summary, §3.3]:
+// D uses the quantized dO that dP uses), G_i = dO~_i 2^-8 / l_i in bf16 (the
+// right operand of dV = P^T G), the dQ accumulator prescale exponent of the
+// block, and zeroes the block's rows of the fp16 dQ accumulator.
+#include "flamia_device.hpp"
+#include "flamia_internal.hpp"
+
+namespace flamia {
+
+constexpr int QUANT_THREADS = 256;
+
+// Index of the document containing packed token t (cu[d] <= t < cu[d+1]).
+__device__ __forceinline__ int find_doc(const int* __restrict__ cu, int ndocs, int t) {
+  int lo = 0, hi = ndocs - 1;   // largest d with cu[d] <= t
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Calls f(block_start, block_end, doc_start, doc) for every document-local
+// 32-token block that starts inside chunk [c0, c0 + 32).  Uniform across the
+// workgroup.
+template <typename F>
+__device__ __forceinline__ void for_blocks_in_chunk(const int* __restrict__ cu, int ndocs, int T, int c0, F f) {
+  const int cend = min(c0 + TOKEN_BLOCK, T);
+  int d = find_doc(cu, ndocs, c0);
+  int s = cu[d], e = cu[d + 1];
+  int p = s + ((c0 - s + TOKEN_BLOCK - 1) / TOKEN_BLOCK) * TOKEN_BLOCK;
+  while (true) {
+    if (p >= e) {               // document exhausted (or empty): next document
+      if (d + 1 >= ndocs) break;
+      ++d;
+      s = cu[d];
+      e = cu[d + 1];
+      p = s;
+      continue;
+    }
+    if (p >= cend) break;       // next block of this document starts past the chunk
+    f(p, min(p + TOKEN_BLOCK, e), s, d);
+    p += TOKEN_BLOCK;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_half_row(const uint16_t* __restrict__ src, bool valid, float (&x)[D / 2]) {
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      v4i w = ld16(src + 8 * c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t u = (uint32_t)w[j];
+        x[8 * c + 2 * j] = __uint_as_float(u << 16);
+        x[8 * c + 2 * j + 1] = __uint_as_float(u & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) x[i] = 0.f;
+  }
+}
+
+// In-place normalised Hadamard transform of a d-row split over two lanes
+// (lane half `hf` holds channels [hf d/2, (hf+1) d/2)).  For h = 1, 2, ...,
+// d/2 every pair (a, a+h) of each aligned 2h-group becomes
+// (x_a + x_{a+h}, x_a - x_{a+h}) in fp32 (round to nearest even), then every
+// element is multiplied once by fp32(1/sqrt(d)).  The last stage pairs the
+// two lanes of a row.
+template <int D>
+__device__ __forceinline__ void fwht_half_row(float (&x)[D / 2], int hf) {
+#pragma unroll
+  for (int h = 1; h < D / 2; h <<= 1) {
+#pragma unroll
+    for (int a = 0; a < D / 2; ++a) {
+      if ((a & h) == 0) {
+        float lo = x[a], hi = x[a + h];
+        x[a] = lo + hi;
+        x[a + h] = lo - hi;
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < D / 2; ++a) {
+    float other = __shfl_xor(x[a], 1, 64);
+    x[a] = hf == 0 ? x[a] + other : other - x[a];
+  }
+  const float inv_sqrt_d = D == 64 ? 0.125f : __uint_as_float(0x3db504f3u);  // fp32(2^-3.5)
+#pragma unroll
+  for (int a = 0; a < D / 2; ++a) x[a] = x[a] * inv_sqrt_d;
+}
+
+// Codes of a half-row, scaled by 2^-e (exact), written as 16-byte chunks.
+template <int D>
+__device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst, const float (&x)[D / 2], int e) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    v4i w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = 16 * c + 4 * j;
+      w[j] = cvt_fp8x4(__builtin_amdgcn_ldexpf(x[b], -e), __builtin_amdgcn_ldexpf(x[b + 1], -e),
+                       __builtin_amdgcn_ldexpf(x[b + 2], -e), __builtin_amdgcn_ldexpf(x[b + 3], -e));
+    }
+    st16(dst + 16 * c, w);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ float half_row_amax(const float (&x)[D / 2]) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 2; ++i) m = fmaxf(m, fabsf(x[i]));
+  return m;
+}
+
+template <int D>
+__global__ void __launch_bounds__(QUANT_THREADS)
+quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                 const uint16_t* __restrict__ v, uint8_t* __restrict__ q_codes,
+                 uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
+                 uint8_t* __restrict__ v_key_codes, uint8_t* __restrict__ q_exp,
+                 uint8_t* __restrict__ k_exp, uint8_t* __restrict__ v_exp,
+                 uint8_t* __restrict__ v_key_exp, uint8_t* __restrict__ v_ref_exp) {
+  const int tensor = blockIdx.y;
+  const uint16_t* src = tensor == 0 ? q : (tensor == 1 ? k : v);
+  uint8_t* codes = tensor == 0 ? q_codes : (tensor == 1 ? k_codes : v_codes);
+  uint8_t* exps = tensor == 0 ? q_exp : (tensor == 1 ? k_exp : v_exp);
+  const bool rotate = p.hadamard && tensor < 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane >> 1, hf = lane & 1;
+  const int c0 = blockIdx.x * TOKEN_BLOCK;
+  const int H = p.H, T = p.T;
+
+  for_blocks_in_chunk(p.cu, p.ndocs, T, c0, [&](int bs, int be, int, int) {
+    const int tok = bs + row;
+    const bool valid = tok < be;
+    for (int h = wave; h < H; h += QUANT_THREADS / 64) {
+      const size_t off = ((size_t)tok * H + h) * D + hf * (D / 2);
+      float x[D / 2];
+      load_half_row<D>(src + off, valid, x);
+      if (rotate) fwht_half_row<D>(x, hf);
+      const float lane_amax = half_row_amax<D>(x);
+      const int e = roundup_exp(wave_max(lane_amax));
+      if (valid) {
+        store_codes<D>(codes + off, x, e);
+        if (hf == 0) exps[(size_t)h * T + tok] = (uint8_t)(e + E8M0_BIAS);
+      }
+      if (tensor == 2) {
+        const float row_amax = fmaxf(lane_amax, __shfl_xor(lane_amax, 1, 64));
+        const int ek = roundup_exp(row_amax);
+        // prefix max of per-key exponents over rows 0..row of the block
+        int ref = valid ? ek : -127;
+#pragma unroll
+        for (int o = 2; o < 64; o <<= 1) {
+          int up = __shfl_up(ref, o, 64);
+          if (lane >= o) ref = max(ref, up);
+        }
+        if (valid) {
+          store_codes<D>(v_key_codes + off, x, ek);
+          if (hf == 0) {
+            v_key_exp[(size_t)h * T + tok] = (uint8_t)(ek + E8M0_BIAS);
+            v_ref_exp[(size_t)h * T + tok] = (uint8_t)(ref + E8M0_BIAS);
+          }
+        }
+      }
+    }
+  });
+}
+
+template <int D>
+__global__ void __launch_bounds__(QUANT_THREADS)
+quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
+                const float* __restrict__ row_sum, const uint8_t* __restrict__ k_exp,
+                const uint8_t* __restrict__ v_exp, uint8_t* __restrict__ do_codes,
+                uint8_t* __restrict__ do_exp, float* __restrict__ delta, uint16_t* __restrict__ g,
+                int* __restrict__ dq_sigma, uint16_t* __restrict__ dq_acc) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane >> 1, hf = lane & 1;
+  const int c0 = blockIdx.x * TOKEN_BLOCK;
+  const int H = p.H, T = p.T;
+  constexpr int LOG2D = D == 64 ? 6 : 7;
+
+  for_blocks_in_chunk(p.cu, p.ndocs, T, c0, [&](int bs, int be, int ds, int doc) {
+    const int tok = bs + row;
+    const bool valid = tok < be;
+    const int blk = (bs - ds) / TOKEN_BLOCK;
+    const int de = p.cu[doc + 1];
+    const int nblk_doc = (de - ds + TOKEN_BLOCK - 1) / TOKEN_BLOCK;
+    const int nvis = p.causal_dq_scale ? blk + 1 : nblk_doc;
+    for (int h = wave; h < H; h += QUANT_THREADS / 64) {
+      const size_t off = ((size_t)tok * H + h) * D + hf * (D / 2);
+      float x[D / 2];
+      load_half_row<D>(dout + off, valid, x);
+      const int e = roundup_exp(wave_max(half_row_amax<D>(x)));
+      // largest K and V block exponents over the visible key blocks
+      int emax_kv = -254;
+      {
+        int ek = -127, ev = -127;
+        for (int J = lane; J < nvis; J += 64) {
+          const size_t t0 = (size_t)h * T + ds + J * TOKEN_BLOCK;
+          ek = max(ek, (int)k_exp[t0] - E8M0_BIAS);
+          ev = max(ev, (int)v_exp[t0] - E8M0_BIAS);
+        }
+        emax_kv = wave_max_i(ek) + wave_max_i(ev);
+      }
+      if (valid) {
+        // codes, dequantized values, D and G
+        float oo[D / 2];
+        load_half_row<D>(o + off, true, oo);
+        float dsum = 0.f;
+        const float l = row_sum[(size_t)h * T + tok];
+        const float ginv = __builtin_amdgcn_ldexpf(1.0f / l, P_EXP);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          v4i w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int b = 16 * c + 4 * j;
+            w[j] = cvt_fp8x4(__builtin_amdgcn_ldexpf(x[b], -e), __builtin_amdgcn_ldexpf(x[b + 1], -e),
+                             __builtin_amdgcn_ldexpf(x[b + 2], -e), __builtin_amdgcn_ldexpf(x[b + 3], -e));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[b + t] = __builtin_amdgcn_ldexpf(fp8_value(w[j], t), e);
+          }
+          st16(do_codes + off + 16 * c, w);
+        }
+#pragma unroll
+        for (int i = 0; i < D / 2; ++i) dsum = __builtin_fmaf(x[i], oo[i], dsum);
+        dsum += __shfl_xor(dsum, 1, 64);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          v4i w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int b = 8 * c + 2 * j;
+            uint32_t lo = f32_to_bf16_bits(x[b] * ginv), hi = f32_to_bf16_bits(x[b + 1] * ginv);
+            w[j] = (int)(lo | (hi << 16));
+          }
+          st16(g + off + 8 * c, w);
+          st16(dq_acc + off + 8 * c, v4i{0, 0, 0, 0});
+        }
+        if (hf == 0) {
+          const size_t mi = (size_t)h * T + tok;
+          do_exp[mi] = (uint8_t)(e + E8M0_BIAS);
+          delta[mi] = dsum;
+          // |dQ partial sum| <= 2.2 d 448^3 2^(e_dO + e_V + e_K) < 2^(27.6 + log2 d + ...);
+          // the prescale keeps it below 2^15 in fp16
+          dq_sigma[mi] = e + emax_kv + LOG2D + 13;
+        }
+      }
+    }
+  });
+}
+
+hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, const void* v,
+                            uint8_t* q_codes, uint8_t* k_codes, uint8_t* v_codes, uint8_t* v_key_codes,
+                            uint8_t* q_exp, uint8_t* k_exp, uint8_t* v_exp, uint8_t* v_key_exp,
+                            uint8_t* v_ref_exp, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK, 3);
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, q_codes, k_codes, v_codes, v_key_codes,
+                       q_exp, k_exp, v_exp, v_key_exp, v_ref_exp);
+  };
+  if (p.D == 64) args(quant_qkv_kernel<64>); else args(quant_qkv_kernel<128>);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const float* row_sum,
+                           const uint8_t* k_exp, const uint8_t* v_exp, uint8_t* do_codes,
+                           uint8_t* do_exp, float* delta, void* g, int* dq_sigma, void* dq_acc,
+                           hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK);
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)dout,
+                       (const uint16_t*)o, row_sum, k_exp, v_exp, do_codes, do_exp, delta,
+                       (uint16_t*)g, dq_sigma, (uint16_t*)dq_acc);
+  };
+  if (p.D == 64) args(quant_do_kernel<64>); else args(quant_do_kernel<128>);
+  return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -1,0 +1,214 @@
+"""Thin Python binding of libflamia.so (ctypes).
+
+Same names as the C ABI in ``include/flamia.h``; this module only marshals
+arguments.  PyTorch supplies device memory and the stream; every step of the
+call runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, ``load()`` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflamia.so")
+
+FLAMIA_OK = 0
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+           3: "size exceeds the library's index limits", 4: "HIP kernel launch failed"}
+
+
+class FlamiaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("total_tokens", ctypes.c_int32), ("num_docs", ctypes.c_int32),
+                ("max_doc_len", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("hadamard", ctypes.c_int32), ("causal_dq_scale", ctypes.c_int32),
+                ("deterministic", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class QTensors(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("q_codes", "k_codes", "v_codes", "v_key_codes", "q_exp", "k_exp", "v_exp",
+                 "v_key_exp", "v_ref_exp", "plan")]
+
+
+EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_quantize", "flamia_attn_fwd",
+           "flamia_attn_bwd", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libflamia.so (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with precision_causal_attention_hadamard_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    dp, qp = ctypes.POINTER(AttnDesc), ctypes.POINTER(QTensors)
+    sig = {
+        "flamia_buffer_sizes": [dp, ctypes.POINTER(S), ctypes.POINTER(S), ctypes.POINTER(S)],
+        "flamia_qtensors_layout": [dp, P, qp],
+        "flamia_quantize": [dp, P, P, P, qp, P],
+        "flamia_attn_fwd": [dp, qp, P, P, P, P, P],
+        "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
+        "flamia_tile_config": [I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
+        "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I)],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.flamia_status_string.argtypes = [ctypes.c_int]
+    lib.flamia_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != FLAMIA_OK:
+        raise FlamiaError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(cu_seqlens_dev: torch.Tensor, total_tokens: int, num_docs: int, max_doc_len: int,
+              num_heads: int, head_dim: int, hadamard: bool = False, causal_dq_scale: bool = False,
+              softmax_scale: float = 0.0, path: int = 0, causal: int = 1, deterministic: int = 0) -> AttnDesc:
+    return AttnDesc(total_tokens, num_docs, max_doc_len,
+                    cu_seqlens_dev.data_ptr() if cu_seqlens_dev is not None else None,
+                    num_heads, head_dim, causal, path, int(hadamard), int(causal_dq_scale),
+                    deterministic, softmax_scale)
+
+
+def buffer_sizes(desc: AttnDesc):
+    q, f, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().flamia_buffer_sizes(ctypes.byref(desc), ctypes.byref(q), ctypes.byref(f), ctypes.byref(b)),
+           "flamia_buffer_sizes")
+    return q.value, f.value, b.value
+
+
+def qtensors_layout(desc: AttnDesc, base: torch.Tensor) -> QTensors:
+    qt = QTensors()
+    _check(load().flamia_qtensors_layout(ctypes.byref(desc), _ptr(base), ctypes.byref(qt)),
+           "flamia_qtensors_layout")
+    return qt
+
+
+def quantize(desc, q, k, v, qt: QTensors, stream=None):
+    _check(load().flamia_quantize(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(qt),
+                                  _stream(stream)), "flamia_quantize")
+
+
+def attn_fwd(desc, qt: QTensors, o, row_max, row_sum, ws=None, stream=None):
+    _check(load().flamia_attn_fwd(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
+                                  _ptr(row_sum), _ptr(ws), _stream(stream)), "flamia_attn_fwd")
+
+
+def attn_bwd(desc, qt: QTensors, o, row_max, row_sum, dout, dq, dk, dv, ws, stream=None):
+    _check(load().flamia_attn_bwd(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
+                                  _ptr(row_sum), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                  _stream(stream)), "flamia_attn_bwd")
+
+
+def tile_config(head_dim: int):
+    v = [ctypes.c_int32() for _ in range(4)]
+    _check(load().flamia_tile_config(head_dim, *[ctypes.byref(x) for x in v]), "flamia_tile_config")
+    return tuple(x.value for x in v)
+
+
+def plan_view(desc: AttnDesc):
+    fo, bo = ctypes.c_size_t(), ctypes.c_size_t()
+    cf, cb = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().flamia_plan_view(ctypes.byref(desc), ctypes.byref(fo), ctypes.byref(cf), ctypes.byref(bo),
+                                   ctypes.byref(cb)), "flamia_plan_view")
+    return fo.value, cf.value, bo.value, cb.value
+
+
+def status_string(status: int) -> str:
+    return load().flamia_status_string(status).decode()
+
+
+class TrainingCall:
+    """Device buffers and the three calls of one packed attention training
+    step (quantize, forward, backward).  Inputs are bf16 ``[T, H, d]`` CUDA
+    tensors; ``cu_seqlens`` a list of ints."""
+
+    def __init__(self, q, k, v, do, cu_seqlens, hadamard=False, causal_dq_scale=False,
+                 softmax_scale=0.0, path=0):
+        dev = q.device
+        self.q, self.k, self.v, self.do = q, k, v, do
+        T, H, d = q.shape
+        self.cu_list = [int(c) for c in cu_seqlens]
+        self.cu = torch.tensor(self.cu_list, dtype=torch.int32, device=dev)
+        lens = [b - a for a, b in zip(self.cu_list, self.cu_list[1:])]
+        self.desc = make_desc(self.cu, T, len(lens), max(lens) if lens else 0, H, d, hadamard,
+                              causal_dq_scale, softmax_scale, path)
+        qb, fb, bb = buffer_sizes(self.desc)
+        self.qbuf = torch.empty(qb, dtype=torch.uint8, device=dev)
+        self.qt = qtensors_layout(self.desc, self.qbuf)
+        self.bws = torch.empty(max(bb, 1), dtype=torch.uint8, device=dev)
+        self.fws = torch.empty(fb, dtype=torch.uint8, device=dev) if fb else None
+        self.o = torch.empty_like(q)
+        self.row_max = torch.empty(H, T, dtype=torch.int32, device=dev)
+        self.row_sum = torch.empty(H, T, dtype=torch.float32, device=dev)
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(q)
+        self.dv = torch.empty_like(q)
+        self.shape = (T, H, d)
+
+    def quantize(self, stream=None):
+        quantize(self.desc, self.q, self.k, self.v, self.qt, stream)
+
+    def forward(self, stream=None):
+        attn_fwd(self.desc, self.qt, self.o, self.row_max, self.row_sum, self.fws, stream)
+
+    def backward(self, stream=None):
+        attn_bwd(self.desc, self.qt, self.o, self.row_max, self.row_sum, self.do, self.dq, self.dk,
+                 self.dv, self.bws, stream)
+
+    def step(self, stream=None):
+        self.quantize(stream)
+        self.forward(stream)
+        self.backward(stream)
+
+    # views of the quantized payload (for tests)
+    def _view(self, field: str, nbytes: int) -> torch.Tensor:
+        off = getattr(self.qt, field) - self.qbuf.data_ptr()
+        return self.qbuf[off:off + nbytes]
+
+    def codes(self, field: str) -> torch.Tensor:
+        T, H, d = self.shape
+        return self._view(field, T * H * d).view(T, H, d)
+
+    def exps(self, field: str) -> torch.Tensor:
+        T, H, _ = self.shape
+        return self._view(field, T * H).view(H, T)
+
+    def plan_lists(self):
+        fo, cf, bo, cb = plan_view(self.desc)
+        base = self.qt.plan - self.qbuf.data_ptr()
+        raw = self.qbuf[base:base + bo + 8 * cb]
+        counts = raw[:16].view(torch.int32).cpu()
+        fwd = raw[fo:fo + 8 * cf].view(torch.int32).view(cf, 2).cpu()
+        bwd = raw[bo:bo + 8 * cb].view(torch.int32).view(cb, 2).cpu()
+        return fwd[: int(counts[0])], bwd[: int(counts[1])]

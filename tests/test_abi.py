@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every function include/flamia.h declares,
+and rejects bad host arguments before launching anything (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from precision_causal_attention_hadamard_amd import flamia
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flamia.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flamia_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return flamia.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(flamia.EXPORTS)
+
+
+def base_desc(**kw):
+    fake_cu = ctypes.c_void_p(0x1000)   # never dereferenced by host-side validation
+    d = flamia.AttnDesc(256, 1, 256, fake_cu.value, 2, 64, 1, 0, 0, 0, 0, 0.0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def sizes_status(lib, d):
+    q, f, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    return lib.flamia_buffer_sizes(ctypes.byref(d), ctypes.byref(q), ctypes.byref(f), ctypes.byref(b)), q.value, b.value
+
+
+def test_buffer_sizes_valid(lib):
+    st, q, b = sizes_status(lib, base_desc())
+    assert st == 0
+    T, H, d = 256, 2, 64
+    assert q >= 4 * T * H * d + 5 * T * H           # codes + exponent bytes + plan
+    assert b >= T * H * d * (1 + 2 + 2 + 4)          # dO codes, G, dQ acc, dK staging
+
+
+@pytest.mark.parametrize("field,value,want", [
+    ("head_dim", 96, 1), ("head_dim", 256, 1), ("num_heads", 0, 1), ("num_docs", 0, 1),
+    ("total_tokens", -1, 1), ("max_doc_len", 300, 1), ("hadamard", 2, 1),
+    ("causal", 0, 2), ("deterministic", 1, 2), ("path", 1, 2), ("path", 7, 1),
+])
+def test_invalid_and_unsupported_descriptors(lib, field, value, want):
+    st, _, _ = sizes_status(lib, base_desc(**{field: value}))
+    assert st == want, (field, value, st)
+
+
+def test_null_arguments_rejected_without_launch(lib):
+    assert lib.flamia_buffer_sizes(None, None, None, None) == 1
+    d = base_desc(cu_seqlens=None)
+    assert sizes_status(lib, d)[0] == 1
+    d = base_desc()
+    qt = flamia.QTensors()
+    # NULL inputs / incomplete qtensors: rejected before any kernel is launched
+    assert lib.flamia_quantize(ctypes.byref(d), None, None, None, ctypes.byref(qt), None) == 1
+    assert lib.flamia_attn_fwd(ctypes.byref(d), ctypes.byref(qt), None, None, None, None, None) == 1
+    assert lib.flamia_attn_bwd(ctypes.byref(d), ctypes.byref(qt), *([None] * 9)) == 1
+
+
+def test_layout_alignment_and_carving(lib):
+    d = base_desc()
+    qt = flamia.QTensors()
+    assert lib.flamia_qtensors_layout(ctypes.byref(d), ctypes.c_void_p(0x10010), ctypes.byref(qt)) == 1
+    assert lib.flamia_qtensors_layout(ctypes.byref(d), ctypes.c_void_p(0x100000), ctypes.byref(qt)) == 0
+    ptrs = [getattr(qt, f) for f, _ in flamia.QTensors._fields_]
+    assert all(p % 256 == 0 for p in ptrs) and len(set(ptrs)) == len(ptrs)
+    assert qt.k_codes - qt.q_codes >= 256 * 2 * 64
+
+
+def test_tile_config_and_status_strings(lib):
+    assert flamia.tile_config(128) == (128, 64, 64, 128)
+    assert flamia.tile_config(64) == (128, 64, 64, 128)
+    with pytest.raises(flamia.FlamiaError):
+        flamia.tile_config(32)
+    for s in range(5):
+        assert flamia.status_string(s)
+    assert flamia.status_string(99) == "unknown status"
+
+
+def test_plan_capacity_limit_is_reported(lib):
+    # more tiles than the in-LDS sort holds: unsupported, not a fault
+    d = base_desc(total_tokens=1 << 20, max_doc_len=1 << 20, num_docs=1)
+    assert sizes_status(lib, d)[0] == 2
