@@ -1,0 +1,189 @@
+"""Benchmark of the causal block-scaled MXFP8 attention training call on one
+MI355X: quantize + forward + backward over packed documents, inputs resident
+in HBM, one JSON line on stdout.
+
+A step is one whole call (flamia_quantize, flamia_attn_fwd, flamia_attn_bwd)
+over the 2 x 4096-token, 16-head, head-dim-128 workload with 1% outlier
+channels and the Hadamard rotation on.  Throughput counts the algorithmic
+causal FLOPs, 14 * d per (query, key) pair with key <= query inside a
+document (forward 2 products, backward 5); quantization adds no FLOPs but
+its time is inside the step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+                       [--no-cpu-baseline] [--copy-calibration]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix-core peak (published)
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E bandwidth (published)
+METRIC = "fwd+bwd attention call ms & TFLOP/s incl. quantization; % of MFMA FP8 peak"
+KERNEL_SOURCES = {
+    "attn_bwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_bwd.hip",
+    "attn_fwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_fwd.hip",
+    "quant_qkv_kernel": "precision_causal_attention_hadamard_amd/csrc/quant.hip",
+}
+
+
+def source_hash(path: str) -> str:
+    h = hashlib.sha256()
+    for p in (path, "precision_causal_attention_hadamard_amd/csrc/flamia_device.hpp"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, cfg: int):
+    """The oracle, as it stands, on one (document, head) slice of the
+    workload, timed on the host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as A
+
+    s, e = wl.cu_seqlens[0], wl.cu_seqlens[1]
+    arrs = [t[s:e, 0:1].float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
+    L = e - s
+    t0 = time.perf_counter()
+    A.training_call(*arrs, [0, L], A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8"))
+    dt = time.perf_counter() - t0
+    flops = 14 * wl.head_dim * L * (L + 1) // 2
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"document 0 ({L} tokens), head 0 of the {wl.name} workload: quantize+fwd+bwd, "
+                      f"{dt:.2f} s; fp64 numpy, BLAS threads={threads}, elementwise steps single-threaded",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (known bytes) for counter calibration")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the call would shard by heads/documents with no exchange, which is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from precision_causal_attention_hadamard_amd import flamia, workloads
+
+    flamia.load()
+    wl = workloads.config(args.config)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
+    call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
+                               causal_dq_scale=wl.causal_dq_scale, path=wl.path)
+    T, H, d = call.shape
+    pairs = wl.causal_pairs()
+    flops = wl.flops()
+
+    def step(ev=None):
+        if ev is not None: ev[0].record()
+        call.quantize()
+        if ev is not None: ev[1].record()
+        call.forward()
+        if ev is not None: ev[2].record()
+        flamia.attn_bwd_prep(call.desc, call.qt, call.o, call.row_sum, call.do, call.bws)
+        if ev is not None: ev[3].record()
+        flamia.attn_bwd_main(call.desc, call.qt, call.row_max, call.row_sum, call.dv, call.bws)
+        if ev is not None: ev[4].record()
+        flamia.attn_bwd_finish(call.desc, call.dq, call.dk, call.bws)
+        if ev is not None: ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    names = ["quantize", "attn_fwd", "bwd_prep", "attn_bwd", "bwd_finish"]
+    stage_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps
+                for i, n in enumerate(names)}
+    event_ms = sum(stage_ms.values())
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel
+    E = T * H * d
+    kernels = {
+        "attn_bwd": ("attn_bwd_kernel", "mfma", 10 * d * pairs),
+        "attn_fwd": ("attn_fwd_kernel", "mfma", 4 * d * pairs),
+        "quantize": ("quant_qkv_kernel", "hbm", 10 * E + 5 * T * H),
+    }
+    dom = max(kernels, key=lambda n: stage_ms[n])
+    kname, bound, work = kernels[dom]
+    t_dom = stage_ms[dom] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = work / t_dom / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / t_dom / 1e9, HBM_PEAK_GBS, "GB/s"
+    roofline = {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": measured_traffic(kname, f"config{args.config}"),
+                "algorithmic_work_per_launch": work, "avg_launch_ms": stage_ms[dom]}
+    qbytes = 10 * E + 5 * T * H
+    quant = {"GB/s": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9,
+             "frac_hbm_peak": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "algorithmic_bytes": qbytes, "launches": 2}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": d,
+                   "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
+                   "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
+                   "causal_pairs": pairs, "flops_per_step": flops},
+        "pct_fp8_peak": 100.0 * value / FP8_PEAK_TFLOPS,
+        "stage_ms": stage_ms, "event_ms_per_step": event_ms,
+        "quantizer": quant,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.config)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

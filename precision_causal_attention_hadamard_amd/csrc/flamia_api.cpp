@@ -158,6 +158,51 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
                                     qt->v_ref_exp, o, row_max, row_sum, stream));
 }
 
+flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
+                                   const float* row_sum, const void* dout, void* ws, hipStream_t stream) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!qt_complete(qt) || !o || !row_sum || !dout || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  const BwdLayout b = bwd_layout(desc);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  return hip_status(launch_quant_do(p, dout, o, row_sum, qt->k_exp, qt->v_exp, w + b.do_codes, w + b.do_exp,
+                                    reinterpret_cast<float*>(w + b.delta), w + b.g,
+                                    reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
+}
+
+flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt,
+                                   const int32_t* row_max, const float* row_sum, void* dv, void* ws,
+                                   hipStream_t stream) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!qt_complete(qt) || !row_max || !row_sum || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  const BwdLayout b = bwd_layout(desc);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  return hip_status(launch_attn_bwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
+                                    qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp,
+                                    qt->v_ref_exp, row_max, row_sum, w + b.do_codes, w + b.do_exp,
+                                    reinterpret_cast<const float*>(w + b.delta), w + b.g,
+                                    reinterpret_cast<const int*>(w + b.dq_sigma), w + b.dq_acc,
+                                    reinterpret_cast<float*>(w + b.dk_f32), dv, stream));
+}
+
+flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, void* dq, void* dk, void* ws,
+                                     hipStream_t stream) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!dq || !dk || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  const BwdLayout b = bwd_layout(desc);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  return hip_status(launch_finalize(p, w + b.dq_acc, reinterpret_cast<const int*>(w + b.dq_sigma),
+                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, stream));
+}
+
 flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
                               const int32_t* row_max, const float* row_sum, const void* dout, void* dq,
                               void* dk, void* dv, void* ws, hipStream_t stream) {
@@ -165,23 +210,11 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
   if (s != FLAMIA_OK) return s;
   if (!qt_complete(qt) || !o || !row_max || !row_sum || !dout || !dq || !dk || !dv || !ws)
     return FLAMIA_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
-  const Problem p = problem(desc);
-  const BwdLayout b = bwd_layout(desc);
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  s = hip_status(launch_quant_do(p, dout, o, row_sum, qt->k_exp, qt->v_exp, w + b.do_codes, w + b.do_exp,
-                                 reinterpret_cast<float*>(w + b.delta), w + b.g,
-                                 reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
+  s = flamia_attn_bwd_prep(desc, qt, o, row_sum, dout, ws, stream);
   if (s != FLAMIA_OK) return s;
-  s = hip_status(launch_attn_bwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
-                                 qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp, qt->v_ref_exp,
-                                 row_max, row_sum, w + b.do_codes, w + b.do_exp,
-                                 reinterpret_cast<const float*>(w + b.delta), w + b.g,
-                                 reinterpret_cast<const int*>(w + b.dq_sigma), w + b.dq_acc,
-                                 reinterpret_cast<float*>(w + b.dk_f32), dv, stream));
+  s = flamia_attn_bwd_main(desc, qt, row_max, row_sum, dv, ws, stream);
   if (s != FLAMIA_OK) return s;
-  return hip_status(launch_finalize(p, w + b.dq_acc, reinterpret_cast<const int*>(w + b.dq_sigma),
-                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, stream));
+  return flamia_attn_bwd_finish(desc, dq, dk, ws, stream);
 }
 
 flamia_status flamia_tile_config(int32_t head_dim, int32_t* fwd_bq, int32_t* fwd_bk, int32_t* bwd_bq,

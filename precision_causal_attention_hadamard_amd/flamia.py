@@ -43,7 +43,8 @@ class QTensors(ctypes.Structure):
 
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_quantize", "flamia_attn_fwd",
-           "flamia_attn_bwd", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
+           "flamia_attn_bwd", "flamia_attn_bwd_prep", "flamia_attn_bwd_main", "flamia_attn_bwd_finish",
+           "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
 
 _lib = None
 
@@ -64,6 +65,9 @@ def load(path: str = LIB_PATH):
         "flamia_quantize": [dp, P, P, P, qp, P],
         "flamia_attn_fwd": [dp, qp, P, P, P, P, P],
         "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
+        "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P],
+        "flamia_attn_bwd_main": [dp, qp, P, P, P, P, P],
+        "flamia_attn_bwd_finish": [dp, P, P, P, P],
         "flamia_tile_config": [I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
         "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I)],
     }
@@ -130,6 +134,21 @@ def attn_bwd(desc, qt: QTensors, o, row_max, row_sum, dout, dq, dk, dv, ws, stre
                                   _stream(stream)), "flamia_attn_bwd")
 
 
+def attn_bwd_prep(desc, qt: QTensors, o, row_sum, dout, ws, stream=None):
+    _check(load().flamia_attn_bwd_prep(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_sum),
+                                       _ptr(dout), _ptr(ws), _stream(stream)), "flamia_attn_bwd_prep")
+
+
+def attn_bwd_main(desc, qt: QTensors, row_max, row_sum, dv, ws, stream=None):
+    _check(load().flamia_attn_bwd_main(ctypes.byref(desc), ctypes.byref(qt), _ptr(row_max), _ptr(row_sum),
+                                       _ptr(dv), _ptr(ws), _stream(stream)), "flamia_attn_bwd_main")
+
+
+def attn_bwd_finish(desc, dq, dk, ws, stream=None):
+    _check(load().flamia_attn_bwd_finish(ctypes.byref(desc), _ptr(dq), _ptr(dk), _ptr(ws), _stream(stream)),
+           "flamia_attn_bwd_finish")
+
+
 def tile_config(head_dim: int):
     v = [ctypes.c_int32() for _ in range(4)]
     _check(load().flamia_tile_config(head_dim, *[ctypes.byref(x) for x in v]), "flamia_tile_config")
@@ -185,6 +204,11 @@ class TrainingCall:
     def backward(self, stream=None):
         attn_bwd(self.desc, self.qt, self.o, self.row_max, self.row_sum, self.do, self.dq, self.dk,
                  self.dv, self.bws, stream)
+
+    def backward_staged(self, stream=None):
+        attn_bwd_prep(self.desc, self.qt, self.o, self.row_sum, self.do, self.bws, stream)
+        attn_bwd_main(self.desc, self.qt, self.row_max, self.row_sum, self.dv, self.bws, stream)
+        attn_bwd_finish(self.desc, self.dq, self.dk, self.bws, stream)
 
     def step(self, stream=None):
         self.quantize(stream)
