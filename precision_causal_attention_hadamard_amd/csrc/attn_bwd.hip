@@ -140,6 +140,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   __shared__ int sVref[BWD_BQ];
   __shared__ int sQeB[2], sDOeB[2], sKeB[4];
   __shared__ int sEds[2][4];
+  __shared__ __attribute__((aligned(16))) uint16_t sdQ[BWD_BQ * D];   // fp16 dQ tile partial
 
   const Problem& p = a.p;
   const int H = p.H, T = p.T;
@@ -347,19 +348,30 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
         acc = mfma_f8(ktreg[ks], cat8(ld16(dr + 16 * hh), ld16(dr + 32 + 16 * hh)), acc,
                       sKeB[2 * ks + hh], sEds[qb][2 * ks + hh] + E8M0_BIAS);
       }
+      // prescaled fp16 partial of this query row into LDS (4 consecutive d per store)
       const int iq = 32 * qb + n;               // query row within the tile
-      if (iq < nq) {
-        const int sig = sSig[iq];
-        uint16_t* dst = a.dq_acc + (size_t)(s_d + q0 + iq) * rs + (size_t)head * D + 32 * ds + 4 * hh;
+      const int sig = sSig[iq];
+      uint16_t* dst = sdQ + iq * D + 32 * ds + 4 * hh;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            v2h hv;
-            hv[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 2 * pr], -sig);
-            hv[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 2 * pr + 1], -sig);
-            __builtin_amdgcn_global_atomic_fadd_v2f16(reinterpret_cast<v2h*>(dst + 8 * g + 2 * pr), hv);
-          }
+      for (int g = 0; g < 4; ++g) {
+        v2h h0, h1;
+        h0[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g], -sig);
+        h0[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 1], -sig);
+        h1[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 2], -sig);
+        h1[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 3], -sig);
+        *reinterpret_cast<v2i*>(dst + 8 * g) = v2i{*reinterpret_cast<int*>(&h0), *reinterpret_cast<int*>(&h1)};
+      }
+    }
+    __syncthreads();
+    // row-contiguous packed fp16 atomics: one wave instruction covers whole rows
+    {
+      constexpr int PAIRS = D / 2;
+      for (int idx = tid; idx < BWD_BQ * PAIRS; idx += BWD_THREADS) {
+        const int row = idx / PAIRS, pr = idx % PAIRS;
+        if (row < nq) {
+          const v2h hv = *reinterpret_cast<const v2h*>(sdQ + row * D + 2 * pr);
+          __builtin_amdgcn_global_atomic_fadd_v2f16(
+              reinterpret_cast<v2h*>(a.dq_acc + (size_t)(s_d + q0 + row) * rs + (size_t)head * D + 2 * pr), hv);
         }
       }
     }
