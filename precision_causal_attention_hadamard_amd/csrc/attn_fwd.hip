@@ -4,9 +4,10 @@
 // items taken longest first from the GPU-built list.  Wave w owns the 32
 // queries of document-local block 4t + w.  The kernel steps over 64-key tiles
 // from the document start to the diagonal.  Per step:
-//   * K~ codes are staged token-major in LDS and V~ codes d-major (transposed
-//     while staging, tokens of each 32-block in pi order), plus the per-key
-//     V codes on the two diagonal key tiles;
+//   * K~ and V~ codes (and, on the two diagonal key tiles, the per-key V
+//     codes) are staged token-major in LDS.  The next tile's global loads are
+//     issued into registers before the current tile is computed, and the LDS
+//     is double-buffered, so memory latency hides behind the matrix work;
 //   * S^T = K~ Q~^T on the scaled FP8 matrix cores: the token-block exponents
 //     are the operand scales, which realises the pages' factorisation
 //     S_ij = 2^(eQ(i) + eK(j)) x code dot product ([Reading, 4.1]);
@@ -22,8 +23,10 @@
 //     exponent of the block, which becomes that query's operand scale
 //     ([Summary], opening paragraphs: per-key V scales folded on diagonal
 //     tiles; [News, "Key design choices"]);
-//   * O^T += V~^T P^^T on the scaled FP8 matrix cores (P^^T is consumed
-//     straight from the S^T accumulator layout, no lane shuffles).
+//   * O^T += V~^T P^^T on the scaled FP8 matrix cores.  P^^T is consumed
+//     straight from the S^T accumulator layout; V~^T (d-major) is read from
+//     the token-major tile with the LDS transpose read, so the one E4M3
+//     payload serves both orientations ([Summary, §3.1 Token-Block Scaling]).
 // Epilogue: O = O_acc / l to bf16, integer row max and fp32 l stored.
 #include "flamia_device.hpp"
 #include "flamia_internal.hpp"
@@ -43,47 +46,36 @@ struct FwdArgs {
   float* row_sum;
 };
 
-// Stage 64 tokens x D codes transposed into dst[D][stride], token t of the
-// tile at column (t / 32) * 32 + pi_pos(t % 32).  Rows past `valid` are zero.
-template <int D>
-__device__ __forceinline__ void stage_transposed64(uint8_t* __restrict__ dst, int stride,
-                                                   const uint8_t* __restrict__ src, size_t row_stride,
-                                                   int valid, int tid) {
-  constexpr int DG = D / 8;
-  for (int t = tid; t < 16 * DG; t += FWD_THREADS) {
-    const int g4 = t / DG, dg = t % DG;
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 4 * g4 + r;
-      if (tok < valid) {
-        v2i w = *reinterpret_cast<const v2i*>(src + tok * row_stride + 8 * dg);
-        lo[r] = (uint32_t)w[0];
-        hi[r] = (uint32_t)w[1];
-      } else {
-        lo[r] = hi[r] = 0u;
-      }
-    }
-    uint32_t c[8];
-    transpose4x4_b8(lo[0], lo[1], lo[2], lo[3], c[0], c[1], c[2], c[3]);
-    transpose4x4_b8(hi[0], hi[1], hi[2], hi[3], c[4], c[5], c[6], c[7]);
-    const int pos = (g4 >> 3) * 32 + (g4 & 1) * 16 + ((g4 & 7) >> 1) * 4;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      *reinterpret_cast<uint32_t*>(dst + (8 * dg + k) * stride + pos) = c[k];
-  }
+// Transposed 8-byte LDS read: within each 16-lane group, lane p receives byte
+// (p % 8) of the 8-byte rows addressed by lanes 2b + p / 8, b = 0..7.
+__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
+}
+
+// 16 codes of one 32-token block for one column, in accumulator order
+// (token 8(rr/4) + 4hh + rr%4 at byte rr), read from a token-major tile with
+// two transpose reads.  `col0` is the first column of the lane's 16-lane
+// group; the lane covers column col0 + (lane & 15).
+__device__ __forceinline__ v4i tr_block16(const uint8_t* tile, int stride, int tok0, int col0, int lane) {
+  const int p = lane & 15, hh = lane >> 5;
+  const int b = p >> 1;                                       // which of the 8 tokens this lane addresses
+  const int t = tok0 + 8 * (b >> 2) + 4 * hh + (b & 3);
+  const uint8_t* a0 = tile + t * stride + col0 + 8 * (p & 1);
+  const v2i lo = lds_tr8(a0);
+  const v2i hi = lds_tr8(a0 + 16 * stride);                  // tokens + 16
+  return v4i{lo[0], lo[1], hi[0], hi[1]};
 }
 
 template <int D>
 __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
-  constexpr int KS = D + 16;      // token-major K row stride (bytes)
-  constexpr int VS = FWD_BK + 16; // d-major V row stride (bytes)
-  constexpr int NS = D / 64;      // K-steps of the S product
-  constexpr int ND = D / 32;      // d-blocks of the output
-  __shared__ __attribute__((aligned(16))) uint8_t sK[FWD_BK * KS];
-  __shared__ __attribute__((aligned(16))) uint8_t sVT[D * VS];
-  __shared__ __attribute__((aligned(16))) uint8_t sVkT[D * VS];
-  __shared__ uint8_t sKe[FWD_BK], sVe[FWD_BK], sVke[FWD_BK];
+  constexpr int KS = D + 16;          // token-major row stride (bytes)
+  constexpr int NS = D / 64;          // K-steps of the S product
+  constexpr int ND = D / 32;          // d-blocks of the output
+  constexpr int NCH = FWD_BK * D / 16 / FWD_THREADS;  // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][FWD_BK * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][FWD_BK * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sVk[2][FWD_BK * KS];
+  __shared__ uint8_t sKe[2][FWD_BK], sVe[2][FWD_BK], sVke[2][FWD_BK];
 
   const Problem& p = a.p;
   const int H = p.H, T = p.T;
@@ -97,12 +89,16 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hh = lane >> 5;
-  const int i = q0 + 32 * wave + n;          // this lane's query (document-local)
+  const int qw0 = q0 + 32 * wave;            // this wave's first query
+  const int i = qw0 + n;                     // this lane's query (document-local)
   const bool iv = i < L;
-  const bool wave_active = q0 + 32 * wave < L;
+  const bool wave_active = qw0 < L;
   const int QB = 4 * qt + wave;              // this wave's query block
   const size_t rs = (size_t)H * D;           // token stride of [T,H,d] codes
   const size_t hT = (size_t)head * T + s_d;  // base of [H,T] metadata of this doc/head
+  const uint8_t* kdoc = a.k_codes + (size_t)s_d * rs + (size_t)head * D;
+  const uint8_t* vdoc = a.v_codes + (size_t)s_d * rs + (size_t)head * D;
+  const uint8_t* vkdoc = a.v_key_codes + (size_t)s_d * rs + (size_t)head * D;
 
   // Q~ as the B operand of S^T = K~ Q~^T (lane = query column)
   v8i qa[NS];
@@ -121,39 +117,67 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
   v16f oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = v16f{};
-  float l_run = 0.f;
+  float l_run = 0.f;          // sum of P * 2^8
   int m_run = M_NONE;
   const float c = p.c_log2;
 
   const int kt_last = (min(q0 + FWD_BQ, L) - 1) / FWD_BK;
-  for (int kt = 0; kt <= kt_last; ++kt) {
+
+  // ---- register prefetch of one key tile
+  v4i pk[NCH], pv[NCH], pvk[NCH];
+  uint8_t pke = 0, pve = 0, pvke = 0;
+  auto prefetch = [&](int kt) {
     const int j0 = kt * FWD_BK;
     const int nvalid = min(FWD_BK, L - j0);
     const bool diag_tile = kt >= 2 * qt;
-    // ---- stage K (token-major), V (d-major), exponents
-    {
-      const uint8_t* kbase = a.k_codes + (size_t)(s_d + j0) * rs + (size_t)head * D;
-      for (int ch = tid; ch < FWD_BK * D / 16; ch += FWD_THREADS) {
-        const int r = ch / (D / 16), c16 = ch % (D / 16);
-        v4i w = r < nvalid ? ld16(kbase + r * rs + 16 * c16) : v4i{0, 0, 0, 0};
-        st16(sK + r * KS + 16 * c16, w);
-      }
-      stage_transposed64<D>(sVT, VS, a.v_codes + (size_t)(s_d + j0) * rs + (size_t)head * D, rs, nvalid, tid);
-      if (diag_tile)
-        stage_transposed64<D>(sVkT, VS, a.v_key_codes + (size_t)(s_d + j0) * rs + (size_t)head * D, rs,
-                              nvalid, tid);
-      if (tid < FWD_BK) {
-        const bool kv = tid < nvalid;
-        sKe[tid] = kv ? a.k_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
-        sVe[tid] = kv ? a.v_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
-        sVke[tid] = (kv && diag_tile) ? a.v_key_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
-      }
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+      const int ch = tid + FWD_THREADS * c2;
+      const int r = ch / (D / 16), c16 = ch % (D / 16);
+      const bool ok = r < nvalid;
+      const size_t off = (size_t)(j0 + r) * rs + 16 * c16;
+      pk[c2] = ok ? ld16(kdoc + off) : v4i{0, 0, 0, 0};
+      pv[c2] = ok ? ld16(vdoc + off) : v4i{0, 0, 0, 0};
+      pvk[c2] = (ok && diag_tile) ? ld16(vkdoc + off) : v4i{0, 0, 0, 0};
     }
-    __syncthreads();
+    if (tid < FWD_BK) {
+      const bool kv = tid < nvalid;
+      pke = kv ? a.k_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
+      pve = kv ? a.v_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
+      pvke = (kv && diag_tile) ? a.v_key_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+      const int ch = tid + FWD_THREADS * c2;
+      const int r = ch / (D / 16), c16 = ch % (D / 16);
+      st16(&sK[buf][r * KS + 16 * c16], pk[c2]);
+      st16(&sV[buf][r * KS + 16 * c16], pv[c2]);
+      st16(&sVk[buf][r * KS + 16 * c16], pvk[c2]);
+    }
+    if (tid < FWD_BK) {
+      sKe[buf][tid] = pke;
+      sVe[buf][tid] = pve;
+      sVke[buf][tid] = pvke;
+    }
+  };
+
+  prefetch(0);
+  commit(0);
+  __syncthreads();
+
+  for (int kt = 0; kt <= kt_last; ++kt) {
+    const int buf = kt & 1;
+    const int j0 = kt * FWD_BK;
+    if (kt < kt_last) prefetch(kt + 1);
 
     if (wave_active) {
+      const uint8_t* tK = sK[buf];
       bool act[2], dia[2];
       v16f st[2];
+      // interior tile: every key precedes every query of the wave and lies in the document
+      const bool interior = j0 + FWD_BK <= qw0 && j0 + FWD_BK <= L;
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -162,16 +186,21 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
         dia[kb] = KB == QB;
         st[kb] = v16f{};
         if (act[kb]) {
-          const uint8_t* krow = sK + (32 * kb + n) * KS;
-          const int ske = sKe[32 * kb + n];
+          const uint8_t* krow = tK + (32 * kb + n) * KS;
+          const int ske = sKe[buf][32 * kb + n];
 #pragma unroll
           for (int s = 0; s < NS; ++s)
             st[kb] = mfma_f8(cat8(ld16(krow + 64 * s + 16 * hh), ld16(krow + 64 * s + 32 + 16 * hh)), qa[s],
                              st[kb], ske, qe);
+          if (interior) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            if (j <= i && j < L) tmax = fmaxf(tmax, st[kb][rr]);
+            for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, st[kb][rr]);
+          } else {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+              if (j <= i && j < L) tmax = fmaxf(tmax, st[kb][rr]);
+            }
           }
         }
       }
@@ -188,49 +217,66 @@ __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
           l_run = __builtin_amdgcn_ldexpf(l_run, sh);
         }
         m_run = m_new;
+        const int kofs = 8 - m_run;       // P * 2^8 = exp2(r) * 2^(floor(S') + 8 - m~)
 
         int pc[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          if (interior && !dia[kb]) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float pv[4];
+            for (int g = 0; g < 4; ++g) {
+              float pv4[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int rr = 4 * g + r;
-              const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
-              const int j = j0 + 32 * kb + jj;
-              float pr = 0.f;
-              if (act[kb] && j <= i && j < L) {
-                const float x = st[kb][rr] * c;
+              for (int r = 0; r < 4; ++r) {
+                const float x = st[kb][4 * g + r] * c;
                 const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                pr = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) - m_run);
+                pv4[r] = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) + kofs);
+                l_run += pv4[r];
               }
-              l_run += pr;
-              const int sh = dia[kb] ? 8 + ((int)sVke[32 * kb + jj] - E8M0_BIAS) - vref : 8;
-              pv[r] = __builtin_amdgcn_ldexpf(pr, sh);
+              pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
             }
-            pc[kb][g] = cvt_fp8x4(pv[0], pv[1], pv[2], pv[3]);
+          } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float pv4[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
+                const int j = j0 + 32 * kb + jj;
+                float pr = 0.f;
+                if (act[kb] && j <= i && j < L) {
+                  const float x = st[kb][4 * g + r] * c;
+                  const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
+                  pr = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) + kofs);
+                }
+                l_run += pr;
+                pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
+              }
+              pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+            }
           }
         }
         const v8i pb = v8i{pc[0][0], pc[0][1], pc[0][2], pc[0][3], pc[1][0], pc[1][1], pc[1][2], pc[1][3]};
         // lane half hh supplies the scales of key block hh
         const int sb = dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP;
-        const int sa = dia[hh] ? E8M0_BIAS : (int)sVe[32 * hh];
-        const uint8_t* v0 = (dia[0] ? sVkT : sVT) + 16 * hh;
-        const uint8_t* v1 = (dia[1] ? sVkT : sVT) + 32 + 16 * hh;
+        const int sa = dia[hh] ? E8M0_BIAS : (int)sVe[buf][32 * hh];
+        const uint8_t* v0 = dia[0] ? sVk[buf] : sV[buf];
+        const uint8_t* v1 = dia[1] ? sVk[buf] : sV[buf];
+        const int colg = 16 * ((lane >> 4) & 1);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const int drow = (32 * db + n) * VS;
-          oacc[db] = mfma_f8(cat8(ld16(v0 + drow), ld16(v1 + drow)), pb, oacc[db], sa, sb);
+          const v4i va0 = tr_block16(v0, KS, 0, 32 * db + colg, lane);
+          const v4i va1 = tr_block16(v1, KS, 32, 32 * db + colg, lane);
+          oacc[db] = mfma_f8(cat8(va0, va1), pb, oacc[db], sa, sb);
         }
       }
     }
+    if (kt < kt_last) commit(buf ^ 1);
     __syncthreads();
   }
 
   if (wave_active) {
-    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float l = __builtin_amdgcn_ldexpf(l_run + __shfl_xor(l_run, 32, 64), P_EXP);
     if (iv) {
       const float inv = 1.0f / l;
       uint16_t* orow = a.o + (size_t)(s_d + i) * rs + (size_t)head * D;
