@@ -6,7 +6,10 @@
 // operands of S = Q~ K~^T and dP = dO~ V~^T, and accumulates dK and dV for
 // them.  The kernel walks the 64-query tiles from the diagonal to the end of
 // the document ([Summary, §3.3 Forward-Backward Numerical Consistency];
-// [Reading, 4.3]; [Reading, 4.4] third bullet):
+// [Reading, 4.3]; [Reading, 4.4] third bullet).  Query tiles (Q~ and dO~
+// codes, G = dO~ 2^-8 / l in bf16, per-row statistics) are staged token-major
+// and double-buffered; the next tile's global loads are in flight while the
+// current one is computed.  Per query tile:
 //   * S is recomputed from the same Q~/K~ codes with the same 32x32x64
 //     scaled FP8 products as the forward (the forward computes S^T with the
 //     operands swapped, which yields the same bits), then the same
@@ -14,19 +17,21 @@
 //     causal mask, the same diagonal decision (query and key in one
 //     document-local 32-token block) and the same per-key fold, so the
 //     probability codes are the forward's;
-//   * dV += P^_eff^T (dO~ 2^-8 / l) on bf16 matrix cores (P^ is exact in
-//     bf16; the per-query 1/l cannot be a per-32-block operand scale);
+//   * dV += P^_eff^T G on bf16 matrix cores (P^ is exact in bf16; the
+//     per-query 1/l cannot be a per-32-block operand scale); G is read
+//     d-major from its token-major tile with the 16-bit LDS transpose read;
 //   * dP = dO~ V~^T on scaled FP8 matrix cores, with the V representation the
 //     forward used for the pair (per-key codes on the diagonal block);
 //   * dS = (P / l)(dP - D) in fp32; one round-up exponent per 32 x 32 block
 //     of dS from the block max-abs (a whole-wave reduction: one C tile is one
 //     such block); dS^ in E4M3 ([Summary, §3.3] second bullet);
-//   * dK += dS^^T Q~ (scaled FP8, dS^ straight from the accumulator layout,
-//     Q~ read d-major from LDS);
-//   * dS^ goes to LDS; each wave then forms dQ^T for one slice of d over all
-//     128 keys (scaled FP8), multiplies by 2^-sigma (the data-dependent
-//     power-of-two prescale of the fp16 accumulator, [Reading, 4.4] third
-//     bullet) and adds it with packed fp16 atomics.
+//   * dK += dS^^T Q~ (scaled FP8; dS^ straight from the accumulator layout,
+//     Q~ d-major through the 8-bit LDS transpose read of the same payload);
+//   * dS^ goes to LDS key-major; each wave then forms dQ^T for one slice of d
+//     over all 128 keys (scaled FP8, dS^ read back transposed), multiplies by
+//     2^-sigma (the data-dependent power-of-two prescale of the fp16
+//     accumulator, [Reading, 4.4] third bullet), stages the fp16 tile in LDS
+//     and adds it with row-contiguous packed fp16 atomics.
 // Item end: dK (times the softmax scale) goes to an fp32 staging buffer (the
 // finaliser rotates it back when the Hadamard option is on); dV to bf16.
 #include "flamia_device.hpp"
@@ -54,93 +59,29 @@ struct BwdArgs {
   uint16_t* dv;
 };
 
-// ntok tokens x D codes transposed into dst[D][stride]; token t at column
-// (t / 32) * 32 + pi_pos(t % 32); tokens past `valid` are zero.
-template <int D, int NTOK>
-__device__ __forceinline__ void stage_t8(uint8_t* __restrict__ dst, int stride, const uint8_t* __restrict__ src,
-                                         size_t row_stride, int valid, int tid) {
-  constexpr int DG = D / 8;
-  for (int t = tid; t < (NTOK / 4) * DG; t += BWD_THREADS) {
-    const int g4 = t / DG, dg = t % DG;
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 4 * g4 + r;
-      if (tok < valid) {
-        v2i w = *reinterpret_cast<const v2i*>(src + tok * row_stride + 8 * dg);
-        lo[r] = (uint32_t)w[0];
-        hi[r] = (uint32_t)w[1];
-      } else {
-        lo[r] = hi[r] = 0u;
-      }
-    }
-    uint32_t c[8];
-    transpose4x4_b8(lo[0], lo[1], lo[2], lo[3], c[0], c[1], c[2], c[3]);
-    transpose4x4_b8(hi[0], hi[1], hi[2], hi[3], c[4], c[5], c[6], c[7]);
-    const int pos = (g4 >> 3) * 32 + (g4 & 1) * 16 + ((g4 & 7) >> 1) * 4;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) *reinterpret_cast<uint32_t*>(dst + (8 * dg + k) * stride + pos) = c[k];
-  }
-}
-
-// 64 tokens x D bf16 transposed into dst[D][stride bytes] in the same order.
-template <int D>
-__device__ __forceinline__ void stage_t16(uint8_t* __restrict__ dst, int stride, const uint16_t* __restrict__ src,
-                                          size_t row_stride, int valid, int tid) {
-  constexpr int DG = D / 4;
-  for (int t = tid; t < 16 * DG; t += BWD_THREADS) {
-    const int g4 = t / DG, dg = t % DG;
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 4 * g4 + r;
-      if (tok < valid) {
-        v2i w = *reinterpret_cast<const v2i*>(src + tok * row_stride + 4 * dg);
-        lo[r] = (uint32_t)w[0];   // d0 | d1 << 16
-        hi[r] = (uint32_t)w[1];   // d2 | d3 << 16
-      } else {
-        lo[r] = hi[r] = 0u;
-      }
-    }
-    const int pos = (g4 >> 3) * 32 + (g4 & 1) * 16 + ((g4 & 7) >> 1) * 4;
-    uint32_t col[4][2];
-    col[0][0] = __builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u);
-    col[0][1] = __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u);
-    col[1][0] = __builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u);
-    col[1][1] = __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u);
-    col[2][0] = __builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u);
-    col[2][1] = __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u);
-    col[3][0] = __builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u);
-    col[3][1] = __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<v2i*>(dst + (4 * dg + k) * stride + 2 * pos) = v2i{(int)col[k][0], (int)col[k][1]};
-  }
-}
-
 template <int D>
 __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
-  constexpr int KS = D + 16;                 // token-major code row stride
-  constexpr int QTS = BWD_BQ + 16;           // d-major Q~ stride (bytes)
-  constexpr int GTS = 2 * BWD_BQ + 16;       // d-major G stride (bytes)
-  constexpr int KTS = BWD_BK + 16;           // d-major K~ stride (bytes)
-  constexpr int DSS = BWD_BK + 16;           // query-major dS^ stride (bytes)
+  constexpr int KS = D + 16;                 // token-major code row stride (bytes)
+  constexpr int GS = 2 * D + 16;             // token-major bf16 row stride (bytes)
+  constexpr int DSK = BWD_BQ + 16;           // key-major dS^ row stride (bytes)
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[BWD_BQ * KS];
-  __shared__ __attribute__((aligned(16))) uint8_t sdO[BWD_BQ * KS];
-  __shared__ __attribute__((aligned(16))) uint8_t sQT[D * QTS];
-  __shared__ __attribute__((aligned(16))) uint8_t sGT[D * GTS];
-  __shared__ __attribute__((aligned(16))) uint8_t sKT[D * KTS];
-  __shared__ __attribute__((aligned(16))) uint8_t sdS[BWD_BQ * DSS];
-  __shared__ __attribute__((aligned(16))) int sM[BWD_BQ];
-  __shared__ __attribute__((aligned(16))) float sIL[BWD_BQ];
-  __shared__ __attribute__((aligned(16))) float sDl[BWD_BQ];
-  __shared__ int sSig[BWD_BQ];
-  __shared__ int sVref[BWD_BQ];
-  __shared__ int sQeB[2], sDOeB[2], sKeB[4];
+  constexpr int NCQ = BWD_BQ * D / 16 / BWD_THREADS;       // 16-byte code chunks per thread
+  constexpr int NCG = BWD_BQ * 2 * D / 16 / BWD_THREADS;   // 16-byte G chunks per thread
+  constexpr int NCK = BWD_BK * D / 16 / BWD_THREADS;       // K tile chunks per thread
+  __shared__ __attribute__((aligned(16))) uint8_t sK[BWD_BK * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BWD_BQ * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sdO[2][BWD_BQ * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sG[2][BWD_BQ * GS];
+  __shared__ __attribute__((aligned(16))) uint8_t sdSK[BWD_BK * DSK];
+  __shared__ __attribute__((aligned(16))) uint16_t sdQ[BWD_BQ * D];
+  __shared__ __attribute__((aligned(16))) int sM[2][BWD_BQ];
+  __shared__ __attribute__((aligned(16))) float sIL[2][BWD_BQ];
+  __shared__ __attribute__((aligned(16))) float sDl[2][BWD_BQ];
+  __shared__ int sSig[2][BWD_BQ];
+  __shared__ int sVref[2][BWD_BQ];
+  __shared__ int sQeB[2][2], sDOeB[2][2], sKeB[4];
   __shared__ int sEds[2][4];
-  __shared__ __attribute__((aligned(16))) uint16_t sdQ[BWD_BQ * D];   // fp16 dQ tile partial
 
   const Problem& p = a.p;
   const int H = p.H, T = p.T;
@@ -154,23 +95,33 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, hh = lane >> 5;
+  const int colg = 16 * ((lane >> 4) & 1);      // first column of this lane's 16-lane group
   const int j = k0 + 32 * wave + n;             // this lane's key (document-local)
   const bool kv = j < L;
   const bool wave_active = k0 + 32 * wave < L;
   const int KB = 4 * u + wave;
   const size_t rs = (size_t)H * D;
   const size_t hT = (size_t)head * T + s_d;
+  const size_t doc0 = (size_t)s_d * rs + (size_t)head * D;   // row 0 of this doc/head
   const float c = p.c_log2;
 
-  // ---- per-item: K~ transposed for dQ, key-block exponents
-  stage_t8<D, BWD_BK>(sKT, KTS, a.k_codes + (size_t)(s_d + k0) * rs + (size_t)head * D, rs, L - k0, tid);
-  if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
+  // ---- per item: the key tile, token-major, for K~^T of dQ
+  {
+    const int nk = L - k0;
+#pragma unroll
+    for (int c2 = 0; c2 < NCK; ++c2) {
+      const int ch = tid + BWD_THREADS * c2;
+      const int r = ch / (D / 16), c16 = ch % (D / 16);
+      st16(sK + r * KS + 16 * c16, r < nk ? ld16(a.k_codes + doc0 + (size_t)(k0 + r) * rs + 16 * c16) : v4i{0, 0, 0, 0});
+    }
+    if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
+  }
 
-  // ---- per-wave registers: K~, V~ (block and per-key) as B operands
+  // ---- per wave: K~, V~ (block and per-key) as B operands (lane = key)
   v8i kreg[NS], vreg[NS], vkreg[NS];
   int ke = E8M0_BIAS, ve = E8M0_BIAS, vke = E8M0_BIAS;
   if (kv) {
-    const size_t ro = (size_t)(s_d + j) * rs + (size_t)head * D;
+    const size_t ro = doc0 + (size_t)j * rs;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       kreg[s] = cat8(ld16(a.k_codes + ro + 64 * s + 16 * hh), ld16(a.k_codes + ro + 64 * s + 32 + 16 * hh));
@@ -185,57 +136,102 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     for (int s = 0; s < NS; ++s) kreg[s] = vreg[s] = vkreg[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   }
   const int e_key = vke - E8M0_BIAS;
+
+  // ---- register prefetch of one query tile
+  v4i pq[NCQ], pdo[NCQ], pg[NCG];
+  // per-row statistics for threads < BWD_BQ; threads BWD_BQ and BWD_BQ + 1
+  // carry the two query blocks' Q and dO exponents in pm / psig
+  int pm = 0, psig = 0, pvref = 0;
+  float pil = 0.f, pdl = 0.f;
+  auto prefetch = [&](int qt) {
+    const int q0 = qt * BWD_BQ;
+    const int nq = min(BWD_BQ, L - q0);
+    const size_t to = doc0 + (size_t)q0 * rs;
+#pragma unroll
+    for (int c2 = 0; c2 < NCQ; ++c2) {
+      const int ch = tid + BWD_THREADS * c2;
+      const int r = ch / (D / 16), c16 = ch % (D / 16);
+      const bool ok = r < nq;
+      pq[c2] = ok ? ld16(a.q_codes + to + r * rs + 16 * c16) : v4i{0, 0, 0, 0};
+      pdo[c2] = ok ? ld16(a.do_codes + to + r * rs + 16 * c16) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < NCG; ++c2) {
+      const int ch = tid + BWD_THREADS * c2;
+      const int r = ch / (D / 8), c8 = ch % (D / 8);
+      pg[c2] = r < nq ? ld16(a.g + to + r * rs + 8 * c8) : v4i{0, 0, 0, 0};
+    }
+    if (tid < BWD_BQ) {
+      const bool ok = tid < nq;
+      const size_t mi = hT + q0 + tid;
+      pm = ok ? a.row_max[mi] : 0;
+      pil = ok ? 1.0f / a.row_sum[mi] : 0.f;
+      pdl = ok ? a.delta[mi] : 0.f;
+      psig = ok ? a.dq_sigma[mi] : 0;
+      pvref = ok ? (int)a.v_ref_exp[mi] - E8M0_BIAS : 0;
+    } else if (tid < BWD_BQ + 2) {
+      const int b = tid - BWD_BQ;
+      const bool ok = 32 * b < nq;
+      pm = ok ? (int)a.q_exp[hT + q0 + 32 * b] : E8M0_BIAS;
+      psig = ok ? (int)a.do_exp[hT + q0 + 32 * b] : E8M0_BIAS;
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int c2 = 0; c2 < NCQ; ++c2) {
+      const int ch = tid + BWD_THREADS * c2;
+      const int r = ch / (D / 16), c16 = ch % (D / 16);
+      st16(&sQ[buf][r * KS + 16 * c16], pq[c2]);
+      st16(&sdO[buf][r * KS + 16 * c16], pdo[c2]);
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < NCG; ++c2) {
+      const int ch = tid + BWD_THREADS * c2;
+      const int r = ch / (D / 8), c8 = ch % (D / 8);
+      st16(&sG[buf][r * GS + 16 * c8], pg[c2]);
+    }
+    if (tid < BWD_BQ) {
+      sM[buf][tid] = pm;
+      sIL[buf][tid] = pil;
+      sDl[buf][tid] = pdl;
+      sSig[buf][tid] = psig;
+      sVref[buf][tid] = pvref;
+    } else if (tid < BWD_BQ + 2) {
+      sQeB[buf][tid - BWD_BQ] = pm;
+      sDOeB[buf][tid - BWD_BQ] = psig;
+    }
+  };
+
+  const int qt_first = k0 / BWD_BQ;
+  const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
+  prefetch(qt_first);
+  commit(0);
   __syncthreads();
 
-  // K~^T slice for dQ^T: wave -> d-slice ds; lane (d row n, half hh)
+  // K~^T slice for dQ^T: wave -> d-slice ds; lane (d row, half hh), K = keys
   const int ds = wave % ND;
   v8i ktreg[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint8_t* kr = sKT + (32 * ds + n) * KTS + 64 * ks;
-    ktreg[ks] = cat8(ld16(kr + 16 * hh), ld16(kr + 32 + 16 * hh));
-  }
+  for (int ks = 0; ks < 2; ++ks)
+    ktreg[ks] = cat8(tr_block16(sK, KS, 64 * ks, 32 * ds + colg, lane),
+                     tr_block16(sK, KS, 64 * ks + 32, 32 * ds + colg, lane));
 
   v16f dk[ND], dv[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) { dk[db] = v16f{}; dv[db] = v16f{}; }
 
-  const int qt_first = k0 / BWD_BQ;
-  const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
   for (int qt = qt_first; qt < qt_end; ++qt) {
+    const int buf = (qt - qt_first) & 1;
     const int q0 = qt * BWD_BQ;
     const int nq = min(BWD_BQ, L - q0);
-    // ---- stage the query tile
-    {
-      const size_t to = (size_t)(s_d + q0) * rs + (size_t)head * D;
-      for (int ch = tid; ch < BWD_BQ * D / 16; ch += BWD_THREADS) {
-        const int r = ch / (D / 16), c16 = ch % (D / 16);
-        const bool ok = r < nq;
-        st16(sQ + r * KS + 16 * c16, ok ? ld16(a.q_codes + to + r * rs + 16 * c16) : v4i{0, 0, 0, 0});
-        st16(sdO + r * KS + 16 * c16, ok ? ld16(a.do_codes + to + r * rs + 16 * c16) : v4i{0, 0, 0, 0});
-      }
-      stage_t8<D, BWD_BQ>(sQT, QTS, a.q_codes + to, rs, nq, tid);
-      stage_t16<D>(sGT, GTS, a.g + to, rs, nq, tid);
-      if (tid < BWD_BQ) {
-        const bool ok = tid < nq;
-        const size_t mi = hT + q0 + tid;
-        sM[tid] = ok ? a.row_max[mi] : 0;
-        sIL[tid] = ok ? 1.0f / a.row_sum[mi] : 0.f;
-        sDl[tid] = ok ? a.delta[mi] : 0.f;
-        sSig[tid] = ok ? a.dq_sigma[mi] : 0;
-        sVref[tid] = ok ? (int)a.v_ref_exp[mi] - E8M0_BIAS : 0;
-      }
-      if (tid < 2) {
-        const bool ok = 32 * tid < nq;
-        sQeB[tid] = ok ? (int)a.q_exp[hT + q0 + 32 * tid] : E8M0_BIAS;
-        sDOeB[tid] = ok ? (int)a.do_exp[hT + q0 + 32 * tid] : E8M0_BIAS;
-      }
-    }
-    __syncthreads();
+    const bool has_next = qt + 1 < qt_end;
+    if (has_next) prefetch(qt + 1);
+    const uint8_t* tQ = sQ[buf];
+    const uint8_t* tdO = sdO[buf];
+    const uint8_t* tG = sG[buf];
 
     int dsc[2][4];
     int eds[2];
-    uint32_t pe[2][8];    // bf16 pairs of P^_eff * 2^8, C-tile register order
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int QB = 2 * qt + qb;
@@ -243,41 +239,40 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       eds[qb] = -127;
 #pragma unroll
       for (int g = 0; g < 4; ++g) dsc[qb][g] = 0;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) pe[qb][g] = 0u;
       if (act) {
         const bool dia = QB == KB;
         v16f sacc = v16f{}, pacc = v16f{};
-        const int sqe = sQeB[qb], sdoe = sDOeB[qb];
+        const int sqe = sQeB[buf][qb], sdoe = sDOeB[buf][qb];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const uint8_t* qr = sQ + (32 * qb + n) * KS + 64 * s;
-          const uint8_t* dr = sdO + (32 * qb + n) * KS + 64 * s;
+          const uint8_t* qr = tQ + (32 * qb + n) * KS + 64 * s;
+          const uint8_t* dr = tdO + (32 * qb + n) * KS + 64 * s;
           sacc = mfma_f8(cat8(ld16(qr + 16 * hh), ld16(qr + 32 + 16 * hh)), kreg[s], sacc, sqe, ke);
           pacc = mfma_f8(cat8(ld16(dr + 16 * hh), ld16(dr + 32 + 16 * hh)), dia ? vkreg[s] : vreg[s], pacc,
                          sdoe, dia ? vke : ve);
         }
         float dsv[16];
+        uint32_t pe[8];    // bf16 pairs of P^_eff * 2^8, accumulator register order
         float amax = 0.f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = 32 * qb + 8 * g + 4 * hh;      // first of 4 consecutive query rows
-          const v4i mv = *reinterpret_cast<const v4i*>(sM + r0);
-          const v4f ilv = *reinterpret_cast<const v4f*>(sIL + r0);
-          const v4f dlv = *reinterpret_cast<const v4f*>(sDl + r0);
+          const v4i mv = *reinterpret_cast<const v4i*>(&sM[buf][r0]);
+          const v4f ilv = *reinterpret_cast<const v4f*>(&sIL[buf][r0]);
+          const v4f dlv = *reinterpret_cast<const v4f*>(&sDl[buf][r0]);
           float pf[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int rr = 4 * g + r;
             const int i = q0 + r0 + r;
-            float pr = 0.f, dsr = 0.f, pev = 0.f;
+            float dsr = 0.f, pev = 0.f;
             if (kv && j <= i && i < L) {
               const float x = sacc[rr] * c;
               const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-              pr = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) - mv[r]);
+              const float pr = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) - mv[r]);
               dsr = (pr * ilv[r]) * (pacc[rr] - dlv[r]);
               if (dia) {
-                const int vref = sVref[r0 + r];
+                const int vref = sVref[buf][r0 + r];
                 const int code = cvt_fp8x2(__builtin_amdgcn_ldexpf(pr, 8 + e_key - vref), 0.f);
                 pev = __builtin_amdgcn_ldexpf(fp8_value(code, 0), vref - e_key);
               } else {
@@ -289,8 +284,8 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
             amax = fmaxf(amax, fabsf(dsr));
             pf[r] = pev;
           }
-          pe[qb][2 * g] = (uint32_t)f32_to_bf16_bits(pf[0]) | ((uint32_t)f32_to_bf16_bits(pf[1]) << 16);
-          pe[qb][2 * g + 1] = (uint32_t)f32_to_bf16_bits(pf[2]) | ((uint32_t)f32_to_bf16_bits(pf[3]) << 16);
+          pe[2 * g] = (uint32_t)f32_to_bf16_bits(pf[0]) | ((uint32_t)f32_to_bf16_bits(pf[1]) << 16);
+          pe[2 * g + 1] = (uint32_t)f32_to_bf16_bits(pf[2]) | ((uint32_t)f32_to_bf16_bits(pf[3]) << 16);
         }
         const int e = roundup_exp(wave_max(amax));
         eds[qb] = e;
@@ -301,16 +296,11 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
         // dV += P^_eff^T G  (two K-steps of 16 queries)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          v8bf av;
-          {
-            uint32_t w4[4] = {pe[qb][4 * ks], pe[qb][4 * ks + 1], pe[qb][4 * ks + 2], pe[qb][4 * ks + 3]};
-            av = *reinterpret_cast<const v8bf*>(w4);
-          }
+          const v8bf av = __builtin_bit_cast(
+              v8bf, v4i{(int)pe[4 * ks], (int)pe[4 * ks + 1], (int)pe[4 * ks + 2], (int)pe[4 * ks + 3]});
 #pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const v4i bw = ld16(sGT + (32 * db + n) * GTS + 2 * (32 * qb + 16 * hh + 8 * ks));
-            dv[db] = mfma_bf16(av, *reinterpret_cast<const v8bf*>(&bw), dv[db]);
-          }
+          for (int db = 0; db < ND; ++db)
+            dv[db] = mfma_bf16(av, tr_bf16x8(tG, GS, 32 * qb, ks, 32 * db + colg, lane), dv[db]);
         }
       }
     }
@@ -318,23 +308,19 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     if (wave_active) {
       const v8i adk = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
       const int sa = (hh == 0 ? eds[0] : eds[1]) + E8M0_BIAS;
-      const int sb = sQeB[hh];
+      const int sb = sQeB[buf][hh];
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const uint8_t* qr = sQT + (32 * db + n) * QTS;
-        dk[db] = mfma_f8(adk, cat8(ld16(qr + 16 * hh), ld16(qr + 32 + 16 * hh)), dk[db], sa, sb);
-      }
+      for (int db = 0; db < ND; ++db)
+        dk[db] = mfma_f8(adk, cat8(tr_block16(tQ, KS, 0, 32 * db + colg, lane), tr_block16(tQ, KS, 32, 32 * db + colg, lane)),
+                         dk[db], sa, sb);
     }
-    // dS^ to LDS, query-major, keys of this wave at columns 32w + pi(n)
+    // dS^ to LDS key-major: row = key of the tile, 4 consecutive queries per dword
     {
-      const int col = 32 * wave + pi_pos(n);
+      uint8_t* row = sdSK + (32 * wave + n) * DSK + 4 * hh;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sdS[(32 * qb + 8 * g + 4 * hh + r) * DSS + col] = (uint8_t)(((uint32_t)dsc[qb][g] >> (8 * r)) & 0xffu);
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<int*>(row + 32 * qb + 8 * g) = dsc[qb][g];
       if (lane == 0) { sEds[0][wave] = eds[0]; sEds[1][wave] = eds[1]; }
     }
     __syncthreads();
@@ -344,13 +330,13 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       v16f acc = v16f{};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint8_t* dr = sdS + (32 * qb + n) * DSS + 64 * ks;
-        acc = mfma_f8(ktreg[ks], cat8(ld16(dr + 16 * hh), ld16(dr + 32 + 16 * hh)), acc,
-                      sKeB[2 * ks + hh], sEds[qb][2 * ks + hh] + E8M0_BIAS);
+        const v8i bq = cat8(tr_block16(sdSK, DSK, 64 * ks, 32 * qb + colg, lane),
+                            tr_block16(sdSK, DSK, 64 * ks + 32, 32 * qb + colg, lane));
+        acc = mfma_f8(ktreg[ks], bq, acc, sKeB[2 * ks + hh], sEds[qb][2 * ks + hh] + E8M0_BIAS);
       }
       // prescaled fp16 partial of this query row into LDS (4 consecutive d per store)
-      const int iq = 32 * qb + n;               // query row within the tile
-      const int sig = sSig[iq];
+      const int iq = 32 * qb + n;
+      const int sig = sSig[buf][iq];
       uint16_t* dst = sdQ + iq * D + 32 * ds + 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -359,7 +345,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
         h0[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 1], -sig);
         h1[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 2], -sig);
         h1[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 3], -sig);
-        *reinterpret_cast<v2i*>(dst + 8 * g) = v2i{*reinterpret_cast<int*>(&h0), *reinterpret_cast<int*>(&h1)};
+        *reinterpret_cast<v2i*>(dst + 8 * g) = v2i{__builtin_bit_cast(int, h0), __builtin_bit_cast(int, h1)};
       }
     }
     __syncthreads();
@@ -371,10 +357,11 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
         if (row < nq) {
           const v2h hv = *reinterpret_cast<const v2h*>(sdQ + row * D + 2 * pr);
           __builtin_amdgcn_global_atomic_fadd_v2f16(
-              reinterpret_cast<v2h*>(a.dq_acc + (size_t)(s_d + q0 + row) * rs + (size_t)head * D + 2 * pr), hv);
+              reinterpret_cast<v2h*>(a.dq_acc + doc0 + (size_t)(q0 + row) * rs + 2 * pr), hv);
         }
       }
     }
+    if (has_next) commit(buf ^ 1);
     __syncthreads();
   }
 
@@ -387,7 +374,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       for (int rr = 0; rr < 16; ++rr) {
         const int jk = k0 + 32 * wave + 8 * (rr >> 2) + 4 * hh + (rr & 3);
         if (jk < L) {
-          const size_t o = (size_t)(s_d + jk) * rs + (size_t)head * D + 32 * db + n;
+          const size_t o = doc0 + (size_t)jk * rs + 32 * db + n;
           a.dk_f32[o] = dk[db][rr] * sc;
           a.dv[o] = f32_to_bf16_bits(dv[db][rr]);
         }

@@ -46,26 +46,6 @@ struct FwdArgs {
   float* row_sum;
 };
 
-// Transposed 8-byte LDS read: within each 16-lane group, lane p receives byte
-// (p % 8) of the 8-byte rows addressed by lanes 2b + p / 8, b = 0..7.
-__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
-}
-
-// 16 codes of one 32-token block for one column, in accumulator order
-// (token 8(rr/4) + 4hh + rr%4 at byte rr), read from a token-major tile with
-// two transpose reads.  `col0` is the first column of the lane's 16-lane
-// group; the lane covers column col0 + (lane & 15).
-__device__ __forceinline__ v4i tr_block16(const uint8_t* tile, int stride, int tok0, int col0, int lane) {
-  const int p = lane & 15, hh = lane >> 5;
-  const int b = p >> 1;                                       // which of the 8 tokens this lane addresses
-  const int t = tok0 + 8 * (b >> 2) + 4 * hh + (b & 3);
-  const uint8_t* a0 = tile + t * stride + col0 + 8 * (p & 1);
-  const v2i lo = lds_tr8(a0);
-  const v2i hi = lds_tr8(a0 + 16 * stride);                  // tokens + 16
-  return v4i{lo[0], lo[1], hi[0], hi[1]};
-}
-
 template <int D>
 __global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D + 16;          // token-major row stride (bytes)

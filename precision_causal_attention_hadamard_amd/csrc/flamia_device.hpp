@@ -145,4 +145,50 @@ __device__ __forceinline__ void transpose4x4_b8(uint32_t r0, uint32_t r1, uint32
   c3 = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
 }
 
+// ---------------------------------------------------------------- LDS transpose reads
+//
+// gfx950 ds_read_b64_tr_b8 / _tr_b16, as measured on the hardware: within each
+// 16-lane group, lane p receives, for b8, byte (p % 8) of the 8-byte rows
+// addressed by lanes 2b + p / 8 (b = 0..7); for b16, element (p % 4) of the
+// 8-byte rows addressed by lanes 4e + p / 4 (e = 0..3).  Letting the lanes of
+// a group address 8 (or 4) token rows of a token-major tile turns a
+// token-major tile into the MN-major operand of a matrix-core product.
+
+__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
+}
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4s lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+}
+
+// 16 one-byte codes of one 32-token block for one column, in accumulator
+// order (token 8(rr/4) + 4hh + rr%4 at byte rr), from a token-major byte tile
+// (row = token, `stride` bytes).  `col0` is the first column of the lane's
+// 16-lane group; the lane receives column col0 + (lane & 15).
+__device__ __forceinline__ v4i tr_block16(const uint8_t* tile, int stride, int tok0, int col0, int lane) {
+  const int p = lane & 15, hh = lane >> 5;
+  const int b = p >> 1;
+  const int t = tok0 + 8 * (b >> 2) + 4 * hh + (b & 3);
+  const uint8_t* a0 = tile + t * stride + col0 + 8 * (p & 1);
+  const v2i lo = lds_tr8(a0);
+  const v2i hi = lds_tr8(a0 + 16 * stride);
+  return v4i{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// 8 bf16 of one column for the 16-token K-step `ks` of a 32-token block
+// (tokens 8(2ks + e/4) + 4hh + e%4 at element e), from a token-major bf16
+// tile (row = token, `stride` bytes); `col0` as above (in elements).
+__device__ __forceinline__ v8bf tr_bf16x8(const uint8_t* tile, int stride, int tok0, int ks, int col0, int lane) {
+  const int p = lane & 15, hh = lane >> 5;
+  const int e = p >> 2, s = p & 3;
+  const int t = tok0 + 16 * ks + 4 * hh + e;
+  const uint8_t* a0 = tile + t * stride + 2 * (col0 + 4 * s);
+  const v4s lo = lds_tr16(a0);
+  const v4s hi = lds_tr16(a0 + 8 * stride);
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(v8bf, both);
+}
+
 }  // namespace flamia
