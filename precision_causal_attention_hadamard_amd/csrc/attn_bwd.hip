@@ -62,7 +62,8 @@ struct BwdArgs {
 template <int D>
 __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   constexpr int KS = D + 16;                 // token-major code row stride (bytes)
-  constexpr int GS = 2 * D + 16;             // token-major bf16 row stride (bytes)
+  constexpr int GS = 2 * D + 64;             // token-major bf16 row stride (bytes); = 64 mod 256 so the
+                                             // four rows of a 16-bit transpose read hit distinct banks
   constexpr int DSK = BWD_BQ + 16;           // key-major dS^ row stride (bytes)
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;

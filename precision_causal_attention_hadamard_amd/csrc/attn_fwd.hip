@@ -47,7 +47,8 @@ struct FwdArgs {
 };
 
 template <int D>
-__global__ void __launch_bounds__(FWD_THREADS) attn_fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D + 16;          // token-major row stride (bytes)
   constexpr int NS = D / 64;          // K-steps of the S product
   constexpr int ND = D / 32;          // d-blocks of the output
