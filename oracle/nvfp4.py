@@ -10,10 +10,12 @@ tokens ([Summary, §3.2 Causally Safe Scales]).
 Readings (the pages print no NVFP4 formula, so parity of this reading is
 UNPINNED beyond the E2M1 table and the exactness checks in the tests):
 
-* tensor scale ``t = fp32(amax_tensor / 2688)`` over the whole (rotated)
-  tensor, with 2688 = 6 * 448; ``t = 1`` when the tensor is all zero;
-* group scale ``s`` = the smallest E4M3 value ``>= fp32(amax_g / fp32(6 t))``,
-  capped at 448 -- the round-up rule applied to a non-power-of-two scale;
+* tensor scale ``t = amax_tensor / 2688`` (one IEEE fp32 division) over the
+  whole (rotated) tensor, with 2688 = 6 * 448; ``t = 1`` when the tensor is
+  all zero;
+* group scale ``s`` = the smallest E4M3 value ``>= amax_g / fp32(6 t)`` (one
+  IEEE fp32 division), capped at 448 -- the round-up rule applied to a
+  non-power-of-two scale;
 * code ``= E2M1_RNE(fp32(x / fp32(s t)))`` saturating at +-6; all codes are
   0 when ``s = 0``;
 * ``S_ij = t_Q t_K sum_g s_Q s_K sum_{k in g} q k``, exact in fp64, rounded
@@ -47,14 +49,15 @@ def quantize_nvfp4(x):
     fp64 [T,H,d])."""
     x = np.asarray(x, dtype=np.float32)
     T, H, d = x.shape
-    amax = float(np.max(np.abs(x))) if x.size else 0.0
-    t = np.float32(amax / 2688.0) if amax > 0 else np.float32(1.0)
-    six_t = np.float32(6.0 * np.float64(t))
+    amax = np.max(np.abs(x)) if x.size else np.float32(0.0)
+    t = (np.float32(amax) / np.float32(2688.0)).astype(np.float32) if amax > 0 else np.float32(1.0)
+    six_t = np.float32(6.0 * np.float64(t))        # exact product, rounded once
     g = x.reshape(T, H, d // GROUP, GROUP)
-    gmax = np.max(np.abs(g), axis=-1)
+    gmax = np.max(np.abs(g), axis=-1).astype(np.float32)
+    need = (gmax / six_t).astype(np.float32)       # IEEE fp32 division
     scales = np.zeros(gmax.shape)
     for idx in np.ndindex(gmax.shape):
-        scales[idx] = e4m3_round_up(float(np.float32(np.float64(gmax[idx]) / np.float64(six_t))))
+        scales[idx] = e4m3_round_up(float(need[idx]))
     st = (scales.astype(np.float32) * t).astype(np.float32)      # fp32(s * t)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(st[..., None] > 0,

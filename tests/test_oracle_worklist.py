@@ -47,7 +47,7 @@ def test_nvfp4_round_up_scale_and_exact_dequant():
     wl = W.small_packed(12, [40], heads=2, head_dim=64)
     x = wl.q.float().numpy()
     codes, scales, t, deq = nvfp4.quantize_nvfp4(x)
-    assert t == np.float32(np.max(np.abs(x)) / 2688.0)
+    assert t == np.float32(np.max(np.abs(x))) / np.float32(2688.0)
     g = x.reshape(40, 2, 4, 16)
     gmax = np.abs(g).max(-1)
     # the scale is an E4M3 value, never below what the group needs, and the
