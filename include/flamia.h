@@ -65,7 +65,7 @@ typedef struct flamia_attn_desc {
   int32_t num_heads;            /* H >= 1 */
   int32_t head_dim;             /* d: 64 or 128 */
   int32_t causal;               /* must be 1 */
-  int32_t path;                 /* 0 = MXFP8 (the only path this build runs) */
+  int32_t path;                 /* 0 = MXFP8; 1 = mixed: QK^T (and its recompute) from NVFP4 Q/K */
   int32_t hadamard;             /* 1: rotate Q and K rows by the normalised Sylvester Hadamard matrix */
   int32_t causal_dq_scale;      /* 1: dQ accumulator prescale from causally visible blocks only */
   int32_t deterministic;        /* must be 0 (dQ is reduced with fp16 atomics) */
@@ -91,6 +91,14 @@ typedef struct flamia_attn_desc {
  *                     its own block it may see (the fold reference of the
  *                     diagonal P^V product).
  *  plan               opaque GPU-built longest-first work lists.
+ *  Mixed path only (NULL when path = 0), [Summary] opening paragraphs and
+ *  [Reading, 4.1]: NVFP4 score operands of Q and K (after the rotation):
+ *  q_fp4, k_fp4       [T,H,d/2] E2M1 codes, two per byte (even element in
+ *                     the low nibble, bit 3 of a nibble = sign).
+ *  q_sf, k_sf         [T,H,d/16] E4M3 scale per 16 head-dim elements of a
+ *                     token: the smallest E4M3 value >= amax_group / fp32(6 t).
+ *  qk_tensor_scale    float[4]: [0], [1] = bits of the Q and K tensor amax
+ *                     (working space), [2], [3] = t_Q, t_K = amax / 2688.
  */
 typedef struct flamia_qtensors {
   uint8_t* q_codes;
@@ -103,6 +111,11 @@ typedef struct flamia_qtensors {
   uint8_t* v_key_exp;
   uint8_t* v_ref_exp;
   void* plan;
+  uint8_t* q_fp4;
+  uint8_t* k_fp4;
+  uint8_t* q_sf;
+  uint8_t* k_sf;
+  float* qk_tensor_scale;
 } flamia_qtensors;
 
 /*
@@ -136,7 +149,10 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base,
  * integer with amax <= 448 * 2^e (rounded up so nothing clamps,
  * [Summary, §3.2 Causally Safe Scales]); codes = RNE_E4M3(x * 2^-e).
  * V also gets per-key exponents/codes and the per-query fold reference.
- * Two kernel launches: the work-list builder and the quantizer.
+ * Mixed path: Q and K also get NVFP4 codes and scales (see flamia_qtensors);
+ * the tensor scale needs the tensor-wide amax, so one more launch computes it
+ * first.  Launches: the work-list builder, (mixed path) the amax pass, the
+ * quantizer.
  */
 flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const void* k,
                               const void* v, const flamia_qtensors* out, hipStream_t stream);

@@ -57,11 +57,17 @@ struct BwdArgs {
   uint16_t* dq_acc;
   float* dk_f32;
   uint16_t* dv;
+  Fp4Operands f4;
 };
 
-template <int D>
+// PATH 0: MXFP8 scores.  PATH 1 (mixed): the recomputed scores come from the
+// NVFP4 Q and K, expanded exactly to bf16 and multiplied on bf16 matrix cores
+// with the same operand split and order as the forward, then scaled by
+// t_Q t_K; dK and dQ still use the E4M3 token-block Q~ and K~.
+template <int D, int PATH>
 __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   constexpr int KS = D + 16;                 // token-major code row stride (bytes)
+  constexpr int QSB = 2 * D + 16;            // token-major bf16 row stride of the mixed-path Q tile
   constexpr int GS = 2 * D + 64;             // token-major bf16 row stride (bytes); = 64 mod 256 so the
                                              // four rows of a 16-bit transpose read hit distinct banks
   constexpr int DSK = BWD_BQ + 16;           // key-major dS^ row stride (bytes)
@@ -73,6 +79,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sK[BWD_BK * KS];
   __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BWD_BQ * KS];
   __shared__ __attribute__((aligned(16))) uint8_t sdO[2][BWD_BQ * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sQb[2][PATH ? BWD_BQ * QSB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sG[2][BWD_BQ * GS];
   __shared__ __attribute__((aligned(16))) uint8_t sdSK[BWD_BK * DSK];
   __shared__ __attribute__((aligned(16))) uint16_t sdQ[BWD_BQ * D];
@@ -118,28 +125,48 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
   }
 
-  // ---- per wave: K~, V~ (block and per-key) as B operands (lane = key)
-  v8i kreg[NS], vreg[NS], vkreg[NS];
+  // ---- per wave: K~ (or the mixed path's bf16 K), V~ (block and per-key) as
+  // B operands (lane = key)
+  v8i kreg[PATH ? 1 : NS], vreg[NS], vkreg[NS];
+  v8bf kb16[PATH ? D / 16 : 1];
   int ke = E8M0_BIAS, ve = E8M0_BIAS, vke = E8M0_BIAS;
+  float tqk = 1.f;
+  if constexpr (PATH == 1) tqk = a.f4.qk_scale[2] * a.f4.qk_scale[3];
   if (kv) {
     const size_t ro = doc0 + (size_t)j * rs;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      kreg[s] = cat8(ld16(a.k_codes + ro + 64 * s + 16 * hh), ld16(a.k_codes + ro + 64 * s + 32 + 16 * hh));
+      if constexpr (PATH == 0)
+        kreg[s] = cat8(ld16(a.k_codes + ro + 64 * s + 16 * hh), ld16(a.k_codes + ro + 64 * s + 32 + 16 * hh));
       vreg[s] = cat8(ld16(a.v_codes + ro + 64 * s + 16 * hh), ld16(a.v_codes + ro + 64 * s + 32 + 16 * hh));
       vkreg[s] = cat8(ld16(a.v_key_codes + ro + 64 * s + 16 * hh), ld16(a.v_key_codes + ro + 64 * s + 32 + 16 * hh));
+    }
+    if constexpr (PATH == 1) {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(a.f4.k_fp4 + ro / 2 + 8 * s + 4 * hh);
+        kb16[s] = __builtin_bit_cast(v8bf, e2m1x8_times_bf16(codes, fp8_value(a.f4.k_sf[ro / 16 + s], 0)));
+      }
     }
     ke = a.k_exp[hT + j];
     ve = a.v_exp[hT + j];
     vke = a.v_key_exp[hT + j];
   } else {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kreg[s] = vreg[s] = vkreg[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) vreg[s] = vkreg[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (PATH == 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) kreg[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) kb16[s] = __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+    }
   }
   const int e_key = vke - E8M0_BIAS;
 
   // ---- register prefetch of one query tile
-  v4i pq[NCQ], pdo[NCQ], pg[NCG];
+  v4i pq[NCQ], pdo[NCQ], pg[NCG], pq4;
+  uint32_t psf = 0;           // mixed path: NVFP4 Q chunk and its two group scales
   // per-row statistics for threads < BWD_BQ; threads BWD_BQ and BWD_BQ + 1
   // carry the two query blocks' Q and dO exponents in pm / psig
   int pm = 0, psig = 0, pvref = 0;
@@ -161,6 +188,15 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       const int ch = tid + BWD_THREADS * c2;
       const int r = ch / (D / 8), c8 = ch % (D / 8);
       pg[c2] = r < nq ? ld16(a.g + to + r * rs + 8 * c8) : v4i{0, 0, 0, 0};
+    }
+    if constexpr (PATH == 1) {
+      constexpr int CPR = D / 32;       // 16-byte NVFP4 chunks (32 codes) per query row
+      if (tid < BWD_BQ * CPR) {
+        const int r = tid / CPR, c4 = tid % CPR;
+        const bool ok = r < nq;
+        pq4 = ok ? ld16(a.f4.q_fp4 + (to + (size_t)r * rs) / 2 + 16 * c4) : v4i{0, 0, 0, 0};
+        psf = ok ? *reinterpret_cast<const uint16_t*>(a.f4.q_sf + (to + (size_t)r * rs) / 16 + 2 * c4) : 0u;
+      }
     }
     if (tid < BWD_BQ) {
       const bool ok = tid < nq;
@@ -190,6 +226,16 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       const int ch = tid + BWD_THREADS * c2;
       const int r = ch / (D / 8), c8 = ch % (D / 8);
       st16(&sG[buf][r * GS + 16 * c8], pg[c2]);
+    }
+    if constexpr (PATH == 1) {
+      constexpr int CPR = D / 32;
+      if (tid < BWD_BQ * CPR) {
+        const int r = tid / CPR, c4 = tid % CPR;
+        uint8_t* dst = &sQb[buf][r * QSB + 64 * c4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          st16(dst + 16 * w, e2m1x8_times_bf16((uint32_t)pq4[w], fp8_value((int)psf, w >> 1)));
+      }
     }
     if (tid < BWD_BQ) {
       sM[buf][tid] = pm;
@@ -246,11 +292,21 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
         const int sqe = sQeB[buf][qb], sdoe = sDOeB[buf][qb];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const uint8_t* qr = tQ + (32 * qb + n) * KS + 64 * s;
           const uint8_t* dr = tdO + (32 * qb + n) * KS + 64 * s;
-          sacc = mfma_f8(cat8(ld16(qr + 16 * hh), ld16(qr + 32 + 16 * hh)), kreg[s], sacc, sqe, ke);
+          if constexpr (PATH == 0) {
+            const uint8_t* qr = tQ + (32 * qb + n) * KS + 64 * s;
+            sacc = mfma_f8(cat8(ld16(qr + 16 * hh), ld16(qr + 32 + 16 * hh)), kreg[s], sacc, sqe, ke);
+          }
           pacc = mfma_f8(cat8(ld16(dr + 16 * hh), ld16(dr + 32 + 16 * hh)), dia ? vkreg[s] : vreg[s], pacc,
                          sdoe, dia ? vke : ve);
+        }
+        if constexpr (PATH == 1) {
+          const uint8_t* qr = sQb[buf] + (32 * qb + n) * QSB;
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s)
+            sacc = mfma_bf16(__builtin_bit_cast(v8bf, ld16(qr + 2 * (16 * s + 8 * hh))), kb16[s], sacc);
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) sacc[rr] = sacc[rr] * tqk;
         }
         float dsv[16];
         uint32_t pe[8];    // bf16 pairs of P^_eff * 2^8, accumulator register order
@@ -390,18 +446,20 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
                            const int* row_max, const float* row_sum, const uint8_t* do_codes,
                            const uint8_t* do_exp, const float* delta, const void* g,
                            const int* dq_sigma, void* dq_acc, float* dk_f32, void* dv,
-                           hipStream_t stream) {
+                           const Fp4Operands& f4, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const char* base = static_cast<const char*>(plan);
   BwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.bwd_offset),
             q_codes, k_codes, v_codes, v_key_codes, q_exp, k_exp, v_exp, v_key_exp, v_ref_exp,
             row_max, row_sum, do_codes, do_exp, delta, static_cast<const uint16_t*>(g), dq_sigma,
-            static_cast<uint16_t*>(dq_acc), dk_f32, static_cast<uint16_t*>(dv)};
+            static_cast<uint16_t*>(dq_acc), dk_f32, static_cast<uint16_t*>(dv), f4};
   dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.H);
-  if (p.D == 64)
-    hipLaunchKernelGGL(attn_bwd_kernel<64>, grid, dim3(BWD_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_bwd_kernel<128>, grid, dim3(BWD_THREADS), 0, stream, a);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };
+  if (p.path == 1) {
+    if (p.D == 64) go(attn_bwd_kernel<64, 1>); else go(attn_bwd_kernel<128, 1>);
+  } else {
+    if (p.D == 64) go(attn_bwd_kernel<64, 0>); else go(attn_bwd_kernel<128, 0>);
+  }
   return hipGetLastError();
 }
 

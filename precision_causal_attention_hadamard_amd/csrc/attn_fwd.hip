@@ -41,19 +41,24 @@ struct FwdArgs {
   const int2* items;
   const uint8_t *q_codes, *k_codes, *v_codes, *v_key_codes;
   const uint8_t *q_exp, *k_exp, *v_exp, *v_key_exp, *v_ref_exp;
+  Fp4Operands f4;
   uint16_t* o;
   int* row_max;
   float* row_sum;
 };
 
-template <int D>
+// PATH 0: MXFP8 scores.  PATH 1 (mixed): scores from NVFP4 Q and K, expanded
+// exactly to bf16 (code x group scale) and multiplied on bf16 matrix cores,
+// then scaled by t_Q t_K; the rest of the kernel is shared.
+template <int D, int PATH>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D + 16;          // token-major row stride (bytes)
-  constexpr int NS = D / 64;          // K-steps of the S product
+  constexpr int KSB = 2 * D + 16;     // token-major bf16 row stride (bytes), mixed path K
+  constexpr int NS = D / 64;          // K-steps of the FP8 S product
   constexpr int ND = D / 32;          // d-blocks of the output
   constexpr int NCH = FWD_BK * D / 16 / FWD_THREADS;  // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint8_t sK[2][FWD_BK * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][FWD_BK * (PATH ? KSB : KS)];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][FWD_BK * KS];
   __shared__ __attribute__((aligned(16))) uint8_t sVk[2][FWD_BK * KS];
   __shared__ uint8_t sKe[2][FWD_BK], sVe[2][FWD_BK], sVke[2][FWD_BK];
@@ -82,17 +87,35 @@ attn_fwd_kernel(FwdArgs a) {
   const uint8_t* vkdoc = a.v_key_codes + (size_t)s_d * rs + (size_t)head * D;
 
   // Q~ as the B operand of S^T = K~ Q~^T (lane = query column)
-  v8i qa[NS];
+  v8i qa[PATH ? 1 : NS];
+  v8bf qb[PATH ? D / 16 : 1];   // mixed path: NVFP4 Q expanded to bf16, K-step s = d in [16s, 16s + 16)
   int qe = E8M0_BIAS, vref = 0;
+  float tqk = 1.f;
+  if constexpr (PATH == 1) tqk = a.f4.qk_scale[2] * a.f4.qk_scale[3];
   if (iv) {
-    const uint8_t* qrow = a.q_codes + (size_t)(s_d + i) * rs + (size_t)head * D;
+    if constexpr (PATH == 0) {
+      const uint8_t* qrow = a.q_codes + (size_t)(s_d + i) * rs + (size_t)head * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qa[s] = cat8(ld16(qrow + 64 * s + 16 * hh), ld16(qrow + 64 * s + 32 + 16 * hh));
-    qe = a.q_exp[hT + i];
+      for (int s = 0; s < NS; ++s) qa[s] = cat8(ld16(qrow + 64 * s + 16 * hh), ld16(qrow + 64 * s + 32 + 16 * hh));
+      qe = a.q_exp[hT + i];
+    } else {
+      const size_t qi = (size_t)(s_d + i) * rs + (size_t)head * D;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(a.f4.q_fp4 + qi / 2 + 8 * s + 4 * hh);
+        const float sc = fp8_value(a.f4.q_sf[qi / 16 + s], 0);
+        qb[s] = __builtin_bit_cast(v8bf, e2m1x8_times_bf16(codes, sc));
+      }
+    }
     vref = (int)a.v_ref_exp[hT + i] - E8M0_BIAS;
   } else {
+    if constexpr (PATH == 0) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qa[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int s = 0; s < NS; ++s) qa[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qb[s] = __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+    }
   }
 
   v16f oacc[ND];
@@ -106,7 +129,10 @@ attn_fwd_kernel(FwdArgs a) {
 
   // ---- register prefetch of one key tile
   v4i pk[NCH], pv[NCH], pvk[NCH];
+  uint32_t psf = 0;           // mixed path: group scales of the prefetched NVFP4 chunk
   uint8_t pke = 0, pve = 0, pvke = 0;
+  const uint8_t* k4doc = PATH ? a.f4.k_fp4 + ((size_t)s_d * rs + (size_t)head * D) / 2 : nullptr;
+  const uint8_t* ksfdoc = PATH ? a.f4.k_sf + ((size_t)s_d * rs + (size_t)head * D) / 16 : nullptr;
   auto prefetch = [&](int kt) {
     const int j0 = kt * FWD_BK;
     const int nvalid = min(FWD_BK, L - j0);
@@ -117,9 +143,19 @@ attn_fwd_kernel(FwdArgs a) {
       const int r = ch / (D / 16), c16 = ch % (D / 16);
       const bool ok = r < nvalid;
       const size_t off = (size_t)(j0 + r) * rs + 16 * c16;
-      pk[c2] = ok ? ld16(kdoc + off) : v4i{0, 0, 0, 0};
+      if constexpr (PATH == 0) pk[c2] = ok ? ld16(kdoc + off) : v4i{0, 0, 0, 0};
       pv[c2] = ok ? ld16(vdoc + off) : v4i{0, 0, 0, 0};
       pvk[c2] = (ok && diag_tile) ? ld16(vkdoc + off) : v4i{0, 0, 0, 0};
+    }
+    if constexpr (PATH == 1) {
+      // NVFP4 K: 16-byte chunk = 32 codes (d in [32 c, 32 c + 32)) of one key, 2 group scales
+      constexpr int CPR = D / 32;       // 16-byte chunks (32 codes) per key row
+      if (tid < FWD_BK * CPR) {
+        const int r = tid / CPR, c4 = tid % CPR;
+        const bool ok = r < nvalid;
+        pk[0] = ok ? ld16(k4doc + (size_t)(j0 + r) * rs / 2 + 16 * c4) : v4i{0, 0, 0, 0};
+        psf = ok ? *reinterpret_cast<const uint16_t*>(ksfdoc + (size_t)(j0 + r) * rs / 16 + 2 * c4) : 0u;
+      }
     }
     if (tid < FWD_BK) {
       const bool kv = tid < nvalid;
@@ -133,9 +169,19 @@ attn_fwd_kernel(FwdArgs a) {
     for (int c2 = 0; c2 < NCH; ++c2) {
       const int ch = tid + FWD_THREADS * c2;
       const int r = ch / (D / 16), c16 = ch % (D / 16);
-      st16(&sK[buf][r * KS + 16 * c16], pk[c2]);
+      if constexpr (PATH == 0) st16(&sK[buf][r * KS + 16 * c16], pk[c2]);
       st16(&sV[buf][r * KS + 16 * c16], pv[c2]);
       st16(&sVk[buf][r * KS + 16 * c16], pvk[c2]);
+    }
+    if constexpr (PATH == 1) {
+      constexpr int CPR = D / 32;
+      if (tid < FWD_BK * CPR) {
+        const int r = tid / CPR, c4 = tid % CPR;
+        uint8_t* dst = &sK[buf][r * KSB + 64 * c4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          st16(dst + 16 * w, e2m1x8_times_bf16((uint32_t)pk[0][w], fp8_value((int)psf, w >> 1)));
+      }
     }
     if (tid < FWD_BK) {
       sKe[buf][tid] = pke;
@@ -167,12 +213,21 @@ attn_fwd_kernel(FwdArgs a) {
         dia[kb] = KB == QB;
         st[kb] = v16f{};
         if (act[kb]) {
-          const uint8_t* krow = tK + (32 * kb + n) * KS;
-          const int ske = sKe[buf][32 * kb + n];
+          if constexpr (PATH == 0) {
+            const uint8_t* krow = tK + (32 * kb + n) * KS;
+            const int ske = sKe[buf][32 * kb + n];
 #pragma unroll
-          for (int s = 0; s < NS; ++s)
-            st[kb] = mfma_f8(cat8(ld16(krow + 64 * s + 16 * hh), ld16(krow + 64 * s + 32 + 16 * hh)), qa[s],
-                             st[kb], ske, qe);
+            for (int s = 0; s < NS; ++s)
+              st[kb] = mfma_f8(cat8(ld16(krow + 64 * s + 16 * hh), ld16(krow + 64 * s + 32 + 16 * hh)), qa[s],
+                               st[kb], ske, qe);
+          } else {
+            const uint8_t* krow = tK + (32 * kb + n) * KSB;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+              st[kb] = mfma_bf16(__builtin_bit_cast(v8bf, ld16(krow + 2 * (16 * s + 8 * hh))), qb[s], st[kb]);
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) st[kb][rr] = st[kb][rr] * tqk;
+          }
           if (interior) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, st[kb][rr]);
@@ -283,17 +338,19 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
                            const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
                            const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
                            const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
-                           void* o, int* row_max, float* row_sum, hipStream_t stream) {
+                           const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const char* base = static_cast<const char*>(plan);
   FwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.fwd_offset),
-            q_codes, k_codes, v_codes, v_key_codes, q_exp, k_exp, v_exp, v_key_exp, v_ref_exp,
+            q_codes, k_codes, v_codes, v_key_codes, q_exp, k_exp, v_exp, v_key_exp, v_ref_exp, f4,
             static_cast<uint16_t*>(o), row_max, row_sum};
   dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
-  if (p.D == 64)
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(FWD_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(FWD_THREADS), 0, stream, a);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(FWD_THREADS), 0, stream, a); };
+  if (p.path == 1) {
+    if (p.D == 64) go(attn_fwd_kernel<64, 1>); else go(attn_fwd_kernel<128, 1>);
+  } else {
+    if (p.D == 64) go(attn_fwd_kernel<64, 0>); else go(attn_fwd_kernel<128, 0>);
+  }
   return hipGetLastError();
 }
 

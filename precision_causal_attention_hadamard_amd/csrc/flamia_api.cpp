@@ -26,7 +26,7 @@ flamia_status validate(const flamia_attn_desc* d) {
   if ((d->hadamard | d->causal_dq_scale | d->deterministic | d->causal) & ~1) return FLAMIA_ERR_INVALID_ARG;
   if (d->path != 0 && d->path != 1) return FLAMIA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
-  if (d->causal != 1 || d->path != 0 || d->deterministic != 0) return FLAMIA_ERR_UNSUPPORTED;
+  if (d->causal != 1 || d->deterministic != 0) return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
   // sort key, costs into 20 bits, grid x into 31 bits
   if (d->num_docs >= (1 << 24) || d->total_tokens >= (1 << 24)) return FLAMIA_ERR_WORKSPACE;
@@ -47,7 +47,7 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
 }
 
 struct QLayout {
-  size_t codes[4], exps[5], plan, bytes;
+  size_t codes[4], exps[5], plan, fp4[2], sf[2], qk_scale, bytes;
 };
 
 QLayout q_layout(const flamia_attn_desc* d) {
@@ -58,7 +58,14 @@ QLayout q_layout(const flamia_attn_desc* d) {
   for (int i = 0; i < 4; ++i) { q.codes[i] = off; off = align_up(off + E); }
   for (int i = 0; i < 5; ++i) { q.exps[i] = off; off = align_up(off + M); }
   q.plan = off;
-  q.bytes = off + plan_layout(d).bytes;
+  off = align_up(off + plan_layout(d).bytes);
+  q.fp4[0] = q.fp4[1] = q.sf[0] = q.sf[1] = q.qk_scale = 0;
+  if (d->path == 1) {
+    for (int i = 0; i < 2; ++i) { q.fp4[i] = off; off = align_up(off + E / 2); }
+    for (int i = 0; i < 2; ++i) { q.sf[i] = off; off = align_up(off + E / 16); }
+    q.qk_scale = off; off = align_up(off + 4 * sizeof(float));
+  }
+  q.bytes = off;
   return q;
 }
 
@@ -87,14 +94,21 @@ Problem problem(const flamia_attn_desc* d) {
   p.D = d->head_dim;
   p.hadamard = d->hadamard;
   p.causal_dq_scale = d->causal_dq_scale;
+  p.path = d->path;
   p.softmax_scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
   p.c_log2 = (float)((double)p.softmax_scale * 1.4426950408889634);
   return p;
 }
 
-bool qt_complete(const flamia_qtensors* q) {
-  return q && q->q_codes && q->k_codes && q->v_codes && q->v_key_codes && q->q_exp && q->k_exp &&
-         q->v_exp && q->v_key_exp && q->v_ref_exp && q->plan;
+bool qt_complete(const flamia_attn_desc* d, const flamia_qtensors* q) {
+  if (!(q && q->q_codes && q->k_codes && q->v_codes && q->v_key_codes && q->q_exp && q->k_exp &&
+        q->v_exp && q->v_key_exp && q->v_ref_exp && q->plan))
+    return false;
+  return d->path != 1 || (q->q_fp4 && q->k_fp4 && q->q_sf && q->k_sf && q->qk_tensor_scale);
+}
+
+Fp4Operands fp4_operands(const flamia_qtensors* q) {
+  return Fp4Operands{q->q_fp4, q->k_fp4, q->q_sf, q->k_sf, q->qk_tensor_scale};
 }
 
 flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
@@ -129,6 +143,12 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base, f
   out->v_key_exp = b + q.exps[3];
   out->v_ref_exp = b + q.exps[4];
   out->plan = b + q.plan;
+  const bool mixed = desc->path == 1;
+  out->q_fp4 = mixed ? b + q.fp4[0] : nullptr;
+  out->k_fp4 = mixed ? b + q.fp4[1] : nullptr;
+  out->q_sf = mixed ? b + q.sf[0] : nullptr;
+  out->k_sf = mixed ? b + q.sf[1] : nullptr;
+  out->qk_tensor_scale = mixed ? reinterpret_cast<float*>(b + q.qk_scale) : nullptr;
   return FLAMIA_OK;
 }
 
@@ -136,14 +156,18 @@ flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const
                               const flamia_qtensors* out, hipStream_t stream) {
   flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!q || !k || !v || !qt_complete(out)) return FLAMIA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !qt_complete(desc, out)) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const PlanLayout pl = plan_layout(desc);
-  s = hip_status(launch_plan(p.cu, p.ndocs, out->plan, pl, stream));
+  s = hip_status(launch_plan(p.cu, p.ndocs, out->plan, pl, p.path == 1 ? out->qk_tensor_scale : nullptr, stream));
   if (s != FLAMIA_OK) return s;
+  if (p.path == 1) {
+    s = hip_status(launch_amax_qk(p, q, k, out->qk_tensor_scale, stream));
+    if (s != FLAMIA_OK) return s;
+  }
   return hip_status(launch_quant_qkv(p, q, k, v, out->q_codes, out->k_codes, out->v_codes, out->v_key_codes,
                                      out->q_exp, out->k_exp, out->v_exp, out->v_key_exp, out->v_ref_exp,
-                                     stream));
+                                     fp4_operands(out), stream));
 }
 
 flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
@@ -151,18 +175,18 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
   (void)ws;
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(qt) || !o || !row_max || !row_sum) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !o || !row_max || !row_sum) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   return hip_status(launch_attn_fwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
                                     qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp,
-                                    qt->v_ref_exp, o, row_max, row_sum, stream));
+                                    qt->v_ref_exp, fp4_operands(qt), o, row_max, row_sum, stream));
 }
 
 flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
                                    const float* row_sum, const void* dout, void* ws, hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(qt) || !o || !row_sum || !dout || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !o || !row_sum || !dout || !ws) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
@@ -177,7 +201,7 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
                                    hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(qt) || !row_max || !row_sum || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !row_max || !row_sum || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
@@ -187,7 +211,7 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
                                     qt->v_ref_exp, row_max, row_sum, w + b.do_codes, w + b.do_exp,
                                     reinterpret_cast<const float*>(w + b.delta), w + b.g,
                                     reinterpret_cast<const int*>(w + b.dq_sigma), w + b.dq_acc,
-                                    reinterpret_cast<float*>(w + b.dk_f32), dv, stream));
+                                    reinterpret_cast<float*>(w + b.dk_f32), dv, fp4_operands(qt), stream));
 }
 
 flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, void* dq, void* dk, void* ws,
@@ -208,7 +232,7 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
                               void* dk, void* dv, void* ws, hipStream_t stream) {
   flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(qt) || !o || !row_max || !row_sum || !dout || !dq || !dk || !dv || !ws)
+  if (!qt_complete(desc, qt) || !o || !row_max || !row_sum || !dout || !dq || !dk || !dv || !ws)
     return FLAMIA_ERR_INVALID_ARG;
   s = flamia_attn_bwd_prep(desc, qt, o, row_sum, dout, ws, stream);
   if (s != FLAMIA_OK) return s;

@@ -145,6 +145,27 @@ __device__ __forceinline__ void transpose4x4_b8(uint32_t r0, uint32_t r1, uint32
   c3 = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
 }
 
+// ---------------------------------------------------------------- NVFP4 expansion
+//
+// bf16 bits of (E2M1 code) x (E4M3 group scale value s).  The product has at
+// most 6 significant bits and lies in [2^-10, 2688], so it is exact in fp32
+// and its top 16 bits are the exact bf16 value.
+__device__ __forceinline__ uint32_t e2m1_times_bf16(uint32_t nib, float s) {
+  const uint32_t e = (nib >> 1) & 3u, m = nib & 1u;
+  const uint32_t mag = e == 0 ? (m ? 0x3f000000u : 0u) : (((126u + e) << 23) | (m << 22));
+  const uint32_t v = __float_as_uint(__uint_as_float(mag) * s) | ((nib & 8u) << 28);
+  return v >> 16;
+}
+
+// Eight E2M1 codes (one dword, element 0 in the low nibble) times s, as 8 bf16.
+__device__ __forceinline__ v4i e2m1x8_times_bf16(uint32_t codes, float s) {
+  v4i r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = (int)(e2m1_times_bf16((codes >> (8 * k)) & 15u, s) | (e2m1_times_bf16((codes >> (8 * k + 4)) & 15u, s) << 16));
+  return r;
+}
+
 // ---------------------------------------------------------------- LDS transpose reads
 //
 // gfx950 ds_read_b64_tr_b8 / _tr_b16, as measured on the hardware: within each

@@ -26,17 +26,26 @@ struct BwdLayout {
 struct Problem {
   const int* cu;
   int T, ndocs, H, D;
-  int hadamard, causal_dq_scale;
+  int hadamard, causal_dq_scale, path;
   float softmax_scale;     // fp32 softmax scale
   float c_log2;            // fp32(softmax_scale * log2(e))
 };
 
-hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, hipStream_t stream);
+hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, float* qk_scale,
+                       hipStream_t stream);
+
+// NVFP4 score operands of the mixed path (null when path = 0).
+struct Fp4Operands {
+  uint8_t *q_fp4, *k_fp4, *q_sf, *k_sf;
+  float* qk_scale;     // [0],[1] amax bits of Q and K; [2],[3] tensor scales
+};
+
+hipError_t launch_amax_qk(const Problem& p, const void* q, const void* k, float* qk_scale, hipStream_t stream);
 
 hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, const void* v,
                             uint8_t* q_codes, uint8_t* k_codes, uint8_t* v_codes, uint8_t* v_key_codes,
                             uint8_t* q_exp, uint8_t* k_exp, uint8_t* v_exp, uint8_t* v_key_exp,
-                            uint8_t* v_ref_exp, hipStream_t stream);
+                            uint8_t* v_ref_exp, const Fp4Operands& f4, hipStream_t stream);
 
 hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const float* row_sum,
                            const uint8_t* k_exp, const uint8_t* v_exp, uint8_t* do_codes,
@@ -47,7 +56,7 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
                            const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
                            const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
                            const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
-                           void* o, int* row_max, float* row_sum, hipStream_t stream);
+                           const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream);
 
 hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl,
                            const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
@@ -56,7 +65,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
                            const int* row_max, const float* row_sum, const uint8_t* do_codes,
                            const uint8_t* do_exp, const float* delta, const void* g,
                            const int* dq_sigma, void* dq_acc, float* dk_f32, void* dv,
-                           hipStream_t stream);
+                           const Fp4Operands& f4, hipStream_t stream);
 
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
                            const float* dk_f32, void* dq, void* dk, hipStream_t stream);

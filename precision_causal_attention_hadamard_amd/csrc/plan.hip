@@ -95,19 +95,22 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
 
 __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restrict__ cu, int ndocs,
                                                             int* counts, int2* fwd_items,
-                                                            int2* bwd_items) {
+                                                            int2* bwd_items, float* qk_scale) {
   __shared__ unsigned long long keys[PLAN_MAX_TILES];
   __shared__ int scan[PLAN_THREADS];
   build_sorted(cu, ndocs, true, FWD_BQ, FWD_BK, keys, scan, counts + 0, fwd_items);
   build_sorted(cu, ndocs, false, BWD_BQ, BWD_BK, keys, scan, counts + 1, bwd_items);
   if (threadIdx.x == 0) { counts[2] = 0; counts[3] = 0; }
+  // mixed path: clear the tensor-amax slots before the amax pass runs
+  if (qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
 }
 
-hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, hipStream_t stream) {
+hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, float* qk_scale,
+                       hipStream_t stream) {
   char* base = static_cast<char*>(plan);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu, ndocs,
                      reinterpret_cast<int*>(base), reinterpret_cast<int2*>(base + pl.fwd_offset),
-                     reinterpret_cast<int2*>(base + pl.bwd_offset));
+                     reinterpret_cast<int2*>(base + pl.bwd_offset), qk_scale);
   return hipGetLastError();
 }
 

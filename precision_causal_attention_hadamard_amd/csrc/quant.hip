@@ -130,6 +130,91 @@ __device__ __forceinline__ float half_row_amax(const float (&x)[D / 2]) {
   return m;
 }
 
+// ---------------------------------------------------------------- NVFP4 (mixed path)
+//
+// Score operands of the mixed path: E2M1 elements, one E4M3 scale per 16
+// head-dimension elements of a token, one fp32 tensor scale t = amax / 2688
+// per tensor ([Summary] opening paragraphs; [Reading, part 一] NVFP4 format).
+// The group scale is the smallest E4M3 value >= amax_group / fp32(6 t)
+// (the round-up rule for a non-power-of-two scale), capped at 448; element
+// codes are E2M1(x / fp32(s t)) rounded to nearest even, saturating at 6.
+
+// E2M1 code (bit 3 = sign) of v, round to nearest even, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t idx = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return ((__float_as_uint(v) >> 28) & 8u) | idx;
+}
+
+// Smallest E4M3 code whose value is >= q (q >= 0); 448 when q >= 448.
+__device__ __forceinline__ int e4m3_round_up_code(float q) {
+  if (q >= 448.f) return 0x7e;
+  int code = cvt_fp8x2(q, 0.f) & 0xff;
+  if (fp8_value(code, 0) < q) ++code;
+  return code;
+}
+
+template <int D>
+__global__ void __launch_bounds__(QUANT_THREADS)
+amax_qk_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+               float* __restrict__ qk_scale) {
+  const int tensor = blockIdx.y;
+  const uint16_t* src = tensor == 0 ? q : k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane >> 1, hf = lane & 1;
+  const int c0 = blockIdx.x * TOKEN_BLOCK;
+  const int H = p.H, T = p.T;
+  float m = 0.f;
+  for_blocks_in_chunk(p.cu, p.ndocs, T, c0, [&](int bs, int be, int, int) {
+    const int tok = bs + row;
+    const bool valid = tok < be;
+    for (int h = wave; h < H; h += QUANT_THREADS / 64) {
+      const size_t off = ((size_t)tok * H + h) * D + hf * (D / 2);
+      float x[D / 2];
+      load_half_row<D>(src + off, valid, x);
+      if (p.hadamard) fwht_half_row<D>(x, hf);
+      m = fmaxf(m, half_row_amax<D>(x));
+    }
+  });
+  m = wave_max(m);
+  if (lane == 0 && m > 0.f)
+    atomicMax(reinterpret_cast<unsigned int*>(qk_scale) + tensor, __float_as_uint(m));
+}
+
+// NVFP4 codes and group scales of one half-row (lane half hf of a token row).
+template <int D>
+__device__ __forceinline__ void store_nvfp4(uint8_t* __restrict__ fp4, uint8_t* __restrict__ sf,
+                                            const float (&x)[D / 2], float t) {
+  const float six_t = 6.0f * t;
+  uint32_t packed[D / 16];     // the half-row's D/2 codes, 8 per dword
+  uint32_t sfw = 0;
+#pragma unroll
+  for (int gi = 0; gi < D / 32; ++gi) {
+    float gmax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gmax = fmaxf(gmax, fabsf(x[16 * gi + e]));
+    const int code = e4m3_round_up_code(gmax / six_t);
+    sfw |= (uint32_t)code << (8 * gi);
+    const float st = fp8_value(code, 0) * t;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = st > 0.f ? x[16 * gi + 8 * w + e] / st : 0.f;
+        word |= e2m1_code(v) << (4 * e);
+      }
+      packed[2 * gi + w] = word;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c)
+    st16(fp4 + 16 * c, v4i{(int)packed[4 * c], (int)packed[4 * c + 1], (int)packed[4 * c + 2], (int)packed[4 * c + 3]});
+  if (D / 32 == 4) *reinterpret_cast<uint32_t*>(sf) = sfw;
+  else *reinterpret_cast<uint16_t*>(sf) = (uint16_t)sfw;
+}
+
 template <int D>
 __global__ void __launch_bounds__(QUANT_THREADS)
 quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -137,8 +222,15 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
                  uint8_t* __restrict__ v_key_codes, uint8_t* __restrict__ q_exp,
                  uint8_t* __restrict__ k_exp, uint8_t* __restrict__ v_exp,
-                 uint8_t* __restrict__ v_key_exp, uint8_t* __restrict__ v_ref_exp) {
+                 uint8_t* __restrict__ v_key_exp, uint8_t* __restrict__ v_ref_exp, Fp4Operands f4) {
   const int tensor = blockIdx.y;
+  const bool nvfp4 = p.path == 1 && tensor < 2;
+  float t = 1.f;
+  if (nvfp4) {
+    const float amax = f4.qk_scale[tensor];
+    t = amax > 0.f ? amax / 2688.0f : 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) f4.qk_scale[2 + tensor] = t;
+  }
   const uint16_t* src = tensor == 0 ? q : (tensor == 1 ? k : v);
   uint8_t* codes = tensor == 0 ? q_codes : (tensor == 1 ? k_codes : v_codes);
   uint8_t* exps = tensor == 0 ? q_exp : (tensor == 1 ? k_exp : v_exp);
@@ -161,6 +253,9 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
       if (valid) {
         store_codes<D>(codes + off, x, e);
         if (hf == 0) exps[(size_t)h * T + tok] = (uint8_t)(e + E8M0_BIAS);
+        if (nvfp4)
+          store_nvfp4<D>((tensor == 0 ? f4.q_fp4 : f4.k_fp4) + off / 2,
+                         (tensor == 0 ? f4.q_sf : f4.k_sf) + off / 16, x, t);
       }
       if (tensor == 2) {
         const float row_amax = fmaxf(lane_amax, __shfl_xor(lane_amax, 1, 64));
@@ -271,15 +366,27 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
 hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, const void* v,
                             uint8_t* q_codes, uint8_t* k_codes, uint8_t* v_codes, uint8_t* v_key_codes,
                             uint8_t* q_exp, uint8_t* k_exp, uint8_t* v_exp, uint8_t* v_key_exp,
-                            uint8_t* v_ref_exp, hipStream_t stream) {
+                            uint8_t* v_ref_exp, const Fp4Operands& f4, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK, 3);
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, q_codes, k_codes, v_codes, v_key_codes,
-                       q_exp, k_exp, v_exp, v_key_exp, v_ref_exp);
+                       q_exp, k_exp, v_exp, v_key_exp, v_ref_exp, f4);
   };
   if (p.D == 64) args(quant_qkv_kernel<64>); else args(quant_qkv_kernel<128>);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_qk(const Problem& p, const void* q, const void* k, float* qk_scale, hipStream_t stream) {
+  if (p.T == 0) return hipSuccess;
+  dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK, 2);
+  if (p.D == 64)
+    hipLaunchKernelGGL(amax_qk_kernel<64>, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)q,
+                       (const uint16_t*)k, qk_scale);
+  else
+    hipLaunchKernelGGL(amax_qk_kernel<128>, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)q,
+                       (const uint16_t*)k, qk_scale);
   return hipGetLastError();
 }
 

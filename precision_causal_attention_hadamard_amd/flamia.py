@@ -39,7 +39,8 @@ class AttnDesc(ctypes.Structure):
 class QTensors(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("q_codes", "k_codes", "v_codes", "v_key_codes", "q_exp", "k_exp", "v_exp",
-                 "v_key_exp", "v_ref_exp", "plan")]
+                 "v_key_exp", "v_ref_exp", "plan", "q_fp4", "k_fp4", "q_sf", "k_sf",
+                 "qk_tensor_scale")]
 
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_quantize", "flamia_attn_fwd",
@@ -227,6 +228,15 @@ class TrainingCall:
     def exps(self, field: str) -> torch.Tensor:
         T, H, _ = self.shape
         return self._view(field, T * H).view(H, T)
+
+    def nvfp4(self, which: str):
+        """Mixed path: (packed E2M1 codes [T,H,d/2], E4M3 group-scale bytes
+        [T,H,d/16], tensor scale) of 'q' or 'k'."""
+        T, H, d = self.shape
+        codes = self._view(f"{which}_fp4", T * H * d // 2).view(T, H, d // 2)
+        sf = self._view(f"{which}_sf", T * H * d // 16).view(T, H, d // 16)
+        ts = self._view("qk_tensor_scale", 16).view(torch.float32)
+        return codes, sf, ts[2 if which == "q" else 3]
 
     def plan_lists(self):
         fo, cf, bo, cb = plan_view(self.desc)

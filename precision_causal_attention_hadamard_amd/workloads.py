@@ -128,10 +128,10 @@ def config(k: int, seed: int | None = None) -> Workload:
 
 
 def small_packed(seed: int, doc_lens, heads: int = 2, head_dim: int = 64,
-                 outlier_scale: float = 0.0, hadamard: bool = False) -> Workload:
+                 outlier_scale: float = 0.0, hadamard: bool = False, path: int = 0) -> Workload:
     """A small packed workload for parity tests (documents off 32-alignment)."""
     rng = np.random.default_rng(seed)
     T = int(sum(doc_lens))
     q, kk, v, do = draw_tensors(rng, T, heads, head_dim, outlier_scale)
     return Workload(f"packed_{'_'.join(map(str, doc_lens))}_h{heads}_d{head_dim}", q, kk, v, do,
-                    _cu(doc_lens), heads, head_dim, hadamard=hadamard)
+                    _cu(doc_lens), heads, head_dim, hadamard=hadamard, path=path)

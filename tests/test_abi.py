@@ -56,7 +56,7 @@ def test_buffer_sizes_valid(lib):
 @pytest.mark.parametrize("field,value,want", [
     ("head_dim", 96, 1), ("head_dim", 256, 1), ("num_heads", 0, 1), ("num_docs", 0, 1),
     ("total_tokens", -1, 1), ("max_doc_len", 300, 1), ("hadamard", 2, 1),
-    ("causal", 0, 2), ("deterministic", 1, 2), ("path", 1, 2), ("path", 7, 1),
+    ("causal", 0, 2), ("deterministic", 1, 2), ("path", 7, 1),
 ])
 def test_invalid_and_unsupported_descriptors(lib, field, value, want):
     st, _, _ = sizes_status(lib, base_desc(**{field: value}))
@@ -80,9 +80,17 @@ def test_layout_alignment_and_carving(lib):
     qt = flamia.QTensors()
     assert lib.flamia_qtensors_layout(ctypes.byref(d), ctypes.c_void_p(0x10010), ctypes.byref(qt)) == 1
     assert lib.flamia_qtensors_layout(ctypes.byref(d), ctypes.c_void_p(0x100000), ctypes.byref(qt)) == 0
-    ptrs = [getattr(qt, f) for f, _ in flamia.QTensors._fields_]
-    assert all(p % 256 == 0 for p in ptrs) and len(set(ptrs)) == len(ptrs)
+    ptrs = [getattr(qt, f) for f, _ in flamia.QTensors._fields_ if getattr(qt, f)]
+    assert all(p % 256 == 0 for p in ptrs) and len(set(ptrs)) == len(ptrs) == 10
     assert qt.k_codes - qt.q_codes >= 256 * 2 * 64
+    assert not qt.q_fp4 and not qt.qk_tensor_scale          # MXFP8 path: no NVFP4 operands
+    # the mixed path carves the NVFP4 operands too, and needs a bigger buffer
+    d1 = base_desc(path=1)
+    qt1 = flamia.QTensors()
+    assert lib.flamia_qtensors_layout(ctypes.byref(d1), ctypes.c_void_p(0x100000), ctypes.byref(qt1)) == 0
+    ptrs1 = [getattr(qt1, f) for f, _ in flamia.QTensors._fields_]
+    assert all(ptrs1) and len(set(ptrs1)) == len(ptrs1)
+    assert sizes_status(lib, d1)[1] >= sizes_status(lib, d)[1] + 256 * 2 * 64 * (2 * 0.5 + 2 / 16)
 
 
 def test_tile_config_and_status_strings(lib):

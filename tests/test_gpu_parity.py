@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from oracle import attention as A
+from oracle import formats, nvfp4, quant
 from oracle import worklist as WL
 from precision_causal_attention_hadamard_amd import workloads as W
 
@@ -29,7 +30,7 @@ def run_gpu(flamia, wl, causal_dq_scale=False):
     dev = torch.device("cuda")
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
-                               causal_dq_scale=causal_dq_scale)
+                               causal_dq_scale=causal_dq_scale, path=wl.path)
     call.step()
     torch.cuda.synchronize()
     return call
@@ -37,7 +38,8 @@ def run_gpu(flamia, wl, causal_dq_scale=False):
 
 def run_oracle(wl):
     q, k, v, do = np_inputs(wl)
-    return A.training_call(q, k, v, do, wl.cu_seqlens, A.Numerics(hadamard=wl.hadamard))
+    return A.training_call(q, k, v, do, wl.cu_seqlens,
+                           A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8"))
 
 
 def metrics(got, want):
@@ -149,3 +151,37 @@ def test_document_isolation_gpu(gpu_lib):
         assert torch.equal(getattr(b, n)[other], base[n][other]), n
     for f in codes:
         assert torch.equal(b.codes(f)[other], codes[f][other]), f
+
+
+MIXED_CASES = {
+    "mixed_ragged_d64": lambda: W.small_packed(41, [1, 70, 33, 130], heads=3, head_dim=64, path=1),
+    "mixed_d128_h2": lambda: W.small_packed(42, [256, 100], heads=2, head_dim=128, path=1),
+    "mixed_hadamard_outliers_d128": lambda: W.small_packed(43, [200, 57], heads=2, head_dim=128,
+                                                           outlier_scale=20.0, hadamard=True, path=1),
+}
+
+
+def check_nvfp4(call, wl):
+    """NVFP4 codes (packed, even element in the low nibble), E4M3 group-scale
+    bytes and tensor scales equal the oracle's, bit for bit."""
+    q, k, v, _ = np_inputs(wl)
+    qt = quant.quantize_qkv(q, k, v, wl.cu_seqlens, wl.hadamard)
+    for which, rot in (("q", qt["q_rot"]), ("k", qt["k_rot"])):
+        codes, scales, t, _ = nvfp4.quantize_nvfp4(rot)
+        packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+        g_codes, g_sf, g_t = call.nvfp4(which)
+        np.testing.assert_array_equal(g_codes.cpu().numpy(), packed, err_msg=f"{which} codes")
+        np.testing.assert_array_equal(g_sf.cpu().numpy(), formats.e4m3_bits(scales), err_msg=f"{which} scales")
+        assert float(g_t) == float(t), which
+
+
+@pytest.mark.parametrize("case", list(MIXED_CASES))
+def test_parity_mixed_path(gpu_lib, case):
+    print(f"[parity] case={case}", flush=True)
+    wl = MIXED_CASES[case]()
+    call = run_gpu(gpu_lib, wl)
+    ref = run_oracle(wl)
+    check_codes(call, ref)
+    check_nvfp4(call, wl)
+    m = check_outputs(call, ref)
+    print(f"[parity] {case}: " + ", ".join(f"{k} rel={v[0]:.2e} cos={v[1]:.6f}" for k, v in m.items()), flush=True)
