@@ -26,7 +26,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix-core peak (published)
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E bandwidth (published)
+CPU_SAMPLE_HEADS = 8          # oracle sample: document 0, this many heads (about 10-20 s)
 METRIC = "fwd+bwd attention call ms & TFLOP/s incl. quantization; % of MFMA FP8 peak"
 KERNEL_SOURCES = {
     "attn_bwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_bwd.hip",
@@ -56,8 +58,72 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def weighted_peak(parts):
+    """Peak of a kernel whose products run in several dtypes: total FLOPs over
+    the time each part would take at its own dtype's peak."""
+    total = sum(f for f, _ in parts)
+    return total / sum(f / p for f, p in parts)
+
+
+def product_mix(d: int, pairs: int, mixed: bool):
+    """(FLOPs, peak) per product dtype for the forward and the backward.
+    Forward: S and P.V; backward: S again, dP, dV, dK, dQ (2 d per pair each).
+    dV runs on bf16 MFMA (1/l rides in G); on the mixed path the S products
+    are bf16 (expanded NVFP4)."""
+    u = 2 * d * pairs
+    s_peak = BF16_PEAK_TFLOPS if mixed else FP8_PEAK_TFLOPS
+    fwd = [(u, s_peak), (u, FP8_PEAK_TFLOPS)]
+    bwd = [(u, s_peak), (u, BF16_PEAK_TFLOPS), (3 * u, FP8_PEAK_TFLOPS)]
+    return fwd, bwd
+
+
+def _pmc_rows(run_dir: str, counter: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    return rows
+
+
+def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, both with --copy-calibration) into the traffic record of the
+    backward kernel.  Each counter is scaled by what it reads for the 1 GiB
+    device copy in the same run (known bytes: 1 GiB read, 1 GiB written)."""
+    kernel = "attn_bwd_kernel"
+    rec = {"kernel": kernel, "workload": f"config{cfg}", "command": command,
+           "source_sha": source_hash(KERNEL_SOURCES[kernel])}
+    total = 0.0
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(run_dir, counter)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit(f"{counter}: no device copy in {run_dir} (run with --copy-calibration)")
+        copy_kib = max(copies)
+        factor = (1 << 30) / 1024.0 / copy_kib
+        vals = [float(r["Counter_Value"]) for r in rows if f"flamia::{kernel}<" in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"{counter}: no {kernel} dispatch in {run_dir}")
+        kib = sum(vals) / len(vals)
+        rec[counter] = {"kib_per_dispatch_raw": kib, "dispatches": len(vals),
+                        "copy_1GiB_reads_kib": copy_kib, "scale": factor,
+                        "bytes_per_launch": kib * 1024.0 * factor}
+        total += kib * 1024.0 * factor
+    rec["hbm_bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", f"{kernel}_config{cfg}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def cpu_baseline(wl, cfg: int):
-    """The oracle, as it stands, on one (document, head) slice of the
+    """The oracle, as it stands, on document 0 and the first few heads of the
     workload, timed on the host cores."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -65,16 +131,18 @@ def cpu_baseline(wl, cfg: int):
     from oracle import attention as A
 
     s, e = wl.cu_seqlens[0], wl.cu_seqlens[1]
-    arrs = [t[s:e, 0:1].float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
+    nh = min(CPU_SAMPLE_HEADS, wl.heads)
+    arrs = [t[s:e, 0:nh].float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
     L = e - s
     t0 = time.perf_counter()
     A.training_call(*arrs, [0, L], A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8"))
     dt = time.perf_counter() - t0
-    flops = 14 * wl.head_dim * L * (L + 1) // 2
+    flops = 14 * wl.head_dim * nh * L * (L + 1) // 2
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"document 0 ({L} tokens), head 0 of the {wl.name} workload: quantize+fwd+bwd, "
-                      f"{dt:.2f} s; fp64 numpy, BLAS threads={threads}, elementwise steps single-threaded",
+            "sample": f"document 0 ({L} tokens), heads 0-{nh - 1} of the {wl.name} workload: "
+                      f"quantize+fwd+bwd, {dt:.2f} s; fp64 numpy, BLAS threads={threads}, "
+                      "elementwise steps single-threaded",
             "seconds": dt}
 
 
@@ -87,7 +155,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (known bytes) for counter calibration")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: write the backward kernel's traffic record from two rocprofv3 --pmc runs")
+    ap.add_argument("--pmc-command", default="",
+                    help="with --write-traffic: the rocprofv3 command that made the runs")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, args.config, args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the call would shard by heads/documents with no exchange, which is not built.",
@@ -147,25 +222,30 @@ def main():
 
     # roofline of the dominant kernel
     E = T * H * d
+    fwd_mix, bwd_mix = product_mix(d, pairs, bool(wl.path))
     kernels = {
-        "attn_bwd": ("attn_bwd_kernel", "mfma", 10 * d * pairs),
-        "attn_fwd": ("attn_fwd_kernel", "mfma", 4 * d * pairs),
-        "quantize": ("quant_qkv_kernel", "hbm", 10 * E + 5 * T * H),
+        "attn_bwd": ("attn_bwd_kernel", "mfma", 10 * d * pairs, weighted_peak(bwd_mix)),
+        "attn_fwd": ("attn_fwd_kernel", "mfma", 4 * d * pairs, weighted_peak(fwd_mix)),
+        "quantize": ("quant_qkv_kernel", "hbm", 10 * E + 5 * T * H, HBM_PEAK_GBS),
     }
     dom = max(kernels, key=lambda n: stage_ms[n])
-    kname, bound, work = kernels[dom]
+    kname, bound, work, peak = kernels[dom]
     t_dom = stage_ms[dom] * 1e-3
     if bound == "mfma":
-        achieved, peak, unit = work / t_dom / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s"
+        achieved, unit = work / t_dom / 1e12, "TFLOP/s"
     else:
-        achieved, peak, unit = work / t_dom / 1e9, HBM_PEAK_GBS, "GB/s"
+        achieved, unit = work / t_dom / 1e9, "GB/s"
+    traffic = measured_traffic(kname, f"config{args.config}") if kname == "attn_bwd_kernel" else None
     roofline = {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": measured_traffic(kname, f"config{args.config}"),
+                "frac": achieved / peak, "traffic": traffic,
+                "peak_note": "dtype-weighted: FP8 products at 5000, bf16 products at 2500 TFLOP/s"
+                             if bound == "mfma" else "HBM3E",
+                "frac_of_fp8_peak": achieved / FP8_PEAK_TFLOPS if bound == "mfma" else None,
                 "algorithmic_work_per_launch": work, "avg_launch_ms": stage_ms[dom]}
     qbytes = 10 * E + 5 * T * H
     quant = {"GB/s": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9,
              "frac_hbm_peak": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-             "algorithmic_bytes": qbytes, "launches": 2}
+             "algorithmic_bytes": qbytes, "launches": 3 if wl.path else 2}
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
