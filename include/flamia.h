@@ -99,6 +99,9 @@ typedef struct flamia_attn_desc {
  *                     token: the smallest E4M3 value >= amax_group / fp32(6 t).
  *  qk_tensor_scale    float[4]: [0], [1] = bits of the Q and K tensor amax
  *                     (working space), [2], [3] = t_Q, t_K = amax / 2688.
+ *  q_fp4_bf16, k_fp4_bf16  [T,H,d] bf16: E2M1 value x E4M3 group scale of
+ *                     each element, exact in bf16 (at most 5 significant
+ *                     bits), the operands of the score products.
  */
 typedef struct flamia_qtensors {
   uint8_t* q_codes;
@@ -116,6 +119,8 @@ typedef struct flamia_qtensors {
   uint8_t* q_sf;
   uint8_t* k_sf;
   float* qk_tensor_scale;
+  void* q_fp4_bf16;
+  void* k_fp4_bf16;
 } flamia_qtensors;
 
 /*

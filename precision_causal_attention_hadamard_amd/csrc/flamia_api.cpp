@@ -47,7 +47,7 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
 }
 
 struct QLayout {
-  size_t codes[4], exps[5], plan, fp4[2], sf[2], qk_scale, bytes;
+  size_t codes[4], exps[5], plan, fp4[2], sf[2], qk_scale, fx[2], bytes;
 };
 
 QLayout q_layout(const flamia_attn_desc* d) {
@@ -59,11 +59,12 @@ QLayout q_layout(const flamia_attn_desc* d) {
   for (int i = 0; i < 5; ++i) { q.exps[i] = off; off = align_up(off + M); }
   q.plan = off;
   off = align_up(off + plan_layout(d).bytes);
-  q.fp4[0] = q.fp4[1] = q.sf[0] = q.sf[1] = q.qk_scale = 0;
+  q.fp4[0] = q.fp4[1] = q.sf[0] = q.sf[1] = q.qk_scale = q.fx[0] = q.fx[1] = 0;
   if (d->path == 1) {
     for (int i = 0; i < 2; ++i) { q.fp4[i] = off; off = align_up(off + E / 2); }
     for (int i = 0; i < 2; ++i) { q.sf[i] = off; off = align_up(off + E / 16); }
     q.qk_scale = off; off = align_up(off + 4 * sizeof(float));
+    for (int i = 0; i < 2; ++i) { q.fx[i] = off; off = align_up(off + 2 * E); }
   }
   q.bytes = off;
   return q;
@@ -77,6 +78,8 @@ BwdLayout bwd_layout(const flamia_attn_desc* d) {
   b.do_codes = off; off = align_up(off + E);
   b.do_exp = off;   off = align_up(off + M);
   b.delta = off;    off = align_up(off + 4 * M);
+  b.il8 = off;      off = align_up(off + 4 * M);
+  b.qexps = off;    off = align_up(off + 4 * M);
   b.g = off;        off = align_up(off + 2 * E);
   b.dq_sigma = off; off = align_up(off + 4 * M);
   b.dq_acc = off;   off = align_up(off + 2 * E);
@@ -104,11 +107,13 @@ bool qt_complete(const flamia_attn_desc* d, const flamia_qtensors* q) {
   if (!(q && q->q_codes && q->k_codes && q->v_codes && q->v_key_codes && q->q_exp && q->k_exp &&
         q->v_exp && q->v_key_exp && q->v_ref_exp && q->plan))
     return false;
-  return d->path != 1 || (q->q_fp4 && q->k_fp4 && q->q_sf && q->k_sf && q->qk_tensor_scale);
+  return d->path != 1 ||
+         (q->q_fp4 && q->k_fp4 && q->q_sf && q->k_sf && q->qk_tensor_scale && q->q_fp4_bf16 && q->k_fp4_bf16);
 }
 
 Fp4Operands fp4_operands(const flamia_qtensors* q) {
-  return Fp4Operands{q->q_fp4, q->k_fp4, q->q_sf, q->k_sf, q->qk_tensor_scale};
+  return Fp4Operands{q->q_fp4, q->k_fp4, q->q_sf, q->k_sf, q->qk_tensor_scale,
+                     static_cast<uint16_t*>(q->q_fp4_bf16), static_cast<uint16_t*>(q->k_fp4_bf16)};
 }
 
 flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
@@ -149,6 +154,8 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base, f
   out->q_sf = mixed ? b + q.sf[0] : nullptr;
   out->k_sf = mixed ? b + q.sf[1] : nullptr;
   out->qk_tensor_scale = mixed ? reinterpret_cast<float*>(b + q.qk_scale) : nullptr;
+  out->q_fp4_bf16 = mixed ? b + q.fx[0] : nullptr;
+  out->k_fp4_bf16 = mixed ? b + q.fx[1] : nullptr;
   return FLAMIA_OK;
 }
 
@@ -191,9 +198,10 @@ flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qt
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
   uint8_t* w = static_cast<uint8_t*>(ws);
-  return hip_status(launch_quant_do(p, dout, o, row_sum, qt->k_exp, qt->v_exp, w + b.do_codes, w + b.do_exp,
-                                    reinterpret_cast<float*>(w + b.delta), w + b.g,
-                                    reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
+  return hip_status(launch_quant_do(p, dout, o, row_sum, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_ref_exp,
+                                    w + b.do_codes, w + b.do_exp, reinterpret_cast<float*>(w + b.delta),
+                                    reinterpret_cast<float*>(w + b.il8), reinterpret_cast<int*>(w + b.qexps),
+                                    w + b.g, reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
 }
 
 flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt,
@@ -206,12 +214,28 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
   uint8_t* w = static_cast<uint8_t*>(ws);
-  return hip_status(launch_attn_bwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
-                                    qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp,
-                                    qt->v_ref_exp, row_max, row_sum, w + b.do_codes, w + b.do_exp,
-                                    reinterpret_cast<const float*>(w + b.delta), w + b.g,
-                                    reinterpret_cast<const int*>(w + b.dq_sigma), w + b.dq_acc,
-                                    reinterpret_cast<float*>(w + b.dk_f32), dv, fp4_operands(qt), stream));
+  BwdInputs in{};
+  in.q_codes = qt->q_codes;
+  in.k_codes = qt->k_codes;
+  in.v_codes = qt->v_codes;
+  in.v_key_codes = qt->v_key_codes;
+  in.k_exp = qt->k_exp;
+  in.v_exp = qt->v_exp;
+  in.v_key_exp = qt->v_key_exp;
+  in.row_max = row_max;
+  in.il8 = reinterpret_cast<const float*>(w + b.il8);
+  in.delta = reinterpret_cast<const float*>(w + b.delta);
+  in.dq_sigma = reinterpret_cast<const int*>(w + b.dq_sigma);
+  in.qexps = reinterpret_cast<const int*>(w + b.qexps);
+  in.do_codes = w + b.do_codes;
+  in.g = w + b.g;
+  in.dq_acc = w + b.dq_acc;
+  in.dk_f32 = reinterpret_cast<float*>(w + b.dk_f32);
+  in.dv = dv;
+  in.q_x = qt->q_fp4_bf16;
+  in.k_x = qt->k_fp4_bf16;
+  in.qk_scale = qt->qk_tensor_scale;
+  return hip_status(launch_attn_bwd(p, qt->plan, plan_layout(desc), in, stream));
 }
 
 flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, void* dq, void* dk, void* ws,

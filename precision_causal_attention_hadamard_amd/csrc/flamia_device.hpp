@@ -212,4 +212,94 @@ __device__ __forceinline__ v8bf tr_bf16x8(const uint8_t* tile, int stride, int t
   return __builtin_bit_cast(v8bf, both);
 }
 
+// ---------------------------------------------------------------- swizzled LDS tiles
+//
+// Tiles staged by direct global->LDS loads are stored without padding; the
+// 16-byte chunk c of row r sits at chunk c ^ key(r) of that row.  The keys
+// spread the rows touched by one read instruction over all 64 banks:
+// * code tiles (one byte per element, d-byte rows; read by 16-byte operand
+//   loads of 32 rows and by 8-bit transpose reads of 16 rows);
+// * wide tiles (bf16, 2d-byte rows; read by 16-bit transpose reads of 8 rows);
+// * the mixed path's bf16 score operand (2d-byte rows; 16-byte operand loads
+//   of 32 rows).
+// Every key has period 16 in r or less, so row r + 16 shares the key of row r.
+
+template <int D> __device__ __forceinline__ int code_key(int r) {
+  return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
+template <int D> __device__ __forceinline__ int wide_key(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 1));
+}
+template <int D> __device__ __forceinline__ int xq_key(int r) {
+  return D == 128 ? wide_key<128>(r) : (r >> 1) & 7;
+}
+template <int D> __device__ __forceinline__ int code_off(int r, int byte) {
+  return r * D + ((((byte >> 4) ^ code_key<D>(r))) << 4) + (byte & 15);
+}
+template <int D> __device__ __forceinline__ int wide_off(int r, int byte) {
+  return r * 2 * D + ((((byte >> 4) ^ wide_key<D>(r))) << 4) + (byte & 15);
+}
+template <int D> __device__ __forceinline__ int xq_off(int r, int byte) {
+  return r * 2 * D + ((((byte >> 4) ^ xq_key<D>(r))) << 4) + (byte & 15);
+}
+
+// Direct global -> LDS loads: every lane fetches 16 (or 4) bytes from its own
+// global address; the wave's 64 results land contiguously at the
+// wave-uniform LDS address `lds` (lane l at lds + 16 l, or + 4 l).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+// Workgroup barrier for LDS traffic only: outstanding global loads, LDS DMA
+// and atomics stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0), vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier after every outstanding memory operation of the wave
+// (global loads, LDS DMA, atomics, LDS) has completed.
+__device__ __forceinline__ void full_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// floor(x) as an integer in one instruction (finite x in int range).
+__device__ __forceinline__ int cvt_floor_i32(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Transpose reads of swizzled tiles: same results as tr_block16 / tr_bf16x8
+// on the unswizzled tile.
+template <int D>
+__device__ __forceinline__ v4i tr_code16(const uint8_t* tile, int tok0, int col0, int lane) {
+  const int p = lane & 15, hh = lane >> 5;
+  const int b = p >> 1;
+  const int t = tok0 + 8 * (b >> 2) + 4 * hh + (b & 3);
+  const uint8_t* a0 = tile + code_off<D>(t, col0 + 8 * (p & 1));
+  const v2i lo = lds_tr8(a0);
+  const v2i hi = lds_tr8(a0 + 16 * D);
+  return v4i{lo[0], lo[1], hi[0], hi[1]};
+}
+template <int D>
+__device__ __forceinline__ v8bf tr_wide_bf16x8(const uint8_t* tile, int tok0, int ks, int col0, int lane) {
+  const int p = lane & 15, hh = lane >> 5;
+  const int e = p >> 2, s = p & 3;
+  const int t = tok0 + 16 * ks + 4 * hh + e;
+  const int byte = 2 * (col0 + 4 * s);
+  const v4s lo = lds_tr16(tile + wide_off<D>(t, byte));
+  const v4s hi = lds_tr16(tile + wide_off<D>(t + 8, byte));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(v8bf, both);
+}
+
 }  // namespace flamia

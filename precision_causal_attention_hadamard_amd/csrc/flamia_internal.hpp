@@ -20,7 +20,7 @@ struct PlanLayout {
 
 // Byte offsets of the backward workspace.
 struct BwdLayout {
-  size_t do_codes, do_exp, delta, g, dq_sigma, dq_acc, dk_f32, bytes;
+  size_t do_codes, do_exp, delta, il8, qexps, g, dq_sigma, dq_acc, dk_f32, bytes;
 };
 
 struct Problem {
@@ -38,6 +38,7 @@ hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& p
 struct Fp4Operands {
   uint8_t *q_fp4, *k_fp4, *q_sf, *k_sf;
   float* qk_scale;     // [0],[1] amax bits of Q and K; [2],[3] tensor scales
+  uint16_t *q_x, *k_x; // code x group scale, exactly, as bf16 [T, H, d]
 };
 
 hipError_t launch_amax_qk(const Problem& p, const void* q, const void* k, float* qk_scale, hipStream_t stream);
@@ -48,9 +49,9 @@ hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, cons
                             uint8_t* v_ref_exp, const Fp4Operands& f4, hipStream_t stream);
 
 hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const float* row_sum,
-                           const uint8_t* k_exp, const uint8_t* v_exp, uint8_t* do_codes,
-                           uint8_t* do_exp, float* delta, void* g, int* dq_sigma, void* dq_acc,
-                           hipStream_t stream);
+                           const uint8_t* q_exp, const uint8_t* k_exp, const uint8_t* v_exp,
+                           const uint8_t* v_ref_exp, uint8_t* do_codes, uint8_t* do_exp, float* delta,
+                           float* il8, int* qexps, void* g, int* dq_sigma, void* dq_acc, hipStream_t stream);
 
 hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout& pl,
                            const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
@@ -58,14 +59,26 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
                            const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
                            const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream);
 
-hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl,
-                           const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
-                           const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
-                           const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
-                           const int* row_max, const float* row_sum, const uint8_t* do_codes,
-                           const uint8_t* do_exp, const float* delta, const void* g,
-                           const int* dq_sigma, void* dq_acc, float* dk_f32, void* dv,
-                           const Fp4Operands& f4, hipStream_t stream);
+// Everything the backward kernel reads and writes.
+struct BwdInputs {
+  const uint8_t *q_codes, *k_codes, *v_codes, *v_key_codes;
+  const uint8_t *k_exp, *v_exp, *v_key_exp;
+  const int* row_max;      // [H, T]
+  const float* il8;        // [H, T] 2^-8 / l
+  const float* delta;      // [H, T]
+  const int* dq_sigma;     // [H, T]
+  const int* qexps;        // [H, T] q_exp | do_exp << 8 | v_ref_exp << 16
+  const uint8_t* do_codes;
+  const void* g;
+  void* dq_acc;
+  float* dk_f32;
+  void* dv;
+  const void *q_x, *k_x;   // mixed path only
+  const float* qk_scale;   // mixed path only
+};
+
+hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl, const BwdInputs& in,
+                           hipStream_t stream);
 
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
                            const float* dk_f32, void* dq, void* dk, hipStream_t stream);

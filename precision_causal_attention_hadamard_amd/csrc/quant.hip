@@ -182,10 +182,11 @@ amax_qk_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __rest
     atomicMax(reinterpret_cast<unsigned int*>(qk_scale) + tensor, __float_as_uint(m));
 }
 
-// NVFP4 codes and group scales of one half-row (lane half hf of a token row).
+// NVFP4 codes and group scales of one half-row (lane half hf of a token row),
+// and each element's code x group scale as bf16 (exact).
 template <int D>
 __device__ __forceinline__ void store_nvfp4(uint8_t* __restrict__ fp4, uint8_t* __restrict__ sf,
-                                            const float (&x)[D / 2], float t) {
+                                            uint16_t* __restrict__ xb, const float (&x)[D / 2], float t) {
   const float six_t = 6.0f * t;
   uint32_t packed[D / 16];     // the half-row's D/2 codes, 8 per dword
   uint32_t sfw = 0;
@@ -196,7 +197,8 @@ __device__ __forceinline__ void store_nvfp4(uint8_t* __restrict__ fp4, uint8_t* 
     for (int e = 0; e < 16; ++e) gmax = fmaxf(gmax, fabsf(x[16 * gi + e]));
     const int code = e4m3_round_up_code(gmax / six_t);
     sfw |= (uint32_t)code << (8 * gi);
-    const float st = fp8_value(code, 0) * t;
+    const float sv = fp8_value(code, 0);
+    const float st = sv * t;
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       uint32_t word = 0;
@@ -206,6 +208,7 @@ __device__ __forceinline__ void store_nvfp4(uint8_t* __restrict__ fp4, uint8_t* 
         word |= e2m1_code(v) << (4 * e);
       }
       packed[2 * gi + w] = word;
+      st16(xb + 16 * gi + 8 * w, e2m1x8_times_bf16(word, sv));
     }
   }
 #pragma unroll
@@ -255,7 +258,7 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         if (hf == 0) exps[(size_t)h * T + tok] = (uint8_t)(e + E8M0_BIAS);
         if (nvfp4)
           store_nvfp4<D>((tensor == 0 ? f4.q_fp4 : f4.k_fp4) + off / 2,
-                         (tensor == 0 ? f4.q_sf : f4.k_sf) + off / 16, x, t);
+                         (tensor == 0 ? f4.q_sf : f4.k_sf) + off / 16, (tensor == 0 ? f4.q_x : f4.k_x) + off, x, t);
       }
       if (tensor == 2) {
         const float row_amax = fmaxf(lane_amax, __shfl_xor(lane_amax, 1, 64));
@@ -282,10 +285,12 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 template <int D>
 __global__ void __launch_bounds__(QUANT_THREADS)
 quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
-                const float* __restrict__ row_sum, const uint8_t* __restrict__ k_exp,
-                const uint8_t* __restrict__ v_exp, uint8_t* __restrict__ do_codes,
-                uint8_t* __restrict__ do_exp, float* __restrict__ delta, uint16_t* __restrict__ g,
-                int* __restrict__ dq_sigma, uint16_t* __restrict__ dq_acc) {
+                const float* __restrict__ row_sum, const uint8_t* __restrict__ q_exp,
+                const uint8_t* __restrict__ k_exp, const uint8_t* __restrict__ v_exp,
+                const uint8_t* __restrict__ v_ref_exp, uint8_t* __restrict__ do_codes,
+                uint8_t* __restrict__ do_exp, float* __restrict__ delta, float* __restrict__ il8,
+                int* __restrict__ qexps, uint16_t* __restrict__ g, int* __restrict__ dq_sigma,
+                uint16_t* __restrict__ dq_acc) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
   const int c0 = blockIdx.x * TOKEN_BLOCK;
@@ -354,6 +359,8 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
           const size_t mi = (size_t)h * T + tok;
           do_exp[mi] = (uint8_t)(e + E8M0_BIAS);
           delta[mi] = dsum;
+          il8[mi] = ginv;
+          qexps[mi] = (int)q_exp[mi] | ((e + E8M0_BIAS) << 8) | ((int)v_ref_exp[mi] << 16);
           // |dQ partial sum| <= 2.2 d 448^3 2^(e_dO + e_V + e_K) < 2^(27.6 + log2 d + ...);
           // the prescale keeps it below 2^15 in fp16
           dq_sigma[mi] = e + emax_kv + LOG2D + 13;
@@ -391,15 +398,15 @@ hipError_t launch_amax_qk(const Problem& p, const void* q, const void* k, float*
 }
 
 hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const float* row_sum,
-                           const uint8_t* k_exp, const uint8_t* v_exp, uint8_t* do_codes,
-                           uint8_t* do_exp, float* delta, void* g, int* dq_sigma, void* dq_acc,
-                           hipStream_t stream) {
+                           const uint8_t* q_exp, const uint8_t* k_exp, const uint8_t* v_exp,
+                           const uint8_t* v_ref_exp, uint8_t* do_codes, uint8_t* do_exp, float* delta,
+                           float* il8, int* qexps, void* g, int* dq_sigma, void* dq_acc, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK);
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)dout,
-                       (const uint16_t*)o, row_sum, k_exp, v_exp, do_codes, do_exp, delta,
-                       (uint16_t*)g, dq_sigma, (uint16_t*)dq_acc);
+                       (const uint16_t*)o, row_sum, q_exp, k_exp, v_exp, v_ref_exp, do_codes, do_exp,
+                       delta, il8, qexps, (uint16_t*)g, dq_sigma, (uint16_t*)dq_acc);
   };
   if (p.D == 64) args(quant_do_kernel<64>); else args(quant_do_kernel<128>);
   return hipGetLastError();

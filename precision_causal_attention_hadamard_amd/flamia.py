@@ -40,7 +40,7 @@ class QTensors(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("q_codes", "k_codes", "v_codes", "v_key_codes", "q_exp", "k_exp", "v_exp",
                  "v_key_exp", "v_ref_exp", "plan", "q_fp4", "k_fp4", "q_sf", "k_sf",
-                 "qk_tensor_scale")]
+                 "qk_tensor_scale", "q_fp4_bf16", "k_fp4_bf16")]
 
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_quantize", "flamia_attn_fwd",
