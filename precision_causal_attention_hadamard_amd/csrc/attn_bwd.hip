@@ -86,10 +86,12 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   constexpr int CT = BWD_BQ * D;             // bytes of a query code tile
   constexpr int WT = BWD_BQ * 2 * D;         // bytes of a query bf16 tile
   constexpr int RT = NPLANES * BWD_BQ * 4;   // bytes of the per-row planes
-  static_assert(BWD_BK * D == WT, "the key tile and the fp16 dQ tile share one buffer");
+  constexpr int DQS = D + 4;                 // fp16 dQ staging row stride (elements): 8 bytes of
+                                             // padding put the 32 rows of one store on distinct banks
+  constexpr int KQ = BWD_BK * D > BWD_BQ * DQS * 2 ? BWD_BK * D : BWD_BQ * DQS * 2;
 
   // K~ tile at item start, then the fp16 dQ partial of the current step
-  __shared__ __attribute__((aligned(1024))) uint8_t sKQ[BWD_BK * D];
+  __shared__ __attribute__((aligned(1024))) uint8_t sKQ[KQ];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ0[CT];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ1[CT];
   __shared__ __attribute__((aligned(1024))) uint8_t sO0[CT];
@@ -124,7 +126,15 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   const size_t rs = (size_t)H * D;
   const size_t hT = (size_t)head * T + s_d;
   const size_t doc0 = (size_t)s_d * rs + (size_t)head * D;   // row 0 of this doc/head
+  const uint32_t rs32 = (uint32_t)rs;
   const float c = p.c_log2;
+  // per-document bases (uniform); per-lane offsets fit 32 bits (checked on the host)
+  const uint8_t* q_doc = a.q_codes + doc0;
+  const uint8_t* do_doc = a.do_codes + doc0;
+  const uint8_t* k_doc = a.k_codes + doc0;
+  const uint8_t* g_doc = reinterpret_cast<const uint8_t*>(a.g + doc0);
+  const uint8_t* x_doc = PATH ? reinterpret_cast<const uint8_t*>(a.q_x + doc0) : nullptr;
+  uint8_t* dq_doc = reinterpret_cast<uint8_t*>(a.dq_acc + doc0);
 
   // ---- staging of 64-row tiles: rows row0 + r, clamped to the document's last row
   auto dma_codes = [&](uint8_t* tile, const uint8_t* src, int row0, int nrows) {
@@ -132,19 +142,19 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     for (int i = wave; i < ninst; i += 4) {
       const int o = i * 1024 + 16 * lane;
       const int r = o / D, slot = (o % D) >> 4;
-      const int gr = min(row0 + r, L - 1);
-      dma16(src + doc0 + (size_t)gr * rs + 16 * (slot ^ code_key<D>(r)), tile + i * 1024);
+      const uint32_t gr = (uint32_t)min(row0 + r, L - 1);
+      dma16(src + (gr * rs32 + 16u * (uint32_t)(slot ^ code_key<D>(r))), tile + i * 1024);
     }
   };
-  auto dma_wide = [&](uint8_t* tile, const uint16_t* src, int row0, bool xq) {
+  auto dma_wide = [&](uint8_t* tile, const uint8_t* src, int row0, bool xq) {
     constexpr int NI = WT / 1024;
 #pragma unroll
     for (int i = wave; i < NI; i += 4) {
       const int o = i * 1024 + 16 * lane;
       const int r = o / (2 * D), slot = (o % (2 * D)) >> 4;
-      const int gr = min(row0 + r, L - 1);
+      const uint32_t gr = (uint32_t)min(row0 + r, L - 1);
       const int key = xq ? xq_key<D>(r) : wide_key<D>(r);
-      dma16(reinterpret_cast<const uint8_t*>(src + doc0 + (size_t)gr * rs) + 16 * (slot ^ key), tile + i * 1024);
+      dma16(src + (2u * gr * rs32 + 16u * (uint32_t)(slot ^ key)), tile + i * 1024);
     }
   };
   auto dma_planes = [&](uint8_t* tile, int row0) {
@@ -160,17 +170,17 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   auto issue_tile = [&](auto Bc, int qt) {
     constexpr int B = decltype(Bc)::value;
     const int q0 = qt * BWD_BQ;
-    dma_codes(B ? sQ1 : sQ0, a.q_codes, q0, BWD_BQ);
-    dma_codes(B ? sO1 : sO0, a.do_codes, q0, BWD_BQ);
-    dma_wide(B ? sG1 : sG0, a.g, q0, false);
-    if constexpr (PATH == 1) dma_wide(B ? sX1 : sX0, a.q_x, q0, true);
+    dma_codes(B ? sQ1 : sQ0, q_doc, q0, BWD_BQ);
+    dma_codes(B ? sO1 : sO0, do_doc, q0, BWD_BQ);
+    dma_wide(B ? sG1 : sG0, g_doc, q0, false);
+    if constexpr (PATH == 1) dma_wide(B ? sX1 : sX0, x_doc, q0, true);
     dma_planes(B ? sR1 : sR0, q0);
   };
 
   // ---- per item: the key tile (for K~^T of dQ) and the first query tile
   const int qt_first = k0 / BWD_BQ;
   const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
-  dma_codes(sKQ, a.k_codes, k0, BWD_BK);
+  dma_codes(sKQ, k_doc, k0, BWD_BK);
   issue_tile(std::integral_constant<int, 0>{}, qt_first);
   if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
 
@@ -235,9 +245,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     for (int idx = tid; idx < BWD_BQ * PAIRS; idx += BWD_THREADS) {
       const int row = idx / PAIRS, pr = idx % PAIRS;
       if (row < nqp) {
-        const v2h hv = *reinterpret_cast<const v2h*>(sdQ + row * D + 2 * pr);
+        const v2h hv = *reinterpret_cast<const v2h*>(sdQ + row * DQS + 2 * pr);
         __builtin_amdgcn_global_atomic_fadd_v2f16(
-            reinterpret_cast<v2h*>(a.dq_acc + doc0 + (size_t)(q0p + row) * rs + 2 * pr), hv);
+            reinterpret_cast<v2h*>(dq_doc + (2u * ((uint32_t)(q0p + row) * rs32) + 4u * (uint32_t)pr)), hv);
       }
     }
   };
@@ -414,7 +424,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       // prescaled fp16 partial of this query row into LDS (4 consecutive d per store)
       const int iq = 32 * qb + n;
       const int sig = psig[iq];
-      uint16_t* dst = sdQ + iq * D + 32 * ds + 4 * hh;
+      uint16_t* dst = sdQ + iq * DQS + 32 * ds + 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         v2h h0, h1;

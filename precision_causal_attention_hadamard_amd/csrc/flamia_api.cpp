@@ -33,6 +33,8 @@ flamia_status validate(const flamia_attn_desc* d) {
   const int cap = cdiv(d->total_tokens, 64) + d->num_docs;
   if (cap > PLAN_MAX_TILES) return FLAMIA_ERR_UNSUPPORTED;
   if ((int64_t)cap * d->num_heads >= (int64_t)1 << 31) return FLAMIA_ERR_WORKSPACE;
+  // the backward addresses a document's rows with 32-bit byte offsets of 2-byte elements
+  if ((int64_t)d->total_tokens * d->num_heads * d->head_dim >= (int64_t)1 << 30) return FLAMIA_ERR_WORKSPACE;
   return FLAMIA_OK;
 }
 

@@ -107,15 +107,32 @@ __device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v1
 
 // ---------------------------------------------------------------- wave reductions
 
+// Whole-wave maxima with DPP lane moves (no LDS round trips): pairs and quads,
+// then halves and whole rows of 16 by mirroring, then rows 0-1 and 0-3 by the
+// row broadcasts of lanes 15 and 31; lane 63 ends with the maximum, which is
+// returned to every lane.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false);
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  auto mx = [](float a, int b) { return fmaxf(a, __int_as_float(b)); };
+  v = mx(v, dpp_move<0xb1>(__float_as_int(v)));          // quad_perm [1,0,3,2]
+  v = mx(v, dpp_move<0x4e>(__float_as_int(v)));          // quad_perm [2,3,0,1]
+  v = mx(v, dpp_move<0x141>(__float_as_int(v)));         // row_half_mirror
+  v = mx(v, dpp_move<0x140>(__float_as_int(v)));         // row_mirror
+  v = mx(v, dpp_move<0x142, 0xa>(__float_as_int(v)));    // row_bcast:15 -> rows 1, 3
+  v = mx(v, dpp_move<0x143, 0xc>(__float_as_int(v)));    // row_bcast:31 -> rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
+  v = max(v, dpp_move<0xb1>(v));
+  v = max(v, dpp_move<0x4e>(v));
+  v = max(v, dpp_move<0x141>(v));
+  v = max(v, dpp_move<0x140>(v));
+  v = max(v, dpp_move<0x142, 0xa>(v));
+  v = max(v, dpp_move<0x143, 0xc>(v));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // ---------------------------------------------------------------- small loads
