@@ -9,8 +9,8 @@
 // [Reading, 4.3]; [Reading, 4.4] third bullet).
 //
 // Staging.  Query tiles (Q~ and dO~ codes, G = dO~ 2^-8 / l in bf16, and five
-// per-row planes: integer row maximum, 2^-8 / l, D, the dQ prescale exponent,
-// the Q / dO / fold-reference exponent bytes) go global -> LDS directly, with
+// per-row planes: 8 - integer row maximum, 2^-8 / l, D, the dQ prescale
+// exponent, the Q / dO / fold-reference exponent bytes) go global -> LDS directly, with
 // no register staging, into two named buffers; the loop is unrolled by two so
 // each step reads one buffer while the next tile streams into the other.
 // Tiles are unpadded and XOR-swizzled per 16-byte chunk.  The fp16 dQ partial
@@ -60,7 +60,7 @@ struct BwdArgs {
   const int2* items;
   const uint8_t *q_codes, *k_codes, *v_codes, *v_key_codes;
   const uint8_t *k_exp, *v_exp, *v_key_exp;
-  const int* row_max;     // [H, T] integer row maxima of the forward
+  const int* kofs;        // [H, T] 8 - integer row maximum of the forward
   const float* il8;       // [H, T] 2^-8 / l
   const float* delta;     // [H, T] D
   const int* dq_sigma;    // [H, T] dQ prescale exponent
@@ -88,10 +88,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   constexpr int RT = NPLANES * BWD_BQ * 4;   // bytes of the per-row planes
   constexpr int DQS = D + 4;                 // fp16 dQ staging row stride (elements): 8 bytes of
                                              // padding put the 32 rows of one store on distinct banks
-  constexpr int KQ = BWD_BK * D > BWD_BQ * DQS * 2 ? BWD_BK * D : BWD_BQ * DQS * 2;
 
-  // K~ tile at item start, then the fp16 dQ partial of the current step
-  __shared__ __attribute__((aligned(1024))) uint8_t sKQ[KQ];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[BWD_BK * D];         // K~ tile of the item
+  __shared__ __attribute__((aligned(1024))) uint8_t sKQ[BWD_BQ * DQS * 2];  // fp16 dQ partial of a step
   __shared__ __attribute__((aligned(1024))) uint8_t sQ0[CT];
   __shared__ __attribute__((aligned(1024))) uint8_t sQ1[CT];
   __shared__ __attribute__((aligned(1024))) uint8_t sO0[CT];
@@ -116,7 +115,8 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   const int L = p.cu[doc + 1] - s_d;
   const int k0 = u * BWD_BK;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int n = lane & 31, hh = lane >> 5;
   const int colg = 16 * ((lane >> 4) & 1);      // first column of this lane's 16-lane group
   const int j = k0 + 32 * wave + n;             // this lane's key (document-local)
@@ -136,7 +136,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   const uint8_t* x_doc = PATH ? reinterpret_cast<const uint8_t*>(a.q_x + doc0) : nullptr;
   uint8_t* dq_doc = reinterpret_cast<uint8_t*>(a.dq_acc + doc0);
 
-  // ---- staging of 64-row tiles: rows row0 + r, clamped to the document's last row
+  // ---- staging of row tiles: rows row0 + r, clamped to the document's last row.
+  // Instruction i of a tile fills tile bytes [1024 i, 1024 i + 1024); lane l
+  // brings the 16-byte chunk that the swizzle puts at byte 1024 i + 16 l.
   auto dma_codes = [&](uint8_t* tile, const uint8_t* src, int row0, int nrows) {
     const int ninst = nrows * D / 1024;
     for (int i = wave; i < ninst; i += 4) {
@@ -146,47 +148,61 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       dma16(src + (gr * rs32 + 16u * (uint32_t)(slot ^ code_key<D>(r))), tile + i * 1024);
     }
   };
-  auto dma_wide = [&](uint8_t* tile, const uint8_t* src, int row0, bool xq) {
-    constexpr int NI = WT / 1024;
+  // the query tiles: instruction k of this wave is tile instruction wave + 4k;
+  // its row and swizzled column are the same for every tile (loop-invariant)
+  constexpr int NIC = CT / 1024 / 4;     // code-tile instructions per wave
+  constexpr int NIW = WT / 1024 / 4;     // bf16-tile instructions per wave
+  // byte offsets: row r of a code tile is r * rs bytes from row 0 (bf16 tiles 2 r rs)
+  uint32_t crow[NIC], wrow[NIW], ccol[NIC], wcol[NIW], xcol[NIW];
 #pragma unroll
-    for (int i = wave; i < NI; i += 4) {
-      const int o = i * 1024 + 16 * lane;
-      const int r = o / (2 * D), slot = (o % (2 * D)) >> 4;
-      const uint32_t gr = (uint32_t)min(row0 + r, L - 1);
-      const int key = xq ? xq_key<D>(r) : wide_key<D>(r);
-      dma16(src + (2u * gr * rs32 + 16u * (uint32_t)(slot ^ key)), tile + i * 1024);
-    }
-  };
-  auto dma_planes = [&](uint8_t* tile, int row0) {
-    const size_t mi = hT + min(row0 + lane, L - 1);
-    for (int pl = wave; pl < NPLANES; pl += 4) {
-      const void* src = pl == 0 ? (const void*)(a.row_max + mi)
-                      : pl == 1 ? (const void*)(a.il8 + mi)
-                      : pl == 2 ? (const void*)(a.delta + mi)
-                      : pl == 3 ? (const void*)(a.dq_sigma + mi) : (const void*)(a.qexps + mi);
-      dma4(src, tile + pl * BWD_BQ * 4);
-    }
-  };
+  for (int k = 0; k < NIC; ++k) {
+    const int o = (wave + 4 * k) * 1024 + 16 * lane;
+    crow[k] = (uint32_t)(o / D) * rs32;
+    ccol[k] = 16u * (uint32_t)(((o % D) >> 4) ^ code_key<D>(o / D));
+  }
+#pragma unroll
+  for (int k = 0; k < NIW; ++k) {
+    const int o = (wave + 4 * k) * 1024 + 16 * lane;
+    const int r = o / (2 * D), slot = (o % (2 * D)) >> 4;
+    wrow[k] = 2u * (uint32_t)r * rs32;
+    wcol[k] = 16u * (uint32_t)(slot ^ wide_key<D>(r));
+    xcol[k] = 16u * (uint32_t)(slot ^ xq_key<D>(r));
+  }
+  const uint32_t last_c = (uint32_t)(L - 1) * rs32;       // the document's last row
+  const uint32_t last_w = 2u * last_c;
+  const int* const planes[NPLANES] = {a.kofs + hT, reinterpret_cast<const int*>(a.il8) + hT,
+                                      reinterpret_cast<const int*>(a.delta) + hT, a.dq_sigma + hT, a.qexps + hT};
   auto issue_tile = [&](auto Bc, int qt) {
     constexpr int B = decltype(Bc)::value;
     const int q0 = qt * BWD_BQ;
-    dma_codes(B ? sQ1 : sQ0, q_doc, q0, BWD_BQ);
-    dma_codes(B ? sO1 : sO0, do_doc, q0, BWD_BQ);
-    dma_wide(B ? sG1 : sG0, g_doc, q0, false);
-    if constexpr (PATH == 1) dma_wide(B ? sX1 : sX0, x_doc, q0, true);
-    dma_planes(B ? sR1 : sR0, q0);
+    const uint32_t q0c = (uint32_t)q0 * rs32, q0w = 2u * q0c;   // uniform
+#pragma unroll
+    for (int k = 0; k < NIC; ++k) {
+      const uint32_t off = min(q0c + crow[k], last_c) + ccol[k];
+      dma16(q_doc + off, (B ? sQ1 : sQ0) + (wave + 4 * k) * 1024);
+      dma16(do_doc + off, (B ? sO1 : sO0) + (wave + 4 * k) * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+      const uint32_t rowb = min(q0w + wrow[k], last_w);
+      dma16(g_doc + (rowb + wcol[k]), (B ? sG1 : sG0) + (wave + 4 * k) * 1024);
+      if constexpr (PATH == 1) dma16(x_doc + (rowb + xcol[k]), (B ? sX1 : sX0) + (wave + 4 * k) * 1024);
+    }
+    const int mrow = min(q0 + lane, L - 1);
+    for (int pl = wave; pl < NPLANES; pl += 4) dma4(planes[pl] + mrow, (B ? sR1 : sR0) + pl * BWD_BQ * 4);
   };
 
   // ---- per item: the key tile (for K~^T of dQ) and the first query tile
   const int qt_first = k0 / BWD_BQ;
   const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
-  dma_codes(sKQ, k_doc, k0, BWD_BK);
+  dma_codes(sK, k_doc, k0, BWD_BK);
   issue_tile(std::integral_constant<int, 0>{}, qt_first);
   if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
 
-  // ---- per wave: K~ (or the mixed path's bf16 K), V~ (block and per-key) as
-  // B operands (lane = key)
-  v8i kreg[PATH ? 1 : NS], vreg[NS], vkreg[NS];
+  // ---- per wave: K~ (or the mixed path's bf16 K) and V~ block codes as B
+  // operands (lane = key); the per-key V~ codes are loaded on the diagonal
+  // block only
+  v8i kreg[PATH ? 1 : NS], vreg[NS];
   v8bf kb16[PATH ? D / 16 : 1];
   int ke = E8M0_BIAS, ve = E8M0_BIAS, vke = E8M0_BIAS;
   float tqk = 1.f;
@@ -198,7 +214,6 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       if constexpr (PATH == 0)
         kreg[s] = cat8(ld16(a.k_codes + ro + 64 * s + 16 * hh), ld16(a.k_codes + ro + 64 * s + 32 + 16 * hh));
       vreg[s] = cat8(ld16(a.v_codes + ro + 64 * s + 16 * hh), ld16(a.v_codes + ro + 64 * s + 32 + 16 * hh));
-      vkreg[s] = cat8(ld16(a.v_key_codes + ro + 64 * s + 16 * hh), ld16(a.v_key_codes + ro + 64 * s + 32 + 16 * hh));
     }
     if constexpr (PATH == 1) {
 #pragma unroll
@@ -210,7 +225,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     vke = a.v_key_exp[mi];
     if (!kv) {    // keys past the document: zero operands
 #pragma unroll
-      for (int s = 0; s < NS; ++s) vreg[s] = vkreg[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int s = 0; s < NS; ++s) vreg[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
       if constexpr (PATH == 0) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) kreg[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -221,36 +236,71 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     }
   }
   const int e_key = vke - E8M0_BIAS;
+  // per-key V~ codes of this lane's key (B operand of dP on the diagonal block)
+  auto vkey = [&](int s2) {
+    const uint8_t* vr = a.v_key_codes + doc0 + (size_t)min(j, L - 1) * rs + 64 * s2 + 16 * hh;
+    return kv ? cat8(ld16(vr), ld16(vr + 32)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  };
   full_barrier();
 
-  // K~^T slice for dQ^T: wave -> d-slice ds; lane (d row, half hh), K = keys
+  // dQ^T: wave -> d-slice ds; K~^T of that slice is read from sK each step
   const int ds = wave % ND;
-  v8i ktreg[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    ktreg[ks] = cat8(tr_code16<D>(sKQ, 64 * ks, 32 * ds + colg, lane),
-                     tr_code16<D>(sKQ, 64 * ks + 32, 32 * ds + colg, lane));
 
   v16f dk[ND], dv[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) { dk[db] = v16f{}; dv[db] = v16f{}; }
 
-  // fp16 dQ partial of query tile qtp (staged in sKQ) -> memory-side atomics,
-  // one wave instruction per row pair run
+  // fp16 dQ partial of query tile qtp (staged in sKQ) -> memory-side atomics.
+  // One wave instruction covers whole rows (one row for d = 128, two for 64),
+  // rows wave, wave + 4, ...; the per-lane parts of both addresses are fixed.
+  constexpr int RPI = 128 / D;                       // rows per wave instruction
+  const int frow = RPI == 1 ? 0 : lane >> 5;
+  const int fpair = RPI == 1 ? lane : lane & 31;
+  const uint16_t* const fsrc = reinterpret_cast<const uint16_t*>(sKQ) + frow * DQS + 2 * fpair;
+  const uint32_t fdst = 2u * (uint32_t)frow * rs32 + 4u * (uint32_t)fpair;
   auto flush_dq = [&](int qtp) {
-    constexpr int PAIRS = D / 2;
+    constexpr int NIT = BWD_BQ / (4 * RPI);
     const int q0p = qtp * BWD_BQ;
     const int nqp = min(BWD_BQ, L - q0p);
-    const uint16_t* sdQ = reinterpret_cast<const uint16_t*>(sKQ);
-    for (int idx = tid; idx < BWD_BQ * PAIRS; idx += BWD_THREADS) {
-      const int row = idx / PAIRS, pr = idx % PAIRS;
-      if (row < nqp) {
-        const v2h hv = *reinterpret_cast<const v2h*>(sdQ + row * DQS + 2 * pr);
+    v2h hv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      hv[it] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 4 * it) * DQS);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int row0 = RPI * (wave + 4 * it);        // uniform
+      if (row0 + frow < nqp)
         __builtin_amdgcn_global_atomic_fadd_v2f16(
-            reinterpret_cast<v2h*>(dq_doc + (2u * ((uint32_t)(q0p + row) * rs32) + 4u * (uint32_t)pr)), hv);
-      }
+            reinterpret_cast<v2h*>(dq_doc + (2u * (uint32_t)(q0p + row0) * rs32 + fdst)), hv[it]);
     }
   };
+
+  // per-lane LDS offsets of the operand reads (loop-invariant; every swizzle
+  // key has period 16 or less in the row, and the reads start at rows that
+  // are multiples of 16)
+  const int ck = code_key<D>(n);
+  int offA[NS][2];                 // row n, 16-byte chunks 4s + hh and 4s + 2 + hh
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) offA[s2][e] = n * D + (((4 * s2 + 2 * e + hh) ^ ck) << 4);
+  int offK[ND];                    // 8-bit transpose reads of the Q~ tile (dK operand)
+  {
+    const int pp = lane & 15, b = pp >> 1;
+    const int t = 8 * (b >> 2) + 4 * hh + (b & 3);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) offK[db] = code_off<D>(t, 32 * db + colg + 8 * (pp & 1));
+  }
+  int offG[ND][2];                 // 16-bit transpose reads of the G tile (dV operand)
+  {
+    const int pp = lane & 15, e = pp >> 2, s4 = pp & 3;
+    const int t = 4 * hh + e;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      offG[db][0] = wide_off<D>(t, 2 * (32 * db + colg + 4 * s4));
+      offG[db][1] = wide_off<D>(t + 8, 2 * (32 * db + colg + 4 * s4));
+    }
+  }
 
   auto step = [&](auto Bc, int qt) {
     constexpr int B = decltype(Bc)::value;
@@ -259,7 +309,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     const uint8_t* tG = B ? sG1 : sG0;
     const uint8_t* tX = B ? sX1 : sX0;
     const uint8_t* tR = B ? sR1 : sR0;
-    const int* pm = reinterpret_cast<const int*>(tR);
+    const int* pko = reinterpret_cast<const int*>(tR);
     const float* pil = reinterpret_cast<const float*>(tR + BWD_BQ * 4);
     const float* pdl = reinterpret_cast<const float*>(tR + 2 * BWD_BQ * 4);
     const int* psig = reinterpret_cast<const int*>(tR + 3 * BWD_BQ * 4);
@@ -288,14 +338,11 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
         v16f sacc = v16f{}, pacc = v16f{};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int row = 32 * qb + n;
           if constexpr (PATH == 0)
-            sacc = mfma_f8(cat8(ld16(tQ + code_off<D>(row, 64 * s + 16 * hh)),
-                                ld16(tQ + code_off<D>(row, 64 * s + 32 + 16 * hh))),
+            sacc = mfma_f8(cat8(ld16(tQ + 32 * qb * D + offA[s][0]), ld16(tQ + 32 * qb * D + offA[s][1])),
                            kreg[s], sacc, sqe, ke);
-          pacc = mfma_f8(cat8(ld16(tdO + code_off<D>(row, 64 * s + 16 * hh)),
-                              ld16(tdO + code_off<D>(row, 64 * s + 32 + 16 * hh))),
-                         dia ? vkreg[s] : vreg[s], pacc, sdoe, dia ? vke : ve);
+          pacc = mfma_f8(cat8(ld16(tdO + 32 * qb * D + offA[s][0]), ld16(tdO + 32 * qb * D + offA[s][1])),
+                         dia ? vkey(s) : vreg[s], pacc, sdoe, dia ? vke : ve);
         }
         if constexpr (PATH == 1) {
           const int row = 32 * qb + n;
@@ -312,7 +359,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int r0 = 32 * qb + 8 * g + 4 * hh;      // first of 4 consecutive query rows
-            const v4i mv = *reinterpret_cast<const v4i*>(pm + r0);
+            const v4i kov = *reinterpret_cast<const v4i*>(pko + r0);
             const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
             const v4f dlv = *reinterpret_cast<const v4f*>(pdl + r0);
             float pf[4];
@@ -321,7 +368,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
               const int rr = 4 * g + r;
               const float x = sacc[rr] * c;
               const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-              pf[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + (8 - mv[r]));   // P 2^8
+              pf[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);   // P 2^8
               dsv[rr] = (pf[r] * ilv[r]) * (pacc[rr] - dlv[r]);
               amax = fmaxf(amax, fabsf(dsv[rr]));
             }
@@ -333,7 +380,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int r0 = 32 * qb + 8 * g + 4 * hh;
-            const v4i mv = *reinterpret_cast<const v4i*>(pm + r0);
+            const v4i kov = *reinterpret_cast<const v4i*>(pko + r0);
             const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
             const v4f dlv = *reinterpret_cast<const v4f*>(pdl + r0);
             float pf[4];
@@ -345,7 +392,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
               if (kv && j <= i && i < L) {
                 const float x = sacc[rr] * c;
                 const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + (8 - mv[r]));
+                const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
                 dsr = (p8 * ilv[r]) * (pacc[rr] - dlv[r]);
                 if (dia) {
                   const int vref = ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
@@ -363,7 +410,8 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
             pe[2 * g + 1] = (uint32_t)f32_to_bf16_bits(pf[2]) | ((uint32_t)f32_to_bf16_bits(pf[3]) << 16);
           }
         }
-        const int e = roundup_exp(wave_max(amax));
+        // amax >= 0, so its bits order like the values
+        const int e = roundup_exp(__int_as_float(wave_max_i(__float_as_int(amax))));
         eds[qb] = e;
         if (e >= -126) {
           const float sc2 = __builtin_amdgcn_ldexpf(1.0f, e);    // the convert divides by it
@@ -385,8 +433,13 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
           const v8bf av = __builtin_bit_cast(
               v8bf, v4i{(int)pe[4 * ks], (int)pe[4 * ks + 1], (int)pe[4 * ks + 2], (int)pe[4 * ks + 3]});
 #pragma unroll
-          for (int db = 0; db < ND; ++db)
-            dv[db] = mfma_bf16(av, tr_wide_bf16x8<D>(tG, 32 * qb, ks, 32 * db + colg, lane), dv[db]);
+          for (int db = 0; db < ND; ++db) {
+            const uint8_t* g0 = tG + (32 * qb + 16 * ks) * 2 * D;
+            const v4s lo = lds_tr16(g0 + offG[db][0]);
+            const v4s hi = lds_tr16(g0 + offG[db][1]);
+            dv[db] = mfma_bf16(av, __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                               dv[db]);
+          }
         }
       }
     }
@@ -396,9 +449,11 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       const int sa = (hh == 0 ? eds[0] : eds[1]) + E8M0_BIAS;
       const int sb = pqx[32 * hh] & 255;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-        dk[db] = mfma_f8(adk, cat8(tr_code16<D>(tQ, 0, 32 * db + colg, lane), tr_code16<D>(tQ, 32, 32 * db + colg, lane)),
-                         dk[db], sa, sb);
+      for (int db = 0; db < ND; ++db) {
+        const uint8_t* q0p = tQ + offK[db];
+        const v2i a0 = lds_tr8(q0p), a1 = lds_tr8(q0p + 16 * D), a2 = lds_tr8(q0p + 32 * D), a3 = lds_tr8(q0p + 48 * D);
+        dk[db] = mfma_f8(adk, v8i{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]}, dk[db], sa, sb);
+      }
     }
     // dS^ to LDS key-major: row = key of the tile, 4 consecutive queries per dword
     {
@@ -419,7 +474,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const v8i bq = cat8(tr_block16(sdSK, DSK, 64 * ks, 32 * qb + colg, lane),
                             tr_block16(sdSK, DSK, 64 * ks + 32, 32 * qb + colg, lane));
-        acc = mfma_f8(ktreg[ks], bq, acc, sKeB[2 * ks + hh], sEds[qb][2 * ks + hh] + E8M0_BIAS);
+        const v8i kt = cat8(tr_code16<D>(sK, 64 * ks, 32 * ds + colg, lane),
+                            tr_code16<D>(sK, 64 * ks + 32, 32 * ds + colg, lane));
+        acc = mfma_f8(kt, bq, acc, sKeB[2 * ks + hh], sEds[qb][2 * ks + hh] + E8M0_BIAS);
       }
       // prescaled fp16 partial of this query row into LDS (4 consecutive d per store)
       const int iq = 32 * qb + n;
@@ -471,7 +528,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
   const char* base = static_cast<const char*>(plan);
   BwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.bwd_offset),
             in.q_codes, in.k_codes, in.v_codes, in.v_key_codes, in.k_exp, in.v_exp, in.v_key_exp,
-            in.row_max, in.il8, in.delta, in.dq_sigma, in.qexps, in.do_codes,
+            in.kofs, in.il8, in.delta, in.dq_sigma, in.qexps, in.do_codes,
             static_cast<const uint16_t*>(in.g), static_cast<uint16_t*>(in.dq_acc), in.dk_f32,
             static_cast<uint16_t*>(in.dv), static_cast<const uint16_t*>(in.q_x),
             static_cast<const uint16_t*>(in.k_x), in.qk_scale};

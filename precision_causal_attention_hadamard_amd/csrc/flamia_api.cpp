@@ -79,6 +79,7 @@ BwdLayout bwd_layout(const flamia_attn_desc* d) {
   size_t off = 0;
   b.do_codes = off; off = align_up(off + E);
   b.do_exp = off;   off = align_up(off + M);
+  b.kofs = off;     off = align_up(off + 4 * M);
   b.delta = off;    off = align_up(off + 4 * M);
   b.il8 = off;      off = align_up(off + 4 * M);
   b.qexps = off;    off = align_up(off + 4 * M);
@@ -192,26 +193,27 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
 }
 
 flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
-                                   const float* row_sum, const void* dout, void* ws, hipStream_t stream) {
+                                   const int32_t* row_max, const float* row_sum, const void* dout, void* ws,
+                                   hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !o || !row_sum || !dout || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !o || !row_max || !row_sum || !dout || !ws) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
   uint8_t* w = static_cast<uint8_t*>(ws);
-  return hip_status(launch_quant_do(p, dout, o, row_sum, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_ref_exp,
-                                    w + b.do_codes, w + b.do_exp, reinterpret_cast<float*>(w + b.delta),
+  return hip_status(launch_quant_do(p, dout, o, row_max, row_sum, qt->q_exp, qt->k_exp, qt->v_exp,
+                                    qt->v_ref_exp, w + b.do_codes, w + b.do_exp, reinterpret_cast<int*>(w + b.kofs),
+                                    reinterpret_cast<float*>(w + b.delta),
                                     reinterpret_cast<float*>(w + b.il8), reinterpret_cast<int*>(w + b.qexps),
                                     w + b.g, reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
 }
 
-flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt,
-                                   const int32_t* row_max, const float* row_sum, void* dv, void* ws,
+flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dv, void* ws,
                                    hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !row_max || !row_sum || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
@@ -224,7 +226,7 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   in.k_exp = qt->k_exp;
   in.v_exp = qt->v_exp;
   in.v_key_exp = qt->v_key_exp;
-  in.row_max = row_max;
+  in.kofs = reinterpret_cast<const int*>(w + b.kofs);
   in.il8 = reinterpret_cast<const float*>(w + b.il8);
   in.delta = reinterpret_cast<const float*>(w + b.delta);
   in.dq_sigma = reinterpret_cast<const int*>(w + b.dq_sigma);
@@ -260,9 +262,9 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
   if (s != FLAMIA_OK) return s;
   if (!qt_complete(desc, qt) || !o || !row_max || !row_sum || !dout || !dq || !dk || !dv || !ws)
     return FLAMIA_ERR_INVALID_ARG;
-  s = flamia_attn_bwd_prep(desc, qt, o, row_sum, dout, ws, stream);
+  s = flamia_attn_bwd_prep(desc, qt, o, row_max, row_sum, dout, ws, stream);
   if (s != FLAMIA_OK) return s;
-  s = flamia_attn_bwd_main(desc, qt, row_max, row_sum, dv, ws, stream);
+  s = flamia_attn_bwd_main(desc, qt, dv, ws, stream);
   if (s != FLAMIA_OK) return s;
   return flamia_attn_bwd_finish(desc, dq, dk, ws, stream);
 }

@@ -20,7 +20,7 @@ struct PlanLayout {
 
 // Byte offsets of the backward workspace.
 struct BwdLayout {
-  size_t do_codes, do_exp, delta, il8, qexps, g, dq_sigma, dq_acc, dk_f32, bytes;
+  size_t do_codes, do_exp, kofs, delta, il8, qexps, g, dq_sigma, dq_acc, dk_f32, bytes;
 };
 
 struct Problem {
@@ -48,9 +48,10 @@ hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, cons
                             uint8_t* q_exp, uint8_t* k_exp, uint8_t* v_exp, uint8_t* v_key_exp,
                             uint8_t* v_ref_exp, const Fp4Operands& f4, hipStream_t stream);
 
-hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const float* row_sum,
-                           const uint8_t* q_exp, const uint8_t* k_exp, const uint8_t* v_exp,
-                           const uint8_t* v_ref_exp, uint8_t* do_codes, uint8_t* do_exp, float* delta,
+hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const int* row_max,
+                           const float* row_sum, const uint8_t* q_exp, const uint8_t* k_exp,
+                           const uint8_t* v_exp, const uint8_t* v_ref_exp, uint8_t* do_codes,
+                           uint8_t* do_exp, int* kofs, float* delta,
                            float* il8, int* qexps, void* g, int* dq_sigma, void* dq_acc, hipStream_t stream);
 
 hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout& pl,
@@ -63,7 +64,7 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
 struct BwdInputs {
   const uint8_t *q_codes, *k_codes, *v_codes, *v_key_codes;
   const uint8_t *k_exp, *v_exp, *v_key_exp;
-  const int* row_max;      // [H, T]
+  const int* kofs;         // [H, T] 8 - integer row maximum
   const float* il8;        // [H, T] 2^-8 / l
   const float* delta;      // [H, T]
   const int* dq_sigma;     // [H, T]

@@ -285,10 +285,12 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 template <int D>
 __global__ void __launch_bounds__(QUANT_THREADS)
 quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
-                const float* __restrict__ row_sum, const uint8_t* __restrict__ q_exp,
+                const int* __restrict__ row_max, const float* __restrict__ row_sum,
+                const uint8_t* __restrict__ q_exp,
                 const uint8_t* __restrict__ k_exp, const uint8_t* __restrict__ v_exp,
                 const uint8_t* __restrict__ v_ref_exp, uint8_t* __restrict__ do_codes,
-                uint8_t* __restrict__ do_exp, float* __restrict__ delta, float* __restrict__ il8,
+                uint8_t* __restrict__ do_exp, int* __restrict__ kofs, float* __restrict__ delta,
+                float* __restrict__ il8,
                 int* __restrict__ qexps, uint16_t* __restrict__ g, int* __restrict__ dq_sigma,
                 uint16_t* __restrict__ dq_acc) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -360,6 +362,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
           do_exp[mi] = (uint8_t)(e + E8M0_BIAS);
           delta[mi] = dsum;
           il8[mi] = ginv;
+          kofs[mi] = 8 - row_max[mi];    // -P_EXP - m~: P 2^8 = exp2(fract S') 2^(floor S' + kofs)
           qexps[mi] = (int)q_exp[mi] | ((e + E8M0_BIAS) << 8) | ((int)v_ref_exp[mi] << 16);
           // |dQ partial sum| <= 2.2 d 448^3 2^(e_dO + e_V + e_K) < 2^(27.6 + log2 d + ...);
           // the prescale keeps it below 2^15 in fp16
@@ -397,16 +400,17 @@ hipError_t launch_amax_qk(const Problem& p, const void* q, const void* k, float*
   return hipGetLastError();
 }
 
-hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const float* row_sum,
-                           const uint8_t* q_exp, const uint8_t* k_exp, const uint8_t* v_exp,
-                           const uint8_t* v_ref_exp, uint8_t* do_codes, uint8_t* do_exp, float* delta,
+hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const int* row_max,
+                           const float* row_sum, const uint8_t* q_exp, const uint8_t* k_exp,
+                           const uint8_t* v_exp, const uint8_t* v_ref_exp, uint8_t* do_codes,
+                           uint8_t* do_exp, int* kofs, float* delta,
                            float* il8, int* qexps, void* g, int* dq_sigma, void* dq_acc, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK);
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)dout,
-                       (const uint16_t*)o, row_sum, q_exp, k_exp, v_exp, v_ref_exp, do_codes, do_exp,
-                       delta, il8, qexps, (uint16_t*)g, dq_sigma, (uint16_t*)dq_acc);
+                       (const uint16_t*)o, row_max, row_sum, q_exp, k_exp, v_exp, v_ref_exp, do_codes,
+                       do_exp, kofs, delta, il8, qexps, (uint16_t*)g, dq_sigma, (uint16_t*)dq_acc);
   };
   if (p.D == 64) args(quant_do_kernel<64>); else args(quant_do_kernel<128>);
   return hipGetLastError();

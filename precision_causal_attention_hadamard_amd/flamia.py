@@ -66,8 +66,8 @@ def load(path: str = LIB_PATH):
         "flamia_quantize": [dp, P, P, P, qp, P],
         "flamia_attn_fwd": [dp, qp, P, P, P, P, P],
         "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
-        "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P],
-        "flamia_attn_bwd_main": [dp, qp, P, P, P, P, P],
+        "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P, P],
+        "flamia_attn_bwd_main": [dp, qp, P, P, P],
         "flamia_attn_bwd_finish": [dp, P, P, P, P],
         "flamia_tile_config": [I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
         "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I)],
@@ -135,14 +135,15 @@ def attn_bwd(desc, qt: QTensors, o, row_max, row_sum, dout, dq, dk, dv, ws, stre
                                   _stream(stream)), "flamia_attn_bwd")
 
 
-def attn_bwd_prep(desc, qt: QTensors, o, row_sum, dout, ws, stream=None):
-    _check(load().flamia_attn_bwd_prep(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_sum),
-                                       _ptr(dout), _ptr(ws), _stream(stream)), "flamia_attn_bwd_prep")
+def attn_bwd_prep(desc, qt: QTensors, o, row_max, row_sum, dout, ws, stream=None):
+    _check(load().flamia_attn_bwd_prep(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
+                                       _ptr(row_sum), _ptr(dout), _ptr(ws), _stream(stream)),
+           "flamia_attn_bwd_prep")
 
 
-def attn_bwd_main(desc, qt: QTensors, row_max, row_sum, dv, ws, stream=None):
-    _check(load().flamia_attn_bwd_main(ctypes.byref(desc), ctypes.byref(qt), _ptr(row_max), _ptr(row_sum),
-                                       _ptr(dv), _ptr(ws), _stream(stream)), "flamia_attn_bwd_main")
+def attn_bwd_main(desc, qt: QTensors, dv, ws, stream=None):
+    _check(load().flamia_attn_bwd_main(ctypes.byref(desc), ctypes.byref(qt), _ptr(dv), _ptr(ws),
+                                       _stream(stream)), "flamia_attn_bwd_main")
 
 
 def attn_bwd_finish(desc, dq, dk, ws, stream=None):
@@ -207,8 +208,8 @@ class TrainingCall:
                  self.dv, self.bws, stream)
 
     def backward_staged(self, stream=None):
-        attn_bwd_prep(self.desc, self.qt, self.o, self.row_sum, self.do, self.bws, stream)
-        attn_bwd_main(self.desc, self.qt, self.row_max, self.row_sum, self.dv, self.bws, stream)
+        attn_bwd_prep(self.desc, self.qt, self.o, self.row_max, self.row_sum, self.do, self.bws, stream)
+        attn_bwd_main(self.desc, self.qt, self.dv, self.bws, stream)
         attn_bwd_finish(self.desc, self.dq, self.dk, self.bws, stream)
 
     def step(self, stream=None):
