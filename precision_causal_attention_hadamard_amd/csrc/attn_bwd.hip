@@ -258,17 +258,18 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   const int fpair = RPI == 1 ? lane : lane & 31;
   const uint16_t* const fsrc = reinterpret_cast<const uint16_t*>(sKQ) + frow * DQS + 2 * fpair;
   const uint32_t fdst = 2u * (uint32_t)frow * rs32 + 4u * (uint32_t)fpair;
-  auto flush_dq = [&](int qtp) {
-    constexpr int NIT = BWD_BQ / (4 * RPI);
+  // (in two halves, so the atomics are spread over the step)
+  auto flush_dq = [&](int qtp, int half) {
+    constexpr int NIT = BWD_BQ / (8 * RPI);
     const int q0p = qtp * BWD_BQ;
     const int nqp = min(BWD_BQ, L - q0p);
     v2h hv[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
-      hv[it] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 4 * it) * DQS);
+      hv[it] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 4 * (it + NIT * half)) * DQS);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int row0 = RPI * (wave + 4 * it);        // uniform
+      const int row0 = RPI * (wave + 4 * (it + NIT * half));    // uniform
       if (row0 + frow < nqp)
         __builtin_amdgcn_global_atomic_fadd_v2f16(
             reinterpret_cast<v2h*>(dq_doc + (2u * (uint32_t)(q0p + row0) * rs32 + fdst)), hv[it]);
@@ -317,9 +318,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     const int q0 = qt * BWD_BQ;
     const int nq = min(BWD_BQ, L - q0);
 
-    // the next tile streams in while this one is computed; last step's dQ goes out
-    if (qt + 1 < qt_end) issue_tile(std::integral_constant<int, 1 - B>{}, qt + 1);
-    if (qt > qt_first) flush_dq(qt - 1);
+    // the next tile streams in while this one is computed (issued once the
+    // first block's products are under way); last step's dQ goes out in two
+    // halves between the blocks
 
     int dsc[2][4];
     int eds[2];
@@ -330,12 +331,12 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       eds[qb] = -127;
 #pragma unroll
       for (int g = 0; g < 4; ++g) dsc[qb][g] = 0;
+      const bool dia = QB == KB;
+      const bool fast = !dia && 32 * qb + 32 <= nq;   // no mask, no fold
+      v16f sacc = v16f{}, pacc = v16f{};
       if (act) {
-        const bool dia = QB == KB;
-        const bool fast = !dia && 32 * qb + 32 <= nq;   // no mask, no fold
         const int qx = pqx[32 * qb];
         const int sqe = qx & 255, sdoe = (qx >> 8) & 255;
-        v16f sacc = v16f{}, pacc = v16f{};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           if constexpr (PATH == 0)
@@ -352,8 +353,11 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) sacc[rr] = sacc[rr] * tqk;
         }
-        float dsv[16];
-        uint32_t pe[8];    // bf16 pairs of P^_eff * 2^8, accumulator register order
+      }
+      if (qb == 0 && qt + 1 < qt_end) issue_tile(std::integral_constant<int, 1 - B>{}, qt + 1);
+      float dsv[16];
+      uint32_t pe[8];      // bf16 pairs of P^_eff * 2^8, accumulator register order
+      if (act) {
         float amax = 0.f;
         if (fast) {
 #pragma unroll
@@ -427,6 +431,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
             dsc[qb][g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(dsv[4 * g], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 1], -e),
                                    __builtin_amdgcn_ldexpf(dsv[4 * g + 2], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 3], -e));
         }
+      }
+      if (qt > qt_first) flush_dq(qt - 1, qb);
+      if (act) {
         // dV += P^_eff^T G  (two K-steps of 16 queries)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -503,7 +510,8 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     step(std::integral_constant<int, 1>{}, qt);
     if (++qt >= qt_end) break;
   }
-  flush_dq(qt_end - 1);
+  flush_dq(qt_end - 1, 0);
+  flush_dq(qt_end - 1, 1);
 
   // ---- item end: dK (scaled, fp32 staging) and dV (bf16)
   if (wave_active) {
@@ -522,6 +530,435 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave backward (MXFP8 path): two waves per SIMD on the same item.
+// Wave w owns key block kb = w & 3 and, of each 64-query tile, query block
+// qh = w >> 2.  It forms S, dP, P, dS and the dS^ codes of its 32 x 32 block
+// (the block exponent is a whole-wave reduction, as above), and adds
+// P^_eff^T G over its 32 queries to a dV accumulator for all of d; the two
+// waves of a key block sum their dV at the end of the item.  dK needs both
+// query blocks: after the barrier that publishes the dS^ codes key-major, each
+// wave of the pair forms dK for half of d over all 64 queries.  dQ^T is one
+// (d slice, query block) pair per wave.  K~ and V~ of the item stay in LDS and
+// are read as operands each step.
+template <int D>
+__global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
+  constexpr int DSK = BWD_BQ + 16;           // key-major dS^ row stride (bytes)
+  constexpr int NS = D / 64;
+  constexpr int ND = D / 32;
+  constexpr int NDK = ND / 2;                // dK d-blocks per wave
+  constexpr int CT = BWD_BQ * D;             // bytes of a query code tile
+  constexpr int WT = BWD_BQ * 2 * D;         // bytes of a query bf16 tile
+  constexpr int RT = NPLANES * BWD_BQ * 4;   // bytes of the per-row planes
+  constexpr int DQS = D + 4;                 // fp16 dQ staging row stride (elements)
+  static_assert(WT >= 64 * ND * 16 * 4, "a key block's dV partial sums fit one bf16 tile buffer");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[BWD_BK * D];         // K~ tile of the item
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[BWD_BK * D];         // V~ block codes of the item
+  // query-tile double buffers (distinct arrays, so reads of one buffer never
+  // wait for the loads into the other); after the last step the bf16 pair
+  // holds the dV partial sums
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ0[CT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ1[CT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sO0[CT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sO1[CT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sG0[WT];
+  __shared__ __attribute__((aligned(1024))) uint8_t sG1[WT];
+  __shared__ __attribute__((aligned(256))) uint8_t sR0[RT];
+  __shared__ __attribute__((aligned(256))) uint8_t sR1[RT];
+  __shared__ __attribute__((aligned(16))) uint8_t sdSK[BWD_BK * DSK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sKQ[BWD_BQ * DQS * 2];  // fp16 dQ partial of a step
+  __shared__ int sEds[2][4];
+  __shared__ int sKeB[4];
+
+  const Problem& p = a.p;
+  const int H = p.H, T = p.T;
+  const int tile_idx = blockIdx.x / H, head = blockIdx.x % H;
+  if (tile_idx >= a.counts[1]) return;
+  const int2 it = a.items[tile_idx];
+  const int doc = it.x, u = it.y;
+  const int s_d = p.cu[doc];
+  const int L = p.cu[doc + 1] - s_d;
+  const int k0 = u * BWD_BK;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
+  const int kb = wave & 3, qh = wave >> 2;
+  const int n = lane & 31, hh = lane >> 5;
+  const int colg = 16 * ((lane >> 4) & 1);
+  const int j = k0 + 32 * kb + n;             // this lane's key (document-local)
+  const bool kv = j < L;
+  const bool kb_active = k0 + 32 * kb < L;
+  const int KB = 4 * u + kb;
+  const size_t rs = (size_t)H * D;
+  const size_t hT = (size_t)head * T + s_d;
+  const size_t doc0 = (size_t)s_d * rs + (size_t)head * D;
+  const uint32_t rs32 = (uint32_t)rs;
+  const float c = p.c_log2;
+  const uint8_t* q_doc = a.q_codes + doc0;
+  const uint8_t* do_doc = a.do_codes + doc0;
+  const uint8_t* g_doc = reinterpret_cast<const uint8_t*>(a.g + doc0);
+  uint8_t* dq_doc = reinterpret_cast<uint8_t*>(a.dq_acc + doc0);
+
+  // ---- item start: K~ and V~ tiles (128 rows), swizzled code layout
+  {
+    constexpr int NI = BWD_BK * D / 1024;
+    for (int i = wave; i < 2 * NI; i += 8) {
+      const int ii = i % NI;
+      const int o = ii * 1024 + 16 * lane;
+      const int r = o / D, slot = (o % D) >> 4;
+      const uint32_t off = (uint32_t)min(k0 + r, L - 1) * rs32 + 16u * (uint32_t)(slot ^ code_key<D>(r));
+      dma16((i < NI ? a.k_codes : a.v_codes) + doc0 + off, (i < NI ? sK : sV) + ii * 1024);
+    }
+  }
+  // ---- query tiles: code instruction `wave` (if any), bf16 instructions wave + 8 k, plane `wave`
+  constexpr int NIC = CT / 1024;              // code-tile instructions (8 or 4)
+  constexpr int NIW = WT / 1024 / 8;          // bf16-tile instructions per wave (2 or 1)
+  const bool has_c = wave < NIC;
+  uint32_t crow = 0, ccol = 0, wrow[NIW], wcol[NIW];
+  {
+    const int o = wave * 1024 + 16 * lane;
+    crow = (uint32_t)(o / D) * rs32;
+    ccol = 16u * (uint32_t)(((o % D) >> 4) ^ code_key<D>(o / D));
+  }
+#pragma unroll
+  for (int k = 0; k < NIW; ++k) {
+    const int o = (wave + 8 * k) * 1024 + 16 * lane;
+    const int r = o / (2 * D), slot = (o % (2 * D)) >> 4;
+    wrow[k] = 2u * (uint32_t)r * rs32;
+    wcol[k] = 16u * (uint32_t)(slot ^ wide_key<D>(r));
+  }
+  const uint32_t last_c = (uint32_t)(L - 1) * rs32, last_w = 2u * last_c;
+  const int* const plane = wave == 0 ? a.kofs + hT
+                         : wave == 1 ? reinterpret_cast<const int*>(a.il8) + hT
+                         : wave == 2 ? reinterpret_cast<const int*>(a.delta) + hT
+                         : wave == 3 ? a.dq_sigma + hT : a.qexps + hT;
+  auto issue_tile = [&](auto Bc, int qt) {
+    constexpr int B = decltype(Bc)::value;
+    const int q0 = qt * BWD_BQ;
+    const uint32_t q0c = (uint32_t)q0 * rs32, q0w = 2u * q0c;
+    if (has_c) {
+      const uint32_t off = min(q0c + crow, last_c) + ccol;
+      dma16(q_doc + off, (B ? sQ1 : sQ0) + wave * 1024);
+      dma16(do_doc + off, (B ? sO1 : sO0) + wave * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < NIW; ++k)
+      dma16(g_doc + (min(q0w + wrow[k], last_w) + wcol[k]), (B ? sG1 : sG0) + (wave + 8 * k) * 1024);
+    if (wave < NPLANES) dma4(plane + min(q0 + lane, L - 1), (B ? sR1 : sR0) + wave * BWD_BQ * 4);
+  };
+
+  const int qt_first = k0 / BWD_BQ;
+  const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
+  issue_tile(std::integral_constant<int, 0>{}, qt_first);
+  if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
+  int ke, ve, vke;
+  {
+    const size_t mi = hT + min(j, L - 1);
+    ke = a.k_exp[mi];
+    ve = a.v_exp[mi];
+    vke = a.v_key_exp[mi];
+  }
+  const int e_key = vke - E8M0_BIAS;
+  auto vkey = [&](int s2) {
+    const uint8_t* vr = a.v_key_codes + doc0 + (size_t)min(j, L - 1) * rs + 64 * s2 + 16 * hh;
+    return kv ? cat8(ld16(vr), ld16(vr + 32)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  };
+  full_barrier();
+
+  // per-lane LDS offsets (loop-invariant)
+  const int ck = code_key<D>(n);
+  int offA[NS][2];                 // row n (of a 32-row block), chunks 4s + hh and 4s + 2 + hh
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) offA[s2][e] = n * D + (((4 * s2 + 2 * e + hh) ^ ck) << 4);
+  int offK[NDK];                   // 8-bit transpose reads of the Q~ tile (dK operand), this wave's half of d
+  {
+    const int pp = lane & 15, b = pp >> 1;
+    const int t = 8 * (b >> 2) + 4 * hh + (b & 3);
+#pragma unroll
+    for (int e = 0; e < NDK; ++e) offK[e] = code_off<D>(t, 32 * (NDK * qh + e) + colg + 8 * (pp & 1));
+  }
+  int offG[ND][2];                 // 16-bit transpose reads of the G tile (dV operand)
+  {
+    const int pp = lane & 15, e = pp >> 2, s4 = pp & 3;
+    const int t = 4 * hh + e;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      offG[db][0] = wide_off<D>(t, 2 * (32 * db + colg + 4 * s4));
+      offG[db][1] = wide_off<D>(t + 8, 2 * (32 * db + colg + 4 * s4));
+    }
+  }
+  // operands of this wave's key block: K~ and V~ rows 32 kb + n
+  const uint8_t* const kbase = sK + 32 * kb * D;
+  const uint8_t* const vbase = sV + 32 * kb * D;
+
+  // dQ^T: wave -> (d slice, query block); d = 64 uses waves 0-3 only
+  const bool dq_wave = D == 128 || wave < 4;
+  const int dq_ds = D == 128 ? wave & 3 : wave & 1;
+  const int dq_qb = D == 128 ? wave >> 2 : (wave >> 1) & 1;
+
+  v16f dk[NDK], dv[ND];
+#pragma unroll
+  for (int e = 0; e < NDK; ++e) dk[e] = v16f{};
+#pragma unroll
+  for (int db = 0; db < ND; ++db) dv[db] = v16f{};
+
+  // fp16 dQ partial of query tile qtp -> memory-side atomics; rows wave, wave + 8, ...
+  constexpr int RPI = 128 / D;                       // rows per wave instruction
+  const int frow = RPI == 1 ? 0 : lane >> 5;
+  const int fpair = RPI == 1 ? lane : lane & 31;
+  const uint16_t* const fsrc = reinterpret_cast<const uint16_t*>(sKQ) + frow * DQS + 2 * fpair;
+  const uint32_t fdst = 2u * (uint32_t)frow * rs32 + 4u * (uint32_t)fpair;
+  auto flush_dq = [&](int qtp) {
+    constexpr int NIT = BWD_BQ / (8 * RPI);
+    const int q0p = qtp * BWD_BQ;
+    const int nqp = min(BWD_BQ, L - q0p);
+    v2h hv[NIT];
+#pragma unroll
+    for (int t2 = 0; t2 < NIT; ++t2) hv[t2] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 8 * t2) * DQS);
+#pragma unroll
+    for (int t2 = 0; t2 < NIT; ++t2) {
+      const int row0 = RPI * (wave + 8 * t2);        // uniform
+      if (row0 + frow < nqp)
+        __builtin_amdgcn_global_atomic_fadd_v2f16(
+            reinterpret_cast<v2h*>(dq_doc + (2u * (uint32_t)(q0p + row0) * rs32 + fdst)), hv[t2]);
+    }
+  };
+
+  auto step = [&](auto Bc, int qt) {
+    constexpr int B = decltype(Bc)::value;
+    const uint8_t* tQ = B ? sQ1 : sQ0;
+    const uint8_t* tdO = B ? sO1 : sO0;
+    const uint8_t* tG = B ? sG1 : sG0;
+    const uint8_t* tR = B ? sR1 : sR0;
+    const int* pko = reinterpret_cast<const int*>(tR);
+    const float* pil = reinterpret_cast<const float*>(tR + BWD_BQ * 4);
+    const float* pdl = reinterpret_cast<const float*>(tR + 2 * BWD_BQ * 4);
+    const int* psig = reinterpret_cast<const int*>(tR + 3 * BWD_BQ * 4);
+    const int* pqx = reinterpret_cast<const int*>(tR + 4 * BWD_BQ * 4);
+    const int q0 = qt * BWD_BQ;
+    const int nq = min(BWD_BQ, L - q0);
+    const int QB = 2 * qt + qh;
+    const bool act = kb_active && QB >= KB && 32 * qh < nq;
+    const bool dia = QB == KB;
+    const bool fast = !dia && 32 * qh + 32 <= nq;   // no mask, no fold
+    int dsc[4] = {0, 0, 0, 0};
+    int eds = -127;
+    v16f sacc = v16f{}, pacc = v16f{};
+    if (act) {
+      const int qx = pqx[32 * qh];
+      const int sqe = qx & 255, sdoe = (qx >> 8) & 255;
+      const uint8_t* qrow = tQ + 32 * qh * D;
+      const uint8_t* drow = tdO + 32 * qh * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sacc = mfma_f8(cat8(ld16(qrow + offA[s][0]), ld16(qrow + offA[s][1])),
+                       cat8(ld16(kbase + offA[s][0]), ld16(kbase + offA[s][1])), sacc, sqe, ke);
+        pacc = mfma_f8(cat8(ld16(drow + offA[s][0]), ld16(drow + offA[s][1])),
+                       dia ? vkey(s) : cat8(ld16(vbase + offA[s][0]), ld16(vbase + offA[s][1])), pacc, sdoe,
+                       dia ? vke : ve);
+      }
+    }
+    // the next tile streams in while this one is computed; last step's dQ goes out
+    if (qt + 1 < qt_end) issue_tile(std::integral_constant<int, 1 - B>{}, qt + 1);
+    if (qt > qt_first) flush_dq(qt - 1);
+    if (act) {
+      float dsv[16];
+      uint32_t pe[8];      // bf16 pairs of P^_eff * 2^8, accumulator register order
+      float amax = 0.f;
+      if (fast) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = 32 * qh + 8 * g + 4 * hh;
+          const v4i kov = *reinterpret_cast<const v4i*>(pko + r0);
+          const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
+          const v4f dlv = *reinterpret_cast<const v4f*>(pdl + r0);
+          float pf[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rr = 4 * g + r;
+            const float x = sacc[rr] * c;
+            const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
+            pf[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);   // P 2^8
+            dsv[rr] = (pf[r] * ilv[r]) * (pacc[rr] - dlv[r]);
+            amax = fmaxf(amax, fabsf(dsv[rr]));
+          }
+          const int code = cvt_fp8x4(pf[0], pf[1], pf[2], pf[3]);
+          pe[2 * g] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false));
+          pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, true));
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = 32 * qh + 8 * g + 4 * hh;
+          const v4i kov = *reinterpret_cast<const v4i*>(pko + r0);
+          const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
+          const v4f dlv = *reinterpret_cast<const v4f*>(pdl + r0);
+          float pf[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rr = 4 * g + r;
+            const int i = q0 + r0 + r;
+            float dsr = 0.f, pev = 0.f;
+            if (kv && j <= i && i < L) {
+              const float x = sacc[rr] * c;
+              const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
+              const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
+              dsr = (p8 * ilv[r]) * (pacc[rr] - dlv[r]);
+              if (dia) {
+                const int vref = ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
+                const int code = cvt_fp8x2(__builtin_amdgcn_ldexpf(p8, e_key - vref), 0.f);
+                pev = __builtin_amdgcn_ldexpf(fp8_value(code, 0), vref - e_key);
+              } else {
+                pev = fp8_value(cvt_fp8x2(p8, 0.f), 0);
+              }
+            }
+            dsv[rr] = dsr;
+            amax = fmaxf(amax, fabsf(dsr));
+            pf[r] = pev;
+          }
+          pe[2 * g] = (uint32_t)f32_to_bf16_bits(pf[0]) | ((uint32_t)f32_to_bf16_bits(pf[1]) << 16);
+          pe[2 * g + 1] = (uint32_t)f32_to_bf16_bits(pf[2]) | ((uint32_t)f32_to_bf16_bits(pf[3]) << 16);
+        }
+      }
+      // amax >= 0, so its bits order like the values
+      const int e = roundup_exp(__int_as_float(wave_max_i(__float_as_int(amax))));
+      eds = e;
+      if (e >= -126) {
+        const float sc2 = __builtin_amdgcn_ldexpf(1.0f, e);    // the convert divides by it
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, dsv[4 * g], dsv[4 * g + 1], sc2, false);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, dsv[4 * g + 2], dsv[4 * g + 3], sc2, true);
+          dsc[g] = __builtin_bit_cast(int, w);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          dsc[g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(dsv[4 * g], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 1], -e),
+                             __builtin_amdgcn_ldexpf(dsv[4 * g + 2], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 3], -e));
+      }
+      // dV += P^_eff^T G over this wave's 32 queries (two K-steps of 16)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const v8bf av = __builtin_bit_cast(
+            v8bf, v4i{(int)pe[4 * ks], (int)pe[4 * ks + 1], (int)pe[4 * ks + 2], (int)pe[4 * ks + 3]});
+        const uint8_t* g0 = tG + (32 * qh + 16 * ks) * 2 * D;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const v4s lo = lds_tr16(g0 + offG[db][0]);
+          const v4s hi = lds_tr16(g0 + offG[db][1]);
+          dv[db] = mfma_bf16(av, __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                             dv[db]);
+        }
+      }
+    }
+    // dS^ to LDS key-major: row = key, 4 consecutive queries per dword
+    {
+      uint8_t* row = sdSK + (32 * kb + n) * DSK + 32 * qh + 4 * hh;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *reinterpret_cast<int*>(row + 8 * g) = dsc[g];
+      if (lane == 0) sEds[qh][kb] = eds;
+    }
+    lds_barrier();
+    // dK += dS^^T Q~ over the 64 queries, this wave's half of d; lane half hh
+    // carries query block hh
+    if (kb_active) {
+      const uint8_t* row = sdSK + (32 * kb + n) * DSK + 4 * hh;
+      const v8i adk = v8i{*reinterpret_cast<const int*>(row), *reinterpret_cast<const int*>(row + 8),
+                          *reinterpret_cast<const int*>(row + 16), *reinterpret_cast<const int*>(row + 24),
+                          *reinterpret_cast<const int*>(row + 32), *reinterpret_cast<const int*>(row + 40),
+                          *reinterpret_cast<const int*>(row + 48), *reinterpret_cast<const int*>(row + 56)};
+      const int sa = sEds[hh][kb] + E8M0_BIAS;
+      const int sb = pqx[32 * hh] & 255;
+#pragma unroll
+      for (int e = 0; e < NDK; ++e) {
+        const uint8_t* qp = tQ + offK[e];
+        const v2i a0 = lds_tr8(qp), a1 = lds_tr8(qp + 16 * D), a2 = lds_tr8(qp + 32 * D), a3 = lds_tr8(qp + 48 * D);
+        dk[e] = mfma_f8(adk, v8i{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]}, dk[e], sa, sb);
+      }
+    }
+    // dQ^T slice: rows d in [32 ds, 32 ds + 32), columns = queries of block dq_qb, K = 128 keys
+    if (dq_wave && 32 * dq_qb < nq) {
+      v16f acc = v16f{};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const v8i bq = cat8(tr_block16(sdSK, DSK, 64 * ks, 32 * dq_qb + colg, lane),
+                            tr_block16(sdSK, DSK, 64 * ks + 32, 32 * dq_qb + colg, lane));
+        const v8i kt = cat8(tr_code16<D>(sK, 64 * ks, 32 * dq_ds + colg, lane),
+                            tr_code16<D>(sK, 64 * ks + 32, 32 * dq_ds + colg, lane));
+        acc = mfma_f8(kt, bq, acc, sKeB[2 * ks + hh], sEds[dq_qb][2 * ks + hh] + E8M0_BIAS);
+      }
+      const int iq = 32 * dq_qb + n;
+      const int sig = psig[iq];
+      uint16_t* dst = reinterpret_cast<uint16_t*>(sKQ) + iq * DQS + 32 * dq_ds + 4 * hh;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        v2h h0, h1;
+        h0[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g], -sig);
+        h0[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 1], -sig);
+        h1[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 2], -sig);
+        h1[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 3], -sig);
+        *reinterpret_cast<v2i*>(dst + 8 * g) = v2i{__builtin_bit_cast(int, h0), __builtin_bit_cast(int, h1)};
+      }
+    }
+    // the next tile has landed, this step's dQ partial is staged, the
+    // previous step's atomics are done
+    full_barrier();
+  };
+
+  for (int qt = qt_first;;) {
+    step(std::integral_constant<int, 0>{}, qt);
+    if (++qt >= qt_end) break;
+    step(std::integral_constant<int, 1>{}, qt);
+    if (++qt >= qt_end) break;
+  }
+  flush_dq(qt_end - 1);
+
+  // ---- item end: dK (scaled, fp32 staging) per half of d; the two
+  // query-half dV partials of each key block meet in the (now free) bf16
+  // tile buffers, key blocks 0-1 first, then 2-3
+  if (kb_active) {
+    const float sc = p.softmax_scale;
+#pragma unroll
+    for (int e = 0; e < NDK; ++e)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int jk = k0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+        if (jk < L) a.dk_f32[doc0 + (size_t)jk * rs + 32 * (NDK * qh + e) + n] = dk[e][rr] * sc;
+      }
+  }
+  for (int round = 0; round < 2; ++round) {
+    const bool mine = (kb >> 1) == round;
+    float* red = reinterpret_cast<float*>((kb & 1) ? sG1 : sG0) + lane * (ND * 16);
+    if (mine && qh == 1) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<v4f*>(red + 16 * db + 4 * q4) =
+              v4f{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]};
+    }
+    __syncthreads();
+    if (mine && qh == 0 && kb_active) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const v4f o = *reinterpret_cast<const v4f*>(red + 16 * db + 4 * q4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jk = k0 + 32 * kb + 8 * q4 + 4 * hh + r;
+            if (jk < L) a.dv[doc0 + (size_t)jk * rs + 32 * db + n] = f32_to_bf16_bits(dv[db][4 * q4 + r] + o[r]);
+          }
+        }
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl, const BwdInputs& in,
                            hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
@@ -537,7 +974,8 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
   if (p.path == 1) {
     if (p.D == 64) go(attn_bwd_kernel<64, 1>); else go(attn_bwd_kernel<128, 1>);
   } else {
-    if (p.D == 64) go(attn_bwd_kernel<64, 0>); else go(attn_bwd_kernel<128, 0>);
+    auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
+    if (p.D == 64) go8(attn_bwd8_kernel<64>); else go8(attn_bwd8_kernel<128>);
   }
   return hipGetLastError();
 }
