@@ -746,8 +746,15 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const bool fast = !dia && 32 * qh + 32 <= nq;   // no mask, no fold
     int dsc[4] = {0, 0, 0, 0};
     int eds = -127;
-    v16f sacc = v16f{}, pacc = v16f{};
+    v16f sacc = v16f{}, pacc;
     if (act) {
+      // dP accumulates onto -D, so the product yields dP - D directly
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const v4f dlv = *reinterpret_cast<const v4f*>(pdl + 32 * qh + 8 * g + 4 * hh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pacc[4 * g + r] = -dlv[r];
+      }
       const int qx = pqx[32 * qh];
       const int sqe = qx & 255, sdoe = (qx >> 8) & 255;
       const uint8_t* qrow = tQ + 32 * qh * D;
@@ -774,7 +781,6 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           const int r0 = 32 * qh + 8 * g + 4 * hh;
           const v4i kov = *reinterpret_cast<const v4i*>(pko + r0);
           const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
-          const v4f dlv = *reinterpret_cast<const v4f*>(pdl + r0);
           float pf[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -782,7 +788,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
             const float x = sacc[rr] * c;
             const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
             pf[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);   // P 2^8
-            dsv[rr] = (pf[r] * ilv[r]) * (pacc[rr] - dlv[r]);
+            dsv[rr] = (pf[r] * ilv[r]) * pacc[rr];
             amax = fmaxf(amax, fabsf(dsv[rr]));
           }
           const int code = cvt_fp8x4(pf[0], pf[1], pf[2], pf[3]);
@@ -795,7 +801,6 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           const int r0 = 32 * qh + 8 * g + 4 * hh;
           const v4i kov = *reinterpret_cast<const v4i*>(pko + r0);
           const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
-          const v4f dlv = *reinterpret_cast<const v4f*>(pdl + r0);
           float pf[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -806,7 +811,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
               const float x = sacc[rr] * c;
               const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
               const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
-              dsr = (p8 * ilv[r]) * (pacc[rr] - dlv[r]);
+              dsr = (p8 * ilv[r]) * pacc[rr];
               if (dia) {
                 const int vref = ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
                 const int code = cvt_fp8x2(__builtin_amdgcn_ldexpf(p8, e_key - vref), 0.f);
