@@ -6,7 +6,7 @@
 // the Hadamard option on, both are rotated back with the same normalised
 // Sylvester matrix as the forward rotation (it is symmetric and orthogonal):
 // fp32 butterflies h = 1, 2, ..., d/2 then one multiply by fp32(1/sqrt(d)).
-// Outputs are bf16 (round to nearest even).  One thread per (token, head) row.
+// Outputs are bf16 (round to nearest even).  Four lanes per (token, head) row.
 #include "flamia_device.hpp"
 #include "flamia_internal.hpp"
 
@@ -14,26 +14,45 @@ namespace flamia {
 
 constexpr int FIN_THREADS = 256;
 
+// Four lanes per row; lane part k holds elements [k d/4, (k+1) d/4).
+constexpr int FIN_PARTS = 4;
+
+// In-place normalised Hadamard transform of a row split over the four lanes
+// of a quad: butterflies h = 1 .. d/8 inside the lane, h = d/4 and d/2
+// between lanes of the quad (lane part bit 0, then bit 1), then one multiply
+// by fp32(1/sqrt(d)); the same butterflies in the same order as a whole-row
+// transform, so the same fp32 results.
 template <int D>
-__device__ __forceinline__ void fwht_row(float (&x)[D]) {
+__device__ __forceinline__ void fwht_quarter_row(float (&x)[D / 4], int part) {
+  constexpr int E = D / 4;
 #pragma unroll
-  for (int h = 1; h < D; h <<= 1)
+  for (int h = 1; h < E; h <<= 1)
 #pragma unroll
-    for (int a = 0; a < D; ++a)
+    for (int a = 0; a < E; ++a)
       if ((a & h) == 0) {
         const float lo = x[a], hi = x[a + h];
         x[a] = lo + hi;
         x[a + h] = lo - hi;
       }
+#pragma unroll
+  for (int a = 0; a < E; ++a) {      // h = d/4: partner lane part ^ 1
+    const float other = __int_as_float(dpp_move<0xb1>(__float_as_int(x[a])));   // quad_perm [1,0,3,2]
+    x[a] = (part & 1) ? other - x[a] : x[a] + other;
+  }
+#pragma unroll
+  for (int a = 0; a < E; ++a) {      // h = d/2: partner lane part ^ 2
+    const float other = __int_as_float(dpp_move<0x4e>(__float_as_int(x[a])));   // quad_perm [2,3,0,1]
+    x[a] = (part & 2) ? other - x[a] : x[a] + other;
+  }
   const float inv_sqrt_d = D == 64 ? 0.125f : __uint_as_float(0x3db504f3u);
 #pragma unroll
-  for (int a = 0; a < D; ++a) x[a] = x[a] * inv_sqrt_d;
+  for (int a = 0; a < E; ++a) x[a] = x[a] * inv_sqrt_d;
 }
 
-template <int D>
-__device__ __forceinline__ void store_bf16_row(uint16_t* __restrict__ dst, const float (&x)[D]) {
+template <int N>
+__device__ __forceinline__ void store_bf16(uint16_t* __restrict__ dst, const float (&x)[N]) {
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
+  for (int c = 0; c < N / 8; ++c) {
     v4i w;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -46,16 +65,19 @@ template <int D>
 __global__ void __launch_bounds__(FIN_THREADS)
 finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __restrict__ dq_sigma,
                 const float* __restrict__ dk_f32, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk) {
-  const size_t row = (size_t)blockIdx.x * FIN_THREADS + threadIdx.x;   // = t * H + h
+  constexpr int E = D / FIN_PARTS;
   const size_t rows = (size_t)p.T * p.H;
+  const size_t row = ((size_t)blockIdx.x * FIN_THREADS + threadIdx.x) / FIN_PARTS;   // = t * H + h
+  const int part = threadIdx.x & (FIN_PARTS - 1);
+  // whole quads leave together, so the lane moves below see only live lanes
   if (row >= rows) return;
   const int t = (int)(row / p.H), h = (int)(row % p.H);
-  const size_t off = row * D;
+  const size_t off = row * D + (size_t)part * E;
   {
-    float x[D];
+    float x[E];
     const int sig = dq_sigma[(size_t)h * p.T + t];
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
+    for (int c = 0; c < E / 8; ++c) {
       const v4i w = ld16(dq_acc + off + 8 * c);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -68,19 +90,19 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
         x[8 * c + 2 * k + 1] = __builtin_amdgcn_ldexpf((float)hi, sig) * p.softmax_scale;
       }
     }
-    if (p.hadamard) fwht_row<D>(x);
-    store_bf16_row<D>(dq + off, x);
+    if (p.hadamard) fwht_quarter_row<D>(x, part);
+    store_bf16<E>(dq + off, x);
   }
   {
-    float x[D];
+    float x[E];
 #pragma unroll
-    for (int c = 0; c < D / 4; ++c) {
+    for (int c = 0; c < E / 4; ++c) {
       const v4f w = *reinterpret_cast<const v4f*>(dk_f32 + off + 4 * c);
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
     }
-    if (p.hadamard) fwht_row<D>(x);
-    store_bf16_row<D>(dk + off, x);
+    if (p.hadamard) fwht_quarter_row<D>(x, part);
+    store_bf16<E>(dk + off, x);
   }
 }
 
@@ -88,7 +110,7 @@ hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_s
                            const float* dk_f32, void* dq, void* dk, hipStream_t stream) {
   const size_t rows = (size_t)p.T * p.H;
   if (rows == 0) return hipSuccess;
-  dim3 grid((unsigned)((rows + FIN_THREADS - 1) / FIN_THREADS));
+  dim3 grid((unsigned)((rows * FIN_PARTS + FIN_THREADS - 1) / FIN_THREADS));
   if (p.D == 64)
     hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(FIN_THREADS), 0, stream, p,
                        (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk);

@@ -161,7 +161,7 @@ amax_qk_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __rest
                float* __restrict__ qk_scale) {
   const int tensor = blockIdx.y;
   const uint16_t* src = tensor == 0 ? q : k;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
   const int c0 = blockIdx.x * TOKEN_BLOCK;
   const int H = p.H, T = p.T;
@@ -238,7 +238,7 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
   uint8_t* codes = tensor == 0 ? q_codes : (tensor == 1 ? k_codes : v_codes);
   uint8_t* exps = tensor == 0 ? q_exp : (tensor == 1 ? k_exp : v_exp);
   const bool rotate = p.hadamard && tensor < 2;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
   const int c0 = blockIdx.x * TOKEN_BLOCK;
   const int H = p.H, T = p.T;
@@ -293,7 +293,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
                 float* __restrict__ il8,
                 int* __restrict__ qexps, uint16_t* __restrict__ g, int* __restrict__ dq_sigma,
                 uint16_t* __restrict__ dq_acc) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
   const int c0 = blockIdx.x * TOKEN_BLOCK;
   const int H = p.H, T = p.T;
