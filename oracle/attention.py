@@ -77,6 +77,7 @@ class Numerics:
     path: str = "mxfp8"              # "mxfp8", or "mixed" (NVFP4 scores)
     fold: str = "causal"             # diagonal V: causal | block | none (block codes)
     softmax_scale: float | None = None
+    nvfp4_amax: tuple | None = None  # (Q, K) tensor max-abs when the inputs are a slice
 
 
 def scale_constants(d: int, softmax_scale: float | None):
@@ -182,8 +183,9 @@ def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
         qs_all, ks_all = qt["q"], qt["k"]
         if num.path == "mixed":
             from .nvfp4 import quantize_nvfp4
-            *_, qs_all = quantize_nvfp4(qt["q_rot"])
-            *_, ks_all = quantize_nvfp4(qt["k_rot"])
+            qa, ka = num.nvfp4_amax if num.nvfp4_amax is not None else (None, None)
+            *_, qs_all = quantize_nvfp4(qt["q_rot"], qa)
+            *_, ks_all = quantize_nvfp4(qt["k_rot"], ka)
         elif num.path != "mxfp8":
             raise ValueError(num.path)
     else:

@@ -43,13 +43,17 @@ def e4m3_round_up(x: float) -> float:
     return min(r, 448.0)
 
 
-def quantize_nvfp4(x):
+def quantize_nvfp4(x, amax=None):
     """x: ``[T, H, d]`` fp32-valued.  Returns (codes u8 [T,H,d] (0..15),
     group scales fp64 [T,H,d/16] (E4M3 values), tensor scale fp32, dequantized
-    fp64 [T,H,d])."""
+    fp64 [T,H,d]).  ``amax`` is the tensor's max-abs; pass it when x is a
+    slice of the tensor (groups are per token, so a slice quantized with the
+    whole tensor's amax is the slice of the whole tensor's quantization)."""
     x = np.asarray(x, dtype=np.float32)
     T, H, d = x.shape
-    amax = np.max(np.abs(x)) if x.size else np.float32(0.0)
+    if amax is None:
+        amax = np.max(np.abs(x)) if x.size else np.float32(0.0)
+    amax = np.float32(amax)
     t = (np.float32(amax) / np.float32(2688.0)).astype(np.float32) if amax > 0 else np.float32(1.0)
     six_t = np.float32(6.0 * np.float64(t))        # exact product, rounded once
     g = x.reshape(T, H, d // GROUP, GROUP)

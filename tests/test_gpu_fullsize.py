@@ -1,0 +1,146 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (the whole packed call on one GPU).
+
+Documents are independent sub-problems with document-local scales, so the
+oracle recomputes chosen (document, head) slices of the full call and the
+slice of every GPU output is compared with it: E4M3 codes, exponent bytes and
+the fold reference bit for bit; O, dQ, dK, dV to the bar of the small cases;
+the integer row maximum and l as there.  The mixed path's NVFP4 tensor scale is
+a whole-tensor quantity, so the oracle is given the tensors' max-abs.
+
+One exception, derived in test_oracle_conditioning.py: on the outlier
+workload the element-wise dQ comparison is ill-posed (rounding decisions of
+the bf16 O that an fp32 evaluation may take either way move the oracle's own
+dQ by more than 2%), so there dQ is held to the cosine bar, to one E4M3 step
+(1/8) in max-abs, and to at most 1% of query rows beyond the base bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from precision_causal_attention_hadamard_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = 2e-2
+TOL_COS = 0.999
+DQ_ILL_POSED_REL = 0.125          # one E4M3 step of a row's dominant dS term
+DQ_ILL_POSED_ROWS = 0.01          # fraction of query rows allowed beyond TOL_REL
+
+
+def metrics(got, want):
+    got = got.astype(np.float64).ravel()
+    want = want.astype(np.float64).ravel()
+    rel = np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30)
+    cos = got @ want / np.sqrt((got @ got) * (want @ want))
+    return rel, cos
+
+
+def run_full(lib, wl, causal_dq_scale=False):
+    dev = torch.device("cuda")
+    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
+    call = lib.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
+                            causal_dq_scale=causal_dq_scale, path=wl.path)
+    call.step()
+    torch.cuda.synchronize()
+    return call
+
+
+def doc_choice(cu, which):
+    lens = np.diff(np.asarray(cu))
+    if which == "longest":
+        return int(np.argmax(lens))
+    if which == "shortest":
+        return int(np.argmin(np.where(lens > 0, lens, 1 << 30)))
+    if which == "ragged":       # a mid-size document whose length is not a multiple of 32
+        cand = [i for i, L in enumerate(lens) if L % 32 and 200 <= L <= 3000]
+        return cand[len(cand) // 2]
+    return int(which)
+
+
+def oracle_slice(wl, doc, heads):
+    s, e = wl.cu_seqlens[doc], wl.cu_seqlens[doc + 1]
+    arrs = [t[s:e][:, heads].float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
+    amax = None
+    if wl.path:
+        assert not wl.hadamard      # the tensor max-abs below is that of the unrotated inputs
+        amax = (float(wl.q.float().abs().max()), float(wl.k.float().abs().max()))
+    num = A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8", nvfp4_amax=amax)
+    return A.training_call(*arrs, [0, e - s], num)
+
+
+def check_slice(call, wl, doc, heads, ref, outputs_only=False, dq_ill_posed=False):
+    s, e = wl.cu_seqlens[doc], wl.cu_seqlens[doc + 1]
+    hs = torch.tensor(heads)
+    if not outputs_only:
+        for f in ("q_codes", "k_codes", "v_codes", "v_key_codes"):
+            got = call.codes(f)[s:e].cpu()[:, hs].numpy()
+            np.testing.assert_array_equal(got, ref[f], err_msg=f)
+        for f in ("q_exp", "k_exp", "v_exp", "v_key_exp", "v_ref_exp"):
+            got = call.exps(f).cpu()[hs][:, s:e].numpy().astype(np.int64)
+            np.testing.assert_array_equal(got, ref[f] + 127, err_msg=f)
+    out, bad_rows = {}, 0.0
+    for n in ("o", "dq", "dk", "dv"):
+        got = getattr(call, n)[s:e].cpu()[:, hs].float().numpy()
+        assert np.all(np.isfinite(got)), n
+        out[n] = metrics(got, ref[n])
+        if n == "dq":
+            row_err = np.abs(got - ref[n]).max(axis=-1) / np.abs(ref[n]).max()
+            bad_rows = float((row_err > TOL_REL).mean())
+    print("[fullsize]   " + ", ".join(f"{k} rel={v[0]:.2e} cos={v[1]:.6f}" for k, v in out.items())
+          + f", dq rows beyond {TOL_REL}: {bad_rows:.2e}", flush=True)
+    for n, (rel, cos) in out.items():
+        assert cos >= TOL_COS, (n, cos)
+        if n == "dq" and dq_ill_posed:
+            assert rel <= DQ_ILL_POSED_REL and bad_rows <= DQ_ILL_POSED_ROWS, (n, rel, bad_rows)
+        else:
+            assert rel <= TOL_REL, (n, rel)
+    rm = call.row_max.cpu()[hs][:, s:e].numpy().astype(np.int64)
+    assert np.all(np.abs(rm - ref["row_max"]) <= 1)
+    assert (rm != ref["row_max"]).mean() <= 1e-3
+    np.testing.assert_allclose(call.row_sum.cpu()[hs][:, s:e].numpy(), ref["row_sum"], rtol=1e-3)
+    return out
+
+
+def report(tag, wl, doc, heads, m):
+    L = wl.cu_seqlens[doc + 1] - wl.cu_seqlens[doc]
+    print(f"[fullsize] {tag} doc {doc} (L={L}) heads {heads}: "
+          + ", ".join(f"{k} rel={v[0]:.2e} cos={v[1]:.6f}" for k, v in m.items()), flush=True)
+
+
+CASES = {      # workload, (document, heads) picks, dQ comparison ill-posed (outlier workload)
+    "config2_batched_outliers_hadamard": (2, [("1", [0, 15]), ("0", [7])], True),
+    "config3_packed_lognormal": (3, [("longest", [0, 9]), ("shortest", [4]), ("ragged", [13])], False),
+    "config5_mixed": (5, [("0", [5])], False),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_fullsize_sampled(gpu_lib, case):
+    cfg, picks, ill_posed = CASES[case]
+    print(f"[fullsize] {case}: building workload", flush=True)
+    wl = W.config(cfg)
+    call = run_full(gpu_lib, wl)
+    print(f"[fullsize] {case}: GPU call done, T={wl.total_tokens}, {len(wl.doc_lens)} documents", flush=True)
+    for which, heads in picks:
+        doc = doc_choice(wl.cu_seqlens, which)
+        ref = oracle_slice(wl, doc, heads)
+        report(case, wl, doc, heads, check_slice(call, wl, doc, heads, ref, dq_ill_posed=ill_posed))
+
+
+def test_fullsize_long_context_both_dq_scales(gpu_lib):
+    """Config 4 (two 12288-token documents plus short ones), run with the
+    default and with the causal dQ accumulator scale; both dQ results meet
+    the bar against the one oracle (the prescale only changes the fp16
+    accumulator's range, not the value computed)."""
+    wl = W.config(4)
+    print("[fullsize] config4: GPU calls", flush=True)
+    calls = {flag: run_full(gpu_lib, wl, causal_dq_scale=flag) for flag in (False, True)}
+    for which, heads in (("0", [3]), ("shortest", [11])):
+        doc = doc_choice(wl.cu_seqlens, which)
+        ref = oracle_slice(wl, doc, heads)
+        report("config4 default", wl, doc, heads, check_slice(calls[False], wl, doc, heads, ref))
+        report("config4 causal_dq_scale", wl, doc, heads,
+               check_slice(calls[True], wl, doc, heads, ref, outputs_only=True))

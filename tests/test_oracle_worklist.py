@@ -66,3 +66,20 @@ def test_nvfp4_round_up_scale_and_exact_dequant():
     prod = formats.e2m1_decode(codes) * np.repeat(scales, 16, axis=-1)
     np.testing.assert_array_equal(formats.fp16_round(prod), prod)
     np.testing.assert_allclose(deq, prod * np.float64(t))
+
+
+def test_nvfp4_slice_with_tensor_amax_equals_slice_of_tensor():
+    """Groups are per token: quantizing a block of rows with the whole
+    tensor's max-abs reproduces those rows of the whole-tensor quantization
+    (what the full-size sampled parity checks rely on)."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((96, 3, 64)).astype(np.float32)
+    x[40, 1, 5] = 37.0                          # the tensor maximum lies outside the slice
+    full = nvfp4.quantize_nvfp4(x)
+    sl = slice(50, 90)
+    part = nvfp4.quantize_nvfp4(x[sl, 1:], amax=np.max(np.abs(x)))
+    assert part[2] == full[2]
+    np.testing.assert_array_equal(part[0], full[0][sl, 1:])
+    np.testing.assert_array_equal(part[1], full[1][sl, 1:])
+    # without the tensor amax the slice gets its own (different) tensor scale
+    assert nvfp4.quantize_nvfp4(x[sl, 1:])[2] != full[2]
