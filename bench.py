@@ -31,7 +31,8 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E bandwidth (published)
 CPU_SAMPLE_HEADS = 8          # oracle sample: document 0, this many heads (about 10-20 s)
 METRIC = "fwd+bwd attention call ms & TFLOP/s incl. quantization; % of MFMA FP8 peak"
 KERNEL_SOURCES = {
-    "attn_bwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_bwd.hip",
+    "attn_bwd8_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_bwd.hip",   # MXFP8 path
+    "attn_bwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_bwd.hip",    # mixed path
     "attn_fwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_fwd.hip",
     "quant_qkv_kernel": "precision_causal_attention_hadamard_amd/csrc/quant.hip",
 }
@@ -90,12 +91,11 @@ def _pmc_rows(run_dir: str, counter: str):
     return rows
 
 
-def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str):
+def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str, kernel: str):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, both with --copy-calibration) into the traffic record of the
     backward kernel.  Each counter is scaled by what it reads for the 1 GiB
     device copy in the same run (known bytes: 1 GiB read, 1 GiB written)."""
-    kernel = "attn_bwd_kernel"
     rec = {"kernel": kernel, "workload": f"config{cfg}", "command": command,
            "source_sha": source_hash(KERNEL_SOURCES[kernel])}
     total = 0.0
@@ -159,9 +159,11 @@ def main():
                     help="no GPU: write the backward kernel's traffic record from two rocprofv3 --pmc runs")
     ap.add_argument("--pmc-command", default="",
                     help="with --write-traffic: the rocprofv3 command that made the runs")
+    ap.add_argument("--traffic-kernel", default="attn_bwd8_kernel",
+                    help="with --write-traffic: the kernel whose dispatches are summed")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic, args.config, args.pmc_command)
+        write_traffic(*args.write_traffic, args.config, args.pmc_command, args.traffic_kernel)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -224,7 +226,8 @@ def main():
     E = T * H * d
     fwd_mix, bwd_mix = product_mix(d, pairs, bool(wl.path))
     kernels = {
-        "attn_bwd": ("attn_bwd_kernel", "mfma", 10 * d * pairs, weighted_peak(bwd_mix)),
+        "attn_bwd": ("attn_bwd_kernel" if wl.path else "attn_bwd8_kernel", "mfma", 10 * d * pairs,
+                     weighted_peak(bwd_mix)),
         "attn_fwd": ("attn_fwd_kernel", "mfma", 4 * d * pairs, weighted_peak(fwd_mix)),
         "quantize": ("quant_qkv_kernel", "hbm", 10 * E + 5 * T * H, HBM_PEAK_GBS),
     }
@@ -235,7 +238,7 @@ def main():
         achieved, unit = work / t_dom / 1e12, "TFLOP/s"
     else:
         achieved, unit = work / t_dom / 1e9, "GB/s"
-    traffic = measured_traffic(kname, f"config{args.config}") if kname == "attn_bwd_kernel" else None
+    traffic = measured_traffic(kname, f"config{args.config}") if kname.startswith("attn_bwd") else None
     roofline = {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic,
                 "peak_note": "dtype-weighted: FP8 products at 5000, bf16 products at 2500 TFLOP/s"
