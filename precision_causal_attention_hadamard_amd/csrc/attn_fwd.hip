@@ -164,14 +164,14 @@ attn_fwd_kernel(FwdArgs a) {
       pvke = (kv && diag_tile) ? a.v_key_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int buf, bool diag_tile) {
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
       const int ch = tid + FWD_THREADS * c2;
       const int r = ch / (D / 16), c16 = ch % (D / 16);
       if constexpr (PATH == 0) st16(&sK[buf][r * KS + 16 * c16], pk[c2]);
       st16(&sV[buf][r * KS + 16 * c16], pv[c2]);
-      st16(&sVk[buf][r * KS + 16 * c16], pvk[c2]);
+      if (diag_tile) st16(&sVk[buf][r * KS + 16 * c16], pvk[c2]);   // read on diagonal blocks only
     }
     if constexpr (PATH == 1) {
       constexpr int CPR = D / 32;
@@ -191,7 +191,7 @@ attn_fwd_kernel(FwdArgs a) {
   };
 
   prefetch(0);
-  commit(0);
+  commit(0, 0 >= 2 * qt);
   __syncthreads();
 
   for (int kt = 0; kt <= kt_last; ++kt) {
@@ -241,7 +241,10 @@ attn_fwd_kernel(FwdArgs a) {
         }
       }
       if (act[0] || act[1]) {
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        {   // the other lane half holds the query's other 16 keys of each block
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+          tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         const int m_tile = tmax == -INFINITY ? M_NONE : (int)ceilf(tmax * c);
         const int m_new = max(m_run, m_tile);
         if (__any(m_new != m_run)) {
@@ -266,7 +269,7 @@ attn_fwd_kernel(FwdArgs a) {
               for (int r = 0; r < 4; ++r) {
                 const float x = st[kb][4 * g + r] * c;
                 const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                pv4[r] = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) + kofs);
+                pv4[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kofs);
                 l_run += pv4[r];
               }
               pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
@@ -283,7 +286,7 @@ attn_fwd_kernel(FwdArgs a) {
                 if (act[kb] && j <= i && j < L) {
                   const float x = st[kb][4 * g + r] * c;
                   const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                  pr = __builtin_amdgcn_ldexpf(e2, (int)floorf(x) + kofs);
+                  pr = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kofs);
                 }
                 l_run += pr;
                 pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
@@ -307,12 +310,13 @@ attn_fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (kt < kt_last) commit(buf ^ 1);
+    if (kt < kt_last) commit(buf ^ 1, kt + 1 >= 2 * qt);
     __syncthreads();
   }
 
   if (wave_active) {
-    const float l = __builtin_amdgcn_ldexpf(l_run + __shfl_xor(l_run, 32, 64), P_EXP);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    const float l = __builtin_amdgcn_ldexpf(l_run + (hh ? __uint_as_float(sw[0]) : __uint_as_float(sw[1])), P_EXP);
     if (iv) {
       const float inv = 1.0f / l;
       uint16_t* orow = a.o + (size_t)(s_d + i) * rs + (size_t)head * D;
