@@ -3,9 +3,10 @@
 // The pages build the schedule once per microbatch on the GPU with a
 // fixed-pass sort and hand items, costliest first, to the grid
 // ([Summary, §3.6.2 Load-Balanced Scheduling]; [Reading, 4.4] last bullet).
-// Here one workgroup enumerates every (document, tile), forms a 64-bit key
+// Here one workgroup per list enumerates every (document, tile), forms a 64-bit key
 //   (COST_MAX - cost) << 44 | doc << 20 | tile
-// and bitonic-sorts the keys in LDS.  The key is unique, so the order is the
+// and bitonic-sorts the keys (in LDS; within one wave for lists of at most
+// 64 tiles).  The key is unique, so the order is the
 // single correct one: cost descending, then document, then tile.  A tile
 // later expands to num_heads consecutive grid items (head ascending).  The
 // attention kernels read item blockIdx.x / H of the sorted list; the
@@ -21,94 +22,125 @@
 namespace flamia {
 
 constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 
-__device__ static void block_inclusive_scan(int* buf, int tid, int& total) {
-  // Hillis-Steele inclusive scan on PLAN_THREADS ints, then shift.
-  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-    int v = buf[tid];
-    int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] = v + add;
-    __syncthreads();
+// Inclusive scan of one int per thread over the workgroup: a scan inside each
+// wave, then one over the wave totals.  `wsum` holds PLAN_WAVES ints.
+__device__ static int block_inclusive_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(v, off, 64);
+    if (lane >= off) v += up;
   }
-  total = buf[PLAN_THREADS - 1];
+  if (lane == 63) wsum[wave] = v;
   __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int w = 0; w < PLAN_WAVES; ++w) {
+    const int t = wsum[w];
+    if (w < wave) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return v + before;
+}
+
+// One 64-bit key per lane of wave 0, sorted ascending across the wave with
+// the same bitonic network (for lists of at most 64 tiles).
+__device__ static unsigned long long wave_bitonic(unsigned long long key) {
+  const int lane = threadIdx.x & 63;
+  for (int k = 2; k <= 64; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const unsigned lo = __shfl_xor((unsigned)key, j, 64), hi = __shfl_xor((unsigned)(key >> 32), j, 64);
+      const unsigned long long other = ((unsigned long long)hi << 32) | lo;
+      const bool up = (lane & k) == 0, first = (lane & j) == 0;
+      // the lower lane of the pair keeps the smaller key when sorting up
+      const bool keep_min = (first == up);
+      key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
+    }
+  return key;
 }
 
 __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool fwd, int bq, int bk,
-                                    unsigned long long* keys, int* scan, int* count_out,
+                                    unsigned long long* keys, int* wsum, int* count_out,
                                     int2* __restrict__ out) {
   const int tid = threadIdx.x;
   int n_tiles = 0;
   // enumerate tiles, chunk of PLAN_THREADS documents at a time
   for (int base = 0; base < ndocs; base += PLAN_THREADS) {
-    int d = base + tid;
+    const int d = base + tid;
     int L = 0, n = 0;
     if (d < ndocs) {
       L = cu[d + 1] - cu[d];
       n = fwd ? (L + bq - 1) / bq : (L + bk - 1) / bk;
     }
-    scan[tid] = n;
-    __syncthreads();
     int total;
-    block_inclusive_scan(scan, tid, total);
-    int first = n_tiles + scan[tid] - n;
+    const int first = n_tiles + block_inclusive_scan(n, wsum, total) - n;
     for (int t = 0; t < n; ++t) {
       int cost;
       if (fwd) {
-        int e = min((t + 1) * bq, L);
+        const int e = min((t + 1) * bq, L);
         cost = (e - 1) / bk + 1;
       } else {
         cost = (L + bq - 1) / bq - (t * bk) / bq;
       }
-      unsigned long long key = ((unsigned long long)(COST_MAX - cost) << 44) |
-                               ((unsigned long long)d << 20) | (unsigned long long)t;
-      keys[first + t] = key;
+      keys[first + t] = ((unsigned long long)(COST_MAX - cost) << 44) |
+                        ((unsigned long long)d << 20) | (unsigned long long)t;
     }
     n_tiles += total;
-    __syncthreads();
   }
-  int n2 = 1;
-  while (n2 < n_tiles) n2 <<= 1;
-  for (int i = n_tiles + tid; i < n2; i += PLAN_THREADS) keys[i] = ~0ull;
   __syncthreads();
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += PLAN_THREADS) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          unsigned long long a = keys[i], b = keys[ixj];
-          bool up = (i & k) == 0;
-          if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
+  if (n_tiles <= 64) {
+    // small list: one wave, no workgroup barriers
+    if (tid < 64) {
+      const unsigned long long key = wave_bitonic(tid < n_tiles ? keys[tid] : ~0ull);
+      if (tid < n_tiles) out[tid] = make_int2((int)((key >> 20) & 0xffffffull), (int)(key & 0xfffffull));
+    }
+  } else {
+    int n2 = 1;
+    while (n2 < n_tiles) n2 <<= 1;
+    for (int i = n_tiles + tid; i < n2; i += PLAN_THREADS) keys[i] = ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += PLAN_THREADS) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const unsigned long long a = keys[i], b = keys[ixj];
+            const bool up = (i & k) == 0;
+            if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
+    }
+    for (int i = tid; i < n_tiles; i += PLAN_THREADS) {
+      const unsigned long long key = keys[i];
+      out[i] = make_int2((int)((key >> 20) & 0xffffffull), (int)(key & 0xfffffull));
     }
   }
-  for (int i = tid; i < n_tiles; i += PLAN_THREADS) {
-    unsigned long long key = keys[i];
-    out[i] = make_int2((int)((key >> 20) & 0xffffffull), (int)(key & 0xfffffull));
-  }
   if (tid == 0) *count_out = n_tiles;
-  __syncthreads();
 }
 
+// Workgroup 0 builds the forward list, workgroup 1 the backward list.
 __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restrict__ cu, int ndocs,
                                                             int* counts, int2* fwd_items,
                                                             int2* bwd_items, float* qk_scale) {
   __shared__ unsigned long long keys[PLAN_MAX_TILES];
-  __shared__ int scan[PLAN_THREADS];
-  build_sorted(cu, ndocs, true, FWD_BQ, FWD_BK, keys, scan, counts + 0, fwd_items);
-  build_sorted(cu, ndocs, false, BWD_BQ, BWD_BK, keys, scan, counts + 1, bwd_items);
-  if (threadIdx.x == 0) { counts[2] = 0; counts[3] = 0; }
+  __shared__ int wsum[PLAN_WAVES];
+  const bool fwd = blockIdx.x == 0;
+  build_sorted(cu, ndocs, fwd, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
+               counts + (fwd ? 0 : 1), fwd ? fwd_items : bwd_items);
+  if (fwd && threadIdx.x == 0) { counts[2] = 0; counts[3] = 0; }
   // mixed path: clear the tensor-amax slots before the amax pass runs
-  if (qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
+  if (fwd && qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
 }
 
 hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, float* qk_scale,
                        hipStream_t stream) {
   char* base = static_cast<char*>(plan);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu, ndocs,
+  hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs,
                      reinterpret_cast<int*>(base), reinterpret_cast<int2*>(base + pl.fwd_offset),
                      reinterpret_cast<int2*>(base + pl.bwd_offset), qk_scale);
   return hipGetLastError();

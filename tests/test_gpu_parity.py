@@ -100,8 +100,18 @@ def test_parity_causal_dq_scale(gpu_lib):
     check_outputs(call, ref)
 
 
-def test_worklists_match_oracle(gpu_lib):
-    wl = W.small_packed(34, [1, 300, 0, 129, 128, 1000, 17, 64], heads=3, head_dim=64)
+WORKLIST_DOCS = {
+    # under 64 tiles per list: the one-wave sort
+    "small": [1, 300, 0, 129, 128, 1000, 17, 64],
+    # above 64 tiles per list: the workgroup sort
+    "many": [int(x) for x in np.random.default_rng(36).integers(0, 700, size=40)] + [2500, 0, 33],
+}
+
+
+@pytest.mark.parametrize("docs", list(WORKLIST_DOCS))
+def test_worklists_match_oracle(gpu_lib, docs):
+    heads = 3 if docs == "small" else 1
+    wl = W.small_packed(34, WORKLIST_DOCS[docs], heads=heads, head_dim=64)
     call = run_gpu(gpu_lib, wl)
     fbq, fbk, bbq, bbk = gpu_lib.tile_config(64)
     fwd, bwd = call.plan_lists()
