@@ -530,6 +530,24 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   }
 }
 
+// Key-major dS^ tile of the eight-wave kernel: row = key (128 rows of 64 B),
+// 16-byte chunk c = 2 hh + qh holds the four dwords one lane of the wave of
+// query half qh wrote (queries 32 qh + 8 g + 4 hh + r, g = dword, r = byte).
+// Chunks are XOR-swizzled by a key of row bits 1-3 so that the 16-byte writes
+// (8-lane passes over 128 B), the 16-byte dK operand reads (16-lane passes
+// over 256 B) and the 8-bit transpose reads of the dQ operand (32-lane passes
+// over 256 B) all reach every bank once per pass.
+// Row of the fp16 dQ staging tile that holds query row q: rows with bit 4 set
+// trade places with their neighbour four rows away, so the 16 query rows one
+// 16-lane store pass writes (q = 8 a + b + const, a, b < 4, lanes split by
+// bit 4 of q) fall on 16 distinct 8-byte bank groups of the 264-byte rows.
+__device__ __forceinline__ int stage_row(int q) { return q ^ (((q >> 4) & 1) << 2); }
+
+__device__ __forceinline__ int dsk_off(int r, int chunk) {
+  const int key = (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
+  return r * 64 + ((chunk ^ key) << 4);
+}
+
 // ---------------------------------------------------------------------------
 // Eight-wave backward (MXFP8 path): two waves per SIMD on the same item.
 // Wave w owns key block kb = w & 3 and, of each 64-query tile, query block
@@ -543,7 +561,6 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 // are read as operands each step.
 template <int D>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
-  constexpr int DSK = BWD_BQ + 16;           // key-major dS^ row stride (bytes)
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
   constexpr int NDK = ND / 2;                // dK d-blocks per wave
@@ -566,7 +583,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sG1[WT];
   __shared__ __attribute__((aligned(256))) uint8_t sR0[RT];
   __shared__ __attribute__((aligned(256))) uint8_t sR1[RT];
-  __shared__ __attribute__((aligned(16))) uint8_t sdSK[BWD_BK * DSK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sdSK[BWD_BK * BWD_BQ];
   __shared__ __attribute__((aligned(1024))) uint8_t sKQ[BWD_BQ * DQS * 2];  // fp16 dQ partial of a step
   __shared__ int sEds[2][4];
   __shared__ int sKeB[4];
@@ -698,6 +715,13 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   const bool dq_wave = D == 128 || wave < 4;
   const int dq_ds = D == 128 ? wave & 3 : wave & 1;
   const int dq_qb = D == 128 ? wave >> 2 : (wave >> 1) & 1;
+  // dS^ operand of dQ^T: the lane's 16-lane group reads chunk dq_qb + 2 grp
+  // (query half dq_qb, writer lane half grp); column n is query iq
+  int offQ;
+  {
+    const int pp = lane & 15, b = pp >> 1;
+    offQ = dsk_off(8 * (b >> 2) + 4 * hh + (b & 3), dq_qb + 2 * ((lane >> 4) & 1)) + 8 * (pp & 1);
+  }
 
   v16f dk[NDK], dv[ND];
 #pragma unroll
@@ -717,7 +741,10 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const int nqp = min(BWD_BQ, L - q0p);
     v2h hv[NIT];
 #pragma unroll
-    for (int t2 = 0; t2 < NIT; ++t2) hv[t2] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 8 * t2) * DQS);
+    for (int t2 = 0; t2 < NIT; ++t2) {
+      const int row0 = RPI * (wave + 8 * t2);        // rows row0 + frow share bit 4
+      hv[t2] = *reinterpret_cast<const v2h*>(fsrc + stage_row(row0) * DQS);
+    }
 #pragma unroll
     for (int t2 = 0; t2 < NIT; ++t2) {
       const int row0 = RPI * (wave + 8 * t2);        // uniform
@@ -860,22 +887,15 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         }
       }
     }
-    // dS^ to LDS key-major: row = key, 4 consecutive queries per dword
-    {
-      uint8_t* row = sdSK + (32 * kb + n) * DSK + 32 * qh + 4 * hh;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) *reinterpret_cast<int*>(row + 8 * g) = dsc[g];
-      if (lane == 0) sEds[qh][kb] = eds;
-    }
+    // dS^ to LDS key-major: row = key, one 16-byte chunk per lane
+    st16(sdSK + dsk_off(32 * kb + n, 2 * hh + qh), v4i{dsc[0], dsc[1], dsc[2], dsc[3]});
+    if (lane == 0) sEds[qh][kb] = eds;
     lds_barrier();
     // dK += dS^^T Q~ over the 64 queries, this wave's half of d; lane half hh
     // carries query block hh
     if (kb_active) {
-      const uint8_t* row = sdSK + (32 * kb + n) * DSK + 4 * hh;
-      const v8i adk = v8i{*reinterpret_cast<const int*>(row), *reinterpret_cast<const int*>(row + 8),
-                          *reinterpret_cast<const int*>(row + 16), *reinterpret_cast<const int*>(row + 24),
-                          *reinterpret_cast<const int*>(row + 32), *reinterpret_cast<const int*>(row + 40),
-                          *reinterpret_cast<const int*>(row + 48), *reinterpret_cast<const int*>(row + 56)};
+      // K-block 0 = query half 0 (chunk 2 hh), K-block 1 = query half 1 (chunk 2 hh + 1)
+      const v8i adk = cat8(ld16(sdSK + dsk_off(32 * kb + n, 2 * hh)), ld16(sdSK + dsk_off(32 * kb + n, 2 * hh + 1)));
       const int sa = sEds[hh][kb] + E8M0_BIAS;
       const int sb = pqx[32 * hh] & 255;
 #pragma unroll
@@ -890,15 +910,16 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       v16f acc = v16f{};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const v8i bq = cat8(tr_block16(sdSK, DSK, 64 * ks, 32 * dq_qb + colg, lane),
-                            tr_block16(sdSK, DSK, 64 * ks + 32, 32 * dq_qb + colg, lane));
+        const uint8_t* b0 = sdSK + 64 * 64 * ks + offQ;
+        const v2i l0 = lds_tr8(b0), h0 = lds_tr8(b0 + 16 * 64), l1 = lds_tr8(b0 + 32 * 64), h1 = lds_tr8(b0 + 48 * 64);
+        const v8i bq = v8i{l0[0], l0[1], h0[0], h0[1], l1[0], l1[1], h1[0], h1[1]};
         const v8i kt = cat8(tr_code16<D>(sK, 64 * ks, 32 * dq_ds + colg, lane),
                             tr_code16<D>(sK, 64 * ks + 32, 32 * dq_ds + colg, lane));
         acc = mfma_f8(kt, bq, acc, sKeB[2 * ks + hh], sEds[dq_qb][2 * ks + hh] + E8M0_BIAS);
       }
-      const int iq = 32 * dq_qb + n;
+      const int iq = 32 * dq_qb + 8 * ((n & 15) >> 2) + 4 * ((lane >> 4) & 1) + (n & 3);
       const int sig = psig[iq];
-      uint16_t* dst = reinterpret_cast<uint16_t*>(sKQ) + iq * DQS + 32 * dq_ds + 4 * hh;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(sKQ) + stage_row(iq) * DQS + 32 * dq_ds + 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         v2h h0, h1;

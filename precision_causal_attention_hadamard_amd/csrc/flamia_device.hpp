@@ -241,8 +241,17 @@ __device__ __forceinline__ v8bf tr_bf16x8(const uint8_t* tile, int stride, int t
 //   of 32 rows).
 // Every key has period 16 in r or less, so row r + 16 shares the key of row r.
 
+// d = 128: with m = (r >> 1) & 7 = (m2 m1 m0), key = (m0 m2 m1).  Rows of one
+// parity get 8 distinct keys (16-byte reads of 16 rows), and the rows
+// {0-3, 8-11} (+4) that one half-wave's 8-bit transpose read touches get
+// disjoint chunk pairs.
 template <int D> __device__ __forceinline__ int code_key(int r) {
-  return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+  if constexpr (D == 128) {
+    const int m = (r >> 1) & 7;
+    return ((m & 1) << 2) | (((m >> 2) & 1) << 1) | ((m >> 1) & 1);
+  } else {
+    return (r >> 2) & 3;
+  }
 }
 template <int D> __device__ __forceinline__ int wide_key(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 1));
