@@ -62,7 +62,7 @@ struct BwdArgs {
   const uint8_t *k_exp, *v_exp, *v_key_exp;
   const int* kofs;        // [H, T] 8 - integer row maximum of the forward
   const float* il8;       // [H, T] 2^-8 / l
-  const float* delta;     // [H, T] D
+  const float* delta;     // [H, T] -D
   const int* dq_sigma;    // [H, T] dQ prescale exponent
   const int* qexps;       // [H, T] q_exp | do_exp << 8 | v_ref_exp << 16 (biased bytes)
   const uint8_t* do_codes;
@@ -373,7 +373,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
               const float x = sacc[rr] * c;
               const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
               pf[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);   // P 2^8
-              dsv[rr] = (pf[r] * ilv[r]) * (pacc[rr] - dlv[r]);
+              dsv[rr] = (pf[r] * ilv[r]) * (pacc[rr] + dlv[r]);
               amax = fmaxf(amax, fabsf(dsv[rr]));
             }
             const int code = cvt_fp8x4(pf[0], pf[1], pf[2], pf[3]);
@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
                 const float x = sacc[rr] * c;
                 const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
                 const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
-                dsr = (p8 * ilv[r]) * (pacc[rr] - dlv[r]);
+                dsr = (p8 * ilv[r]) * (pacc[rr] + dlv[r]);
                 if (dia) {
                   const int vref = ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
                   const int code = cvt_fp8x2(__builtin_amdgcn_ldexpf(p8, e_key - vref), 0.f);
@@ -773,23 +773,28 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const bool fast = !dia && 32 * qh + 32 <= nq;   // no mask, no fold
     int dsc[4] = {0, 0, 0, 0};
     int eds = -127;
-    v16f sacc = v16f{}, pacc;
+    v16f sacc, pacc;     // set (and read) only when act
     if (act) {
-      // dP accumulates onto -D, so the product yields dP - D directly
+      // dP accumulates onto -D (the plane holds -D), so the product yields dP - D directly
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const v4f dlv = *reinterpret_cast<const v4f*>(pdl + 32 * qh + 8 * g + 4 * hh);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pacc[4 * g + r] = -dlv[r];
+        for (int r = 0; r < 4; ++r) pacc[4 * g + r] = dlv[r];
       }
       const int qx = pqx[32 * qh];
       const int sqe = qx & 255, sdoe = (qx >> 8) & 255;
       const uint8_t* qrow = tQ + 32 * qh * D;
       const uint8_t* drow = tdO + 32 * qh * D;
+      auto s_step = [&](int s) {
+        const v8i qa = cat8(ld16(qrow + offA[s][0]), ld16(qrow + offA[s][1]));
+        const v8i kb8 = cat8(ld16(kbase + offA[s][0]), ld16(kbase + offA[s][1]));
+        sacc = s == 0 ? mfma_f8(qa, kb8, v16f{}, sqe, ke) : mfma_f8(qa, kb8, sacc, sqe, ke);
+      };
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        sacc = mfma_f8(cat8(ld16(qrow + offA[s][0]), ld16(qrow + offA[s][1])),
-                       cat8(ld16(kbase + offA[s][0]), ld16(kbase + offA[s][1])), sacc, sqe, ke);
+        s_step(s);
+        // diagonal block: per-key V~ codes
         pacc = mfma_f8(cat8(ld16(drow + offA[s][0]), ld16(drow + offA[s][1])),
                        dia ? vkey(s) : cat8(ld16(vbase + offA[s][0]), ld16(vbase + offA[s][1])), pacc, sdoe,
                        dia ? vke : ve);
@@ -862,7 +867,9 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         const float sc2 = __builtin_amdgcn_ldexpf(1.0f, e);    // the convert divides by it
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, dsv[4 * g], dsv[4 * g + 1], sc2, false);
+          // (the first convert's other half is overwritten by the second)
+          v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, dsv[4 * g]), dsv[4 * g],
+                                                          dsv[4 * g + 1], sc2, false);
           w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, dsv[4 * g + 2], dsv[4 * g + 3], sc2, true);
           dsc[g] = __builtin_bit_cast(int, w);
         }

@@ -70,7 +70,8 @@ __device__ __forceinline__ int cvt_fp8x2(float a, float b) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffff;
 }
 __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first convert's upper half is overwritten by the second
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 __device__ __forceinline__ float fp8_value(int packed, int byte) {

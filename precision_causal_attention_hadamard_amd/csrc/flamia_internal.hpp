@@ -66,7 +66,7 @@ struct BwdInputs {
   const uint8_t *k_exp, *v_exp, *v_key_exp;
   const int* kofs;         // [H, T] 8 - integer row maximum
   const float* il8;        // [H, T] 2^-8 / l
-  const float* delta;      // [H, T]
+  const float* delta;      // [H, T] -D
   const int* dq_sigma;     // [H, T]
   const int* qexps;        // [H, T] q_exp | do_exp << 8 | v_ref_exp << 16
   const uint8_t* do_codes;

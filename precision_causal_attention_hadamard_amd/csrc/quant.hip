@@ -360,7 +360,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
         if (hf == 0) {
           const size_t mi = (size_t)h * T + tok;
           do_exp[mi] = (uint8_t)(e + E8M0_BIAS);
-          delta[mi] = dsum;
+          delta[mi] = -dsum;           // the backward adds -D
           il8[mi] = ginv;
           kofs[mi] = 8 - row_max[mi];    // -P_EXP - m~: P 2^8 = exp2(fract S') 2^(floor S' + kofs)
           qexps[mi] = (int)q_exp[mi] | ((e + E8M0_BIAS) << 8) | ((int)v_ref_exp[mi] << 16);
