@@ -193,7 +193,7 @@ def main():
         if ev is not None: ev[2].record()
         flamia.attn_bwd_prep(call.desc, call.qt, call.o, call.row_max, call.row_sum, call.do, call.bws)
         if ev is not None: ev[3].record()
-        flamia.attn_bwd_main(call.desc, call.qt, call.dv, call.bws)
+        flamia.attn_bwd_main(call.desc, call.qt, call.dk, call.dv, call.bws)
         if ev is not None: ev[4].record()
         flamia.attn_bwd_finish(call.desc, call.dq, call.dk, call.bws)
         if ev is not None: ev[5].record()

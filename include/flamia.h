@@ -212,17 +212,19 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
  *   accumulator, and the per-query values the backward kernel reads with
  *   each query tile (8 - row_max, 2^-8 / row_sum, D, the prescale exponent,
  *   the Q / dO / fold-reference exponent bytes); all inside ws.  One launch.
- * flamia_attn_bwd_main -- the backward kernel: recompute, dV (written to dv),
- *   dK (fp32 staging in ws) and dQ (fp16 accumulator in ws); everything else
- *   it reads is in qt and ws.  One launch.
- * flamia_attn_bwd_finish -- dQ and dK to bf16 (rotated back when the
- *   Hadamard option is on).  One launch.
+ * flamia_attn_bwd_main -- the backward kernel: recompute, dV (bf16, written
+ *   to dv), dK and dQ (fp16 accumulator in ws).  On the MXFP8 path dK is
+ *   written to dk as bf16, rotated back when the Hadamard option is on; on
+ *   the mixed path it goes to fp32 staging in ws and dk is not written here.
+ *   Everything else it reads is in qt and ws.  One launch.
+ * flamia_attn_bwd_finish -- dQ to bf16 (rotated back when the Hadamard
+ *   option is on); on the mixed path also dK from its staging.  One launch.
  */
 flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qtensors* qt,
                                    const void* o, const int32_t* row_max, const float* row_sum,
                                    const void* dout, void* ws, hipStream_t stream);
-flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dv,
-                                   void* ws, hipStream_t stream);
+flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dk,
+                                   void* dv, void* ws, hipStream_t stream);
 flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, void* dq, void* dk, void* ws,
                                      hipStream_t stream);
 

@@ -68,7 +68,8 @@ struct BwdArgs {
   const uint8_t* do_codes;
   const uint16_t* g;
   uint16_t* dq_acc;
-  float* dk_f32;
+  float* dk_f32;          // mixed path: fp32 dK staging
+  uint16_t* dk;           // MXFP8 path: bf16 dK
   uint16_t* dv;
   const uint16_t *q_x, *k_x;   // mixed path: NVFP4 Q and K expanded to bf16
   const float* qk_scale;       // mixed path: [2], [3] tensor scales
@@ -950,19 +951,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   }
   flush_dq(qt_end - 1);
 
-  // ---- item end: dK (scaled, fp32 staging) per half of d; the two
-  // query-half dV partials of each key block meet in the (now free) bf16
-  // tile buffers, key blocks 0-1 first, then 2-3
-  if (kb_active) {
-    const float sc = p.softmax_scale;
-#pragma unroll
-    for (int e = 0; e < NDK; ++e)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int jk = k0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-        if (jk < L) a.dk_f32[doc0 + (size_t)jk * rs + 32 * (NDK * qh + e) + n] = dk[e][rr] * sc;
-      }
-  }
+  // ---- item end: the two query-half dV partials of each key block meet in
+  // the (now free) bf16 tile buffers, key blocks 0-1 first, then 2-3; then dK
   for (int round = 0; round < 2; ++round) {
     const bool mine = (kb >> 1) == round;
     float* red = reinterpret_cast<float*>((kb & 1) ? sG1 : sG0) + lane * (ND * 16);
@@ -990,6 +980,40 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
+  // dK times the softmax scale into a key-major fp32 tile (key block kb in
+  // one free buffer, 32 rows of d), then four lanes per key row rotate it
+  // back (Hadamard option) with the same butterflies as the dQ finaliser and
+  // store bf16 rows
+  {
+    float* const tile = reinterpret_cast<float*>(kb == 0 ? sK : kb == 1 ? sV : kb == 2 ? sG0 : sG1);
+    static_assert(BWD_BK / 4 * D * 4 <= BWD_BK * D && BWD_BK / 4 * D * 4 <= WT, "a key block of fp32 dK fits one buffer");
+    const float sc = p.softmax_scale;
+#pragma unroll
+    for (int e = 0; e < NDK; ++e)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        tile[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * D + 32 * (NDK * qh + e) + n] = dk[e][rr] * sc;
+  }
+  __syncthreads();
+  {
+    constexpr int E = D / 4;
+    const int row = tid >> 2, part = tid & 3;         // 128 key rows, four lanes each
+    const int jk = k0 + row;
+    if (jk < L) {                                     // whole quads leave together
+      const int rb = row >> 5;
+      const float* const src = reinterpret_cast<const float*>(rb == 0 ? sK : rb == 1 ? sV : rb == 2 ? sG0 : sG1) +
+                               (row & 31) * D + part * E;
+      float x[E];
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c) {
+        const v4f w = *reinterpret_cast<const v4f*>(src + 4 * c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
+      }
+      if (p.hadamard) fwht_quarter_row<D>(x, part);
+      store_bf16<E>(a.dk + doc0 + (size_t)jk * rs + part * E, x);
+    }
+  }
 }
 
 hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl, const BwdInputs& in,
@@ -1000,7 +1024,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
             in.q_codes, in.k_codes, in.v_codes, in.v_key_codes, in.k_exp, in.v_exp, in.v_key_exp,
             in.kofs, in.il8, in.delta, in.dq_sigma, in.qexps, in.do_codes,
             static_cast<const uint16_t*>(in.g), static_cast<uint16_t*>(in.dq_acc), in.dk_f32,
-            static_cast<uint16_t*>(in.dv), static_cast<const uint16_t*>(in.q_x),
+            static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv), static_cast<const uint16_t*>(in.q_x),
             static_cast<const uint16_t*>(in.k_x), in.qk_scale};
   dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };

@@ -2,7 +2,8 @@
 //
 // dQ: the fp16 accumulator holds dQ 2^-sigma (sigma per query block, chosen
 // so partial sums stay inside fp16); multiply back by 2^sigma and the
-// softmax scale.  dK: fp32 staging already carries the softmax scale.  With
+// softmax scale.  dK (mixed path only; the MXFP8 backward kernel writes bf16
+// dK itself): fp32 staging already carries the softmax scale.  With
 // the Hadamard option on, both are rotated back with the same normalised
 // Sylvester matrix as the forward rotation (it is symmetric and orthogonal):
 // fp32 butterflies h = 1, 2, ..., d/2 then one multiply by fp32(1/sqrt(d)).
@@ -13,58 +14,13 @@
 namespace flamia {
 
 constexpr int FIN_THREADS = 256;
-
-// Four lanes per row; lane part k holds elements [k d/4, (k+1) d/4).
-constexpr int FIN_PARTS = 4;
-
-// In-place normalised Hadamard transform of a row split over the four lanes
-// of a quad: butterflies h = 1 .. d/8 inside the lane, h = d/4 and d/2
-// between lanes of the quad (lane part bit 0, then bit 1), then one multiply
-// by fp32(1/sqrt(d)); the same butterflies in the same order as a whole-row
-// transform, so the same fp32 results.
-template <int D>
-__device__ __forceinline__ void fwht_quarter_row(float (&x)[D / 4], int part) {
-  constexpr int E = D / 4;
-#pragma unroll
-  for (int h = 1; h < E; h <<= 1)
-#pragma unroll
-    for (int a = 0; a < E; ++a)
-      if ((a & h) == 0) {
-        const float lo = x[a], hi = x[a + h];
-        x[a] = lo + hi;
-        x[a + h] = lo - hi;
-      }
-#pragma unroll
-  for (int a = 0; a < E; ++a) {      // h = d/4: partner lane part ^ 1
-    const float other = __int_as_float(dpp_move<0xb1>(__float_as_int(x[a])));   // quad_perm [1,0,3,2]
-    x[a] = (part & 1) ? other - x[a] : x[a] + other;
-  }
-#pragma unroll
-  for (int a = 0; a < E; ++a) {      // h = d/2: partner lane part ^ 2
-    const float other = __int_as_float(dpp_move<0x4e>(__float_as_int(x[a])));   // quad_perm [2,3,0,1]
-    x[a] = (part & 2) ? other - x[a] : x[a] + other;
-  }
-  const float inv_sqrt_d = D == 64 ? 0.125f : __uint_as_float(0x3db504f3u);
-#pragma unroll
-  for (int a = 0; a < E; ++a) x[a] = x[a] * inv_sqrt_d;
-}
-
-template <int N>
-__device__ __forceinline__ void store_bf16(uint16_t* __restrict__ dst, const float (&x)[N]) {
-#pragma unroll
-  for (int c = 0; c < N / 8; ++c) {
-    v4i w;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = (int)((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k]) | ((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k + 1]) << 16));
-    st16(dst + 8 * c, w);
-  }
-}
+constexpr int FIN_PARTS = 4;     // lanes per row
 
 template <int D>
 __global__ void __launch_bounds__(FIN_THREADS)
 finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __restrict__ dq_sigma,
-                const float* __restrict__ dk_f32, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk) {
+                const float* __restrict__ dk_f32, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
+                bool with_dk) {
   constexpr int E = D / FIN_PARTS;
   const size_t rows = (size_t)p.T * p.H;
   const size_t row = ((size_t)blockIdx.x * FIN_THREADS + threadIdx.x) / FIN_PARTS;   // = t * H + h
@@ -93,7 +49,7 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
     if (p.hadamard) fwht_quarter_row<D>(x, part);
     store_bf16<E>(dq + off, x);
   }
-  {
+  if (with_dk) {
     float x[E];
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) {
@@ -107,16 +63,16 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
 }
 
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
-                           const float* dk_f32, void* dq, void* dk, hipStream_t stream) {
+                           const float* dk_f32, void* dq, void* dk, bool with_dk, hipStream_t stream) {
   const size_t rows = (size_t)p.T * p.H;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((rows * FIN_PARTS + FIN_THREADS - 1) / FIN_THREADS));
   if (p.D == 64)
     hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(FIN_THREADS), 0, stream, p,
-                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk);
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk);
   else
     hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(FIN_THREADS), 0, stream, p,
-                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk);
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk);
   return hipGetLastError();
 }
 

@@ -209,11 +209,11 @@ flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qt
                                     w + b.g, reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
 }
 
-flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dv, void* ws,
-                                   hipStream_t stream) {
+flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dk, void* dv,
+                                   void* ws, hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !dk || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
@@ -235,6 +235,7 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   in.g = w + b.g;
   in.dq_acc = w + b.dq_acc;
   in.dk_f32 = reinterpret_cast<float*>(w + b.dk_f32);
+  in.dk = dk;
   in.dv = dv;
   in.q_x = qt->q_fp4_bf16;
   in.k_x = qt->k_fp4_bf16;
@@ -252,7 +253,7 @@ flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, void* dq, voi
   const BwdLayout b = bwd_layout(desc);
   uint8_t* w = static_cast<uint8_t*>(ws);
   return hip_status(launch_finalize(p, w + b.dq_acc, reinterpret_cast<const int*>(w + b.dq_sigma),
-                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, stream));
+                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, p.path == 1, stream));
 }
 
 flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
@@ -264,7 +265,7 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
     return FLAMIA_ERR_INVALID_ARG;
   s = flamia_attn_bwd_prep(desc, qt, o, row_max, row_sum, dout, ws, stream);
   if (s != FLAMIA_OK) return s;
-  s = flamia_attn_bwd_main(desc, qt, dv, ws, stream);
+  s = flamia_attn_bwd_main(desc, qt, dk, dv, ws, stream);
   if (s != FLAMIA_OK) return s;
   return flamia_attn_bwd_finish(desc, dq, dk, ws, stream);
 }

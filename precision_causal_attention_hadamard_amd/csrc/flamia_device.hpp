@@ -329,4 +329,53 @@ __device__ __forceinline__ v8bf tr_wide_bf16x8(const uint8_t* tile, int tok0, in
   return __builtin_bit_cast(v8bf, both);
 }
 
+// ---------------------------------------------------------------- bf16 rows, Hadamard back-rotation
+//
+// A (token, head) row of d fp32 values split over the four lanes of a quad,
+// lane part k holding elements [k d/4, (k+1) d/4).
+// In-place normalised Hadamard transform of a row split over the four lanes
+// of a quad: butterflies h = 1 .. d/8 inside the lane, h = d/4 and d/2
+// between lanes of the quad (lane part bit 0, then bit 1), then one multiply
+// by fp32(1/sqrt(d)); the same butterflies in the same order as a whole-row
+// transform, so the same fp32 results.
+template <int D>
+__device__ __forceinline__ void fwht_quarter_row(float (&x)[D / 4], int part) {
+  constexpr int E = D / 4;
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1)
+#pragma unroll
+    for (int a = 0; a < E; ++a)
+      if ((a & h) == 0) {
+        const float lo = x[a], hi = x[a + h];
+        x[a] = lo + hi;
+        x[a + h] = lo - hi;
+      }
+#pragma unroll
+  for (int a = 0; a < E; ++a) {      // h = d/4: partner lane part ^ 1
+    const float other = __int_as_float(dpp_move<0xb1>(__float_as_int(x[a])));   // quad_perm [1,0,3,2]
+    x[a] = (part & 1) ? other - x[a] : x[a] + other;
+  }
+#pragma unroll
+  for (int a = 0; a < E; ++a) {      // h = d/2: partner lane part ^ 2
+    const float other = __int_as_float(dpp_move<0x4e>(__float_as_int(x[a])));   // quad_perm [2,3,0,1]
+    x[a] = (part & 2) ? other - x[a] : x[a] + other;
+  }
+  const float inv_sqrt_d = D == 64 ? 0.125f : __uint_as_float(0x3db504f3u);
+#pragma unroll
+  for (int a = 0; a < E; ++a) x[a] = x[a] * inv_sqrt_d;
+}
+
+template <int N>
+__device__ __forceinline__ void store_bf16(uint16_t* __restrict__ dst, const float (&x)[N]) {
+#pragma unroll
+  for (int c = 0; c < N / 8; ++c) {
+    v4i w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (int)((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k]) | ((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k + 1]) << 16));
+    st16(dst + 8 * c, w);
+  }
+}
+
+
 }  // namespace flamia

@@ -72,7 +72,8 @@ struct BwdInputs {
   const uint8_t* do_codes;
   const void* g;
   void* dq_acc;
-  float* dk_f32;
+  float* dk_f32;           // mixed path: fp32 dK staging (the finaliser rotates and rounds it)
+  void* dk;                // MXFP8 path: bf16 dK, written by the backward kernel
   void* dv;
   const void *q_x, *k_x;   // mixed path only
   const float* qk_scale;   // mixed path only
@@ -82,6 +83,6 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
                            hipStream_t stream);
 
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
-                           const float* dk_f32, void* dq, void* dk, hipStream_t stream);
+                           const float* dk_f32, void* dq, void* dk, bool with_dk, hipStream_t stream);
 
 }  // namespace flamia

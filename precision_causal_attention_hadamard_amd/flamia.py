@@ -67,7 +67,7 @@ def load(path: str = LIB_PATH):
         "flamia_attn_fwd": [dp, qp, P, P, P, P, P],
         "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
         "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P, P],
-        "flamia_attn_bwd_main": [dp, qp, P, P, P],
+        "flamia_attn_bwd_main": [dp, qp, P, P, P, P],
         "flamia_attn_bwd_finish": [dp, P, P, P, P],
         "flamia_tile_config": [I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
         "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I)],
@@ -141,8 +141,8 @@ def attn_bwd_prep(desc, qt: QTensors, o, row_max, row_sum, dout, ws, stream=None
            "flamia_attn_bwd_prep")
 
 
-def attn_bwd_main(desc, qt: QTensors, dv, ws, stream=None):
-    _check(load().flamia_attn_bwd_main(ctypes.byref(desc), ctypes.byref(qt), _ptr(dv), _ptr(ws),
+def attn_bwd_main(desc, qt: QTensors, dk, dv, ws, stream=None):
+    _check(load().flamia_attn_bwd_main(ctypes.byref(desc), ctypes.byref(qt), _ptr(dk), _ptr(dv), _ptr(ws),
                                        _stream(stream)), "flamia_attn_bwd_main")
 
 
@@ -209,7 +209,7 @@ class TrainingCall:
 
     def backward_staged(self, stream=None):
         attn_bwd_prep(self.desc, self.qt, self.o, self.row_max, self.row_sum, self.do, self.bws, stream)
-        attn_bwd_main(self.desc, self.qt, self.dv, self.bws, stream)
+        attn_bwd_main(self.desc, self.qt, self.dk, self.dv, self.bws, stream)
         attn_bwd_finish(self.desc, self.dq, self.dk, self.bws, stream)
 
     def step(self, stream=None):
