@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="ordered dQ reduction (per-step partials, fixed-order fp16 sum) instead of atomics")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (known bytes) for counter calibration")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -180,7 +182,8 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
-                               causal_dq_scale=wl.causal_dq_scale, path=wl.path)
+                               causal_dq_scale=wl.causal_dq_scale, path=wl.path,
+                               deterministic=args.deterministic)
     T, H, d = call.shape
     pairs = wl.causal_pairs()
     flops = wl.flops()
@@ -195,7 +198,7 @@ def main():
         if ev is not None: ev[3].record()
         flamia.attn_bwd_main(call.desc, call.qt, call.dk, call.dv, call.bws)
         if ev is not None: ev[4].record()
-        flamia.attn_bwd_finish(call.desc, call.dq, call.dk, call.bws)
+        flamia.attn_bwd_finish(call.desc, call.qt, call.dq, call.dk, call.bws)
         if ev is not None: ev[5].record()
 
     for _ in range(args.warmup):
@@ -257,6 +260,7 @@ def main():
         "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": d,
                    "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
                    "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
+                   "deterministic": bool(args.deterministic),
                    "causal_pairs": pairs, "flops_per_step": flops},
         "pct_fp8_peak": 100.0 * value / FP8_PEAK_TFLOPS,
         "stage_ms": stage_ms, "event_ms_per_step": event_ms,

@@ -60,7 +60,8 @@ typedef enum {
 typedef struct flamia_attn_desc {
   int32_t total_tokens;         /* T >= 0 */
   int32_t num_docs;             /* >= 1 */
-  int32_t max_doc_len;          /* caller's upper bound of any document length, 1..T */
+  int32_t max_doc_len;          /* caller's upper bound of any document length, 1..T (0: T);
+                                   sizes the deterministic-mode dQ partial buffer */
   const int32_t* cu_seqlens;    /* device int32[num_docs + 1] */
   int32_t num_heads;            /* H >= 1 */
   int32_t head_dim;             /* d: 64 or 128 */
@@ -68,7 +69,12 @@ typedef struct flamia_attn_desc {
   int32_t path;                 /* 0 = MXFP8; 1 = mixed: QK^T (and its recompute) from NVFP4 Q/K */
   int32_t hadamard;             /* 1: rotate Q and K rows by the normalised Sylvester Hadamard matrix */
   int32_t causal_dq_scale;      /* 1: dQ accumulator prescale from causally visible blocks only */
-  int32_t deterministic;        /* must be 0 (dQ is reduced with fp16 atomics) */
+  int32_t deterministic;        /* 0: dQ reduced with fp16 atomics (order not fixed);
+                                   1: each (key tile, query tile) dQ partial is stored in its own
+                                   fp16 slot and the finaliser adds the slots of a query in fp16 in
+                                   ascending key-tile order -- bitwise reproducible
+                                   ([Reading, 6.3]: atomic dQ reduction by default, a slower
+                                   deterministic mode beside it) */
   float softmax_scale;          /* <= 0 selects 1/sqrt(head_dim) */
 } flamia_attn_desc;
 
@@ -128,8 +134,15 @@ typedef struct flamia_qtensors {
  *   qtensor_bytes : one buffer for flamia_qtensors (codes, exponents, plan).
  *   fwd_ws_bytes  : workspace of flamia_attn_fwd (may be 0; pass NULL then).
  *   bwd_ws_bytes  : workspace of flamia_attn_bwd (quantized dO, D, dO/l,
- *                   fp16 dQ accumulator, fp32 dK staging, prescale exponents).
- * Any output pointer may be NULL.  Host only; launches nothing.
+ *                   fp16 dQ accumulator, fp32 dK staging, prescale exponents;
+ *                   in deterministic mode also the dQ partial slots: 64 x d
+ *                   fp16 per head for at most ceil(T M / 16384) + ceil(3T / 128)
+ *                   + 2 num_docs steps, M = max_doc_len, a bound of the causal
+ *                   (key tile, query tile) steps of documents of at most M tokens).
+ * If the documents need more steps than max_doc_len promised, the
+ * deterministic backward drops the excess partials and sets word 2 of the
+ * plan (int32 at byte 8 of qtensors.plan) to 1; the library never reads it
+ * back itself.  Any output pointer may be NULL.  Host only; launches nothing.
  */
 flamia_status flamia_buffer_sizes(const flamia_attn_desc* desc, size_t* qtensor_bytes,
                                   size_t* fwd_ws_bytes, size_t* bwd_ws_bytes);
@@ -218,15 +231,17 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
  *   the mixed path it goes to fp32 staging in ws and dk is not written here.
  *   Everything else it reads is in qt and ws.  One launch.
  * flamia_attn_bwd_finish -- dQ to bf16 (rotated back when the Hadamard
- *   option is on); on the mixed path also dK from its staging.  One launch.
+ *   option is on; in deterministic mode first summed from the partial slots);
+ *   on the mixed path also dK from its staging.  Reads the plan in qt.  One
+ *   launch.
  */
 flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qtensors* qt,
                                    const void* o, const int32_t* row_max, const float* row_sum,
                                    const void* dout, void* ws, hipStream_t stream);
 flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dk,
                                    void* dv, void* ws, hipStream_t stream);
-flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, void* dq, void* dk, void* ws,
-                                     hipStream_t stream);
+flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dq,
+                                     void* dk, void* ws, hipStream_t stream);
 
 /*
  * flamia_tile_config -- tile sizes the kernels use for a head dim, i.e. the

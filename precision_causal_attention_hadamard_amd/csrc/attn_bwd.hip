@@ -71,6 +71,9 @@ struct BwdArgs {
   float* dk_f32;          // mixed path: fp32 dK staging
   uint16_t* dk;           // MXFP8 path: bf16 dK
   uint16_t* dv;
+  uint16_t* dq_part;      // deterministic mode: fp16 dQ partial slots
+  const int* det_base;    // deterministic mode: first step of each document
+  int det_cap;            // deterministic mode: steps per head in dq_part
   const uint16_t *q_x, *k_x;   // mixed path: NVFP4 Q and K expanded to bf16
   const float* qk_scale;       // mixed path: [2], [3] tensor scales
 };
@@ -260,6 +263,8 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   const uint16_t* const fsrc = reinterpret_cast<const uint16_t*>(sKQ) + frow * DQS + 2 * fpair;
   const uint32_t fdst = 2u * (uint32_t)frow * rs32 + 4u * (uint32_t)fpair;
   // (in two halves, so the atomics are spread over the step)
+  // deterministic mode: plain stores into the step's own partial slot instead
+  const int nq_doc = (L + BWD_BQ - 1) / BWD_BQ;
   auto flush_dq = [&](int qtp, int half) {
     constexpr int NIT = BWD_BQ / (8 * RPI);
     const int q0p = qtp * BWD_BQ;
@@ -268,6 +273,17 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
       hv[it] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 4 * (it + NIT * half)) * DQS);
+    if (p.deterministic) {
+      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc);
+      if (step >= a.det_cap) return;      // the plan flags the overflow
+      uint8_t* const slot = reinterpret_cast<uint8_t*>(a.dq_part) + ((size_t)step * H + head) * (BWD_BQ * D * 2);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int row0 = RPI * (wave + 4 * (it + NIT * half));
+        *reinterpret_cast<v2h*>(slot + (row0 + frow) * (D * 2) + 4 * fpair) = hv[it];
+      }
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int row0 = RPI * (wave + 4 * (it + NIT * half));    // uniform
@@ -560,7 +576,7 @@ __device__ __forceinline__ int dsk_off(int r, int chunk) {
 // wave of the pair forms dK for half of d over all 64 queries.  dQ^T is one
 // (d slice, query block) pair per wave.  K~ and V~ of the item stay in LDS and
 // are read as operands each step.
-template <int D>
+template <int D, bool DET>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
@@ -736,6 +752,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   const int fpair = RPI == 1 ? lane : lane & 31;
   const uint16_t* const fsrc = reinterpret_cast<const uint16_t*>(sKQ) + frow * DQS + 2 * fpair;
   const uint32_t fdst = 2u * (uint32_t)frow * rs32 + 4u * (uint32_t)fpair;
+  // deterministic mode: plain stores into the step's own partial slot instead
+  const int nq_doc = (L + BWD_BQ - 1) / BWD_BQ;
   auto flush_dq = [&](int qtp) {
     constexpr int NIT = BWD_BQ / (8 * RPI);
     const int q0p = qtp * BWD_BQ;
@@ -745,6 +763,17 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     for (int t2 = 0; t2 < NIT; ++t2) {
       const int row0 = RPI * (wave + 8 * t2);        // rows row0 + frow share bit 4
       hv[t2] = *reinterpret_cast<const v2h*>(fsrc + stage_row(row0) * DQS);
+    }
+    if constexpr (DET) {
+      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc);
+      if (step >= a.det_cap) return;      // the plan flags the overflow
+      uint8_t* const slot = reinterpret_cast<uint8_t*>(a.dq_part) + ((size_t)step * H + head) * (BWD_BQ * D * 2);
+#pragma unroll
+      for (int t2 = 0; t2 < NIT; ++t2) {
+        const int row0 = RPI * (wave + 8 * t2);
+        *reinterpret_cast<v2h*>(slot + (row0 + frow) * (D * 2) + 4 * fpair) = hv[t2];
+      }
+      return;
     }
 #pragma unroll
     for (int t2 = 0; t2 < NIT; ++t2) {
@@ -1024,7 +1053,8 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
             in.q_codes, in.k_codes, in.v_codes, in.v_key_codes, in.k_exp, in.v_exp, in.v_key_exp,
             in.kofs, in.il8, in.delta, in.dq_sigma, in.qexps, in.do_codes,
             static_cast<const uint16_t*>(in.g), static_cast<uint16_t*>(in.dq_acc), in.dk_f32,
-            static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv), static_cast<const uint16_t*>(in.q_x),
+            static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv),
+            static_cast<uint16_t*>(in.dq_part), in.det_base, in.det_cap, static_cast<const uint16_t*>(in.q_x),
             static_cast<const uint16_t*>(in.k_x), in.qk_scale};
   dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };
@@ -1032,7 +1062,11 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
     if (p.D == 64) go(attn_bwd_kernel<64, 1>); else go(attn_bwd_kernel<128, 1>);
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
-    if (p.D == 64) go8(attn_bwd8_kernel<64>); else go8(attn_bwd8_kernel<128>);
+    if (p.deterministic) {
+      if (p.D == 64) go8(attn_bwd8_kernel<64, true>); else go8(attn_bwd8_kernel<128, true>);
+    } else {
+      if (p.D == 64) go8(attn_bwd8_kernel<64, false>); else go8(attn_bwd8_kernel<128, false>);
+    }
   }
   return hipGetLastError();
 }

@@ -20,7 +20,8 @@ template <int D>
 __global__ void __launch_bounds__(FIN_THREADS)
 finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __restrict__ dq_sigma,
                 const float* __restrict__ dk_f32, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
-                bool with_dk) {
+                bool with_dk, const uint16_t* __restrict__ dq_part, const int* __restrict__ det_base,
+                int det_cap) {
   constexpr int E = D / FIN_PARTS;
   const size_t rows = (size_t)p.T * p.H;
   const size_t row = ((size_t)blockIdx.x * FIN_THREADS + threadIdx.x) / FIN_PARTS;   // = t * H + h
@@ -32,9 +33,35 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
   {
     float x[E];
     const int sig = dq_sigma[(size_t)h * p.T + t];
+    // deterministic mode: the fp16 accumulator is rebuilt here from the
+    // step partials of every key tile that sees this query, added in fp16 in
+    // ascending key-tile order
+    v4i acc[E / 8];
+    if (p.deterministic) {
+      const int d = find_doc(p.cu, p.ndocs, t);
+      const int s0 = p.cu[d], L = p.cu[d + 1] - s0, lp = t - s0;
+      const int qt = lp / BWD_BQ, r = lp % BWD_BQ;
+      const int nq = (L + BWD_BQ - 1) / BWD_BQ, nk = (L + BWD_BK - 1) / BWD_BK;
+      const int umax = min(qt / 2, nk - 1);
+      v8h a8[E / 8];
+#pragma unroll
+      for (int c = 0; c < E / 8; ++c) a8[c] = v8h{};
+      for (int u = 0; u <= umax; ++u) {
+        const long long step = det_step(det_base[d], u, qt, nq);
+        if (step >= det_cap) break;       // the plan flags the overflow
+        const uint16_t* src = dq_part + (((size_t)step * p.H + h) * BWD_BQ + r) * D + (size_t)part * E;
+#pragma unroll
+        for (int c = 0; c < E / 8; ++c) a8[c] = a8[c] + __builtin_bit_cast(v8h, ld16(src + 8 * c));
+      }
+#pragma unroll
+      for (int c = 0; c < E / 8; ++c) acc[c] = __builtin_bit_cast(v4i, a8[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < E / 8; ++c) acc[c] = ld16(dq_acc + off + 8 * c);
+    }
 #pragma unroll
     for (int c = 0; c < E / 8; ++c) {
-      const v4i w = ld16(dq_acc + off + 8 * c);
+      const v4i w = acc[c];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t u = (uint32_t)w[k];
@@ -63,16 +90,19 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
 }
 
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
-                           const float* dk_f32, void* dq, void* dk, bool with_dk, hipStream_t stream) {
+                           const float* dk_f32, void* dq, void* dk, bool with_dk, const void* dq_part,
+                           const int* det_base, int det_cap, hipStream_t stream) {
   const size_t rows = (size_t)p.T * p.H;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((rows * FIN_PARTS + FIN_THREADS - 1) / FIN_THREADS));
   if (p.D == 64)
     hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(FIN_THREADS), 0, stream, p,
-                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk);
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk,
+                       (const uint16_t*)dq_part, det_base, det_cap);
   else
     hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(FIN_THREADS), 0, stream, p,
-                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk);
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk,
+                       (const uint16_t*)dq_part, det_base, det_cap);
   return hipGetLastError();
 }
 

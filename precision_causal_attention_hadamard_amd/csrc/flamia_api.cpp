@@ -18,6 +18,16 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 // Tile sizes of the kernels (kept in step with flamia_device.hpp).
 constexpr int K_FWD_BQ = 128, K_FWD_BK = 64, K_BWD_BQ = 64, K_BWD_BK = 128;
 
+// Deterministic mode: an upper bound of the dQ partial steps per head.  A
+// document of L tokens has n Q - n (n - 1) <= n^2 + n steps (n = ceil(L/128)
+// key tiles, Q = ceil(L/64) <= 2n query tiles), and n^2 + n <= L^2/16384 +
+// 3L/128 + 2; summed over documents of at most M tokens that is at most
+// T M / 16384 + 3 T / 128 + 2 num_docs.
+int64_t det_step_cap(const flamia_attn_desc* d) {
+  const int64_t T = d->total_tokens, M = d->max_doc_len > 0 ? d->max_doc_len : d->total_tokens;
+  return (T * M + 16383) / 16384 + (3 * T + 127) / 128 + 2 * (int64_t)d->num_docs;
+}
+
 flamia_status validate(const flamia_attn_desc* d) {
   if (!d || !d->cu_seqlens) return FLAMIA_ERR_INVALID_ARG;
   if (d->total_tokens < 0 || d->num_docs < 1 || d->num_heads < 1) return FLAMIA_ERR_INVALID_ARG;
@@ -26,7 +36,7 @@ flamia_status validate(const flamia_attn_desc* d) {
   if ((d->hadamard | d->causal_dq_scale | d->deterministic | d->causal) & ~1) return FLAMIA_ERR_INVALID_ARG;
   if (d->path != 0 && d->path != 1) return FLAMIA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
-  if (d->causal != 1 || d->deterministic != 0) return FLAMIA_ERR_UNSUPPORTED;
+  if (d->causal != 1) return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
   // sort key, costs into 20 bits, grid x into 31 bits
   if (d->num_docs >= (1 << 24) || d->total_tokens >= (1 << 24)) return FLAMIA_ERR_WORKSPACE;
@@ -35,6 +45,8 @@ flamia_status validate(const flamia_attn_desc* d) {
   if ((int64_t)cap * d->num_heads >= (int64_t)1 << 31) return FLAMIA_ERR_WORKSPACE;
   // the backward addresses a document's rows with 32-bit byte offsets of 2-byte elements
   if ((int64_t)d->total_tokens * d->num_heads * d->head_dim >= (int64_t)1 << 30) return FLAMIA_ERR_WORKSPACE;
+  // deterministic mode: steps are 32-bit in the plan
+  if (d->deterministic && det_step_cap(d) >= ((int64_t)1 << 31)) return FLAMIA_ERR_WORKSPACE;
   return FLAMIA_OK;
 }
 
@@ -44,7 +56,9 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
   pl.cap_bwd = cdiv(d->total_tokens, K_BWD_BK) + d->num_docs;
   pl.fwd_offset = ALIGN;
   pl.bwd_offset = align_up(pl.fwd_offset + sizeof(int) * 2 * (size_t)pl.cap_fwd);
-  pl.bytes = align_up(pl.bwd_offset + sizeof(int) * 2 * (size_t)pl.cap_bwd);
+  pl.det_offset = align_up(pl.bwd_offset + sizeof(int) * 2 * (size_t)pl.cap_bwd);
+  pl.det_cap = d->deterministic ? (int)det_step_cap(d) : 0;
+  pl.bytes = align_up(pl.det_offset + sizeof(int) * ((size_t)d->num_docs + 1));
   return pl;
 }
 
@@ -87,6 +101,9 @@ BwdLayout bwd_layout(const flamia_attn_desc* d) {
   b.dq_sigma = off; off = align_up(off + 4 * M);
   b.dq_acc = off;   off = align_up(off + 2 * E);
   b.dk_f32 = off;   off = align_up(off + 4 * E);
+  b.dq_part = off;
+  if (d->deterministic)
+    off = align_up(off + (size_t)det_step_cap(d) * d->num_heads * K_BWD_BQ * d->head_dim * 2);
   b.bytes = off;
   return b;
 }
@@ -101,6 +118,7 @@ Problem problem(const flamia_attn_desc* d) {
   p.hadamard = d->hadamard;
   p.causal_dq_scale = d->causal_dq_scale;
   p.path = d->path;
+  p.deterministic = d->deterministic;
   p.softmax_scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
   p.c_log2 = (float)((double)p.softmax_scale * 1.4426950408889634);
   return p;
@@ -237,23 +255,31 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   in.dk_f32 = reinterpret_cast<float*>(w + b.dk_f32);
   in.dk = dk;
   in.dv = dv;
+  const PlanLayout pl = plan_layout(desc);
+  in.dq_part = w + b.dq_part;
+  in.det_base = reinterpret_cast<const int*>(static_cast<const uint8_t*>(qt->plan) + pl.det_offset);
+  in.det_cap = pl.det_cap;
   in.q_x = qt->q_fp4_bf16;
   in.k_x = qt->k_fp4_bf16;
   in.qk_scale = qt->qk_tensor_scale;
-  return hip_status(launch_attn_bwd(p, qt->plan, plan_layout(desc), in, stream));
+  return hip_status(launch_attn_bwd(p, qt->plan, pl, in, stream));
 }
 
-flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, void* dq, void* dk, void* ws,
-                                     hipStream_t stream) {
+flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dq,
+                                     void* dk, void* ws, hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!dq || !dk || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !dq || !dk || !ws) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
   uint8_t* w = static_cast<uint8_t*>(ws);
+  const PlanLayout pl = plan_layout(desc);
   return hip_status(launch_finalize(p, w + b.dq_acc, reinterpret_cast<const int*>(w + b.dq_sigma),
-                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, p.path == 1, stream));
+                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, p.path == 1,
+                                    w + b.dq_part,
+                                    reinterpret_cast<const int*>(static_cast<const uint8_t*>(qt->plan) + pl.det_offset),
+                                    pl.det_cap, stream));
 }
 
 flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
@@ -267,7 +293,7 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
   if (s != FLAMIA_OK) return s;
   s = flamia_attn_bwd_main(desc, qt, dk, dv, ws, stream);
   if (s != FLAMIA_OK) return s;
-  return flamia_attn_bwd_finish(desc, dq, dk, ws, stream);
+  return flamia_attn_bwd_finish(desc, qt, dq, dk, ws, stream);
 }
 
 flamia_status flamia_tile_config(int32_t head_dim, int32_t* fwd_bq, int32_t* fwd_bk, int32_t* bwd_bq,

@@ -36,6 +36,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int TOKEN_BLOCK = 32;   // tokens per scale block
 constexpr int FWD_BQ = 128;       // queries per forward work item
@@ -134,6 +135,16 @@ __device__ __forceinline__ int wave_max_i(int v) {
   v = max(v, dpp_move<0x142, 0xa>(v));
   v = max(v, dpp_move<0x143, 0xc>(v));
   return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Index of the document containing packed token t (cu[d] <= t < cu[d+1]).
+__device__ __forceinline__ int find_doc(const int* __restrict__ cu, int ndocs, int t) {
+  int lo = 0, hi = ndocs - 1;   // largest d with cu[d] <= t
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 // ---------------------------------------------------------------- small loads

@@ -10,29 +10,42 @@ namespace flamia {
 constexpr int PLAN_MAX_TILES = 8192;      // LDS capacity of the work-list sort
 constexpr int COST_MAX = (1 << 20) - 1;   // costs must stay below this
 
+// Plan words: [0] forward items, [1] backward items, [2] deterministic-mode
+// error word (1: the documents need more dQ partial slots than the
+// workspace holds), [3] reserved.
 struct PlanLayout {
   size_t fwd_offset;   // bytes from the plan base to the forward (doc, tile) list
   size_t bwd_offset;
+  size_t det_offset;   // int [num_docs + 1]: first dQ partial step of each document (per head)
   int cap_fwd;         // ceil(T / FWD_BQ) + num_docs
   int cap_bwd;         // ceil(T / BWD_BK) + num_docs
+  int det_cap;         // deterministic mode: dQ partial steps per head the workspace holds
   size_t bytes;
 };
 
 // Byte offsets of the backward workspace.
 struct BwdLayout {
-  size_t do_codes, do_exp, kofs, delta, il8, qexps, g, dq_sigma, dq_acc, dk_f32, bytes;
+  size_t do_codes, do_exp, kofs, delta, il8, qexps, g, dq_sigma, dq_acc, dk_f32, dq_part, bytes;
 };
 
 struct Problem {
   const int* cu;
   int T, ndocs, H, D;
   int hadamard, causal_dq_scale, path;
+  int deterministic;       // dQ from per-step partials added in a fixed order
   float softmax_scale;     // fp32 softmax scale
   float c_log2;            // fp32(softmax_scale * log2(e))
 };
 
 hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, float* qk_scale,
                        hipStream_t stream);
+
+// Deterministic-mode dQ partials: one fp16 [BWD_BQ, d] slot per (step, head),
+// step = first step of the document + u Q - u (u - 1) + (qt - 2 u) for key tile
+// u and query tile qt of a document with Q query tiles.
+__host__ __device__ inline long long det_step(int base, int u, int qt, int nq_tiles) {
+  return (long long)base + (long long)u * nq_tiles - (long long)u * (u - 1) + (qt - 2 * u);
+}
 
 // NVFP4 score operands of the mixed path (null when path = 0).
 struct Fp4Operands {
@@ -75,6 +88,9 @@ struct BwdInputs {
   float* dk_f32;           // mixed path: fp32 dK staging (the finaliser rotates and rounds it)
   void* dk;                // MXFP8 path: bf16 dK, written by the backward kernel
   void* dv;
+  void* dq_part;           // deterministic mode: fp16 dQ partial slots
+  const int* det_base;     // deterministic mode: first step of each document (plan)
+  int det_cap;             // deterministic mode: steps per head in dq_part
   const void *q_x, *k_x;   // mixed path only
   const float* qk_scale;   // mixed path only
 };
@@ -83,6 +99,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
                            hipStream_t stream);
 
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
-                           const float* dk_f32, void* dq, void* dk, bool with_dk, hipStream_t stream);
+                           const float* dk_f32, void* dq, void* dk, bool with_dk, const void* dq_part,
+                           const int* det_base, int det_cap, hipStream_t stream);
 
 }  // namespace flamia

@@ -46,6 +46,28 @@ __device__ static int block_inclusive_scan(int v, int* wsum, int& total) {
   return v + before;
 }
 
+// Inclusive scan of one 64-bit value per thread over the workgroup (same
+// scheme; `wsum` holds PLAN_WAVES values).
+__device__ static long long block_inclusive_scan64(long long v, long long* wsum, long long& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned lo = __shfl_up((unsigned)v, off, 64), hi = __shfl_up((unsigned)((unsigned long long)v >> 32), off, 64);
+    if (lane >= off) v += (long long)(((unsigned long long)hi << 32) | lo);
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  long long before = 0;
+  total = 0;
+  for (int w = 0; w < PLAN_WAVES; ++w) {
+    const long long t = wsum[w];
+    if (w < wave) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return v + before;
+}
+
 // One 64-bit key per lane of wave 0, sorted ascending across the wave with
 // the same bitonic network (for lists of at most 64 tiles).
 __device__ static unsigned long long wave_bitonic(unsigned long long key) {
@@ -123,16 +145,43 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
   if (tid == 0) *count_out = n_tiles;
 }
 
-// Workgroup 0 builds the forward list, workgroup 1 the backward list.
+// Workgroup 0 builds the forward list, workgroup 1 the backward list and the
+// deterministic-mode step prefix: document d's dQ partial steps (per head)
+// start at det_base[d]; a document of L tokens has n = ceil(L / BWD_BK) key
+// tiles and Q = ceil(L / BWD_BQ) query tiles, and key tile u visits query
+// tiles 2u .. Q-1, so n Q - n (n - 1) steps.  Word 2 of the plan flags a
+// total beyond det_cap.
 __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restrict__ cu, int ndocs,
                                                             int* counts, int2* fwd_items,
-                                                            int2* bwd_items, float* qk_scale) {
+                                                            int2* bwd_items, float* qk_scale, int* det_base,
+                                                            int det_cap) {
   __shared__ unsigned long long keys[PLAN_MAX_TILES];
   __shared__ int wsum[PLAN_WAVES];
+  __shared__ long long wsum64[PLAN_WAVES];
   const bool fwd = blockIdx.x == 0;
   build_sorted(cu, ndocs, fwd, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
                counts + (fwd ? 0 : 1), fwd ? fwd_items : bwd_items);
-  if (fwd && threadIdx.x == 0) { counts[2] = 0; counts[3] = 0; }
+  if (fwd && threadIdx.x == 0) counts[3] = 0;
+  if (!fwd) {
+    long long done = 0;
+    for (int base = 0; base < ndocs; base += PLAN_THREADS) {
+      const int d = base + threadIdx.x;
+      long long st = 0;
+      if (d < ndocs) {
+        const long long L = cu[d + 1] - cu[d];
+        const long long n = (L + BWD_BK - 1) / BWD_BK, q = (L + BWD_BQ - 1) / BWD_BQ;
+        st = n * q - n * (n - 1);
+      }
+      long long chunk;
+      const long long incl = block_inclusive_scan64(st, wsum64, chunk);
+      if (d < ndocs) det_base[d] = (int)min(done + incl - st, (long long)INT_MAX);
+      done += chunk;
+    }
+    if (threadIdx.x == 0) {
+      det_base[ndocs] = (int)min(done, (long long)INT_MAX);
+      counts[2] = done > det_cap ? 1 : 0;
+    }
+  }
   // mixed path: clear the tensor-amax slots before the amax pass runs
   if (fwd && qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
 }
@@ -142,7 +191,8 @@ hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& p
   char* base = static_cast<char*>(plan);
   hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs,
                      reinterpret_cast<int*>(base), reinterpret_cast<int2*>(base + pl.fwd_offset),
-                     reinterpret_cast<int2*>(base + pl.bwd_offset), qk_scale);
+                     reinterpret_cast<int2*>(base + pl.bwd_offset), qk_scale,
+                     reinterpret_cast<int*>(base + pl.det_offset), pl.det_cap);
   return hipGetLastError();
 }
 

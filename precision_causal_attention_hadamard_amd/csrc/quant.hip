@@ -24,16 +24,6 @@ namespace flamia {
 
 constexpr int QUANT_THREADS = 256;
 
-// Index of the document containing packed token t (cu[d] <= t < cu[d+1]).
-__device__ __forceinline__ int find_doc(const int* __restrict__ cu, int ndocs, int t) {
-  int lo = 0, hi = ndocs - 1;   // largest d with cu[d] <= t
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Calls f(block_start, block_end, doc_start, doc) for every document-local
 // 32-token block that starts inside chunk [c0, c0 + 32).  Uniform across the
 // workgroup.
@@ -355,7 +345,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
             w[j] = (int)(lo | (hi << 16));
           }
           st16(g + off + 8 * c, w);
-          st16(dq_acc + off + 8 * c, v4i{0, 0, 0, 0});
+          if (!p.deterministic) st16(dq_acc + off + 8 * c, v4i{0, 0, 0, 0});   // (unused in deterministic mode)
         }
         if (hf == 0) {
           const size_t mi = (size_t)h * T + tok;

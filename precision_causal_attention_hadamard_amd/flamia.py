@@ -68,7 +68,7 @@ def load(path: str = LIB_PATH):
         "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
         "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P, P],
         "flamia_attn_bwd_main": [dp, qp, P, P, P, P],
-        "flamia_attn_bwd_finish": [dp, P, P, P, P],
+        "flamia_attn_bwd_finish": [dp, qp, P, P, P, P],
         "flamia_tile_config": [I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
         "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I)],
     }
@@ -146,9 +146,9 @@ def attn_bwd_main(desc, qt: QTensors, dk, dv, ws, stream=None):
                                        _stream(stream)), "flamia_attn_bwd_main")
 
 
-def attn_bwd_finish(desc, dq, dk, ws, stream=None):
-    _check(load().flamia_attn_bwd_finish(ctypes.byref(desc), _ptr(dq), _ptr(dk), _ptr(ws), _stream(stream)),
-           "flamia_attn_bwd_finish")
+def attn_bwd_finish(desc, qt: QTensors, dq, dk, ws, stream=None):
+    _check(load().flamia_attn_bwd_finish(ctypes.byref(desc), ctypes.byref(qt), _ptr(dq), _ptr(dk), _ptr(ws),
+                                         _stream(stream)), "flamia_attn_bwd_finish")
 
 
 def tile_config(head_dim: int):
@@ -175,7 +175,7 @@ class TrainingCall:
     tensors; ``cu_seqlens`` a list of ints."""
 
     def __init__(self, q, k, v, do, cu_seqlens, hadamard=False, causal_dq_scale=False,
-                 softmax_scale=0.0, path=0):
+                 softmax_scale=0.0, path=0, deterministic=False):
         dev = q.device
         self.q, self.k, self.v, self.do = q, k, v, do
         T, H, d = q.shape
@@ -183,7 +183,7 @@ class TrainingCall:
         self.cu = torch.tensor(self.cu_list, dtype=torch.int32, device=dev)
         lens = [b - a for a, b in zip(self.cu_list, self.cu_list[1:])]
         self.desc = make_desc(self.cu, T, len(lens), max(lens) if lens else 0, H, d, hadamard,
-                              causal_dq_scale, softmax_scale, path)
+                              causal_dq_scale, softmax_scale, path, deterministic=int(deterministic))
         qb, fb, bb = buffer_sizes(self.desc)
         self.qbuf = torch.empty(qb, dtype=torch.uint8, device=dev)
         self.qt = qtensors_layout(self.desc, self.qbuf)
@@ -210,7 +210,7 @@ class TrainingCall:
     def backward_staged(self, stream=None):
         attn_bwd_prep(self.desc, self.qt, self.o, self.row_max, self.row_sum, self.do, self.bws, stream)
         attn_bwd_main(self.desc, self.qt, self.dk, self.dv, self.bws, stream)
-        attn_bwd_finish(self.desc, self.dq, self.dk, self.bws, stream)
+        attn_bwd_finish(self.desc, self.qt, self.dq, self.dk, self.bws, stream)
 
     def step(self, stream=None):
         self.quantize(stream)
@@ -247,3 +247,8 @@ class TrainingCall:
         fwd = raw[fo:fo + 8 * cf].view(torch.int32).view(cf, 2).cpu()
         bwd = raw[bo:bo + 8 * cb].view(torch.int32).view(cb, 2).cpu()
         return fwd[: int(counts[0])], bwd[: int(counts[1])]
+
+    def plan_error_word(self) -> int:
+        """Word 2 of the plan: 1 when deterministic mode ran out of dQ partial slots."""
+        base = self.qt.plan - self.qbuf.data_ptr()
+        return int(self.qbuf[base + 8:base + 12].view(torch.int32).cpu()[0])

@@ -56,11 +56,53 @@ def test_buffer_sizes_valid(lib):
 @pytest.mark.parametrize("field,value,want", [
     ("head_dim", 96, 1), ("head_dim", 256, 1), ("num_heads", 0, 1), ("num_docs", 0, 1),
     ("total_tokens", -1, 1), ("max_doc_len", 300, 1), ("hadamard", 2, 1),
-    ("causal", 0, 2), ("deterministic", 1, 2), ("path", 7, 1),
+    ("causal", 0, 2), ("deterministic", 2, 1), ("path", 7, 1),
 ])
 def test_invalid_and_unsupported_descriptors(lib, field, value, want):
     st, _, _ = sizes_status(lib, base_desc(**{field: value}))
     assert st == want, (field, value, st)
+
+
+def causal_steps(L, bq=64, bk=128):
+    """(key tile, query tile) pairs of a causal document: key tile u visits query tiles 2u .. Q-1."""
+    n, q = -(-L // bk), -(-L // bq)
+    return sum(q - (u * bk) // bq for u in range(n))
+
+
+def test_deterministic_workspace_holds_every_partition():
+    """Deterministic mode adds one 64 x d fp16 slot per (step, head).  The
+    host's bound must cover the causal steps of any split of T tokens into
+    documents of at most max_doc_len tokens; check it against brute-force
+    step counts of extreme and random splits."""
+    import random
+    lib = flamia.load()
+    rng = random.Random(5)
+    for T, M, ndocs_hint in ((256, 256, 1), (4096, 64, 64), (8192, 4096, 2), (5000, 1000, 9), (3000, 1, 3000)):
+        for trial in range(6):
+            if trial == 0:
+                lens = [M] * (T // M) + ([T % M] if T % M else [])
+            elif trial == 1:
+                lens = [1] * T if T <= 4096 else [M] * (T // M) + ([T % M] if T % M else [])
+            else:
+                lens, left = [], T
+                while left:
+                    L = min(left, rng.randint(1, M))
+                    lens.append(L)
+                    left -= L
+            d0 = base_desc(total_tokens=T, max_doc_len=M, num_docs=len(lens), num_heads=3, head_dim=64)
+            d1 = base_desc(total_tokens=T, max_doc_len=M, num_docs=len(lens), num_heads=3, head_dim=64,
+                           deterministic=1)
+            st0, _, b0 = sizes_status(lib, d0)
+            st1, _, b1 = sizes_status(lib, d1)
+            assert st0 == 0 and st1 == 0
+            cap_steps = (b1 - b0) // (3 * 64 * 64 * 2)
+            need = sum(causal_steps(L) for L in lens)
+            assert cap_steps >= need, (T, M, len(lens), cap_steps, need)
+    # the bound is tight enough for long documents (within 10 % of two 4096-token documents)
+    d0 = base_desc(total_tokens=8192, max_doc_len=4096, num_docs=2, num_heads=1, head_dim=128)
+    d1 = base_desc(total_tokens=8192, max_doc_len=4096, num_docs=2, num_heads=1, head_dim=128, deterministic=1)
+    cap = (sizes_status(lib, d1)[2] - sizes_status(lib, d0)[2]) // (64 * 128 * 2)
+    assert 2 * causal_steps(4096) <= cap <= 1.1 * 2 * causal_steps(4096)
 
 
 def test_null_arguments_rejected_without_launch(lib):
@@ -73,6 +115,8 @@ def test_null_arguments_rejected_without_launch(lib):
     assert lib.flamia_quantize(ctypes.byref(d), None, None, None, ctypes.byref(qt), None) == 1
     assert lib.flamia_attn_fwd(ctypes.byref(d), ctypes.byref(qt), None, None, None, None, None) == 1
     assert lib.flamia_attn_bwd(ctypes.byref(d), ctypes.byref(qt), *([None] * 9)) == 1
+    assert lib.flamia_attn_bwd_main(ctypes.byref(d), ctypes.byref(qt), None, None, None, None) == 1
+    assert lib.flamia_attn_bwd_finish(ctypes.byref(d), None, None, None, None, None) == 1
 
 
 def test_layout_alignment_and_carving(lib):
