@@ -167,15 +167,24 @@ def backward_doc(fw, qd, kd, vblk, vkey, dod, o_out, s32, num: Numerics):
 def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
     """Quantize, forward and backward of the whole packed call.
 
-    q, k, v, do: ``[T, H, d]`` arrays holding bf16 values.  Returns a dict
-    with the quantized payloads (codes and exponents, bit-comparable), the
-    forward statistics ``row_max`` (int) and ``row_sum`` (fp32) in ``[H, T]``,
-    ``D`` in ``[H, T]``, and the outputs O, dQ, dK, dV as fp64 arrays holding
-    bf16 values (or unrounded values when ``round_outputs`` is off).
+    q, do: ``[T, H, d]``; k, v: ``[T, Hk, d]`` with Hk dividing H -- grouped
+    query attention when Hk < H: query head h reads key/value head
+    h // (H / Hk), and the dK, dV of a key/value head are the sums over its
+    query heads, rounded once ([Reading, 5.2] lists GQA variants among the measured
+    workloads; [Reading, 6.3] its deterministic reduction).  All hold bf16
+    values.  Returns a dict with the quantized payloads (codes and exponents,
+    bit-comparable), the forward statistics ``row_max`` (int) and ``row_sum``
+    (fp32) in ``[H, T]``, ``D`` in ``[H, T]``, and the outputs O, dQ, dK, dV as
+    fp64 arrays holding bf16 values (or unrounded values when
+    ``round_outputs`` is off).
     """
     num = num or Numerics()
     q = np.asarray(q, dtype=np.float64)
     T, H, d = q.shape
+    Hk = np.asarray(k).shape[1]
+    if H % Hk:
+        raise ValueError("key/value heads must divide query heads")
+    group = H // Hk
     s32, c32 = scale_constants(d, num.softmax_scale)
     if num.quantize_operands:
         qt = quantize_qkv(q, k, v, cu_seqlens, num.hadamard, num.rule, num.granularity)
@@ -195,16 +204,17 @@ def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
         if num.hadamard:
             q32, k32 = fwht_fp32(q32), fwht_fp32(k32)
         z = np.zeros((H, T), dtype=np.int64)
+        zk = np.zeros((Hk, T), dtype=np.int64)
         v64 = np.asarray(v, dtype=np.float64)
         qt = dict(q=q32.astype(np.float64), k=k32.astype(np.float64), v=v64, v_key=v64,
-                  v_exp=z, v_key_exp=z)
+                  v_exp=zk, v_key_exp=zk)
         do_codes, do_exp, do_deq = None, z, np.asarray(do, dtype=np.float64)
         qs_all, ks_all = qt["q"], qt["k"]
 
     o = np.zeros((T, H, d))
     dq = np.zeros((T, H, d))
-    dk = np.zeros((T, H, d))
-    dv = np.zeros((T, H, d))
+    dk_sum = np.zeros((T, Hk, d))     # unrounded sums over the query heads of a group
+    dv_sum = np.zeros((T, Hk, d))
     row_max = np.zeros((H, T), dtype=np.int64)
     row_sum = np.zeros((H, T), dtype=np.float64)
     Dst = np.zeros((H, T))
@@ -214,11 +224,12 @@ def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
             continue
         for h in range(H):
             sl = slice(s, e)
-            fw = forward_doc(qs_all[sl, h], ks_all[sl, h], qt["v"][sl, h], qt["v_key"][sl, h],
-                             qt["v_exp"][h, sl], qt["v_key_exp"][h, sl], c32, num)
+            hk = h // group
+            fw = forward_doc(qs_all[sl, h], ks_all[sl, hk], qt["v"][sl, hk], qt["v_key"][sl, hk],
+                             qt["v_exp"][hk, sl], qt["v_key_exp"][hk, sl], c32, num)
             o_out = _out(fw["o"], num)
-            bw = backward_doc(fw, qt["q"][sl, h], qt["k"][sl, h], qt["v"][sl, h],
-                              qt["v_key"][sl, h], do_deq[sl, h], o_out, s32, num)
+            bw = backward_doc(fw, qt["q"][sl, h], qt["k"][sl, hk], qt["v"][sl, hk],
+                              qt["v_key"][sl, hk], do_deq[sl, h], o_out, s32, num)
             o[sl, h] = o_out
             row_max[h, sl] = fw["m"]
             row_sum[h, sl] = fw["l"]
@@ -227,10 +238,11 @@ def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
             if num.hadamard:
                 dqh, dkh = rotate_back_fp64(dqh), rotate_back_fp64(dkh)
             dq[sl, h] = _out(dqh, num)
-            dk[sl, h] = _out(dkh, num)
-            dv[sl, h] = _out(bw["dv"], num)
+            dk_sum[sl, hk] += dkh
+            dv_sum[sl, hk] += bw["dv"]
             ds_nonzero += bw["ds_nonzero"]
             ds_zeroed += bw["ds_zeroed"]
+    dk, dv = _out(dk_sum, num), _out(dv_sum, num)
     res = dict(o=o, dq=dq, dk=dk, dv=dv, row_max=row_max, row_sum=row_sum, D=Dst,
                do_codes=do_codes, do_exp=do_exp,
                ds_zero_fraction=(ds_zeroed / ds_nonzero) if ds_nonzero else 0.0)

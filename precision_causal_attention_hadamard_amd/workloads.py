@@ -40,6 +40,10 @@ class Workload:
     notes: dict = field(default_factory=dict)
 
     @property
+    def kv_heads(self) -> int:
+        return int(self.k.shape[1])
+
+    @property
     def total_tokens(self) -> int:
         return int(self.cu_seqlens[-1])
 
@@ -61,13 +65,15 @@ def _bf16(x: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
 
 
-def draw_tensors(rng, T: int, H: int, d: int, outlier_scale: float = 0.0):
-    """Q, K, V, dO as bf16; optional outlier channels drawn after the tensors."""
-    raw = [rng.standard_normal((T, H, d), dtype=np.float32) for _ in range(4)]
+def draw_tensors(rng, T: int, H: int, d: int, outlier_scale: float = 0.0, kv_heads: int = 0):
+    """Q, K, V, dO as bf16; optional outlier channels drawn after the tensors.
+    K and V carry ``kv_heads`` heads (0 = H; fewer for grouped query attention)."""
+    Hk = kv_heads or H
+    raw = [rng.standard_normal((T, h, d), dtype=np.float32) for h in (H, Hk, Hk, H)]
     if outlier_scale:
         n_out = max(1, int(round(0.01 * d)))
         for x in raw:
-            for h in range(H):
+            for h in range(x.shape[1]):
                 ch = rng.choice(d, size=n_out, replace=False)
                 x[:, h, ch] *= np.float32(outlier_scale)
     return [_bf16(x) for x in raw]
@@ -128,10 +134,13 @@ def config(k: int, seed: int | None = None) -> Workload:
 
 
 def small_packed(seed: int, doc_lens, heads: int = 2, head_dim: int = 64,
-                 outlier_scale: float = 0.0, hadamard: bool = False, path: int = 0) -> Workload:
-    """A small packed workload for parity tests (documents off 32-alignment)."""
+                 outlier_scale: float = 0.0, hadamard: bool = False, path: int = 0,
+                 kv_heads: int = 0) -> Workload:
+    """A small packed workload for parity tests (documents off 32-alignment);
+    ``kv_heads`` < ``heads`` gives grouped query attention."""
     rng = np.random.default_rng(seed)
     T = int(sum(doc_lens))
-    q, kk, v, do = draw_tensors(rng, T, heads, head_dim, outlier_scale)
-    return Workload(f"packed_{'_'.join(map(str, doc_lens))}_h{heads}_d{head_dim}", q, kk, v, do,
+    q, kk, v, do = draw_tensors(rng, T, heads, head_dim, outlier_scale, kv_heads)
+    kvs = f"_kv{kv_heads}" if kv_heads and kv_heads != heads else ""
+    return Workload(f"packed_{'_'.join(map(str, doc_lens))}_h{heads}{kvs}_d{head_dim}", q, kk, v, do,
                     _cu(doc_lens), heads, head_dim, hadamard=hadamard, path=path)

@@ -46,6 +46,39 @@ def test_unquantized_core_equals_fp64_bruteforce(hadamard_on):
         assert rel(got, want) <= 1e-5, name
 
 
+@pytest.mark.parametrize("heads,kv_heads", [(4, 2), (6, 2), (3, 1)])
+def test_unquantized_gqa_core_equals_fp64_bruteforce(heads, kv_heads):
+    """Grouped query attention: with quantization off the oracle equals torch
+    fp64 attention over K, V repeated per query head, whose autograd sums
+    the group's dK, dV."""
+    wl = W.small_packed(2, [50, 1, 77], heads=heads, head_dim=64, kv_heads=kv_heads)
+    q, k, v, do = np_inputs(wl)
+    assert k.shape[1] == kv_heads and q.shape[1] == heads
+    num = A.Numerics(quantize_operands=False, quantize_p=False, quantize_ds=False, round_outputs=False)
+    r = A.training_call(q, k, v, do, wl.cu_seqlens, num)
+    ref = causal_attention_fp64(q, k, v, do, wl.cu_seqlens)
+    for name, got, want in zip(("o", "dq", "dk", "dv"), (r["o"], r["dq"], r["dk"], r["dv"]), ref):
+        assert got.shape == want.shape and rel(got, want) <= 1e-5, name
+
+
+def test_gqa_with_one_group_per_head_is_mha():
+    """kv_heads = heads: the grouped oracle is the plain one, bit for bit;
+    and a grouped call equals the plain call on K, V repeated per query head
+    except that dK, dV are the group sums (rounded once)."""
+    wl = W.small_packed(3, [40, 70], heads=4, head_dim=64, kv_heads=2)
+    q, k, v, do = np_inputs(wl)
+    g = A.training_call(q, k, v, do, wl.cu_seqlens)
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    m = A.training_call(q, kr, vr, do, wl.cu_seqlens)
+    for n in ("o", "dq", "row_max", "row_sum"):
+        np.testing.assert_array_equal(g[n], m[n], err_msg=n)
+    num = A.Numerics(round_outputs=False)
+    gu = A.training_call(q, k, v, do, wl.cu_seqlens, num)
+    mu = A.training_call(q, kr, vr, do, wl.cu_seqlens, num)
+    for n in ("dk", "dv"):
+        np.testing.assert_allclose(gu[n], mu[n][:, 0::2] + mu[n][:, 1::2], rtol=0, atol=1e-12, err_msg=n)
+
+
 def test_quantized_oracle_close_to_fp64_on_tiny_workload():
     wl = W.config(1)
     q, k, v, do = np_inputs(wl)
