@@ -10,7 +10,8 @@ document (forward 2 products, backward 5); quantization adds no FLOPs but
 its time is inside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
-                       [--no-cpu-baseline] [--copy-calibration]
+                       [--kv-heads Hk] [--deterministic] [--no-cpu-baseline]
+                       [--copy-calibration]
 """
 
 from __future__ import annotations
@@ -131,8 +132,10 @@ def cpu_baseline(wl, cfg: int):
     from oracle import attention as A
 
     s, e = wl.cu_seqlens[0], wl.cu_seqlens[1]
-    nh = min(CPU_SAMPLE_HEADS, wl.heads)
-    arrs = [t[s:e, 0:nh].float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
+    g = wl.heads // wl.kv_heads                       # query heads per key/value head
+    nh = max(g, min(CPU_SAMPLE_HEADS, wl.heads) // g * g)
+    arrs = [t[s:e, 0:(nh if t.shape[1] == wl.heads else nh // g)].float().numpy().astype(np.float64)
+            for t in (wl.q, wl.k, wl.v, wl.do)]
     L = e - s
     t0 = time.perf_counter()
     A.training_call(*arrs, [0, L], A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8"))
@@ -152,6 +155,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="grouped-query variant of the workload: K and V with this many heads (0: one per query head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true",
                     help="ordered dQ reduction (per-step partials, fixed-order fp16 sum) instead of atomics")
@@ -178,13 +183,15 @@ def main():
     from precision_causal_attention_hadamard_amd import flamia, workloads
 
     flamia.load()
-    wl = workloads.config(args.config)
+    wl = workloads.config(args.config, kv_heads=args.kv_heads)
     dev = torch.device("cuda:0")
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
                                causal_dq_scale=wl.causal_dq_scale, path=wl.path,
                                deterministic=args.deterministic)
     T, H, d = call.shape
+    Hk = call.kv_heads
+    grouped = Hk != H
     pairs = wl.causal_pairs()
     flops = wl.flops()
 
@@ -226,13 +233,16 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
 
     # roofline of the dominant kernel
-    E = T * H * d
+    E, Ek = T * H * d, T * Hk * d
+    # quantizer bytes: bf16 Q, K, V read; Q, K, V, per-key V codes written;
+    # one exponent byte per token and head of Q and four planes of the K side
+    qbytes = 3 * E + 7 * Ek + T * H + 4 * T * Hk
     fwd_mix, bwd_mix = product_mix(d, pairs, bool(wl.path))
     kernels = {
         "attn_bwd": ("attn_bwd_kernel" if wl.path else "attn_bwd8_kernel", "mfma", 10 * d * pairs,
                      weighted_peak(bwd_mix)),
         "attn_fwd": ("attn_fwd_kernel", "mfma", 4 * d * pairs, weighted_peak(fwd_mix)),
-        "quantize": ("quant_qkv_kernel", "hbm", 10 * E + 5 * T * H, HBM_PEAK_GBS),
+        "quantize": ("quant_qkv_kernel", "hbm", qbytes, HBM_PEAK_GBS),
     }
     dom = max(kernels, key=lambda n: stage_ms[n])
     kname, bound, work, peak = kernels[dom]
@@ -241,14 +251,14 @@ def main():
         achieved, unit = work / t_dom / 1e12, "TFLOP/s"
     else:
         achieved, unit = work / t_dom / 1e9, "GB/s"
-    traffic = measured_traffic(kname, f"config{args.config}") if kname.startswith("attn_bwd") else None
+    traffic = (measured_traffic(kname, f"config{args.config}")
+               if kname.startswith("attn_bwd") and not grouped else None)
     roofline = {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic,
                 "peak_note": "dtype-weighted: FP8 products at 5000, bf16 products at 2500 TFLOP/s"
                              if bound == "mfma" else "HBM3E",
                 "frac_of_fp8_peak": achieved / FP8_PEAK_TFLOPS if bound == "mfma" else None,
                 "algorithmic_work_per_launch": work, "avg_launch_ms": stage_ms[dom]}
-    qbytes = 10 * E + 5 * T * H
     quant = {"GB/s": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9,
              "frac_hbm_peak": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
              "algorithmic_bytes": qbytes, "launches": 3 if wl.path else 2}
@@ -257,7 +267,7 @@ def main():
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": T, "heads": H, "head_dim": d,
+        "config": {"workload": wl.name, "tokens": T, "heads": H, "kv_heads": Hk, "head_dim": d,
                    "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
                    "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
                    "deterministic": bool(args.deterministic),

@@ -20,7 +20,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Layouts.  Per-token tensors are [T, H, d] row-major ("THD": packed tokens,
- *   then heads, then the head dimension), no padding between documents.
+ *   then heads, then the head dimension), no padding between documents;
+ *   k, v, dk, dv and the K-side quantized tensors have Hk = num_kv_heads heads.
  *   Per-token metadata (exponent bytes, row statistics, D) is [H, T].
  *   Documents are given by cu_seqlens (device int32[num_docs + 1],
  *   0 = cu[0] <= cu[1] <= ... <= cu[num_docs] = T).
@@ -76,6 +77,12 @@ typedef struct flamia_attn_desc {
                                    ([Reading, 6.3]: atomic dQ reduction by default, a slower
                                    deterministic mode beside it) */
   float softmax_scale;          /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t num_kv_heads;         /* Hk: heads of k and v; 0 (or H) = one per query head.  A proper
+                                   divisor of H gives grouped query attention: query head h reads
+                                   key/value head h / (H / Hk), and dk, dv of a key/value head are
+                                   the sums over its H / Hk query heads, accumulated in fp32 and
+                                   rounded once ([Reading, 5.2] measures GQA workloads).  MXFP8
+                                   path only (path = 1 with Hk < H: FLAMIA_ERR_UNSUPPORTED) */
 } flamia_attn_desc;
 
 /*
@@ -83,6 +90,10 @@ typedef struct flamia_attn_desc {
  * saved set together with o, row_max and row_sum.  All pointers point into
  * one caller buffer of `qtensor_bytes` (flamia_buffer_sizes); fill them with
  * flamia_qtensors_layout.
+ *
+ * K-side tensors (k_codes, v_codes, v_key_codes: [T,Hk,d]; k_exp, v_exp,
+ * v_key_exp, v_ref_exp: [Hk,T]) carry the num_kv_heads heads; [T,H,d] and
+ * [H,T] below read [T,Hk,d] and [Hk,T] for them.
  *
  *  q_codes, k_codes   [T,H,d] E4M3 token-block codes of Q and K (after the
  *                     optional Hadamard rotation) -- [Summary, §3.1 Token-Block
@@ -160,7 +171,7 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base,
  * bullet (rotation, block statistics, codes and scales generated together)
  * and [Summary, §4.3 Ablation Study]; plus the GPU-built work lists of
  * [Summary, §3.6.2 Load-Balanced Scheduling] and [Reading, 4.4] last bullet.
- *   q, k, v : bf16 [T,H,d] inputs (device).
+ *   q, k, v : bf16 inputs (device): q [T,H,d]; k, v [T,Hk,d].
  *   out     : filled qtensors (device buffers, caller-owned).
  * Per (document, 32-token block, head): optional fp32 Hadamard rotation of
  * Q and K rows; amax over the 32 x d block; exponent e = the smallest
@@ -205,7 +216,8 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
  * atomics); with the rotation on, dQ and dK are rotated back.
  *   o, row_max, row_sum : forward outputs.
  *   dout                : bf16 [T,H,d] upstream gradient.
- *   dq, dk, dv          : bf16 [T,H,d] gradients w.r.t. the unrotated q, k, v.
+ *   dq, dk, dv          : bf16 gradients w.r.t. the unrotated q, k, v (dq [T,H,d];
+ *                         dk, dv [T,Hk,d]).
  *   ws                  : bwd workspace of bwd_ws_bytes (device).
  * Four kernel launches: dO quantizer, backward, two finalisers.
  */

@@ -1,0 +1,159 @@
+"""Decision bounds of the attention call (oracle; test infrastructure).
+
+The method accumulates S = Q~ K~^T, dP = dO~ V~^T, D, the softmax
+denominator l and the output products in fp32 ([Summary] opening paragraphs;
+[Reading, 4.1], [Reading, 4.3]); the order of that accumulation is not fixed,
+and matrix cores do not add a product's terms one by one.  Any fp32 evaluation
+of a sum of n exact terms x_k is within gamma_n * sum |x_k| of the exact sum,
+gamma_n = n u / (1 - n u), u = 2**-24 (the standard error bound of floating
+point summation in any order: Higham, "Accuracy and Stability of Numerical
+Algorithms", ch. 3 and 4).  The attention oracle evaluates every such sum
+exactly and rounds once, which is one admissible result.
+
+Where the interval of values that bound admits straddles a rounding boundary
+of a quantized decision -- the E4M3 code of P 2^8 (with the diagonal fold) or
+the bf16 rounding of O -- more than one result is correct.  Such a decision
+moves a row of O, and through D_i = sum_d dO~_id O_id it shifts every dS_ij of
+the row in the same direction, so dQ_i and the dK_j of the row's keys move
+coherently; the P^ decision also enters dV directly.  ``allowances`` returns,
+per output element, the width those alternative decisions can produce, so a
+comparison can hold every element to its tolerance plus that width.  The dS^
+codes themselves are re-rounded around the shifted values; that part, and the
+continuous fp32 differences, scatter in sign and stay with the tolerance.
+Elements no decision reaches get nothing beyond the span of their own final
+bf16 rounding.
+
+Bounds used (per (document, head), vectorised; e = error, rel = relative):
+* S: e <= gamma_d sum_k |q~_ik k~_jk| + u |S| (the oracle rounds once);
+* S' = fp32(S c) adds 2 u |S'|; P = 2^(S' - m) from a hardware exp2:
+  rel <= 2^(c e_S + 2u|S'|) (1 + 4 u) - 1; the integer row maximum is taken as
+  equal on both sides (a different one scales every P of the row by an exact
+  power of two, which leaves O and dS unchanged outside E4M3 subnormals);
+* P^: the code span of [x (1 - rel), x (1 + rel)], x = P 2^8 f;
+* l = sum P: rel <= (1 + max rel(P) over the row)(1 + gamma_L) - 1;
+* O (before bf16): w = (1 + rel(l)) sum_j span(P^)_ij |V_j| / l_i
+  + gamma_L (|P^| |V|)_i / l_i + (rel(l) + u) |O_i|; the bf16 span of
+  [O - w, O + w] is the O allowance (the rounding of O to bf16 is itself a
+  decision: D is formed from the stored bf16 O);
+* D: e(D_i) = sum_d |dO~_id| allowance(O)_id;
+* dV_j: sum_i (1 + rel(l_i)) span(P^)_ij / l_i |dO~_i|, then the span of the
+  final bf16 rounding.
+A shift of D_i by delta moves dQ_i by delta times the row's direction
+g_i = -s32 sum_j (P_ij / l_i) K~_j (rotated back with the Hadamard option),
+before dS^ re-rounding; ``allowances`` returns g and e(D), and a comparison
+fits one coefficient |a_i| <= e(D_i) per row and holds the remainder to the
+tolerance.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats
+from .attention import Numerics, forward_doc, scale_constants
+from .quant import doc_bounds, fold_reference, quantize_qkv, quantize_token_blocks
+
+U = 2.0 ** -24
+
+
+def gamma(n: int) -> float:
+    """gamma_n = n u / (1 - n u) for fp32 summation of n terms."""
+    return n * U / (1.0 - n * U)
+
+
+def _span(rounder, lo, hi):
+    """Width of the set of values ``rounder`` maps [lo, hi] to (monotone)."""
+    return np.abs(rounder(hi) - rounder(lo))
+
+
+def _e4m3_span(lo, hi):
+    return _span(formats.e4m3_round, lo, hi)
+
+
+def _bf16_span(x, w):
+    return _span(formats.bf16_round, x - w, x + w)
+
+
+def doc_head_allowances(fw, qs, ks, qd, kd, vblk, vkey, dod, s32, c32, num: Numerics):
+    """Allowances of one (document, head).  qs, ks: score operands; qd, kd:
+    the dQ/dK operands; vblk, vkey, dod as for forward_doc/backward_doc.
+    Returns the O allowance (after its bf16 span), e(D) per row, the dQ
+    direction of a D shift (unrotated) and the dV width before its bf16
+    rounding."""
+    L, d = qd.shape
+    valid, diag = fw["valid"], fw["diag"]
+    p, l, peff = fw["p"], fw["l"], fw["peff"]
+    c = float(c32)
+    # scores
+    S = qs @ ks.T
+    e_s = gamma(d) * (np.abs(qs) @ np.abs(ks).T) + U * np.abs(S)
+    sp = fw["sp"]
+    w_sp = c * e_s + 2 * U * np.abs(sp)
+    rel_p = np.where(valid, np.exp2(w_sp) * (1 + 4 * U) - 1.0, 0.0)
+    # P^ decisions (diagonal pairs are folded, then unfolded)
+    v_exp_key = fw.get("v_exp_key")
+    f = np.ones_like(p)
+    if num.quantize_p:
+        if v_exp_key is not None:
+            e_ref = fold_reference(v_exp_key, num.causal)
+            f = np.where(diag, np.ldexp(1.0, np.minimum(v_exp_key[None, :] - e_ref[:, None], 0)), 1.0)
+        x = np.ldexp(p * f, 8)
+        span_pe = np.where(valid, np.ldexp(_e4m3_span(x * (1 - rel_p), x * (1 + rel_p)), -8) / f, 0.0)
+    else:
+        span_pe = rel_p * p
+    rel_l = (1 + np.max(rel_p, axis=1, initial=0.0)) * (1 + gamma(L)) - 1
+    # O before bf16
+    av_off, av_dia = np.abs(vblk), np.abs(vkey)
+    flips = (np.where(diag, 0.0, span_pe) @ av_off + np.where(diag, span_pe, 0.0) @ av_dia) / l[:, None]
+    acc = (np.where(diag, 0.0, np.abs(peff)) @ av_off + np.where(diag, np.abs(peff), 0.0) @ av_dia) / l[:, None]
+    o = fw["o"]
+    w_o = flips * (1 + rel_l[:, None]) + gamma(L) * acc + (rel_l[:, None] + U) * np.abs(o)
+    o_span = _bf16_span(o, w_o) if num.round_outputs else w_o
+    # backward: the decisions above shift D, hence every dS of the row
+    e_D = np.sum(np.abs(dod) * o_span, axis=1)
+    g = -float(s32) * (np.where(valid, p / l[:, None], 0.0) @ kd)
+    dv = ((span_pe * (1 + rel_l[:, None])) / l[:, None]).T @ np.abs(dod)
+    return dict(o=o_span, e_D=e_D, dq_dir=g, dv=dv, p_span=span_pe, rel_p=rel_p, rel_l=rel_l)
+
+
+def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
+    """Decision bounds of the whole call (see the module docstring): ``o``
+    ``[T, H, d]`` and ``dv`` ``[T, Hk, d]`` per-element allowances; ``e_D``
+    ``[T, H]``, the bound of the admissible shift of D per query row; and
+    ``dq_dir`` ``[T, H, d]``, the change of dQ per unit shift of D."""
+    num = num or Numerics()
+    q = np.asarray(q, dtype=np.float64)
+    T, H, d = q.shape
+    Hk = np.asarray(k).shape[1]
+    group = H // Hk
+    s32, c32 = scale_constants(d, num.softmax_scale)
+    qt = quantize_qkv(q, k, v, cu_seqlens, num.hadamard, num.rule, num.granularity)
+    _, _, do_deq = quantize_token_blocks(do, cu_seqlens, num.rule, num.granularity)
+    qs_all, ks_all = qt["q"], qt["k"]
+    if num.path == "mixed":
+        from .nvfp4 import quantize_nvfp4
+        qa, ka = num.nvfp4_amax if num.nvfp4_amax is not None else (None, None)
+        *_, qs_all = quantize_nvfp4(qt["q_rot"], qa)
+        *_, ks_all = quantize_nvfp4(qt["k_rot"], ka)
+    from .hadamard import rotate_back_fp64
+    out = dict(o=np.zeros((T, H, d)), dq_dir=np.zeros((T, H, d)), e_D=np.zeros((T, H)))
+    dv_w = np.zeros((T, Hk, d))
+    dv_raw = np.zeros((T, Hk, d))
+    for s, e in doc_bounds(cu_seqlens):
+        if e == s:
+            continue
+        sl = slice(s, e)
+        for h in range(H):
+            hk = h // group
+            fw = forward_doc(qs_all[sl, h], ks_all[sl, hk], qt["v"][sl, hk], qt["v_key"][sl, hk],
+                             qt["v_exp"][hk, sl], qt["v_key_exp"][hk, sl], c32, num)
+            fw["v_exp_key"] = qt["v_key_exp"][hk, sl]
+            a = doc_head_allowances(fw, qs_all[sl, h], ks_all[sl, hk], qt["q"][sl, h], qt["k"][sl, hk],
+                                    qt["v"][sl, hk], qt["v_key"][sl, hk], do_deq[sl, h], s32, c32, num)
+            out["o"][sl, h] = a["o"]
+            out["e_D"][sl, h] = a["e_D"]
+            out["dq_dir"][sl, h] = rotate_back_fp64(a["dq_dir"]) if num.hadamard else a["dq_dir"]
+            dv_w[sl, hk] += a["dv"]
+            dv_raw[sl, hk] += (fw["peff"] / fw["l"][:, None]).T @ do_deq[sl, h]
+    out["dv"] = _bf16_span(dv_raw, dv_w) if num.round_outputs else dv_w
+    return out

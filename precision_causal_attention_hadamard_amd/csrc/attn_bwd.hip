@@ -576,6 +576,9 @@ __device__ __forceinline__ int dsk_off(int r, int chunk) {
 // wave of the pair forms dK for half of d over all 64 queries.  dQ^T is one
 // (d slice, query block) pair per wave.  K~ and V~ of the item stay in LDS and
 // are read as operands each step.
+// Grouped query attention: the item is (document, key tile, key/value head)
+// and the query-tile loop runs over each of the group's H / Hk query heads in
+// turn, so dK and dV sum the group in fp32 registers and are rounded once.
 template <int D, bool DET>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   constexpr int NS = D / 64;
@@ -606,14 +609,15 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   __shared__ int sKeB[4];
 
   const Problem& p = a.p;
-  const int H = p.H, T = p.T;
-  const int tile_idx = blockIdx.x / H, head = blockIdx.x % H;
+  const int H = p.H, T = p.T, Hk = p.Hk;
+  const int tile_idx = blockIdx.x / Hk, hk = blockIdx.x % Hk;
   if (tile_idx >= a.counts[1]) return;
   const int2 it = a.items[tile_idx];
   const int doc = it.x, u = it.y;
   const int s_d = p.cu[doc];
   const int L = p.cu[doc + 1] - s_d;
   const int k0 = u * BWD_BK;
+  const int h_first = hk * (H / Hk), h_end = h_first + H / Hk;   // the group's query heads
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
@@ -624,15 +628,18 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   const bool kv = j < L;
   const bool kb_active = k0 + 32 * kb < L;
   const int KB = 4 * u + kb;
-  const size_t rs = (size_t)H * D;
-  const size_t hT = (size_t)head * T + s_d;
-  const size_t doc0 = (size_t)s_d * rs + (size_t)head * D;
-  const uint32_t rs32 = (uint32_t)rs;
+  const size_t rs = (size_t)H * D;            // query side: [T,H,d], [H,T]
+  const size_t rsk = (size_t)Hk * D;          // key side: [T,Hk,d], [Hk,T]
+  const size_t hTk = (size_t)hk * T + s_d;
+  const size_t doc0k = (size_t)s_d * rsk + (size_t)hk * D;
+  const uint32_t rs32 = (uint32_t)rs, rsk32 = (uint32_t)rsk;
   const float c = p.c_log2;
-  const uint8_t* q_doc = a.q_codes + doc0;
-  const uint8_t* do_doc = a.do_codes + doc0;
-  const uint8_t* g_doc = reinterpret_cast<const uint8_t*>(a.g + doc0);
-  uint8_t* dq_doc = reinterpret_cast<uint8_t*>(a.dq_acc + doc0);
+  // query-side document bases of head 0; a head adds head * d elements
+  const size_t docq = (size_t)s_d * rs;
+  const uint8_t* q_doc = a.q_codes + docq;
+  const uint8_t* do_doc = a.do_codes + docq;
+  const uint8_t* g_doc = reinterpret_cast<const uint8_t*>(a.g + docq);
+  uint8_t* dq_doc = reinterpret_cast<uint8_t*>(a.dq_acc + docq);
 
   // ---- item start: K~ and V~ tiles (128 rows), swizzled code layout
   {
@@ -641,8 +648,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       const int ii = i % NI;
       const int o = ii * 1024 + 16 * lane;
       const int r = o / D, slot = (o % D) >> 4;
-      const uint32_t off = (uint32_t)min(k0 + r, L - 1) * rs32 + 16u * (uint32_t)(slot ^ code_key<D>(r));
-      dma16((i < NI ? a.k_codes : a.v_codes) + doc0 + off, (i < NI ? sK : sV) + ii * 1024);
+      const uint32_t off = (uint32_t)min(k0 + r, L - 1) * rsk32 + 16u * (uint32_t)(slot ^ code_key<D>(r));
+      dma16((i < NI ? a.k_codes : a.v_codes) + doc0k + off, (i < NI ? sK : sV) + ii * 1024);
     }
   }
   // ---- query tiles: code instruction `wave` (if any), bf16 instructions wave + 8 k, plane `wave`
@@ -663,39 +670,41 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     wcol[k] = 16u * (uint32_t)(slot ^ wide_key<D>(r));
   }
   const uint32_t last_c = (uint32_t)(L - 1) * rs32, last_w = 2u * last_c;
-  const int* const plane = wave == 0 ? a.kofs + hT
-                         : wave == 1 ? reinterpret_cast<const int*>(a.il8) + hT
-                         : wave == 2 ? reinterpret_cast<const int*>(a.delta) + hT
-                         : wave == 3 ? a.dq_sigma + hT : a.qexps + hT;
-  auto issue_tile = [&](auto Bc, int qt) {
+  const int* const plane = (wave == 0 ? a.kofs
+                          : wave == 1 ? reinterpret_cast<const int*>(a.il8)
+                          : wave == 2 ? reinterpret_cast<const int*>(a.delta)
+                          : wave == 3 ? a.dq_sigma : a.qexps) + s_d;
+  // query tile qt of query head h
+  auto issue_tile = [&](auto Bc, int qt, int h) {
     constexpr int B = decltype(Bc)::value;
     const int q0 = qt * BWD_BQ;
     const uint32_t q0c = (uint32_t)q0 * rs32, q0w = 2u * q0c;
+    const uint32_t hd = (uint32_t)h * D;
     if (has_c) {
-      const uint32_t off = min(q0c + crow, last_c) + ccol;
+      const uint32_t off = min(q0c + crow, last_c) + ccol + hd;
       dma16(q_doc + off, (B ? sQ1 : sQ0) + wave * 1024);
       dma16(do_doc + off, (B ? sO1 : sO0) + wave * 1024);
     }
 #pragma unroll
     for (int k = 0; k < NIW; ++k)
-      dma16(g_doc + (min(q0w + wrow[k], last_w) + wcol[k]), (B ? sG1 : sG0) + (wave + 8 * k) * 1024);
-    if (wave < NPLANES) dma4(plane + min(q0 + lane, L - 1), (B ? sR1 : sR0) + wave * BWD_BQ * 4);
+      dma16(g_doc + (min(q0w + wrow[k], last_w) + wcol[k] + 2u * hd), (B ? sG1 : sG0) + (wave + 8 * k) * 1024);
+    if (wave < NPLANES) dma4(plane + (size_t)h * T + min(q0 + lane, L - 1), (B ? sR1 : sR0) + wave * BWD_BQ * 4);
   };
 
   const int qt_first = k0 / BWD_BQ;
   const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
-  issue_tile(std::integral_constant<int, 0>{}, qt_first);
-  if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
+  issue_tile(std::integral_constant<int, 0>{}, qt_first, h_first);
+  if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hTk + k0 + 32 * tid] : E8M0_BIAS;
   int ke, ve, vke;
   {
-    const size_t mi = hT + min(j, L - 1);
+    const size_t mi = hTk + min(j, L - 1);
     ke = a.k_exp[mi];
     ve = a.v_exp[mi];
     vke = a.v_key_exp[mi];
   }
   const int e_key = vke - E8M0_BIAS;
   auto vkey = [&](int s2) {
-    const uint8_t* vr = a.v_key_codes + doc0 + (size_t)min(j, L - 1) * rs + 64 * s2 + 16 * hh;
+    const uint8_t* vr = a.v_key_codes + doc0k + (size_t)min(j, L - 1) * rsk + 64 * s2 + 16 * hh;
     return kv ? cat8(ld16(vr), ld16(vr + 32)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
   };
   full_barrier();
@@ -754,7 +763,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   const uint32_t fdst = 2u * (uint32_t)frow * rs32 + 4u * (uint32_t)fpair;
   // deterministic mode: plain stores into the step's own partial slot instead
   const int nq_doc = (L + BWD_BQ - 1) / BWD_BQ;
-  auto flush_dq = [&](int qtp) {
+  auto flush_dq = [&](int qtp, int h) {
     constexpr int NIT = BWD_BQ / (8 * RPI);
     const int q0p = qtp * BWD_BQ;
     const int nqp = min(BWD_BQ, L - q0p);
@@ -767,7 +776,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     if constexpr (DET) {
       const long long step = det_step(a.det_base[doc], u, qtp, nq_doc);
       if (step >= a.det_cap) return;      // the plan flags the overflow
-      uint8_t* const slot = reinterpret_cast<uint8_t*>(a.dq_part) + ((size_t)step * H + head) * (BWD_BQ * D * 2);
+      uint8_t* const slot = reinterpret_cast<uint8_t*>(a.dq_part) + ((size_t)step * H + h) * (BWD_BQ * D * 2);
 #pragma unroll
       for (int t2 = 0; t2 < NIT; ++t2) {
         const int row0 = RPI * (wave + 8 * t2);
@@ -780,11 +789,11 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       const int row0 = RPI * (wave + 8 * t2);        // uniform
       if (row0 + frow < nqp)
         __builtin_amdgcn_global_atomic_fadd_v2f16(
-            reinterpret_cast<v2h*>(dq_doc + (2u * (uint32_t)(q0p + row0) * rs32 + fdst)), hv[t2]);
+            reinterpret_cast<v2h*>(dq_doc + (2u * (uint32_t)(q0p + row0) * rs32 + fdst + 2u * (uint32_t)h * D)), hv[t2]);
     }
   };
 
-  auto step = [&](auto Bc, int qt) {
+  auto step = [&](auto Bc, int qt, int h) {
     constexpr int B = decltype(Bc)::value;
     const uint8_t* tQ = B ? sQ1 : sQ0;
     const uint8_t* tdO = B ? sO1 : sO0;
@@ -830,9 +839,16 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
                        dia ? vke : ve);
       }
     }
-    // the next tile streams in while this one is computed; last step's dQ goes out
-    if (qt + 1 < qt_end) issue_tile(std::integral_constant<int, 1 - B>{}, qt + 1);
-    if (qt > qt_first) flush_dq(qt - 1);
+    // the next tile streams in while this one is computed; last step's dQ
+    // goes out (steps run over the query tiles of one head, then the next head)
+    {
+      const bool wrap = qt + 1 >= qt_end;
+      const int nh = wrap ? h + 1 : h;
+      if (nh < h_end) issue_tile(std::integral_constant<int, 1 - B>{}, wrap ? qt_first : qt + 1, nh);
+      const bool first = qt == qt_first;
+      const int ph = first ? h - 1 : h;
+      if (ph >= h_first) flush_dq(first ? qt_end - 1 : qt - 1, ph);
+    }
     if (act) {
       float dsv[16];
       uint32_t pe[8];      // bf16 pairs of P^_eff * 2^8, accumulator register order
@@ -972,13 +988,13 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     full_barrier();
   };
 
-  for (int qt = qt_first;;) {
-    step(std::integral_constant<int, 0>{}, qt);
-    if (++qt >= qt_end) break;
-    step(std::integral_constant<int, 1>{}, qt);
-    if (++qt >= qt_end) break;
+  for (int qt = qt_first, h = h_first;;) {
+    step(std::integral_constant<int, 0>{}, qt, h);
+    if (++qt >= qt_end) { qt = qt_first; if (++h >= h_end) break; }
+    step(std::integral_constant<int, 1>{}, qt, h);
+    if (++qt >= qt_end) { qt = qt_first; if (++h >= h_end) break; }
   }
-  flush_dq(qt_end - 1);
+  flush_dq(qt_end - 1, h_end - 1);
 
   // ---- item end: the two query-half dV partials of each key block meet in
   // the (now free) bf16 tile buffers, key blocks 0-1 first, then 2-3; then dK
@@ -1003,7 +1019,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int jk = k0 + 32 * kb + 8 * q4 + 4 * hh + r;
-            if (jk < L) a.dv[doc0 + (size_t)jk * rs + 32 * db + n] = f32_to_bf16_bits(dv[db][4 * q4 + r] + o[r]);
+            if (jk < L) a.dv[doc0k + (size_t)jk * rsk + 32 * db + n] = f32_to_bf16_bits(dv[db][4 * q4 + r] + o[r]);
           }
         }
     }
@@ -1040,7 +1056,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
       }
       if (p.hadamard) fwht_quarter_row<D>(x, part);
-      store_bf16<E>(a.dk + doc0 + (size_t)jk * rs + part * E, x);
+      store_bf16<E>(a.dk + doc0k + (size_t)jk * rsk + part * E, x);
     }
   }
 }
@@ -1056,7 +1072,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
             static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv),
             static_cast<uint16_t*>(in.dq_part), in.det_base, in.det_cap, static_cast<const uint16_t*>(in.q_x),
             static_cast<const uint16_t*>(in.k_x), in.qk_scale};
-  dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.H);
+  dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.Hk);   // the mixed path has Hk = H
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };
   if (p.path == 1) {
     if (p.D == 64) go(attn_bwd_kernel<64, 1>); else go(attn_bwd_kernel<128, 1>);

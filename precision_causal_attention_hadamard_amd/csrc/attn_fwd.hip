@@ -1,7 +1,8 @@
 // Forward kernel of the causal block-scaled MXFP8 attention call.
 //
 // One workgroup (4 waves) per work item (document, 128-query tile, head),
-// items taken longest first from the GPU-built list.  Wave w owns the 32
+// items taken longest first from the GPU-built list.  With grouped query
+// attention the K-side operands are those of key/value head h / (H / Hk).  Wave w owns the 32
 // queries of document-local block 4t + w.  The kernel steps over 64-key tiles
 // from the document start to the diagonal.  Per step:
 //   * K~ and V~ codes (and, on the two diagonal key tiles, the per-key V
@@ -82,9 +83,13 @@ attn_fwd_kernel(FwdArgs a) {
   const int QB = 4 * qt + wave;              // this wave's query block
   const size_t rs = (size_t)H * D;           // token stride of [T,H,d] codes
   const size_t hT = (size_t)head * T + s_d;  // base of [H,T] metadata of this doc/head
-  const uint8_t* kdoc = a.k_codes + (size_t)s_d * rs + (size_t)head * D;
-  const uint8_t* vdoc = a.v_codes + (size_t)s_d * rs + (size_t)head * D;
-  const uint8_t* vkdoc = a.v_key_codes + (size_t)s_d * rs + (size_t)head * D;
+  // K side: the key/value head of this query head ([T,Hk,d] codes, [Hk,T] metadata)
+  const int hk = head / (H / p.Hk);
+  const size_t rsk = (size_t)p.Hk * D;
+  const size_t hTk = (size_t)hk * T + s_d;
+  const uint8_t* kdoc = a.k_codes + (size_t)s_d * rsk + (size_t)hk * D;
+  const uint8_t* vdoc = a.v_codes + (size_t)s_d * rsk + (size_t)hk * D;
+  const uint8_t* vkdoc = a.v_key_codes + (size_t)s_d * rsk + (size_t)hk * D;
 
   // Q~ as the B operand of S^T = K~ Q~^T (lane = query column)
   v8i qa[PATH ? 1 : NS];
@@ -107,7 +112,7 @@ attn_fwd_kernel(FwdArgs a) {
         qb[s] = __builtin_bit_cast(v8bf, e2m1x8_times_bf16(codes, sc));
       }
     }
-    vref = (int)a.v_ref_exp[hT + i] - E8M0_BIAS;
+    vref = (int)a.v_ref_exp[hTk + i] - E8M0_BIAS;
   } else {
     if constexpr (PATH == 0) {
 #pragma unroll
@@ -131,8 +136,8 @@ attn_fwd_kernel(FwdArgs a) {
   v4i pk[NCH], pv[NCH], pvk[NCH];
   uint32_t psf = 0;           // mixed path: group scales of the prefetched NVFP4 chunk
   uint8_t pke = 0, pve = 0, pvke = 0;
-  const uint8_t* k4doc = PATH ? a.f4.k_fp4 + ((size_t)s_d * rs + (size_t)head * D) / 2 : nullptr;
-  const uint8_t* ksfdoc = PATH ? a.f4.k_sf + ((size_t)s_d * rs + (size_t)head * D) / 16 : nullptr;
+  const uint8_t* k4doc = PATH ? a.f4.k_fp4 + ((size_t)s_d * rsk + (size_t)hk * D) / 2 : nullptr;
+  const uint8_t* ksfdoc = PATH ? a.f4.k_sf + ((size_t)s_d * rsk + (size_t)hk * D) / 16 : nullptr;
   auto prefetch = [&](int kt) {
     const int j0 = kt * FWD_BK;
     const int nvalid = min(FWD_BK, L - j0);
@@ -142,7 +147,7 @@ attn_fwd_kernel(FwdArgs a) {
       const int ch = tid + FWD_THREADS * c2;
       const int r = ch / (D / 16), c16 = ch % (D / 16);
       const bool ok = r < nvalid;
-      const size_t off = (size_t)(j0 + r) * rs + 16 * c16;
+      const size_t off = (size_t)(j0 + r) * rsk + 16 * c16;
       if constexpr (PATH == 0) pk[c2] = ok ? ld16(kdoc + off) : v4i{0, 0, 0, 0};
       pv[c2] = ok ? ld16(vdoc + off) : v4i{0, 0, 0, 0};
       pvk[c2] = (ok && diag_tile) ? ld16(vkdoc + off) : v4i{0, 0, 0, 0};
@@ -153,15 +158,15 @@ attn_fwd_kernel(FwdArgs a) {
       if (tid < FWD_BK * CPR) {
         const int r = tid / CPR, c4 = tid % CPR;
         const bool ok = r < nvalid;
-        pk[0] = ok ? ld16(k4doc + (size_t)(j0 + r) * rs / 2 + 16 * c4) : v4i{0, 0, 0, 0};
-        psf = ok ? *reinterpret_cast<const uint16_t*>(ksfdoc + (size_t)(j0 + r) * rs / 16 + 2 * c4) : 0u;
+        pk[0] = ok ? ld16(k4doc + (size_t)(j0 + r) * rsk / 2 + 16 * c4) : v4i{0, 0, 0, 0};
+        psf = ok ? *reinterpret_cast<const uint16_t*>(ksfdoc + (size_t)(j0 + r) * rsk / 16 + 2 * c4) : 0u;
       }
     }
     if (tid < FWD_BK) {
       const bool kv = tid < nvalid;
-      pke = kv ? a.k_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
-      pve = kv ? a.v_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
-      pvke = (kv && diag_tile) ? a.v_key_exp[hT + j0 + tid] : (uint8_t)E8M0_BIAS;
+      pke = kv ? a.k_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
+      pve = kv ? a.v_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
+      pvke = (kv && diag_tile) ? a.v_key_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
     }
   };
   auto commit = [&](int buf, bool diag_tile) {

@@ -36,7 +36,12 @@ flamia_status validate(const flamia_attn_desc* d) {
   if ((d->hadamard | d->causal_dq_scale | d->deterministic | d->causal) & ~1) return FLAMIA_ERR_INVALID_ARG;
   if (d->path != 0 && d->path != 1) return FLAMIA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
+  if (d->num_kv_heads < 0 || d->num_kv_heads > d->num_heads ||
+      (d->num_kv_heads > 0 && d->num_heads % d->num_kv_heads != 0))
+    return FLAMIA_ERR_INVALID_ARG;
   if (d->causal != 1) return FLAMIA_ERR_UNSUPPORTED;
+  // grouped query attention is built for the MXFP8 path only
+  if (d->path == 1 && d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads) return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
   // sort key, costs into 20 bits, grid x into 31 bits
   if (d->num_docs >= (1 << 24) || d->total_tokens >= (1 << 24)) return FLAMIA_ERR_WORKSPACE;
@@ -66,13 +71,17 @@ struct QLayout {
   size_t codes[4], exps[5], plan, fp4[2], sf[2], qk_scale, fx[2], bytes;
 };
 
+inline int kv_heads(const flamia_attn_desc* d) { return d->num_kv_heads > 0 ? d->num_kv_heads : d->num_heads; }
+
 QLayout q_layout(const flamia_attn_desc* d) {
   QLayout q{};
   const size_t E = (size_t)d->total_tokens * d->num_heads * d->head_dim;
   const size_t M = (size_t)d->total_tokens * d->num_heads;
+  const size_t Ek = (size_t)d->total_tokens * kv_heads(d) * d->head_dim;   // K, V: [T, Hk, d]
+  const size_t Mk = (size_t)d->total_tokens * kv_heads(d);
   size_t off = 0;
-  for (int i = 0; i < 4; ++i) { q.codes[i] = off; off = align_up(off + E); }
-  for (int i = 0; i < 5; ++i) { q.exps[i] = off; off = align_up(off + M); }
+  for (int i = 0; i < 4; ++i) { q.codes[i] = off; off = align_up(off + (i == 0 ? E : Ek)); }
+  for (int i = 0; i < 5; ++i) { q.exps[i] = off; off = align_up(off + (i == 0 ? M : Mk)); }
   q.plan = off;
   off = align_up(off + plan_layout(d).bytes);
   q.fp4[0] = q.fp4[1] = q.sf[0] = q.sf[1] = q.qk_scale = q.fx[0] = q.fx[1] = 0;
@@ -114,6 +123,7 @@ Problem problem(const flamia_attn_desc* d) {
   p.T = d->total_tokens;
   p.ndocs = d->num_docs;
   p.H = d->num_heads;
+  p.Hk = kv_heads(d);
   p.D = d->head_dim;
   p.hadamard = d->hadamard;
   p.causal_dq_scale = d->causal_dq_scale;

@@ -31,6 +31,7 @@ struct BwdLayout {
 struct Problem {
   const int* cu;
   int T, ndocs, H, D;
+  int Hk;                  // key/value heads (= H, or a divisor of H: grouped query attention)
   int hadamard, causal_dq_scale, path;
   int deterministic;       // dQ from per-step partials added in a fixed order
   float softmax_scale;     // fp32 softmax scale
@@ -76,7 +77,7 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
 // Everything the backward kernel reads and writes.
 struct BwdInputs {
   const uint8_t *q_codes, *k_codes, *v_codes, *v_key_codes;
-  const uint8_t *k_exp, *v_exp, *v_key_exp;
+  const uint8_t *k_exp, *v_exp, *v_key_exp;   // [Hk, T]
   const int* kofs;         // [H, T] 8 - integer row maximum
   const float* il8;        // [H, T] 2^-8 / l
   const float* delta;      // [H, T] -D

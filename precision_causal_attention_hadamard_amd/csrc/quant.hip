@@ -2,7 +2,8 @@
 //
 // quant_qkv_kernel: one workgroup per (32-token chunk of the packed array,
 // tensor in {Q, K, V}); it quantizes every document-local 32-token block
-// that STARTS in its chunk, for all heads (wave w takes heads w, w+4, ...).
+// that STARTS in its chunk, for all heads of the tensor (wave w takes heads
+// w, w+4, ...; K and V have the key/value heads).
 // A block never crosses a document, so a document boundary may fall
 // anywhere inside a chunk and a block may run past the chunk's end.
 // Per (block, head): load 32 rows x d bf16 (lane = (row, half-row)),
@@ -154,7 +155,7 @@ amax_qk_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __rest
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
   const int c0 = blockIdx.x * TOKEN_BLOCK;
-  const int H = p.H, T = p.T;
+  const int H = tensor == 0 ? p.H : p.Hk, T = p.T;
   float m = 0.f;
   for_blocks_in_chunk(p.cu, p.ndocs, T, c0, [&](int bs, int be, int, int) {
     const int tok = bs + row;
@@ -231,7 +232,7 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
   const int c0 = blockIdx.x * TOKEN_BLOCK;
-  const int H = p.H, T = p.T;
+  const int H = tensor == 0 ? p.H : p.Hk, T = p.T;      // K and V carry the key/value heads
 
   for_blocks_in_chunk(p.cu, p.ndocs, T, c0, [&](int bs, int be, int, int) {
     const int tok = bs + row;
@@ -301,12 +302,14 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
       float x[D / 2];
       load_half_row<D>(dout + off, valid, x);
       const int e = roundup_exp(wave_max(half_row_amax<D>(x)));
-      // largest K and V block exponents over the visible key blocks
+      // largest K and V block exponents over the visible key blocks (of the
+      // key/value head this query head reads)
+      const size_t hkT = (size_t)(h / (H / p.Hk)) * T;
       int emax_kv = -254;
       {
         int ek = -127, ev = -127;
         for (int J = lane; J < nvis; J += 64) {
-          const size_t t0 = (size_t)h * T + ds + J * TOKEN_BLOCK;
+          const size_t t0 = hkT + ds + J * TOKEN_BLOCK;
           ek = max(ek, (int)k_exp[t0] - E8M0_BIAS);
           ev = max(ev, (int)v_exp[t0] - E8M0_BIAS);
         }
@@ -353,7 +356,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
           delta[mi] = -dsum;           // the backward adds -D
           il8[mi] = ginv;
           kofs[mi] = 8 - row_max[mi];    // -P_EXP - m~: P 2^8 = exp2(fract S') 2^(floor S' + kofs)
-          qexps[mi] = (int)q_exp[mi] | ((e + E8M0_BIAS) << 8) | ((int)v_ref_exp[mi] << 16);
+          qexps[mi] = (int)q_exp[mi] | ((e + E8M0_BIAS) << 8) | ((int)v_ref_exp[hkT + tok] << 16);
           // |dQ partial sum| <= 2.2 d 448^3 2^(e_dO + e_V + e_K) < 2^(27.6 + log2 d + ...);
           // the prescale keeps it below 2^15 in fp16
           dq_sigma[mi] = e + emax_kv + LOG2D + 13;

@@ -33,7 +33,8 @@ class AttnDesc(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("hadamard", ctypes.c_int32), ("causal_dq_scale", ctypes.c_int32),
-                ("deterministic", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("deterministic", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("num_kv_heads", ctypes.c_int32)]
 
 
 class QTensors(ctypes.Structure):
@@ -98,11 +99,12 @@ def _stream(stream=None):
 
 def make_desc(cu_seqlens_dev: torch.Tensor, total_tokens: int, num_docs: int, max_doc_len: int,
               num_heads: int, head_dim: int, hadamard: bool = False, causal_dq_scale: bool = False,
-              softmax_scale: float = 0.0, path: int = 0, causal: int = 1, deterministic: int = 0) -> AttnDesc:
+              softmax_scale: float = 0.0, path: int = 0, causal: int = 1, deterministic: int = 0,
+              num_kv_heads: int = 0) -> AttnDesc:
     return AttnDesc(total_tokens, num_docs, max_doc_len,
                     cu_seqlens_dev.data_ptr() if cu_seqlens_dev is not None else None,
                     num_heads, head_dim, causal, path, int(hadamard), int(causal_dq_scale),
-                    deterministic, softmax_scale)
+                    deterministic, softmax_scale, num_kv_heads)
 
 
 def buffer_sizes(desc: AttnDesc):
@@ -171,19 +173,22 @@ def status_string(status: int) -> str:
 
 class TrainingCall:
     """Device buffers and the three calls of one packed attention training
-    step (quantize, forward, backward).  Inputs are bf16 ``[T, H, d]`` CUDA
-    tensors; ``cu_seqlens`` a list of ints."""
+    step (quantize, forward, backward).  Inputs are bf16 CUDA tensors, q and
+    do ``[T, H, d]``, k and v ``[T, Hk, d]`` (Hk dividing H: grouped query
+    attention when Hk < H); ``cu_seqlens`` a list of ints."""
 
     def __init__(self, q, k, v, do, cu_seqlens, hadamard=False, causal_dq_scale=False,
                  softmax_scale=0.0, path=0, deterministic=False):
         dev = q.device
         self.q, self.k, self.v, self.do = q, k, v, do
         T, H, d = q.shape
+        Hk = k.shape[1]
         self.cu_list = [int(c) for c in cu_seqlens]
         self.cu = torch.tensor(self.cu_list, dtype=torch.int32, device=dev)
         lens = [b - a for a, b in zip(self.cu_list, self.cu_list[1:])]
         self.desc = make_desc(self.cu, T, len(lens), max(lens) if lens else 0, H, d, hadamard,
-                              causal_dq_scale, softmax_scale, path, deterministic=int(deterministic))
+                              causal_dq_scale, softmax_scale, path, deterministic=int(deterministic),
+                              num_kv_heads=Hk)
         qb, fb, bb = buffer_sizes(self.desc)
         self.qbuf = torch.empty(qb, dtype=torch.uint8, device=dev)
         self.qt = qtensors_layout(self.desc, self.qbuf)
@@ -193,9 +198,10 @@ class TrainingCall:
         self.row_max = torch.empty(H, T, dtype=torch.int32, device=dev)
         self.row_sum = torch.empty(H, T, dtype=torch.float32, device=dev)
         self.dq = torch.empty_like(q)
-        self.dk = torch.empty_like(q)
-        self.dv = torch.empty_like(q)
+        self.dk = torch.empty_like(k)
+        self.dv = torch.empty_like(v)
         self.shape = (T, H, d)
+        self.kv_heads = Hk
 
     def quantize(self, stream=None):
         quantize(self.desc, self.q, self.k, self.v, self.qt, stream)
@@ -222,12 +228,17 @@ class TrainingCall:
         off = getattr(self.qt, field) - self.qbuf.data_ptr()
         return self.qbuf[off:off + nbytes]
 
+    def _heads(self, field: str) -> int:
+        return self.shape[1] if field.startswith("q") else self.kv_heads
+
     def codes(self, field: str) -> torch.Tensor:
-        T, H, d = self.shape
+        T, _, d = self.shape
+        H = self._heads(field)
         return self._view(field, T * H * d).view(T, H, d)
 
     def exps(self, field: str) -> torch.Tensor:
-        T, H, _ = self.shape
+        T = self.shape[0]
+        H = self._heads(field)
         return self._view(field, T * H).view(H, T)
 
     def nvfp4(self, which: str):

@@ -51,6 +51,10 @@ class Workload:
     def doc_lens(self) -> list:
         return [b - a for a, b in zip(self.cu_seqlens, self.cu_seqlens[1:])]
 
+    @property
+    def has_outliers(self) -> bool:
+        return bool(self.notes.get("outlier_scale"))
+
     def causal_pairs(self) -> int:
         """Number of (query, key) pairs the causal call computes, all heads."""
         return self.heads * sum(L * (L + 1) // 2 for L in self.doc_lens)
@@ -105,31 +109,38 @@ def _cu(lens) -> list:
     return [0] + list(np.cumsum(lens).astype(int).tolist())
 
 
-def config(k: int, seed: int | None = None) -> Workload:
-    """The five workloads of the call (k = 1..5)."""
+def config(k: int, seed: int | None = None, kv_heads: int = 0) -> Workload:
+    """The five workloads of the call (k = 1..5).  ``kv_heads`` (0 = one per
+    query head) gives the grouped-query variant: K and V drawn with that many
+    heads, everything else as in the plain workload."""
     seed = SEED_BASE + k if seed is None else seed
     rng = np.random.default_rng(seed)
+
+    def wl(name, q, kk, v, do, cu, heads, d, **kw):
+        if kv_heads and kv_heads != heads:
+            name = name.replace(f"_h{heads}_", f"_h{heads}_kv{kv_heads}_")
+        return Workload(name, q, kk, v, do, cu, heads, d, **kw)
+
     if k == 1:   # tiny: one 256-token document, 2 heads, head dim 64
-        q, kk, v, do = draw_tensors(rng, 256, 2, 64)
-        return Workload("tiny_1x256_h2_d64", q, kk, v, do, [0, 256], 2, 64)
+        q, kk, v, do = draw_tensors(rng, 256, 2, 64, kv_heads=kv_heads)
+        return wl("tiny_1x256_h2_d64", q, kk, v, do, [0, 256], 2, 64)
     if k == 2:   # batch 2 x 4096, 16 heads, d 128, 1% outlier channels x20, Hadamard on
-        q, kk, v, do = draw_tensors(rng, 8192, 16, 128, outlier_scale=20.0)
-        return Workload("batched_2x4096_h16_d128_outliers_hadamard", q, kk, v, do,
-                        [0, 4096, 8192], 16, 128, hadamard=True)
+        q, kk, v, do = draw_tensors(rng, 8192, 16, 128, outlier_scale=20.0, kv_heads=kv_heads)
+        return wl("batched_2x4096_h16_d128_outliers_hadamard", q, kk, v, do,
+                  [0, 4096, 8192], 16, 128, hadamard=True, notes={"outlier_scale": 20.0})
     if k == 3:   # packed 4 rows x 16384, lognormal documents
-        q, kk, v, do = draw_tensors(rng, 65536, 16, 128)
+        q, kk, v, do = draw_tensors(rng, 65536, 16, 128, kv_heads=kv_heads)
         lens = []
         for _ in range(4):
             lens += lognormal_fill(rng, 16384)
-        return Workload("packed_4x16384_lognormal_h16_d128", q, kk, v, do, _cu(lens), 16, 128)
+        return wl("packed_4x16384_lognormal_h16_d128", q, kk, v, do, _cu(lens), 16, 128)
     if k == 4:   # long context 32768: two 12288-token docs + lognormal shorts
-        q, kk, v, do = draw_tensors(rng, 32768, 16, 128)
+        q, kk, v, do = draw_tensors(rng, 32768, 16, 128, kv_heads=kv_heads)
         lens = [12288, 12288] + lognormal_fill(rng, 8192)
-        return Workload("long_1x32768_h16_d128", q, kk, v, do, _cu(lens), 16, 128)
+        return wl("long_1x32768_h16_d128", q, kk, v, do, _cu(lens), 16, 128)
     if k == 5:   # mixed path, shapes of config 2, no outliers
-        q, kk, v, do = draw_tensors(rng, 8192, 16, 128)
-        return Workload("mixed_2x4096_h16_d128", q, kk, v, do, [0, 4096, 8192], 16, 128,
-                        path=1)
+        q, kk, v, do = draw_tensors(rng, 8192, 16, 128, kv_heads=kv_heads)
+        return wl("mixed_2x4096_h16_d128", q, kk, v, do, [0, 4096, 8192], 16, 128, path=1)
     raise ValueError(k)
 
 
@@ -143,4 +154,5 @@ def small_packed(seed: int, doc_lens, heads: int = 2, head_dim: int = 64,
     q, kk, v, do = draw_tensors(rng, T, heads, head_dim, outlier_scale, kv_heads)
     kvs = f"_kv{kv_heads}" if kv_heads and kv_heads != heads else ""
     return Workload(f"packed_{'_'.join(map(str, doc_lens))}_h{heads}{kvs}_d{head_dim}", q, kk, v, do,
-                    _cu(doc_lens), heads, head_dim, hadamard=hadamard, path=path)
+                    _cu(doc_lens), heads, head_dim, hadamard=hadamard, path=path,
+                    notes={"outlier_scale": outlier_scale} if outlier_scale else {})

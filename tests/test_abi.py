@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def base_desc(**kw):
     fake_cu = ctypes.c_void_p(0x1000)   # never dereferenced by host-side validation
-    d = flamia.AttnDesc(256, 1, 256, fake_cu.value, 2, 64, 1, 0, 0, 0, 0, 0.0)
+    d = flamia.AttnDesc(256, 1, 256, fake_cu.value, 2, 64, 1, 0, 0, 0, 0, 0.0, 0)
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -57,10 +57,31 @@ def test_buffer_sizes_valid(lib):
     ("head_dim", 96, 1), ("head_dim", 256, 1), ("num_heads", 0, 1), ("num_docs", 0, 1),
     ("total_tokens", -1, 1), ("max_doc_len", 300, 1), ("hadamard", 2, 1),
     ("causal", 0, 2), ("deterministic", 2, 1), ("path", 7, 1),
+    ("num_kv_heads", -1, 1), ("num_kv_heads", 3, 1),
 ])
 def test_invalid_and_unsupported_descriptors(lib, field, value, want):
     st, _, _ = sizes_status(lib, base_desc(**{field: value}))
     assert st == want, (field, value, st)
+
+
+def test_grouped_query_heads_validation_and_layout(lib):
+    """num_kv_heads: 0 or H is MHA; a proper divisor of H shrinks the K-side
+    buffers to Hk heads; a non-divisor is invalid; the mixed path rejects
+    grouping as unsupported."""
+    T, d = 256, 64
+    full = sizes_status(lib, base_desc(num_heads=6))
+    assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=6))[1:] == full[1:]
+    assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=4))[0] == 1
+    st, q, b = sizes_status(lib, base_desc(num_heads=6, num_kv_heads=2))
+    assert st == 0 and b == full[2]                 # the backward workspace is per query head
+    assert full[1] - q >= 3 * T * 4 * d + 4 * T * 4   # three K-side code tensors, four exponent planes
+    assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=2, path=1))[0] == 2
+    assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=6, path=1))[0] == 0
+    qt = flamia.QTensors()
+    dg = base_desc(num_heads=6, num_kv_heads=2)
+    assert lib.flamia_qtensors_layout(ctypes.byref(dg), ctypes.c_void_p(0x100000), ctypes.byref(qt)) == 0
+    assert qt.k_codes - qt.q_codes >= T * 6 * d and qt.v_codes - qt.k_codes == T * 2 * d
+    assert qt.k_exp - qt.q_exp == T * 6 and qt.v_exp - qt.k_exp == T * 2
 
 
 def causal_steps(L, bq=64, bk=128):

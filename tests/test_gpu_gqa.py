@@ -1,0 +1,140 @@
+"""Grouped query attention on the GPU (K and V with Hk < H heads), through the
+C ABI, against the CPU oracle.
+
+The bar is that of the plain call: codes, exponent bytes and the fold
+reference bit for bit (the K side has Hk heads); O, dQ, dK, dV to max-abs
+relative error 2e-2 and cosine 0.999 as decision_compare.py applies it; the
+integer row maximum and l as there.
+Two checks need no oracle: a grouped call computes, per query head, exactly
+what the plain call computes on K and V repeated per query head, so O, the row
+statistics and (in deterministic mode, where the dQ reduction order is fixed)
+dQ agree bit for bit; and dK, dV of a key/value head are the sums of the
+repeated call's per-head dK, dV up to one bf16 rounding of each side.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decision_compare as DCMP
+from oracle import attention as A
+from oracle import decisions as DC
+from precision_causal_attention_hadamard_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def np_inputs(wl):
+    return [t.float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
+
+
+def run_gpu(lib, wl, deterministic=False, k=None, v=None):
+    dev = torch.device("cuda")
+    q, do = wl.q.to(dev), wl.do.to(dev)
+    k = (wl.k if k is None else k).to(dev)
+    v = (wl.v if v is None else v).to(dev)
+    call = lib.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard, deterministic=deterministic)
+    call.step()
+    torch.cuda.synchronize()
+    return call
+
+
+def check_against_oracle(call, wl, tag):
+    q, k, v, do = np_inputs(wl)
+    num = A.Numerics(hadamard=wl.hadamard)
+    ref = A.training_call(q, k, v, do, wl.cu_seqlens, num)
+    al = DC.allowances(q, k, v, do, wl.cu_seqlens, num)
+    for f in ("q_codes", "k_codes", "v_codes", "v_key_codes"):
+        np.testing.assert_array_equal(call.codes(f).cpu().numpy(), ref[f], err_msg=f)
+    for f in ("q_exp", "k_exp", "v_exp", "v_key_exp", "v_ref_exp"):
+        np.testing.assert_array_equal(call.exps(f).cpu().numpy().astype(np.int64), ref[f] + 127, err_msg=f)
+    outs = {n: getattr(call, n).float().cpu().numpy() for n in ("o", "dq", "dk", "dv")}
+    for n in outs:
+        assert outs[n].shape == ref[n].shape, (n, outs[n].shape, ref[n].shape)
+    DCMP.check_outputs(outs, ref, al, f"gqa {tag}", outliers=wl.has_outliers)
+    rm = call.row_max.cpu().numpy().astype(np.int64)
+    assert np.all(np.abs(rm - ref["row_max"]) <= 1)
+    assert (rm != ref["row_max"]).mean() <= 1e-3
+    np.testing.assert_allclose(call.row_sum.cpu().numpy(), ref["row_sum"], rtol=1e-3)
+
+
+CASES = {
+    "h4_kv2_d64_ragged": lambda: W.small_packed(41, [1, 17, 45, 100, 33, 64, 130, 2], heads=4, head_dim=64,
+                                                kv_heads=2),
+    "h6_kv2_d128_hadamard_outliers": lambda: W.small_packed(42, [300, 211], heads=6, head_dim=128,
+                                                            outlier_scale=20.0, hadamard=True, kv_heads=2),
+    "h4_kv1_d128_ragged": lambda: W.small_packed(43, [129, 64, 31, 250], heads=4, head_dim=128, kv_heads=1),
+    "h3_kv1_d64_one_tile": lambda: W.small_packed(44, [97], heads=3, head_dim=64, kv_heads=1),
+}
+
+
+@pytest.mark.parametrize("det", [False, True], ids=["atomic", "deterministic"])
+@pytest.mark.parametrize("case", list(CASES))
+def test_gqa_parity_small(gpu_lib, case, det):
+    print(f"[gqa] case={case} deterministic={det}", flush=True)
+    wl = CASES[case]()
+    assert wl.kv_heads < wl.heads
+    call = run_gpu(gpu_lib, wl, deterministic=det)
+    check_against_oracle(call, wl, case)
+
+
+@pytest.mark.parametrize("case", ["h4_kv2_d64_ragged", "h6_kv2_d128_hadamard_outliers"])
+def test_gqa_equals_repeated_heads(gpu_lib, case):
+    """The grouped call against the plain call on K, V repeated per query
+    head, both deterministic: O, row statistics and dQ bit for bit; dK, dV of
+    a key/value head within two bf16 roundings of the repeated call's group
+    sum (the grouped call sums in fp32 and rounds once)."""
+    wl = CASES[case]()
+    g = wl.heads // wl.kv_heads
+    grouped = run_gpu(gpu_lib, wl, deterministic=True)
+    rep = run_gpu(gpu_lib, wl, deterministic=True, k=wl.k.repeat_interleave(g, dim=1),
+                  v=wl.v.repeat_interleave(g, dim=1))
+    for n in ("o", "dq", "row_max", "row_sum"):
+        assert torch.equal(getattr(grouped, n), getattr(rep, n)), n
+    T, d = wl.total_tokens, wl.head_dim
+    for n in ("dk", "dv"):
+        got = getattr(grouped, n).double().cpu()
+        terms = getattr(rep, n).double().cpu().view(T, wl.kv_heads, g, d)
+        want = terms.sum(dim=2)
+        # each repeated-call term carries one bf16 rounding (relative 2^-8), the
+        # grouped result one more; fp32 accumulation order adds far less
+        bound = 2.0 ** -8 * (terms.abs().sum(dim=2) + got.abs())
+        assert torch.all((got - want).abs() <= bound), (n, float((got - want).abs().max()))
+
+
+def test_gqa_deterministic_repeatable(gpu_lib):
+    wl = CASES["h6_kv2_d128_hadamard_outliers"]()
+    call = run_gpu(gpu_lib, wl, deterministic=True)
+    first = {n: getattr(call, n).clone() for n in ("o", "dq", "dk", "dv")}
+    call.step()
+    torch.cuda.synchronize()
+    for n, t in first.items():
+        assert torch.equal(getattr(call, n), t), n
+
+
+def test_gqa_fullsize_sampled(gpu_lib):
+    """The grouped variant of the 2 x 4096-token, 16-head, d = 128 outlier
+    workload with 4 key/value heads, whole call on the GPU; the oracle
+    recomputes document 1 for key/value head 3 and its four query heads."""
+    wl = W.config(2, kv_heads=4)
+    print(f"[gqa] fullsize {wl.name}: GPU call", flush=True)
+    call = run_gpu(gpu_lib, wl)
+    doc, hk, g = 1, 3, wl.heads // wl.kv_heads
+    qh = list(range(hk * g, hk * g + g))
+    s, e = wl.cu_seqlens[doc], wl.cu_seqlens[doc + 1]
+    arrs = [wl.q[s:e][:, qh], wl.k[s:e][:, [hk]], wl.v[s:e][:, [hk]], wl.do[s:e][:, qh]]
+    arrs = [t.float().numpy().astype(np.float64) for t in arrs]
+    print("[gqa] fullsize: oracle slice", flush=True)
+    num = A.Numerics(hadamard=wl.hadamard)
+    ref = A.training_call(*arrs, [0, e - s], num)
+    al = DC.allowances(*arrs, [0, e - s], num)
+    hq, hkv = torch.tensor(qh), torch.tensor([hk])
+    np.testing.assert_array_equal(call.codes("k_codes")[s:e].cpu()[:, hkv].numpy(), ref["k_codes"])
+    np.testing.assert_array_equal(call.codes("q_codes")[s:e].cpu()[:, hq].numpy(), ref["q_codes"])
+    np.testing.assert_array_equal(call.exps("v_ref_exp").cpu()[hkv][:, s:e].numpy().astype(np.int64),
+                                  ref["v_ref_exp"] + 127)
+    outs = {n: getattr(call, n)[s:e].cpu()[:, hs].float().numpy()
+            for n, hs in (("o", hq), ("dq", hq), ("dk", hkv), ("dv", hkv))}
+    DCMP.check_outputs(outs, ref, al, "gqa fullsize", outliers=wl.has_outliers)
+    rm = call.row_max.cpu()[hq][:, s:e].numpy().astype(np.int64)
+    assert np.all(np.abs(rm - ref["row_max"]) <= 1) and (rm != ref["row_max"]).mean() <= 1e-3
