@@ -146,6 +146,8 @@ typedef struct flamia_qtensors {
  *   fwd_ws_bytes  : workspace of flamia_attn_fwd (may be 0; pass NULL then).
  *   bwd_ws_bytes  : workspace of flamia_attn_bwd (quantized dO, D, dO/l,
  *                   fp16 dQ accumulator, fp32 dK staging, prescale exponents;
+ *                   with grouped query attention on a grid too small to fill
+ *                   the GPU, also fp32 dV partials of the split groups;
  *                   in deterministic mode also the dQ partial slots: 64 x d
  *                   fp16 per head for at most ceil(T M / 16384) + ceil(3T / 128)
  *                   + 2 num_docs steps, M = max_doc_len, a bound of the causal
@@ -241,7 +243,11 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
  *   to dv), dK and dQ (fp16 accumulator in ws).  On the MXFP8 path dK is
  *   written to dk as bf16, rotated back when the Hadamard option is on; on
  *   the mixed path it goes to fp32 staging in ws and dk is not written here.
- *   Everything else it reads is in qt and ws.  One launch.
+ *   Everything else it reads is in qt and ws.  One launch; two when grouped
+ *   query attention splits each key/value head's group over several items
+ *   (fewer than 512 (document, key tile, key/value head) items): the kernel
+ *   then leaves fp32 dK/dV partials in ws and a second launch adds them in a
+ *   fixed order and writes dk, dv (still rounded once, still deterministic).
  * flamia_attn_bwd_finish -- dQ to bf16 (rotated back when the Hadamard
  *   option is on; in deterministic mode first summed from the partial slots);
  *   on the mixed path also dK from its staging.  Reads the plan in qt.  One

@@ -68,9 +68,11 @@ struct BwdArgs {
   const uint8_t* do_codes;
   const uint16_t* g;
   uint16_t* dq_acc;
-  float* dk_f32;          // mixed path: fp32 dK staging
+  float* dk_f32;          // mixed path: fp32 dK staging; split groups: fp32 dK partials
   uint16_t* dk;           // MXFP8 path: bf16 dK
   uint16_t* dv;
+  float* dv_f32;          // split groups: fp32 dV partials [gsplit, T, Hk, d]
+  int gsplit;             // items per key/value head group
   uint16_t* dq_part;      // deterministic mode: fp16 dQ partial slots
   const int* det_base;    // deterministic mode: first step of each document
   int det_cap;            // deterministic mode: steps per head in dq_part
@@ -576,9 +578,12 @@ __device__ __forceinline__ int dsk_off(int r, int chunk) {
 // wave of the pair forms dK for half of d over all 64 queries.  dQ^T is one
 // (d slice, query block) pair per wave.  K~ and V~ of the item stay in LDS and
 // are read as operands each step.
-// Grouped query attention: the item is (document, key tile, key/value head)
-// and the query-tile loop runs over each of the group's H / Hk query heads in
-// turn, so dK and dV sum the group in fp32 registers and are rounded once.
+// Grouped query attention: the item is (document, key tile, key/value head,
+// part) and the query-tile loop runs over the part's query heads in turn, so
+// dK and dV sum them in fp32 registers.  With one part per group (the usual
+// case) they are rounded once here; when the grid would be too small the
+// group is split over gsplit items, which store fp32 partials that a reduce
+// kernel adds in order and rounds once.
 template <int D, bool DET>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   constexpr int NS = D / 64;
@@ -610,14 +615,15 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 
   const Problem& p = a.p;
   const int H = p.H, T = p.T, Hk = p.Hk;
-  const int tile_idx = blockIdx.x / Hk, hk = blockIdx.x % Hk;
+  const int tile_idx = blockIdx.x / (Hk * a.gsplit), hk = (blockIdx.x / a.gsplit) % Hk;
   if (tile_idx >= a.counts[1]) return;
   const int2 it = a.items[tile_idx];
   const int doc = it.x, u = it.y;
   const int s_d = p.cu[doc];
   const int L = p.cu[doc + 1] - s_d;
   const int k0 = u * BWD_BK;
-  const int h_first = hk * (H / Hk), h_end = h_first + H / Hk;   // the group's query heads
+  const int hpp = H / Hk / a.gsplit;                                  // query heads per part
+  const int h_first = hk * (H / Hk) + (int)(blockIdx.x % a.gsplit) * hpp, h_end = h_first + hpp;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
@@ -996,6 +1002,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   }
   flush_dq(qt_end - 1, h_end - 1);
 
+  // split groups: this item's part (recomputed here rather than kept live)
+  const int GS = a.gsplit, part = blockIdx.x % GS;
   // ---- item end: the two query-half dV partials of each key block meet in
   // the (now free) bf16 tile buffers, key blocks 0-1 first, then 2-3; then dK
   for (int round = 0; round < 2; ++round) {
@@ -1019,7 +1027,11 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int jk = k0 + 32 * kb + 8 * q4 + 4 * hh + r;
-            if (jk < L) a.dv[doc0k + (size_t)jk * rsk + 32 * db + n] = f32_to_bf16_bits(dv[db][4 * q4 + r] + o[r]);
+            if (jk < L) {
+              const size_t oi = doc0k + (size_t)jk * rsk + 32 * db + n;
+              if (GS == 1) a.dv[oi] = f32_to_bf16_bits(dv[db][4 * q4 + r] + o[r]);
+              else a.dv_f32[(size_t)part * T * rsk + oi] = dv[db][4 * q4 + r] + o[r];
+            }
           }
         }
     }
@@ -1042,21 +1054,27 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   __syncthreads();
   {
     constexpr int E = D / 4;
-    const int row = tid >> 2, part = tid & 3;         // 128 key rows, four lanes each
+    const int row = tid >> 2, q4p = tid & 3;          // 128 key rows, four lanes each
     const int jk = k0 + row;
     if (jk < L) {                                     // whole quads leave together
       const int rb = row >> 5;
       const float* const src = reinterpret_cast<const float*>(rb == 0 ? sK : rb == 1 ? sV : rb == 2 ? sG0 : sG1) +
-                               (row & 31) * D + part * E;
-      float x[E];
+                               (row & 31) * D + q4p * E;
+      if (GS == 1) {
+        float x[E];
 #pragma unroll
-      for (int c = 0; c < E / 4; ++c) {
-        const v4f w = *reinterpret_cast<const v4f*>(src + 4 * c);
+        for (int c = 0; c < E / 4; ++c) {
+          const v4f w = *reinterpret_cast<const v4f*>(src + 4 * c);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
+          for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
+        }
+        if (p.hadamard) fwht_quarter_row<D>(x, q4p);
+        store_bf16<E>(a.dk + doc0k + (size_t)jk * rsk + q4p * E, x);
+      } else {
+        float* dst = a.dk_f32 + (size_t)part * T * rsk + doc0k + (size_t)jk * rsk + q4p * E;
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c) *reinterpret_cast<v4f*>(dst + 4 * c) = *reinterpret_cast<const v4f*>(src + 4 * c);
       }
-      if (p.hadamard) fwht_quarter_row<D>(x, part);
-      store_bf16<E>(a.dk + doc0k + (size_t)jk * rsk + part * E, x);
     }
   }
 }
@@ -1069,10 +1087,10 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
             in.q_codes, in.k_codes, in.v_codes, in.v_key_codes, in.k_exp, in.v_exp, in.v_key_exp,
             in.kofs, in.il8, in.delta, in.dq_sigma, in.qexps, in.do_codes,
             static_cast<const uint16_t*>(in.g), static_cast<uint16_t*>(in.dq_acc), in.dk_f32,
-            static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv),
+            static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv), in.dv_f32, in.gsplit,
             static_cast<uint16_t*>(in.dq_part), in.det_base, in.det_cap, static_cast<const uint16_t*>(in.q_x),
             static_cast<const uint16_t*>(in.k_x), in.qk_scale};
-  dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.Hk);   // the mixed path has Hk = H
+  dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.Hk * (unsigned)in.gsplit);   // the mixed path has Hk = H, gsplit = 1
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };
   if (p.path == 1) {
     if (p.D == 64) go(attn_bwd_kernel<64, 1>); else go(attn_bwd_kernel<128, 1>);

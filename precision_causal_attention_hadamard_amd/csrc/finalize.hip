@@ -89,6 +89,57 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
   }
 }
 
+// Split groups (grouped query attention with the group spread over several
+// backward items): dK and dV of each (token, key/value head) row are the sums
+// of the gsplit fp32 partials, added in part order; dK is rotated back with the
+// Hadamard option; both are rounded to bf16 once.  Four lanes per row.
+template <int D>
+__global__ void __launch_bounds__(FIN_THREADS)
+group_reduce_kernel(Problem p, int gsplit, const float* __restrict__ dk_f32, const float* __restrict__ dv_f32,
+                    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  constexpr int E = D / FIN_PARTS;
+  const size_t rows = (size_t)p.T * p.Hk;
+  const size_t row = ((size_t)blockIdx.x * FIN_THREADS + threadIdx.x) / FIN_PARTS;
+  const int part = threadIdx.x & (FIN_PARTS - 1);
+  if (row >= rows) return;      // whole quads leave together
+  const size_t off = row * D + (size_t)part * E, plane = rows * D;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const float* src = (which == 0 ? dk_f32 : dv_f32) + off;
+    float x[E];
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+      const v4f w = *reinterpret_cast<const v4f*>(src + 4 * c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
+    }
+    for (int s = 1; s < gsplit; ++s) {
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c) {
+        const v4f w = *reinterpret_cast<const v4f*>(src + (size_t)s * plane + 4 * c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[4 * c + k] = x[4 * c + k] + w[k];
+      }
+    }
+    if (which == 0 && p.hadamard) fwht_quarter_row<D>(x, part);
+    store_bf16<E>((which == 0 ? dk : dv) + off, x);
+  }
+}
+
+hipError_t launch_group_reduce(const Problem& p, int gsplit, const float* dk_f32, const float* dv_f32, void* dk,
+                               void* dv, hipStream_t stream) {
+  const size_t rows = (size_t)p.T * p.Hk;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows * FIN_PARTS + FIN_THREADS - 1) / FIN_THREADS));
+  if (p.D == 64)
+    hipLaunchKernelGGL(group_reduce_kernel<64>, grid, dim3(FIN_THREADS), 0, stream, p, gsplit, dk_f32, dv_f32,
+                       (uint16_t*)dk, (uint16_t*)dv);
+  else
+    hipLaunchKernelGGL(group_reduce_kernel<128>, grid, dim3(FIN_THREADS), 0, stream, p, gsplit, dk_f32, dv_f32,
+                       (uint16_t*)dk, (uint16_t*)dv);
+  return hipGetLastError();
+}
+
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
                            const float* dk_f32, void* dq, void* dk, bool with_dk, const void* dq_part,
                            const int* det_base, int det_cap, hipStream_t stream) {

@@ -55,6 +55,23 @@ flamia_status validate(const flamia_attn_desc* d) {
   return FLAMIA_OK;
 }
 
+inline int kv_heads(const flamia_attn_desc* d) { return d->num_kv_heads > 0 ? d->num_kv_heads : d->num_heads; }
+
+// Grouped query attention: the backward item is (document, key tile,
+// key/value head) and runs the group's query heads itself.  When that gives
+// fewer than K_BWD_MIN_ITEMS items (two per CU of an MI355X), each group is
+// split over the smallest divisor s of H/Hk that reaches it, and the s fp32
+// partials of dK and dV are reduced afterwards.
+constexpr int64_t K_BWD_MIN_ITEMS = 512;
+int bwd_group_split(const flamia_attn_desc* d) {
+  const int g = d->num_heads / kv_heads(d);
+  if (g == 1 || d->path == 1) return 1;
+  const int64_t items = (int64_t)(cdiv(d->total_tokens, K_BWD_BK) + d->num_docs) * kv_heads(d);
+  for (int s = 1; s < g; ++s)
+    if (g % s == 0 && items * s >= K_BWD_MIN_ITEMS) return s;
+  return g;
+}
+
 PlanLayout plan_layout(const flamia_attn_desc* d) {
   PlanLayout pl{};
   pl.cap_fwd = cdiv(d->total_tokens, K_FWD_BQ) + d->num_docs;
@@ -70,8 +87,6 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
 struct QLayout {
   size_t codes[4], exps[5], plan, fp4[2], sf[2], qk_scale, fx[2], bytes;
 };
-
-inline int kv_heads(const flamia_attn_desc* d) { return d->num_kv_heads > 0 ? d->num_kv_heads : d->num_heads; }
 
 QLayout q_layout(const flamia_attn_desc* d) {
   QLayout q{};
@@ -109,7 +124,10 @@ BwdLayout bwd_layout(const flamia_attn_desc* d) {
   b.g = off;        off = align_up(off + 2 * E);
   b.dq_sigma = off; off = align_up(off + 4 * M);
   b.dq_acc = off;   off = align_up(off + 2 * E);
-  b.dk_f32 = off;   off = align_up(off + 4 * E);
+  b.dk_f32 = off;   off = align_up(off + 4 * E);     // also holds split-group dK partials (s Hk <= H)
+  b.dv_f32 = off;
+  const int gs = bwd_group_split(d);
+  if (gs > 1) off = align_up(off + 4 * (size_t)gs * d->total_tokens * kv_heads(d) * d->head_dim);
   b.dq_part = off;
   if (d->deterministic)
     off = align_up(off + (size_t)det_step_cap(d) * d->num_heads * K_BWD_BQ * d->head_dim * 2);
@@ -265,6 +283,8 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   in.dk_f32 = reinterpret_cast<float*>(w + b.dk_f32);
   in.dk = dk;
   in.dv = dv;
+  in.dv_f32 = reinterpret_cast<float*>(w + b.dv_f32);
+  in.gsplit = bwd_group_split(desc);
   const PlanLayout pl = plan_layout(desc);
   in.dq_part = w + b.dq_part;
   in.det_base = reinterpret_cast<const int*>(static_cast<const uint8_t*>(qt->plan) + pl.det_offset);
@@ -272,7 +292,9 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   in.q_x = qt->q_fp4_bf16;
   in.k_x = qt->k_fp4_bf16;
   in.qk_scale = qt->qk_tensor_scale;
-  return hip_status(launch_attn_bwd(p, qt->plan, pl, in, stream));
+  const flamia_status st = hip_status(launch_attn_bwd(p, qt->plan, pl, in, stream));
+  if (st != FLAMIA_OK || in.gsplit == 1) return st;
+  return hip_status(launch_group_reduce(p, in.gsplit, in.dk_f32, in.dv_f32, dk, dv, stream));
 }
 
 flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dq,

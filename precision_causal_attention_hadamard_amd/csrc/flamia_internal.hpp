@@ -25,7 +25,7 @@ struct PlanLayout {
 
 // Byte offsets of the backward workspace.
 struct BwdLayout {
-  size_t do_codes, do_exp, kofs, delta, il8, qexps, g, dq_sigma, dq_acc, dk_f32, dq_part, bytes;
+  size_t do_codes, do_exp, kofs, delta, il8, qexps, g, dq_sigma, dq_acc, dk_f32, dv_f32, dq_part, bytes;
 };
 
 struct Problem {
@@ -86,7 +86,10 @@ struct BwdInputs {
   const uint8_t* do_codes;
   const void* g;
   void* dq_acc;
-  float* dk_f32;           // mixed path: fp32 dK staging (the finaliser rotates and rounds it)
+  float* dk_f32;           // mixed path: fp32 dK staging (the finaliser rotates and rounds it);
+                           // split groups: fp32 dK partials [gsplit, T, Hk, d]
+  float* dv_f32;           // split groups: fp32 dV partials [gsplit, T, Hk, d]
+  int gsplit;              // items per key/value head group (1: one item runs the whole group)
   void* dk;                // MXFP8 path: bf16 dK, written by the backward kernel
   void* dv;
   void* dq_part;           // deterministic mode: fp16 dQ partial slots
@@ -98,6 +101,11 @@ struct BwdInputs {
 
 hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl, const BwdInputs& in,
                            hipStream_t stream);
+
+// Split groups: dK, dV of each key/value head = the sum of the gsplit fp32
+// partials in order, dK rotated back (Hadamard option), both rounded to bf16.
+hipError_t launch_group_reduce(const Problem& p, int gsplit, const float* dk_f32, const float* dv_f32, void* dk,
+                               void* dv, hipStream_t stream);
 
 hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_sigma,
                            const float* dk_f32, void* dq, void* dk, bool with_dk, const void* dq_part,

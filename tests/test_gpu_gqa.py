@@ -112,11 +112,14 @@ def test_gqa_deterministic_repeatable(gpu_lib):
         assert torch.equal(getattr(call, n), t), n
 
 
-def test_gqa_fullsize_sampled(gpu_lib):
-    """The grouped variant of the 2 x 4096-token, 16-head, d = 128 outlier
-    workload with 4 key/value heads, whole call on the GPU; the oracle
-    recomputes document 1 for key/value head 3 and its four query heads."""
-    wl = W.config(2, kv_heads=4)
+@pytest.mark.parametrize("kv_heads", [4, 8])
+def test_gqa_fullsize_sampled(gpu_lib, kv_heads):
+    """The grouped variants of the 2 x 4096-token, 16-head, d = 128 outlier
+    workload, whole call on the GPU; the oracle recomputes document 1 for
+    key/value head 3 and its query heads.  With 8 key/value heads one
+    backward item runs a whole group (528 items); with 4 the groups are split
+    over two items each and their fp32 partials reduced."""
+    wl = W.config(2, kv_heads=kv_heads)
     print(f"[gqa] fullsize {wl.name}: GPU call", flush=True)
     call = run_gpu(gpu_lib, wl)
     doc, hk, g = 1, 3, wl.heads // wl.kv_heads
