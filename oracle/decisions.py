@@ -11,17 +11,17 @@ Algorithms", ch. 3 and 4).  The attention oracle evaluates every such sum
 exactly and rounds once, which is one admissible result.
 
 Where the interval of values that bound admits straddles a rounding boundary
-of a quantized decision -- the E4M3 code of P 2^8 (with the diagonal fold) or
-the bf16 rounding of O -- more than one result is correct.  Such a decision
-moves a row of O, and through D_i = sum_d dO~_id O_id it shifts every dS_ij of
-the row in the same direction, so dQ_i and the dK_j of the row's keys move
-coherently; the P^ decision also enters dV directly.  ``allowances`` returns,
-per output element, the width those alternative decisions can produce, so a
-comparison can hold every element to its tolerance plus that width.  The dS^
-codes themselves are re-rounded around the shifted values; that part, and the
-continuous fp32 differences, scatter in sign and stay with the tolerance.
-Elements no decision reaches get nothing beyond the span of their own final
-bf16 rounding.
+of a quantized decision -- the E4M3 code of P 2^8 (with the diagonal fold),
+the bf16 rounding of O, the E4M3 code of dS -- more than one result is
+correct.  A P^ or O decision moves a row of O, and through
+D_i = sum_d dO~_id O_id it shifts every dS_ij of the row in the same
+direction, so dQ_i moves along a known direction; the P^ decision also
+enters dV directly.  A dS^ decision moves dQ_i along K~_j and dK_j along
+Q~_i by at most the code range it admits.  ``allowances`` returns these, so
+a comparison can hold every element to its tolerance plus what the
+alternative decisions explain (tests/decision_compare.py fits them, each
+coefficient bounded).  The continuous fp32 differences are left to the
+tolerance.
 
 Bounds used (per (document, head), vectorised; e = error, rel = relative):
 * S: e <= gamma_d sum_k |q~_ik k~_jk| + u |S| (the oracle rounds once);
@@ -51,7 +51,7 @@ import numpy as np
 
 from . import formats
 from .attention import Numerics, forward_doc, scale_constants
-from .quant import doc_bounds, fold_reference, quantize_qkv, quantize_token_blocks
+from .quant import BLOCK, doc_bounds, fold_reference, quantize_qkv, quantize_token_blocks
 
 U = 2.0 ** -24
 
@@ -113,14 +113,71 @@ def doc_head_allowances(fw, qs, ks, qd, kd, vblk, vkey, dod, s32, c32, num: Nume
     e_D = np.sum(np.abs(dod) * o_span, axis=1)
     g = -float(s32) * (np.where(valid, p / l[:, None], 0.0) @ kd)
     dv = ((span_pe * (1 + rel_l[:, None])) / l[:, None]).T @ np.abs(dod)
-    return dict(o=o_span, e_D=e_D, dq_dir=g, dv=dv, p_span=span_pe, rel_p=rel_p, rel_l=rel_l)
+    res = dict(o=o_span, e_D=e_D, dq_dir=g, dv=dv, p_span=span_pe, rel_p=rel_p, rel_l=rel_l)
+    if num.quantize_ds:
+        res.update(_ds_decisions(fw, dod, vblk, vkey, rel_p, rel_l, num))
+    return res
+
+
+def _ds_decisions(fw, dod, vblk, vkey, rel_p, rel_l, num: Numerics):
+    """dS^ codes that admissible evaluations may round either way.
+
+    dS = fp32(fp32(P 2^8 2^-8/l) (dP - D)) with dP - D accumulated in fp32 from
+    -D: e(dP - D) <= gamma_(d+1) (|D| + sum |dO~ V|) + gamma_d sum |dO~ O|
+    (the D shift the O decisions allow is fitted as one coherent direction
+    and not spread over every code of the row again); with
+    g = (1 + rel(P))(1 + rel(l)), e(dS) <= |dS| (g (1 + 3u) - 1) + g P/l
+    e(dP - D).  An element whose interval [dS - e, dS + e], scaled by its
+    block's exponent, holds an E4M3 rounding boundary is returned with the
+    range of dS^ values the interval maps to (relative to the oracle's
+    dS^).  The block exponent itself is counted as ambiguous when the block
+    max-abs interval straddles a power of two (reported, not spanned)."""
+    L, d = dod.shape
+    p, l, valid, diag = fw["p"], fw["l"], fw["valid"], fw["diag"]
+    o_out = formats.bf16_round(fw["o"]) if num.round_outputs else fw["o"]
+    D = np.sum(dod * o_out, axis=1)
+    dp = np.where(diag, dod @ vkey.T, dod @ vblk.T)
+    dp_abs = np.where(diag, np.abs(dod) @ np.abs(vkey).T, np.abs(dod) @ np.abs(vblk).T)
+    ds = np.where(valid, (p / l[:, None]) * (dp - D[:, None]), 0.0)
+    e_dpd = (gamma(d + 1) * (np.abs(D)[:, None] + dp_abs)
+             + gamma(d) * np.sum(np.abs(dod * o_out), axis=1)[:, None])
+    grow = (1 + rel_p) * (1 + rel_l[:, None])
+    e_ds = np.where(valid, np.abs(ds) * (grow * (1 + 3 * U) - 1) + (p / l[:, None]) * grow * e_dpd, 0.0)
+    rows, cols, lo, hi = [], [], [], []
+    blocks_ambiguous = 0
+    for i0 in range(0, L, BLOCK):
+        for j0 in range(0, L, BLOCK):
+            v = valid[i0:i0 + BLOCK, j0:j0 + BLOCK]
+            if not v.any():
+                continue
+            x = np.where(v, ds[i0:i0 + BLOCK, j0:j0 + BLOCK], 0.0)
+            ex = np.where(v, e_ds[i0:i0 + BLOCK, j0:j0 + BLOCK], 0.0)
+            amax, emax = np.abs(x).max(), ex.max()
+            eb = formats.roundup_exponent(amax)
+            if formats.roundup_exponent(max(amax - emax, 0.0)) != formats.roundup_exponent(amax + emax):
+                blocks_ambiguous += 1
+            q0 = np.ldexp(formats.e4m3_round(np.ldexp(x, -eb)), eb)
+            ql = np.ldexp(formats.e4m3_round(np.ldexp(x - ex, -eb), saturate=True), eb)
+            qh = np.ldexp(formats.e4m3_round(np.ldexp(x + ex, -eb), saturate=True), eb)
+            ii, jj = np.nonzero(v & (ql != qh))
+            rows.append(ii + i0)
+            cols.append(jj + j0)
+            lo.append((ql - q0)[ii, jj])
+            hi.append((qh - q0)[ii, jj])
+    cat = (lambda a, t: np.concatenate(a).astype(t) if a else np.zeros(0, t))
+    return dict(ds_rows=cat(rows, np.int64), ds_cols=cat(cols, np.int64), ds_lo=cat(lo, np.float64),
+                ds_hi=cat(hi, np.float64), ds_blocks_ambiguous=blocks_ambiguous)
 
 
 def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
     """Decision bounds of the whole call (see the module docstring): ``o``
     ``[T, H, d]`` and ``dv`` ``[T, Hk, d]`` per-element allowances; ``e_D``
-    ``[T, H]``, the bound of the admissible shift of D per query row; and
-    ``dq_dir`` ``[T, H, d]``, the change of dQ per unit shift of D."""
+    ``[T, H]``, the bound of the admissible shift of D per query row;
+    ``dq_dir`` ``[T, H, d]``, the change of dQ per unit shift of D; and ``ds``,
+    the dS^ codes admissible evaluations may round either way: query token
+    ``tq`` and head ``h``, key token ``tk`` and key/value head ``hk``, the
+    range [lo, hi] of the change of the dS^ value, and the changes of the dQ
+    row (``dq_vec``) and of the dK row (``dk_vec``) per unit change of it."""
     num = num or Numerics()
     q = np.asarray(q, dtype=np.float64)
     T, H, d = q.shape
@@ -137,6 +194,8 @@ def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
         *_, ks_all = quantize_nvfp4(qt["k_rot"], ka)
     from .hadamard import rotate_back_fp64
     out = dict(o=np.zeros((T, H, d)), dq_dir=np.zeros((T, H, d)), e_D=np.zeros((T, H)))
+    amb = {k_: [] for k_ in ("tq", "h", "tk", "hk", "lo", "hi", "dq_vec", "dk_vec")}
+    blocks_ambiguous = 0
     dv_w = np.zeros((T, Hk, d))
     dv_raw = np.zeros((T, Hk, d))
     for s, e in doc_bounds(cu_seqlens):
@@ -155,5 +214,23 @@ def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
             out["dq_dir"][sl, h] = rotate_back_fp64(a["dq_dir"]) if num.hadamard else a["dq_dir"]
             dv_w[sl, hk] += a["dv"]
             dv_raw[sl, hk] += (fw["peff"] / fw["l"][:, None]).T @ do_deq[sl, h]
+            if "ds_rows" in a:
+                r, cidx = a["ds_rows"], a["ds_cols"]
+                kd_o = qt["k"][sl, hk][cidx]
+                qd_o = qt["q"][sl, h][r]
+                if num.hadamard:
+                    kd_o, qd_o = rotate_back_fp64(kd_o), rotate_back_fp64(qd_o)
+                amb["tq"].append(r + s)
+                amb["h"].append(np.full(len(r), h))
+                amb["tk"].append(cidx + s)
+                amb["hk"].append(np.full(len(r), hk))
+                amb["lo"].append(a["ds_lo"])
+                amb["hi"].append(a["ds_hi"])
+                amb["dq_vec"].append(float(s32) * kd_o)
+                amb["dk_vec"].append(float(s32) * qd_o)
+                blocks_ambiguous += a["ds_blocks_ambiguous"]
     out["dv"] = _bf16_span(dv_raw, dv_w) if num.round_outputs else dv_w
+    out["ds"] = {k_: (np.concatenate(v_) if v_ else np.zeros((0, d) if k_.endswith("vec") else 0))
+                 for k_, v_ in amb.items()}
+    out["ds_blocks_ambiguous"] = blocks_ambiguous
     return out

@@ -8,10 +8,13 @@ is unique:
 * O, dV: |got - want| <= 2e-2 max|want| + allowance (the width the admissible
   decisions span; zero for almost every element);
 * dQ: a decision that moves O shifts D_i, which moves dQ_i along a known
-  direction g_i; one coefficient a_i with |a_i| <= e(D_i) is fitted per row
-  (least squares, then clipped to the bound) and the remainder
-  dQ_i - want_i - a_i g_i is held to 2e-2 max|want| on every element;
-* dK: plain.
+  direction g_i (|coefficient| <= e(D_i)), and each ambiguous dS^ code of the
+  row moves it along s32 K~_j (coefficient within the code range the fp32
+  bound admits); the coefficients are fitted per row (the D shift in closed
+  form, and for rows still above the bar jointly with the row's dS^
+  decisions by bounded least squares) and the remainder is held to 2e-2
+  max|want| on every element;
+* dK: likewise with the ambiguous dS^ codes of the key row (along s32 Q~_i).
 On workloads with outlier channels (a few channels x20), a dS^ code decision
 in a short row moves dQ_i by a sizable part of the tensor's maximum (the keys'
 outlier channels multiply it), and the matrix cores' FP8 products are not
@@ -35,31 +38,84 @@ def cosine(got, want):
     return float(g @ w / np.sqrt((g @ g) * (w @ w)))
 
 
-def compare(name, got, want, allow=None, tol=TOL_REL):
-    """Returns (rel_plain, rel_applied, cosine, extra) for one output tensor.
-    ``allow``: for "o"/"dv" the per-element allowance; for "dq" a pair
-    (direction [.., d], e_D [..]); None for a plain comparison."""
+def _row_fit(diff, groups, fixed, bar):
+    """Remainder of ``diff`` ([R, d]) after fitting each row's admissible
+    directions.  fixed: optional (directions [R, d], bound [R]) present in
+    every row, fitted in closed form and clipped; rows still above ``bar``
+    are refitted jointly with their listed decisions (groups: row ->
+    (vectors [k, d], lo [k], hi [k])) by bounded least squares.  Rows within
+    the bar need no further explanation, so only those are refitted."""
+    from scipy.optimize import lsq_linear
+    resid = diff.copy()
+    if fixed is not None:
+        g, b = fixed
+        gg = np.sum(g * g, axis=-1)
+        a = np.where(gg > 0, np.sum(diff * g, axis=-1) / np.where(gg > 0, gg, 1.0), 0.0)
+        resid = diff - np.clip(a, -b, b)[:, None] * g
+    for r in np.flatnonzero(np.max(np.abs(resid), axis=-1) > bar):
+        if int(r) not in groups:
+            continue
+        vec, lo, hi = groups[int(r)]
+        cols, lb, ub = [vec], [lo], [hi]
+        if fixed is not None and np.any(fixed[0][r]):
+            cols.insert(0, fixed[0][r][None])
+            lb.insert(0, [-fixed[1][r]])
+            ub.insert(0, [fixed[1][r]])
+        A = np.concatenate(cols).T
+        lb, ub = np.concatenate(lb), np.concatenate(ub)
+        ub = np.where(ub > lb, ub, lb + 1e-300)      # lsq_linear needs lb < ub
+        x = lsq_linear(A, diff[r], bounds=(lb, ub)).x
+        resid[r] = diff[r] - A @ x
+    return resid
+
+
+def _groups(rows_flat, vec, lo, hi):
+    order = np.argsort(rows_flat, kind="stable")
+    rows_s = rows_flat[order]
+    out = {}
+    if len(rows_s) == 0:
+        return out
+    starts = np.flatnonzero(np.r_[True, rows_s[1:] != rows_s[:-1]])
+    ends = np.r_[starts[1:], len(rows_s)]
+    for a_, b_ in zip(starts, ends):
+        idx = order[a_:b_]
+        out[int(rows_s[a_])] = (vec[idx], lo[idx], hi[idx])
+    return out
+
+
+def compare(name, got, want, al=None, tol=TOL_REL):
+    """Returns (rel_plain, rel_applied, cosine, extra) for one output tensor
+    ([T, heads, d]); ``al`` is oracle/decisions.allowances of the same inputs
+    (None: plain comparison)."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     M = max(np.max(np.abs(want)), 1e-30)
     diff = got - want
     rel_plain = float(np.max(np.abs(diff)) / M)
     extra = {}
-    if allow is None:
+    if al is None:
         rel = rel_plain
-    elif name == "dq":
-        g, e_D = allow
-        gg = np.sum(g * g, axis=-1)
-        a = np.where(gg > 0, np.sum(diff * g, axis=-1) / np.where(gg > 0, gg, 1.0), 0.0)
-        a = np.clip(a, -e_D, e_D)
-        resid = diff - a[..., None] * g
+    elif name in ("dq", "dk"):
+        T, Hx, d = diff.shape
+        ds = al["ds"]
+        if name == "dq":
+            rows = ds["tq"] * Hx + ds["h"]
+            fixed = (al["dq_dir"].reshape(-1, d), al["e_D"].reshape(-1))
+            vec = ds["dq_vec"]
+        else:
+            rows = ds["tk"] * Hx + ds["hk"]
+            fixed, vec = None, ds["dk_vec"]
+        # rows above half the bar are refitted, so the reported remainder shows
+        # what the decisions explain near the bar, not only the pass/fail
+        resid = _row_fit(diff.reshape(-1, d), _groups(rows, vec, ds["lo"], ds["hi"]), fixed,
+                         0.5 * tol * M).reshape(diff.shape)
         rel = float(np.max(np.abs(resid)) / M)
-        extra["rows_shifted"] = float(np.mean(np.abs(a) * np.sqrt(gg) > 1e-3 * M))
         extra["rows_beyond"] = float(np.mean(np.max(np.abs(resid), axis=-1) / M > tol))
+        extra["ds_decisions"] = int(len(rows))
     else:
-        excess = np.abs(diff) - allow
+        excess = np.abs(diff) - al[name]
         rel = float(max(np.max(excess), 0.0) / M)
-        extra["allowed_elems"] = float(np.mean(allow > 0))
+        extra["allowed_elems"] = float(np.mean(al[name] > 1e-3 * M))
     return rel_plain, rel, cosine(got, want), extra
 
 
@@ -71,8 +127,7 @@ def check_outputs(outs, ref, al, tag, names=("o", "dq", "dk", "dv"), outliers=Fa
     for n in names:
         got = outs[n]
         assert np.all(np.isfinite(got)), n
-        allow = {"o": al["o"], "dv": al["dv"], "dq": (al["dq_dir"], al["e_D"])}.get(n)
-        res[n] = compare(n, got, ref[n], allow)
+        res[n] = compare(n, got, ref[n], al)
     print(f"[{tag}] " + ", ".join(
         f"{n} rel={r[0]:.2e}" + (f"->{r[1]:.2e}" if r[1] != r[0] else "") + f" cos={r[2]:.6f}"
         for n, r in res.items()), flush=True)

@@ -58,7 +58,9 @@ def oracle_slice(wl, doc, heads):
         assert not wl.hadamard      # the tensor max-abs below is that of the unrotated inputs
         amax = (float(wl.q.float().abs().max()), float(wl.k.float().abs().max()))
     num = A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8", nvfp4_amax=amax)
+    print(f"[fullsize]   oracle slice doc {doc} heads {heads}", flush=True)
     ref = A.training_call(*arrs, [0, e - s], num)
+    print("[fullsize]   decision bounds", flush=True)
     ref["_allow"] = DC.allowances(*arrs, [0, e - s], num)
     return ref
 

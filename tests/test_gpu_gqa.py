@@ -130,7 +130,9 @@ def test_gqa_fullsize_sampled(gpu_lib, kv_heads):
     print("[gqa] fullsize: oracle slice", flush=True)
     num = A.Numerics(hadamard=wl.hadamard)
     ref = A.training_call(*arrs, [0, e - s], num)
+    print("[gqa] fullsize: decision bounds", flush=True)
     al = DC.allowances(*arrs, [0, e - s], num)
+    print("[gqa] fullsize: compare", flush=True)
     hq, hkv = torch.tensor(qh), torch.tensor([hk])
     np.testing.assert_array_equal(call.codes("k_codes")[s:e].cpu()[:, hkv].numpy(), ref["k_codes"])
     np.testing.assert_array_equal(call.codes("q_codes")[s:e].cpu()[:, hq].numpy(), ref["q_codes"])

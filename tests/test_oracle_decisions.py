@@ -7,6 +7,9 @@ emulation of admissible evaluations, on the CPU.
   O stays inside the O allowance, and D moves by at most e(D).
 * A shift of the stored O moves the oracle's own (unquantized-dS) dQ exactly
   along the stated direction, by the shift of D.
+* dS evaluated from admissible P, l, dP and D: every dS^ code that changes is
+  a listed decision and moves inside its listed range (blocks whose exponent
+  the bound leaves open are excluded and counted).
 * The near-tie behind one GPU-observed difference is flagged.
 """
 
@@ -124,13 +127,66 @@ def test_dq_moves_along_the_stated_direction_under_a_shift_of_o():
     assert np.count_nonzero(np.abs(b1["dq"] - b0["dq"]).max(axis=1) > 0) == len(rows)
 
 
-def test_the_observed_near_tie_is_flagged():
-    """One query row of a grouped-head workload holds a probability whose
-    P 2^8 = 136.0002 lies 1.7e-6 above the E4M3 rounding boundary 136 between
-    the codes 128 and 144; the fp32 bound admits both codes."""
+@pytest.mark.parametrize("case", list(CASES))
+def test_admissible_ds_codes_are_listed_decisions(case):
+    wl = CASES[case]()
+    doc, h = (1, 3) if case.startswith("outliers") else (0, 1)
+    ops, fw, al, num, s32, c32 = doc_head(wl, doc, h)
+    rng = np.random.default_rng(11)
+    L, d = ops["q"].shape
+    valid, diag, p, l = fw["valid"], fw["diag"], fw["p"], fw["l"]
+    o_out = formats.bf16_round(fw["o"])
+    ref = A.backward_doc(fw, ops["q"], ops["k"], ops["v"], ops["vk"], ops["do"], o_out, s32, num)
+    D = np.sum(ops["do"] * o_out, axis=1)
+    dp = np.where(diag, ops["do"] @ ops["vk"].T, ops["do"] @ ops["v"].T)
+    dp_abs = np.where(diag, np.abs(ops["do"]) @ np.abs(ops["vk"]).T, np.abs(ops["do"]) @ np.abs(ops["v"]).T)
+    listed = {}
+    for r, c_, lo, hi in zip(al["ds_rows"], al["ds_cols"], al["ds_lo"], al["ds_hi"]):
+        listed[(int(r), int(c_))] = (lo, hi)
+    changed = 0
+    for trial in range(6):
+        sgn = (lambda shape: np.sign(rng.uniform(-1, 1, shape))) if trial % 2 else \
+              (lambda shape: rng.uniform(-1, 1, shape))
+        p_a = p * (1 + sgn(p.shape) * al["rel_p"])
+        l_a = l * (1 + sgn(l.shape) * al["rel_l"])
+        e_dpd = DC.gamma(d + 1) * (np.abs(D)[:, None] + dp_abs) + \
+            DC.gamma(d) * np.sum(np.abs(ops["do"] * o_out), axis=1)[:, None]
+        dpd = dp - D[:, None] + sgn(dp.shape) * e_dpd
+        ds = np.where(valid, (p_a / l_a[:, None]) * dpd * (1 + sgn(dp.shape) * 3 * DC.U), 0.0)
+        dsq = A._ds_quantize(ds, valid, "roundup")
+        # blocks whose exponent moved are outside what the list covers
+        same_exp = np.ones_like(valid)
+        for i0 in range(0, L, 32):
+            for j0 in range(0, L, 32):
+                v = valid[i0:i0 + 32, j0:j0 + 32]
+                if v.any():
+                    e0 = formats.roundup_exponent(np.abs(np.where(v, ref["ds"][i0:i0 + 32, j0:j0 + 32], 0)).max())
+                    e1 = formats.roundup_exponent(np.abs(np.where(v, ds[i0:i0 + 32, j0:j0 + 32], 0)).max())
+                    same_exp[i0:i0 + 32, j0:j0 + 32] = e0 == e1
+        delta = dsq - ref["dsq"]
+        ii, jj = np.nonzero((delta != 0) & same_exp)
+        for i, j in zip(ii, jj):
+            assert (i, j) in listed, (trial, i, j, ds[i, j], ref["ds"][i, j])
+            lo, hi = listed[(i, j)]
+            assert lo - 1e-300 <= delta[i, j] <= hi + 1e-300
+        changed += len(ii)
+    assert changed > 0
+
+
+def test_the_observed_near_ties_are_flagged():
+    """Two decisions behind GPU differences of grouped-head workloads: a
+    probability with P 2^8 = 136.0002, 1.7e-6 above the E4M3 rounding
+    boundary 136 between the codes 128 and 144, and a dS scaled by its block
+    exponent to 84.00003, 3.4e-7 above the boundary 84 between 80 and 88; the
+    fp32 bound admits both codes of each."""
     wl = W.small_packed(43, [129, 64, 31, 250], heads=4, head_dim=128, kv_heads=1)
     ops, fw, al, *_ = doc_head(wl, 0, 1)
     x = fw["p"][73, 35] * 256
     assert 136.0 < x < 136.001
     assert al["p_span"][73, 35] == pytest.approx(16 / 256)
     assert al["o"][73].max() > 0
+    wl2 = W.small_packed(41, [1, 17, 45, 100, 33, 64, 130, 2], heads=4, head_dim=64, kv_heads=2)
+    ops2, fw2, al2, *_ = doc_head(wl2, 6, 1)
+    k_ = [n for n, (r, c_) in enumerate(zip(al2["ds_rows"], al2["ds_cols"])) if (r, c_) == (30, 20)]
+    assert len(k_) == 1
+    assert (al2["ds_lo"][k_[0]], al2["ds_hi"][k_[0]]) == (-8 * 2.0 ** -6, 0.0)
