@@ -583,8 +583,9 @@ __device__ __forceinline__ int dsk_off(int r, int chunk) {
 // dK and dV sum them in fp32 registers.  With one part per group (the usual
 // case) they are rounded once here; when the grid would be too small the
 // group is split over gsplit items, which store fp32 partials that a reduce
-// kernel adds in order and rounds once.
-template <int D, bool DET>
+// kernel adds in order and rounds once.  GRP = false is the one-head-per-item
+// instantiation (H = Hk): the loop runs the query tiles of one head only.
+template <int D, bool DET, bool GRP>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
@@ -615,15 +616,16 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 
   const Problem& p = a.p;
   const int H = p.H, T = p.T, Hk = p.Hk;
-  const int tile_idx = blockIdx.x / (Hk * a.gsplit), hk = (blockIdx.x / a.gsplit) % Hk;
+  const int tile_idx = GRP ? (int)(blockIdx.x / (Hk * a.gsplit)) : (int)(blockIdx.x / H);
+  const int hk = GRP ? (int)((blockIdx.x / a.gsplit) % Hk) : (int)(blockIdx.x % H);
   if (tile_idx >= a.counts[1]) return;
   const int2 it = a.items[tile_idx];
   const int doc = it.x, u = it.y;
   const int s_d = p.cu[doc];
   const int L = p.cu[doc + 1] - s_d;
   const int k0 = u * BWD_BK;
-  const int hpp = H / Hk / a.gsplit;                                  // query heads per part
-  const int h_first = hk * (H / Hk) + (int)(blockIdx.x % a.gsplit) * hpp, h_end = h_first + hpp;
+  const int hpp = GRP ? H / Hk / a.gsplit : 1;                        // query heads per part
+  const int h_first = GRP ? hk * (H / Hk) + (int)(blockIdx.x % a.gsplit) * hpp : hk, h_end = h_first + hpp;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
@@ -847,13 +849,16 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     }
     // the next tile streams in while this one is computed; last step's dQ
     // goes out (steps run over the query tiles of one head, then the next head)
-    {
+    if constexpr (GRP) {
       const bool wrap = qt + 1 >= qt_end;
       const int nh = wrap ? h + 1 : h;
       if (nh < h_end) issue_tile(std::integral_constant<int, 1 - B>{}, wrap ? qt_first : qt + 1, nh);
       const bool first = qt == qt_first;
       const int ph = first ? h - 1 : h;
       if (ph >= h_first) flush_dq(first ? qt_end - 1 : qt - 1, ph);
+    } else {
+      if (qt + 1 < qt_end) issue_tile(std::integral_constant<int, 1 - B>{}, qt + 1, h);
+      if (qt > qt_first) flush_dq(qt - 1, h);
     }
     if (act) {
       float dsv[16];
@@ -994,16 +999,25 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     full_barrier();
   };
 
-  for (int qt = qt_first, h = h_first;;) {
-    step(std::integral_constant<int, 0>{}, qt, h);
-    if (++qt >= qt_end) { qt = qt_first; if (++h >= h_end) break; }
-    step(std::integral_constant<int, 1>{}, qt, h);
-    if (++qt >= qt_end) { qt = qt_first; if (++h >= h_end) break; }
+  if constexpr (GRP) {
+    for (int qt = qt_first, h = h_first;;) {
+      step(std::integral_constant<int, 0>{}, qt, h);
+      if (++qt >= qt_end) { qt = qt_first; if (++h >= h_end) break; }
+      step(std::integral_constant<int, 1>{}, qt, h);
+      if (++qt >= qt_end) { qt = qt_first; if (++h >= h_end) break; }
+    }
+  } else {
+    for (int qt = qt_first;;) {
+      step(std::integral_constant<int, 0>{}, qt, h_first);
+      if (++qt >= qt_end) break;
+      step(std::integral_constant<int, 1>{}, qt, h_first);
+      if (++qt >= qt_end) break;
+    }
   }
   flush_dq(qt_end - 1, h_end - 1);
 
   // split groups: this item's part (recomputed here rather than kept live)
-  const int GS = a.gsplit, part = blockIdx.x % GS;
+  const int GS = GRP ? a.gsplit : 1, part = GRP ? (int)(blockIdx.x % GS) : 0;
   // ---- item end: the two query-half dV partials of each key block meet in
   // the (now free) bf16 tile buffers, key blocks 0-1 first, then 2-3; then dK
   for (int round = 0; round < 2; ++round) {
@@ -1097,9 +1111,17 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
     if (p.deterministic) {
-      if (p.D == 64) go8(attn_bwd8_kernel<64, true>); else go8(attn_bwd8_kernel<128, true>);
+      if (p.Hk != p.H) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, true, true>); else go8(attn_bwd8_kernel<128, true, true>);
+      } else {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, true, false>); else go8(attn_bwd8_kernel<128, true, false>);
+      }
     } else {
-      if (p.D == 64) go8(attn_bwd8_kernel<64, false>); else go8(attn_bwd8_kernel<128, false>);
+      if (p.Hk != p.H) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, false, true>); else go8(attn_bwd8_kernel<128, false, true>);
+      } else {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, false, false>); else go8(attn_bwd8_kernel<128, false, false>);
+      }
     }
   }
   return hipGetLastError();
