@@ -274,6 +274,9 @@ def main():
                    "causal_pairs": pairs, "flops_per_step": flops},
         "pct_fp8_peak": 100.0 * value / FP8_PEAK_TFLOPS,
         "stage_ms": stage_ms, "event_ms_per_step": event_ms,
+        # the attention kernels alone: forward, and backward without the dO
+        # quantization / D preparation (quantization excluded on both sides)
+        "kernel_only_ms": {"fwd": stage_ms["attn_fwd"], "bwd": stage_ms["attn_bwd"] + stage_ms["bwd_finish"]},
         "quantizer": quant,
         "roofline": roofline,
     }
