@@ -78,6 +78,7 @@ class Numerics:
     fold: str = "causal"             # diagonal V: causal | block | none (block codes)
     softmax_scale: float | None = None
     nvfp4_amax: tuple | None = None  # (Q, K) tensor max-abs when the inputs are a slice
+    exact: bool = False              # the exact option (see exact_fold_reference, _ds_exact)
 
 
 def scale_constants(d: int, softmax_scale: float | None):
@@ -111,6 +112,55 @@ def _ds_quantize(ds: np.ndarray, valid: np.ndarray, rule: str):
     return out
 
 
+def exact_fold_reference(v_exp_key, L: int):
+    """Exact option: fold reference of every (query i, key j) pair, the
+    largest per-key V exponent among the keys of j's 32-token block that i
+    may see: ``max{e_key(j') : blk(j') = blk(j), j' <= i}`` ([Summary] opening
+    paragraphs and [Reading, 4.2]: per-key V scales folded into P; the exact
+    option applies the fold to every tile).  Entries with j > i are unused."""
+    e = np.asarray(v_exp_key, dtype=np.int64)
+    ref = np.zeros((L, L), dtype=np.int64)
+    for j0 in range(0, L, BLOCK):
+        cm = np.maximum.accumulate(e[j0:j0 + BLOCK])          # prefix max inside block J
+        n = len(cm)
+        i = np.arange(L)
+        idx = np.clip(i - j0, 0, n - 1)                         # last key of J that query i sees
+        ref[:, j0:j0 + n] = cm[idx][:, None]
+    return ref
+
+
+def _ds_exact(ds, valid, e_fold, rows: bool, rule: str):
+    """Exact option: a dS payload for one product.  ``e_fold`` ([L] per-token
+    exponent) is folded into dS along the product's contraction axis -- the
+    key's K exponent for dQ (``rows``: groups are one query row x 32 keys),
+    the query's Q exponent for dK (groups are one key x 32 queries) -- and the
+    folded values are quantized with one round-up exponent per group (the
+    per-query-row dS exponent of [Reading, 4.2]/[Summary]; a group of 32 along
+    the contraction axis is the microscaling block of the product).  Returns
+    the effective dS value each product uses (fold removed)."""
+    L = ds.shape[0]
+    ex_rule = formats.EXPONENT_RULES[rule]
+    scale = np.ldexp(1.0, np.asarray(e_fold, dtype=np.int64))
+    x = ds * (scale[None, :] if rows else scale[:, None])
+    out = np.zeros_like(ds)
+    if not rows:
+        x, valid_t = x.T, valid.T
+    else:
+        valid_t = valid
+    for r in range(L):
+        for c0 in range(0, L, BLOCK):
+            v = valid_t[r, c0:c0 + BLOCK]
+            if not v.any():
+                continue
+            seg = np.where(v, x[r, c0:c0 + BLOCK], 0.0)
+            e = ex_rule(np.max(np.abs(seg)))
+            q = formats.e4m3_decode(formats.e4m3_encode(np.ldexp(seg, -e), saturate=(rule == "floor")))
+            out[r, c0:c0 + BLOCK] = np.where(v, np.ldexp(q, e), 0.0)
+    if not rows:
+        out = out.T
+    return out / (scale[None, :] if rows else scale[:, None])
+
+
 def forward_doc(qd, kd, vblk, vkey, v_exp_blk, v_exp_key, c32, num: Numerics):
     """Forward of one (document, head).
 
@@ -135,8 +185,15 @@ def forward_doc(qd, kd, vblk, vkey, v_exp_blk, v_exp_key, c32, num: Numerics):
     e_ref = fold_reference(v_exp_key, num.causal)
     if num.fold == "block":
         e_ref = v_exp_blk
+    if num.exact:
+        # every visible pair uses the per-key (per-token) V codes, folded into
+        # P against the reference of its (query, key block)
+        diag = valid.copy()
+        e_ref2 = exact_fold_reference(v_exp_key, L)
+    else:
+        e_ref2 = np.broadcast_to(e_ref[:, None], (L, L))
     if num.quantize_p:
-        f = np.where(diag, np.ldexp(1.0, np.minimum(v_exp_key[None, :] - e_ref[:, None], 0)), 1.0)
+        f = np.where(diag, np.ldexp(1.0, np.minimum(v_exp_key[None, :] - e_ref2, 0)), 1.0)
         p_off = np.ldexp(formats.e4m3_round(np.ldexp(p, -P_EXP)), P_EXP)
         p_dia = np.ldexp(formats.e4m3_round(np.ldexp(p * f, -P_EXP)), P_EXP) / f
         peff = np.where(diag, p_dia, p_off)
@@ -144,7 +201,7 @@ def forward_doc(qd, kd, vblk, vkey, v_exp_blk, v_exp_key, c32, num: Numerics):
         peff = p
     o = (np.where(diag, 0.0, peff) @ vblk + np.where(diag, peff, 0.0) @ vkey) / l[:, None]
     return dict(sp=sp, m=m.astype(np.int64), p=p, l=l, peff=peff, diag=diag,
-                valid=valid, o=o)
+                valid=valid, o=o, fold=f if num.quantize_p else None)
 
 
 def backward_doc(fw, qd, kd, vblk, vkey, dod, o_out, s32, num: Numerics):
@@ -154,13 +211,21 @@ def backward_doc(fw, qd, kd, vblk, vkey, dod, o_out, s32, num: Numerics):
     D = np.sum(dod * o_out, axis=1)                                   # fp64
     dp = np.where(diag, dod @ vkey.T, dod @ vblk.T)
     ds = np.where(valid, (p / l[:, None]) * (dp - D[:, None]), 0.0)
-    dsq = _ds_quantize(ds, valid, num.rule) if num.quantize_ds else ds
+    if num.exact and num.quantize_ds:
+        # exact option: one payload per product, each with the other operand's
+        # per-token exponent folded in and one exponent per 32 along its
+        # contraction axis (fw carries the per-token Q and K exponents)
+        dsq = _ds_exact(ds, valid, fw["k_exp_tok"], True, num.rule)
+        dsq_k = _ds_exact(ds, valid, fw["q_exp_tok"], False, num.rule)
+    else:
+        dsq = _ds_quantize(ds, valid, num.rule) if num.quantize_ds else ds
+        dsq_k = dsq
     dv = (peff / l[:, None]).T @ dod
     dq = float(s32) * (dsq @ kd)
-    dk = float(s32) * (dsq.T @ qd)
+    dk = float(s32) * (dsq_k.T @ qd)
     nz = valid & (ds != 0)
     zeroed = int(np.count_nonzero(nz & (dsq == 0)))
-    return dict(D=D, ds=ds, dsq=dsq, dq=dq, dk=dk, dv=dv,
+    return dict(D=D, ds=ds, dsq=dsq, dsq_k=dsq_k, dq=dq, dk=dk, dv=dv,
                 ds_nonzero=int(np.count_nonzero(nz)), ds_zeroed=zeroed)
 
 
@@ -186,9 +251,12 @@ def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
         raise ValueError("key/value heads must divide query heads")
     group = H // Hk
     s32, c32 = scale_constants(d, num.softmax_scale)
+    gran = "token" if num.exact else num.granularity      # exact option: per-token operand scales
+    if num.exact and num.path != "mxfp8":
+        raise ValueError("the exact option is defined for the MXFP8 path")
     if num.quantize_operands:
-        qt = quantize_qkv(q, k, v, cu_seqlens, num.hadamard, num.rule, num.granularity)
-        do_codes, do_exp, do_deq = quantize_token_blocks(do, cu_seqlens, num.rule, num.granularity)
+        qt = quantize_qkv(q, k, v, cu_seqlens, num.hadamard, num.rule, gran)
+        do_codes, do_exp, do_deq = quantize_token_blocks(do, cu_seqlens, num.rule, gran)
         qs_all, ks_all = qt["q"], qt["k"]
         if num.path == "mixed":
             from .nvfp4 import quantize_nvfp4
@@ -228,6 +296,8 @@ def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
             fw = forward_doc(qs_all[sl, h], ks_all[sl, hk], qt["v"][sl, hk], qt["v_key"][sl, hk],
                              qt["v_exp"][hk, sl], qt["v_key_exp"][hk, sl], c32, num)
             o_out = _out(fw["o"], num)
+            if num.exact:
+                fw["q_exp_tok"], fw["k_exp_tok"] = qt["q_exp"][h, sl], qt["k_exp"][hk, sl]
             bw = backward_doc(fw, qt["q"][sl, h], qt["k"][sl, hk], qt["v"][sl, hk],
                               qt["v_key"][sl, hk], do_deq[sl, h], o_out, s32, num)
             o[sl, h] = o_out

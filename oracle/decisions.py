@@ -91,12 +91,8 @@ def doc_head_allowances(fw, qs, ks, qd, kd, vblk, vkey, dod, s32, c32, num: Nume
     w_sp = c * e_s + 2 * U * np.abs(sp)
     rel_p = np.where(valid, np.exp2(w_sp) * (1 + 4 * U) - 1.0, 0.0)
     # P^ decisions (diagonal pairs are folded, then unfolded)
-    v_exp_key = fw.get("v_exp_key")
-    f = np.ones_like(p)
     if num.quantize_p:
-        if v_exp_key is not None:
-            e_ref = fold_reference(v_exp_key, num.causal)
-            f = np.where(diag, np.ldexp(1.0, np.minimum(v_exp_key[None, :] - e_ref[:, None], 0)), 1.0)
+        f = fw["fold"]                      # the forward's fold factor of every pair (1 off the fold)
         x = np.ldexp(p * f, 8)
         span_pe = np.where(valid, np.ldexp(_e4m3_span(x * (1 - rel_p), x * (1 + rel_p)), -8) / f, 0.0)
     else:
@@ -143,49 +139,77 @@ def _ds_decisions(fw, dod, vblk, vkey, rel_p, rel_l, num: Numerics):
              + gamma(d) * np.sum(np.abs(dod * o_out), axis=1)[:, None])
     grow = (1 + rel_p) * (1 + rel_l[:, None])
     e_ds = np.where(valid, np.abs(ds) * (grow * (1 + 3 * U) - 1) + (p / l[:, None]) * grow * e_dpd, 0.0)
-    rows, cols, lo, hi = [], [], [], []
+    payloads = {"q": (None, True), "k": (None, False)}
+    if num.exact:
+        payloads = {"q": (fw["k_exp_tok"], True), "k": (fw["q_exp_tok"], False)}
+    res = {}
     blocks_ambiguous = 0
-    for i0 in range(0, L, BLOCK):
-        for j0 in range(0, L, BLOCK):
-            v = valid[i0:i0 + BLOCK, j0:j0 + BLOCK]
-            if not v.any():
-                continue
-            x = np.where(v, ds[i0:i0 + BLOCK, j0:j0 + BLOCK], 0.0)
-            ex = np.where(v, e_ds[i0:i0 + BLOCK, j0:j0 + BLOCK], 0.0)
-            amax, emax = np.abs(x).max(), ex.max()
-            eb = formats.roundup_exponent(amax)
-            if formats.roundup_exponent(max(amax - emax, 0.0)) != formats.roundup_exponent(amax + emax):
-                blocks_ambiguous += 1
-            q0 = np.ldexp(formats.e4m3_round(np.ldexp(x, -eb)), eb)
-            ql = np.ldexp(formats.e4m3_round(np.ldexp(x - ex, -eb), saturate=True), eb)
-            qh = np.ldexp(formats.e4m3_round(np.ldexp(x + ex, -eb), saturate=True), eb)
-            ii, jj = np.nonzero(v & (ql != qh))
-            rows.append(ii + i0)
-            cols.append(jj + j0)
-            lo.append((ql - q0)[ii, jj])
-            hi.append((qh - q0)[ii, jj])
+    for name, (e_fold, by_rows) in payloads.items():
+        if not num.exact and name == "k":
+            res["k"] = res["q"]             # one payload serves both products
+            continue
+        sc = np.ones(L) if e_fold is None else np.ldexp(1.0, np.asarray(e_fold, dtype=np.int64))
+        fold = sc[None, :] if by_rows else sc[:, None]
+        xs, es = ds * fold, e_ds * fold
+        if num.exact and not by_rows:
+            xs, es, vt = xs.T, es.T, valid.T
+        else:
+            vt = valid
+        rows, cols, lo, hi = [], [], [], []
+        # groups: 32 x 32 blocks (default), or one row x 32 along the contraction axis (exact)
+        gr = 1 if num.exact else BLOCK
+        for i0 in range(0, L, gr):
+            for j0 in range(0, L, BLOCK):
+                v = vt[i0:i0 + gr, j0:j0 + BLOCK]
+                if not v.any():
+                    continue
+                x = np.where(v, xs[i0:i0 + gr, j0:j0 + BLOCK], 0.0)
+                ex = np.where(v, es[i0:i0 + gr, j0:j0 + BLOCK], 0.0)
+                amax, emax = np.abs(x).max(), ex.max()
+                eb = formats.roundup_exponent(amax)
+                if formats.roundup_exponent(max(amax - emax, 0.0)) != formats.roundup_exponent(amax + emax):
+                    blocks_ambiguous += 1
+                q0 = np.ldexp(formats.e4m3_round(np.ldexp(x, -eb)), eb)
+                ql = np.ldexp(formats.e4m3_round(np.ldexp(x - ex, -eb), saturate=True), eb)
+                qh = np.ldexp(formats.e4m3_round(np.ldexp(x + ex, -eb), saturate=True), eb)
+                gi, gj = np.nonzero(v & (ql != qh))
+                dlo, dhi = (ql - q0)[gi, gj], (qh - q0)[gi, gj]
+                ti, tj = gi + i0, gj + j0
+                i_, j_ = (tj, ti) if (num.exact and not by_rows) else (ti, tj)
+                fl = sc[j_] if by_rows else sc[i_]     # remove the fold: deltas of the unfolded dS
+                rows.append(i_)
+                cols.append(j_)
+                lo.append(dlo / fl)
+                hi.append(dhi / fl)
+        res[name] = (rows, cols, lo, hi)
     cat = (lambda a, t: np.concatenate(a).astype(t) if a else np.zeros(0, t))
-    return dict(ds_rows=cat(rows, np.int64), ds_cols=cat(cols, np.int64), ds_lo=cat(lo, np.float64),
-                ds_hi=cat(hi, np.float64), ds_blocks_ambiguous=blocks_ambiguous)
+    out = {"ds_blocks_ambiguous": blocks_ambiguous}
+    for name, (rows, cols, lo, hi) in res.items():
+        out[f"ds{name}_rows"], out[f"ds{name}_cols"] = cat(rows, np.int64), cat(cols, np.int64)
+        out[f"ds{name}_lo"], out[f"ds{name}_hi"] = cat(lo, np.float64), cat(hi, np.float64)
+    return out
 
 
 def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
     """Decision bounds of the whole call (see the module docstring): ``o``
     ``[T, H, d]`` and ``dv`` ``[T, Hk, d]`` per-element allowances; ``e_D``
     ``[T, H]``, the bound of the admissible shift of D per query row;
-    ``dq_dir`` ``[T, H, d]``, the change of dQ per unit shift of D; and ``ds``,
-    the dS^ codes admissible evaluations may round either way: query token
-    ``tq`` and head ``h``, key token ``tk`` and key/value head ``hk``, the
-    range [lo, hi] of the change of the dS^ value, and the changes of the dQ
-    row (``dq_vec``) and of the dK row (``dk_vec``) per unit change of it."""
+    ``dq_dir`` ``[T, H, d]``, the change of dQ per unit shift of D; and
+    ``ds_q`` / ``ds_k``, the codes of the dS^ payload of dQ / of dK that
+    admissible evaluations may round either way (one payload serves both
+    unless the exact option is on): query token ``tq`` and head ``h``, key
+    token ``tk`` and key/value head ``hk``, the range [lo, hi] of the change
+    of the effective dS value, and ``vec``, the change of the dQ row (of the
+    dK row) per unit change of it."""
     num = num or Numerics()
     q = np.asarray(q, dtype=np.float64)
     T, H, d = q.shape
     Hk = np.asarray(k).shape[1]
     group = H // Hk
     s32, c32 = scale_constants(d, num.softmax_scale)
-    qt = quantize_qkv(q, k, v, cu_seqlens, num.hadamard, num.rule, num.granularity)
-    _, _, do_deq = quantize_token_blocks(do, cu_seqlens, num.rule, num.granularity)
+    gran = "token" if num.exact else num.granularity
+    qt = quantize_qkv(q, k, v, cu_seqlens, num.hadamard, num.rule, gran)
+    _, _, do_deq = quantize_token_blocks(do, cu_seqlens, num.rule, gran)
     qs_all, ks_all = qt["q"], qt["k"]
     if num.path == "mixed":
         from .nvfp4 import quantize_nvfp4
@@ -194,7 +218,7 @@ def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
         *_, ks_all = quantize_nvfp4(qt["k_rot"], ka)
     from .hadamard import rotate_back_fp64
     out = dict(o=np.zeros((T, H, d)), dq_dir=np.zeros((T, H, d)), e_D=np.zeros((T, H)))
-    amb = {k_: [] for k_ in ("tq", "h", "tk", "hk", "lo", "hi", "dq_vec", "dk_vec")}
+    amb = {n_: {k_: [] for k_ in ("tq", "h", "tk", "hk", "lo", "hi", "vec")} for n_ in ("q", "k")}
     blocks_ambiguous = 0
     dv_w = np.zeros((T, Hk, d))
     dv_raw = np.zeros((T, Hk, d))
@@ -207,6 +231,8 @@ def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
             fw = forward_doc(qs_all[sl, h], ks_all[sl, hk], qt["v"][sl, hk], qt["v_key"][sl, hk],
                              qt["v_exp"][hk, sl], qt["v_key_exp"][hk, sl], c32, num)
             fw["v_exp_key"] = qt["v_key_exp"][hk, sl]
+            if num.exact:
+                fw["q_exp_tok"], fw["k_exp_tok"] = qt["q_exp"][h, sl], qt["k_exp"][hk, sl]
             a = doc_head_allowances(fw, qs_all[sl, h], ks_all[sl, hk], qt["q"][sl, h], qt["k"][sl, hk],
                                     qt["v"][sl, hk], qt["v_key"][sl, hk], do_deq[sl, h], s32, c32, num)
             out["o"][sl, h] = a["o"]
@@ -214,23 +240,24 @@ def allowances(q, k, v, do, cu_seqlens, num: Numerics | None = None):
             out["dq_dir"][sl, h] = rotate_back_fp64(a["dq_dir"]) if num.hadamard else a["dq_dir"]
             dv_w[sl, hk] += a["dv"]
             dv_raw[sl, hk] += (fw["peff"] / fw["l"][:, None]).T @ do_deq[sl, h]
-            if "ds_rows" in a:
-                r, cidx = a["ds_rows"], a["ds_cols"]
-                kd_o = qt["k"][sl, hk][cidx]
-                qd_o = qt["q"][sl, h][r]
-                if num.hadamard:
-                    kd_o, qd_o = rotate_back_fp64(kd_o), rotate_back_fp64(qd_o)
-                amb["tq"].append(r + s)
-                amb["h"].append(np.full(len(r), h))
-                amb["tk"].append(cidx + s)
-                amb["hk"].append(np.full(len(r), hk))
-                amb["lo"].append(a["ds_lo"])
-                amb["hi"].append(a["ds_hi"])
-                amb["dq_vec"].append(float(s32) * kd_o)
-                amb["dk_vec"].append(float(s32) * qd_o)
+            if "dsq_rows" in a:
+                for name, vec_src, vec_idx in (("q", qt["k"][sl, hk], "cols"), ("k", qt["q"][sl, h], "rows")):
+                    r, cidx = a[f"ds{name}_rows"], a[f"ds{name}_cols"]
+                    vecs = vec_src[cidx if vec_idx == "cols" else r]
+                    if num.hadamard:
+                        vecs = rotate_back_fp64(vecs)
+                    e_ = amb[name]
+                    e_["tq"].append(r + s)
+                    e_["h"].append(np.full(len(r), h))
+                    e_["tk"].append(cidx + s)
+                    e_["hk"].append(np.full(len(r), hk))
+                    e_["lo"].append(a[f"ds{name}_lo"])
+                    e_["hi"].append(a[f"ds{name}_hi"])
+                    e_["vec"].append(float(s32) * vecs)
                 blocks_ambiguous += a["ds_blocks_ambiguous"]
     out["dv"] = _bf16_span(dv_raw, dv_w) if num.round_outputs else dv_w
-    out["ds"] = {k_: (np.concatenate(v_) if v_ else np.zeros((0, d) if k_.endswith("vec") else 0))
-                 for k_, v_ in amb.items()}
+    for n_ in ("q", "k"):
+        out[f"ds_{n_}"] = {k_: (np.concatenate(v_) if v_ else np.zeros((0, d) if k_ == "vec" else 0))
+                           for k_, v_ in amb[n_].items()}
     out["ds_blocks_ambiguous"] = blocks_ambiguous
     return out

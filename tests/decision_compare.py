@@ -97,14 +97,15 @@ def compare(name, got, want, al=None, tol=TOL_REL):
         rel = rel_plain
     elif name in ("dq", "dk"):
         T, Hx, d = diff.shape
-        ds = al["ds"]
         if name == "dq":
+            ds = al["ds_q"]
             rows = ds["tq"] * Hx + ds["h"]
             fixed = (al["dq_dir"].reshape(-1, d), al["e_D"].reshape(-1))
-            vec = ds["dq_vec"]
         else:
+            ds = al["ds_k"]
             rows = ds["tk"] * Hx + ds["hk"]
-            fixed, vec = None, ds["dk_vec"]
+            fixed = None
+        vec = ds["vec"]
         # rows above half the bar are refitted, so the reported remainder shows
         # what the decisions explain near the bar, not only the pass/fail
         resid = _row_fit(diff.reshape(-1, d), _groups(rows, vec, ds["lo"], ds["hi"]), fixed,

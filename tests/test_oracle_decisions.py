@@ -22,19 +22,22 @@ from oracle import formats, quant
 from precision_causal_attention_hadamard_amd import workloads as W
 
 
-def doc_head(wl, doc, h):
+def doc_head(wl, doc, h, exact=False):
     """Quantized operands, forward record and allowances of one (document, head)."""
     q, k, v, do = [t.float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
-    num = A.Numerics(hadamard=wl.hadamard)
+    num = A.Numerics(hadamard=wl.hadamard, exact=exact)
     s32, c32 = A.scale_constants(wl.head_dim, None)
-    qt = quant.quantize_qkv(q, k, v, wl.cu_seqlens, wl.hadamard)
-    _, _, dod = quant.quantize_token_blocks(do, wl.cu_seqlens)
+    gran = "token" if exact else "block"
+    qt = quant.quantize_qkv(q, k, v, wl.cu_seqlens, wl.hadamard, granularity=gran)
+    _, _, dod = quant.quantize_token_blocks(do, wl.cu_seqlens, granularity=gran)
     hk = h // (wl.heads // wl.kv_heads)
     s, e = wl.cu_seqlens[doc], wl.cu_seqlens[doc + 1]
     ops = dict(q=qt["q"][s:e, h], k=qt["k"][s:e, hk], v=qt["v"][s:e, hk], vk=qt["v_key"][s:e, hk],
                vx=qt["v_exp"][hk, s:e], vkx=qt["v_key_exp"][hk, s:e], do=dod[s:e, h])
     fw = A.forward_doc(ops["q"], ops["k"], ops["v"], ops["vk"], ops["vx"], ops["vkx"], c32, num)
     fw["v_exp_key"] = ops["vkx"]
+    if exact:
+        fw["q_exp_tok"], fw["k_exp_tok"] = qt["q_exp"][h, s:e], qt["k_exp"][hk, s:e]
     al = DC.doc_head_allowances(fw, ops["q"], ops["k"], ops["q"], ops["k"], ops["v"], ops["vk"], ops["do"],
                                 s32, c32, num)
     return ops, fw, al, num, s32, c32
@@ -50,8 +53,11 @@ def peff_from_scores(S, fw, ops, c32, rng):
     p = np.where(valid, np.exp2(np.where(valid, sp - m[:, None], 0.0)), 0.0)
     p = p * (1 + rng.uniform(-4, 4, p.shape) * DC.U)
     l = p.sum(axis=1) * (1 + rng.uniform(-1, 1, L) * DC.gamma(L))
-    e_ref = quant.fold_reference(ops["vkx"], True)
-    f = np.where(diag, np.ldexp(1.0, np.minimum(ops["vkx"][None, :] - e_ref[:, None], 0)), 1.0)
+    if np.array_equal(diag, valid):      # exact option: the all-tile fold (pinned by test_oracle_exact)
+        f = fw["fold"]
+    else:
+        e_ref = quant.fold_reference(ops["vkx"], True)
+        f = np.where(diag, np.ldexp(1.0, np.minimum(ops["vkx"][None, :] - e_ref[:, None], 0)), 1.0)
     pe = np.where(diag, np.ldexp(formats.e4m3_round(np.ldexp(p * f, 8)), -8) / f,
                   np.ldexp(formats.e4m3_round(np.ldexp(p, 8)), -8))
     pe = np.where(valid, pe, 0.0)
@@ -75,11 +81,12 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("exact", [False, True], ids=["default", "exact"])
 @pytest.mark.parametrize("case", list(CASES))
-def test_admissible_scores_stay_inside_the_bounds(case):
+def test_admissible_scores_stay_inside_the_bounds(case, exact):
     wl = CASES[case]()
     doc, h = (1, 3) if case.startswith("outliers") else (0, 1)
-    ops, fw, al, num, s32, c32 = doc_head(wl, doc, h)
+    ops, fw, al, num, s32, c32 = doc_head(wl, doc, h, exact)
     rng = np.random.default_rng(5)
     S0 = ops["q"] @ ops["k"].T
     e_s = DC.gamma(wl.head_dim) * (np.abs(ops["q"]) @ np.abs(ops["k"]).T) + DC.U * np.abs(S0)
@@ -127,22 +134,25 @@ def test_dq_moves_along_the_stated_direction_under_a_shift_of_o():
     assert np.count_nonzero(np.abs(b1["dq"] - b0["dq"]).max(axis=1) > 0) == len(rows)
 
 
+@pytest.mark.parametrize("exact", [False, True], ids=["default", "exact"])
 @pytest.mark.parametrize("case", list(CASES))
-def test_admissible_ds_codes_are_listed_decisions(case):
+def test_admissible_ds_codes_are_listed_decisions(case, exact):
     wl = CASES[case]()
     doc, h = (1, 3) if case.startswith("outliers") else (0, 1)
-    ops, fw, al, num, s32, c32 = doc_head(wl, doc, h)
+    ops, fw, al, num, s32, c32 = doc_head(wl, doc, h, exact)
     rng = np.random.default_rng(11)
     L, d = ops["q"].shape
     valid, diag, p, l = fw["valid"], fw["diag"], fw["p"], fw["l"]
     o_out = formats.bf16_round(fw["o"])
     ref = A.backward_doc(fw, ops["q"], ops["k"], ops["v"], ops["vk"], ops["do"], o_out, s32, num)
     D = np.sum(ops["do"] * o_out, axis=1)
+    if exact:       # every pair uses the per-key V codes (the forward's diag covers all visible pairs)
+        assert np.array_equal(diag, valid)
     dp = np.where(diag, ops["do"] @ ops["vk"].T, ops["do"] @ ops["v"].T)
     dp_abs = np.where(diag, np.abs(ops["do"]) @ np.abs(ops["vk"]).T, np.abs(ops["do"]) @ np.abs(ops["v"]).T)
-    listed = {}
-    for r, c_, lo, hi in zip(al["ds_rows"], al["ds_cols"], al["ds_lo"], al["ds_hi"]):
-        listed[(int(r), int(c_))] = (lo, hi)
+    listed = {n_: {(int(r), int(c_)): (lo, hi) for r, c_, lo, hi in
+                   zip(al[f"ds{n_}_rows"], al[f"ds{n_}_cols"], al[f"ds{n_}_lo"], al[f"ds{n_}_hi"])}
+              for n_ in ("q", "k")}
     changed = 0
     for trial in range(6):
         sgn = (lambda shape: np.sign(rng.uniform(-1, 1, shape))) if trial % 2 else \
@@ -153,23 +163,31 @@ def test_admissible_ds_codes_are_listed_decisions(case):
             DC.gamma(d) * np.sum(np.abs(ops["do"] * o_out), axis=1)[:, None]
         dpd = dp - D[:, None] + sgn(dp.shape) * e_dpd
         ds = np.where(valid, (p_a / l_a[:, None]) * dpd * (1 + sgn(dp.shape) * 3 * DC.U), 0.0)
-        dsq = A._ds_quantize(ds, valid, "roundup")
-        # blocks whose exponent moved are outside what the list covers
-        same_exp = np.ones_like(valid)
-        for i0 in range(0, L, 32):
-            for j0 in range(0, L, 32):
-                v = valid[i0:i0 + 32, j0:j0 + 32]
-                if v.any():
-                    e0 = formats.roundup_exponent(np.abs(np.where(v, ref["ds"][i0:i0 + 32, j0:j0 + 32], 0)).max())
-                    e1 = formats.roundup_exponent(np.abs(np.where(v, ds[i0:i0 + 32, j0:j0 + 32], 0)).max())
-                    same_exp[i0:i0 + 32, j0:j0 + 32] = e0 == e1
-        delta = dsq - ref["dsq"]
-        ii, jj = np.nonzero((delta != 0) & same_exp)
-        for i, j in zip(ii, jj):
-            assert (i, j) in listed, (trial, i, j, ds[i, j], ref["ds"][i, j])
-            lo, hi = listed[(i, j)]
-            assert lo - 1e-300 <= delta[i, j] <= hi + 1e-300
-        changed += len(ii)
+        for n_, ref_q in (("q", ref["dsq"]), ("k", ref["dsq_k"])):
+            if exact:
+                e_fold = fw["k_exp_tok"] if n_ == "q" else fw["q_exp_tok"]
+                dsq = A._ds_exact(ds, valid, e_fold, n_ == "q", "roundup")
+                fold = np.ldexp(1.0, e_fold)[None, :] if n_ == "q" else np.ldexp(1.0, e_fold)[:, None]
+                g0, g1 = (1, 32) if n_ == "q" else (32, 1)
+            else:
+                dsq = A._ds_quantize(ds, valid, "roundup")
+                fold, (g0, g1) = 1.0, (32, 32)
+            # groups whose exponent moved are outside what the list covers
+            same_exp = np.ones_like(valid)
+            for i0 in range(0, L, g0):
+                for j0 in range(0, L, g1):
+                    v = valid[i0:i0 + g0, j0:j0 + g1]
+                    if v.any():
+                        a0 = np.abs(np.where(v, (ref["ds"] * fold)[i0:i0 + g0, j0:j0 + g1], 0)).max()
+                        a1 = np.abs(np.where(v, (ds * fold)[i0:i0 + g0, j0:j0 + g1], 0)).max()
+                        same_exp[i0:i0 + g0, j0:j0 + g1] = formats.roundup_exponent(a0) == formats.roundup_exponent(a1)
+            delta = dsq - ref_q
+            ii, jj = np.nonzero((delta != 0) & same_exp)
+            for i, j in zip(ii, jj):
+                assert (i, j) in listed[n_], (n_, trial, i, j, ds[i, j], ref["ds"][i, j])
+                lo, hi = listed[n_][(i, j)]
+                assert lo * (1 + 1e-12) - 1e-300 <= delta[i, j] <= hi * (1 + 1e-12) + 1e-300
+            changed += len(ii)
     assert changed > 0
 
 
@@ -187,6 +205,6 @@ def test_the_observed_near_ties_are_flagged():
     assert al["o"][73].max() > 0
     wl2 = W.small_packed(41, [1, 17, 45, 100, 33, 64, 130, 2], heads=4, head_dim=64, kv_heads=2)
     ops2, fw2, al2, *_ = doc_head(wl2, 6, 1)
-    k_ = [n for n, (r, c_) in enumerate(zip(al2["ds_rows"], al2["ds_cols"])) if (r, c_) == (30, 20)]
+    k_ = [n for n, (r, c_) in enumerate(zip(al2["dsq_rows"], al2["dsq_cols"])) if (r, c_) == (30, 20)]
     assert len(k_) == 1
-    assert (al2["ds_lo"][k_[0]], al2["ds_hi"][k_[0]]) == (-8 * 2.0 ** -6, 0.0)
+    assert (al2["dsq_lo"][k_[0]], al2["dsq_hi"][k_[0]]) == (-8 * 2.0 ** -6, 0.0)
