@@ -157,6 +157,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped-query variant of the workload: K and V with this many heads (0: one per query head)")
+    ap.add_argument("--exact", action="store_true",
+                    help="the exact option: per-token scales, all-tile V fold, per-row/per-key dS exponents")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true",
                     help="ordered dQ reduction (per-step partials, fixed-order fp16 sum) instead of atomics")
@@ -188,7 +190,7 @@ def main():
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
                                causal_dq_scale=wl.causal_dq_scale, path=wl.path,
-                               deterministic=args.deterministic)
+                               deterministic=args.deterministic, exact=args.exact)
     T, H, d = call.shape
     Hk = call.kv_heads
     grouped = Hk != H
@@ -252,7 +254,7 @@ def main():
     else:
         achieved, unit = work / t_dom / 1e9, "GB/s"
     traffic = (measured_traffic(kname, f"config{args.config}")
-               if kname.startswith("attn_bwd") and not grouped else None)
+               if kname.startswith("attn_bwd") and not grouped and not args.exact else None)
     roofline = {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic,
                 "peak_note": "dtype-weighted: FP8 products at 5000, bf16 products at 2500 TFLOP/s"
@@ -270,7 +272,7 @@ def main():
         "config": {"workload": wl.name, "tokens": T, "heads": H, "kv_heads": Hk, "head_dim": d,
                    "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
                    "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
-                   "deterministic": bool(args.deterministic),
+                   "deterministic": bool(args.deterministic), "exact": bool(args.exact),
                    "causal_pairs": pairs, "flops_per_step": flops},
         "pct_fp8_peak": 100.0 * value / FP8_PEAK_TFLOPS,
         "stage_ms": stage_ms, "event_ms_per_step": event_ms,

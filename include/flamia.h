@@ -83,6 +83,16 @@ typedef struct flamia_attn_desc {
                                    the sums over its H / Hk query heads, accumulated in fp32 and
                                    rounded once ([Reading, 5.2] measures GQA workloads).  MXFP8
                                    path only (path = 1 with Hk < H: FLAMIA_ERR_UNSUPPORTED) */
+  int32_t exact;                /* 1: the exact option ([Summary] bullets on causally safe scales;
+                                   [Reading, 4.2]): one exponent per token (and head) for Q, K, V
+                                   and dO; V's per-token exponents folded into P on every tile
+                                   against the largest exponent of the key block the query may see;
+                                   dS quantized twice -- for dQ with the key's K exponent folded in,
+                                   one exponent per (query, 32 keys), for dK with the query's Q
+                                   exponent folded in, one exponent per (key, 32 queries) -- and a
+                                   per-token causal dQ prescale.  No output depends on a later
+                                   position's inputs.  MXFP8 path with Hk = H only (else
+                                   FLAMIA_ERR_UNSUPPORTED) */
 } flamia_attn_desc;
 
 /*
@@ -107,6 +117,9 @@ typedef struct flamia_attn_desc {
  *  v_ref_exp          [H,T] per query: largest v_key_exp among the keys of
  *                     its own block it may see (the fold reference of the
  *                     diagonal P^V product).
+ *  k_ref_exp          [H,T] exact option only (else NULL): per token, the
+ *                     largest k_exp among the tokens of its own block up to
+ *                     it (with v_ref_exp, the causal dQ prescale's inputs).
  *  plan               opaque GPU-built longest-first work lists.
  *  Mixed path only (NULL when path = 0), [Summary] opening paragraphs and
  *  [Reading, 4.1]: NVFP4 score operands of Q and K (after the rotation):
@@ -138,6 +151,7 @@ typedef struct flamia_qtensors {
   float* qk_tensor_scale;
   void* q_fp4_bf16;
   void* k_fp4_bf16;
+  uint8_t* k_ref_exp;
 } flamia_qtensors;
 
 /*

@@ -76,6 +76,7 @@ struct BwdArgs {
   uint16_t* dq_part;      // deterministic mode: fp16 dQ partial slots
   const int* det_base;    // deterministic mode: first step of each document
   int det_cap;            // deterministic mode: steps per head in dq_part
+  const uint8_t* v_ref_exp;    // exact option: V's in-block prefix maximum (block maxima at block ends)
   const uint16_t *q_x, *k_x;   // mixed path: NVFP4 Q and K expanded to bf16
   const float* qk_scale;       // mixed path: [2], [3] tensor scales
 };
@@ -585,7 +586,12 @@ __device__ __forceinline__ int dsk_off(int r, int chunk) {
 // group is split over gsplit items, which store fp32 partials that a reduce
 // kernel adds in order and rounds once.  GRP = false is the one-head-per-item
 // instantiation (H = Hk): the loop runs the query tiles of one head only.
-template <int D, bool DET, bool GRP>
+// EXACT (exact option, with GRP = false): Q, K, V, dO scales are per token --
+// the recomputed S and dP take each row's exponent as its operand scale; every
+// key block folds V's exponents into P for dV; dS is quantized twice, with
+// K's exponent folded in and one exponent per (query, 32 keys) for dQ, and
+// with Q's exponent folded in and one exponent per (key, 32 queries) for dK.
+template <int D, bool DET, bool GRP, bool EXACT>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
@@ -613,6 +619,13 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sKQ[BWD_BQ * DQS * 2];  // fp16 dQ partial of a step
   __shared__ int sEds[2][4];
   __shared__ int sKeB[4];
+  // exact option: the dQ payload (same layout as sdSK), its exponents per (key
+  // block, query), the dK payload's exponents per (query half, key), and each
+  // key block's largest V exponent
+  __shared__ __attribute__((aligned(1024))) uint8_t sdSQ[EXACT ? BWD_BK * BWD_BQ : 16];
+  __shared__ uint8_t sRowE[EXACT ? 4 : 1][BWD_BQ];
+  __shared__ uint8_t sColE[EXACT ? 2 : 1][BWD_BK];
+  __shared__ int sVrB[4];
 
   const Problem& p = a.p;
   const int H = p.H, T = p.T, Hk = p.Hk;
@@ -703,6 +716,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
   issue_tile(std::integral_constant<int, 0>{}, qt_first, h_first);
   if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hTk + k0 + 32 * tid] : E8M0_BIAS;
+  if (EXACT && tid >= 4 && tid < 8) sVrB[tid - 4] = a.v_ref_exp[hTk + min(k0 + 32 * (tid - 4) + 31, L - 1)];
   int ke, ve, vke;
   {
     const size_t mi = hTk + min(j, L - 1);
@@ -817,7 +831,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const int QB = 2 * qt + qh;
     const bool act = kb_active && QB >= KB && 32 * qh < nq;
     const bool dia = QB == KB;
-    const bool fast = !dia && 32 * qh + 32 <= nq;   // no mask, no fold
+    const bool fast = !EXACT && !dia && 32 * qh + 32 <= nq;   // no mask, no fold
     int dsc[4] = {0, 0, 0, 0};
     int eds = -127;
     v16f sacc, pacc;     // set (and read) only when act
@@ -829,7 +843,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) pacc[4 * g + r] = dlv[r];
       }
-      const int qx = pqx[32 * qh];
+      // exact option: each row's own exponent (lane n supplies row n's scale)
+      const int qx = pqx[32 * qh + (EXACT ? n : 0)];
       const int sqe = qx & 255, sdoe = (qx >> 8) & 255;
       const uint8_t* qrow = tQ + 32 * qh * D;
       const uint8_t* drow = tdO + 32 * qh * D;
@@ -843,8 +858,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         s_step(s);
         // diagonal block: per-key V~ codes
         pacc = mfma_f8(cat8(ld16(drow + offA[s][0]), ld16(drow + offA[s][1])),
-                       dia ? vkey(s) : cat8(ld16(vbase + offA[s][0]), ld16(vbase + offA[s][1])), pacc, sdoe,
-                       dia ? vke : ve);
+                       (!EXACT && dia) ? vkey(s) : cat8(ld16(vbase + offA[s][0]), ld16(vbase + offA[s][1])), pacc,
+                       sdoe, (!EXACT && dia) ? vke : ve);
       }
     }
     // the next tile streams in while this one is computed; last step's dQ
@@ -901,8 +916,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
               const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
               const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
               dsr = (p8 * ilv[r]) * pacc[rr];
-              if (dia) {
-                const int vref = ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
+              if (EXACT || dia) {
+                const int vref = (EXACT && !dia) ? sVrB[kb] - E8M0_BIAS : ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
                 const int code = cvt_fp8x2(__builtin_amdgcn_ldexpf(p8, e_key - vref), 0.f);
                 pev = __builtin_amdgcn_ldexpf(fp8_value(code, 0), vref - e_key);
               } else {
@@ -917,6 +932,45 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           pe[2 * g + 1] = (uint32_t)f32_to_bf16_bits(pf[2]) | ((uint32_t)f32_to_bf16_bits(pf[3]) << 16);
         }
       }
+      if constexpr (EXACT) {
+        // dQ payload: K's per-token exponent of the lane's key folded in, one
+        // exponent per query row over this block's 32 keys (the lanes of a half)
+        const int ekf = ke - E8M0_BIAS;
+        int dqc[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float xq[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rr = 4 * g + r;
+            float m = fabsf(__builtin_amdgcn_ldexpf(dsv[rr], ekf));
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            const int er = roundup_exp(m);
+            if (n == rr) sRowE[kb][32 * qh + 8 * (rr >> 2) + 4 * hh + (rr & 3)] = (uint8_t)(er + E8M0_BIAS);
+            xq[r] = __builtin_amdgcn_ldexpf(dsv[rr], ekf - er);
+          }
+          dqc[g] = cvt_fp8x4(xq[0], xq[1], xq[2], xq[3]);
+        }
+        st16(sdSQ + dsk_off(32 * kb + n, 2 * hh + qh), v4i{dqc[0], dqc[1], dqc[2], dqc[3]});
+        // dK payload: Q's per-token exponent of each row folded in, one exponent
+        // per key (lane) over the wave's 32 queries (both halves)
+        float mk = 0.f;
+        float xk[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int eqf = (pqx[32 * qh + 8 * (rr >> 2) + 4 * hh + (rr & 3)] & 255) - E8M0_BIAS;
+          xk[rr] = __builtin_amdgcn_ldexpf(dsv[rr], eqf);
+          mk = fmaxf(mk, fabsf(xk[rr]));
+        }
+        mk = fmaxf(mk, __shfl_xor(mk, 32, 64));
+        const int ec = roundup_exp(mk);
+        if (hh == 0) sColE[qh][32 * kb + n] = (uint8_t)(ec + E8M0_BIAS);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          dsc[g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(xk[4 * g], -ec), __builtin_amdgcn_ldexpf(xk[4 * g + 1], -ec),
+                             __builtin_amdgcn_ldexpf(xk[4 * g + 2], -ec), __builtin_amdgcn_ldexpf(xk[4 * g + 3], -ec));
+      } else {
       // amax >= 0, so its bits order like the values
       const int e = roundup_exp(__int_as_float(wave_max_i(__float_as_int(amax))));
       eds = e;
@@ -936,6 +990,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           dsc[g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(dsv[4 * g], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 1], -e),
                              __builtin_amdgcn_ldexpf(dsv[4 * g + 2], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 3], -e));
       }
+      }
       // dV += P^_eff^T G over this wave's 32 queries (two K-steps of 16)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -951,6 +1006,11 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         }
       }
     }
+    if (EXACT && !act) {     // zero codes; any finite scale
+      st16(sdSQ + dsk_off(32 * kb + n, 2 * hh + qh), v4i{0, 0, 0, 0});
+      if (n < 16) sRowE[kb][32 * qh + 8 * (n >> 2) + 4 * hh + (n & 3)] = (uint8_t)E8M0_BIAS;
+      if (hh == 0) sColE[qh][32 * kb + n] = (uint8_t)E8M0_BIAS;
+    }
     // dS^ to LDS key-major: row = key, one 16-byte chunk per lane
     st16(sdSK + dsk_off(32 * kb + n, 2 * hh + qh), v4i{dsc[0], dsc[1], dsc[2], dsc[3]});
     if (lane == 0) sEds[qh][kb] = eds;
@@ -960,8 +1020,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     if (kb_active) {
       // K-block 0 = query half 0 (chunk 2 hh), K-block 1 = query half 1 (chunk 2 hh + 1)
       const v8i adk = cat8(ld16(sdSK + dsk_off(32 * kb + n, 2 * hh)), ld16(sdSK + dsk_off(32 * kb + n, 2 * hh + 1)));
-      const int sa = sEds[hh][kb] + E8M0_BIAS;
-      const int sb = pqx[32 * hh] & 255;
+      const int sa = EXACT ? (int)sColE[hh][32 * kb + n] : sEds[hh][kb] + E8M0_BIAS;
+      const int sb = EXACT ? E8M0_BIAS : pqx[32 * hh] & 255;
 #pragma unroll
       for (int e = 0; e < NDK; ++e) {
         const uint8_t* qp = tQ + offK[e];
@@ -972,16 +1032,19 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     // dQ^T slice: rows d in [32 ds, 32 ds + 32), columns = queries of block dq_qb, K = 128 keys
     if (dq_wave && 32 * dq_qb < nq) {
       v16f acc = v16f{};
+      const int iq = 32 * dq_qb + 8 * ((n & 15) >> 2) + 4 * ((lane >> 4) & 1) + (n & 3);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint8_t* b0 = sdSK + 64 * 64 * ks + offQ;
+        const uint8_t* b0 = (EXACT ? sdSQ : sdSK) + 64 * 64 * ks + offQ;
         const v2i l0 = lds_tr8(b0), h0 = lds_tr8(b0 + 16 * 64), l1 = lds_tr8(b0 + 32 * 64), h1 = lds_tr8(b0 + 48 * 64);
         const v8i bq = v8i{l0[0], l0[1], h0[0], h0[1], l1[0], l1[1], h1[0], h1[1]};
         const v8i kt = cat8(tr_code16<D>(sK, 64 * ks, 32 * dq_ds + colg, lane),
                             tr_code16<D>(sK, 64 * ks + 32, 32 * dq_ds + colg, lane));
-        acc = mfma_f8(kt, bq, acc, sKeB[2 * ks + hh], sEds[dq_qb][2 * ks + hh] + E8M0_BIAS);
+        if constexpr (EXACT)
+          acc = mfma_f8(kt, bq, acc, E8M0_BIAS, sRowE[2 * ks + hh][iq]);
+        else
+          acc = mfma_f8(kt, bq, acc, sKeB[2 * ks + hh], sEds[dq_qb][2 * ks + hh] + E8M0_BIAS);
       }
-      const int iq = 32 * dq_qb + 8 * ((n & 15) >> 2) + 4 * ((lane >> 4) & 1) + (n & 3);
       const int sig = psig[iq];
       uint16_t* dst = reinterpret_cast<uint16_t*>(sKQ) + stage_row(iq) * DQS + 32 * dq_ds + 4 * hh;
 #pragma unroll
@@ -1102,7 +1165,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
             in.kofs, in.il8, in.delta, in.dq_sigma, in.qexps, in.do_codes,
             static_cast<const uint16_t*>(in.g), static_cast<uint16_t*>(in.dq_acc), in.dk_f32,
             static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv), in.dv_f32, in.gsplit,
-            static_cast<uint16_t*>(in.dq_part), in.det_base, in.det_cap, static_cast<const uint16_t*>(in.q_x),
+            static_cast<uint16_t*>(in.dq_part), in.det_base, in.det_cap, in.v_ref_exp, static_cast<const uint16_t*>(in.q_x),
             static_cast<const uint16_t*>(in.k_x), in.qk_scale};
   dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.Hk * (unsigned)in.gsplit);   // the mixed path has Hk = H, gsplit = 1
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };
@@ -1111,16 +1174,20 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
     if (p.deterministic) {
-      if (p.Hk != p.H) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, true, true>); else go8(attn_bwd8_kernel<128, true, true>);
+      if (p.exact) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, true, false, true>); else go8(attn_bwd8_kernel<128, true, false, true>);
+      } else if (p.Hk != p.H) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, true, true, false>); else go8(attn_bwd8_kernel<128, true, true, false>);
       } else {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, true, false>); else go8(attn_bwd8_kernel<128, true, false>);
+        if (p.D == 64) go8(attn_bwd8_kernel<64, true, false, false>); else go8(attn_bwd8_kernel<128, true, false, false>);
       }
     } else {
-      if (p.Hk != p.H) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, false, true>); else go8(attn_bwd8_kernel<128, false, true>);
+      if (p.exact) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, true>); else go8(attn_bwd8_kernel<128, false, false, true>);
+      } else if (p.Hk != p.H) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, false, true, false>); else go8(attn_bwd8_kernel<128, false, true, false>);
       } else {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, false, false>); else go8(attn_bwd8_kernel<128, false, false>);
+        if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, false>); else go8(attn_bwd8_kernel<128, false, false, false>);
       }
     }
   }

@@ -29,6 +29,10 @@
 //     the token-major tile with the LDS transpose read, so the one E4M3
 //     payload serves both orientations ([Summary, §3.1 Token-Block Scaling]).
 // Epilogue: O = O_acc / l to bf16, integer row max and fp32 l stored.
+// Exact option (EXACT): V's codes are per token, and every key block folds
+// its keys' exponents into P against a reference -- the query's v_ref_exp on
+// its own block, the block's largest exponent on earlier blocks -- which is
+// the P operand's scale of that block.
 #include "flamia_device.hpp"
 #include "flamia_internal.hpp"
 
@@ -51,7 +55,7 @@ struct FwdArgs {
 // PATH 0: MXFP8 scores.  PATH 1 (mixed): scores from NVFP4 Q and K, expanded
 // exactly to bf16 (code x group scale) and multiplied on bf16 matrix cores,
 // then scaled by t_Q t_K; the rest of the kernel is shared.
-template <int D, int PATH>
+template <int D, int PATH, bool EXACT>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D + 16;          // token-major row stride (bytes)
@@ -63,6 +67,7 @@ attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][FWD_BK * KS];
   __shared__ __attribute__((aligned(16))) uint8_t sVk[2][FWD_BK * KS];
   __shared__ uint8_t sKe[2][FWD_BK], sVe[2][FWD_BK], sVke[2][FWD_BK];
+  __shared__ uint8_t sVr[2][2];      // exact option: fold reference (block max) of each key block
 
   const Problem& p = a.p;
   const int H = p.H, T = p.T;
@@ -135,7 +140,7 @@ attn_fwd_kernel(FwdArgs a) {
   // ---- register prefetch of one key tile
   v4i pk[NCH], pv[NCH], pvk[NCH];
   uint32_t psf = 0;           // mixed path: group scales of the prefetched NVFP4 chunk
-  uint8_t pke = 0, pve = 0, pvke = 0;
+  uint8_t pke = 0, pve = 0, pvke = 0, pvr = 0;
   const uint8_t* k4doc = PATH ? a.f4.k_fp4 + ((size_t)s_d * rsk + (size_t)hk * D) / 2 : nullptr;
   const uint8_t* ksfdoc = PATH ? a.f4.k_sf + ((size_t)s_d * rsk + (size_t)hk * D) / 16 : nullptr;
   auto prefetch = [&](int kt) {
@@ -162,6 +167,10 @@ attn_fwd_kernel(FwdArgs a) {
         psf = ok ? *reinterpret_cast<const uint16_t*>(ksfdoc + (size_t)(j0 + r) * rsk / 16 + 2 * c4) : 0u;
       }
     }
+    // exact option: the largest per-key exponent of each key block is the
+    // in-block prefix maximum at its last token (only read for blocks that
+    // lie wholly before the query's own block)
+    if (EXACT && tid < 2) pvr = a.v_ref_exp[hTk + min(j0 + 32 * tid + 31, L - 1)];
     if (tid < FWD_BK) {
       const bool kv = tid < nvalid;
       pke = kv ? a.k_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
@@ -188,6 +197,7 @@ attn_fwd_kernel(FwdArgs a) {
           st16(dst + 16 * w, e2m1x8_times_bf16((uint32_t)pk[0][w], fp8_value((int)psf, w >> 1)));
       }
     }
+    if (EXACT && tid < 2) sVr[buf][tid] = pvr;
     if (tid < FWD_BK) {
       sKe[buf][tid] = pke;
       sVe[buf][tid] = pve;
@@ -266,7 +276,7 @@ attn_fwd_kernel(FwdArgs a) {
         int pc[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if (interior && !dia[kb]) {
+          if (!EXACT && interior && !dia[kb]) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               float pv4[4];
@@ -294,7 +304,11 @@ attn_fwd_kernel(FwdArgs a) {
                   pr = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kofs);
                 }
                 l_run += pr;
-                pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
+                if constexpr (EXACT)   // every block folds V's per-token exponent into P
+                  pv4[r] = __builtin_amdgcn_ldexpf(pr, ((int)sVe[buf][32 * kb + jj] - E8M0_BIAS) -
+                                                           (dia[kb] ? vref : (int)sVr[buf][kb] - E8M0_BIAS));
+                else
+                  pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
               }
               pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
             }
@@ -302,10 +316,12 @@ attn_fwd_kernel(FwdArgs a) {
         }
         const v8i pb = v8i{pc[0][0], pc[0][1], pc[0][2], pc[0][3], pc[1][0], pc[1][1], pc[1][2], pc[1][3]};
         // lane half hh supplies the scales of key block hh
-        const int sb = dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP;
-        const int sa = dia[hh] ? E8M0_BIAS : (int)sVe[buf][32 * hh];
-        const uint8_t* v0 = dia[0] ? sVk[buf] : sV[buf];
-        const uint8_t* v1 = dia[1] ? sVk[buf] : sV[buf];
+        const int sb = EXACT ? (dia[hh] ? E8M0_BIAS + vref + P_EXP : (int)sVr[buf][hh] + P_EXP)
+                             : (dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP);
+        const int sa = (EXACT || dia[hh]) ? E8M0_BIAS : (int)sVe[buf][32 * hh];
+        // exact option: V's codes are per token everywhere
+        const uint8_t* v0 = (!EXACT && dia[0]) ? sVk[buf] : sV[buf];
+        const uint8_t* v1 = (!EXACT && dia[1]) ? sVk[buf] : sV[buf];
         const int colg = 16 * ((lane >> 4) & 1);
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
@@ -356,9 +372,11 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
   dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(FWD_THREADS), 0, stream, a); };
   if (p.path == 1) {
-    if (p.D == 64) go(attn_fwd_kernel<64, 1>); else go(attn_fwd_kernel<128, 1>);
+    if (p.D == 64) go(attn_fwd_kernel<64, 1, false>); else go(attn_fwd_kernel<128, 1, false>);
+  } else if (p.exact) {
+    if (p.D == 64) go(attn_fwd_kernel<64, 0, true>); else go(attn_fwd_kernel<128, 0, true>);
   } else {
-    if (p.D == 64) go(attn_fwd_kernel<64, 0>); else go(attn_fwd_kernel<128, 0>);
+    if (p.D == 64) go(attn_fwd_kernel<64, 0, false>); else go(attn_fwd_kernel<128, 0, false>);
   }
   return hipGetLastError();
 }

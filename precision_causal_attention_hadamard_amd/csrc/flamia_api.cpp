@@ -33,7 +33,7 @@ flamia_status validate(const flamia_attn_desc* d) {
   if (d->total_tokens < 0 || d->num_docs < 1 || d->num_heads < 1) return FLAMIA_ERR_INVALID_ARG;
   if (d->max_doc_len < 0 || d->max_doc_len > d->total_tokens) return FLAMIA_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return FLAMIA_ERR_INVALID_ARG;
-  if ((d->hadamard | d->causal_dq_scale | d->deterministic | d->causal) & ~1) return FLAMIA_ERR_INVALID_ARG;
+  if ((d->hadamard | d->causal_dq_scale | d->deterministic | d->causal | d->exact) & ~1) return FLAMIA_ERR_INVALID_ARG;
   if (d->path != 0 && d->path != 1) return FLAMIA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
   if (d->num_kv_heads < 0 || d->num_kv_heads > d->num_heads ||
@@ -42,6 +42,9 @@ flamia_status validate(const flamia_attn_desc* d) {
   if (d->causal != 1) return FLAMIA_ERR_UNSUPPORTED;
   // grouped query attention is built for the MXFP8 path only
   if (d->path == 1 && d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads) return FLAMIA_ERR_UNSUPPORTED;
+  // the exact option is built for the MXFP8 path with one key/value head per query head
+  if (d->exact && (d->path != 0 || (d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads)))
+    return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
   // sort key, costs into 20 bits, grid x into 31 bits
   if (d->num_docs >= (1 << 24) || d->total_tokens >= (1 << 24)) return FLAMIA_ERR_WORKSPACE;
@@ -85,7 +88,7 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
 }
 
 struct QLayout {
-  size_t codes[4], exps[5], plan, fp4[2], sf[2], qk_scale, fx[2], bytes;
+  size_t codes[4], exps[5], plan, fp4[2], sf[2], qk_scale, fx[2], k_ref, bytes;
 };
 
 QLayout q_layout(const flamia_attn_desc* d) {
@@ -99,6 +102,8 @@ QLayout q_layout(const flamia_attn_desc* d) {
   for (int i = 0; i < 5; ++i) { q.exps[i] = off; off = align_up(off + (i == 0 ? M : Mk)); }
   q.plan = off;
   off = align_up(off + plan_layout(d).bytes);
+  q.k_ref = 0;
+  if (d->exact) { q.k_ref = off; off = align_up(off + Mk); }
   q.fp4[0] = q.fp4[1] = q.sf[0] = q.sf[1] = q.qk_scale = q.fx[0] = q.fx[1] = 0;
   if (d->path == 1) {
     for (int i = 0; i < 2; ++i) { q.fp4[i] = off; off = align_up(off + E / 2); }
@@ -147,6 +152,9 @@ Problem problem(const flamia_attn_desc* d) {
   p.causal_dq_scale = d->causal_dq_scale;
   p.path = d->path;
   p.deterministic = d->deterministic;
+  p.exact = d->exact;
+  // the exact option carries its own (per-token) causal dQ prescale
+  if (p.exact) p.causal_dq_scale = 1;
   p.softmax_scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
   p.c_log2 = (float)((double)p.softmax_scale * 1.4426950408889634);
   return p;
@@ -154,7 +162,7 @@ Problem problem(const flamia_attn_desc* d) {
 
 bool qt_complete(const flamia_attn_desc* d, const flamia_qtensors* q) {
   if (!(q && q->q_codes && q->k_codes && q->v_codes && q->v_key_codes && q->q_exp && q->k_exp &&
-        q->v_exp && q->v_key_exp && q->v_ref_exp && q->plan))
+        q->v_exp && q->v_key_exp && q->v_ref_exp && q->plan && (!d->exact || q->k_ref_exp)))
     return false;
   return d->path != 1 ||
          (q->q_fp4 && q->k_fp4 && q->q_sf && q->k_sf && q->qk_tensor_scale && q->q_fp4_bf16 && q->k_fp4_bf16);
@@ -205,6 +213,7 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base, f
   out->qk_tensor_scale = mixed ? reinterpret_cast<float*>(b + q.qk_scale) : nullptr;
   out->q_fp4_bf16 = mixed ? b + q.fx[0] : nullptr;
   out->k_fp4_bf16 = mixed ? b + q.fx[1] : nullptr;
+  out->k_ref_exp = desc->exact ? b + q.k_ref : nullptr;
   return FLAMIA_OK;
 }
 
@@ -223,7 +232,7 @@ flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const
   }
   return hip_status(launch_quant_qkv(p, q, k, v, out->q_codes, out->k_codes, out->v_codes, out->v_key_codes,
                                      out->q_exp, out->k_exp, out->v_exp, out->v_key_exp, out->v_ref_exp,
-                                     fp4_operands(out), stream));
+                                     out->k_ref_exp, fp4_operands(out), stream));
 }
 
 flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
@@ -249,7 +258,7 @@ flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qt
   const BwdLayout b = bwd_layout(desc);
   uint8_t* w = static_cast<uint8_t*>(ws);
   return hip_status(launch_quant_do(p, dout, o, row_max, row_sum, qt->q_exp, qt->k_exp, qt->v_exp,
-                                    qt->v_ref_exp, w + b.do_codes, w + b.do_exp, reinterpret_cast<int*>(w + b.kofs),
+                                    qt->v_ref_exp, qt->k_ref_exp, w + b.do_codes, w + b.do_exp, reinterpret_cast<int*>(w + b.kofs),
                                     reinterpret_cast<float*>(w + b.delta),
                                     reinterpret_cast<float*>(w + b.il8), reinterpret_cast<int*>(w + b.qexps),
                                     w + b.g, reinterpret_cast<int*>(w + b.dq_sigma), w + b.dq_acc, stream));
@@ -289,6 +298,7 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   in.dq_part = w + b.dq_part;
   in.det_base = reinterpret_cast<const int*>(static_cast<const uint8_t*>(qt->plan) + pl.det_offset);
   in.det_cap = pl.det_cap;
+  in.v_ref_exp = qt->v_ref_exp;
   in.q_x = qt->q_fp4_bf16;
   in.k_x = qt->k_fp4_bf16;
   in.qk_scale = qt->qk_tensor_scale;

@@ -34,6 +34,7 @@ struct Problem {
   int Hk;                  // key/value heads (= H, or a divisor of H: grouped query attention)
   int hadamard, causal_dq_scale, path;
   int deterministic;       // dQ from per-step partials added in a fixed order
+  int exact;               // the exact option: per-token scales, all-tile V fold, two dS payloads
   float softmax_scale;     // fp32 softmax scale
   float c_log2;            // fp32(softmax_scale * log2(e))
 };
@@ -60,11 +61,12 @@ hipError_t launch_amax_qk(const Problem& p, const void* q, const void* k, float*
 hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, const void* v,
                             uint8_t* q_codes, uint8_t* k_codes, uint8_t* v_codes, uint8_t* v_key_codes,
                             uint8_t* q_exp, uint8_t* k_exp, uint8_t* v_exp, uint8_t* v_key_exp,
-                            uint8_t* v_ref_exp, const Fp4Operands& f4, hipStream_t stream);
+                            uint8_t* v_ref_exp, uint8_t* k_ref_exp, const Fp4Operands& f4, hipStream_t stream);
 
 hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const int* row_max,
                            const float* row_sum, const uint8_t* q_exp, const uint8_t* k_exp,
-                           const uint8_t* v_exp, const uint8_t* v_ref_exp, uint8_t* do_codes,
+                           const uint8_t* v_exp, const uint8_t* v_ref_exp, const uint8_t* k_ref_exp,
+                           uint8_t* do_codes,
                            uint8_t* do_exp, int* kofs, float* delta,
                            float* il8, int* qexps, void* g, int* dq_sigma, void* dq_acc, hipStream_t stream);
 
@@ -95,6 +97,7 @@ struct BwdInputs {
   void* dq_part;           // deterministic mode: fp16 dQ partial slots
   const int* det_base;     // deterministic mode: first step of each document (plan)
   int det_cap;             // deterministic mode: steps per head in dq_part
+  const uint8_t* v_ref_exp;   // exact option: V's in-block prefix maximum
   const void *q_x, *k_x;   // mixed path only
   const float* qk_scale;   // mixed path only
 };

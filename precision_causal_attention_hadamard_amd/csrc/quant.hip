@@ -12,6 +12,9 @@
 // codes and the per-query fold reference (prefix max of the per-key
 // exponents inside the block).  [Summary, §3.1 Token-Block Scaling; §3.2
 // Causally Safe Scales; §4.3 Ablation Study]; [Reading, 4.4] first bullet.
+// Exact option: one exponent per token instead of per block (V's block and
+// per-key codes then coincide), and K's in-block prefix maximum of the
+// per-token exponents for the causal dQ prescale.
 //
 // quant_do_kernel: the backward's preparation, per block and head: token-block
 // codes of dO, D_i = sum_d dO~_id O_id from the same codes ([Summary, §3.3]:
@@ -216,7 +219,8 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes,
                  uint8_t* __restrict__ v_key_codes, uint8_t* __restrict__ q_exp,
                  uint8_t* __restrict__ k_exp, uint8_t* __restrict__ v_exp,
-                 uint8_t* __restrict__ v_key_exp, uint8_t* __restrict__ v_ref_exp, Fp4Operands f4) {
+                 uint8_t* __restrict__ v_key_exp, uint8_t* __restrict__ v_ref_exp,
+                 uint8_t* __restrict__ k_ref_exp, Fp4Operands f4) {
   const int tensor = blockIdx.y;
   const bool nvfp4 = p.path == 1 && tensor < 2;
   float t = 1.f;
@@ -243,13 +247,24 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
       load_half_row<D>(src + off, valid, x);
       if (rotate) fwht_half_row<D>(x, hf);
       const float lane_amax = half_row_amax<D>(x);
-      const int e = roundup_exp(wave_max(lane_amax));
+      // exact option: one exponent per token (the row's two lane halves)
+      const int e = roundup_exp(p.exact ? fmaxf(lane_amax, __shfl_xor(lane_amax, 1, 64)) : wave_max(lane_amax));
       if (valid) {
         store_codes<D>(codes + off, x, e);
         if (hf == 0) exps[(size_t)h * T + tok] = (uint8_t)(e + E8M0_BIAS);
         if (nvfp4)
           store_nvfp4<D>((tensor == 0 ? f4.q_fp4 : f4.k_fp4) + off / 2,
                          (tensor == 0 ? f4.q_sf : f4.k_sf) + off / 16, (tensor == 0 ? f4.q_x : f4.k_x) + off, x, t);
+      }
+      if (tensor == 1 && p.exact) {
+        // prefix max of the per-token K exponents over rows 0..row of the block
+        int ref = valid ? e : -127;
+#pragma unroll
+        for (int o = 2; o < 64; o <<= 1) {
+          int up = __shfl_up(ref, o, 64);
+          if (lane >= o) ref = max(ref, up);
+        }
+        if (valid && hf == 0) k_ref_exp[(size_t)h * T + tok] = (uint8_t)(ref + E8M0_BIAS);
       }
       if (tensor == 2) {
         const float row_amax = fmaxf(lane_amax, __shfl_xor(lane_amax, 1, 64));
@@ -279,7 +294,8 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
                 const int* __restrict__ row_max, const float* __restrict__ row_sum,
                 const uint8_t* __restrict__ q_exp,
                 const uint8_t* __restrict__ k_exp, const uint8_t* __restrict__ v_exp,
-                const uint8_t* __restrict__ v_ref_exp, uint8_t* __restrict__ do_codes,
+                const uint8_t* __restrict__ v_ref_exp, const uint8_t* __restrict__ k_ref_exp,
+                uint8_t* __restrict__ do_codes,
                 uint8_t* __restrict__ do_exp, int* __restrict__ kofs, float* __restrict__ delta,
                 float* __restrict__ il8,
                 int* __restrict__ qexps, uint16_t* __restrict__ g, int* __restrict__ dq_sigma,
@@ -301,12 +317,27 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
       const size_t off = ((size_t)tok * H + h) * D + hf * (D / 2);
       float x[D / 2];
       load_half_row<D>(dout + off, valid, x);
-      const int e = roundup_exp(wave_max(half_row_amax<D>(x)));
+      const float lane_amax = half_row_amax<D>(x);
+      const int e = roundup_exp(p.exact ? fmaxf(lane_amax, __shfl_xor(lane_amax, 1, 64)) : wave_max(lane_amax));
       // largest K and V block exponents over the visible key blocks (of the
       // key/value head this query head reads)
       const size_t hkT = (size_t)(h / (H / p.Hk)) * T;
       int emax_kv = -254;
-      {
+      if (p.exact) {
+        // per token: the largest K and V exponents over positions j <= tok of the
+        // document -- earlier blocks through their last token's in-block prefix
+        // maximum, this block through the prefix at tok itself
+        int ek = -127, ev = -127;
+        for (int J = lane; J < blk; J += 64) {
+          const size_t t1 = hkT + ds + J * TOKEN_BLOCK + TOKEN_BLOCK - 1;
+          ek = max(ek, (int)k_ref_exp[t1] - E8M0_BIAS);
+          ev = max(ev, (int)v_ref_exp[t1] - E8M0_BIAS);
+        }
+        ek = wave_max_i(ek);
+        ev = wave_max_i(ev);
+        const size_t tt = hkT + min(tok, be - 1);
+        emax_kv = max(ek, (int)k_ref_exp[tt] - E8M0_BIAS) + max(ev, (int)v_ref_exp[tt] - E8M0_BIAS);
+      } else {
         int ek = -127, ev = -127;
         for (int J = lane; J < nvis; J += 64) {
           const size_t t0 = hkT + ds + J * TOKEN_BLOCK;
@@ -369,13 +400,13 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
 hipError_t launch_quant_qkv(const Problem& p, const void* q, const void* k, const void* v,
                             uint8_t* q_codes, uint8_t* k_codes, uint8_t* v_codes, uint8_t* v_key_codes,
                             uint8_t* q_exp, uint8_t* k_exp, uint8_t* v_exp, uint8_t* v_key_exp,
-                            uint8_t* v_ref_exp, const Fp4Operands& f4, hipStream_t stream) {
+                            uint8_t* v_ref_exp, uint8_t* k_ref_exp, const Fp4Operands& f4, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK, 3);
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, q_codes, k_codes, v_codes, v_key_codes,
-                       q_exp, k_exp, v_exp, v_key_exp, v_ref_exp, f4);
+                       q_exp, k_exp, v_exp, v_key_exp, v_ref_exp, k_ref_exp, f4);
   };
   if (p.D == 64) args(quant_qkv_kernel<64>); else args(quant_qkv_kernel<128>);
   return hipGetLastError();
@@ -395,14 +426,15 @@ hipError_t launch_amax_qk(const Problem& p, const void* q, const void* k, float*
 
 hipError_t launch_quant_do(const Problem& p, const void* dout, const void* o, const int* row_max,
                            const float* row_sum, const uint8_t* q_exp, const uint8_t* k_exp,
-                           const uint8_t* v_exp, const uint8_t* v_ref_exp, uint8_t* do_codes,
+                           const uint8_t* v_exp, const uint8_t* v_ref_exp, const uint8_t* k_ref_exp,
+                           uint8_t* do_codes,
                            uint8_t* do_exp, int* kofs, float* delta,
                            float* il8, int* qexps, void* g, int* dq_sigma, void* dq_acc, hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((p.T + TOKEN_BLOCK - 1) / TOKEN_BLOCK);
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(QUANT_THREADS), 0, stream, p, (const uint16_t*)dout,
-                       (const uint16_t*)o, row_max, row_sum, q_exp, k_exp, v_exp, v_ref_exp, do_codes,
+                       (const uint16_t*)o, row_max, row_sum, q_exp, k_exp, v_exp, v_ref_exp, k_ref_exp, do_codes,
                        do_exp, kofs, delta, il8, qexps, (uint16_t*)g, dq_sigma, (uint16_t*)dq_acc);
   };
   if (p.D == 64) args(quant_do_kernel<64>); else args(quant_do_kernel<128>);

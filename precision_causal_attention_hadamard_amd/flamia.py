@@ -34,14 +34,14 @@ class AttnDesc(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("hadamard", ctypes.c_int32), ("causal_dq_scale", ctypes.c_int32),
                 ("deterministic", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("num_kv_heads", ctypes.c_int32)]
+                ("num_kv_heads", ctypes.c_int32), ("exact", ctypes.c_int32)]
 
 
 class QTensors(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("q_codes", "k_codes", "v_codes", "v_key_codes", "q_exp", "k_exp", "v_exp",
                  "v_key_exp", "v_ref_exp", "plan", "q_fp4", "k_fp4", "q_sf", "k_sf",
-                 "qk_tensor_scale", "q_fp4_bf16", "k_fp4_bf16")]
+                 "qk_tensor_scale", "q_fp4_bf16", "k_fp4_bf16", "k_ref_exp")]
 
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_quantize", "flamia_attn_fwd",
@@ -100,11 +100,11 @@ def _stream(stream=None):
 def make_desc(cu_seqlens_dev: torch.Tensor, total_tokens: int, num_docs: int, max_doc_len: int,
               num_heads: int, head_dim: int, hadamard: bool = False, causal_dq_scale: bool = False,
               softmax_scale: float = 0.0, path: int = 0, causal: int = 1, deterministic: int = 0,
-              num_kv_heads: int = 0) -> AttnDesc:
+              num_kv_heads: int = 0, exact: int = 0) -> AttnDesc:
     return AttnDesc(total_tokens, num_docs, max_doc_len,
                     cu_seqlens_dev.data_ptr() if cu_seqlens_dev is not None else None,
                     num_heads, head_dim, causal, path, int(hadamard), int(causal_dq_scale),
-                    deterministic, softmax_scale, num_kv_heads)
+                    deterministic, softmax_scale, num_kv_heads, exact)
 
 
 def buffer_sizes(desc: AttnDesc):
@@ -178,7 +178,7 @@ class TrainingCall:
     attention when Hk < H); ``cu_seqlens`` a list of ints."""
 
     def __init__(self, q, k, v, do, cu_seqlens, hadamard=False, causal_dq_scale=False,
-                 softmax_scale=0.0, path=0, deterministic=False):
+                 softmax_scale=0.0, path=0, deterministic=False, exact=False):
         dev = q.device
         self.q, self.k, self.v, self.do = q, k, v, do
         T, H, d = q.shape
@@ -188,7 +188,7 @@ class TrainingCall:
         lens = [b - a for a, b in zip(self.cu_list, self.cu_list[1:])]
         self.desc = make_desc(self.cu, T, len(lens), max(lens) if lens else 0, H, d, hadamard,
                               causal_dq_scale, softmax_scale, path, deterministic=int(deterministic),
-                              num_kv_heads=Hk)
+                              num_kv_heads=Hk, exact=int(exact))
         qb, fb, bb = buffer_sizes(self.desc)
         self.qbuf = torch.empty(qb, dtype=torch.uint8, device=dev)
         self.qt = qtensors_layout(self.desc, self.qbuf)

@@ -156,8 +156,17 @@ def test_layout_alignment_and_carving(lib):
     d1 = base_desc(path=1)
     qt1 = flamia.QTensors()
     assert lib.flamia_qtensors_layout(ctypes.byref(d1), ctypes.c_void_p(0x100000), ctypes.byref(qt1)) == 0
-    ptrs1 = [getattr(qt1, f) for f, _ in flamia.QTensors._fields_]
-    assert all(ptrs1) and len(set(ptrs1)) == len(ptrs1)
+    ptrs1 = [getattr(qt1, f) for f, _ in flamia.QTensors._fields_ if f != "k_ref_exp"]
+    assert all(ptrs1) and len(set(ptrs1)) == len(ptrs1) and not qt1.k_ref_exp
+    # the exact option adds K's in-block prefix maximum, [H, T] bytes
+    de = base_desc(exact=1)
+    qte = flamia.QTensors()
+    assert lib.flamia_qtensors_layout(ctypes.byref(de), ctypes.c_void_p(0x100000), ctypes.byref(qte)) == 0
+    assert qte.k_ref_exp and qte.k_ref_exp % 256 == 0 and qte.k_ref_exp not in ptrs
+    assert sizes_status(lib, de)[1] >= sizes_status(lib, d)[1] + 256 * 2
+    assert sizes_status(lib, base_desc(exact=1, path=1))[0] == 2
+    assert sizes_status(lib, base_desc(exact=1, num_heads=4, num_kv_heads=2))[0] == 2
+    assert sizes_status(lib, base_desc(exact=2))[0] == 1
     assert sizes_status(lib, d1)[1] >= sizes_status(lib, d)[1] + 256 * 2 * 64 * (2 * 0.5 + 2 / 16)
 
 
