@@ -568,6 +568,46 @@ __device__ __forceinline__ int dsk_off(int r, int chunk) {
   return r * 64 + ((chunk ^ key) << 4);
 }
 
+// Largest value over the 32 lanes of the calling lane's wave half: four DPP
+// rotations inside each 16-lane row, then one swizzle that pairs lane l with
+// lane l ^ 16.
+// Reduce-scatter of 16 registers over the 32 lanes of a wave half: lane n of
+// the half returns the largest value of register (n >> 1) over the half.
+// Each level pairs two registers, keeps one in the lanes whose bit is clear
+// and the other where it is set, and takes the maximum with the partner lane
+// across that bit (bits 4, 3, 2, 1 by swizzle or DPP), then bit 0 finishes.
+template <int PAT>
+__device__ __forceinline__ float swizzle_f(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), PAT));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float rows_max16(const float (&v)[16], int n) {
+  const bool b4 = n & 16, b3 = n & 8, b2 = n & 4, b1 = n & 2;
+  float w[8], x[4], y[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    w[k] = fmaxf(b4 ? v[k + 8] : v[k], swizzle_f<0x401f>(b4 ? v[k] : v[k + 8]));    // xor 16
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    x[k] = fmaxf(b3 ? w[k + 4] : w[k], dpp_f<0x128>(b3 ? w[k] : w[k + 4]));         // xor 8 (row_ror:8)
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    y[k] = fmaxf(b2 ? x[k + 2] : x[k], swizzle_f<0x101f>(b2 ? x[k] : x[k + 2]));    // xor 4
+  const float z = fmaxf(b1 ? y[1] : y[0], dpp_f<0x4e>(b1 ? y[0] : y[1]));            // xor 2 (quad_perm)
+  return fmaxf(z, dpp_f<0xb1>(z));                                                  // xor 1 (quad_perm)
+}
+
+__device__ __forceinline__ float half_max32(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x128, 0xf, 0xf, false)));  // row_ror:8
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x124, 0xf, 0xf, false)));  // row_ror:4
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x122, 0xf, 0xf, false)));  // row_ror:2
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x121, 0xf, 0xf, false)));  // row_ror:1
+  return fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x401f)));               // xor 16
+}
+
 // ---------------------------------------------------------------------------
 // Eight-wave backward (MXFP8 path): two waves per SIMD on the same item.
 // Wave w owns key block kb = w & 3 and, of each 64-query tile, query block
@@ -623,7 +663,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   // block, query), the dK payload's exponents per (query half, key), and each
   // key block's largest V exponent
   __shared__ __attribute__((aligned(1024))) uint8_t sdSQ[EXACT ? BWD_BK * BWD_BQ : 16];
-  __shared__ uint8_t sRowE[EXACT ? 4 : 1][BWD_BQ];
+  __shared__ __attribute__((aligned(16))) uint8_t sRowE[EXACT ? 4 : 1][BWD_BQ];
   __shared__ uint8_t sColE[EXACT ? 2 : 1][BWD_BK];
   __shared__ int sVrB[4];
 
@@ -831,7 +871,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const int QB = 2 * qt + qh;
     const bool act = kb_active && QB >= KB && 32 * qh < nq;
     const bool dia = QB == KB;
-    const bool fast = !EXACT && !dia && 32 * qh + 32 <= nq;   // no mask, no fold
+    const bool fast = !dia && 32 * qh + 32 <= nq;   // no mask (and, but for the exact option, no fold)
     int dsc[4] = {0, 0, 0, 0};
     int eds = -127;
     v16f sacc, pacc;     // set (and read) only when act
@@ -880,6 +920,10 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       uint32_t pe[8];      // bf16 pairs of P^_eff * 2^8, accumulator register order
       float amax = 0.f;
       if (fast) {
+        // exact option: the lane's key folds against its block's largest V
+        // exponent; the fold is a constant per lane here
+        const int fd = EXACT ? e_key - (sVrB[kb] - E8M0_BIAS) : 0;
+        const float ufd = __builtin_amdgcn_ldexpf(1.0f, -fd);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = 32 * qh + 8 * g + 4 * hh;
@@ -895,9 +939,11 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
             dsv[rr] = (pf[r] * ilv[r]) * pacc[rr];
             amax = fmaxf(amax, fabsf(dsv[rr]));
           }
-          const int code = cvt_fp8x4(pf[0], pf[1], pf[2], pf[3]);
-          pe[2 * g] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false));
-          pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, true));
+          const int code = EXACT ? cvt_fp8x4(__builtin_amdgcn_ldexpf(pf[0], fd), __builtin_amdgcn_ldexpf(pf[1], fd),
+                                             __builtin_amdgcn_ldexpf(pf[2], fd), __builtin_amdgcn_ldexpf(pf[3], fd))
+                                 : cvt_fp8x4(pf[0], pf[1], pf[2], pf[3]);
+          pe[2 * g] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, EXACT ? ufd : 1.0f, false));
+          pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, EXACT ? ufd : 1.0f, true));
         }
       } else {
 #pragma unroll
@@ -937,39 +983,44 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         // exponent per query row over this block's 32 keys (the lanes of a half)
         const int ekf = ke - E8M0_BIAS;
         int dqc[4];
+        {
+          float av[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float xq[4];
+          for (int rr = 0; rr < 16; ++rr) av[rr] = fabsf(__builtin_amdgcn_ldexpf(dsv[rr], ekf));
+          // each row's maximum lands in lanes 2 r, 2 r + 1 of the half; its
+          // exponent goes to the table the dQ product reads, and every lane
+          // reads back the exponents of its 16 rows (four bytes per dword)
+          const int rw = n >> 1;
+          const int er = roundup_exp(rows_max16(av, n));
+          if (!(n & 1)) sRowE[kb][32 * qh + 8 * (rw >> 2) + 4 * hh + (rw & 3)] = (uint8_t)(er + E8M0_BIAS);
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int rr = 4 * g + r;
-            float m = fabsf(__builtin_amdgcn_ldexpf(dsv[rr], ekf));
+          for (int g = 0; g < 4; ++g) {
+            const int e4 = *reinterpret_cast<const int*>(&sRowE[kb][32 * qh + 8 * g + 4 * hh]);
+            float xq[4];
 #pragma unroll
-            for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-            const int er = roundup_exp(m);
-            if (n == rr) sRowE[kb][32 * qh + 8 * (rr >> 2) + 4 * hh + (rr & 3)] = (uint8_t)(er + E8M0_BIAS);
-            xq[r] = __builtin_amdgcn_ldexpf(dsv[rr], ekf - er);
+            for (int r = 0; r < 4; ++r)
+              xq[r] = __builtin_amdgcn_ldexpf(dsv[4 * g + r], ekf - (((e4 >> (8 * r)) & 255) - E8M0_BIAS));
+            dqc[g] = cvt_fp8x4(xq[0], xq[1], xq[2], xq[3]);
           }
-          dqc[g] = cvt_fp8x4(xq[0], xq[1], xq[2], xq[3]);
         }
         st16(sdSQ + dsk_off(32 * kb + n, 2 * hh + qh), v4i{dqc[0], dqc[1], dqc[2], dqc[3]});
         // dK payload: Q's per-token exponent of each row folded in, one exponent
         // per key (lane) over the wave's 32 queries (both halves)
+        auto eq = [&](int rr) { return (pqx[32 * qh + 8 * (rr >> 2) + 4 * hh + (rr & 3)] & 255) - E8M0_BIAS; };
         float mk = 0.f;
-        float xk[16];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int eqf = (pqx[32 * qh + 8 * (rr >> 2) + 4 * hh + (rr & 3)] & 255) - E8M0_BIAS;
-          xk[rr] = __builtin_amdgcn_ldexpf(dsv[rr], eqf);
-          mk = fmaxf(mk, fabsf(xk[rr]));
-        }
+        for (int rr = 0; rr < 16; ++rr) mk = fmaxf(mk, fabsf(__builtin_amdgcn_ldexpf(dsv[rr], eq(rr))));
         mk = fmaxf(mk, __shfl_xor(mk, 32, 64));
         const int ec = roundup_exp(mk);
         if (hh == 0) sColE[qh][32 * kb + n] = (uint8_t)(ec + E8M0_BIAS);
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          dsc[g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(xk[4 * g], -ec), __builtin_amdgcn_ldexpf(xk[4 * g + 1], -ec),
-                             __builtin_amdgcn_ldexpf(xk[4 * g + 2], -ec), __builtin_amdgcn_ldexpf(xk[4 * g + 3], -ec));
+          dsc[g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(dsv[4 * g], eq(4 * g) - ec),
+                             __builtin_amdgcn_ldexpf(dsv[4 * g + 1], eq(4 * g + 1) - ec),
+                             __builtin_amdgcn_ldexpf(dsv[4 * g + 2], eq(4 * g + 2) - ec),
+                             __builtin_amdgcn_ldexpf(dsv[4 * g + 3], eq(4 * g + 3) - ec));
       } else {
       // amax >= 0, so its bits order like the values
       const int e = roundup_exp(__int_as_float(wave_max_i(__float_as_int(amax))));

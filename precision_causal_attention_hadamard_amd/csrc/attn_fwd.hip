@@ -66,7 +66,9 @@ attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][FWD_BK * (PATH ? KSB : KS)];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][FWD_BK * KS];
   __shared__ __attribute__((aligned(16))) uint8_t sVk[2][FWD_BK * KS];
-  __shared__ uint8_t sKe[2][FWD_BK], sVe[2][FWD_BK], sVke[2][FWD_BK];
+  __shared__ __attribute__((aligned(16))) uint8_t sKe[2][FWD_BK];
+  __shared__ __attribute__((aligned(16))) uint8_t sVe[2][FWD_BK];    // read four bytes at a time (exact option)
+  __shared__ __attribute__((aligned(16))) uint8_t sVke[2][FWD_BK];
   __shared__ uint8_t sVr[2][2];      // exact option: fold reference (block max) of each key block
 
   const Problem& p = a.p;
@@ -276,16 +278,23 @@ attn_fwd_kernel(FwdArgs a) {
         int pc[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if (!EXACT && interior && !dia[kb]) {
+          if (interior && !dia[kb]) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+              // exact option: the fold of keys 8g + 4hh + r against the block's
+              // reference joins the power of two of P (four exponent bytes at once)
+              int fold4 = 0;
+              if constexpr (EXACT) fold4 = *reinterpret_cast<const int*>(&sVe[buf][32 * kb + 8 * g + 4 * hh]);
+              const int fref = EXACT ? (int)sVr[buf][kb] : 0;
               float pv4[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float x = st[kb][4 * g + r] * c;
                 const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                pv4[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kofs);
-                l_run += pv4[r];
+                const int fe = cvt_floor_i32(x) + kofs;
+                l_run += __builtin_amdgcn_ldexpf(e2, fe);
+                pv4[r] = EXACT ? __builtin_amdgcn_ldexpf(e2, fe + (((fold4 >> (8 * r)) & 255) - fref))
+                               : __builtin_amdgcn_ldexpf(e2, fe);
               }
               pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
             }
