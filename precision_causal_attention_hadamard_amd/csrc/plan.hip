@@ -4,10 +4,13 @@
 // fixed-pass sort and hand items, costliest first, to the grid
 // ([Summary, §3.6.2 Load-Balanced Scheduling]; [Reading, 4.4] last bullet).
 // Here one workgroup per list enumerates every (document, tile), forms a 64-bit key
-//   (COST_MAX - cost) << 44 | doc << 20 | tile
+//   (COST_MAX - c) << 44 | doc << 20 | tile
 // and bitonic-sorts the keys (in LDS; within one wave for lists of at most
-// 64 tiles).  The key is unique, so the order is the
-// single correct one: cost descending, then document, then tile.  A tile
+// 64 tiles).  c is the tile's cost in the forward list and the cost of the
+// document's costliest (first) key tile in the backward list, which keeps a
+// document's key tiles together (longest document first, tiles in order, so
+// still costliest first inside it) for L2 reuse of its query rows.  The key
+// is unique, so the order is the single correct one.  A tile
 // later expands to num_heads consecutive grid items (head ascending).  The
 // attention kernels read item blockIdx.x / H of the sorted list; the
 // hardware dispatcher hands workgroups out in index order, which plays the
@@ -107,7 +110,10 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
       } else {
         cost = (L + bq - 1) / bq - (t * bk) / bq;
       }
-      keys[first + t] = ((unsigned long long)(COST_MAX - cost) << 44) |
+      // backward: a document's tiles share the key of its costliest (first)
+      // tile, so they stay together, longest document first, tiles in order
+      const int kcost = fwd ? cost : (L + bq - 1) / bq;
+      keys[first + t] = ((unsigned long long)(COST_MAX - kcost) << 44) |
                         ((unsigned long long)d << 20) | (unsigned long long)t;
     }
     n_tiles += total;

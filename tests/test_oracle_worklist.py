@@ -35,7 +35,18 @@ def test_worklist_is_sorted_permutation():
     assert len(keys) == len(items) == 3 * (1 + 3 + 0 + 10 + 1)
     b = worklist.bwd_items(cu, 3, 64, 128)
     assert len(b) == 3 * (1 + 3 + 0 + 10 + 1)
-    assert [it[3] for it in b] == sorted((it[3] for it in b), reverse=True)
+    assert len({(d, t, h) for d, t, h, _ in b}) == len(b)
+    # backward: documents by their costliest (first) tile, descending; inside a
+    # document tiles ascending, i.e. costs descending, heads innermost
+    docs = [d for d, _, _, _ in b]
+    firsts = {d: max(c for dd, _, _, c in b if dd == d) for d in set(docs)}
+    order = [d for i, d in enumerate(docs) if i == 0 or docs[i - 1] != d]
+    assert len(order) == len(set(order))                      # each document's items are contiguous
+    assert [firsts[d] for d in order] == sorted(firsts.values(), reverse=True)
+    for d in order:
+        mine = [(t, h, c) for dd, t, h, c in b if dd == d]
+        assert mine == sorted(mine, key=lambda x: (x[0], x[1]))
+        assert [c for _, _, c in mine] == sorted((c for _, _, c in mine), reverse=True)
 
 
 def test_skew_rule():
