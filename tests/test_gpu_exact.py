@@ -91,3 +91,30 @@ def test_exact_leak_probe_is_zero_on_the_gpu(gpu_lib, j0):
         assert torch.equal(a, b), (n, j0, float((a.float() - b.float()).abs().max()))
     assert torch.equal(base.o[130:], moved.o[130:])            # the other document
     assert not torch.equal(base.o[j0:130], moved.o[j0:130])     # the perturbation reached the call
+
+
+def test_exact_fullsize_sampled(gpu_lib):
+    """The 2 x 4096-token, 16-head, d = 128 outlier workload with the exact
+    option, whole call on the GPU; the oracle recomputes document 1, heads 0
+    and 9."""
+    wl = W.config(2)
+    print(f"[exact] fullsize {wl.name}: GPU call", flush=True)
+    call = run_gpu(gpu_lib, wl)
+    doc, heads = 1, [0, 9]
+    s, e = wl.cu_seqlens[doc], wl.cu_seqlens[doc + 1]
+    arrs = [t[s:e][:, heads].float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
+    num = A.Numerics(hadamard=wl.hadamard, exact=True)
+    print("[exact] fullsize: oracle slice", flush=True)
+    ref = A.training_call(*arrs, [0, e - s], num)
+    print("[exact] fullsize: decision bounds", flush=True)
+    al = DC.allowances(*arrs, [0, e - s], num)
+    hs = torch.tensor(heads)
+    for f in ("q_codes", "k_codes", "v_codes"):
+        np.testing.assert_array_equal(call.codes(f)[s:e].cpu()[:, hs].numpy(), ref[f], err_msg=f)
+    for f in ("q_exp", "k_exp", "v_exp", "v_ref_exp"):
+        np.testing.assert_array_equal(call.exps(f).cpu()[hs][:, s:e].numpy().astype(np.int64), ref[f] + 127,
+                                      err_msg=f)
+    outs = {n: getattr(call, n)[s:e].cpu()[:, hs].float().numpy() for n in ("o", "dq", "dk", "dv")}
+    DCMP.check_outputs(outs, ref, al, "exact fullsize", outliers=wl.has_outliers)
+    rm = call.row_max.cpu()[hs][:, s:e].numpy().astype(np.int64)
+    assert np.all(np.abs(rm - ref["row_max"]) <= 1) and (rm != ref["row_max"]).mean() <= 1e-3
