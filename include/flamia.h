@@ -91,7 +91,7 @@ typedef struct flamia_attn_desc {
                                    one exponent per (query, 32 keys), for dK with the query's Q
                                    exponent folded in, one exponent per (key, 32 queries) -- and a
                                    per-token causal dQ prescale.  No output depends on a later
-                                   position's inputs.  MXFP8 path with Hk = H only (else
+                                   position's inputs.  MXFP8 path only (path = 1:
                                    FLAMIA_ERR_UNSUPPORTED) */
 } flamia_attn_desc;
 

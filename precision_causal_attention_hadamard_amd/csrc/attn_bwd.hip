@@ -626,7 +626,7 @@ __device__ __forceinline__ float half_max32(float m) {
 // group is split over gsplit items, which store fp32 partials that a reduce
 // kernel adds in order and rounds once.  GRP = false is the one-head-per-item
 // instantiation (H = Hk): the loop runs the query tiles of one head only.
-// EXACT (exact option, with GRP = false): Q, K, V, dO scales are per token --
+// EXACT (exact option): Q, K, V, dO scales are per token --
 // the recomputed S and dP take each row's exponent as its operand scale; every
 // key block folds V's exponents into P for dV; dS is quantized twice, with
 // K's exponent folded in and one exponent per (query, 32 keys) for dQ, and
@@ -1225,7 +1225,9 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
     if (p.deterministic) {
-      if (p.exact) {
+      if (p.exact && p.Hk != p.H) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, true, true, true>); else go8(attn_bwd8_kernel<128, true, true, true>);
+      } else if (p.exact) {
         if (p.D == 64) go8(attn_bwd8_kernel<64, true, false, true>); else go8(attn_bwd8_kernel<128, true, false, true>);
       } else if (p.Hk != p.H) {
         if (p.D == 64) go8(attn_bwd8_kernel<64, true, true, false>); else go8(attn_bwd8_kernel<128, true, true, false>);
@@ -1233,7 +1235,9 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
         if (p.D == 64) go8(attn_bwd8_kernel<64, true, false, false>); else go8(attn_bwd8_kernel<128, true, false, false>);
       }
     } else {
-      if (p.exact) {
+      if (p.exact && p.Hk != p.H) {
+        if (p.D == 64) go8(attn_bwd8_kernel<64, false, true, true>); else go8(attn_bwd8_kernel<128, false, true, true>);
+      } else if (p.exact) {
         if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, true>); else go8(attn_bwd8_kernel<128, false, false, true>);
       } else if (p.Hk != p.H) {
         if (p.D == 64) go8(attn_bwd8_kernel<64, false, true, false>); else go8(attn_bwd8_kernel<128, false, true, false>);

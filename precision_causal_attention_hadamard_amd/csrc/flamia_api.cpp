@@ -42,9 +42,8 @@ flamia_status validate(const flamia_attn_desc* d) {
   if (d->causal != 1) return FLAMIA_ERR_UNSUPPORTED;
   // grouped query attention is built for the MXFP8 path only
   if (d->path == 1 && d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads) return FLAMIA_ERR_UNSUPPORTED;
-  // the exact option is built for the MXFP8 path with one key/value head per query head
-  if (d->exact && (d->path != 0 || (d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads)))
-    return FLAMIA_ERR_UNSUPPORTED;
+  // the exact option is built for the MXFP8 path
+  if (d->exact && d->path != 0) return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
   // sort key, costs into 20 bits, grid x into 31 bits
   if (d->num_docs >= (1 << 24) || d->total_tokens >= (1 << 24)) return FLAMIA_ERR_WORKSPACE;

@@ -165,7 +165,7 @@ def test_layout_alignment_and_carving(lib):
     assert qte.k_ref_exp and qte.k_ref_exp % 256 == 0 and qte.k_ref_exp not in ptrs
     assert sizes_status(lib, de)[1] >= sizes_status(lib, d)[1] + 256 * 2
     assert sizes_status(lib, base_desc(exact=1, path=1))[0] == 2
-    assert sizes_status(lib, base_desc(exact=1, num_heads=4, num_kv_heads=2))[0] == 2
+    assert sizes_status(lib, base_desc(exact=1, num_heads=4, num_kv_heads=2))[0] == 0
     assert sizes_status(lib, base_desc(exact=2))[0] == 1
     assert sizes_status(lib, d1)[1] >= sizes_status(lib, d)[1] + 256 * 2 * 64 * (2 * 0.5 + 2 / 16)
 

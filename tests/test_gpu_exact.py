@@ -42,6 +42,9 @@ CASES = {
     "ragged_d128_h2": lambda: W.small_packed(72, [129, 64, 31, 250], heads=2, head_dim=128),
     "hadamard_outliers_d128": lambda: W.small_packed(73, [300, 211], heads=2, head_dim=128,
                                                      outlier_scale=20.0, hadamard=True),
+    "gqa_h6_kv2_d128": lambda: W.small_packed(75, [129, 64, 31, 250], heads=6, head_dim=128, kv_heads=2),
+    "gqa_h4_kv1_d64": lambda: W.small_packed(76, [1, 17, 45, 100, 33, 64, 130, 2], heads=4, head_dim=64,
+                                             kv_heads=1),
 }
 
 
