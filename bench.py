@@ -10,7 +10,8 @@ document (forward 2 products, backward 5); quantization adds no FLOPs but
 its time is inside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
-                       [--kv-heads Hk] [--deterministic] [--no-cpu-baseline]
+                       [--kv-heads Hk] [--deterministic] [--exact] [--non-causal]
+                       [--no-cpu-baseline]
                        [--copy-calibration]
 """
 
@@ -123,7 +124,7 @@ def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str, kernel
     print(json.dumps(rec))
 
 
-def cpu_baseline(wl, cfg: int):
+def cpu_baseline(wl, cfg: int, causal: bool = True):
     """The oracle, as it stands, on document 0 and the first few heads of the
     workload, timed on the host cores."""
     import numpy as np
@@ -138,9 +139,10 @@ def cpu_baseline(wl, cfg: int):
             for t in (wl.q, wl.k, wl.v, wl.do)]
     L = e - s
     t0 = time.perf_counter()
-    A.training_call(*arrs, [0, L], A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8"))
+    A.training_call(*arrs, [0, L], A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8",
+                                              causal=causal))
     dt = time.perf_counter() - t0
-    flops = 14 * wl.head_dim * nh * L * (L + 1) // 2
+    flops = 14 * wl.head_dim * nh * (L * (L + 1) // 2 if causal else L * L)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"document 0 ({L} tokens), heads 0-{nh - 1} of the {wl.name} workload: "
@@ -159,6 +161,9 @@ def main():
                     help="grouped-query variant of the workload: K and V with this many heads (0: one per query head)")
     ap.add_argument("--exact", action="store_true",
                     help="the exact option: per-token scales, all-tile V fold, per-row/per-key dS exponents")
+    ap.add_argument("--non-causal", action="store_true",
+                    help="the call without the causal mask (every key of a document visible); "
+                         "FLOPs then count every (query, key) pair of a document")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true",
                     help="ordered dQ reduction (per-step partials, fixed-order fp16 sum) instead of atomics")
@@ -190,12 +195,17 @@ def main():
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
                                causal_dq_scale=wl.causal_dq_scale, path=wl.path,
-                               deterministic=args.deterministic, exact=args.exact)
+                               deterministic=args.deterministic, exact=args.exact,
+                               causal=not args.non_causal)
     T, H, d = call.shape
     Hk = call.kv_heads
     grouped = Hk != H
-    pairs = wl.causal_pairs()
-    flops = wl.flops()
+    if args.non_causal:
+        pairs = H * sum(L * L for L in wl.doc_lens)
+        flops = 14 * d * pairs
+    else:
+        pairs = wl.causal_pairs()
+        flops = wl.flops()
 
     def step(ev=None):
         if ev is not None: ev[0].record()
@@ -254,7 +264,8 @@ def main():
     else:
         achieved, unit = work / t_dom / 1e9, "GB/s"
     traffic = (measured_traffic(kname, f"config{args.config}")
-               if kname.startswith("attn_bwd") and not grouped and not args.exact else None)
+               if kname.startswith("attn_bwd") and not grouped and not args.exact and not args.non_causal
+               else None)
     roofline = {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic,
                 "peak_note": "dtype-weighted: FP8 products at 5000, bf16 products at 2500 TFLOP/s"
@@ -273,7 +284,7 @@ def main():
                    "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
                    "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
                    "deterministic": bool(args.deterministic), "exact": bool(args.exact),
-                   "causal_pairs": pairs, "flops_per_step": flops},
+                   "causal": not args.non_causal, "causal_pairs": pairs, "flops_per_step": flops},
         "pct_fp8_peak": 100.0 * value / FP8_PEAK_TFLOPS,
         "stage_ms": stage_ms, "event_ms_per_step": event_ms,
         # the attention kernels alone: forward, and backward without the dO
@@ -283,7 +294,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.config)
+        out["cpu_baseline"] = cpu_baseline(wl, args.config, causal=not args.non_causal)
     print(json.dumps(out), flush=True)
 
 

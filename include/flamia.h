@@ -4,7 +4,8 @@
  *
  * The call is three steps over packed variable-length documents:
  *   flamia_quantize   fused quantization of Q, K, V (+ the work list),
- *   flamia_attn_fwd   S = Q K^T, causal online softmax, O = P^ V,
+ *   flamia_attn_fwd   S = Q K^T, causal (or, with causal = 0, unmasked)
+ *                     online softmax, O = P^ V,
  *   flamia_attn_bwd   dO quantization + D, then dV, dP, dS, dQ, dK.
  *
  * Method (from the pages describing FLAMIA; page titles are cited in full
@@ -66,7 +67,12 @@ typedef struct flamia_attn_desc {
   const int32_t* cu_seqlens;    /* device int32[num_docs + 1] */
   int32_t num_heads;            /* H >= 1 */
   int32_t head_dim;             /* d: 64 or 128 */
-  int32_t causal;               /* must be 1 */
+  int32_t causal;               /* 1: query i sees keys j <= i of its document (the call the pages
+                                   define); 0: every key of its document, same quantization rules
+                                   without the mask -- the diagonal per-key V fold then takes the
+                                   whole 32-token block as visible, so its reference is the block
+                                   exponent.  0 with causal_dq_scale or exact: FLAMIA_ERR_INVALID_ARG;
+                                   0 with path = 1: FLAMIA_ERR_UNSUPPORTED */
   int32_t path;                 /* 0 = MXFP8; 1 = mixed: QK^T (and its recompute) from NVFP4 Q/K */
   int32_t hadamard;             /* 1: rotate Q and K rows by the normalised Sylvester Hadamard matrix */
   int32_t causal_dq_scale;      /* 1: dQ accumulator prescale from causally visible blocks only */
@@ -165,7 +171,8 @@ typedef struct flamia_qtensors {
  *                   in deterministic mode also the dQ partial slots: 64 x d
  *                   fp16 per head for at most ceil(T M / 16384) + ceil(3T / 128)
  *                   + 2 num_docs steps, M = max_doc_len, a bound of the causal
- *                   (key tile, query tile) steps of documents of at most M tokens).
+ *                   (key tile, query tile) steps of documents of at most M tokens;
+ *                   ceil(T M / 8192) in the first term when causal = 0).
  * If the documents need more steps than max_doc_len promised, the
  * deterministic backward drops the excess partials and sets word 2 of the
  * plan (int32 at byte 8 of qtensors.plan) to 1; the library never reads it

@@ -277,7 +277,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     for (int it = 0; it < NIT; ++it)
       hv[it] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 4 * (it + NIT * half)) * DQS);
     if (p.deterministic) {
-      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc);
+      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc, true);
       if (step >= a.det_cap) return;      // the plan flags the overflow
       uint8_t* const slot = reinterpret_cast<uint8_t*>(a.dq_part) + ((size_t)step * H + head) * (BWD_BQ * D * 2);
 #pragma unroll
@@ -631,7 +631,10 @@ __device__ __forceinline__ float half_max32(float m) {
 // key block folds V's exponents into P for dV; dS is quantized twice, with
 // K's exponent folded in and one exponent per (query, 32 keys) for dQ, and
 // with Q's exponent folded in and one exponent per (key, 32 queries) for dK.
-template <int D, bool DET, bool GRP, bool EXACT>
+// CAUSAL false: every query tile of the document visits the key tile (no
+// j <= i mask); the diagonal per-key V codes and fold stay, against the block
+// exponent as the quantizer then writes it.
+template <int D, bool DET, bool GRP, bool EXACT, bool CAUSAL>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
@@ -752,7 +755,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     if (wave < NPLANES) dma4(plane + (size_t)h * T + min(q0 + lane, L - 1), (B ? sR1 : sR0) + wave * BWD_BQ * 4);
   };
 
-  const int qt_first = k0 / BWD_BQ;
+  const int qt_first = CAUSAL ? k0 / BWD_BQ : 0;
   const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
   issue_tile(std::integral_constant<int, 0>{}, qt_first, h_first);
   if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hTk + k0 + 32 * tid] : E8M0_BIAS;
@@ -836,7 +839,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       hv[t2] = *reinterpret_cast<const v2h*>(fsrc + stage_row(row0) * DQS);
     }
     if constexpr (DET) {
-      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc);
+      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc, CAUSAL);
       if (step >= a.det_cap) return;      // the plan flags the overflow
       uint8_t* const slot = reinterpret_cast<uint8_t*>(a.dq_part) + ((size_t)step * H + h) * (BWD_BQ * D * 2);
 #pragma unroll
@@ -869,9 +872,11 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const int q0 = qt * BWD_BQ;
     const int nq = min(BWD_BQ, L - q0);
     const int QB = 2 * qt + qh;
-    const bool act = kb_active && QB >= KB && 32 * qh < nq;
+    const bool act = kb_active && (!CAUSAL || QB >= KB) && 32 * qh < nq;
     const bool dia = QB == KB;
-    const bool fast = !dia && 32 * qh + 32 <= nq;   // no mask (and, but for the exact option, no fold)
+    // no mask (and, but for the exact option, no fold); without the causal
+    // mask a block may also hold keys past the document end
+    const bool fast = !dia && 32 * qh + 32 <= nq && (CAUSAL || k0 + 32 * kb + 32 <= L);
     int dsc[4] = {0, 0, 0, 0};
     int eds = -127;
     v16f sacc, pacc;     // set (and read) only when act
@@ -957,7 +962,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
             const int rr = 4 * g + r;
             const int i = q0 + r0 + r;
             float dsr = 0.f, pev = 0.f;
-            if (kv && j <= i && i < L) {
+            if (kv && (!CAUSAL || j <= i) && i < L) {
               const float x = sacc[rr] * c;
               const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
               const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
@@ -1224,27 +1229,24 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
     if (p.D == 64) go(attn_bwd_kernel<64, 1>); else go(attn_bwd_kernel<128, 1>);
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
-    if (p.deterministic) {
-      if (p.exact && p.Hk != p.H) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, true, true, true>); else go8(attn_bwd8_kernel<128, true, true, true>);
-      } else if (p.exact) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, true, false, true>); else go8(attn_bwd8_kernel<128, true, false, true>);
-      } else if (p.Hk != p.H) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, true, true, false>); else go8(attn_bwd8_kernel<128, true, true, false>);
-      } else {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, true, false, false>); else go8(attn_bwd8_kernel<128, true, false, false>);
-      }
-    } else {
-      if (p.exact && p.Hk != p.H) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, false, true, true>); else go8(attn_bwd8_kernel<128, false, true, true>);
-      } else if (p.exact) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, true>); else go8(attn_bwd8_kernel<128, false, false, true>);
-      } else if (p.Hk != p.H) {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, false, true, false>); else go8(attn_bwd8_kernel<128, false, true, false>);
-      } else {
-        if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, false>); else go8(attn_bwd8_kernel<128, false, false, false>);
-      }
-    }
+    // one instantiation per (determinism, grouped heads, exact option, causal);
+    // the exact option is causal only
+    auto pick = [&](auto det, auto grp, auto exact, auto causal) {
+      constexpr bool DT = decltype(det)::value, GR = decltype(grp)::value;
+      constexpr bool EX = decltype(exact)::value, CA = decltype(causal)::value;
+      if (p.D == 64) go8(attn_bwd8_kernel<64, DT, GR, EX, CA>); else go8(attn_bwd8_kernel<128, DT, GR, EX, CA>);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    auto by_causal = [&](auto det, auto grp) {
+      if (p.exact) pick(det, grp, T_{}, T_{});
+      else if (p.causal) pick(det, grp, F_{}, T_{});
+      else pick(det, grp, F_{}, F_{});
+    };
+    auto by_group = [&](auto det) {
+      if (p.Hk != p.H) by_causal(det, T_{}); else by_causal(det, F_{});
+    };
+    if (p.deterministic) by_group(T_{}); else by_group(F_{});
   }
   return hipGetLastError();
 }

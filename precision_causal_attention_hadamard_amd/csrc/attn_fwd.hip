@@ -4,7 +4,8 @@
 // items taken longest first from the GPU-built list.  With grouped query
 // attention the K-side operands are those of key/value head h / (H / Hk).  Wave w owns the 32
 // queries of document-local block 4t + w.  The kernel steps over 64-key tiles
-// from the document start to the diagonal.  Per step:
+// from the document start to the diagonal (to the document end when the call
+// is not causal).  Per step:
 //   * K~ and V~ codes (and, on the two diagonal key tiles, the per-key V
 //     codes) are staged token-major in LDS.  The next tile's global loads are
 //     issued into registers before the current tile is computed, and the LDS
@@ -55,7 +56,10 @@ struct FwdArgs {
 // PATH 0: MXFP8 scores.  PATH 1 (mixed): scores from NVFP4 Q and K, expanded
 // exactly to bf16 (code x group scale) and multiplied on bf16 matrix cores,
 // then scaled by t_Q t_K; the rest of the kernel is shared.
-template <int D, int PATH, bool EXACT>
+// CAUSAL false: every key of the document is visible (no j <= i mask); the
+// diagonal per-key V fold is unchanged, its reference then being the block
+// exponent (written so by the quantizer).
+template <int D, int PATH, bool EXACT, bool CAUSAL>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D + 16;          // token-major row stride (bytes)
@@ -137,7 +141,7 @@ attn_fwd_kernel(FwdArgs a) {
   int m_run = M_NONE;
   const float c = p.c_log2;
 
-  const int kt_last = (min(q0 + FWD_BQ, L) - 1) / FWD_BK;
+  const int kt_last = ((CAUSAL ? min(q0 + FWD_BQ, L) : L) - 1) / FWD_BK;
 
   // ---- register prefetch of one key tile
   v4i pk[NCH], pv[NCH], pvk[NCH];
@@ -148,7 +152,7 @@ attn_fwd_kernel(FwdArgs a) {
   auto prefetch = [&](int kt) {
     const int j0 = kt * FWD_BK;
     const int nvalid = min(FWD_BK, L - j0);
-    const bool diag_tile = kt >= 2 * qt;
+    const bool diag_tile = (kt >> 1) == qt;   // holds the query tile's diagonal blocks
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
       const int ch = tid + FWD_THREADS * c2;
@@ -208,7 +212,7 @@ attn_fwd_kernel(FwdArgs a) {
   };
 
   prefetch(0);
-  commit(0, 0 >= 2 * qt);
+  commit(0, qt == 0);
   __syncthreads();
 
   for (int kt = 0; kt <= kt_last; ++kt) {
@@ -220,13 +224,14 @@ attn_fwd_kernel(FwdArgs a) {
       const uint8_t* tK = sK[buf];
       bool act[2], dia[2];
       v16f st[2];
-      // interior tile: every key precedes every query of the wave and lies in the document
-      const bool interior = j0 + FWD_BK <= qw0 && j0 + FWD_BK <= L;
+      // interior tile: every key precedes every query of the wave (or, not
+      // causal, any key) and lies in the document
+      const bool interior = (!CAUSAL || j0 + FWD_BK <= qw0) && j0 + FWD_BK <= L;
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int KB = 2 * kt + kb;
-        act[kb] = KB <= QB && j0 + 32 * kb < L;
+        act[kb] = (!CAUSAL || KB <= QB) && j0 + 32 * kb < L;
         dia[kb] = KB == QB;
         st[kb] = v16f{};
         if (act[kb]) {
@@ -252,7 +257,7 @@ attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
               const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-              if (j <= i && j < L) tmax = fmaxf(tmax, st[kb][rr]);
+              if ((!CAUSAL || j <= i) && j < L) tmax = fmaxf(tmax, st[kb][rr]);
             }
           }
         }
@@ -307,7 +312,7 @@ attn_fwd_kernel(FwdArgs a) {
                 const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
                 const int j = j0 + 32 * kb + jj;
                 float pr = 0.f;
-                if (act[kb] && j <= i && j < L) {
+                if (act[kb] && (!CAUSAL || j <= i) && j < L) {
                   const float x = st[kb][4 * g + r] * c;
                   const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
                   pr = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kofs);
@@ -340,7 +345,7 @@ attn_fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (kt < kt_last) commit(buf ^ 1, kt + 1 >= 2 * qt);
+    if (kt < kt_last) commit(buf ^ 1, ((kt + 1) >> 1) == qt);
     __syncthreads();
   }
 
@@ -381,11 +386,13 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
   dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(FWD_THREADS), 0, stream, a); };
   if (p.path == 1) {
-    if (p.D == 64) go(attn_fwd_kernel<64, 1, false>); else go(attn_fwd_kernel<128, 1, false>);
+    if (p.D == 64) go(attn_fwd_kernel<64, 1, false, true>); else go(attn_fwd_kernel<128, 1, false, true>);
   } else if (p.exact) {
-    if (p.D == 64) go(attn_fwd_kernel<64, 0, true>); else go(attn_fwd_kernel<128, 0, true>);
+    if (p.D == 64) go(attn_fwd_kernel<64, 0, true, true>); else go(attn_fwd_kernel<128, 0, true, true>);
+  } else if (!p.causal) {
+    if (p.D == 64) go(attn_fwd_kernel<64, 0, false, false>); else go(attn_fwd_kernel<128, 0, false, false>);
   } else {
-    if (p.D == 64) go(attn_fwd_kernel<64, 0, false>); else go(attn_fwd_kernel<128, 0, false>);
+    if (p.D == 64) go(attn_fwd_kernel<64, 0, false, true>); else go(attn_fwd_kernel<128, 0, false, true>);
   }
   return hipGetLastError();
 }

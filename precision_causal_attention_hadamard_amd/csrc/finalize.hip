@@ -42,12 +42,12 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
       const int s0 = p.cu[d], L = p.cu[d + 1] - s0, lp = t - s0;
       const int qt = lp / BWD_BQ, r = lp % BWD_BQ;
       const int nq = (L + BWD_BQ - 1) / BWD_BQ, nk = (L + BWD_BK - 1) / BWD_BK;
-      const int umax = min(qt / 2, nk - 1);
+      const int umax = p.causal ? min(qt / 2, nk - 1) : nk - 1;
       v8h a8[E / 8];
 #pragma unroll
       for (int c = 0; c < E / 8; ++c) a8[c] = v8h{};
       for (int u = 0; u <= umax; ++u) {
-        const long long step = det_step(det_base[d], u, qt, nq);
+        const long long step = det_step(det_base[d], u, qt, nq, p.causal);
         if (step >= det_cap) break;       // the plan flags the overflow
         const uint16_t* src = dq_part + (((size_t)step * p.H + h) * BWD_BQ + r) * D + (size_t)part * E;
 #pragma unroll

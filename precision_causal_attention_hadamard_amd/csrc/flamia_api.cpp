@@ -22,10 +22,13 @@ constexpr int K_FWD_BQ = 128, K_FWD_BK = 64, K_BWD_BQ = 64, K_BWD_BK = 128;
 // document of L tokens has n Q - n (n - 1) <= n^2 + n steps (n = ceil(L/128)
 // key tiles, Q = ceil(L/64) <= 2n query tiles), and n^2 + n <= L^2/16384 +
 // 3L/128 + 2; summed over documents of at most M tokens that is at most
-// T M / 16384 + 3 T / 128 + 2 num_docs.
+// T M / 16384 + 3 T / 128 + 2 num_docs.  Without the mask a document has
+// n Q <= (L/128 + 1)(L/64 + 1) = L^2/8192 + 3L/128 + 1 steps, so at most
+// T M / 8192 + 3 T / 128 + num_docs in all.
 int64_t det_step_cap(const flamia_attn_desc* d) {
   const int64_t T = d->total_tokens, M = d->max_doc_len > 0 ? d->max_doc_len : d->total_tokens;
-  return (T * M + 16383) / 16384 + (3 * T + 127) / 128 + 2 * (int64_t)d->num_docs;
+  const int64_t div = d->causal ? 16384 : 8192;
+  return (T * M + div - 1) / div + (3 * T + 127) / 128 + 2 * (int64_t)d->num_docs;
 }
 
 flamia_status validate(const flamia_attn_desc* d) {
@@ -39,7 +42,11 @@ flamia_status validate(const flamia_attn_desc* d) {
   if (d->num_kv_heads < 0 || d->num_kv_heads > d->num_heads ||
       (d->num_kv_heads > 0 && d->num_heads % d->num_kv_heads != 0))
     return FLAMIA_ERR_INVALID_ARG;
-  if (d->causal != 1) return FLAMIA_ERR_UNSUPPORTED;
+  // without the mask: the causal dQ prescale and the exact option (both
+  // defined by which keys a query may see) do not apply; the mixed path is
+  // built for causal calls only
+  if (!d->causal && (d->causal_dq_scale || d->exact)) return FLAMIA_ERR_INVALID_ARG;
+  if (!d->causal && d->path == 1) return FLAMIA_ERR_UNSUPPORTED;
   // grouped query attention is built for the MXFP8 path only
   if (d->path == 1 && d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads) return FLAMIA_ERR_UNSUPPORTED;
   // the exact option is built for the MXFP8 path
@@ -152,6 +159,7 @@ Problem problem(const flamia_attn_desc* d) {
   p.path = d->path;
   p.deterministic = d->deterministic;
   p.exact = d->exact;
+  p.causal = d->causal;
   // the exact option carries its own (per-token) causal dQ prescale
   if (p.exact) p.causal_dq_scale = 1;
   p.softmax_scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
@@ -223,7 +231,7 @@ flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const
   if (!q || !k || !v || !qt_complete(desc, out)) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const PlanLayout pl = plan_layout(desc);
-  s = hip_status(launch_plan(p.cu, p.ndocs, out->plan, pl, p.path == 1 ? out->qk_tensor_scale : nullptr, stream));
+  s = hip_status(launch_plan(p.cu, p.ndocs, p.causal, out->plan, pl, p.path == 1 ? out->qk_tensor_scale : nullptr, stream));
   if (s != FLAMIA_OK) return s;
   if (p.path == 1) {
     s = hip_status(launch_amax_qk(p, q, k, out->qk_tensor_scale, stream));

@@ -35,17 +35,21 @@ struct Problem {
   int hadamard, causal_dq_scale, path;
   int deterministic;       // dQ from per-step partials added in a fixed order
   int exact;               // the exact option: per-token scales, all-tile V fold, two dS payloads
+  int causal;              // 1: key j visible to query i for j <= i; 0: every key of the document
   float softmax_scale;     // fp32 softmax scale
   float c_log2;            // fp32(softmax_scale * log2(e))
 };
 
-hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, float* qk_scale,
+hipError_t launch_plan(const int* cu, int ndocs, int causal, void* plan, const PlanLayout& pl, float* qk_scale,
                        hipStream_t stream);
 
 // Deterministic-mode dQ partials: one fp16 [BWD_BQ, d] slot per (step, head),
 // step = first step of the document + u Q - u (u - 1) + (qt - 2 u) for key tile
-// u and query tile qt of a document with Q query tiles.
-__host__ __device__ inline long long det_step(int base, int u, int qt, int nq_tiles) {
+// u and query tile qt of a document with Q query tiles (causal: key tile u
+// visits query tiles 2u .. Q-1), or + u Q + qt without the mask (every key
+// tile visits every query tile).
+__host__ __device__ inline long long det_step(int base, int u, int qt, int nq_tiles, bool causal) {
+  if (!causal) return (long long)base + (long long)u * nq_tiles + qt;
   return (long long)base + (long long)u * nq_tiles - (long long)u * (u - 1) + (qt - 2 * u);
 }
 

@@ -19,6 +19,8 @@
 // Costs (number of tile pairs the causal tile touches):
 //   forward  query tile t of a document of length L: floor((min((t+1)Bq, L)-1)/Bk) + 1
 //   backward key tile u:                             ceil(L/Bq) - floor(u Bk / Bq)
+// Without the mask every tile of a document touches all ceil(L/Bk) key tiles
+// (forward) or all ceil(L/Bq) query tiles (backward).
 #include "flamia_device.hpp"
 #include "flamia_internal.hpp"
 
@@ -87,7 +89,7 @@ __device__ static unsigned long long wave_bitonic(unsigned long long key) {
   return key;
 }
 
-__device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool fwd, int bq, int bk,
+__device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool fwd, bool causal, int bq, int bk,
                                     unsigned long long* keys, int* wsum, int* count_out,
                                     int2* __restrict__ out) {
   const int tid = threadIdx.x;
@@ -104,7 +106,9 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
     const int first = n_tiles + block_inclusive_scan(n, wsum, total) - n;
     for (int t = 0; t < n; ++t) {
       int cost;
-      if (fwd) {
+      if (!causal) {
+        cost = fwd ? (L + bk - 1) / bk : (L + bq - 1) / bq;
+      } else if (fwd) {
         const int e = min((t + 1) * bq, L);
         cost = (e - 1) / bk + 1;
       } else {
@@ -155,9 +159,9 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
 // deterministic-mode step prefix: document d's dQ partial steps (per head)
 // start at det_base[d]; a document of L tokens has n = ceil(L / BWD_BK) key
 // tiles and Q = ceil(L / BWD_BQ) query tiles, and key tile u visits query
-// tiles 2u .. Q-1, so n Q - n (n - 1) steps.  Word 2 of the plan flags a
-// total beyond det_cap.
-__global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restrict__ cu, int ndocs,
+// tiles 2u .. Q-1, so n Q - n (n - 1) steps (n Q without the mask).  Word 2
+// of the plan flags a total beyond det_cap.
+__global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restrict__ cu, int ndocs, int causal,
                                                             int* counts, int2* fwd_items,
                                                             int2* bwd_items, float* qk_scale, int* det_base,
                                                             int det_cap) {
@@ -165,7 +169,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restric
   __shared__ int wsum[PLAN_WAVES];
   __shared__ long long wsum64[PLAN_WAVES];
   const bool fwd = blockIdx.x == 0;
-  build_sorted(cu, ndocs, fwd, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
+  build_sorted(cu, ndocs, fwd, causal != 0, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
                counts + (fwd ? 0 : 1), fwd ? fwd_items : bwd_items);
   if (fwd && threadIdx.x == 0) counts[3] = 0;
   if (!fwd) {
@@ -176,7 +180,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restric
       if (d < ndocs) {
         const long long L = cu[d + 1] - cu[d];
         const long long n = (L + BWD_BK - 1) / BWD_BK, q = (L + BWD_BQ - 1) / BWD_BQ;
-        st = n * q - n * (n - 1);
+        st = causal ? n * q - n * (n - 1) : n * q;
       }
       long long chunk;
       const long long incl = block_inclusive_scan64(st, wsum64, chunk);
@@ -192,10 +196,10 @@ __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restric
   if (fwd && qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
 }
 
-hipError_t launch_plan(const int* cu, int ndocs, void* plan, const PlanLayout& pl, float* qk_scale,
+hipError_t launch_plan(const int* cu, int ndocs, int causal, void* plan, const PlanLayout& pl, float* qk_scale,
                        hipStream_t stream) {
   char* base = static_cast<char*>(plan);
-  hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs,
+  hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs, causal,
                      reinterpret_cast<int*>(base), reinterpret_cast<int2*>(base + pl.fwd_offset),
                      reinterpret_cast<int2*>(base + pl.bwd_offset), qk_scale,
                      reinterpret_cast<int*>(base + pl.det_offset), pl.det_cap);

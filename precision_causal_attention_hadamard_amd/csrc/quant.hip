@@ -10,7 +10,7 @@
 // optional fp32 Hadamard butterflies on Q and K, amax over the block, the
 // round-up exponent, E4M3 codes; for V also the per-key exponents, per-key
 // codes and the per-query fold reference (prefix max of the per-key
-// exponents inside the block).  [Summary, §3.1 Token-Block Scaling; §3.2
+// exponents inside the block; the block exponent when the call is not causal).  [Summary, §3.1 Token-Block Scaling; §3.2
 // Causally Safe Scales; §4.3 Ablation Study]; [Reading, 4.4] first bullet.
 // Exact option: one exponent per token instead of per block (V's block and
 // per-key codes then coincide), and K's in-block prefix maximum of the
@@ -280,7 +280,9 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
           store_codes<D>(v_key_codes + off, x, ek);
           if (hf == 0) {
             v_key_exp[(size_t)h * T + tok] = (uint8_t)(ek + E8M0_BIAS);
-            v_ref_exp[(size_t)h * T + tok] = (uint8_t)(ref + E8M0_BIAS);
+            // without the mask every key of the block is visible: the
+            // reference is the block's largest per-key exponent, i.e. e
+            v_ref_exp[(size_t)h * T + tok] = (uint8_t)((p.causal ? ref : e) + E8M0_BIAS);
           }
         }
       }

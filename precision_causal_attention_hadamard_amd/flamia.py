@@ -175,10 +175,11 @@ class TrainingCall:
     """Device buffers and the three calls of one packed attention training
     step (quantize, forward, backward).  Inputs are bf16 CUDA tensors, q and
     do ``[T, H, d]``, k and v ``[T, Hk, d]`` (Hk dividing H: grouped query
-    attention when Hk < H); ``cu_seqlens`` a list of ints."""
+    attention when Hk < H); ``cu_seqlens`` a list of ints; ``causal`` False
+    drops the j <= i mask (every key of a document is visible)."""
 
     def __init__(self, q, k, v, do, cu_seqlens, hadamard=False, causal_dq_scale=False,
-                 softmax_scale=0.0, path=0, deterministic=False, exact=False):
+                 softmax_scale=0.0, path=0, deterministic=False, exact=False, causal=True):
         dev = q.device
         self.q, self.k, self.v, self.do = q, k, v, do
         T, H, d = q.shape
@@ -187,7 +188,8 @@ class TrainingCall:
         self.cu = torch.tensor(self.cu_list, dtype=torch.int32, device=dev)
         lens = [b - a for a, b in zip(self.cu_list, self.cu_list[1:])]
         self.desc = make_desc(self.cu, T, len(lens), max(lens) if lens else 0, H, d, hadamard,
-                              causal_dq_scale, softmax_scale, path, deterministic=int(deterministic),
+                              causal_dq_scale, softmax_scale, path, causal=int(causal),
+                              deterministic=int(deterministic),
                               num_kv_heads=Hk, exact=int(exact))
         qb, fb, bb = buffer_sizes(self.desc)
         self.qbuf = torch.empty(qb, dtype=torch.uint8, device=dev)

@@ -56,7 +56,7 @@ def test_buffer_sizes_valid(lib):
 @pytest.mark.parametrize("field,value,want", [
     ("head_dim", 96, 1), ("head_dim", 256, 1), ("num_heads", 0, 1), ("num_docs", 0, 1),
     ("total_tokens", -1, 1), ("max_doc_len", 300, 1), ("hadamard", 2, 1),
-    ("causal", 0, 2), ("deterministic", 2, 1), ("path", 7, 1),
+    ("causal", 2, 1), ("deterministic", 2, 1), ("path", 7, 1),
     ("num_kv_heads", -1, 1), ("num_kv_heads", 3, 1),
 ])
 def test_invalid_and_unsupported_descriptors(lib, field, value, want):
@@ -184,3 +184,44 @@ def test_plan_capacity_limit_is_reported(lib):
     # more tiles than the in-LDS sort holds: unsupported, not a fault
     d = base_desc(total_tokens=1 << 20, max_doc_len=1 << 20, num_docs=1)
     assert sizes_status(lib, d)[0] == 2
+
+
+def test_noncausal_descriptor_rules(lib):
+    """causal = 0 is accepted on the MXFP8 path (also grouped and
+    deterministic); the causal dQ prescale and the exact option, both defined
+    by which keys a query may see, are invalid without the mask; the mixed
+    path is built for causal calls only."""
+    assert sizes_status(lib, base_desc(causal=0))[0] == 0
+    assert sizes_status(lib, base_desc(causal=0, deterministic=1))[0] == 0
+    assert sizes_status(lib, base_desc(causal=0, num_heads=4, num_kv_heads=2))[0] == 0
+    assert sizes_status(lib, base_desc(causal=0, causal_dq_scale=1))[0] == 1
+    assert sizes_status(lib, base_desc(causal=0, exact=1))[0] == 1
+    assert sizes_status(lib, base_desc(causal=0, path=1))[0] == 2
+
+
+def noncausal_steps(L, bq=64, bk=128):
+    """Every key tile of a document visits every query tile without the mask."""
+    return (-(-L // bk)) * (-(-L // bq))
+
+
+def test_noncausal_deterministic_workspace_bound():
+    import random
+    lib = flamia.load()
+    rng = random.Random(6)
+    for T, M in ((256, 256), (4096, 64), (8192, 4096), (5000, 1000), (3000, 1), (1000, 129)):
+        for trial in range(5):
+            if trial == 0:
+                lens = [M] * (T // M) + ([T % M] if T % M else [])
+            else:
+                lens, left = [], T
+                while left:
+                    L = min(left, rng.randint(1, M))
+                    lens.append(L)
+                    left -= L
+            kw = dict(total_tokens=T, max_doc_len=M, num_docs=len(lens), num_heads=3, head_dim=64, causal=0)
+            st0, _, b0 = sizes_status(lib, base_desc(**kw))
+            st1, _, b1 = sizes_status(lib, base_desc(deterministic=1, **kw))
+            assert st0 == 0 and st1 == 0
+            cap_steps = (b1 - b0) // (3 * 64 * 64 * 2)
+            need = sum(noncausal_steps(L) for L in lens)
+            assert cap_steps >= need, (T, M, len(lens), cap_steps, need)
