@@ -124,6 +124,28 @@ def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str, kernel
     print(json.dumps(rec))
 
 
+def worklist_build(flamia, torch, ndocs: int = 131072):
+    """The GPU work-list build alone (flamia_plan_build) on the pages' stress
+    case: ndocs single-token documents.  HIP events on the launch stream,
+    median of 20 builds after 3 warm-ups."""
+    dev = torch.device("cuda:0")
+    z = torch.zeros(ndocs, 1, 64, dtype=torch.bfloat16, device=dev)
+    call = flamia.TrainingCall(z, z, z, z, list(range(ndocs + 1)))
+    for _ in range(3):
+        flamia.plan_build(call.desc, call.qt)
+    ms = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flamia.plan_build(call.desc, call.qt)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    fwd, bwd = call.plan_lists()
+    return {"docs": ndocs, "tokens": ndocs, "ms": ms[len(ms) // 2], "fwd_items": len(fwd), "bwd_items": len(bwd)}
+
+
 def cpu_baseline(wl, cfg: int, causal: bool = True):
     """The oracle, as it stands, on document 0 and the first few heads of the
     workload, timed on the host cores."""
@@ -293,6 +315,7 @@ def main():
         "quantizer": quant,
         "roofline": roofline,
     }
+    out["worklist"] = worklist_build(flamia, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.config, causal=not args.non_causal)
     print(json.dumps(out), flush=True)

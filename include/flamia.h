@@ -190,6 +190,21 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base,
                                      flamia_qtensors* out);
 
 /*
+ * flamia_plan_build -- the GPU-built longest-first work lists alone
+ * ([Summary, §3.6.2 Load-Balanced Scheduling]; [Reading, 4.4] last bullet:
+ * the schedule is built on the GPU once per microbatch with a fixed-pass
+ * sort).  flamia_quantize runs it first; it is exported so the schedule can
+ * be rebuilt or timed on its own.  Reads cu_seqlens, writes out->plan (and,
+ * on the mixed path, clears the two amax slots of out->qk_tensor_scale).
+ * Lists of at most 8192 tiles are sorted by one workgroup in LDS; longer
+ * lists by runs of 8192 keys sorted in LDS and merge passes over a key area
+ * inside the plan (sized by flamia_buffer_sizes).  No limit on the number
+ * of documents beyond the descriptor's.  Enqueues only; errors as for
+ * flamia_quantize.
+ */
+flamia_status flamia_plan_build(const flamia_attn_desc* desc, const flamia_qtensors* out, hipStream_t stream);
+
+/*
  * flamia_quantize -- fused forward-side quantization, [Reading, 4.4] first
  * bullet (rotation, block statistics, codes and scales generated together)
  * and [Summary, §4.3 Ablation Study]; plus the GPU-built work lists of
@@ -203,8 +218,8 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base,
  * V also gets per-key exponents/codes and the per-query fold reference.
  * Mixed path: Q and K also get NVFP4 codes and scales (see flamia_qtensors);
  * the tensor scale needs the tensor-wide amax, so one more launch computes it
- * first.  Launches: the work-list builder, (mixed path) the amax pass, the
- * quantizer.
+ * first.  Launches: the work-list builder (flamia_plan_build), (mixed path)
+ * the amax pass, the quantizer.
  */
 flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const void* k,
                               const void* v, const flamia_qtensors* out, hipStream_t stream);

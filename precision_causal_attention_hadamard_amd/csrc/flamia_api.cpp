@@ -52,11 +52,11 @@ flamia_status validate(const flamia_attn_desc* d) {
   // the exact option is built for the MXFP8 path
   if (d->exact && d->path != 0) return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
-  // sort key, costs into 20 bits, grid x into 31 bits
+  // sort key, costs into 20 bits; a launch's work-items (up to 512 per
+  // workgroup, one workgroup per tile and head) must fit 32 bits
   if (d->num_docs >= (1 << 24) || d->total_tokens >= (1 << 24)) return FLAMIA_ERR_WORKSPACE;
-  const int cap = cdiv(d->total_tokens, 64) + d->num_docs;
-  if (cap > PLAN_MAX_TILES) return FLAMIA_ERR_UNSUPPORTED;
-  if ((int64_t)cap * d->num_heads >= (int64_t)1 << 31) return FLAMIA_ERR_WORKSPACE;
+  const int64_t cap = cdiv(d->total_tokens, K_FWD_BQ) + (int64_t)d->num_docs;
+  if (cap * d->num_heads * 512 >= (int64_t)1 << 32) return FLAMIA_ERR_WORKSPACE;
   // the backward addresses a document's rows with 32-bit byte offsets of 2-byte elements
   if ((int64_t)d->total_tokens * d->num_heads * d->head_dim >= (int64_t)1 << 30) return FLAMIA_ERR_WORKSPACE;
   // deterministic mode: steps are 32-bit in the plan
@@ -90,6 +90,14 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
   pl.det_offset = align_up(pl.bwd_offset + sizeof(int) * 2 * (size_t)pl.cap_bwd);
   pl.det_cap = d->deterministic ? (int)det_step_cap(d) : 0;
   pl.bytes = align_up(pl.det_offset + sizeof(int) * ((size_t)d->num_docs + 1));
+  // lists beyond one workgroup's LDS: padded keys of both lists, two buffers
+  pl.cap_r = 0;
+  pl.keys_offset = 0;
+  if (pl.cap_fwd > PLAN_MAX_TILES) {
+    pl.cap_r = cdiv(pl.cap_fwd, PLAN_MAX_TILES) * PLAN_MAX_TILES;
+    pl.keys_offset = pl.bytes;
+    pl.bytes = align_up(pl.keys_offset + 4 * sizeof(uint64_t) * (size_t)pl.cap_r);
+  }
   return pl;
 }
 
@@ -224,14 +232,22 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base, f
   return FLAMIA_OK;
 }
 
+flamia_status flamia_plan_build(const flamia_attn_desc* desc, const flamia_qtensors* out, hipStream_t stream) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!qt_complete(desc, out)) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  return hip_status(launch_plan(p.cu, p.ndocs, p.causal, out->plan, plan_layout(desc),
+                                p.path == 1 ? out->qk_tensor_scale : nullptr, stream));
+}
+
 flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const void* k, const void* v,
                               const flamia_qtensors* out, hipStream_t stream) {
   flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
   if (!q || !k || !v || !qt_complete(desc, out)) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
-  const PlanLayout pl = plan_layout(desc);
-  s = hip_status(launch_plan(p.cu, p.ndocs, p.causal, out->plan, pl, p.path == 1 ? out->qk_tensor_scale : nullptr, stream));
+  s = flamia_plan_build(desc, out, stream);
   if (s != FLAMIA_OK) return s;
   if (p.path == 1) {
     s = hip_status(launch_amax_qk(p, q, k, out->qk_tensor_scale, stream));

@@ -6,7 +6,14 @@
 // Here one workgroup per list enumerates every (document, tile), forms a 64-bit key
 //   (COST_MAX - c) << 44 | doc << 20 | tile
 // and bitonic-sorts the keys (in LDS; within one wave for lists of at most
-// 64 tiles).  c is the tile's cost in the forward list and the cost of the
+// 64 tiles).  Lists that do not fit one workgroup's LDS (more than
+// PLAN_MAX_TILES tiles) take a multi-workgroup path: the keys are enumerated
+// into a padded array (tile t of document d at slot floor(cu[d] / 128) + d + t,
+// which never overlaps the next document's slots; empty slots hold the
+// largest key), runs of PLAN_MAX_TILES keys are bitonic-sorted in LDS, and
+// merge passes double the run length (each output element finds its source
+// by a co-rank binary search over the two runs), so the order is again the
+// single correct one.  c is the tile's cost in the forward list and the cost of the
 // document's costliest (first) key tile in the backward list, which keeps a
 // document's key tiles together (longest document first, tiles in order, so
 // still costliest first inside it) for L2 reuse of its query rows.  The key
@@ -21,6 +28,8 @@
 //   backward key tile u:                             ceil(L/Bq) - floor(u Bk / Bq)
 // Without the mask every tile of a document touches all ceil(L/Bk) key tiles
 // (forward) or all ceil(L/Bq) query tiles (backward).
+#include <utility>
+
 #include "flamia_device.hpp"
 #include "flamia_internal.hpp"
 
@@ -89,6 +98,48 @@ __device__ static unsigned long long wave_bitonic(unsigned long long key) {
   return key;
 }
 
+static_assert(FWD_BQ == BWD_BK, "both lists count 128-token tiles");
+constexpr int PLAN_TILE = FWD_BQ;
+
+// Sort key of tile t of document d (L tokens) in the forward or backward list.
+__device__ __forceinline__ unsigned long long tile_key(bool fwd, bool causal, int d, int t, int L, int bq, int bk) {
+  int cost;
+  if (!causal) {
+    cost = fwd ? (L + bk - 1) / bk : (L + bq - 1) / bq;
+  } else if (fwd) {
+    const int e = min((t + 1) * bq, L);
+    cost = (e - 1) / bk + 1;
+  } else {
+    cost = (L + bq - 1) / bq - (t * bk) / bq;
+  }
+  // backward: a document's tiles share the key of its costliest (first)
+  // tile, so they stay together, longest document first, tiles in order
+  const int kcost = fwd ? cost : (L + bq - 1) / bq;
+  return ((unsigned long long)(COST_MAX - kcost) << 44) | ((unsigned long long)d << 20) | (unsigned long long)t;
+}
+
+__device__ __forceinline__ int2 key_item(unsigned long long key) {
+  return make_int2((int)((key >> 20) & 0xffffffull), (int)(key & 0xfffffull));
+}
+
+// Ascending bitonic sort of n2 (a power of two) keys in LDS by the whole
+// workgroup.
+__device__ static void lds_bitonic(unsigned long long* keys, int n2) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += PLAN_THREADS) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = keys[i], b = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool fwd, bool causal, int bq, int bk,
                                     unsigned long long* keys, int* wsum, int* count_out,
                                     int2* __restrict__ out) {
@@ -104,22 +155,7 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
     }
     int total;
     const int first = n_tiles + block_inclusive_scan(n, wsum, total) - n;
-    for (int t = 0; t < n; ++t) {
-      int cost;
-      if (!causal) {
-        cost = fwd ? (L + bk - 1) / bk : (L + bq - 1) / bq;
-      } else if (fwd) {
-        const int e = min((t + 1) * bq, L);
-        cost = (e - 1) / bk + 1;
-      } else {
-        cost = (L + bq - 1) / bq - (t * bk) / bq;
-      }
-      // backward: a document's tiles share the key of its costliest (first)
-      // tile, so they stay together, longest document first, tiles in order
-      const int kcost = fwd ? cost : (L + bq - 1) / bq;
-      keys[first + t] = ((unsigned long long)(COST_MAX - kcost) << 44) |
-                        ((unsigned long long)d << 20) | (unsigned long long)t;
-    }
+    for (int t = 0; t < n; ++t) keys[first + t] = tile_key(fwd, causal, d, t, L, bq, bk);
     n_tiles += total;
   }
   __syncthreads();
@@ -127,30 +163,15 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
     // small list: one wave, no workgroup barriers
     if (tid < 64) {
       const unsigned long long key = wave_bitonic(tid < n_tiles ? keys[tid] : ~0ull);
-      if (tid < n_tiles) out[tid] = make_int2((int)((key >> 20) & 0xffffffull), (int)(key & 0xfffffull));
+      if (tid < n_tiles) out[tid] = key_item(key);
     }
   } else {
     int n2 = 1;
     while (n2 < n_tiles) n2 <<= 1;
     for (int i = n_tiles + tid; i < n2; i += PLAN_THREADS) keys[i] = ~0ull;
     __syncthreads();
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < n2; i += PLAN_THREADS) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const unsigned long long a = keys[i], b = keys[ixj];
-            const bool up = (i & k) == 0;
-            if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
-          }
-        }
-        __syncthreads();
-      }
-    }
-    for (int i = tid; i < n_tiles; i += PLAN_THREADS) {
-      const unsigned long long key = keys[i];
-      out[i] = make_int2((int)((key >> 20) & 0xffffffull), (int)(key & 0xfffffull));
-    }
+    lds_bitonic(keys, n2);
+    for (int i = tid; i < n_tiles; i += PLAN_THREADS) out[i] = key_item(keys[i]);
   }
   if (tid == 0) *count_out = n_tiles;
 }
@@ -161,18 +182,26 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
 // tiles and Q = ceil(L / BWD_BQ) query tiles, and key tile u visits query
 // tiles 2u .. Q-1, so n Q - n (n - 1) steps (n Q without the mask).  Word 2
 // of the plan flags a total beyond det_cap.
+// With `large` set the lists are left to the multi-workgroup kernels below
+// and this kernel only clears the tile counts.  The step prefix is built only in
+// deterministic mode (det_cap > 0).
 __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restrict__ cu, int ndocs, int causal,
-                                                            int* counts, int2* fwd_items,
+                                                            int large, int* counts, int2* fwd_items,
                                                             int2* bwd_items, float* qk_scale, int* det_base,
                                                             int det_cap) {
   __shared__ unsigned long long keys[PLAN_MAX_TILES];
   __shared__ int wsum[PLAN_WAVES];
   __shared__ long long wsum64[PLAN_WAVES];
   const bool fwd = blockIdx.x == 0;
-  build_sorted(cu, ndocs, fwd, causal != 0, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
-               counts + (fwd ? 0 : 1), fwd ? fwd_items : bwd_items);
+  if (large) {                    // the fill kernel adds the counts
+    if (threadIdx.x == 0) counts[fwd ? 0 : 1] = 0;
+  } else {
+    build_sorted(cu, ndocs, fwd, causal != 0, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
+                 counts + (fwd ? 0 : 1), fwd ? fwd_items : bwd_items);
+  }
   if (fwd && threadIdx.x == 0) counts[3] = 0;
-  if (!fwd) {
+  if (!fwd && det_cap == 0 && threadIdx.x == 0) counts[2] = 0;
+  if (!fwd && det_cap > 0) {
     long long done = 0;
     for (int base = 0; base < ndocs; base += PLAN_THREADS) {
       const int d = base + threadIdx.x;
@@ -196,13 +225,107 @@ __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restric
   if (fwd && qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
 }
 
+// ---- multi-workgroup path (lists of more than PLAN_MAX_TILES tiles)
+
+// First padded slot of document d: floor(cu[d] / 128) + d.  Strictly
+// increasing in d, and slot(d + 1) - slot(d) >= ceil(L_d / 128).
+__device__ __forceinline__ int doc_slot(const int* __restrict__ cu, int d) { return cu[d] / PLAN_TILE + d; }
+
+// Keys of both lists into padded arrays of cap_r slots (blockIdx.y = list);
+// each workgroup adds its number of real tiles to the list's count.
+__global__ void __launch_bounds__(256) plan_fill_kernel(const int* __restrict__ cu, int ndocs, int causal,
+                                                        unsigned long long* __restrict__ keys, int cap_r,
+                                                        int* counts) {
+  __shared__ int wcount[4];
+  const bool fwd = blockIdx.y == 0;
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  unsigned long long key = ~0ull;
+  if (s < cap_r && s < doc_slot(cu, ndocs - 1) + (cu[ndocs] - cu[ndocs - 1] + PLAN_TILE - 1) / PLAN_TILE) {
+    // largest d with doc_slot(d) <= s
+    int lo = 0, hi = ndocs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (doc_slot(cu, mid) <= s) lo = mid; else hi = mid - 1;
+    }
+    const int L = cu[lo + 1] - cu[lo], t = s - doc_slot(cu, lo);
+    if (t < (L + PLAN_TILE - 1) / PLAN_TILE)
+      key = tile_key(fwd, causal != 0, lo, t, L, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK);
+  }
+  if (s < cap_r) keys[(size_t)blockIdx.y * cap_r + s] = key;
+  const int n = __popcll(__ballot(key != ~0ull));
+  if ((threadIdx.x & 63) == 0) wcount[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int tot = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+    if (tot) atomicAdd(counts + blockIdx.y, tot);
+  }
+}
+
+// Each workgroup sorts one run of PLAN_MAX_TILES keys in LDS, in place.
+__global__ void __launch_bounds__(PLAN_THREADS) plan_sort_runs_kernel(unsigned long long* keys, int cap_r) {
+  __shared__ unsigned long long sk[PLAN_MAX_TILES];
+  unsigned long long* run = keys + (size_t)blockIdx.y * cap_r + (size_t)blockIdx.x * PLAN_MAX_TILES;
+  for (int i = threadIdx.x; i < PLAN_MAX_TILES; i += PLAN_THREADS) sk[i] = run[i];
+  __syncthreads();
+  lds_bitonic(sk, PLAN_MAX_TILES);
+  for (int i = threadIdx.x; i < PLAN_MAX_TILES; i += PLAN_THREADS) run[i] = sk[i];
+}
+
+// One merge pass: sorted runs of `width` keys are merged pairwise from src
+// into dst.  Output element k of a pair takes i elements from run A and k - i
+// from run B, with i the smallest index where B[k - i - 1] < A[i] (equal keys
+// -- only the padding -- come from A first).
+__global__ void __launch_bounds__(256) plan_merge_kernel(const unsigned long long* __restrict__ src,
+                                                         unsigned long long* __restrict__ dst, int cap_r,
+                                                         int width) {
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= cap_r) return;
+  const size_t lb0 = (size_t)blockIdx.y * cap_r;
+  const int base = g / (2 * width) * (2 * width);
+  const int la = min(width, cap_r - base), lb = max(0, min(width, cap_r - base - width));
+  const unsigned long long* A = src + lb0 + base;
+  const unsigned long long* B = A + la;
+  const int k = g - base;
+  int lo = max(0, k - lb), hi = min(k, la);
+  while (lo < hi) {
+    const int i = (lo + hi) >> 1;          // i < la, k - i - 1 >= 0
+    if (B[k - i - 1] < A[i]) hi = i; else lo = i + 1;
+  }
+  const int i = lo, j = k - lo;
+  const bool take_a = i < la && (j >= lb || A[i] <= B[j]);
+  dst[lb0 + g] = take_a ? A[i] : B[j];
+}
+
+// Sorted keys -> (doc, tile) items of both lists.
+__global__ void __launch_bounds__(256) plan_extract_kernel(const unsigned long long* __restrict__ keys, int cap_r,
+                                                           int cap, int2* fwd_items, int2* bwd_items) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= cap) return;
+  (blockIdx.y == 0 ? fwd_items : bwd_items)[i] = key_item(keys[(size_t)blockIdx.y * cap_r + i]);
+}
+
 hipError_t launch_plan(const int* cu, int ndocs, int causal, void* plan, const PlanLayout& pl, float* qk_scale,
                        hipStream_t stream) {
   char* base = static_cast<char*>(plan);
-  hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs, causal,
-                     reinterpret_cast<int*>(base), reinterpret_cast<int2*>(base + pl.fwd_offset),
-                     reinterpret_cast<int2*>(base + pl.bwd_offset), qk_scale,
-                     reinterpret_cast<int*>(base + pl.det_offset), pl.det_cap);
+  int* counts = reinterpret_cast<int*>(base);
+  int2* fwd_items = reinterpret_cast<int2*>(base + pl.fwd_offset);
+  int2* bwd_items = reinterpret_cast<int2*>(base + pl.bwd_offset);
+  hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs, causal, pl.cap_r > 0 ? 1 : 0,
+                     counts, fwd_items, bwd_items, qk_scale, reinterpret_cast<int*>(base + pl.det_offset), pl.det_cap);
+  if (pl.cap_r == 0) return hipGetLastError();
+  // cap_r: a multiple of PLAN_MAX_TILES holding cap_fwd = cap_bwd slots
+  unsigned long long* k0 = reinterpret_cast<unsigned long long*>(base + pl.keys_offset);
+  unsigned long long* k1 = k0 + 2 * (size_t)pl.cap_r;
+  const dim3 g256((unsigned)((pl.cap_r + 255) / 256), 2);
+  hipLaunchKernelGGL(plan_fill_kernel, g256, dim3(256), 0, stream, cu, ndocs, causal, k0, pl.cap_r, counts);
+  hipLaunchKernelGGL(plan_sort_runs_kernel, dim3((unsigned)(pl.cap_r / PLAN_MAX_TILES), 2), dim3(PLAN_THREADS), 0,
+                     stream, k0, pl.cap_r);
+  for (int w = PLAN_MAX_TILES; w < pl.cap_r; w *= 2) {
+    hipLaunchKernelGGL(plan_merge_kernel, g256, dim3(256), 0, stream, k0, k1, pl.cap_r, w);
+    std::swap(k0, k1);
+  }
+  hipLaunchKernelGGL(plan_extract_kernel, dim3((unsigned)((pl.cap_fwd + 255) / 256), 2), dim3(256), 0, stream, k0,
+                     pl.cap_r, pl.cap_fwd, fwd_items, bwd_items);
   return hipGetLastError();
 }
 

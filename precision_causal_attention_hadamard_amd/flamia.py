@@ -44,7 +44,7 @@ class QTensors(ctypes.Structure):
                  "qk_tensor_scale", "q_fp4_bf16", "k_fp4_bf16", "k_ref_exp")]
 
 
-EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_quantize", "flamia_attn_fwd",
+EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_plan_build", "flamia_quantize", "flamia_attn_fwd",
            "flamia_attn_bwd", "flamia_attn_bwd_prep", "flamia_attn_bwd_main", "flamia_attn_bwd_finish",
            "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
 
@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH):
     sig = {
         "flamia_buffer_sizes": [dp, ctypes.POINTER(S), ctypes.POINTER(S), ctypes.POINTER(S)],
         "flamia_qtensors_layout": [dp, P, qp],
+        "flamia_plan_build": [dp, qp, P],
         "flamia_quantize": [dp, P, P, P, qp, P],
         "flamia_attn_fwd": [dp, qp, P, P, P, P, P],
         "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
@@ -119,6 +120,10 @@ def qtensors_layout(desc: AttnDesc, base: torch.Tensor) -> QTensors:
     _check(load().flamia_qtensors_layout(ctypes.byref(desc), _ptr(base), ctypes.byref(qt)),
            "flamia_qtensors_layout")
     return qt
+
+
+def plan_build(desc, qt: QTensors, stream=None):
+    _check(load().flamia_plan_build(ctypes.byref(desc), ctypes.byref(qt), _stream(stream)), "flamia_plan_build")
 
 
 def quantize(desc, q, k, v, qt: QTensors, stream=None):

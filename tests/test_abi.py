@@ -180,10 +180,31 @@ def test_tile_config_and_status_strings(lib):
     assert flamia.status_string(99) == "unknown status"
 
 
-def test_plan_capacity_limit_is_reported(lib):
-    # more tiles than the in-LDS sort holds: unsupported, not a fault
-    d = base_desc(total_tokens=1 << 20, max_doc_len=1 << 20, num_docs=1)
-    assert sizes_status(lib, d)[0] == 2
+def test_large_worklists_get_a_key_area_and_launch_limits_are_reported(lib):
+    """Lists beyond one workgroup's LDS sort (8192 tiles of 128 tokens) take
+    the multi-workgroup path, whose padded keys (two buffers of both lists,
+    rounded up to runs of 8192) live in the plan; a call whose launches
+    would exceed 32-bit work-item counts is reported, not launched."""
+    def plan_bytes(d):
+        off, cap, boff, bcap = ctypes.c_size_t(), ctypes.c_int32(), ctypes.c_size_t(), ctypes.c_int32()
+        assert lib.flamia_plan_view(ctypes.byref(d), ctypes.byref(off), ctypes.byref(cap),
+                                    ctypes.byref(boff), ctypes.byref(bcap)) == 0
+        return cap.value, bcap.value
+    small = base_desc(total_tokens=8192 * 128 - 128, max_doc_len=8192 * 128 - 128, num_docs=1)
+    big = base_desc(total_tokens=1 << 20, max_doc_len=1 << 20, num_docs=1)
+    many = base_desc(total_tokens=131072, max_doc_len=1, num_docs=131072)
+    st_s, q_s, _ = sizes_status(lib, small)
+    st_b, q_b, _ = sizes_status(lib, big)
+    st_m, q_m, _ = sizes_status(lib, many)
+    assert st_s == st_b == st_m == 0
+    assert plan_bytes(small) == (8192, 8192) and plan_bytes(big) == (8193, 8193)
+    assert plan_bytes(many) == (132096, 132096)
+    runs = -(-132096 // 8192) * 8192
+    assert q_m >= 4 * 8 * runs
+    # codes grow by 4 bytes per element, the key area by 4 x 8 bytes per padded slot
+    assert q_b - q_s >= 4 * 128 * 2 * 64 + 4 * 8 * 16384
+    huge = base_desc(total_tokens=(1 << 23), max_doc_len=1, num_docs=(1 << 23), head_dim=64)
+    assert sizes_status(lib, huge)[0] == 3
 
 
 def test_noncausal_descriptor_rules(lib):
