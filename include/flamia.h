@@ -197,7 +197,7 @@ flamia_status flamia_qtensors_layout(const flamia_attn_desc* desc, void* base,
  * be rebuilt or timed on its own.  Reads cu_seqlens, writes out->plan (and,
  * on the mixed path, clears the two amax slots of out->qk_tensor_scale).
  * Lists of at most 8192 tiles are sorted by one workgroup in LDS; longer
- * lists by runs of 8192 keys sorted in LDS and merge passes over a key area
+ * lists by runs of 2048 keys sorted in LDS and merge passes over a key area
  * inside the plan (sized by flamia_buffer_sizes).  No limit on the number
  * of documents beyond the descriptor's.  Enqueues only; errors as for
  * flamia_quantize.

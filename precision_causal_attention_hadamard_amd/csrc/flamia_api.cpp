@@ -94,7 +94,7 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
   pl.cap_r = 0;
   pl.keys_offset = 0;
   if (pl.cap_fwd > PLAN_MAX_TILES) {
-    pl.cap_r = cdiv(pl.cap_fwd, PLAN_MAX_TILES) * PLAN_MAX_TILES;
+    pl.cap_r = cdiv(pl.cap_fwd, PLAN_RUN) * PLAN_RUN;
     pl.keys_offset = pl.bytes;
     pl.bytes = align_up(pl.keys_offset + 4 * sizeof(uint64_t) * (size_t)pl.cap_r);
   }

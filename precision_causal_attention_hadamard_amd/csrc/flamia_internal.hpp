@@ -7,8 +7,8 @@
 
 namespace flamia {
 
-constexpr int PLAN_MAX_TILES = 8192;      // LDS capacity of the one-workgroup work-list sort (and the
-                                          // run length of the multi-workgroup sort)
+constexpr int PLAN_MAX_TILES = 8192;      // LDS capacity of the one-workgroup work-list sort
+constexpr int PLAN_RUN = 2048;            // run length of the multi-workgroup sort (sorted in LDS)
 constexpr int COST_MAX = (1 << 20) - 1;   // costs must stay below this
 
 // Plan words: [0] forward items, [1] backward items, [2] deterministic-mode
@@ -22,7 +22,7 @@ struct PlanLayout {
   int cap_bwd;         // ceil(T / BWD_BK) + num_docs
   int det_cap;         // deterministic mode: dQ partial steps per head the workspace holds
   int cap_r;           // lists beyond PLAN_MAX_TILES: padded key slots per list (a multiple of
-                       // PLAN_MAX_TILES), else 0
+                       // PLAN_RUN), else 0
   size_t keys_offset;  // with cap_r: two key buffers of 2 x cap_r uint64 (both lists)
   size_t bytes;
 };

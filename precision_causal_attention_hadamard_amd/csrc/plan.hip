@@ -10,7 +10,7 @@
 // PLAN_MAX_TILES tiles) take a multi-workgroup path: the keys are enumerated
 // into a padded array (tile t of document d at slot floor(cu[d] / 128) + d + t,
 // which never overlaps the next document's slots; empty slots hold the
-// largest key), runs of PLAN_MAX_TILES keys are bitonic-sorted in LDS, and
+// largest key), runs of PLAN_RUN keys are bitonic-sorted in LDS, and
 // merge passes double the run length (each output element finds its source
 // by a co-rank binary search over the two runs), so the order is again the
 // single correct one.  c is the tile's cost in the forward list and the cost of the
@@ -261,14 +261,14 @@ __global__ void __launch_bounds__(256) plan_fill_kernel(const int* __restrict__ 
   }
 }
 
-// Each workgroup sorts one run of PLAN_MAX_TILES keys in LDS, in place.
+// Each workgroup sorts one run of PLAN_RUN keys in LDS, in place.
 __global__ void __launch_bounds__(PLAN_THREADS) plan_sort_runs_kernel(unsigned long long* keys, int cap_r) {
-  __shared__ unsigned long long sk[PLAN_MAX_TILES];
-  unsigned long long* run = keys + (size_t)blockIdx.y * cap_r + (size_t)blockIdx.x * PLAN_MAX_TILES;
-  for (int i = threadIdx.x; i < PLAN_MAX_TILES; i += PLAN_THREADS) sk[i] = run[i];
+  __shared__ unsigned long long sk[PLAN_RUN];
+  unsigned long long* run = keys + (size_t)blockIdx.y * cap_r + (size_t)blockIdx.x * PLAN_RUN;
+  for (int i = threadIdx.x; i < PLAN_RUN; i += PLAN_THREADS) sk[i] = run[i];
   __syncthreads();
-  lds_bitonic(sk, PLAN_MAX_TILES);
-  for (int i = threadIdx.x; i < PLAN_MAX_TILES; i += PLAN_THREADS) run[i] = sk[i];
+  lds_bitonic(sk, PLAN_RUN);
+  for (int i = threadIdx.x; i < PLAN_RUN; i += PLAN_THREADS) run[i] = sk[i];
 }
 
 // One merge pass: sorted runs of `width` keys are merged pairwise from src
@@ -313,14 +313,14 @@ hipError_t launch_plan(const int* cu, int ndocs, int causal, void* plan, const P
   hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs, causal, pl.cap_r > 0 ? 1 : 0,
                      counts, fwd_items, bwd_items, qk_scale, reinterpret_cast<int*>(base + pl.det_offset), pl.det_cap);
   if (pl.cap_r == 0) return hipGetLastError();
-  // cap_r: a multiple of PLAN_MAX_TILES holding cap_fwd = cap_bwd slots
+  // cap_r: a multiple of PLAN_RUN holding cap_fwd = cap_bwd slots
   unsigned long long* k0 = reinterpret_cast<unsigned long long*>(base + pl.keys_offset);
   unsigned long long* k1 = k0 + 2 * (size_t)pl.cap_r;
   const dim3 g256((unsigned)((pl.cap_r + 255) / 256), 2);
   hipLaunchKernelGGL(plan_fill_kernel, g256, dim3(256), 0, stream, cu, ndocs, causal, k0, pl.cap_r, counts);
-  hipLaunchKernelGGL(plan_sort_runs_kernel, dim3((unsigned)(pl.cap_r / PLAN_MAX_TILES), 2), dim3(PLAN_THREADS), 0,
+  hipLaunchKernelGGL(plan_sort_runs_kernel, dim3((unsigned)(pl.cap_r / PLAN_RUN), 2), dim3(PLAN_THREADS), 0,
                      stream, k0, pl.cap_r);
-  for (int w = PLAN_MAX_TILES; w < pl.cap_r; w *= 2) {
+  for (int w = PLAN_RUN; w < pl.cap_r; w *= 2) {
     hipLaunchKernelGGL(plan_merge_kernel, g256, dim3(256), 0, stream, k0, k1, pl.cap_r, w);
     std::swap(k0, k1);
   }

@@ -183,7 +183,7 @@ def test_tile_config_and_status_strings(lib):
 def test_large_worklists_get_a_key_area_and_launch_limits_are_reported(lib):
     """Lists beyond one workgroup's LDS sort (8192 tiles of 128 tokens) take
     the multi-workgroup path, whose padded keys (two buffers of both lists,
-    rounded up to runs of 8192) live in the plan; a call whose launches
+    rounded up to runs of 2048) live in the plan; a call whose launches
     would exceed 32-bit work-item counts is reported, not launched."""
     def plan_bytes(d):
         off, cap, boff, bcap = ctypes.c_size_t(), ctypes.c_int32(), ctypes.c_size_t(), ctypes.c_int32()
@@ -199,10 +199,10 @@ def test_large_worklists_get_a_key_area_and_launch_limits_are_reported(lib):
     assert st_s == st_b == st_m == 0
     assert plan_bytes(small) == (8192, 8192) and plan_bytes(big) == (8193, 8193)
     assert plan_bytes(many) == (132096, 132096)
-    runs = -(-132096 // 8192) * 8192
+    runs = -(-132096 // 2048) * 2048
     assert q_m >= 4 * 8 * runs
     # codes grow by 4 bytes per element, the key area by 4 x 8 bytes per padded slot
-    assert q_b - q_s >= 4 * 128 * 2 * 64 + 4 * 8 * 16384
+    assert q_b - q_s >= 4 * 128 * 2 * 64 + 4 * 8 * 10240
     huge = base_desc(total_tokens=(1 << 23), max_doc_len=1, num_docs=(1 << 23), head_dim=64)
     assert sizes_status(lib, huge)[0] == 3
 

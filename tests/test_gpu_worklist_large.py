@@ -1,7 +1,7 @@
 """Work lists beyond one workgroup's LDS sort (more than 8192 tiles of 128
 tokens), on the GPU through the C ABI.
 
-The multi-workgroup path (padded key enumeration, runs of 8192 keys sorted in
+The multi-workgroup path (padded key enumeration, runs of 2048 keys sorted in
 LDS, merge passes) must give exactly the oracle's longest-first lists --
 causal and not -- including the pages' stress case of 131072 single-token
 documents ([Reading, 4.4] last bullet times the GPU schedule build there);
