@@ -11,7 +11,7 @@ its time is inside the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
                        [--kv-heads Hk] [--deterministic] [--exact] [--non-causal]
-                       [--no-cpu-baseline]
+                       [--causal-dq-scale] [--no-cpu-baseline]
                        [--copy-calibration]
 """
 
@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--non-causal", action="store_true",
                     help="the call without the causal mask (every key of a document visible); "
                          "FLOPs then count every (query, key) pair of a document")
+    ap.add_argument("--causal-dq-scale", action="store_true",
+                    help="the optional causal dQ accumulator scale (prescale from causally visible key blocks only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true",
                     help="ordered dQ reduction (per-step partials, fixed-order fp16 sum) instead of atomics")
@@ -216,7 +218,7 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
-                               causal_dq_scale=wl.causal_dq_scale, path=wl.path,
+                               causal_dq_scale=wl.causal_dq_scale or args.causal_dq_scale, path=wl.path,
                                deterministic=args.deterministic, exact=args.exact,
                                causal=not args.non_causal)
     T, H, d = call.shape
@@ -306,7 +308,8 @@ def main():
                    "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
                    "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
                    "deterministic": bool(args.deterministic), "exact": bool(args.exact),
-                   "causal": not args.non_causal, "causal_pairs": pairs, "flops_per_step": flops},
+                   "causal": not args.non_causal, "causal_dq_scale": bool(wl.causal_dq_scale or args.causal_dq_scale),
+                   "causal_pairs": pairs, "flops_per_step": flops},
         "pct_fp8_peak": 100.0 * value / FP8_PEAK_TFLOPS,
         "stage_ms": stage_ms, "event_ms_per_step": event_ms,
         # the attention kernels alone: forward, and backward without the dO
