@@ -71,8 +71,8 @@ typedef struct flamia_attn_desc {
                                    define); 0: every key of its document, same quantization rules
                                    without the mask -- the diagonal per-key V fold then takes the
                                    whole 32-token block as visible, so its reference is the block
-                                   exponent.  0 with causal_dq_scale or exact: FLAMIA_ERR_INVALID_ARG;
-                                   0 with path = 1: FLAMIA_ERR_UNSUPPORTED */
+                                   exponent.  Both paths.  0 with causal_dq_scale or exact:
+                                   FLAMIA_ERR_INVALID_ARG */
   int32_t path;                 /* 0 = MXFP8; 1 = mixed: QK^T (and its recompute) from NVFP4 Q/K */
   int32_t hadamard;             /* 1: rotate Q and K rows by the normalised Sylvester Hadamard matrix */
   int32_t causal_dq_scale;      /* 1: dQ accumulator prescale from causally visible blocks only */

@@ -85,7 +85,9 @@ struct BwdArgs {
 // NVFP4 Q and K (expanded exactly to bf16) on bf16 matrix cores with the same
 // operand split and order as the forward, then scaled by t_Q t_K; dK and dQ
 // still use the E4M3 token-block Q~ and K~.
-template <int D, int PATH>
+// CAUSAL false: every query tile of the document visits the key tile (no
+// j <= i mask), as in attn_bwd8_kernel.
+template <int D, int PATH, bool CAUSAL>
 __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   constexpr int DSK = BWD_BQ + 16;           // key-major dS^ row stride (bytes)
   constexpr int NS = D / 64;
@@ -200,7 +202,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   };
 
   // ---- per item: the key tile (for K~^T of dQ) and the first query tile
-  const int qt_first = k0 / BWD_BQ;
+  const int qt_first = CAUSAL ? k0 / BWD_BQ : 0;
   const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
   dma_codes(sK, k_doc, k0, BWD_BK);
   issue_tile(std::integral_constant<int, 0>{}, qt_first);
@@ -277,7 +279,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
     for (int it = 0; it < NIT; ++it)
       hv[it] = *reinterpret_cast<const v2h*>(fsrc + RPI * (wave + 4 * (it + NIT * half)) * DQS);
     if (p.deterministic) {
-      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc, true);
+      const long long step = det_step(a.det_base[doc], u, qtp, nq_doc, CAUSAL);
       if (step >= a.det_cap) return;      // the plan flags the overflow
       uint8_t* const slot = reinterpret_cast<uint8_t*>(a.dq_part) + ((size_t)step * H + head) * (BWD_BQ * D * 2);
 #pragma unroll
@@ -347,12 +349,13 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int QB = 2 * qt + qb;
-      const bool act = wave_active && QB >= KB && 32 * qb < nq;
+      const bool act = wave_active && (!CAUSAL || QB >= KB) && 32 * qb < nq;
       eds[qb] = -127;
 #pragma unroll
       for (int g = 0; g < 4; ++g) dsc[qb][g] = 0;
       const bool dia = QB == KB;
-      const bool fast = !dia && 32 * qb + 32 <= nq;   // no mask, no fold
+      // no mask, no fold; without the causal mask a key block may also run past the document end
+      const bool fast = !dia && 32 * qb + 32 <= nq && (CAUSAL || k0 + 32 * wave + 32 <= L);
       v16f sacc = v16f{}, pacc = v16f{};
       if (act) {
         const int qx = pqx[32 * qb];
@@ -413,7 +416,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
               const int rr = 4 * g + r;
               const int i = q0 + r0 + r;
               float dsr = 0.f, pev = 0.f;
-              if (kv && j <= i && i < L) {
+              if (kv && (!CAUSAL || j <= i) && i < L) {
                 const float x = sacc[rr] * c;
                 const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
                 const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
@@ -1226,7 +1229,11 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
   dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.Hk * (unsigned)in.gsplit);   // the mixed path has Hk = H, gsplit = 1
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };
   if (p.path == 1) {
-    if (p.D == 64) go(attn_bwd_kernel<64, 1>); else go(attn_bwd_kernel<128, 1>);
+    if (p.causal) {
+      if (p.D == 64) go(attn_bwd_kernel<64, 1, true>); else go(attn_bwd_kernel<128, 1, true>);
+    } else {
+      if (p.D == 64) go(attn_bwd_kernel<64, 1, false>); else go(attn_bwd_kernel<128, 1, false>);
+    }
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
     // one instantiation per (determinism, grouped heads, exact option, causal);

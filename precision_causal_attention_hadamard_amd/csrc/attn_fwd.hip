@@ -385,8 +385,10 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
             static_cast<uint16_t*>(o), row_max, row_sum};
   dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(FWD_THREADS), 0, stream, a); };
-  if (p.path == 1) {
+  if (p.path == 1 && p.causal) {
     if (p.D == 64) go(attn_fwd_kernel<64, 1, false, true>); else go(attn_fwd_kernel<128, 1, false, true>);
+  } else if (p.path == 1) {
+    if (p.D == 64) go(attn_fwd_kernel<64, 1, false, false>); else go(attn_fwd_kernel<128, 1, false, false>);
   } else if (p.exact) {
     if (p.D == 64) go(attn_fwd_kernel<64, 0, true, true>); else go(attn_fwd_kernel<128, 0, true, true>);
   } else if (!p.causal) {

@@ -43,10 +43,8 @@ flamia_status validate(const flamia_attn_desc* d) {
       (d->num_kv_heads > 0 && d->num_heads % d->num_kv_heads != 0))
     return FLAMIA_ERR_INVALID_ARG;
   // without the mask: the causal dQ prescale and the exact option (both
-  // defined by which keys a query may see) do not apply; the mixed path is
-  // built for causal calls only
+  // defined by which keys a query may see) do not apply
   if (!d->causal && (d->causal_dq_scale || d->exact)) return FLAMIA_ERR_INVALID_ARG;
-  if (!d->causal && d->path == 1) return FLAMIA_ERR_UNSUPPORTED;
   // grouped query attention is built for the MXFP8 path only
   if (d->path == 1 && d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads) return FLAMIA_ERR_UNSUPPORTED;
   // the exact option is built for the MXFP8 path

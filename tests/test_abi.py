@@ -208,16 +208,15 @@ def test_large_worklists_get_a_key_area_and_launch_limits_are_reported(lib):
 
 
 def test_noncausal_descriptor_rules(lib):
-    """causal = 0 is accepted on the MXFP8 path (also grouped and
-    deterministic); the causal dQ prescale and the exact option, both defined
-    by which keys a query may see, are invalid without the mask; the mixed
-    path is built for causal calls only."""
+    """causal = 0 is accepted on both paths (also grouped and deterministic);
+    the causal dQ prescale and the exact option, both defined by which keys a
+    query may see, are invalid without the mask."""
     assert sizes_status(lib, base_desc(causal=0))[0] == 0
     assert sizes_status(lib, base_desc(causal=0, deterministic=1))[0] == 0
     assert sizes_status(lib, base_desc(causal=0, num_heads=4, num_kv_heads=2))[0] == 0
     assert sizes_status(lib, base_desc(causal=0, causal_dq_scale=1))[0] == 1
     assert sizes_status(lib, base_desc(causal=0, exact=1))[0] == 1
-    assert sizes_status(lib, base_desc(causal=0, path=1))[0] == 2
+    assert sizes_status(lib, base_desc(causal=0, path=1))[0] == 0
 
 
 def noncausal_steps(L, bq=64, bk=128):

@@ -9,7 +9,7 @@ block exponent.  Checked here:
   exponent;
 - O, dQ, dK, dV to the bar of the causal cases (decision_compare.py), the
   integer row maximum and l as there; MHA, Hadamard with outliers, grouped
-  query heads, deterministic dQ;
+  query heads, deterministic dQ, the mixed NVFP4-score path;
 - the work lists equal the oracle's non-causal lists;
 - the last token of each document sees the same keys with and without the
   mask, so its O row, row maximum and l are bitwise those of the causal call;
@@ -39,15 +39,15 @@ def run_nc(flamia, wl, deterministic=False, causal=False, steps=1):
     dev = torch.device("cuda")
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard, causal=causal,
-                               deterministic=deterministic)
+                               deterministic=deterministic, path=wl.path)
     for _ in range(steps):
         call.step()
     torch.cuda.synchronize()
     return call
 
 
-def oracle_nc(arrs, cu, hadamard, outliers):
-    num = A.Numerics(hadamard=hadamard, causal=False)
+def oracle_nc(arrs, cu, hadamard, outliers, path=0):
+    num = A.Numerics(hadamard=hadamard, causal=False, path="mixed" if path else "mxfp8")
     ref = A.training_call(*arrs, cu, num)
     ref["_allow"] = DC.allowances(*arrs, cu, num)
     ref["_outliers"] = outliers
@@ -83,6 +83,8 @@ CASES = {
     "long_doc_d128": lambda: W.small_packed(54, [1000], heads=2, head_dim=128),
     "gqa_d128_h4_kv2": lambda: W.small_packed(55, [129, 64, 31, 250], heads=4, head_dim=128, kv_heads=2),
     "gqa_d64_h6_kv2": lambda: W.small_packed(56, [50, 1, 177], heads=6, head_dim=64, kv_heads=2),
+    "mixed_ragged_d64": lambda: W.small_packed(63, [1, 70, 33, 130], heads=3, head_dim=64, path=1),
+    "mixed_d128_h2": lambda: W.small_packed(64, [256, 100], heads=2, head_dim=128, path=1),
 }
 
 
@@ -91,7 +93,7 @@ def parity(lib, case, deterministic=False):
     call = run_nc(lib, wl, deterministic=deterministic)
     if deterministic:
         assert call.plan_error_word() == 0
-    ref = oracle_nc(np_inputs(wl), wl.cu_seqlens, wl.hadamard, wl.has_outliers)
+    ref = oracle_nc(np_inputs(wl), wl.cu_seqlens, wl.hadamard, wl.has_outliers, wl.path)
     check_codes(call, ref)
     outs = {n: getattr(call, n).float().cpu().numpy() for n in ("o", "dq", "dk", "dv")}
     m = check_outputs(outs, call.row_max.cpu().numpy(), call.row_sum.cpu().numpy(), ref, "noncausal")
@@ -106,7 +108,7 @@ def test_noncausal_parity(gpu_lib, case):
     parity(gpu_lib, case)
 
 
-@pytest.mark.parametrize("case", ["ragged_d128_h4", "gqa_d128_h4_kv2", "hadamard_outliers_d128"])
+@pytest.mark.parametrize("case", ["ragged_d128_h4", "gqa_d128_h4_kv2", "hadamard_outliers_d128", "mixed_d128_h2"])
 def test_noncausal_deterministic_parity_repeat_and_atomic_agreement(gpu_lib, case):
     print(f"[noncausal] deterministic case={case}", flush=True)
     a = parity(gpu_lib, case, deterministic=True)
