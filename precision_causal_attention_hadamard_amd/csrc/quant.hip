@@ -20,7 +20,10 @@
 // codes of dO, D_i = sum_d dO~_id O_id from the same codes ([Summary, §3.3]:
 // D uses the quantized dO that dP uses), G_i = dO~_i 2^-8 / l_i in bf16 (the
 // right operand of dV = P^T G), the dQ accumulator prescale exponent of the
-// block, and zeroes the block's rows of the fp16 dQ accumulator.
+// block, and zeroes the block's rows of the fp16 dQ accumulator.  G and the
+// zeros leave as whole rows per store instruction (G through a wave-private
+// LDS tile): half-row stores from each lane left partial lines that doubled
+// the write traffic.
 #include "flamia_device.hpp"
 #include "flamia_internal.hpp"
 
@@ -290,6 +293,16 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
   });
 }
 
+// LDS slot (16-byte unit within a 2d-byte row) of chunk c of half hf of row r
+// of a wave's G tile: chunks are XOR-swizzled within their half by the row and
+// the half, so that both the half-row writes (8 lanes per pass) and the
+// whole-row reads (16 lanes per pass) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int g_slot(int r, int hf, int c) {
+  constexpr int HC = D / 16;                       // chunks per half-row
+  return hf * HC + (c ^ (r & (HC - 1)) ^ (hf * (HC / 2)));
+}
+
 template <int D>
 __global__ void __launch_bounds__(QUANT_THREADS)
 quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
@@ -302,6 +315,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
                 float* __restrict__ il8,
                 int* __restrict__ qexps, uint16_t* __restrict__ g, int* __restrict__ dq_sigma,
                 uint16_t* __restrict__ dq_acc) {
+  __shared__ __attribute__((aligned(16))) uint8_t gstage[QUANT_THREADS / 64][32 * D * 2];   // G rows of a block
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
   const int c0 = blockIdx.x * TOKEN_BLOCK;
@@ -348,6 +362,17 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
         }
         emax_kv = wave_max_i(ek) + wave_max_i(ev);
       }
+      if (!p.deterministic) {
+        // zero the block's rows of the fp16 dQ accumulator (unused in
+        // deterministic mode): whole rows per store instruction, 16 lanes
+        // per 2d-byte row (d = 128), so every instruction writes full lines
+        constexpr int CPR = D / 8, RPI = 64 / CPR;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int r = RPI * i + lane / CPR;
+          if (bs + r < be) st16(dq_acc + ((size_t)(bs + r) * H + h) * D + 8 * (lane % CPR), v4i{0, 0, 0, 0});
+        }
+      }
       if (valid) {
         // codes, dequantized values, D and G
         float oo[D / 2];
@@ -371,6 +396,8 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
 #pragma unroll
         for (int i = 0; i < D / 2; ++i) dsum = __builtin_fmaf(x[i], oo[i], dsum);
         dsum += __shfl_xor(dsum, 1, 64);
+        // G half-row into the wave's LDS tile (16-byte chunks swizzled so the
+        // writes and the row reads below are free of bank conflicts)
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
           v4i w;
@@ -380,8 +407,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
             uint32_t lo = f32_to_bf16_bits(x[b] * ginv), hi = f32_to_bf16_bits(x[b + 1] * ginv);
             w[j] = (int)(lo | (hi << 16));
           }
-          st16(g + off + 8 * c, w);
-          if (!p.deterministic) st16(dq_acc + off + 8 * c, v4i{0, 0, 0, 0});   // (unused in deterministic mode)
+          st16(gstage[wave] + row * (2 * D) + 16 * g_slot<D>(row, hf, c), w);
         }
         if (hf == 0) {
           const size_t mi = (size_t)h * T + tok;
@@ -395,6 +421,21 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
           dq_sigma[mi] = e + emax_kv + LOG2D + 13;
         }
       }
+      // G rows to memory: 16 lanes per 2d-byte row (d = 128), whole lines per instruction
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      {
+        constexpr int CPR = D / 8, HC = CPR / 2, RPI = 64 / CPR;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int r = RPI * i + lane / CPR, lc = lane % CPR;
+          if (bs + r < be)
+            st16(g + ((size_t)(bs + r) * H + h) * D + 8 * lc,
+                 ld16(gstage[wave] + r * (2 * D) + 16 * g_slot<D>(r, lc / HC, lc % HC)));
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
   });
 }
