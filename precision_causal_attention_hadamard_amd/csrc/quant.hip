@@ -103,11 +103,26 @@ __device__ __forceinline__ void fwht_half_row(float (&x)[D / 2], int hf) {
   for (int a = 0; a < D / 2; ++a) x[a] = x[a] * inv_sqrt_d;
 }
 
-// Codes of a half-row, scaled by 2^-e (exact), written as 16-byte chunks.
+// LDS slot (16-byte unit within a d-byte code row) of chunk c of half hf of
+// row r of a wave's code tile: XOR-swizzled within the half by the row and the
+// half, so the half-row writes (8 lanes per pass) spread over the banks.
 template <int D>
-__device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst, const float (&x)[D / 2], int e) {
+__device__ __forceinline__ int code_slot(int r, int hf, int c) {
+  constexpr int HC = D / 32;                       // chunks per half-row
+  return hf * HC + (c ^ (r & (HC - 1)) ^ (hf * (HC / 2)));
+}
+
+// Codes of the half-rows of one 32-token block (lane = (row, half)), scaled
+// by 2^-e (exact), to memory as whole rows per store instruction: the
+// half-rows go through the wave's LDS tile `stage` (32 x d bytes), then 2d/32
+// lanes per row store 16 bytes each.  Rows at or past nrows are not stored.
+template <int D>
+__device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst_row0, size_t row_stride, int nrows,
+                                            uint8_t* stage, const float (&x)[D / 2], int e) {
+  constexpr int HC = D / 32, CPR = 2 * HC, RPI = 64 / CPR;
+  const int lane = threadIdx.x & 63, row = lane >> 1, hf = lane & 1;
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
+  for (int c = 0; c < HC; ++c) {
     v4i w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -115,8 +130,17 @@ __device__ __forceinline__ void store_codes(uint8_t* __restrict__ dst, const flo
       w[j] = cvt_fp8x4(__builtin_amdgcn_ldexpf(x[b], -e), __builtin_amdgcn_ldexpf(x[b + 1], -e),
                        __builtin_amdgcn_ldexpf(x[b + 2], -e), __builtin_amdgcn_ldexpf(x[b + 3], -e));
     }
-    st16(dst + 16 * c, w);
+    st16(stage + row * D + 16 * code_slot<D>(row, hf, c), w);
   }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / CPR, lc = lane % CPR;
+    if (r < nrows) st16(dst_row0 + (size_t)r * row_stride + 16 * lc, ld16(stage + r * D + 16 * code_slot<D>(r, lc / HC, lc % HC)));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
 template <int D>
@@ -224,6 +248,7 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  uint8_t* __restrict__ k_exp, uint8_t* __restrict__ v_exp,
                  uint8_t* __restrict__ v_key_exp, uint8_t* __restrict__ v_ref_exp,
                  uint8_t* __restrict__ k_ref_exp, Fp4Operands f4) {
+  __shared__ __attribute__((aligned(16))) uint8_t cstage[QUANT_THREADS / 64][32 * D];   // code rows of a block
   const int tensor = blockIdx.y;
   const bool nvfp4 = p.path == 1 && tensor < 2;
   float t = 1.f;
@@ -252,8 +277,8 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
       const float lane_amax = half_row_amax<D>(x);
       // exact option: one exponent per token (the row's two lane halves)
       const int e = roundup_exp(p.exact ? fmaxf(lane_amax, __shfl_xor(lane_amax, 1, 64)) : wave_max(lane_amax));
+      store_codes<D>(codes + ((size_t)bs * H + h) * D, (size_t)H * D, be - bs, cstage[wave], x, e);
       if (valid) {
-        store_codes<D>(codes + off, x, e);
         if (hf == 0) exps[(size_t)h * T + tok] = (uint8_t)(e + E8M0_BIAS);
         if (nvfp4)
           store_nvfp4<D>((tensor == 0 ? f4.q_fp4 : f4.k_fp4) + off / 2,
@@ -279,8 +304,8 @@ quant_qkv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
           int up = __shfl_up(ref, o, 64);
           if (lane >= o) ref = max(ref, up);
         }
+        store_codes<D>(v_key_codes + ((size_t)bs * H + h) * D, (size_t)H * D, be - bs, cstage[wave], x, ek);
         if (valid) {
-          store_codes<D>(v_key_codes + off, x, ek);
           if (hf == 0) {
             v_key_exp[(size_t)h * T + tok] = (uint8_t)(ek + E8M0_BIAS);
             // without the mask every key of the block is visible: the
@@ -315,6 +340,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
                 float* __restrict__ il8,
                 int* __restrict__ qexps, uint16_t* __restrict__ g, int* __restrict__ dq_sigma,
                 uint16_t* __restrict__ dq_acc) {
+  __shared__ __attribute__((aligned(16))) uint8_t cstage[QUANT_THREADS / 64][32 * D];       // dO~ code rows of a block
   __shared__ __attribute__((aligned(16))) uint8_t gstage[QUANT_THREADS / 64][32 * D * 2];   // G rows of a block
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = lane >> 1, hf = lane & 1;
@@ -391,7 +417,7 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
 #pragma unroll
             for (int t = 0; t < 4; ++t) x[b + t] = __builtin_amdgcn_ldexpf(fp8_value(w[j], t), e);
           }
-          st16(do_codes + off + 16 * c, w);
+          st16(cstage[wave] + row * D + 16 * code_slot<D>(row, hf, c), w);   // rows leave below
         }
 #pragma unroll
         for (int i = 0; i < D / 2; ++i) dsum = __builtin_fmaf(x[i], oo[i], dsum);
@@ -421,9 +447,19 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
           dq_sigma[mi] = e + emax_kv + LOG2D + 13;
         }
       }
-      // G rows to memory: 16 lanes per 2d-byte row (d = 128), whole lines per instruction
+      // dO~ code rows and G rows to memory: whole rows per store instruction
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      {
+        constexpr int HC = D / 32, CPR = 2 * HC, RPI = 64 / CPR;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int r = RPI * i + lane / CPR, lc = lane % CPR;
+          if (bs + r < be)
+            st16(do_codes + ((size_t)(bs + r) * H + h) * D + 16 * lc,
+                 ld16(cstage[wave] + r * D + 16 * code_slot<D>(r, lc / HC, lc % HC)));
+        }
+      }
       {
         constexpr int CPR = D / 8, HC = CPR / 2, RPI = 64 / CPR;
 #pragma unroll
