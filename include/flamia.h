@@ -87,8 +87,8 @@ typedef struct flamia_attn_desc {
                                    divisor of H gives grouped query attention: query head h reads
                                    key/value head h / (H / Hk), and dk, dv of a key/value head are
                                    the sums over its H / Hk query heads, accumulated in fp32 and
-                                   rounded once ([Reading, 5.2] measures GQA workloads).  MXFP8
-                                   path only (path = 1 with Hk < H: FLAMIA_ERR_UNSUPPORTED) */
+                                   rounded once ([Reading, 5.2] measures GQA workloads).  Both
+                                   paths */
   int32_t exact;                /* 1: the exact option ([Summary] bullets on causally safe scales;
                                    [Reading, 4.2]): one exponent per token (and head) for Q, K, V
                                    and dO; V's per-token exponents folded into P on every tile

@@ -136,11 +136,19 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   const size_t hT = (size_t)head * T + s_d;
   const size_t doc0 = (size_t)s_d * rs + (size_t)head * D;   // row 0 of this doc/head
   const uint32_t rs32 = (uint32_t)rs;
+  // K side: the key/value head of this query head ([T,Hk,d] codes, [Hk,T] metadata);
+  // with grouped heads (gsplit = H / Hk) dK and dV leave as fp32 partials, one
+  // per query head of the group, which the group reduction adds and rounds once
+  const int hk = head / (H / p.Hk);
+  const size_t rsk = (size_t)p.Hk * D;
+  const size_t hTk = (size_t)hk * T + s_d;
+  const size_t doc0k = (size_t)s_d * rsk + (size_t)hk * D;
+  const uint32_t rsk32 = (uint32_t)rsk;
   const float c = p.c_log2;
   // per-document bases (uniform); per-lane offsets fit 32 bits (checked on the host)
   const uint8_t* q_doc = a.q_codes + doc0;
   const uint8_t* do_doc = a.do_codes + doc0;
-  const uint8_t* k_doc = a.k_codes + doc0;
+  const uint8_t* k_doc = a.k_codes + doc0k;
   const uint8_t* g_doc = reinterpret_cast<const uint8_t*>(a.g + doc0);
   const uint8_t* x_doc = PATH ? reinterpret_cast<const uint8_t*>(a.q_x + doc0) : nullptr;
   uint8_t* dq_doc = reinterpret_cast<uint8_t*>(a.dq_acc + doc0);
@@ -148,13 +156,13 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   // ---- staging of row tiles: rows row0 + r, clamped to the document's last row.
   // Instruction i of a tile fills tile bytes [1024 i, 1024 i + 1024); lane l
   // brings the 16-byte chunk that the swizzle puts at byte 1024 i + 16 l.
-  auto dma_codes = [&](uint8_t* tile, const uint8_t* src, int row0, int nrows) {
+  auto dma_codes = [&](uint8_t* tile, const uint8_t* src, uint32_t stride, int row0, int nrows) {
     const int ninst = nrows * D / 1024;
     for (int i = wave; i < ninst; i += 4) {
       const int o = i * 1024 + 16 * lane;
       const int r = o / D, slot = (o % D) >> 4;
       const uint32_t gr = (uint32_t)min(row0 + r, L - 1);
-      dma16(src + (gr * rs32 + 16u * (uint32_t)(slot ^ code_key<D>(r))), tile + i * 1024);
+      dma16(src + (gr * stride + 16u * (uint32_t)(slot ^ code_key<D>(r))), tile + i * 1024);
     }
   };
   // the query tiles: instruction k of this wave is tile instruction wave + 4k;
@@ -204,9 +212,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   // ---- per item: the key tile (for K~^T of dQ) and the first query tile
   const int qt_first = CAUSAL ? k0 / BWD_BQ : 0;
   const int qt_end = (L + BWD_BQ - 1) / BWD_BQ;
-  dma_codes(sK, k_doc, k0, BWD_BK);
+  dma_codes(sK, k_doc, rsk32, k0, BWD_BK);
   issue_tile(std::integral_constant<int, 0>{}, qt_first);
-  if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hT + k0 + 32 * tid] : E8M0_BIAS;
+  if (tid < 4) sKeB[tid] = k0 + 32 * tid < L ? (int)a.k_exp[hTk + k0 + 32 * tid] : E8M0_BIAS;
 
   // ---- per wave: K~ (or the mixed path's bf16 K) and V~ block codes as B
   // operands (lane = key); the per-key V~ codes are loaded on the diagonal
@@ -217,7 +225,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   float tqk = 1.f;
   if constexpr (PATH == 1) tqk = a.qk_scale[2] * a.qk_scale[3];
   {
-    const size_t ro = doc0 + (size_t)min(j, L - 1) * rs;
+    const size_t ro = doc0k + (size_t)min(j, L - 1) * rsk;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if constexpr (PATH == 0)
@@ -228,7 +236,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) kb16[s] = __builtin_bit_cast(v8bf, ld16(a.k_x + ro + 16 * s + 8 * hh));
     }
-    const size_t mi = hT + min(j, L - 1);
+    const size_t mi = hTk + min(j, L - 1);
     ke = a.k_exp[mi];
     ve = a.v_exp[mi];
     vke = a.v_key_exp[mi];
@@ -247,7 +255,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
   const int e_key = vke - E8M0_BIAS;
   // per-key V~ codes of this lane's key (B operand of dP on the diagonal block)
   auto vkey = [&](int s2) {
-    const uint8_t* vr = a.v_key_codes + doc0 + (size_t)min(j, L - 1) * rs + 64 * s2 + 16 * hh;
+    const uint8_t* vr = a.v_key_codes + doc0k + (size_t)min(j, L - 1) * rsk + 64 * s2 + 16 * hh;
     return kv ? cat8(ld16(vr), ld16(vr + 32)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
   };
   full_barrier();
@@ -544,7 +552,11 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int jk = k0 + 32 * wave + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-        if (jk < L) {
+        if (jk < L && a.gsplit > 1) {
+          const size_t o = (size_t)(head % a.gsplit) * T * rsk + doc0k + (size_t)jk * rsk + 32 * db + n;
+          a.dk_f32[o] = dk[db][rr] * sc;
+          a.dv_f32[o] = dv[db][rr];
+        } else if (jk < L) {
           const size_t o = doc0 + (size_t)jk * rs + 32 * db + n;
           a.dk_f32[o] = dk[db][rr] * sc;
           a.dv[o] = f32_to_bf16_bits(dv[db][rr]);

@@ -45,8 +45,6 @@ flamia_status validate(const flamia_attn_desc* d) {
   // without the mask: the causal dQ prescale and the exact option (both
   // defined by which keys a query may see) do not apply
   if (!d->causal && (d->causal_dq_scale || d->exact)) return FLAMIA_ERR_INVALID_ARG;
-  // grouped query attention is built for the MXFP8 path only
-  if (d->path == 1 && d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads) return FLAMIA_ERR_UNSUPPORTED;
   // the exact option is built for the MXFP8 path
   if (d->exact && d->path != 0) return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
@@ -64,15 +62,17 @@ flamia_status validate(const flamia_attn_desc* d) {
 
 inline int kv_heads(const flamia_attn_desc* d) { return d->num_kv_heads > 0 ? d->num_kv_heads : d->num_heads; }
 
-// Grouped query attention: the backward item is (document, key tile,
+// Grouped query attention: the MXFP8 backward item is (document, key tile,
 // key/value head) and runs the group's query heads itself.  When that gives
 // fewer than K_BWD_MIN_ITEMS items (two per CU of an MI355X), each group is
 // split over the smallest divisor s of H/Hk that reaches it, and the s fp32
-// partials of dK and dV are reduced afterwards.
+// partials of dK and dV are reduced afterwards.  The mixed path's item is one
+// query head, so its s is H/Hk.
 constexpr int64_t K_BWD_MIN_ITEMS = 512;
 int bwd_group_split(const flamia_attn_desc* d) {
   const int g = d->num_heads / kv_heads(d);
-  if (g == 1 || d->path == 1) return 1;
+  if (g == 1) return 1;
+  if (d->path == 1) return g;     // the mixed path's backward item is one query head
   const int64_t items = (int64_t)(cdiv(d->total_tokens, K_BWD_BK) + d->num_docs) * kv_heads(d);
   for (int s = 1; s < g; ++s)
     if (g % s == 0 && items * s >= K_BWD_MIN_ITEMS) return s;
@@ -339,7 +339,8 @@ flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_
   uint8_t* w = static_cast<uint8_t*>(ws);
   const PlanLayout pl = plan_layout(desc);
   return hip_status(launch_finalize(p, w + b.dq_acc, reinterpret_cast<const int*>(w + b.dq_sigma),
-                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk, p.path == 1,
+                                    reinterpret_cast<const float*>(w + b.dk_f32), dq, dk,
+                                    p.path == 1 && bwd_group_split(desc) == 1,   // else dK came from the group reduction
                                     w + b.dq_part,
                                     reinterpret_cast<const int*>(static_cast<const uint8_t*>(qt->plan) + pl.det_offset),
                                     pl.det_cap, stream));

@@ -66,8 +66,8 @@ def test_invalid_and_unsupported_descriptors(lib, field, value, want):
 
 def test_grouped_query_heads_validation_and_layout(lib):
     """num_kv_heads: 0 or H is MHA; a proper divisor of H shrinks the K-side
-    buffers to Hk heads; a non-divisor is invalid; the mixed path rejects
-    grouping as unsupported."""
+    buffers to Hk heads; a non-divisor is invalid; the mixed path takes
+    grouping with one query head per backward item."""
     T, d = 256, 64
     full = sizes_status(lib, base_desc(num_heads=6))
     assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=6))[1:] == full[1:]
@@ -78,7 +78,9 @@ def test_grouped_query_heads_validation_and_layout(lib):
     # partials need their own staging (dK partials reuse the fp32 dK region)
     assert st == 0 and b == full[2] + 4 * 3 * T * 2 * d
     assert full[1] - q >= 3 * T * 4 * d + 4 * T * 4   # three K-side code tensors, four exponent planes
-    assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=2, path=1))[0] == 2
+    # the mixed path runs one query head per item: fp32 dK, dV partials of each group's 3 heads
+    st_m, _, b_m = sizes_status(lib, base_desc(num_heads=6, num_kv_heads=2, path=1))
+    assert st_m == 0 and b_m == sizes_status(lib, base_desc(num_heads=6, path=1))[2] + 4 * 3 * T * 2 * d
     assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=6, path=1))[0] == 0
     qt = flamia.QTensors()
     dg = base_desc(num_heads=6, num_kv_heads=2)

@@ -33,7 +33,8 @@ def run_gpu(lib, wl, deterministic=False, k=None, v=None):
     q, do = wl.q.to(dev), wl.do.to(dev)
     k = (wl.k if k is None else k).to(dev)
     v = (wl.v if v is None else v).to(dev)
-    call = lib.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard, deterministic=deterministic)
+    call = lib.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard, deterministic=deterministic,
+                            path=wl.path)
     call.step()
     torch.cuda.synchronize()
     return call
@@ -41,7 +42,7 @@ def run_gpu(lib, wl, deterministic=False, k=None, v=None):
 
 def check_against_oracle(call, wl, tag):
     q, k, v, do = np_inputs(wl)
-    num = A.Numerics(hadamard=wl.hadamard)
+    num = A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8")
     ref = A.training_call(q, k, v, do, wl.cu_seqlens, num)
     al = DC.allowances(q, k, v, do, wl.cu_seqlens, num)
     for f in ("q_codes", "k_codes", "v_codes", "v_key_codes"):
@@ -65,6 +66,11 @@ CASES = {
                                                             outlier_scale=20.0, hadamard=True, kv_heads=2),
     "h4_kv1_d128_ragged": lambda: W.small_packed(43, [129, 64, 31, 250], heads=4, head_dim=128, kv_heads=1),
     "h3_kv1_d64_one_tile": lambda: W.small_packed(44, [97], heads=3, head_dim=64, kv_heads=1),
+    # mixed path (NVFP4 scores): one query head per backward item, fp32 partials reduced once
+    "mixed_h4_kv2_d64_ragged": lambda: W.small_packed(45, [1, 70, 33, 130], heads=4, head_dim=64, kv_heads=2,
+                                                      path=1),
+    "mixed_h6_kv2_d128_hadamard": lambda: W.small_packed(46, [256, 100], heads=6, head_dim=128, kv_heads=2,
+                                                         hadamard=True, path=1),
 }
 
 
@@ -78,7 +84,7 @@ def test_gqa_parity_small(gpu_lib, case, det):
     check_against_oracle(call, wl, case)
 
 
-@pytest.mark.parametrize("case", ["h4_kv2_d64_ragged", "h6_kv2_d128_hadamard_outliers"])
+@pytest.mark.parametrize("case", ["h4_kv2_d64_ragged", "h6_kv2_d128_hadamard_outliers", "mixed_h6_kv2_d128_hadamard"])
 def test_gqa_equals_repeated_heads(gpu_lib, case):
     """The grouped call against the plain call on K, V repeated per query
     head, both deterministic: O, row statistics and dQ bit for bit; dK, dV of
