@@ -126,6 +126,26 @@ def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str, kernel
     print(json.dumps(rec))
 
 
+def toolchain(torch):
+    """Versions the numbers depend on (the pages warn that results drift
+    with toolchain versions)."""
+    import subprocess
+    info = {"torch": torch.__version__, "hip_runtime": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
+        info["hipcc"] = next((l.strip() for l in r.stdout.splitlines() if "HIP version" in l), None)
+    except (OSError, subprocess.SubprocessError):
+        info["hipcc"] = None
+    info["device"] = torch.cuda.get_device_name(0)
+    info["arch"] = getattr(torch.cuda.get_device_properties(0), "gcnArchName", None)
+    return info
+
+
 def graph_replay(call, torch, steps: int, warmup: int, flops: int):
     """The same step captured once in a HIP graph and replayed (the pages time
     the call this way): K timed replays after W warm-ups, bracketed by
@@ -348,6 +368,7 @@ def main():
         "quantizer": quant,
         "roofline": roofline,
     }
+    out["toolchain"] = toolchain(torch)
     out["timing"] = timing
     out["eager_ms_per_step"] = eager_ms
     out["graph"] = graph
