@@ -71,6 +71,8 @@ CASES = {
     "hadamard_outliers_d128": lambda: W.small_packed(32, [300, 211], heads=2, head_dim=128,
                                                      outlier_scale=20.0, hadamard=True),
     "ragged_d128_h4": lambda: W.small_packed(33, [129, 64, 31, 250], heads=4, head_dim=128),
+    # zero-length documents at the start, in the middle and at the end of the packed batch
+    "empty_docs_d64": lambda: W.small_packed(37, [0, 45, 0, 0, 100, 33, 0], heads=2, head_dim=64),
 }
 
 
