@@ -35,6 +35,9 @@
  * Errors.  Every function returns a flamia_status and never throws.  Only
  *   host scalars and pointer non-nullness are validated (before anything is
  *   launched); a malformed device-side cu_seqlens is undefined behaviour.
+ *   An empty call (total_tokens = 0, cu_seqlens all zero) is valid: tensor
+ *   and workspace pointers may then be NULL, and only the work-list build
+ *   is launched.
  *   FLAMIA_ERR_HIP reports a failed kernel launch (hipGetLastError).
  * Descriptor.  The same flamia_attn_desc (all fields equal) must be passed
  *   to flamia_quantize, flamia_attn_fwd and flamia_attn_bwd of one call.

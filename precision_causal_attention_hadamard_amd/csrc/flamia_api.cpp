@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "../../include/flamia.h"
 #include "flamia_internal.hpp"
@@ -188,6 +189,15 @@ Fp4Operands fp4_operands(const flamia_qtensors* q) {
 
 flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
 
+// Tensor and workspace pointers may be null only for an empty call (T = 0),
+// which launches nothing but the work-list build.
+bool tensors_ok(const flamia_attn_desc* d, std::initializer_list<const void*> ps) {
+  if (d->total_tokens == 0) return true;
+  for (const void* p : ps)
+    if (!p) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,7 +253,7 @@ flamia_status flamia_quantize(const flamia_attn_desc* desc, const void* q, const
                               const flamia_qtensors* out, hipStream_t stream) {
   flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!q || !k || !v || !qt_complete(desc, out)) return FLAMIA_ERR_INVALID_ARG;
+  if (!tensors_ok(desc, {q, k, v}) || !qt_complete(desc, out)) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   s = flamia_plan_build(desc, out, stream);
   if (s != FLAMIA_OK) return s;
@@ -261,7 +271,7 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
   (void)ws;
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !o || !row_max || !row_sum) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {o, row_max, row_sum})) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   return hip_status(launch_attn_fwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
                                     qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp,
@@ -273,7 +283,7 @@ flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qt
                                    hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !o || !row_max || !row_sum || !dout || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {o, row_max, row_sum, dout, ws})) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
@@ -289,7 +299,7 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
                                    void* ws, hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !dk || !dv || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {dk, dv, ws})) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
@@ -332,7 +342,7 @@ flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_
                                      void* dk, void* ws, hipStream_t stream) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !dq || !dk || !ws) return FLAMIA_ERR_INVALID_ARG;
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {dq, dk, ws})) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
@@ -351,7 +361,7 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
                               void* dk, void* dv, void* ws, hipStream_t stream) {
   flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (!qt_complete(desc, qt) || !o || !row_max || !row_sum || !dout || !dq || !dk || !dv || !ws)
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {o, row_max, row_sum, dout, dq, dk, dv, ws}))
     return FLAMIA_ERR_INVALID_ARG;
   s = flamia_attn_bwd_prep(desc, qt, o, row_max, row_sum, dout, ws, stream);
   if (s != FLAMIA_OK) return s;

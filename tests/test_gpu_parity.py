@@ -189,3 +189,18 @@ def test_parity_mixed_path(gpu_lib, case):
     check_nvfp4(call, wl)
     m = check_outputs(call, ref)
     print(f"[parity] {case}: " + ", ".join(f"{k} rel={v[0]:.2e} cos={v[1]:.6f}" for k, v in m.items()), flush=True)
+
+
+def test_empty_call(gpu_lib):
+    """No tokens at all (one or several empty documents): every entry point
+    succeeds with the empty tensors torch hands over, and the work lists are
+    empty."""
+    dev = torch.device("cuda")
+    for cu in ([0, 0], [0, 0, 0, 0]):
+        z = torch.empty(0, 2, 64, dtype=torch.bfloat16, device=dev)
+        call = gpu_lib.TrainingCall(z, z, z, z, cu)
+        call.step()
+        torch.cuda.synchronize()
+        fwd, bwd = call.plan_lists()
+        assert len(fwd) == 0 and len(bwd) == 0
+        assert call.o.numel() == 0 and call.dq.numel() == 0
