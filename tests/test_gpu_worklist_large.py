@@ -105,3 +105,30 @@ def test_call_parity_on_a_large_worklist(gpu_lib):
         m = DCMP.check_outputs(outs, ref, allow, "large worklist", ("o", "dq", "dk", "dv"))
         print(f"[worklist] doc {doc} (L={e - s}): "
               + ", ".join(f"{n} rel={v[1]:.2e} cos={v[2]:.6f}" for n, v in m.items()), flush=True)
+
+
+def test_call_parity_large_worklist_noncausal_deterministic_grouped(gpu_lib):
+    """The multi-workgroup lists under the other options at once: no causal
+    mask, deterministic dQ (per-document slot bases over 8000+ documents) and
+    grouped key/value heads; oracle slices of a long and a single-token
+    document."""
+    lens = [500] + [1] * 8200 + [260]
+    wl = W.small_packed(63, lens, heads=4, head_dim=64, kv_heads=2)
+    dev = torch.device("cuda")
+    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
+    call = gpu_lib.TrainingCall(q, k, v, do, wl.cu_seqlens, causal=False, deterministic=True)
+    call.step()
+    torch.cuda.synchronize()
+    assert call.plan_error_word() == 0
+    cu = wl.cu_seqlens
+    for doc in (0, 3000, len(lens) - 1):
+        s, e = cu[doc], cu[doc + 1]
+        arrs = [t[s:e].float().numpy().astype(np.float64) for t in (wl.q, wl.k, wl.v, wl.do)]
+        num = A.Numerics(causal=False)
+        ref = A.training_call(*arrs, [0, e - s], num)
+        allow = DC.allowances(*arrs, [0, e - s], num)
+        outs = {n: getattr(call, n)[s:e].float().cpu().numpy() for n in ("o", "dq", "dk", "dv")}
+        m = DCMP.check_outputs(outs, ref, allow, "large worklist, non-causal, deterministic, grouped",
+                               ("o", "dq", "dk", "dv"))
+        print(f"[worklist] non-causal det gqa doc {doc} (L={e - s}): "
+              + ", ".join(f"{n} rel={v[1]:.2e} cos={v[2]:.6f}" for n, v in m.items()), flush=True)
