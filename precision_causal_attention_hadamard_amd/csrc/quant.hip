@@ -10,8 +10,10 @@
 // optional fp32 Hadamard butterflies on Q and K, amax over the block, the
 // round-up exponent, E4M3 codes; for V also the per-key exponents, per-key
 // codes and the per-query fold reference (prefix max of the per-key
-// exponents inside the block; the block exponent when the call is not causal).  [Summary, §3.1 Token-Block Scaling; §3.2
-// Causally Safe Scales; §4.3 Ablation Study]; [Reading, 4.4] first bullet.
+// exponents inside the block; the block exponent when the call is not
+// causal).  [Summary, §3.1 Token-Block Scaling; §3.2 Causally Safe Scales;
+// §4.3 Ablation Study]; [Reading, 4.4] first bullet.  Code rows leave as
+// whole rows per store instruction through a wave-private LDS tile.
 // Exact option: one exponent per token instead of per block (V's block and
 // per-key codes then coincide), and K's in-block prefix maximum of the
 // per-token exponents for the causal dQ prescale.
