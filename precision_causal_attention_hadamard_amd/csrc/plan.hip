@@ -3,23 +3,24 @@
 // The pages build the schedule once per microbatch on the GPU with a
 // fixed-pass sort and hand items, costliest first, to the grid
 // ([Summary, §3.6.2 Load-Balanced Scheduling]; [Reading, 4.4] last bullet).
-// Here one workgroup per list enumerates every (document, tile), forms a 64-bit key
+// Here each (document, tile) gets a unique 64-bit key
 //   (COST_MAX - c) << 44 | doc << 20 | tile
-// and bitonic-sorts the keys (in LDS; within one wave for lists of at most
-// 64 tiles).  Lists that do not fit one workgroup's LDS (more than
-// PLAN_MAX_TILES tiles) take a multi-workgroup path: the keys are enumerated
-// into a padded array (tile t of document d at slot floor(cu[d] / 128) + d + t,
-// which never overlaps the next document's slots; empty slots hold the
-// largest key), runs of PLAN_RUN keys are bitonic-sorted in LDS, and
-// merge passes double the run length (each output element finds its source
-// by a co-rank binary search over the two runs), so the order is again the
-// single correct one.  c is the tile's cost in the forward list and the cost of the
-// document's costliest (first) key tile in the backward list, which keeps a
-// document's key tiles together (longest document first, tiles in order, so
-// still costliest first inside it) for L2 reuse of its query rows.  The key
-// is unique, so the order is the single correct one.  A tile
-// later expands to num_heads consecutive grid items (head ascending).  The
-// attention kernels read item blockIdx.x / H of the sorted list; the
+// where c is the tile's cost in the forward list and the cost of the
+// document's costliest (first) key tile in the backward list; the latter
+// keeps a document's key tiles together (longest document first, tiles in
+// order, so still costliest first inside it) for L2 reuse of its query rows.
+// Every key is unique, so exactly one order is correct.
+//   * Lists of at most PLAN_MAX_TILES tiles: one workgroup per list
+//     enumerates the keys and bitonic-sorts them in LDS (within one wave for
+//     at most 64 tiles).
+//   * Longer lists: the keys are enumerated into a padded array (tile t of
+//     document d at slot floor(cu[d] / 128) + d + t, which never reaches the
+//     next document's first slot; empty slots hold the largest key), runs of
+//     PLAN_RUN keys are bitonic-sorted in LDS, and merge passes double the run
+//     length (each output element finds its source by a co-rank binary search
+//     over the two runs).
+// A tile later expands to num_heads consecutive grid items (head ascending).
+// The attention kernels read item blockIdx.x / H of the sorted list; the
 // hardware dispatcher hands workgroups out in index order, which plays the
 // role of the pages' dynamic fetch.
 //
