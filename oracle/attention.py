@@ -93,23 +93,36 @@ def _out(x, num: Numerics):
     return formats.bf16_round(x) if num.round_outputs else np.asarray(x, dtype=np.float64)
 
 
-def _ds_quantize(ds: np.ndarray, valid: np.ndarray, rule: str):
-    """dS^ of one (document, head): one exponent per 32 x 32 block from the
-    block's max-abs over valid entries (masked entries count as 0)."""
-    L = ds.shape[0]
+def ds_block_quantize(ds: np.ndarray, valid: np.ndarray, rule: str = "roundup"):
+    """dS^ of one (document, head) ([Summary, §3.3], second bullet; [Reading,
+    4.3]): the document-local 32 x 32 blocks (query block I, key block J) of
+    dS each get one exponent, the round-up exponent of the block's max-abs
+    taken over its valid entries (masked entries count as 0), and every valid
+    entry becomes E4M3(dS 2^-e) 2^e.  Returns ``(dS^, e)`` with ``e[I, J]``
+    the exponent of block (I, J), or -128 where the block holds no valid
+    entry (such blocks stay zero).  ``ds`` may be a rectangular slice whose
+    first row and column start blocks."""
+    Lr, Lc = ds.shape
     out = np.zeros_like(ds)
+    exps = np.full((-(-Lr // BLOCK), -(-Lc // BLOCK)), -128, dtype=np.int64)
     ex_rule = formats.EXPONENT_RULES[rule]
-    for i0 in range(0, L, BLOCK):
-        for j0 in range(0, L, BLOCK):
+    for bi, i0 in enumerate(range(0, Lr, BLOCK)):
+        for bj, j0 in enumerate(range(0, Lc, BLOCK)):
             blk = ds[i0:i0 + BLOCK, j0:j0 + BLOCK]
             v = valid[i0:i0 + BLOCK, j0:j0 + BLOCK]
             if not v.any():
                 continue
             e = ex_rule(np.max(np.abs(np.where(v, blk, 0.0))))
+            exps[bi, bj] = e
             q = formats.e4m3_encode(np.ldexp(np.where(v, blk, 0.0), -e), saturate=(rule == "floor"))
             out[i0:i0 + BLOCK, j0:j0 + BLOCK] = np.where(
                 v, np.ldexp(formats.e4m3_decode(q), e), 0.0)
-    return out
+    return out, exps
+
+
+def _ds_quantize(ds: np.ndarray, valid: np.ndarray, rule: str):
+    """dS^ values alone (see ds_block_quantize)."""
+    return ds_block_quantize(ds, valid, rule)[0]
 
 
 def exact_fold_reference(v_exp_key, L: int):
@@ -227,6 +240,44 @@ def backward_doc(fw, qd, kd, vblk, vkey, dod, o_out, s32, num: Numerics):
     zeroed = int(np.count_nonzero(nz & (dsq == 0)))
     return dict(D=D, ds=ds, dsq=dsq, dsq_k=dsq_k, dq=dq, dk=dk, dv=dv,
                 ds_nonzero=int(np.count_nonzero(nz)), ds_zeroed=zeroed)
+
+
+def dq_prescale(do_exp, k_exp, v_exp, cu_seqlens, head_dim: int, causal_dq_scale: bool = False,
+                exact: bool = False):
+    """Power-of-two prescale of the fp16 dQ accumulator ([Reading, 4.4] third
+    bullet: dQ partials are reduced in FP16 after a data-dependent power-of-two
+    scale; [Summary] bullets on the optional causal dQ scale).  For query
+    token i of a document, with exponents as integers ([H, T] for dO, [Hk, T]
+    for K and V; query head h reads key/value head h // (H / Hk)):
+
+        sigma_i = e_dO(i) + E_V + E_K + log2(d) + 13
+
+    E_V, E_K: the largest V and K exponents over the document (default), over
+    the tokens j <= i (``causal_dq_scale``, or per token with the exact
+    option, whose exponents are per token).  Since every |dS~_ij| sums to at
+    most 2.2 d 448^2 2^(e_dO + E_V) over a row (P / l sums to 1, |dP - D| is
+    at most twice a d-term dot product of codes, E4M3 rounding adds 1/16) and
+    |K~| <= 448 2^E_K, every partial sum of sum_j dS~_ij K~_j scaled by
+    2^-sigma stays below 2^15, inside fp16.  Returns int64 [H, T]."""
+    do_exp = np.asarray(do_exp, np.int64)
+    k_exp = np.asarray(k_exp, np.int64)
+    v_exp = np.asarray(v_exp, np.int64)
+    H, T = do_exp.shape
+    group = H // k_exp.shape[0]
+    lg = int(np.log2(head_dim))
+    out = np.zeros((H, T), dtype=np.int64)
+    for s, e in doc_bounds(cu_seqlens):
+        if e == s:
+            continue
+        for h in range(H):
+            ek, ev = k_exp[h // group, s:e], v_exp[h // group, s:e]
+            if causal_dq_scale or exact:
+                # (block exponents repeat over a block, so this is the max over blocks J <= I)
+                ek, ev = np.maximum.accumulate(ek), np.maximum.accumulate(ev)
+            else:
+                ek, ev = np.full(e - s, ek.max()), np.full(e - s, ev.max())
+            out[h, s:e] = do_exp[h, s:e] + ek + ev + lg + 13
+    return out
 
 
 def training_call(q, k, v, do, cu_seqlens, num: Numerics | None = None):
