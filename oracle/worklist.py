@@ -3,22 +3,16 @@
 The pages build the schedule once per microbatch on the GPU: items are sorted
 by cost, longest first, and handed to a persistent grid; skewed loads (longest
 document at least 4x the mean) fetch work dynamically
-([Summary, §3.6.2 Load-Balanced Scheduling]; [Reading, 4.4], last bullet
-"GPU 端调度").  The cost model and tie-break are not given; the reading taken
+([Summary, §3.6.2 Load-Balanced Scheduling]; [Reading, 4.4], last bullet).
+The cost model and tie-break are not given; the reading taken
 here:
 
 * forward item = (document, query tile t, head); cost = number of key tiles
   the causal query tile touches: ``floor((min((t+1)*Bq, L) - 1) / Bk) + 1``;
 * backward item = (document, key tile u, head); cost = number of query tiles
   at or after the key tile: ``ceil(L/Bq) - floor(u*Bk/Bq)``;
-* forward order: cost descending, then document, tile, head ascending;
-* backward order: longest document first -- by the cost of its costliest
-  (first) key tile -- then document, tile, head ascending.  A document's key
-  tiles stay together and, tile 0 being its costliest, still come longest
-  first inside it; on gfx950 that keeps the tiles that share a document's
-  query rows together in L2 (measured: 3.9% faster backward on the packed
-  lognormal workload, no change on equal documents), where a tile-level sort
-  interleaves documents.
+* both lists: cost descending, then document, tile, head ascending (the
+  pages sort the work items by cost, costliest first).
 Every key is unique, so exactly one order is correct.
 """
 
@@ -59,12 +53,10 @@ def bwd_items(cu_seqlens, heads: int, bq: int, bk: int, causal: bool = True):
     items = []
     for doc, (s, e) in enumerate(doc_bounds(cu_seqlens)):
         L = e - s
-        first = bwd_cost(0, L, bq, bk, causal) if L else 0
         for u in range(_cdiv(L, bk)):
             c = bwd_cost(u, L, bq, bk, causal)
-            items.extend((doc, u, h, c, first) for h in range(heads))
-    items.sort(key=lambda it: (-it[4], it[0], it[1], it[2]))
-    return [it[:4] for it in items]
+            items.extend((doc, u, h, c) for h in range(heads))
+    return sorted(items, key=lambda it: (-it[3], it[0], it[1], it[2]))
 
 
 def is_skewed(cu_seqlens) -> bool:

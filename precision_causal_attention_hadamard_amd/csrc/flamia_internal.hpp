@@ -13,17 +13,18 @@ constexpr int COST_MAX = (1 << 20) - 1;   // costs must stay below this
 
 // Plan words: [0] forward items, [1] backward items, [2] deterministic-mode
 // error word (1: the documents need more dQ partial slots than the
-// workspace holds), [3] reserved.
+// workspace holds), [3] backward dispatch items (= [1]).
 struct PlanLayout {
   size_t fwd_offset;   // bytes from the plan base to the forward (doc, tile) list
-  size_t bwd_offset;
+  size_t bwd_offset;   // the backward list in the pages' order (cost descending)
+  size_t disp_offset;  // the backward's dispatch order: the same items, grouped by document
   size_t det_offset;   // int [num_docs + 1]: first dQ partial step of each document (per head)
   int cap_fwd;         // ceil(T / FWD_BQ) + num_docs
   int cap_bwd;         // ceil(T / BWD_BK) + num_docs
   int det_cap;         // deterministic mode: dQ partial steps per head the workspace holds
   int cap_r;           // lists beyond PLAN_MAX_TILES: padded key slots per list (a multiple of
                        // PLAN_RUN), else 0
-  size_t keys_offset;  // with cap_r: two key buffers of 2 x cap_r uint64 (both lists)
+  size_t keys_offset;  // with cap_r: two key buffers of 3 x cap_r uint64 (the three lists)
   size_t bytes;
 };
 

@@ -5,10 +5,15 @@
 // ([Summary, §3.6.2 Load-Balanced Scheduling]; [Reading, 4.4] last bullet).
 // Here each (document, tile) gets a unique 64-bit key
 //   (COST_MAX - c) << 44 | doc << 20 | tile
-// where c is the tile's cost in the forward list and the cost of the
-// document's costliest (first) key tile in the backward list; the latter
-// keeps a document's key tiles together (longest document first, tiles in
-// order, so still costliest first inside it) for L2 reuse of its query rows.
+// where c is the tile's cost; sorting the keys gives the pages' order: cost
+// descending, then document, then tile.  Three lists are built:
+//   0  forward query tiles, that order;
+//   1  backward key tiles, that order (the published schedule);
+//   2  the backward's dispatch order, a permutation of list 1: c is the cost
+//      of the document's costliest (first) key tile, so a document's key
+//      tiles stay together (longest document first, tiles in order, so still
+//      costliest first inside it) and its query rows are reused from L2 while
+//      its tiles run.
 // Every key is unique, so exactly one order is correct.
 //   * Lists of at most PLAN_MAX_TILES tiles: one workgroup per list
 //     enumerates the keys and bitonic-sorts them in LDS (within one wave for
@@ -20,9 +25,9 @@
 //     length (each output element finds its source by a co-rank binary search
 //     over the two runs).
 // A tile later expands to num_heads consecutive grid items (head ascending).
-// The attention kernels read item blockIdx.x / H of the sorted list; the
-// hardware dispatcher hands workgroups out in index order, which plays the
-// role of the pages' dynamic fetch.
+// The forward reads item blockIdx.x / H of list 0, the backward of list 2;
+// the hardware dispatcher hands workgroups out in index order, which plays
+// the role of the pages' dynamic fetch.
 //
 // Costs (number of tile pairs the causal tile touches):
 //   forward  query tile t of a document of length L: floor((min((t+1)Bq, L)-1)/Bk) + 1
@@ -102,21 +107,28 @@ __device__ static unsigned long long wave_bitonic(unsigned long long key) {
 static_assert(FWD_BQ == BWD_BK, "both lists count 128-token tiles");
 constexpr int PLAN_TILE = FWD_BQ;
 
-// Sort key of tile t of document d (L tokens) in the forward or backward list.
-__device__ __forceinline__ unsigned long long tile_key(bool fwd, bool causal, int d, int t, int L, int bq, int bk) {
+constexpr int PLAN_LISTS = 3;          // forward, backward, backward dispatch
+
+// Plan word holding the tile count of list `lst` (word 2 is the
+// deterministic-mode error word).
+__device__ __forceinline__ int count_slot(int lst) { return lst == 2 ? 3 : lst; }
+
+// Sort key of tile t of document d (L tokens) in list `lst`.
+__device__ __forceinline__ unsigned long long tile_key(int lst, bool causal, int d, int t, int L, int bq, int bk) {
   int cost;
   if (!causal) {
-    cost = fwd ? (L + bk - 1) / bk : (L + bq - 1) / bq;
-  } else if (fwd) {
+    cost = lst == 0 ? (L + bk - 1) / bk : (L + bq - 1) / bq;
+  } else if (lst == 0) {
     const int e = min((t + 1) * bq, L);
     cost = (e - 1) / bk + 1;
-  } else {
+  } else if (lst == 1) {
     cost = (L + bq - 1) / bq - (t * bk) / bq;
+  } else {
+    // dispatch order: every tile of a document carries the cost of its
+    // costliest (first) key tile
+    cost = (L + bq - 1) / bq;
   }
-  // backward: a document's tiles share the key of its costliest (first)
-  // tile, so they stay together, longest document first, tiles in order
-  const int kcost = fwd ? cost : (L + bq - 1) / bq;
-  return ((unsigned long long)(COST_MAX - kcost) << 44) | ((unsigned long long)d << 20) | (unsigned long long)t;
+  return ((unsigned long long)(COST_MAX - cost) << 44) | ((unsigned long long)d << 20) | (unsigned long long)t;
 }
 
 __device__ __forceinline__ int2 key_item(unsigned long long key) {
@@ -141,9 +153,10 @@ __device__ static void lds_bitonic(unsigned long long* keys, int n2) {
   }
 }
 
-__device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool fwd, bool causal, int bq, int bk,
+__device__ static void build_sorted(const int* __restrict__ cu, int ndocs, int lst, bool causal, int bq, int bk,
                                     unsigned long long* keys, int* wsum, int* count_out,
                                     int2* __restrict__ out) {
+  const bool fwd = lst == 0;
   const int tid = threadIdx.x;
   int n_tiles = 0;
   // enumerate tiles, chunk of PLAN_THREADS documents at a time
@@ -156,7 +169,7 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
     }
     int total;
     const int first = n_tiles + block_inclusive_scan(n, wsum, total) - n;
-    for (int t = 0; t < n; ++t) keys[first + t] = tile_key(fwd, causal, d, t, L, bq, bk);
+    for (int t = 0; t < n; ++t) keys[first + t] = tile_key(lst, causal, d, t, L, bq, bk);
     n_tiles += total;
   }
   __syncthreads();
@@ -178,7 +191,7 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
 }
 
 // Workgroup 0 builds the forward list, workgroup 1 the backward list and the
-// deterministic-mode step prefix: document d's dQ partial steps (per head)
+// deterministic-mode step prefix, workgroup 2 the backward dispatch order: document d's dQ partial steps (per head)
 // start at det_base[d]; a document of L tokens has n = ceil(L / BWD_BK) key
 // tiles and Q = ceil(L / BWD_BQ) query tiles, and key tile u visits query
 // tiles 2u .. Q-1, so n Q - n (n - 1) steps (n Q without the mask).  Word 2
@@ -188,21 +201,22 @@ __device__ static void build_sorted(const int* __restrict__ cu, int ndocs, bool 
 // deterministic mode (det_cap > 0).
 __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restrict__ cu, int ndocs, int causal,
                                                             int large, int* counts, int2* fwd_items,
-                                                            int2* bwd_items, float* qk_scale, int* det_base,
-                                                            int det_cap) {
+                                                            int2* bwd_items, int2* disp_items, float* qk_scale,
+                                                            int* det_base, int det_cap) {
   __shared__ unsigned long long keys[PLAN_MAX_TILES];
   __shared__ int wsum[PLAN_WAVES];
   __shared__ long long wsum64[PLAN_WAVES];
-  const bool fwd = blockIdx.x == 0;
+  const int lst = blockIdx.x;
+  const bool fwd = lst == 0;
   if (large) {                    // the fill kernel adds the counts
-    if (threadIdx.x == 0) counts[fwd ? 0 : 1] = 0;
+    if (threadIdx.x == 0) counts[count_slot(lst)] = 0;
   } else {
-    build_sorted(cu, ndocs, fwd, causal != 0, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
-                 counts + (fwd ? 0 : 1), fwd ? fwd_items : bwd_items);
+    build_sorted(cu, ndocs, lst, causal != 0, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK, keys, wsum,
+                 counts + count_slot(lst), lst == 0 ? fwd_items : lst == 1 ? bwd_items : disp_items);
   }
-  if (fwd && threadIdx.x == 0) counts[3] = 0;
-  if (!fwd && det_cap == 0 && threadIdx.x == 0) counts[2] = 0;
-  if (!fwd && det_cap > 0) {
+  if (lst != 1) return;
+  if (det_cap == 0 && threadIdx.x == 0) counts[2] = 0;
+  if (det_cap > 0) {
     long long done = 0;
     for (int base = 0; base < ndocs; base += PLAN_THREADS) {
       const int d = base + threadIdx.x;
@@ -223,7 +237,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restric
     }
   }
   // mixed path: clear the tensor-amax slots before the amax pass runs
-  if (fwd && qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
+  if (qk_scale != nullptr && threadIdx.x < 2) qk_scale[threadIdx.x] = 0.f;
 }
 
 // ---- multi-workgroup path (lists of more than PLAN_MAX_TILES tiles)
@@ -232,13 +246,14 @@ __global__ void __launch_bounds__(PLAN_THREADS) plan_kernel(const int* __restric
 // increasing in d, and slot(d + 1) - slot(d) >= ceil(L_d / 128).
 __device__ __forceinline__ int doc_slot(const int* __restrict__ cu, int d) { return cu[d] / PLAN_TILE + d; }
 
-// Keys of both lists into padded arrays of cap_r slots (blockIdx.y = list);
-// each workgroup adds its number of real tiles to the list's count.
+// Keys of the three lists into padded arrays of cap_r slots (blockIdx.y =
+// list); each workgroup adds its number of real tiles to the list's count.
 __global__ void __launch_bounds__(256) plan_fill_kernel(const int* __restrict__ cu, int ndocs, int causal,
                                                         unsigned long long* __restrict__ keys, int cap_r,
                                                         int* counts) {
   __shared__ int wcount[4];
-  const bool fwd = blockIdx.y == 0;
+  const int lst = blockIdx.y;
+  const bool fwd = lst == 0;
   const int s = blockIdx.x * 256 + threadIdx.x;
   unsigned long long key = ~0ull;
   if (s < cap_r && s < doc_slot(cu, ndocs - 1) + (cu[ndocs] - cu[ndocs - 1] + PLAN_TILE - 1) / PLAN_TILE) {
@@ -250,7 +265,7 @@ __global__ void __launch_bounds__(256) plan_fill_kernel(const int* __restrict__ 
     }
     const int L = cu[lo + 1] - cu[lo], t = s - doc_slot(cu, lo);
     if (t < (L + PLAN_TILE - 1) / PLAN_TILE)
-      key = tile_key(fwd, causal != 0, lo, t, L, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK);
+      key = tile_key(lst, causal != 0, lo, t, L, fwd ? FWD_BQ : BWD_BQ, fwd ? FWD_BK : BWD_BK);
   }
   if (s < cap_r) keys[(size_t)blockIdx.y * cap_r + s] = key;
   const int n = __popcll(__ballot(key != ~0ull));
@@ -258,7 +273,7 @@ __global__ void __launch_bounds__(256) plan_fill_kernel(const int* __restrict__ 
   __syncthreads();
   if (threadIdx.x == 0) {
     const int tot = wcount[0] + wcount[1] + wcount[2] + wcount[3];
-    if (tot) atomicAdd(counts + blockIdx.y, tot);
+    if (tot) atomicAdd(counts + count_slot(lst), tot);
   }
 }
 
@@ -297,12 +312,14 @@ __global__ void __launch_bounds__(256) plan_merge_kernel(const unsigned long lon
   dst[lb0 + g] = take_a ? A[i] : B[j];
 }
 
-// Sorted keys -> (doc, tile) items of both lists.
+// Sorted keys -> (doc, tile) items of the three lists.
 __global__ void __launch_bounds__(256) plan_extract_kernel(const unsigned long long* __restrict__ keys, int cap_r,
-                                                           int cap, int2* fwd_items, int2* bwd_items) {
+                                                           int cap, int2* fwd_items, int2* bwd_items,
+                                                           int2* disp_items) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= cap) return;
-  (blockIdx.y == 0 ? fwd_items : bwd_items)[i] = key_item(keys[(size_t)blockIdx.y * cap_r + i]);
+  (blockIdx.y == 0 ? fwd_items : blockIdx.y == 1 ? bwd_items : disp_items)[i] =
+      key_item(keys[(size_t)blockIdx.y * cap_r + i]);
 }
 
 hipError_t launch_plan(const int* cu, int ndocs, int causal, void* plan, const PlanLayout& pl, float* qk_scale,
@@ -311,22 +328,24 @@ hipError_t launch_plan(const int* cu, int ndocs, int causal, void* plan, const P
   int* counts = reinterpret_cast<int*>(base);
   int2* fwd_items = reinterpret_cast<int2*>(base + pl.fwd_offset);
   int2* bwd_items = reinterpret_cast<int2*>(base + pl.bwd_offset);
-  hipLaunchKernelGGL(plan_kernel, dim3(2), dim3(PLAN_THREADS), 0, stream, cu, ndocs, causal, pl.cap_r > 0 ? 1 : 0,
-                     counts, fwd_items, bwd_items, qk_scale, reinterpret_cast<int*>(base + pl.det_offset), pl.det_cap);
+  int2* disp_items = reinterpret_cast<int2*>(base + pl.disp_offset);
+  hipLaunchKernelGGL(plan_kernel, dim3(PLAN_LISTS), dim3(PLAN_THREADS), 0, stream, cu, ndocs, causal,
+                     pl.cap_r > 0 ? 1 : 0, counts, fwd_items, bwd_items, disp_items, qk_scale,
+                     reinterpret_cast<int*>(base + pl.det_offset), pl.det_cap);
   if (pl.cap_r == 0) return hipGetLastError();
   // cap_r: a multiple of PLAN_RUN holding cap_fwd = cap_bwd slots
   unsigned long long* k0 = reinterpret_cast<unsigned long long*>(base + pl.keys_offset);
-  unsigned long long* k1 = k0 + 2 * (size_t)pl.cap_r;
-  const dim3 g256((unsigned)((pl.cap_r + 255) / 256), 2);
+  unsigned long long* k1 = k0 + PLAN_LISTS * (size_t)pl.cap_r;
+  const dim3 g256((unsigned)((pl.cap_r + 255) / 256), PLAN_LISTS);
   hipLaunchKernelGGL(plan_fill_kernel, g256, dim3(256), 0, stream, cu, ndocs, causal, k0, pl.cap_r, counts);
-  hipLaunchKernelGGL(plan_sort_runs_kernel, dim3((unsigned)(pl.cap_r / PLAN_RUN), 2), dim3(PLAN_THREADS), 0,
+  hipLaunchKernelGGL(plan_sort_runs_kernel, dim3((unsigned)(pl.cap_r / PLAN_RUN), PLAN_LISTS), dim3(PLAN_THREADS), 0,
                      stream, k0, pl.cap_r);
   for (int w = PLAN_RUN; w < pl.cap_r; w *= 2) {
     hipLaunchKernelGGL(plan_merge_kernel, g256, dim3(256), 0, stream, k0, k1, pl.cap_r, w);
     std::swap(k0, k1);
   }
-  hipLaunchKernelGGL(plan_extract_kernel, dim3((unsigned)((pl.cap_fwd + 255) / 256), 2), dim3(256), 0, stream, k0,
-                     pl.cap_r, pl.cap_fwd, fwd_items, bwd_items);
+  hipLaunchKernelGGL(plan_extract_kernel, dim3((unsigned)((pl.cap_fwd + 255) / 256), PLAN_LISTS), dim3(256), 0,
+                     stream, k0, pl.cap_r, pl.cap_fwd, fwd_items, bwd_items, disp_items);
   return hipGetLastError();
 }
 

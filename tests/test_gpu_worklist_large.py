@@ -3,7 +3,7 @@ tokens), on the GPU through the C ABI.
 
 The multi-workgroup path (padded key enumeration, runs of 2048 keys sorted in
 LDS, merge passes) must give exactly the oracle's longest-first lists --
-causal and not -- including the pages' stress case of 131072 single-token
+causal and not -- and the backward's dispatch permutation of them, including the pages' stress case of 131072 single-token
 documents ([Reading, 4.4] last bullet times the GPU schedule build there);
 and a whole call on a workload that needs it must meet the parity bar on
 sampled document/head slices (documents are independent).
@@ -18,6 +18,7 @@ from oracle import attention as A
 from oracle import decisions as DC
 from oracle import worklist as WL
 from precision_causal_attention_hadamard_amd import workloads as W
+from test_gpu_parity import check_dispatch
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +43,7 @@ def check_lists(lib, call, cu, causal):
     want_b = np.array([(d, t) for d, t, h, c in WL.bwd_items(cu, 1, bbq, bbk, causal)], dtype=np.int64)
     np.testing.assert_array_equal(fwd.numpy().astype(np.int64), want_f)
     np.testing.assert_array_equal(bwd.numpy().astype(np.int64), want_b)
+    check_dispatch(bwd.numpy(), call.plan_dispatch().numpy())
 
 
 def mixed_docs(seed):

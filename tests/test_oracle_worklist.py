@@ -36,17 +36,21 @@ def test_worklist_is_sorted_permutation():
     b = worklist.bwd_items(cu, 3, 64, 128)
     assert len(b) == 3 * (1 + 3 + 0 + 10 + 1)
     assert len({(d, t, h) for d, t, h, _ in b}) == len(b)
-    # backward: documents by their costliest (first) tile, descending; inside a
-    # document tiles ascending, i.e. costs descending, heads innermost
-    docs = [d for d, _, _, _ in b]
-    firsts = {d: max(c for dd, _, _, c in b if dd == d) for d in set(docs)}
-    order = [d for i, d in enumerate(docs) if i == 0 or docs[i - 1] != d]
-    assert len(order) == len(set(order))                      # each document's items are contiguous
-    assert [firsts[d] for d in order] == sorted(firsts.values(), reverse=True)
-    for d in order:
-        mine = [(t, h, c) for dd, t, h, c in b if dd == d]
-        assert mine == sorted(mine, key=lambda x: (x[0], x[1]))
-        assert [c for _, _, c in mine] == sorted((c for _, _, c in mine), reverse=True)
+    # backward: the pages' order too -- cost descending, then document, tile, head
+    bc = [c for _, _, _, c in b]
+    assert bc == sorted(bc, reverse=True)
+    assert b == sorted(b, key=lambda it: (-it[3], it[0], it[1], it[2]))
+
+
+def test_backward_list_interleaves_documents_by_cost():
+    """Cost descending across documents: the cheap last tile of a long
+    document comes after the costliest tile of a shorter one (a document-
+    grouped order would fail this)."""
+    cu = [0, 1024, 1024 + 300]          # 8 key tiles (16 query tiles) and 3 key tiles (5 query tiles)
+    b = [(d, t) for d, t, h, c in worklist.bwd_items(cu, 1, 64, 128)]
+    assert b.index((1, 0)) < b.index((0, 7))
+    assert b[:2] == [(0, 0), (0, 1)]
+    assert [c for *_, c in worklist.bwd_items(cu, 1, 64, 128)] == [16, 14, 12, 10, 8, 6, 5, 4, 3, 2, 1]
 
 
 def test_skew_rule():
