@@ -6,22 +6,14 @@ value) and cosine >= 0.999 per output.  Where admissible fp32 evaluations can
 take a quantized decision either way, the element-wise part is applied to what
 is unique:
 * O, dV: |got - want| <= 2e-2 max|want| + allowance (the width the admissible
-  decisions span; zero for almost every element);
-* dQ: a decision that moves O shifts D_i, which moves dQ_i along a known
-  direction g_i (|coefficient| <= e(D_i)), and each ambiguous dS^ code of the
-  row moves it along s32 K~_j (coefficient within the code range the fp32
-  bound admits); the coefficients are fitted per row (the D shift in closed
-  form, and for rows still above the bar jointly with the row's dS^
-  decisions by bounded least squares) and the remainder is held to 2e-2
-  max|want| on every element;
-* dK: likewise with the ambiguous dS^ codes of the key row (along s32 Q~_i).
-On workloads with outlier channels (a few channels x20), a dS^ code decision
-in a short row moves dQ_i by a sizable part of the tensor's maximum (the keys'
-outlier channels multiply it), and the matrix cores' FP8 products are not
-accumulated to fp32 precision, so such decisions are not rare there; for those
-workloads the dQ remainder is held to one E4M3 step (1/8) of max|want| with at
-most 1% of rows beyond 2e-2 -- the same rule the oracle-only conditioning test
-derives for the O-rounding path.
+  P^ and bf16 decisions span; zero for almost every element);
+* dQ: a row within 2e-2 max|want| passes as it is.  A row beyond it passes
+  if the oracle, recomputing that row with D_i shifted by an admissible
+  amount (|a| <= e(D_i), the shift the O decisions allow) and the row's dS^
+  codes re-rounded, lands within 2e-2 max|want| of it for some listed a
+  (rows beyond half the bar are scanned, so the reported error shows what
+  the shift explains);
+* dK: |got - want| <= 2e-2 max|want|.
 The cosine is always taken on the raw outputs.
 """
 
@@ -29,8 +21,6 @@ import numpy as np
 
 TOL_REL = 2e-2
 TOL_COS = 0.999
-OUTLIER_DQ_REL = 0.125        # one E4M3 step
-OUTLIER_DQ_ROWS = 0.01        # fraction of rows allowed beyond TOL_REL
 
 
 def cosine(got, want):
@@ -38,48 +28,33 @@ def cosine(got, want):
     return float(g @ w / np.sqrt((g @ g) * (w @ w)))
 
 
-def _row_fit(diff, groups, fixed, bar):
-    """Remainder of ``diff`` ([R, d]) after fitting each row's admissible
-    directions.  fixed: optional (directions [R, d], bound [R]) present in
-    every row, fitted in closed form and clipped; rows still above ``bar``
-    are refitted jointly with their listed decisions (groups: row ->
-    (vectors [k, d], lo [k], hi [k])) by bounded least squares.  Rows within
-    the bar need no further explanation, so only those are refitted."""
-    from scipy.optimize import lsq_linear
-    resid = diff.copy()
-    if fixed is not None:
-        g, b = fixed
-        gg = np.sum(g * g, axis=-1)
-        a = np.where(gg > 0, np.sum(diff * g, axis=-1) / np.where(gg > 0, gg, 1.0), 0.0)
-        resid = diff - np.clip(a, -b, b)[:, None] * g
-    for r in np.flatnonzero(np.max(np.abs(resid), axis=-1) > bar):
-        if int(r) not in groups:
-            continue
-        vec, lo, hi = groups[int(r)]
-        cols, lb, ub = [vec], [lo], [hi]
-        if fixed is not None and np.any(fixed[0][r]):
-            cols.insert(0, fixed[0][r][None])
-            lb.insert(0, [-fixed[1][r]])
-            ub.insert(0, [fixed[1][r]])
-        A = np.concatenate(cols).T
-        lb, ub = np.concatenate(lb), np.concatenate(ub)
-        ub = np.where(ub > lb, ub, lb + 1e-300)      # lsq_linear needs lb < ub
-        x = lsq_linear(A, diff[r], bounds=(lb, ub)).x
-        resid[r] = diff[r] - A @ x
-    return resid
+def _doc_of(al, t):
+    """(document start, local row) of slice token t."""
+    for s, e in al["docs"]:
+        if s <= t < e:
+            return s, t - s
+    raise KeyError(t)
 
 
-def _groups(rows_flat, vec, lo, hi):
-    order = np.argsort(rows_flat, kind="stable")
-    rows_s = rows_flat[order]
+def dq_rows_under_shift(got, want, al, bar):
+    """For each dQ row of ``got`` ([T, heads, d]) beyond half the bar: the
+    smallest residual over the admissible D shifts the oracle lists (the scan
+    stops once a shift brings the row within a tenth of the bar), and the
+    shift that gives it.  Returns {(t, h): (residual, a)}."""
     out = {}
-    if len(rows_s) == 0:
-        return out
-    starts = np.flatnonzero(np.r_[True, rows_s[1:] != rows_s[:-1]])
-    ends = np.r_[starts[1:], len(rows_s)]
-    for a_, b_ in zip(starts, ends):
-        idx = order[a_:b_]
-        out[int(rows_s[a_])] = (vec[idx], lo[idx], hi[idx])
+    diff = np.abs(got - want).max(axis=-1)
+    for t, h in zip(*np.nonzero(diff > 0.5 * bar)):
+        s, i = _doc_of(al, int(t))
+        ev = al["dq_rows"][(s, int(h))]
+        eD = float(al["e_D"][t, h])
+        best = (float(diff[t, h]), 0.0)
+        for a in ev.shifts(i, -eD, eD):
+            r = float(np.abs(got[t, h] - ev.row(i, a)).max())
+            if r < best[0]:
+                best = (r, float(a))
+            if r <= 0.1 * bar:
+                break
+        out[(int(t), int(h))] = best
     return out
 
 
@@ -93,26 +68,17 @@ def compare(name, got, want, al=None, tol=TOL_REL):
     diff = got - want
     rel_plain = float(np.max(np.abs(diff)) / M)
     extra = {}
-    if al is None:
+    if al is None or name == "dk":
         rel = rel_plain
-    elif name in ("dq", "dk"):
-        T, Hx, d = diff.shape
-        if name == "dq":
-            ds = al["ds_q"]
-            rows = ds["tq"] * Hx + ds["h"]
-            fixed = (al["dq_dir"].reshape(-1, d), al["e_D"].reshape(-1))
-        else:
-            ds = al["ds_k"]
-            rows = ds["tk"] * Hx + ds["hk"]
-            fixed = None
-        vec = ds["vec"]
-        # rows above half the bar are refitted, so the reported remainder shows
-        # what the decisions explain near the bar, not only the pass/fail
-        resid = _row_fit(diff.reshape(-1, d), _groups(rows, vec, ds["lo"], ds["hi"]), fixed,
-                         0.5 * tol * M).reshape(diff.shape)
-        rel = float(np.max(np.abs(resid)) / M)
-        extra["rows_beyond"] = float(np.mean(np.max(np.abs(resid), axis=-1) / M > tol))
-        extra["ds_decisions"] = int(len(rows))
+    elif name == "dq":
+        shifted = dq_rows_under_shift(got, want, al, tol * M)
+        rest = np.abs(diff).max(axis=-1)
+        for (t, h), (r, _) in shifted.items():
+            rest[t, h] = r
+        rel = float(rest.max() / M)
+        extra["rows_shifted"] = len(shifted)
+        extra["max_shift_over_eD"] = max((abs(a) / max(float(al["e_D"][t, h]), 1e-300)
+                                          for (t, h), (_, a) in shifted.items()), default=0.0)
     else:
         excess = np.abs(diff) - al[name]
         rel = float(max(np.max(excess), 0.0) / M)
@@ -120,10 +86,9 @@ def compare(name, got, want, al=None, tol=TOL_REL):
     return rel_plain, rel, cosine(got, want), extra
 
 
-def check_outputs(outs, ref, al, tag, names=("o", "dq", "dk", "dv"), outliers=False):
+def check_outputs(outs, ref, al, tag, names=("o", "dq", "dk", "dv")):
     """outs: name -> GPU array; ref: oracle result; al: oracle/decisions.allowances
-    of the same inputs; outliers: the workload has outlier channels.  Asserts
-    the bar and returns the metrics."""
+    of the same inputs.  Asserts the bar and returns the metrics."""
     res = {}
     for n in names:
         got = outs[n]
@@ -131,11 +96,9 @@ def check_outputs(outs, ref, al, tag, names=("o", "dq", "dk", "dv"), outliers=Fa
         res[n] = compare(n, got, ref[n], al)
     print(f"[{tag}] " + ", ".join(
         f"{n} rel={r[0]:.2e}" + (f"->{r[1]:.2e}" if r[1] != r[0] else "") + f" cos={r[2]:.6f}"
+        + (f" {r[3]}" if r[3] else "")
         for n, r in res.items()), flush=True)
     for n, (_, rel, cos, extra) in res.items():
         assert cos >= TOL_COS, (n, cos)
-        if n == "dq" and outliers:
-            assert rel <= OUTLIER_DQ_REL and extra["rows_beyond"] <= OUTLIER_DQ_ROWS, (n, rel, extra)
-        else:
-            assert rel <= TOL_REL, (n, rel, extra)
+        assert rel <= TOL_REL, (n, rel, extra)
     return res

@@ -52,7 +52,7 @@ def check_against_oracle(call, wl, tag):
     outs = {n: getattr(call, n).float().cpu().numpy() for n in ("o", "dq", "dk", "dv")}
     for n in outs:
         assert outs[n].shape == ref[n].shape, (n, outs[n].shape, ref[n].shape)
-    DCMP.check_outputs(outs, ref, al, f"gqa {tag}", outliers=wl.has_outliers)
+    DCMP.check_outputs(outs, ref, al, f"gqa {tag}")
     rm = call.row_max.cpu().numpy().astype(np.int64)
     assert np.all(np.abs(rm - ref["row_max"]) <= 1)
     assert (rm != ref["row_max"]).mean() <= 1e-3
@@ -146,6 +146,6 @@ def test_gqa_fullsize_sampled(gpu_lib, kv_heads):
                                   ref["v_ref_exp"] + 127)
     outs = {n: getattr(call, n)[s:e].cpu()[:, hs].float().numpy()
             for n, hs in (("o", hq), ("dq", hq), ("dk", hkv), ("dv", hkv))}
-    DCMP.check_outputs(outs, ref, al, "gqa fullsize", outliers=wl.has_outliers)
+    DCMP.check_outputs(outs, ref, al, "gqa fullsize")
     rm = call.row_max.cpu()[hq][:, s:e].numpy().astype(np.int64)
     assert np.all(np.abs(rm - ref["row_max"]) <= 1) and (rm != ref["row_max"]).mean() <= 1e-3
