@@ -177,9 +177,10 @@ typedef struct flamia_qtensors {
  *                   (key tile, query tile) steps of documents of at most M tokens;
  *                   ceil(T M / 8192) in the first term when causal = 0).
  * If the documents need more steps than max_doc_len promised, the
- * deterministic backward drops the excess partials and sets word 2 of the
- * plan (int32 at byte 8 of qtensors.plan) to 1; the library never reads it
- * back itself.  Any output pointer may be NULL.  Host only; launches nothing.
+ * deterministic backward drops the partials beyond the workspace, writes NaN
+ * to every dq row that lost one, and sets word 2 of the plan (int32 at byte 8
+ * of qtensors.plan) to 1; the library never reads it back itself.  Any
+ * output pointer may be NULL.  Host only; launches nothing.
  */
 flamia_status flamia_buffer_sizes(const flamia_attn_desc* desc, size_t* qtensor_bytes,
                                   size_t* fwd_ws_bytes, size_t* bwd_ws_bytes);
@@ -301,6 +302,29 @@ flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_
                                      void* dk, void* ws, hipStream_t stream);
 
 /*
+ * flamia_bwd_ws_layout -- where flamia_attn_bwd_prep leaves its payload
+ * inside the backward workspace: byte offsets from ws, so a caller (or a
+ * test) can read it back after the prep stage.  Host only.
+ *   do_codes   [T,H,d] E4M3 token-block codes of dO (32 tokens of one
+ *              document x d per exponent, no rotation) -- the one payload
+ *              that dP and D are formed from ([Summary, §3.3])
+ *   do_exp     [H,T] UE8M0 exponent of each token's dO block
+ *   neg_delta  [H,T] fp32 -D_i, D_i = sum_d dO~_id O_id summed in fp32 over
+ *              the stored bf16 O
+ *   inv_l      [H,T] fp32 2^-8 / l_i (row_sum l_i)
+ *   g          [T,H,d] bf16 G_i = dO~_i 2^-8 / l_i, the right operand of dV
+ *   dq_sigma   [H,T] int32 exponent sigma_i of the fp16 dQ accumulator's
+ *              power-of-two prescale ([Reading, 4.4] third bullet):
+ *              e_dO(i) + E_V + E_K + log2 d + 13, E_V and E_K the largest V
+ *              and K exponents of the document (of its blocks up to i's with
+ *              causal_dq_scale; of its tokens up to i with the exact option)
+ */
+typedef struct flamia_bwd_ws_offsets {
+  size_t do_codes, do_exp, neg_delta, inv_l, g, dq_sigma;
+} flamia_bwd_ws_offsets;
+flamia_status flamia_bwd_ws_layout(const flamia_attn_desc* desc, flamia_bwd_ws_offsets* out);
+
+/*
  * flamia_tile_config -- tile sizes the kernels use for a head dim, i.e. the
  * Bq/Bk of the work-list cost model.  Host only.
  */
@@ -310,14 +334,24 @@ flamia_status flamia_tile_config(int32_t head_dim, int32_t* fwd_bq, int32_t* fwd
 /*
  * flamia_plan_view -- where the work lists live inside qt->plan, so a caller
  * (or a test) can copy them back.  Host only.  Layout of the plan:
- *   int32 counts[4]   at byte 0: n_fwd_tiles, n_bwd_tiles, 0, 0
+ *   int32 counts[4]   at byte 0: n_fwd_tiles, n_bwd_tiles, deterministic-mode
+ *                     error word (see flamia_buffer_sizes), n_bwd_tiles again
+ *                     (the dispatch list's count)
  *   int32 fwd[cap_fwd][2] at fwd_offset: (doc, q tile), longest first
  *   int32 bwd[cap_bwd][2] at bwd_offset: (doc, k tile), longest first
- * Sort key: cost descending, then doc, then tile; each tile expands to
- * num_heads consecutive items, head ascending.
+ *   int32 dispatch[cap_bwd][2] at bwd_dispatch_offset: the backward kernel's
+ *                     launch order, a permutation of bwd that keeps each
+ *                     document's key tiles together: documents by the cost of
+ *                     their costliest (first) key tile, descending, then
+ *                     document, then tile (so its query rows stay in L2
+ *                     while its tiles run)
+ * Sort key of fwd and bwd ([Summary, §3.6.2 Load-Balanced Scheduling];
+ * [Reading, 4.4] last bullet): cost descending, then doc, then tile; each
+ * tile expands to num_heads consecutive items, head ascending.  Any output
+ * pointer may be NULL.
  */
 flamia_status flamia_plan_view(const flamia_attn_desc* desc, size_t* fwd_offset, int32_t* cap_fwd,
-                               size_t* bwd_offset, int32_t* cap_bwd);
+                               size_t* bwd_offset, int32_t* cap_bwd, size_t* bwd_dispatch_offset);
 
 /* Static description of a status code; never NULL. */
 const char* flamia_status_string(flamia_status status);

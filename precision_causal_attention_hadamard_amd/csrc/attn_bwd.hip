@@ -1231,7 +1231,8 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
                            hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
   const char* base = static_cast<const char*>(plan);
-  BwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.bwd_offset),
+  // items in the dispatch order (the backward list grouped by document)
+  BwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.disp_offset),
             in.q_codes, in.k_codes, in.v_codes, in.v_key_codes, in.k_exp, in.v_exp, in.v_key_exp,
             in.kofs, in.il8, in.delta, in.dq_sigma, in.qexps, in.do_codes,
             static_cast<const uint16_t*>(in.g), static_cast<uint16_t*>(in.dq_acc), in.dk_f32,

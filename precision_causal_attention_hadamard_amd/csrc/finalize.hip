@@ -35,8 +35,10 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
     const int sig = dq_sigma[(size_t)h * p.T + t];
     // deterministic mode: the fp16 accumulator is rebuilt here from the
     // step partials of every key tile that sees this query, added in fp16 in
-    // ascending key-tile order
+    // ascending key-tile order; a row one of whose partials did not fit the
+    // workspace (max_doc_len under-promised) is written as NaN
     v4i acc[E / 8];
+    bool lost = false;
     if (p.deterministic) {
       const int d = find_doc(p.cu, p.ndocs, t);
       const int s0 = p.cu[d], L = p.cu[d + 1] - s0, lp = t - s0;
@@ -48,7 +50,7 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
       for (int c = 0; c < E / 8; ++c) a8[c] = v8h{};
       for (int u = 0; u <= umax; ++u) {
         const long long step = det_step(det_base[d], u, qt, nq, p.causal);
-        if (step >= det_cap) break;       // the plan flags the overflow
+        if (step >= det_cap) { lost = true; break; }    // the plan flags the overflow too
         const uint16_t* src = dq_part + (((size_t)step * p.H + h) * BWD_BQ + r) * D + (size_t)part * E;
 #pragma unroll
         for (int c = 0; c < E / 8; ++c) a8[c] = a8[c] + __builtin_bit_cast(v8h, ld16(src + 8 * c));
@@ -72,6 +74,10 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
         x[8 * c + 2 * k] = __builtin_amdgcn_ldexpf((float)lo, sig) * p.softmax_scale;
         x[8 * c + 2 * k + 1] = __builtin_amdgcn_ldexpf((float)hi, sig) * p.softmax_scale;
       }
+    }
+    if (lost) {
+#pragma unroll
+      for (int k = 0; k < E; ++k) x[k] = __builtin_nanf("");
     }
     if (p.hadamard) fwht_quarter_row<D>(x, part);
     store_bf16<E>(dq + off, x);

@@ -86,16 +86,17 @@ PlanLayout plan_layout(const flamia_attn_desc* d) {
   pl.cap_bwd = cdiv(d->total_tokens, K_BWD_BK) + d->num_docs;
   pl.fwd_offset = ALIGN;
   pl.bwd_offset = align_up(pl.fwd_offset + sizeof(int) * 2 * (size_t)pl.cap_fwd);
-  pl.det_offset = align_up(pl.bwd_offset + sizeof(int) * 2 * (size_t)pl.cap_bwd);
+  pl.disp_offset = align_up(pl.bwd_offset + sizeof(int) * 2 * (size_t)pl.cap_bwd);
+  pl.det_offset = align_up(pl.disp_offset + sizeof(int) * 2 * (size_t)pl.cap_bwd);
   pl.det_cap = d->deterministic ? (int)det_step_cap(d) : 0;
   pl.bytes = align_up(pl.det_offset + sizeof(int) * ((size_t)d->num_docs + 1));
-  // lists beyond one workgroup's LDS: padded keys of both lists, two buffers
+  // lists beyond one workgroup's LDS: padded keys of the three lists, two buffers
   pl.cap_r = 0;
   pl.keys_offset = 0;
   if (pl.cap_fwd > PLAN_MAX_TILES) {
     pl.cap_r = cdiv(pl.cap_fwd, PLAN_RUN) * PLAN_RUN;
     pl.keys_offset = pl.bytes;
-    pl.bytes = align_up(pl.keys_offset + 4 * sizeof(uint64_t) * (size_t)pl.cap_r);
+    pl.bytes = align_up(pl.keys_offset + 6 * sizeof(uint64_t) * (size_t)pl.cap_r);
   }
   return pl;
 }
@@ -370,6 +371,20 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
   return flamia_attn_bwd_finish(desc, qt, dq, dk, ws, stream);
 }
 
+flamia_status flamia_bwd_ws_layout(const flamia_attn_desc* desc, flamia_bwd_ws_offsets* out) {
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (!out) return FLAMIA_ERR_INVALID_ARG;
+  const BwdLayout b = bwd_layout(desc);
+  out->do_codes = b.do_codes;
+  out->do_exp = b.do_exp;
+  out->neg_delta = b.delta;
+  out->inv_l = b.il8;
+  out->g = b.g;
+  out->dq_sigma = b.dq_sigma;
+  return FLAMIA_OK;
+}
+
 flamia_status flamia_tile_config(int32_t head_dim, int32_t* fwd_bq, int32_t* fwd_bk, int32_t* bwd_bq,
                                  int32_t* bwd_bk) {
   if (head_dim != 64 && head_dim != 128) return FLAMIA_ERR_INVALID_ARG;
@@ -381,7 +396,7 @@ flamia_status flamia_tile_config(int32_t head_dim, int32_t* fwd_bq, int32_t* fwd
 }
 
 flamia_status flamia_plan_view(const flamia_attn_desc* desc, size_t* fwd_offset, int32_t* cap_fwd,
-                               size_t* bwd_offset, int32_t* cap_bwd) {
+                               size_t* bwd_offset, int32_t* cap_bwd, size_t* bwd_dispatch_offset) {
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
   const PlanLayout pl = plan_layout(desc);
@@ -389,6 +404,7 @@ flamia_status flamia_plan_view(const flamia_attn_desc* desc, size_t* fwd_offset,
   if (cap_fwd) *cap_fwd = pl.cap_fwd;
   if (bwd_offset) *bwd_offset = pl.bwd_offset;
   if (cap_bwd) *cap_bwd = pl.cap_bwd;
+  if (bwd_dispatch_offset) *bwd_dispatch_offset = pl.disp_offset;
   return FLAMIA_OK;
 }
 

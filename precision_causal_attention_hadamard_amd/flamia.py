@@ -44,9 +44,13 @@ class QTensors(ctypes.Structure):
                  "qk_tensor_scale", "q_fp4_bf16", "k_fp4_bf16", "k_ref_exp")]
 
 
+class BwdWsOffsets(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_size_t) for name in ("do_codes", "do_exp", "neg_delta", "inv_l", "g", "dq_sigma")]
+
+
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_plan_build", "flamia_quantize", "flamia_attn_fwd",
            "flamia_attn_bwd", "flamia_attn_bwd_prep", "flamia_attn_bwd_main", "flamia_attn_bwd_finish",
-           "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
+           "flamia_bwd_ws_layout", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
 
 _lib = None
 
@@ -71,8 +75,10 @@ def load(path: str = LIB_PATH):
         "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P, P],
         "flamia_attn_bwd_main": [dp, qp, P, P, P, P],
         "flamia_attn_bwd_finish": [dp, qp, P, P, P, P],
+        "flamia_bwd_ws_layout": [dp, ctypes.POINTER(BwdWsOffsets)],
         "flamia_tile_config": [I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
-        "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I)],
+        "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I),
+                             ctypes.POINTER(S)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -158,6 +164,12 @@ def attn_bwd_finish(desc, qt: QTensors, dq, dk, ws, stream=None):
                                          _stream(stream)), "flamia_attn_bwd_finish")
 
 
+def bwd_ws_layout(desc: AttnDesc) -> BwdWsOffsets:
+    out = BwdWsOffsets()
+    _check(load().flamia_bwd_ws_layout(ctypes.byref(desc), ctypes.byref(out)), "flamia_bwd_ws_layout")
+    return out
+
+
 def tile_config(head_dim: int):
     v = [ctypes.c_int32() for _ in range(4)]
     _check(load().flamia_tile_config(head_dim, *[ctypes.byref(x) for x in v]), "flamia_tile_config")
@@ -165,11 +177,11 @@ def tile_config(head_dim: int):
 
 
 def plan_view(desc: AttnDesc):
-    fo, bo = ctypes.c_size_t(), ctypes.c_size_t()
+    fo, bo, do_ = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     cf, cb = ctypes.c_int32(), ctypes.c_int32()
     _check(load().flamia_plan_view(ctypes.byref(desc), ctypes.byref(fo), ctypes.byref(cf), ctypes.byref(bo),
-                                   ctypes.byref(cb)), "flamia_plan_view")
-    return fo.value, cf.value, bo.value, cb.value
+                                   ctypes.byref(cb), ctypes.byref(do_)), "flamia_plan_view")
+    return fo.value, cf.value, bo.value, cb.value, do_.value
 
 
 def status_string(status: int) -> str:
@@ -184,7 +196,7 @@ class TrainingCall:
     drops the j <= i mask (every key of a document is visible)."""
 
     def __init__(self, q, k, v, do, cu_seqlens, hadamard=False, causal_dq_scale=False,
-                 softmax_scale=0.0, path=0, deterministic=False, exact=False, causal=True):
+                 softmax_scale=0.0, path=0, deterministic=False, exact=False, causal=True, max_doc_len=None):
         dev = q.device
         self.q, self.k, self.v, self.do = q, k, v, do
         T, H, d = q.shape
@@ -192,7 +204,8 @@ class TrainingCall:
         self.cu_list = [int(c) for c in cu_seqlens]
         self.cu = torch.tensor(self.cu_list, dtype=torch.int32, device=dev)
         lens = [b - a for a, b in zip(self.cu_list, self.cu_list[1:])]
-        self.desc = make_desc(self.cu, T, len(lens), max(lens) if lens else 0, H, d, hadamard,
+        mdl = (max(lens) if lens else 0) if max_doc_len is None else max_doc_len
+        self.desc = make_desc(self.cu, T, len(lens), mdl, H, d, hadamard,
                               causal_dq_scale, softmax_scale, path, causal=int(causal),
                               deterministic=int(deterministic),
                               num_kv_heads=Hk, exact=int(exact))
@@ -258,13 +271,37 @@ class TrainingCall:
         return codes, sf, ts[2 if which == "q" else 3]
 
     def plan_lists(self):
-        fo, cf, bo, cb = plan_view(self.desc)
+        """(forward, backward) work lists as (doc, tile) rows, longest first."""
+        fo, cf, bo, cb, _ = plan_view(self.desc)
         base = self.qt.plan - self.qbuf.data_ptr()
         raw = self.qbuf[base:base + bo + 8 * cb]
         counts = raw[:16].view(torch.int32).cpu()
         fwd = raw[fo:fo + 8 * cf].view(torch.int32).view(cf, 2).cpu()
         bwd = raw[bo:bo + 8 * cb].view(torch.int32).view(cb, 2).cpu()
         return fwd[: int(counts[0])], bwd[: int(counts[1])]
+
+    def plan_dispatch(self):
+        """The backward kernel's launch order (doc, tile), a permutation of
+        the backward list grouped by document."""
+        _, _, _, cb, so = plan_view(self.desc)
+        base = self.qt.plan - self.qbuf.data_ptr()
+        raw = self.qbuf[base:base + so + 8 * cb]
+        n = int(raw[12:16].view(torch.int32).cpu()[0])
+        return raw[so:so + 8 * cb].view(torch.int32).view(cb, 2).cpu()[:n]
+
+    def bwd_payload(self):
+        """What the backward's prep stage left in the workspace: dO codes
+        [T,H,d], dO exponent bytes [H,T], D [H,T] (fp32), 2^-8 / l [H,T], G
+        [T,H,d] (bf16) and the dQ prescale exponent [H,T] (int32)."""
+        T, H, d = self.shape
+        o = bwd_ws_layout(self.desc)
+        w = self.bws
+        return dict(do_codes=w[o.do_codes:o.do_codes + T * H * d].view(T, H, d),
+                    do_exp=w[o.do_exp:o.do_exp + T * H].view(H, T),
+                    D=-w[o.neg_delta:o.neg_delta + 4 * T * H].view(torch.float32).view(H, T),
+                    inv_l=w[o.inv_l:o.inv_l + 4 * T * H].view(torch.float32).view(H, T),
+                    g=w[o.g:o.g + 2 * T * H * d].view(torch.bfloat16).view(T, H, d),
+                    dq_sigma=w[o.dq_sigma:o.dq_sigma + 4 * T * H].view(torch.int32).view(H, T))
 
     def plan_error_word(self) -> int:
         """Word 2 of the plan: 1 when deterministic mode ran out of dQ partial slots."""

@@ -156,3 +156,41 @@ def small_packed(seed: int, doc_lens, heads: int = 2, head_dim: int = 64,
     return Workload(f"packed_{'_'.join(map(str, doc_lens))}_h{heads}{kvs}_d{head_dim}", q, kk, v, do,
                     _cu(doc_lens), heads, head_dim, hadamard=hadamard, path=path,
                     notes={"outlier_scale": outlier_scale} if outlier_scale else {})
+
+
+def saved_forward_state(seed: int, T: int, H: int, d: int):
+    """Stand-ins for the forward's saved outputs, for tests of the backward's
+    preparation stage on its own: O bf16 ``[T, H, d]`` drawn N(0, 1), the
+    integer row maximum int32 ``[H, T]`` uniform in [-4, 12] and the row sum
+    fp32 ``[H, T]`` uniform in [1, 64]."""
+    rng = np.random.default_rng(SEED_BASE + 900 + seed)
+    o = _bf16(rng.standard_normal((T, H, d), dtype=np.float32))
+    row_max = torch.from_numpy(rng.integers(-4, 13, size=(H, T)).astype(np.int32))
+    row_sum = torch.from_numpy(rng.uniform(1.0, 64.0, size=(H, T)).astype(np.float32))
+    return o, row_max, row_sum
+
+
+def e4m3_sweep(shifts=range(-20, 21), head_dim: int = 128) -> Workload:
+    """Every finite bf16 value times every power of two 2^k (k in ``shifts``)
+    that stays inside the E4M3 range of a 32-token block scaled by 2^k: each
+    block holds one anchor of magnitude 448 * 2^k (so its exponent is k) and
+    then bf16 values v with |v| <= 448 * 2^k, in increasing order of their
+    bit patterns.  One head; Q = K = V = dO; one document per shift so that
+    blocks never mix shifts."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    rows, lens = [], []
+    per_row = head_dim
+    for k in shifts:
+        anchor = np.float32(448.0 * 2.0 ** k)
+        v = vals[np.abs(vals) <= anchor]
+        n_tok = -(-len(v) // (31 * per_row))            # 31 value rows + 1 anchor row per block
+        pad = np.zeros(n_tok * 31 * per_row - len(v), np.float32)
+        body = np.concatenate([v, pad]).reshape(n_tok, 31, per_row)
+        blocks = np.concatenate([np.full((n_tok, 1, per_row), anchor, np.float32), body], axis=1)
+        rows.append(blocks.reshape(-1, per_row))
+        lens.append(blocks.shape[0] * 32)
+    x = np.concatenate(rows)[:, None, :]
+    t = _bf16(x)
+    return Workload(f"e4m3_sweep_{len(lens)}shifts", t, t.clone(), t.clone(), t.clone(), _cu(lens), 1, head_dim)

@@ -131,6 +131,23 @@ def test_deterministic_workspace_holds_every_partition():
     assert 2 * causal_steps(4096) <= cap <= 1.1 * 2 * causal_steps(4096)
 
 
+def test_under_promised_max_doc_len_leaves_too_few_slots():
+    """The deterministic workspace is sized from max_doc_len, which the host
+    cannot check (the lengths live on the GPU).  Promising 100 tokens for two
+    2000-token documents sizes it for fewer causal steps than they need, so
+    the backward must flag the overflow (the GPU test checks that the rows
+    that lose a partial come out as NaN and the plan's word 2 is set)."""
+    lib = flamia.load()
+    def cap(M):
+        d0 = base_desc(total_tokens=4000, max_doc_len=M, num_docs=2, num_heads=1, head_dim=64)
+        d1 = base_desc(total_tokens=4000, max_doc_len=M, num_docs=2, num_heads=1, head_dim=64, deterministic=1)
+        return (sizes_status(lib, d1)[2] - sizes_status(lib, d0)[2]) // (64 * 64 * 2)
+    need = 2 * causal_steps(2000)
+    assert cap(2000) >= need
+    assert cap(100) < need // 2
+    assert all(cap(m) <= cap(m + 100) for m in range(100, 2000, 100))      # grows with the promise
+
+
 def test_null_arguments_rejected_without_launch(lib):
     assert lib.flamia_buffer_sizes(None, None, None, None) == 1
     d = base_desc(cu_seqlens=None)
@@ -184,13 +201,15 @@ def test_tile_config_and_status_strings(lib):
 
 def test_large_worklists_get_a_key_area_and_launch_limits_are_reported(lib):
     """Lists beyond one workgroup's LDS sort (8192 tiles of 128 tokens) take
-    the multi-workgroup path, whose padded keys (two buffers of both lists,
-    rounded up to runs of 2048) live in the plan; a call whose launches
+    the multi-workgroup path, whose padded keys (two buffers of the three
+    lists, rounded up to runs of 2048) live in the plan; a call whose launches
     would exceed 32-bit work-item counts is reported, not launched."""
     def plan_bytes(d):
         off, cap, boff, bcap = ctypes.c_size_t(), ctypes.c_int32(), ctypes.c_size_t(), ctypes.c_int32()
+        doff = ctypes.c_size_t()
         assert lib.flamia_plan_view(ctypes.byref(d), ctypes.byref(off), ctypes.byref(cap),
-                                    ctypes.byref(boff), ctypes.byref(bcap)) == 0
+                                    ctypes.byref(boff), ctypes.byref(bcap), ctypes.byref(doff)) == 0
+        assert doff.value >= boff.value + 8 * bcap.value        # the dispatch list follows the backward list
         return cap.value, bcap.value
     small = base_desc(total_tokens=8192 * 128 - 128, max_doc_len=8192 * 128 - 128, num_docs=1)
     big = base_desc(total_tokens=1 << 20, max_doc_len=1 << 20, num_docs=1)
@@ -202,9 +221,9 @@ def test_large_worklists_get_a_key_area_and_launch_limits_are_reported(lib):
     assert plan_bytes(small) == (8192, 8192) and plan_bytes(big) == (8193, 8193)
     assert plan_bytes(many) == (132096, 132096)
     runs = -(-132096 // 2048) * 2048
-    assert q_m >= 4 * 8 * runs
-    # codes grow by 4 bytes per element, the key area by 4 x 8 bytes per padded slot
-    assert q_b - q_s >= 4 * 128 * 2 * 64 + 4 * 8 * 10240
+    assert q_m >= 6 * 8 * runs
+    # codes grow by 4 bytes per element, the key area by 6 x 8 bytes per padded slot
+    assert q_b - q_s >= 4 * 128 * 2 * 64 + 6 * 8 * 10240
     huge = base_desc(total_tokens=(1 << 23), max_doc_len=1, num_docs=(1 << 23), head_dim=64)
     assert sizes_status(lib, huge)[0] == 3
 

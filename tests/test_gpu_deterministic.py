@@ -81,3 +81,28 @@ def test_deterministic_dq_causality_probe(gpu_lib):
     assert torch.equal(b.o[: i0 + 1], a.o[: i0 + 1])
     assert torch.equal(b.dq[: i0 + 1], a.dq[: i0 + 1])
     assert not torch.equal(b.dq, a.dq)
+
+
+def test_deterministic_overflow_is_loud(gpu_lib):
+    """max_doc_len under-promised (100 tokens for two 2000-token documents):
+    the partials that do not fit are dropped, every dQ row that lost one is
+    NaN, the plan's error word is 1, and everything else -- O, dK, dV and the
+    dQ rows that kept all their partials -- equals the call with the true
+    bound bit for bit."""
+    wl = W.small_packed(38, [2000, 2000], heads=1, head_dim=64)
+    dev = torch.device("cuda")
+    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
+    bad = gpu_lib.TrainingCall(q, k, v, do, wl.cu_seqlens, deterministic=True, max_doc_len=100)
+    good = gpu_lib.TrainingCall(q, k, v, do, wl.cu_seqlens, deterministic=True)
+    bad.step()
+    good.step()
+    torch.cuda.synchronize()
+    assert bad.plan_error_word() == 1 and good.plan_error_word() == 0
+    for n in ("o", "dk", "dv"):
+        assert torch.equal(getattr(bad, n), getattr(good, n)), n
+    nan_rows = torch.isnan(bad.dq.float()).any(dim=-1).squeeze(1).cpu()
+    assert torch.isnan(bad.dq.float()[nan_rows]).all()
+    assert 0 < int(nan_rows.sum()) < wl.total_tokens
+    assert int(nan_rows[2000:].sum()) == 2000             # the second document's steps all lie beyond the cap
+    keep = ~nan_rows
+    assert torch.equal(bad.dq[keep], good.dq[keep])

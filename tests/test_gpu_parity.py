@@ -37,13 +37,11 @@ def run_gpu(flamia, wl, causal_dq_scale=False):
 
 
 def run_oracle(wl):
-    """The oracle's result, with its decision bounds and the workload's
-    outlier flag attached for check_outputs."""
+    """The oracle's result, with its decision bounds attached for check_outputs."""
     q, k, v, do = np_inputs(wl)
     num = A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8")
     ref = A.training_call(q, k, v, do, wl.cu_seqlens, num)
     ref["_allow"] = DC.allowances(q, k, v, do, wl.cu_seqlens, num)
-    ref["_outliers"] = wl.has_outliers
     return ref
 
 
@@ -56,7 +54,7 @@ def check_codes(call, ref):
 
 def check_outputs(call, ref, names=("o", "dq", "dk", "dv"), tag="parity"):
     outs = {n: getattr(call, n).float().cpu().numpy() for n in names}
-    m = DCMP.check_outputs(outs, ref, ref["_allow"], tag, names, outliers=ref["_outliers"])
+    m = DCMP.check_outputs(outs, ref, ref["_allow"], tag, names)
     rm = call.row_max.cpu().numpy().astype(np.int64)
     diff = rm != ref["row_max"]
     assert np.all(np.abs(rm - ref["row_max"]) <= 1)
@@ -102,6 +100,25 @@ WORKLIST_DOCS = {
 }
 
 
+def check_dispatch(bwd, disp):
+    """The backward's launch order is a permutation of the backward list
+    that keeps each document's key tiles together, in tile order, with the
+    documents in the order their first tiles take in the backward list."""
+    b, s_ = np.asarray(bwd, np.int64), np.asarray(disp, np.int64)
+    assert b.shape == s_.shape
+    kb, ks = b[:, 0] * (1 << 20) + b[:, 1], s_[:, 0] * (1 << 20) + s_[:, 1]
+    assert np.array_equal(np.sort(kb), np.sort(ks)) and len(np.unique(ks)) == len(ks)
+    if not len(b):
+        return
+    _, first = np.unique(b[:, 0], return_index=True)
+    doc_order = b[np.sort(first), 0]
+    starts = np.r_[True, s_[1:, 0] != s_[:-1, 0]]
+    assert np.array_equal(s_[starts, 0], doc_order)          # contiguous, in first-appearance order
+    run_start = np.flatnonzero(starts)
+    pos = np.arange(len(s_)) - run_start[np.cumsum(starts) - 1]
+    assert np.array_equal(s_[:, 1], pos)                      # tiles 0, 1, ... inside each document
+
+
 @pytest.mark.parametrize("docs", list(WORKLIST_DOCS))
 def test_worklists_match_oracle(gpu_lib, docs):
     heads = 3 if docs == "small" else 1
@@ -113,6 +130,7 @@ def test_worklists_match_oracle(gpu_lib, docs):
     want_b = [(d, t) for d, t, h, c in WL.bwd_items(wl.cu_seqlens, 1, bbq, bbk)]
     assert [tuple(x) for x in fwd.tolist()] == want_f
     assert [tuple(x) for x in bwd.tolist()] == want_b
+    check_dispatch(bwd, call.plan_dispatch())
 
 
 def test_repeatable_bitwise(gpu_lib):
