@@ -168,9 +168,10 @@ typedef struct flamia_qtensors {
  *   qtensor_bytes : one buffer for flamia_qtensors (codes, exponents, plan).
  *   fwd_ws_bytes  : workspace of flamia_attn_fwd (may be 0; pass NULL then).
  *   bwd_ws_bytes  : workspace of flamia_attn_bwd (quantized dO, D, dO/l,
- *                   fp16 dQ accumulator, fp32 dK staging, prescale exponents;
+ *                   fp16 dQ accumulator, prescale exponents; on the mixed
+ *                   path fp32 dK staging;
  *                   with grouped query attention on a grid too small to fill
- *                   the GPU, also fp32 dV partials of the split groups;
+ *                   the GPU, also fp32 dK and dV partials of the split groups;
  *                   in deterministic mode also the dQ partial slots: 64 x d
  *                   fp16 per head for at most ceil(T M / 16384) + ceil(3T / 128)
  *                   + 2 num_docs steps, M = max_doc_len, a bound of the causal

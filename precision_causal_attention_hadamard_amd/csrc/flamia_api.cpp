@@ -143,9 +143,13 @@ BwdLayout bwd_layout(const flamia_attn_desc* d) {
   b.g = off;        off = align_up(off + 2 * E);
   b.dq_sigma = off; off = align_up(off + 4 * M);
   b.dq_acc = off;   off = align_up(off + 2 * E);
-  b.dk_f32 = off;   off = align_up(off + 4 * E);     // also holds split-group dK partials (s Hk <= H)
-  b.dv_f32 = off;
+  // fp32 dK staging: the mixed path's dK, or the split-group dK partials
+  // (s Hk <= H, so E holds them); the MXFP8 path otherwise writes bf16 dK
+  // from the backward kernel and needs none
   const int gs = bwd_group_split(d);
+  b.dk_f32 = off;
+  if (d->path == 1 || gs > 1) off = align_up(off + 4 * E);
+  b.dv_f32 = off;
   if (gs > 1) off = align_up(off + 4 * (size_t)gs * d->total_tokens * kv_heads(d) * d->head_dim);
   b.dq_part = off;
   if (d->deterministic)

@@ -50,7 +50,9 @@ def test_buffer_sizes_valid(lib):
     assert st == 0
     T, H, d = 256, 2, 64
     assert q >= 4 * T * H * d + 5 * T * H           # codes + exponent bytes + plan
-    assert b >= T * H * d * (1 + 2 + 2 + 4)          # dO codes, G, dQ acc, dK staging
+    assert b >= T * H * d * (1 + 2 + 2)              # dO codes, G, dQ acc
+    st_m, _, b_m = sizes_status(lib, base_desc(path=1))
+    assert st_m == 0 and b_m >= b + 4 * T * H * d    # the mixed path also stages fp32 dK
 
 
 @pytest.mark.parametrize("field,value,want", [
@@ -74,9 +76,10 @@ def test_grouped_query_heads_validation_and_layout(lib):
     assert sizes_status(lib, base_desc(num_heads=6, num_kv_heads=4))[0] == 1
     st, q, b = sizes_status(lib, base_desc(num_heads=6, num_kv_heads=2))
     # 6 backward items (3 key tiles x 2 key/value heads) are far below two per CU,
-    # so each group of 3 query heads is split over 3 items whose fp32 dV
-    # partials need their own staging (dK partials reuse the fp32 dK region)
-    assert st == 0 and b == full[2] + 4 * 3 * T * 2 * d
+    # so each group of 3 query heads is split over 3 items whose fp32 dK and
+    # dV partials need staging: the fp32 dK region (T x 6 x d, which holds the
+    # 3 x T x 2 x d dK partials) and a dV region of its own
+    assert st == 0 and b == full[2] + 4 * T * 6 * d + 4 * 3 * T * 2 * d
     assert full[1] - q >= 3 * T * 4 * d + 4 * T * 4   # three K-side code tensors, four exponent planes
     # the mixed path runs one query head per item: fp32 dK, dV partials of each group's 3 heads
     st_m, _, b_m = sizes_status(lib, base_desc(num_heads=6, num_kv_heads=2, path=1))
