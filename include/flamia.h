@@ -270,6 +270,24 @@ flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensor
                               hipStream_t stream);
 
 /*
+ * flamia_attn_bwd_noalloc -- flamia_attn_bwd without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a device array inside the library, 32 MiB on each GPU the
+ * library runs on, held until the process ends; its address is looked up on
+ * the first call on each device.  Same arguments, kernels and results as
+ * flamia_attn_bwd otherwise.  Nothing is allocated or freed.
+ * Errors: FLAMIA_ERR_WORKSPACE when the call's bwd_ws_bytes
+ * (flamia_buffer_sizes) exceed 32 MiB; FLAMIA_ERR_INVALID_ARG when `stream`
+ * does not belong to the current device; FLAMIA_ERR_HIP when the array's
+ * address cannot be obtained; else as flamia_attn_bwd.
+ * Every call on one GPU shares the array: calls that overlap on one GPU race.
+ */
+flamia_status flamia_attn_bwd_noalloc(const flamia_attn_desc* desc, const flamia_qtensors* qt,
+                                      const void* o, const int32_t* row_max, const float* row_sum,
+                                      const void* dout, void* dq, void* dk, void* dv, hipStream_t stream);
+
+/*
  * The three stages of flamia_attn_bwd, for callers that schedule them
  * separately (e.g. to overlap the dO preparation with other work).  Calling
  * them in this order on one stream is exactly flamia_attn_bwd.

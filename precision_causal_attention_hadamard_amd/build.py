@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libflamia.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["plan.hip", "quant.hip", "attn_fwd.hip", "attn_bwd.hip", "finalize.hip", "flamia_api.cpp"]
+SOURCES = ["plan.hip", "quant.hip", "attn_fwd.hip", "attn_bwd.hip", "finalize.hip", "flamia_api.cpp", "noalloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

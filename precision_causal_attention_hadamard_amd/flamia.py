@@ -49,8 +49,8 @@ class BwdWsOffsets(ctypes.Structure):
 
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_plan_build", "flamia_quantize", "flamia_attn_fwd",
-           "flamia_attn_bwd", "flamia_attn_bwd_prep", "flamia_attn_bwd_main", "flamia_attn_bwd_finish",
-           "flamia_bwd_ws_layout", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
+           "flamia_attn_bwd", "flamia_attn_bwd_noalloc", "flamia_attn_bwd_prep", "flamia_attn_bwd_main",
+           "flamia_attn_bwd_finish", "flamia_bwd_ws_layout", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
 
 _lib = None
 
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH):
         "flamia_quantize": [dp, P, P, P, qp, P],
         "flamia_attn_fwd": [dp, qp, P, P, P, P, P],
         "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
+        "flamia_attn_bwd_noalloc": [dp, qp, P, P, P, P, P, P, P, P],
         "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P, P],
         "flamia_attn_bwd_main": [dp, qp, P, P, P, P],
         "flamia_attn_bwd_finish": [dp, qp, P, P, P, P],
@@ -146,6 +147,12 @@ def attn_bwd(desc, qt: QTensors, o, row_max, row_sum, dout, dq, dk, dv, ws, stre
     _check(load().flamia_attn_bwd(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
                                   _ptr(row_sum), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                   _stream(stream)), "flamia_attn_bwd")
+
+
+def attn_bwd_noalloc(desc, qt: QTensors, o, row_max, row_sum, dout, dq, dk, dv, stream=None):
+    _check(load().flamia_attn_bwd_noalloc(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
+                                          _ptr(row_sum), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                          _stream(stream)), "flamia_attn_bwd_noalloc")
 
 
 def attn_bwd_prep(desc, qt: QTensors, o, row_max, row_sum, dout, ws, stream=None):
