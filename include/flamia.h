@@ -321,6 +321,39 @@ flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_
                                      void* dk, void* ws, hipStream_t stream);
 
 /*
+ * Diagnostic entry points: flamia_attn_fwd and flamia_attn_bwd_main run as a
+ * second instantiation of the same kernels that also reports what the pages
+ * make checkable ([Summary, §3.3 Forward-Backward Numerical Consistency]):
+ * the probability codes each pass computes, and the share of nonzero dS that
+ * its 32x32 block scale rounds to zero ([Summary, §3.3] second bullet).
+ * Same results as the plain calls.  Supported for the MXFP8 causal call
+ * with num_kv_heads = num_heads, block scales and atomic dQ (exact = 0,
+ * deterministic = 0); anything else returns FLAMIA_ERR_UNSUPPORTED.
+ *
+ * flamia_attn_fwd_diag -- flamia_attn_fwd, plus (when phat is not NULL):
+ *   phat      uint8 [H, T, row_len]: E4M3 code of P^ (with the diagonal
+ *             fold) of query token t and document-local key j, for every
+ *             key the query sees, taken against the running integer row
+ *             maximum of the 64-key step that holds the key; other bytes are
+ *             left as they are.
+ *   phat_max  int32 [H, T, ceil(row_len / 64)]: that running maximum per step.
+ *   row_len   >= max_doc_len (else FLAMIA_ERR_INVALID_ARG).
+ * flamia_attn_bwd_main_diag -- flamia_attn_bwd_main, plus:
+ *   phat       (may be NULL) as above, the backward's recomputed codes,
+ *              taken against the stored final row maximum.  Where P 2^8
+ *              (times the fold) is at least 2^-6 (E4M3's normal range) the
+ *              forward's code times 2^(run max - final max) equals it.
+ *   ds_counts  (may be NULL) uint64[2]: nonzero dS entries, and those whose
+ *              E4M3 code is zero; zeroed by the call before it counts.
+ */
+flamia_status flamia_attn_fwd_diag(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
+                                   int32_t* row_max, float* row_sum, void* ws, uint8_t* phat, int32_t* phat_max,
+                                   int32_t row_len, hipStream_t stream);
+flamia_status flamia_attn_bwd_main_diag(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dk,
+                                        void* dv, void* ws, uint8_t* phat, int32_t row_len,
+                                        uint64_t* ds_counts, hipStream_t stream);
+
+/*
  * flamia_bwd_ws_layout -- where flamia_attn_bwd_prep leaves its payload
  * inside the backward workspace: byte offsets from ws, so a caller (or a
  * test) can read it back after the prep stage.  Host only.

@@ -79,6 +79,9 @@ struct BwdArgs {
   const uint8_t* v_ref_exp;    // exact option: V's in-block prefix maximum (block maxima at block ends)
   const uint16_t *q_x, *k_x;   // mixed path: NVFP4 Q and K expanded to bf16
   const float* qk_scale;       // mixed path: [2], [3] tensor scales
+  uint8_t* dump;               // diagnostic instantiation: P^ codes [H, T, dump_len] (or null)
+  int dump_len;
+  unsigned long long* ds_counts;   // diagnostic instantiation: [0] nonzero dS, [1] those coded 0
 };
 
 // PATH 0: MXFP8 scores.  PATH 1 (mixed): the recomputed scores come from the
@@ -649,7 +652,11 @@ __device__ __forceinline__ float half_max32(float m) {
 // CAUSAL false: every query tile of the document visits the key tile (no
 // j <= i mask); the diagonal per-key V codes and fold stay, against the block
 // exponent as the quantizer then writes it.
-template <int D, bool DET, bool GRP, bool EXACT, bool CAUSAL>
+// DIAG: also writes each recomputed P^ code (the forward's, relative to the
+// final row maximum, when the replay is exact: [Summary, §3.3
+// Forward-Backward Numerical Consistency]) and counts the nonzero dS and
+// those whose E4M3 code is zero ([Summary, §3.3] second bullet).
+template <int D, bool DET, bool GRP, bool EXACT, bool CAUSAL, bool DIAG = false>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
@@ -830,6 +837,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   }
 
   v16f dk[NDK], dv[ND];
+  uint32_t ds_nz = 0, ds_zero = 0;       // diagnostic counts of this lane
 #pragma unroll
   for (int e = 0; e < NDK; ++e) dk[e] = v16f{};
 #pragma unroll
@@ -962,6 +970,13 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           const int code = EXACT ? cvt_fp8x4(__builtin_amdgcn_ldexpf(pf[0], fd), __builtin_amdgcn_ldexpf(pf[1], fd),
                                              __builtin_amdgcn_ldexpf(pf[2], fd), __builtin_amdgcn_ldexpf(pf[3], fd))
                                  : cvt_fp8x4(pf[0], pf[1], pf[2], pf[3]);
+          if constexpr (DIAG) {
+            if (a.dump != nullptr && j < a.dump_len) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                a.dump[((size_t)h * T + s_d + q0 + r0 + r) * a.dump_len + j] = (uint8_t)((code >> (8 * r)) & 255);
+            }
+          }
           pe[2 * g] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, EXACT ? ufd : 1.0f, false));
           pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, EXACT ? ufd : 1.0f, true));
         }
@@ -982,12 +997,18 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
               const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
               const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
               dsr = (p8 * ilv[r]) * pacc[rr];
+              int code;
               if (EXACT || dia) {
                 const int vref = (EXACT && !dia) ? sVrB[kb] - E8M0_BIAS : ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
-                const int code = cvt_fp8x2(__builtin_amdgcn_ldexpf(p8, e_key - vref), 0.f);
+                code = cvt_fp8x2(__builtin_amdgcn_ldexpf(p8, e_key - vref), 0.f);
                 pev = __builtin_amdgcn_ldexpf(fp8_value(code, 0), vref - e_key);
               } else {
-                pev = fp8_value(cvt_fp8x2(p8, 0.f), 0);
+                code = cvt_fp8x2(p8, 0.f);
+                pev = fp8_value(code, 0);
+              }
+              if constexpr (DIAG) {
+                if (a.dump != nullptr && j < a.dump_len)
+                  a.dump[((size_t)h * T + s_d + i) * a.dump_len + j] = (uint8_t)(code & 255);
               }
             }
             dsv[rr] = dsr;
@@ -1061,6 +1082,14 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           dsc[g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(dsv[4 * g], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 1], -e),
                              __builtin_amdgcn_ldexpf(dsv[4 * g + 2], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 3], -e));
       }
+      }
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const bool nz = dsv[rr] != 0.f;      // masked and out-of-range entries are exactly 0
+          ds_nz += nz;
+          ds_zero += nz && ((dsc[rr >> 2] >> (8 * (rr & 3))) & 0x7f) == 0;
+        }
       }
       // dV += P^_eff^T G over this wave's 32 queries (two K-steps of 16)
 #pragma unroll
@@ -1149,6 +1178,20 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     }
   }
   flush_dq(qt_end - 1, h_end - 1);
+  if constexpr (DIAG) {
+    if (a.ds_counts != nullptr) {
+      unsigned long long nz = ds_nz, zr = ds_zero;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        nz += __shfl_xor(nz, off, 64);
+        zr += __shfl_xor(zr, off, 64);
+      }
+      if (lane == 0) {
+        atomicAdd(a.ds_counts, nz);
+        atomicAdd(a.ds_counts + 1, zr);
+      }
+    }
+  }
 
   // split groups: this item's part (recomputed here rather than kept live)
   const int GS = GRP ? a.gsplit : 1, part = GRP ? (int)(blockIdx.x % GS) : 0;
@@ -1227,6 +1270,12 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   }
 }
 
+// Clears n 64-bit counters (a kernel rather than a memset, so a captured
+// graph replays it correctly).
+__global__ void zero_u64_kernel(unsigned long long* x, int n) {
+  if ((int)threadIdx.x < n) x[threadIdx.x] = 0ull;
+}
+
 hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl, const BwdInputs& in,
                            hipStream_t stream) {
   if (p.T == 0) return hipSuccess;
@@ -1238,7 +1287,7 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
             static_cast<const uint16_t*>(in.g), static_cast<uint16_t*>(in.dq_acc), in.dk_f32,
             static_cast<uint16_t*>(in.dk), static_cast<uint16_t*>(in.dv), in.dv_f32, in.gsplit,
             static_cast<uint16_t*>(in.dq_part), in.det_base, in.det_cap, in.v_ref_exp, static_cast<const uint16_t*>(in.q_x),
-            static_cast<const uint16_t*>(in.k_x), in.qk_scale};
+            static_cast<const uint16_t*>(in.k_x), in.qk_scale, in.dump, in.dump_len, in.ds_counts};
   dim3 grid((unsigned)pl.cap_bwd * (unsigned)p.Hk * (unsigned)in.gsplit);   // the mixed path has Hk = H, gsplit = 1
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(BWD_THREADS), 0, stream, a); };
   if (p.path == 1) {
@@ -1247,6 +1296,13 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
     } else {
       if (p.D == 64) go(attn_bwd_kernel<64, 1, false>); else go(attn_bwd_kernel<128, 1, false>);
     }
+  } else if (in.diag) {
+    // diagnostic instantiation: MXFP8, one head per item, causal, atomic dQ
+    if (in.ds_counts != nullptr)
+      hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, stream, in.ds_counts, 2);
+    auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
+    if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, false, true, true>);
+    else go8(attn_bwd8_kernel<128, false, false, false, true, true>);
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
     // one instantiation per (determinism, grouped heads, exact option, causal);

@@ -51,6 +51,12 @@ struct FwdArgs {
   uint16_t* o;
   int* row_max;
   float* row_sum;
+  // diagnostic instantiation only: the P^ codes of every visible (query, key)
+  // pair, [H, T, dump_len] by document-local key, and the running integer
+  // row maximum each 64-key step used, [H, T, ceil(dump_len / 64)]
+  uint8_t* dump;
+  int* dump_max;
+  int dump_len;
 };
 
 // PATH 0: MXFP8 scores.  PATH 1 (mixed): scores from NVFP4 Q and K, expanded
@@ -59,7 +65,10 @@ struct FwdArgs {
 // CAUSAL false: every key of the document is visible (no j <= i mask); the
 // diagonal per-key V fold is unchanged, its reference then being the block
 // exponent (written so by the quantizer).
-template <int D, int PATH, bool EXACT, bool CAUSAL>
+// DIAG: also writes each P^ code and the running row maximum it was taken
+// against, for the check that the backward replays the forward's codes
+// ([Summary, §3.3 Forward-Backward Numerical Consistency]).
+template <int D, int PATH, bool EXACT, bool CAUSAL, bool DIAG = false>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int KS = D + 16;          // token-major row stride (bytes)
@@ -329,6 +338,23 @@ attn_fwd_kernel(FwdArgs a) {
           }
         }
         const v8i pb = v8i{pc[0][0], pc[0][1], pc[0][2], pc[0][3], pc[1][0], pc[1][1], pc[1][2], pc[1][3]};
+        if constexpr (DIAG) {
+          if (a.dump != nullptr && iv) {
+            const size_t row = (size_t)head * T + s_d + i;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int j = j0 + 32 * kb + 8 * g + 4 * hh + r;
+                  if (act[kb] && j < L && j < a.dump_len && (!CAUSAL || j <= i))
+                    a.dump[row * a.dump_len + j] = (uint8_t)((pc[kb][g] >> (8 * r)) & 255);
+                }
+            const int nkt = (a.dump_len + FWD_BK - 1) / FWD_BK;
+            if (hh == 0 && kt < nkt) a.dump_max[row * nkt + kt] = m_run;
+          }
+        }
         // lane half hh supplies the scales of key block hh
         const int sb = EXACT ? (dia[hh] ? E8M0_BIAS + vref + P_EXP : (int)sVr[buf][hh] + P_EXP)
                              : (dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP);
@@ -377,15 +403,18 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
                            const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
                            const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
                            const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
-                           const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream) {
+                           const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream,
+                           uint8_t* dump, int* dump_max, int dump_len) {
   if (p.T == 0) return hipSuccess;
   const char* base = static_cast<const char*>(plan);
   FwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.fwd_offset),
             q_codes, k_codes, v_codes, v_key_codes, q_exp, k_exp, v_exp, v_key_exp, v_ref_exp, f4,
-            static_cast<uint16_t*>(o), row_max, row_sum};
+            static_cast<uint16_t*>(o), row_max, row_sum, dump, dump_max, dump_len};
   dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(FWD_THREADS), 0, stream, a); };
-  if (p.path == 1 && p.causal) {
+  if (dump_len > 0) {      // diagnostic instantiation: MXFP8 path, causal, no exact option
+    if (p.D == 64) go(attn_fwd_kernel<64, 0, false, true, true>); else go(attn_fwd_kernel<128, 0, false, true, true>);
+  } else if (p.path == 1 && p.causal) {
     if (p.D == 64) go(attn_fwd_kernel<64, 1, false, true>); else go(attn_fwd_kernel<128, 1, false, true>);
   } else if (p.path == 1) {
     if (p.D == 64) go(attn_fwd_kernel<64, 1, false, false>); else go(attn_fwd_kernel<128, 1, false, false>);

@@ -1,5 +1,6 @@
 // Host side of the flamia C ABI: argument validation, buffer layouts and
 // kernel launches.  Nothing here allocates, frees or synchronises.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -194,6 +195,20 @@ Fp4Operands fp4_operands(const flamia_qtensors* q) {
 
 flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
 
+flamia_status bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dk, void* dv, void* ws,
+                       hipStream_t stream, uint8_t* dump, int dump_len, unsigned long long* ds_counts, bool diag);
+
+// The diagnostic instantiations cover the MXFP8 causal call with one
+// key/value head per query head, atomic dQ and block scales.
+flamia_status diag_supported(const flamia_attn_desc* d, const void* dump, int32_t dump_len) {
+  if (d->path != 0 || kv_heads(d) != d->num_heads || d->exact || d->deterministic || !d->causal)
+    return FLAMIA_ERR_UNSUPPORTED;
+  const int32_t mdl = d->max_doc_len > 0 ? d->max_doc_len : d->total_tokens;
+  if (dump != nullptr && dump_len < std::max(mdl, 1)) return FLAMIA_ERR_INVALID_ARG;
+  return FLAMIA_OK;
+}
+
+
 // Tensor and workspace pointers may be null only for an empty call (T = 0),
 // which launches nothing but the work-list build.
 bool tensors_ok(const flamia_attn_desc* d, std::initializer_list<const void*> ps) {
@@ -306,6 +321,16 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   if (s != FLAMIA_OK) return s;
   if (!qt_complete(desc, qt) || !tensors_ok(desc, {dk, dv, ws})) return FLAMIA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
+  return bwd_main(desc, qt, dk, dv, ws, stream, nullptr, 0, nullptr, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+flamia_status bwd_main(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dk, void* dv, void* ws,
+                       hipStream_t stream, uint8_t* dump, int dump_len, unsigned long long* ds_counts,
+                       bool diag) {
   const Problem p = problem(desc);
   const BwdLayout b = bwd_layout(desc);
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -338,10 +363,18 @@ flamia_status flamia_attn_bwd_main(const flamia_attn_desc* desc, const flamia_qt
   in.q_x = qt->q_fp4_bf16;
   in.k_x = qt->k_fp4_bf16;
   in.qk_scale = qt->qk_tensor_scale;
+  in.dump = dump;
+  in.dump_len = dump_len;
+  in.ds_counts = ds_counts;
+  in.diag = diag;
   const flamia_status st = hip_status(launch_attn_bwd(p, qt->plan, pl, in, stream));
   if (st != FLAMIA_OK || in.gsplit == 1) return st;
   return hip_status(launch_group_reduce(p, in.gsplit, in.dk_f32, in.dv_f32, dk, dv, stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dq,
                                      void* dk, void* ws, hipStream_t stream) {
@@ -359,6 +392,34 @@ flamia_status flamia_attn_bwd_finish(const flamia_attn_desc* desc, const flamia_
                                     w + b.dq_part,
                                     reinterpret_cast<const int*>(static_cast<const uint8_t*>(qt->plan) + pl.det_offset),
                                     pl.det_cap, stream));
+}
+
+flamia_status flamia_attn_fwd_diag(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
+                                   int32_t* row_max, float* row_sum, void* ws, uint8_t* phat, int32_t* phat_max,
+                                   int32_t row_len, hipStream_t stream) {
+  (void)ws;
+  flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if ((s = diag_supported(desc, phat, row_len)) != FLAMIA_OK) return s;
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {o, row_max, row_sum, phat, phat_max}))
+    return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  return hip_status(launch_attn_fwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
+                                    qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp,
+                                    qt->v_ref_exp, fp4_operands(qt), o, row_max, row_sum, stream, phat,
+                                    phat_max, std::max(row_len, 1)));
+}
+
+flamia_status flamia_attn_bwd_main_diag(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* dk,
+                                        void* dv, void* ws, uint8_t* phat, int32_t row_len,
+                                        uint64_t* ds_counts, hipStream_t stream) {
+  flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if ((s = diag_supported(desc, phat, row_len)) != FLAMIA_OK) return s;
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {dk, dv, ws})) return FLAMIA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0) return FLAMIA_ERR_INVALID_ARG;
+  return bwd_main(desc, qt, dk, dv, ws, stream, phat, row_len, reinterpret_cast<unsigned long long*>(ds_counts),
+                  true);
 }
 
 flamia_status flamia_attn_bwd(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,

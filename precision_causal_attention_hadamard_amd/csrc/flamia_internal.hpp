@@ -83,7 +83,8 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
                            const uint8_t* q_codes, const uint8_t* k_codes, const uint8_t* v_codes,
                            const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
                            const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
-                           const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream);
+                           const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream,
+                           uint8_t* dump = nullptr, int* dump_max = nullptr, int dump_len = 0);
 
 // Everything the backward kernel reads and writes.
 struct BwdInputs {
@@ -109,6 +110,13 @@ struct BwdInputs {
   const uint8_t* v_ref_exp;   // exact option: V's in-block prefix maximum
   const void *q_x, *k_x;   // mixed path only
   const float* qk_scale;   // mixed path only
+  // diagnostic instantiation (MXFP8, one head per item, causal, atomic dQ):
+  // P^ codes [H, T, dump_len] (may be null) and counts of nonzero dS and of
+  // those whose E4M3 code is zero (zeroed here before the launch)
+  uint8_t* dump = nullptr;
+  int dump_len = 0;
+  unsigned long long* ds_counts = nullptr;
+  bool diag = false;
 };
 
 hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout& pl, const BwdInputs& in,

@@ -50,7 +50,7 @@ class BwdWsOffsets(ctypes.Structure):
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_plan_build", "flamia_quantize", "flamia_attn_fwd",
            "flamia_attn_bwd", "flamia_attn_bwd_noalloc", "flamia_attn_bwd_prep", "flamia_attn_bwd_main",
-           "flamia_attn_bwd_finish", "flamia_bwd_ws_layout", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
+           "flamia_attn_bwd_finish", "flamia_attn_fwd_diag", "flamia_attn_bwd_main_diag", "flamia_bwd_ws_layout", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
 
 _lib = None
 
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH):
         "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P, P],
         "flamia_attn_bwd_main": [dp, qp, P, P, P, P],
         "flamia_attn_bwd_finish": [dp, qp, P, P, P, P],
+        "flamia_attn_fwd_diag": [dp, qp, P, P, P, P, P, P, I, P],
+        "flamia_attn_bwd_main_diag": [dp, qp, P, P, P, P, I, P, P],
         "flamia_bwd_ws_layout": [dp, ctypes.POINTER(BwdWsOffsets)],
         "flamia_tile_config": [I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
         "flamia_plan_view": [dp, ctypes.POINTER(S), ctypes.POINTER(I), ctypes.POINTER(S), ctypes.POINTER(I),
@@ -169,6 +171,18 @@ def attn_bwd_main(desc, qt: QTensors, dk, dv, ws, stream=None):
 def attn_bwd_finish(desc, qt: QTensors, dq, dk, ws, stream=None):
     _check(load().flamia_attn_bwd_finish(ctypes.byref(desc), ctypes.byref(qt), _ptr(dq), _ptr(dk), _ptr(ws),
                                          _stream(stream)), "flamia_attn_bwd_finish")
+
+
+def attn_fwd_diag(desc, qt: QTensors, o, row_max, row_sum, phat, phat_max, row_len: int, ws=None, stream=None):
+    _check(load().flamia_attn_fwd_diag(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
+                                       _ptr(row_sum), _ptr(ws), _ptr(phat), _ptr(phat_max), row_len,
+                                       _stream(stream)), "flamia_attn_fwd_diag")
+
+
+def attn_bwd_main_diag(desc, qt: QTensors, dk, dv, ws, phat, row_len: int, ds_counts, stream=None):
+    _check(load().flamia_attn_bwd_main_diag(ctypes.byref(desc), ctypes.byref(qt), _ptr(dk), _ptr(dv), _ptr(ws),
+                                            _ptr(phat), row_len, _ptr(ds_counts), _stream(stream)),
+           "flamia_attn_bwd_main_diag")
 
 
 def bwd_ws_layout(desc: AttnDesc) -> BwdWsOffsets:
