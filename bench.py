@@ -2,18 +2,23 @@
 MI355X: quantize + forward + backward over packed documents, inputs resident
 in HBM, one JSON line on stdout.
 
-A step is one whole call (flamia_quantize, flamia_attn_fwd, flamia_attn_bwd;
-the timed steps are replays of the step captured once in a HIP graph, with the
-eager timing beside them)
-over the 2 x 4096-token, 16-head, head-dim-128 workload with 1% outlier
-channels and the Hadamard rotation on.  Throughput counts the algorithmic
-causal FLOPs, 14 * d per (query, key) pair with key <= query inside a
-document (forward 2 products, backward 5); quantization adds no FLOPs but
-its time is inside the step.
+A step is one whole call (flamia_quantize, flamia_attn_fwd, flamia_attn_bwd),
+captured once in a HIP graph and replayed: W warm-up replays, then 3 rounds
+of exactly K timed replays, each bracketed by synchronisations; the median
+round is the headline (the eager timing and per-stage HIP events are beside
+it).  The default workload is the packed-document call: 4 rows x 16384
+tokens of lognormal-length documents, 16 heads, head dim 128; the
+long-context workload (2 x 12288 + short documents, 32768 tokens) is timed
+after it with and without the causal dQ scale and reported under "extra".
+Throughput counts the algorithmic causal FLOPs, 14 * d per (query, key) pair
+with key <= query inside a document (forward 2 products, backward 5);
+quantization adds no FLOPs but its time is inside the step.  The CPU
+baseline (the oracle on a bounded sample, on the host's cores) runs first,
+before the GPU is touched.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
                        [--kv-heads Hk] [--deterministic] [--exact] [--non-causal]
-                       [--causal-dq-scale] [--no-cpu-baseline]
+                       [--causal-dq-scale] [--no-cpu-baseline] [--no-extra]
                        [--copy-calibration]
 """
 
@@ -32,7 +37,8 @@ sys.path.insert(0, ROOT)
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix-core peak (published)
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E bandwidth (published)
-CPU_SAMPLE_HEADS = 8          # oracle sample: document 0, this many heads (about 10-20 s)
+CPU_SAMPLE_MAX_LEN = 2048     # oracle sample: documents of at most this many tokens, all heads
+CPU_WORKERS = 16              # worker processes of the CPU baseline: the GPU's share of a box
 METRIC = "fwd+bwd attention call ms & TFLOP/s incl. quantization; % of MFMA FP8 peak"
 KERNEL_SOURCES = {
     "attn_bwd8_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_bwd.hip",   # MXFP8 path
@@ -128,8 +134,9 @@ def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str, kernel
 
 def toolchain(torch):
     """Versions the numbers depend on (the pages warn that results drift
-    with toolchain versions)."""
-    import subprocess
+    with toolchain versions).  Read from files: nothing is started as a child
+    process once the GPU is in use."""
+    import re
     info = {"torch": torch.__version__, "hip_runtime": getattr(torch.version, "hip", None)}
     try:
         with open("/opt/rocm/.info/version") as f:
@@ -137,32 +144,45 @@ def toolchain(torch):
     except OSError:
         info["rocm"] = None
     try:
-        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
-        info["hipcc"] = next((l.strip() for l in r.stdout.splitlines() if "HIP version" in l), None)
-    except (OSError, subprocess.SubprocessError):
-        info["hipcc"] = None
+        with open("/opt/rocm/include/hip/hip_version.h") as f:
+            h = f.read()
+        v = [re.search(rf"#define HIP_VERSION_{k}\s+(\S+)", h) for k in ("MAJOR", "MINOR", "PATCH")]
+        info["hip_headers"] = ".".join(m.group(1) for m in v) if all(v) else None
+    except OSError:
+        info["hip_headers"] = None
     info["device"] = torch.cuda.get_device_name(0)
     info["arch"] = getattr(torch.cuda.get_device_properties(0), "gcnArchName", None)
     return info
 
 
+def timed_rounds(run, torch, steps: int, rounds: int = 3):
+    """``rounds`` rounds of exactly ``steps`` calls of ``run``, each bracketed
+    by synchronisations; ms per step of every round."""
+    out = []
+    for _ in range(rounds):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        out.append((time.perf_counter() - t0) * 1e3 / steps)
+    return out
+
+
 def graph_replay(call, torch, steps: int, warmup: int, flops: int):
     """The same step captured once in a HIP graph and replayed (the pages time
-    the call this way): K timed replays after W warm-ups, bracketed by
-    synchronisations; reported beside the eager timing."""
+    the call this way): W warm-up replays, then 3 rounds of K timed replays,
+    median round reported; beside the eager timing."""
     try:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             call.step()
         for _ in range(warmup):
             g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
-        return {"ms_per_step": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12, "replays": steps}
+        rounds = timed_rounds(g.replay, torch, steps)
+        ms = sorted(rounds)[len(rounds) // 2]
+        return {"ms_per_step": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12, "replays_per_round": steps,
+                "round_ms": rounds}
     except RuntimeError as e:      # reported, never fatal to the eager measurement
         return {"error": str(e)[:200]}
 
@@ -174,10 +194,18 @@ def worklist_build(flamia, torch, ndocs: int = 131072):
     dev = torch.device("cuda:0")
     z = torch.zeros(ndocs, 1, 64, dtype=torch.bfloat16, device=dev)
     call = flamia.TrainingCall(z, z, z, z, list(range(ndocs + 1)))
+    ms = plan_build_ms(flamia, torch, call)
+    fwd, bwd = call.plan_lists()
+    return {"docs": ndocs, "tokens": ndocs, "ms": ms, "fwd_items": len(fwd), "bwd_items": len(bwd)}
+
+
+def plan_build_ms(flamia, torch, call, reps: int = 20):
+    """Median of ``reps`` work-list builds of a call (HIP events on the launch
+    stream, after 3 warm-ups)."""
     for _ in range(3):
         flamia.plan_build(call.desc, call.qt)
     ms = []
-    for _ in range(20):
+    for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         flamia.plan_build(call.desc, call.qt)
@@ -185,35 +213,113 @@ def worklist_build(flamia, torch, ndocs: int = 131072):
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     ms.sort()
-    fwd, bwd = call.plan_lists()
-    return {"docs": ndocs, "tokens": ndocs, "ms": ms[len(ms) // 2], "fwd_items": len(fwd), "bwd_items": len(bwd)}
+    return ms[len(ms) // 2]
 
 
-def cpu_baseline(wl, cfg: int, causal: bool = True):
-    """The oracle, as it stands, on document 0 and the first few heads of the
-    workload, timed on the host cores."""
+def _oracle_unit(args):
+    """One (document, heads) unit of the CPU baseline, in a worker process
+    with single-threaded BLAS."""
     import numpy as np
-    from threadpoolctl import threadpool_info
-
+    from threadpoolctl import threadpool_limits
     from oracle import attention as A
+    arrs, L, hadamard, path, causal = args
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        A.training_call(*[np.asarray(a, np.float64) for a in arrs], [0, L],
+                        A.Numerics(hadamard=hadamard, path="mixed" if path else "mxfp8", causal=causal))
+        return time.perf_counter() - t0
 
-    s, e = wl.cu_seqlens[0], wl.cu_seqlens[1]
-    g = wl.heads // wl.kv_heads                       # query heads per key/value head
-    nh = max(g, min(CPU_SAMPLE_HEADS, wl.heads) // g * g)
-    arrs = [t[s:e, 0:(nh if t.shape[1] == wl.heads else nh // g)].float().numpy().astype(np.float64)
-            for t in (wl.q, wl.k, wl.v, wl.do)]
-    L = e - s
+
+def host_cpu():
+    """(usable cores, CPU model) of this host."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(wl, causal: bool = True, max_len: int = CPU_SAMPLE_MAX_LEN):
+    """The oracle, as it stands, on a bounded sample of the workload: every
+    head of every document of at most ``max_len`` tokens (the first document
+    if none is that short), one (document, head) per task over a pool of
+    worker processes on the host's cores (at most CPU_WORKERS, the GPU's
+    share of a box).  Run before the GPU is touched."""
+    import multiprocessing as mp
+    import numpy as np
+    nproc, model = host_cpu()
+    workers = max(1, min(CPU_WORKERS, nproc))
+    g = wl.heads // wl.kv_heads
+    docs = [i for i, L in enumerate(wl.doc_lens) if 0 < L <= max_len] or [0]
+    tasks, flops = [], 0
+    for i in docs:
+        s, e = wl.cu_seqlens[i], wl.cu_seqlens[i + 1]
+        L = e - s
+        for hk in range(wl.kv_heads):
+            qs = slice(hk * g, hk * g + g)
+            arrs = [t[s:e][:, qs if t.shape[1] == wl.heads else slice(hk, hk + 1)].float().numpy()
+                    for t in (wl.q, wl.k, wl.v, wl.do)]
+            tasks.append((arrs, L, wl.hadamard, wl.path, causal))
+            flops += 14 * wl.head_dim * g * (L * (L + 1) // 2 if causal else L * L)
+    tasks.sort(key=lambda t: -t[1])            # longest first
     t0 = time.perf_counter()
-    A.training_call(*arrs, [0, L], A.Numerics(hadamard=wl.hadamard, path="mixed" if wl.path else "mxfp8",
-                                              causal=causal))
+    with mp.get_context("fork").Pool(workers) as pool:
+        cpu_s = sum(pool.map(_oracle_unit, tasks, chunksize=1))
     dt = time.perf_counter() - t0
-    flops = 14 * wl.head_dim * nh * (L * (L + 1) // 2 if causal else L * L)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"document 0 ({L} tokens), heads 0-{nh - 1} of the {wl.name} workload: "
-                      f"quantize+fwd+bwd, {dt:.2f} s; fp64 numpy, BLAS threads={threads}, "
-                      "elementwise steps single-threaded",
-            "seconds": dt}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {wl.heads} heads of the {len(docs)} documents of at most {max_len} tokens "
+                      f"({sum(wl.doc_lens[i] for i in docs)} tokens) of the {wl.name} workload: "
+                      f"quantize+fwd+bwd of each (document, key/value head) unit, fp64 numpy, "
+                      f"{workers} worker processes with single-threaded BLAS, {dt:.1f} s wall, {cpu_s:.1f} s CPU",
+            "seconds": dt, "host_cores": nproc, "cpu_model": model, "flops": flops}
+
+
+def measure(flamia, torch, wl, steps, warmup, causal_dq_scale=False, deterministic=False, exact=False,
+            non_causal=False):
+    """Eager stage timing (HIP events between the entry points) over W + K
+    steps, then the graph-replayed headline (median of 3 rounds of K)."""
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
+    call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
+                               causal_dq_scale=wl.causal_dq_scale or causal_dq_scale, path=wl.path,
+                               deterministic=deterministic, exact=exact, causal=not non_causal)
+    if non_causal:
+        pairs = wl.heads * sum(L * L for L in wl.doc_lens)
+    else:
+        pairs = wl.causal_pairs()
+    flops = 14 * wl.head_dim * pairs
+
+    def step(ev=None):
+        if ev is not None: ev[0].record()
+        call.quantize()
+        if ev is not None: ev[1].record()
+        call.forward()
+        if ev is not None: ev[2].record()
+        flamia.attn_bwd_prep(call.desc, call.qt, call.o, call.row_max, call.row_sum, call.do, call.bws)
+        if ev is not None: ev[3].record()
+        flamia.attn_bwd_main(call.desc, call.qt, call.dk, call.dv, call.bws)
+        if ev is not None: ev[4].record()
+        flamia.attn_bwd_finish(call.desc, call.qt, call.dq, call.dk, call.bws)
+        if ev is not None: ev[5].record()
+
+    for _ in range(warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    names = ["quantize", "attn_fwd", "bwd_prep", "attn_bwd", "bwd_finish"]
+    stage_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / steps for i, n in enumerate(names)}
+    graph = graph_replay(call, torch, steps, warmup, flops)
+    ms, timing = (graph["ms_per_step"], "hip_graph_replay") if "ms_per_step" in graph else (eager_ms, "eager")
+    return dict(call=call, pairs=pairs, flops=flops, stage_ms=stage_ms, eager_ms=eager_ms, graph=graph,
+                ms=ms, timing=timing)
 
 
 def main():
@@ -221,7 +327,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped-query variant of the workload: K and V with this many heads (0: one per query head)")
     ap.add_argument("--exact", action="store_true",
@@ -232,6 +338,8 @@ def main():
     ap.add_argument("--causal-dq-scale", action="store_true",
                     help="the optional causal dQ accumulator scale (prescale from causally visible key blocks only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-context workload's extra measurements on the default run")
     ap.add_argument("--deterministic", action="store_true",
                     help="ordered dQ reduction (per-step partials, fixed-order fp16 sum) instead of atomics")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -256,66 +364,24 @@ def main():
 
     from precision_causal_attention_hadamard_amd import flamia, workloads
 
-    flamia.load()
     wl = workloads.config(args.config, kv_heads=args.kv_heads)
-    dev = torch.device("cuda:0")
-    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
-    call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
-                               causal_dq_scale=wl.causal_dq_scale or args.causal_dq_scale, path=wl.path,
-                               deterministic=args.deterministic, exact=args.exact,
-                               causal=not args.non_causal)
-    T, H, d = call.shape
-    Hk = call.kv_heads
-    grouped = Hk != H
-    if args.non_causal:
-        pairs = H * sum(L * L for L in wl.doc_lens)
-        flops = 14 * d * pairs
-    else:
-        pairs = wl.causal_pairs()
-        flops = wl.flops()
+    # the CPU baseline runs first, in forked workers, before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, causal=not args.non_causal)
 
-    def step(ev=None):
-        if ev is not None: ev[0].record()
-        call.quantize()
-        if ev is not None: ev[1].record()
-        call.forward()
-        if ev is not None: ev[2].record()
-        flamia.attn_bwd_prep(call.desc, call.qt, call.o, call.row_max, call.row_sum, call.do, call.bws)
-        if ev is not None: ev[3].record()
-        flamia.attn_bwd_main(call.desc, call.qt, call.dk, call.dv, call.bws)
-        if ev is not None: ev[4].record()
-        flamia.attn_bwd_finish(call.desc, call.qt, call.dq, call.dk, call.bws)
-        if ev is not None: ev[5].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    flamia.load()
+    m = measure(flamia, torch, wl, args.steps, args.warmup, args.causal_dq_scale, args.deterministic,
+                args.exact, args.non_causal)
+    call, stage_ms, pairs, flops, ms_per_step = m["call"], m["stage_ms"], m["pairs"], m["flops"], m["ms"]
     if args.copy_calibration:
+        dev = torch.device("cuda:0")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    names = ["quantize", "attn_fwd", "bwd_prep", "attn_bwd", "bwd_finish"]
-    stage_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps
-                for i, n in enumerate(names)}
-    event_ms = sum(stage_ms.values())
-    eager_ms = ms_per_step
-    # the headline: the same step captured once in a HIP graph and replayed K
-    # times (how the pages time the call); eager timing if capture fails
-    graph = graph_replay(call, torch, args.steps, args.warmup, flops)
-    timing = "eager"
-    if "ms_per_step" in graph:
-        ms_per_step, timing = graph["ms_per_step"], "hip_graph_replay"
+    T, H, d = call.shape
+    Hk = call.kv_heads
+    grouped = Hk != H
     value = flops / (ms_per_step * 1e-3) / 1e12
 
     # roofline of the dominant kernel
@@ -323,6 +389,7 @@ def main():
     # quantizer bytes: bf16 Q, K, V read; Q, K, V, per-key V codes written;
     # one exponent byte per token and head of Q and four planes of the K side
     qbytes = 3 * E + 7 * Ek + T * H + 4 * T * Hk
+    plan_ms = plan_build_ms(flamia, torch, call)
     fwd_mix, bwd_mix = product_mix(d, pairs, bool(wl.path))
     kernels = {
         "attn_bwd": ("attn_bwd_kernel" if wl.path else "attn_bwd8_kernel", "mfma", 10 * d * pairs,
@@ -331,24 +398,29 @@ def main():
         "quantize": ("quant_qkv_kernel", "hbm", qbytes, HBM_PEAK_GBS),
     }
     dom = max(kernels, key=lambda n: stage_ms[n])
-    kname, bound, work, peak = kernels[dom]
+    kname, bound, work, wpeak = kernels[dom]
     t_dom = stage_ms[dom] * 1e-3
     if bound == "mfma":
-        achieved, unit = work / t_dom / 1e12, "TFLOP/s"
+        achieved, unit, peak = work / t_dom / 1e12, "TFLOP/s", FP8_PEAK_TFLOPS
     else:
-        achieved, unit = work / t_dom / 1e9, "GB/s"
+        achieved, unit, peak = work / t_dom / 1e9, "GB/s", HBM_PEAK_GBS
     traffic = (measured_traffic(kname, f"config{args.config}")
                if kname.startswith("attn_bwd") and not grouped and not args.exact and not args.non_causal
+               and not args.deterministic and not args.causal_dq_scale
                else None)
     roofline = {"bound": bound, "kernel": kname, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic,
-                "peak_note": "dtype-weighted: FP8 products at 5000, bf16 products at 2500 TFLOP/s"
-                             if bound == "mfma" else "HBM3E",
-                "frac_of_fp8_peak": achieved / FP8_PEAK_TFLOPS if bound == "mfma" else None,
+                "peak_note": ("MI355X dense FP8 matrix-core peak (every product counted at it)"
+                              if bound == "mfma" else "HBM3E"),
+                "frac_dtype_weighted": achieved / wpeak if bound == "mfma" else None,
+                "dtype_weighted_peak": wpeak if bound == "mfma" else None,
                 "algorithmic_work_per_launch": work, "avg_launch_ms": stage_ms[dom]}
-    quant = {"GB/s": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9,
-             "frac_hbm_peak": qbytes / (stage_ms["quantize"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-             "algorithmic_bytes": qbytes, "launches": 3 if wl.path else 2}
+    qk_ms = max(stage_ms["quantize"] - plan_ms, 1e-6)
+    quant = {"quant_qkv_ms": qk_ms, "plan_ms": plan_ms, "launches": 3 if wl.path else 2,
+             "GB/s": qbytes / (qk_ms * 1e-3) / 1e9,
+             "frac_hbm_peak": qbytes / (qk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "algorithmic_bytes": qbytes,
+             "note": "quant_qkv_ms = quantize stage (HIP events) minus a separately timed work-list build"}
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -358,23 +430,44 @@ def main():
                    "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
                    "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
                    "deterministic": bool(args.deterministic), "exact": bool(args.exact),
-                   "causal": not args.non_causal, "causal_dq_scale": bool(wl.causal_dq_scale or args.causal_dq_scale),
+                   "causal": not args.non_causal,
+                   "causal_dq_scale": bool(wl.causal_dq_scale or args.causal_dq_scale),
                    "causal_pairs": pairs, "flops_per_step": flops},
         "pct_fp8_peak": 100.0 * value / FP8_PEAK_TFLOPS,
-        "stage_ms": stage_ms, "event_ms_per_step": event_ms,
+        "stage_ms": stage_ms, "event_ms_per_step": sum(stage_ms.values()),
         # the attention kernels alone: forward, and backward without the dO
         # quantization / D preparation (quantization excluded on both sides)
         "kernel_only_ms": {"fwd": stage_ms["attn_fwd"], "bwd": stage_ms["attn_bwd"] + stage_ms["bwd_finish"]},
         "quantizer": quant,
         "roofline": roofline,
     }
+    if not (wl.path or grouped or args.exact or args.deterministic or args.non_causal):
+        # one untimed diagnostic backward on the state the timed steps left:
+        # nonzero dS and those whose E4M3 code is zero
+        counts = torch.zeros(2, dtype=torch.int64, device=call.dq.device)
+        flamia.attn_bwd_main_diag(call.desc, call.qt, call.dk, call.dv, call.bws, None, 0, counts)
+        nz, zero = (int(x) for x in counts.cpu())
+        out["ds_zero_fraction"] = {"value": zero / max(nz, 1), "nonzero_ds": nz, "coded_zero": zero}
     out["toolchain"] = toolchain(torch)
-    out["timing"] = timing
-    out["eager_ms_per_step"] = eager_ms
-    out["graph"] = graph
+    out["timing"] = m["timing"]
+    out["eager_ms_per_step"] = m["eager_ms"]
+    out["graph"] = m["graph"]
+    del call, m
+    if args.config == 3 and not args.no_extra and not (args.kv_heads or args.exact or args.non_causal
+                                                       or args.deterministic or args.causal_dq_scale):
+        wl4 = workloads.config(4)
+        extra = {}
+        for tag, cds in (("long_context_32768", False), ("long_context_32768_causal_dq_scale", True)):
+            m4 = measure(flamia, torch, wl4, args.steps, args.warmup, causal_dq_scale=cds)
+            extra[tag] = {"workload": wl4.name, "causal_dq_scale": cds, "ms_per_step": m4["ms"],
+                          "TFLOP/s": m4["flops"] / (m4["ms"] * 1e-3) / 1e12,
+                          "pct_fp8_peak": 100.0 * m4["flops"] / (m4["ms"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+                          "timing": m4["timing"], "stage_ms": m4["stage_ms"], "flops_per_step": m4["flops"]}
+            del m4
+        out["extra"] = extra
     out["worklist"] = worklist_build(flamia, torch)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.config, causal=not args.non_causal)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
