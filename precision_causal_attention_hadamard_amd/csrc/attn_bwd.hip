@@ -1063,8 +1063,9 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
                              __builtin_amdgcn_ldexpf(dsv[4 * g + 2], eq(4 * g + 2) - ec),
                              __builtin_amdgcn_ldexpf(dsv[4 * g + 3], eq(4 * g + 3) - ec));
       } else {
-      // amax >= 0, so its bits order like the values
-      const int e = roundup_exp(__int_as_float(wave_max_i(__float_as_int(amax))));
+      // amax >= 0, so its bits order like the values; the exponent is the
+      // same in every lane, so the rare branch below is a scalar branch
+      const int e = __builtin_amdgcn_readfirstlane(roundup_exp(__int_as_float(wave_max_i(__float_as_int(amax)))));
       eds = e;
       if (e >= -126) {
         const float sc2 = __builtin_amdgcn_ldexpf(1.0f, e);    // the convert divides by it
@@ -1077,6 +1078,10 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           dsc[g] = __builtin_bit_cast(int, w);
         }
       } else {
+        // e = -127 (2^e is no normal fp32 scale): kept out of line -- the
+        // empty volatile statement stops the compiler from evaluating this
+        // branch on every step
+        asm volatile("");
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           dsc[g] = cvt_fp8x4(__builtin_amdgcn_ldexpf(dsv[4 * g], -e), __builtin_amdgcn_ldexpf(dsv[4 * g + 1], -e),
@@ -1133,6 +1138,9 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     if (dq_wave && 32 * dq_qb < nq) {
       v16f acc = v16f{};
       const int iq = 32 * dq_qb + 8 * ((n & 15) >> 2) + 4 * ((lane >> 4) & 1) + (n & 3);
+      // the dQ prescale of this query block (one value per block but for the
+      // exact option, whose prescale is per token)
+      const int dq_sig = EXACT ? 0 : __builtin_amdgcn_readfirstlane(psig[32 * dq_qb]);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const uint8_t* b0 = (EXACT ? sdSQ : sdSK) + 64 * 64 * ks + offQ;
@@ -1140,20 +1148,41 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         const v8i bq = v8i{l0[0], l0[1], h0[0], h0[1], l1[0], l1[1], h1[0], h1[1]};
         const v8i kt = cat8(tr_code16<D>(sK, 64 * ks, 32 * dq_ds + colg, lane),
                             tr_code16<D>(sK, 64 * ks + 32, 32 * dq_ds + colg, lane));
-        if constexpr (EXACT)
+        if constexpr (EXACT) {
           acc = mfma_f8(kt, bq, acc, E8M0_BIAS, sRowE[2 * ks + hh][iq]);
-        else
-          acc = mfma_f8(kt, bq, acc, sKeB[2 * ks + hh], sEds[dq_qb][2 * ks + hh] + E8M0_BIAS);
+        } else {
+          // the prescale 2^-sigma rides in the operands' scales: sigma is one
+          // value per 32-query block here.  Only the sum of the two E8M0 bytes
+          // matters, so what would leave the dS byte's finite range [0, 254]
+          // moves to the K byte; a sum still below 0 scales the product (at
+          // most 2^24 in magnitude) below 2^-230, zero in fp16 either way
+          int kb = sKeB[2 * ks + hh], sb = sEds[dq_qb][2 * ks + hh] + E8M0_BIAS - dq_sig;
+          if (sb < 0) {
+            kb += sb;
+            sb = 0;
+          } else if (sb > 254) {
+            kb += sb - 254;
+            sb = 254;
+          }
+          acc = mfma_f8(kt, bq, acc, min(max(kb, 0), 254), sb);
+        }
       }
-      const int sig = psig[iq];
+      const int sig = EXACT ? psig[iq] : 0;
       uint16_t* dst = reinterpret_cast<uint16_t*>(sKQ) + stage_row(iq) * DQS + 32 * dq_ds + 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         v2h h0, h1;
-        h0[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g], -sig);
-        h0[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 1], -sig);
-        h1[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 2], -sig);
-        h1[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 3], -sig);
+        if constexpr (EXACT) {
+          h0[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g], -sig);
+          h0[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 1], -sig);
+          h1[0] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 2], -sig);
+          h1[1] = (_Float16)__builtin_amdgcn_ldexpf(acc[4 * g + 3], -sig);
+        } else {
+          h0[0] = (_Float16)acc[4 * g];
+          h0[1] = (_Float16)acc[4 * g + 1];
+          h1[0] = (_Float16)acc[4 * g + 2];
+          h1[1] = (_Float16)acc[4 * g + 3];
+        }
         *reinterpret_cast<v2i*>(dst + 8 * g) = v2i{__builtin_bit_cast(int, h0), __builtin_bit_cast(int, h1)};
       }
     }
