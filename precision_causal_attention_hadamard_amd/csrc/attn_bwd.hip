@@ -22,7 +22,8 @@
 //   * S is recomputed from the same Q~/K~ codes with the same 32x32x64
 //     scaled FP8 products as the forward (the forward computes S^T with the
 //     operands swapped, which yields the same bits), then the same
-//     P 2^8 = exp2(fract S') 2^(floor S' + 8 - m~) with the stored integer
+//     evaluation of P 2^8 = 2^(S' + 8 - m~) (p_scaled; its fast form where
+//     the query block's flag allows) with the stored integer
 //     row maximum, the same causal mask, the same diagonal decision (query
 //     and key in one document-local 32-token block) and the same per-key
 //     fold, so the probability codes are the forward's;
@@ -64,7 +65,7 @@ struct BwdArgs {
   const float* il8;       // [H, T] 2^-8 / l
   const float* delta;     // [H, T] -D
   const int* dq_sigma;    // [H, T] dQ prescale exponent
-  const int* qexps;       // [H, T] q_exp | do_exp << 8 | v_ref_exp << 16 (biased bytes)
+  const int* qexps;       // [H, T] q_exp | do_exp << 8 | v_ref_exp << 16 (biased bytes) | fast-form flag << 24
   const uint8_t* do_codes;
   const uint16_t* g;
   uint16_t* dq_acc;
@@ -394,6 +395,9 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
       if (act) {
         float amax = 0.f;
         if (fast) {
+          // one straight-line body per probability form (fast where every
+          // row of the query block allows it)
+          auto rows = [&](auto PW) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int r0 = 32 * qb + 8 * g + 4 * hh;      // first of 4 consecutive query rows
@@ -402,11 +406,13 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
             const v4f dlv = *reinterpret_cast<const v4f*>(pdl + r0);
             float pf[4];
 #pragma unroll
+            for (int r = 0; r < 4; ++r)      // P 2^8
+              pf[r] = decltype(PW)::value
+                          ? __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(sacc[4 * g + r] * c), kov[r])
+                          : p_scaled(sacc[4 * g + r] * c, kov[r]);
+#pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int rr = 4 * g + r;
-              const float x = sacc[rr] * c;
-              const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-              pf[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);   // P 2^8
               dsv[rr] = (pf[r] * ilv[r]) * (pacc[rr] + dlv[r]);
               amax = fmaxf(amax, fabsf(dsv[rr]));
             }
@@ -414,6 +420,11 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
             pe[2 * g] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false));
             pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, true));
           }
+          };
+          if ((__builtin_amdgcn_readfirstlane(pqx[32 * qb]) >> 24) & 1)
+            rows(std::true_type{});
+          else
+            rows(std::false_type{});
         } else {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -428,9 +439,7 @@ __global__ void __launch_bounds__(BWD_THREADS) attn_bwd_kernel(BwdArgs a) {
               const int i = q0 + r0 + r;
               float dsr = 0.f, pev = 0.f;
               if (kv && (!CAUSAL || j <= i) && i < L) {
-                const float x = sacc[rr] * c;
-                const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
+                const float p8 = p_scaled(sacc[rr] * c, kov[r]);
                 dsr = (p8 * ilv[r]) * (pacc[rr] + dlv[r]);
                 if (dia) {
                   const int vref = ((pqx[r0 + r] >> 16) & 255) - E8M0_BIAS;
@@ -952,6 +961,9 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         // exponent; the fold is a constant per lane here
         const int fd = EXACT ? e_key - (sVrB[kb] - E8M0_BIAS) : 0;
         const float ufd = __builtin_amdgcn_ldexpf(1.0f, -fd);
+        // the block's rows as one straight-line body per probability form
+        // (fast where every row of the query block allows it)
+        auto rows = [&](auto PW) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = 32 * qh + 8 * g + 4 * hh;
@@ -959,11 +971,13 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
           float pf[4];
 #pragma unroll
+          for (int r = 0; r < 4; ++r)        // P 2^8
+            pf[r] = decltype(PW)::value
+                        ? __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(sacc[4 * g + r] * c), kov[r])
+                        : p_scaled(sacc[4 * g + r] * c, kov[r]);
+#pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int rr = 4 * g + r;
-            const float x = sacc[rr] * c;
-            const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-            pf[r] = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);   // P 2^8
             dsv[rr] = (pf[r] * ilv[r]) * pacc[rr];
             amax = fmaxf(amax, fabsf(dsv[rr]));
           }
@@ -980,6 +994,11 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           pe[2 * g] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, EXACT ? ufd : 1.0f, false));
           pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, EXACT ? ufd : 1.0f, true));
         }
+        };
+        if ((__builtin_amdgcn_readfirstlane(pqx[32 * qh]) >> 24) & 1)
+          rows(std::true_type{});
+        else
+          rows(std::false_type{});
       } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -993,9 +1012,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
             const int i = q0 + r0 + r;
             float dsr = 0.f, pev = 0.f;
             if (kv && (!CAUSAL || j <= i) && i < L) {
-              const float x = sacc[rr] * c;
-              const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-              const float p8 = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kov[r]);
+              const float p8 = p_scaled(sacc[rr] * c, kov[r]);
               dsr = (p8 * ilv[r]) * pacc[rr];
               int code;
               if (EXACT || dia) {

@@ -10,15 +10,19 @@
 //     codes) are staged token-major in LDS.  The next tile's global loads are
 //     issued into registers before the current tile is computed, and the LDS
 //     is double-buffered, so memory latency hides behind the matrix work;
-//   * S^T = K~ Q~^T on the scaled FP8 matrix cores: the token-block exponents
+//   * S^T = K~ Q~^T on the scaled FP8 matrix cores (all K operand reads of
+//     the tile first, then the products): the token-block exponents
 //     are the operand scales, which realises the pages' factorisation
 //     S_ij = 2^(eQ(i) + eK(j)) x code dot product ([Reading, 4.1]);
 //   * each lane owns one query, so the row maximum is a lane-local max plus
 //     one cross-half exchange; it is rounded up to an integer m~ in the
 //     log2 domain and every rescale of the running output is a power of two;
-//   * P = 2^(n - m~) exp2(r) with n = floor(S'), r = S' - n, S' = S c, so P
-//     relative to the final m~ is exactly P relative to the running m~ times a
-//     power of two (the backward's replay relies on it);
+//   * P 2^8 = 2^(S' + 8 - m~), S' = S c, evaluated as the backward does
+//     (p_scaled): exp2(S') once per score, then the power of two 2^(8 - m~),
+//     which rows with m~ in [-100, 120] apply inside the E4M3 convert and once
+//     to the tile's sum.  P relative to the final m~ is then exactly P
+//     relative to the running m~ times a power of two (the backward's replay
+//     relies on it);
 //   * P^ = E4M3(P 2^8) enters the P^V product with the constant scale 2^-8;
 //     on a query's own 32-token block V uses per-key codes and each key's
 //     exponent is folded into P relative to the largest visible per-key
@@ -94,7 +98,9 @@ attn_fwd_kernel(FwdArgs a) {
   const int L = p.cu[doc + 1] - s_d;
   const int q0 = qt * FWD_BQ;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is read into a scalar register, so every per-wave
+  // condition below (active key blocks, interior tiles) is a scalar branch
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 31, hh = lane >> 5;
   const int qw0 = q0 + 32 * wave;            // this wave's first query
   const int i = qw0 + n;                     // this lane's query (document-local)
@@ -152,27 +158,23 @@ attn_fwd_kernel(FwdArgs a) {
 
   const int kt_last = ((CAUSAL ? min(q0 + FWD_BQ, L) : L) - 1) / FWD_BK;
 
-  // ---- register prefetch of one key tile
+  // ---- register prefetch of one key tile (K side and V side)
   v4i pk[NCH], pv[NCH], pvk[NCH];
   uint32_t psf = 0;           // mixed path: group scales of the prefetched NVFP4 chunk
   uint8_t pke = 0, pve = 0, pvke = 0, pvr = 0;
   const uint8_t* k4doc = PATH ? a.f4.k_fp4 + ((size_t)s_d * rsk + (size_t)hk * D) / 2 : nullptr;
   const uint8_t* ksfdoc = PATH ? a.f4.k_sf + ((size_t)s_d * rsk + (size_t)hk * D) / 16 : nullptr;
-  auto prefetch = [&](int kt) {
+  auto prefetch_k = [&](int kt) {
     const int j0 = kt * FWD_BK;
     const int nvalid = min(FWD_BK, L - j0);
-    const bool diag_tile = (kt >> 1) == qt;   // holds the query tile's diagonal blocks
+    if constexpr (PATH == 0) {
 #pragma unroll
-    for (int c2 = 0; c2 < NCH; ++c2) {
-      const int ch = tid + FWD_THREADS * c2;
-      const int r = ch / (D / 16), c16 = ch % (D / 16);
-      const bool ok = r < nvalid;
-      const size_t off = (size_t)(j0 + r) * rsk + 16 * c16;
-      if constexpr (PATH == 0) pk[c2] = ok ? ld16(kdoc + off) : v4i{0, 0, 0, 0};
-      pv[c2] = ok ? ld16(vdoc + off) : v4i{0, 0, 0, 0};
-      pvk[c2] = (ok && diag_tile) ? ld16(vkdoc + off) : v4i{0, 0, 0, 0};
-    }
-    if constexpr (PATH == 1) {
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        const int ch = tid + FWD_THREADS * c2;
+        const int r = ch / (D / 16), c16 = ch % (D / 16);
+        pk[c2] = r < nvalid ? ld16(kdoc + (size_t)(j0 + r) * rsk + 16 * c16) : v4i{0, 0, 0, 0};
+      }
+    } else {
       // NVFP4 K: 16-byte chunk = 32 codes (d in [32 c, 32 c + 32)) of one key, 2 group scales
       constexpr int CPR = D / 32;       // 16-byte chunks (32 codes) per key row
       if (tid < FWD_BK * CPR) {
@@ -182,196 +184,270 @@ attn_fwd_kernel(FwdArgs a) {
         psf = ok ? *reinterpret_cast<const uint16_t*>(ksfdoc + (size_t)(j0 + r) * rsk / 16 + 2 * c4) : 0u;
       }
     }
+    if (tid < FWD_BK) pke = tid < nvalid ? a.k_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
+  };
+  auto prefetch_v = [&](int kt) {
+    const int j0 = kt * FWD_BK;
+    const int nvalid = min(FWD_BK, L - j0);
+    const bool diag_tile = (kt >> 1) == qt;   // holds the query tile's diagonal blocks
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+      const int ch = tid + FWD_THREADS * c2;
+      const int r = ch / (D / 16), c16 = ch % (D / 16);
+      const bool ok = r < nvalid;
+      const size_t off = (size_t)(j0 + r) * rsk + 16 * c16;
+      pv[c2] = ok ? ld16(vdoc + off) : v4i{0, 0, 0, 0};
+      pvk[c2] = (ok && diag_tile) ? ld16(vkdoc + off) : v4i{0, 0, 0, 0};
+    }
     // exact option: the largest per-key exponent of each key block is the
     // in-block prefix maximum at its last token (only read for blocks that
     // lie wholly before the query's own block)
     if (EXACT && tid < 2) pvr = a.v_ref_exp[hTk + min(j0 + 32 * tid + 31, L - 1)];
     if (tid < FWD_BK) {
       const bool kv = tid < nvalid;
-      pke = kv ? a.k_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
       pve = kv ? a.v_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
       pvke = (kv && diag_tile) ? a.v_key_exp[hTk + j0 + tid] : (uint8_t)E8M0_BIAS;
     }
   };
-  auto commit = [&](int buf, bool diag_tile) {
+  auto commit_k = [&](int slot) {
+    if constexpr (PATH == 0) {
 #pragma unroll
-    for (int c2 = 0; c2 < NCH; ++c2) {
-      const int ch = tid + FWD_THREADS * c2;
-      const int r = ch / (D / 16), c16 = ch % (D / 16);
-      if constexpr (PATH == 0) st16(&sK[buf][r * KS + 16 * c16], pk[c2]);
-      st16(&sV[buf][r * KS + 16 * c16], pv[c2]);
-      if (diag_tile) st16(&sVk[buf][r * KS + 16 * c16], pvk[c2]);   // read on diagonal blocks only
-    }
-    if constexpr (PATH == 1) {
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        const int ch = tid + FWD_THREADS * c2;
+        const int r = ch / (D / 16), c16 = ch % (D / 16);
+        st16(&sK[slot][r * KS + 16 * c16], pk[c2]);
+      }
+    } else {
       constexpr int CPR = D / 32;
       if (tid < FWD_BK * CPR) {
         const int r = tid / CPR, c4 = tid % CPR;
-        uint8_t* dst = &sK[buf][r * KSB + 64 * c4];
+        uint8_t* dst = &sK[slot][r * KSB + 64 * c4];
 #pragma unroll
         for (int w = 0; w < 4; ++w)
           st16(dst + 16 * w, e2m1x8_times_bf16((uint32_t)pk[0][w], fp8_value((int)psf, w >> 1)));
       }
     }
+    if (tid < FWD_BK) sKe[slot][tid] = pke;
+  };
+  auto commit_v = [&](int buf, bool diag_tile) {
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+      const int ch = tid + FWD_THREADS * c2;
+      const int r = ch / (D / 16), c16 = ch % (D / 16);
+      st16(&sV[buf][r * KS + 16 * c16], pv[c2]);
+      if (diag_tile) st16(&sVk[buf][r * KS + 16 * c16], pvk[c2]);   // read on diagonal blocks only
+    }
     if (EXACT && tid < 2) sVr[buf][tid] = pvr;
     if (tid < FWD_BK) {
-      sKe[buf][tid] = pke;
       sVe[buf][tid] = pve;
       sVke[buf][tid] = pvke;
     }
   };
 
-  prefetch(0);
-  commit(0, qt == 0);
-  __syncthreads();
-
-  for (int kt = 0; kt <= kt_last; ++kt) {
-    const int buf = kt & 1;
+  // ---- S^T of key tile kt for this wave's 32 queries (lane = query column)
+  auto scores = [&](int kt, v16f (&st)[2]) {
     const int j0 = kt * FWD_BK;
-    if (kt < kt_last) prefetch(kt + 1);
-
-    if (wave_active) {
-      const uint8_t* tK = sK[buf];
-      bool act[2], dia[2];
-      v16f st[2];
-      // interior tile: every key precedes every query of the wave (or, not
-      // causal, any key) and lies in the document
-      const bool interior = (!CAUSAL || j0 + FWD_BK <= qw0) && j0 + FWD_BK <= L;
-      float tmax = -INFINITY;
+    const uint8_t* tK = sK[kt & 1];
+    const uint8_t* tKe = sKe[kt & 1];
+    if constexpr (PATH == 0) {
+      // all K operand reads first (one LDS round trip), then the products;
+      // a block the wave does not see is computed too (the tile holds its
+      // rows, zero past the document end) and ignored by the softmax
+      v8i ka[2][NS];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const uint8_t* krow = tK + (32 * kb + n) * KS;
+          ka[kb][s] = cat8(ld16(krow + 64 * s + 16 * hh), ld16(krow + 64 * s + 32 + 16 * hh));
+        }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int KB = 2 * kt + kb;
-        act[kb] = (!CAUSAL || KB <= QB) && j0 + 32 * kb < L;
-        dia[kb] = KB == QB;
-        st[kb] = v16f{};
-        if (act[kb]) {
-          if constexpr (PATH == 0) {
-            const uint8_t* krow = tK + (32 * kb + n) * KS;
-            const int ske = sKe[buf][32 * kb + n];
+        const int ske = tKe[32 * kb + n];
+        st[kb] = mfma_f8(ka[kb][0], qa[0], v16f{}, ske, qe);
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-              st[kb] = mfma_f8(cat8(ld16(krow + 64 * s + 16 * hh), ld16(krow + 64 * s + 32 + 16 * hh)), qa[s],
-                               st[kb], ske, qe);
-          } else {
-            const uint8_t* krow = tK + (32 * kb + n) * KSB;
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-              st[kb] = mfma_bf16(__builtin_bit_cast(v8bf, ld16(krow + 2 * (16 * s + 8 * hh))), qb[s], st[kb]);
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) st[kb][rr] = st[kb][rr] * tqk;
-          }
-          if (interior) {
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, st[kb][rr]);
-          } else {
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-              const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-              if ((!CAUSAL || j <= i) && j < L) tmax = fmaxf(tmax, st[kb][rr]);
-            }
-          }
-        }
+        for (int s = 1; s < NS; ++s) st[kb] = mfma_f8(ka[kb][s], qa[s], st[kb], ske, qe);
       }
-      if (act[0] || act[1]) {
-        {   // the other lane half holds the query's other 16 keys of each block
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-          tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const int m_tile = tmax == -INFINITY ? M_NONE : (int)ceilf(tmax * c);
-        const int m_new = max(m_run, m_tile);
-        if (__any(m_new != m_run)) {
-          const int sh = m_run - m_new;   // <= 0
+    } else {
 #pragma unroll
-          for (int db = 0; db < ND; ++db)
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = v16f{};
+        if ((!CAUSAL || 2 * kt + kb <= QB) && j0 + 32 * kb < L) {
+          const uint8_t* krow = tK + (32 * kb + n) * KSB;
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) oacc[db][rr] = __builtin_amdgcn_ldexpf(oacc[db][rr], sh);
-          l_run = __builtin_amdgcn_ldexpf(l_run, sh);
-        }
-        m_run = m_new;
-        const int kofs = 8 - m_run;       // P * 2^8 = exp2(r) * 2^(floor(S') + 8 - m~)
-
-        int pc[2][4];
+          for (int s = 0; s < D / 16; ++s)
+            st[kb] = mfma_bf16(__builtin_bit_cast(v8bf, ld16(krow + 2 * (16 * s + 8 * hh))), qb[s], st[kb]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (interior && !dia[kb]) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              // exact option: the fold of keys 8g + 4hh + r against the block's
-              // reference joins the power of two of P (four exponent bytes at once)
-              int fold4 = 0;
-              if constexpr (EXACT) fold4 = *reinterpret_cast<const int*>(&sVe[buf][32 * kb + 8 * g + 4 * hh]);
-              const int fref = EXACT ? (int)sVr[buf][kb] : 0;
-              float pv4[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float x = st[kb][4 * g + r] * c;
-                const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                const int fe = cvt_floor_i32(x) + kofs;
-                l_run += __builtin_amdgcn_ldexpf(e2, fe);
-                pv4[r] = EXACT ? __builtin_amdgcn_ldexpf(e2, fe + (((fold4 >> (8 * r)) & 255) - fref))
-                               : __builtin_amdgcn_ldexpf(e2, fe);
-              }
-              pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
-            }
-          } else {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              float pv4[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
-                const int j = j0 + 32 * kb + jj;
-                float pr = 0.f;
-                if (act[kb] && (!CAUSAL || j <= i) && j < L) {
-                  const float x = st[kb][4 * g + r] * c;
-                  const float e2 = __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
-                  pr = __builtin_amdgcn_ldexpf(e2, cvt_floor_i32(x) + kofs);
-                }
-                l_run += pr;
-                if constexpr (EXACT)   // every block folds V's per-token exponent into P
-                  pv4[r] = __builtin_amdgcn_ldexpf(pr, ((int)sVe[buf][32 * kb + jj] - E8M0_BIAS) -
-                                                           (dia[kb] ? vref : (int)sVr[buf][kb] - E8M0_BIAS));
-                else
-                  pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
-              }
-              pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
-            }
-          }
-        }
-        const v8i pb = v8i{pc[0][0], pc[0][1], pc[0][2], pc[0][3], pc[1][0], pc[1][1], pc[1][2], pc[1][3]};
-        if constexpr (DIAG) {
-          if (a.dump != nullptr && iv) {
-            const size_t row = (size_t)head * T + s_d + i;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const int j = j0 + 32 * kb + 8 * g + 4 * hh + r;
-                  if (act[kb] && j < L && j < a.dump_len && (!CAUSAL || j <= i))
-                    a.dump[row * a.dump_len + j] = (uint8_t)((pc[kb][g] >> (8 * r)) & 255);
-                }
-            const int nkt = (a.dump_len + FWD_BK - 1) / FWD_BK;
-            if (hh == 0 && kt < nkt) a.dump_max[row * nkt + kt] = m_run;
-          }
-        }
-        // lane half hh supplies the scales of key block hh
-        const int sb = EXACT ? (dia[hh] ? E8M0_BIAS + vref + P_EXP : (int)sVr[buf][hh] + P_EXP)
-                             : (dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP);
-        const int sa = (EXACT || dia[hh]) ? E8M0_BIAS : (int)sVe[buf][32 * hh];
-        // exact option: V's codes are per token everywhere
-        const uint8_t* v0 = (!EXACT && dia[0]) ? sVk[buf] : sV[buf];
-        const uint8_t* v1 = (!EXACT && dia[1]) ? sVk[buf] : sV[buf];
-        const int colg = 16 * ((lane >> 4) & 1);
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const v4i va0 = tr_block16(v0, KS, 0, 32 * db + colg, lane);
-          const v4i va1 = tr_block16(v1, KS, 32, 32 * db + colg, lane);
-          oacc[db] = mfma_f8(cat8(va0, va1), pb, oacc[db], sa, sb);
+          for (int rr = 0; rr < 16; ++rr) st[kb][rr] = st[kb][rr] * tqk;
         }
       }
     }
-    if (kt < kt_last) commit(buf ^ 1, ((kt + 1) >> 1) == qt);
+  };
+
+  // ---- online softmax of key tile kt (scores st) and O^T += V~^T P^^T
+  auto softmax_pv = [&](int kt, v16f (&st)[2]) {
+    const int buf = kt & 1;
+    const int j0 = kt * FWD_BK;
+    bool act[2], dia[2];
+    // interior tile: every key precedes every query of the wave (or, not
+    // causal, any key) and lies in the document
+    const bool interior = (!CAUSAL || j0 + FWD_BK <= qw0) && j0 + FWD_BK <= L;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int KB = 2 * kt + kb;
+      act[kb] = (!CAUSAL || KB <= QB) && j0 + 32 * kb < L;
+      dia[kb] = KB == QB;
+      if (act[kb]) {
+        if (interior) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, st[kb][rr]);
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+            if ((!CAUSAL || j <= i) && j < L) tmax = fmaxf(tmax, st[kb][rr]);
+          }
+        }
+      }
+    }
+    if (!(act[0] || act[1])) return;
+    {   // the other lane half holds the query's other 16 keys of each block
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const int m_tile = tmax == -INFINITY ? M_NONE : (int)ceilf(tmax * c);
+    const int m_new = max(m_run, m_tile);
+    const int sh = m_run - m_new;     // <= 0: every online rescale is a power of two
+    const bool rescale = __any(sh != 0);
+    l_run = __builtin_amdgcn_ldexpf(l_run, sh);
+    m_run = m_new;
+    const int kofs = 8 - m_run;       // P 2^8 = 2^(S' + 8 - m~)
+    // fast form (p_scaled's codes, see there): exp2(S') per score, the row's
+    // 2^(8 - m~) applied inside the E4M3 convert and once to the tile's sum
+    const bool fast = !EXACT && __all(m_run >= P_M_LO && m_run <= P_M_HI);
+    const float psc = __builtin_amdgcn_ldexpf(1.0f, fast ? m_run - 8 : 0);
+
+    // l gains one partial sum per 32-key block, summed in the same order on
+    // every path (the fast form sums exp2(S') and scales the sum by 2^(8 - m~),
+    // which gives the bits of the sum of the scaled terms)
+    int pc[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ls = 0.f;
+      if (fast && interior && !dia[kb]) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(st[kb][4 * g + r] * c);
+            ls += e[r];
+          }
+          pc[kb][g] = cvt_fp8x4_scaled(e[0], e[1], e[2], e[3], psc);
+        }
+        ls = __builtin_amdgcn_ldexpf(ls, kofs);
+      } else if (interior && !dia[kb]) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // exact option: the fold of keys 8g + 4hh + r against the block's
+          // reference joins the power of two of P (four exponent bytes at once)
+          int fold4 = 0;
+          if constexpr (EXACT) fold4 = *reinterpret_cast<const int*>(&sVe[buf][32 * kb + 8 * g + 4 * hh]);
+          const int fref = EXACT ? (int)sVr[buf][kb] : 0;
+          float pv4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pr = p_scaled(st[kb][4 * g + r] * c, kofs);
+            ls += pr;
+            pv4[r] = EXACT ? __builtin_amdgcn_ldexpf(pr, ((fold4 >> (8 * r)) & 255) - fref) : pr;
+          }
+          pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float pv4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
+            const int j = j0 + 32 * kb + jj;
+            float pr = 0.f;
+            if (act[kb] && (!CAUSAL || j <= i) && j < L) pr = p_scaled(st[kb][4 * g + r] * c, kofs);
+            ls += pr;
+            if constexpr (EXACT)   // every block folds V's per-token exponent into P
+              pv4[r] = __builtin_amdgcn_ldexpf(pr, ((int)sVe[buf][32 * kb + jj] - E8M0_BIAS) -
+                                                       (dia[kb] ? vref : (int)sVr[buf][kb] - E8M0_BIAS));
+            else
+              pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
+          }
+          pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+        }
+      }
+      l_run += ls;
+    }
+    if (rescale) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) oacc[db][rr] = __builtin_amdgcn_ldexpf(oacc[db][rr], sh);
+    }
+    const v8i pb = v8i{pc[0][0], pc[0][1], pc[0][2], pc[0][3], pc[1][0], pc[1][1], pc[1][2], pc[1][3]};
+    if constexpr (DIAG) {
+      if (a.dump != nullptr && iv) {
+        const size_t row = (size_t)head * T + s_d + i;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = j0 + 32 * kb + 8 * g + 4 * hh + r;
+              if (act[kb] && j < L && j < a.dump_len && (!CAUSAL || j <= i))
+                a.dump[row * a.dump_len + j] = (uint8_t)((pc[kb][g] >> (8 * r)) & 255);
+            }
+        const int nkt = (a.dump_len + FWD_BK - 1) / FWD_BK;
+        if (hh == 0 && kt < nkt) a.dump_max[row * nkt + kt] = m_run;
+      }
+    }
+    // lane half hh supplies the scales of key block hh
+    const int sb = EXACT ? (dia[hh] ? E8M0_BIAS + vref + P_EXP : (int)sVr[buf][hh] + P_EXP)
+                         : (dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP);
+    const int sa = (EXACT || dia[hh]) ? E8M0_BIAS : (int)sVe[buf][32 * hh];
+    // exact option: V's codes are per token everywhere
+    const uint8_t* v0 = (!EXACT && dia[0]) ? sVk[buf] : sV[buf];
+    const uint8_t* v1 = (!EXACT && dia[1]) ? sVk[buf] : sV[buf];
+    const int colg = 16 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const v4i va0 = tr_block16(v0, KS, 0, 32 * db + colg, lane);
+      const v4i va1 = tr_block16(v1, KS, 32, 32 * db + colg, lane);
+      oacc[db] = mfma_f8(cat8(va0, va1), pb, oacc[db], sa, sb);
+    }
+  };
+
+  // ---- one key step: the next tile's loads go out first, the LDS tiles are
+  // double-buffered, one barrier per step
+  prefetch_k(0);
+  prefetch_v(0);
+  commit_k(0);
+  commit_v(0, qt == 0);
+  __syncthreads();
+
+  for (int kt = 0; kt <= kt_last; ++kt) {
+    if (kt < kt_last) {
+      prefetch_k(kt + 1);
+      prefetch_v(kt + 1);
+    }
+    if (wave_active) {
+      v16f st[2];
+      scores(kt, st);
+      softmax_pv(kt, st);
+    }
+    if (kt < kt_last) {
+      commit_k((kt + 1) & 1);
+      commit_v((kt + 1) & 1, ((kt + 1) >> 1) == qt);
+    }
     __syncthreads();
   }
 

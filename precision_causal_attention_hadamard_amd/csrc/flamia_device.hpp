@@ -315,6 +315,34 @@ __device__ __forceinline__ int cvt_floor_i32(float x) {
   return r;
 }
 
+// ---------------------------------------------------------------- the probability evaluation
+// Both passes evaluate P 2^8 = 2^(S' - m~ + 8) for a score S' and integer row
+// maximum m~ the same way, so the backward's P^ codes replay the forward's:
+// exp2 of S' whole (one transcendental), then the power of two 2^(8 - m~)
+// applied exactly, for S' <= P_X_HI (exp2 finite) when either S' >= P_X_LO
+// (exp2 a normal fp32 value) or m~ >= P_M_LO (then S' < -126 gives
+// P 2^8 < 2^-18, E4M3 code 0, whatever exp2 returns there); otherwise
+// 2^floor(S') exp2(fract(S')).  `kofs` = 8 - m~.
+constexpr float P_X_LO = -126.f, P_X_HI = 120.f;
+constexpr int P_M_LO = -100, P_M_HI = 120;
+__device__ __forceinline__ float p_scaled(float x, int kofs) {
+  const float whole = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(x), kofs);
+  const float split = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x)), cvt_floor_i32(x) + kofs);
+  return (x <= P_X_HI && (x >= P_X_LO || kofs <= 8 - P_M_LO)) ? whole : split;
+}
+// Rows whose m~ lies in [P_M_LO, P_M_HI] take the fast form, p_scaled's whole
+// branch for every visible score (S' <= m~ <= 120), with 2^(8 - m~) applied
+// inside the E4M3 convert (same codes as ldexp, then convert) and once to a
+// block's sum (sums of 64 such values stay finite).
+// E4M3 codes of a / sc .. d / sc for a power of two sc: the convert's scale
+// divides exactly before its single rounding (the same codes as ldexp, then
+// convert).
+__device__ __forceinline__ int cvt_fp8x4_scaled(float a, float b, float c, float d, float sc) {
+  v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, sc, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, sc, true);
+  return __builtin_bit_cast(int, w);
+}
+
 // Transpose reads of swizzled tiles: same results as tr_block16 / tr_bf16x8
 // on the unswizzled tile.
 template <int D>

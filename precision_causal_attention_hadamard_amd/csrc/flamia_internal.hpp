@@ -94,7 +94,7 @@ struct BwdInputs {
   const float* il8;        // [H, T] 2^-8 / l
   const float* delta;      // [H, T] -D
   const int* dq_sigma;     // [H, T]
-  const int* qexps;        // [H, T] q_exp | do_exp << 8 | v_ref_exp << 16
+  const int* qexps;        // [H, T] q_exp | do_exp << 8 | v_ref_exp << 16 | fast-form flag << 24
   const uint8_t* do_codes;
   const void* g;
   void* dq_acc;

@@ -401,6 +401,11 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
           if (bs + r < be) st16(dq_acc + ((size_t)(bs + r) * H + h) * D + 8 * (lane % CPR), v4i{0, 0, 0, 0});
         }
       }
+      // every row of the block has its integer row maximum where the
+      // backward may take the fast probability form (p_scaled); one bit,
+      // bit 24 of each row's qexps word
+      const int mrow = valid ? row_max[(size_t)h * T + tok] : 0;
+      const int pfast = __all(mrow >= P_M_LO && mrow <= P_M_HI) ? 1 << 24 : 0;
       if (valid) {
         // codes, dequantized values, D and G
         float oo[D / 2];
@@ -442,8 +447,8 @@ quant_do_kernel(Problem p, const uint16_t* __restrict__ dout, const uint16_t* __
           do_exp[mi] = (uint8_t)(e + E8M0_BIAS);
           delta[mi] = -dsum;           // the backward adds -D
           il8[mi] = ginv;
-          kofs[mi] = 8 - row_max[mi];    // -P_EXP - m~: P 2^8 = exp2(fract S') 2^(floor S' + kofs)
-          qexps[mi] = (int)q_exp[mi] | ((e + E8M0_BIAS) << 8) | ((int)v_ref_exp[hkT + tok] << 16);
+          kofs[mi] = 8 - mrow;           // -P_EXP - m~: P 2^8 = 2^(S' + kofs)
+          qexps[mi] = (int)q_exp[mi] | ((e + E8M0_BIAS) << 8) | ((int)v_ref_exp[hkT + tok] << 16) | pfast;
           // |dQ partial sum| <= 2.2 d 448^3 2^(e_dO + e_V + e_K) < 2^(27.6 + log2 d + ...);
           // the prescale keeps it below 2^15 in fp16
           dq_sigma[mi] = e + emax_kv + LOG2D + 13;
