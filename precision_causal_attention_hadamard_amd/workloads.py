@@ -158,6 +158,27 @@ def small_packed(seed: int, doc_lens, heads: int = 2, head_dim: int = 64,
                     notes={"outlier_scale": outlier_scale} if outlier_scale else {})
 
 
+def extreme_rows(seed: int, doc_lens, heads: int = 2, head_dim: int = 64, logit: float = 150.0) -> Workload:
+    """Rows whose scores all sit far above or far below zero: K rows are
+    beta u + N(0, 0.3^2) noise with u the all-ones vector, and each query row is
+    s beta u + N(0, 0.3^2) noise with s = +1, -1 or 0 in runs of 32 rows (one
+    32-token block each, cycling +1, 0, -1, 0), beta chosen so that
+    beta^2 d log2(e) / sqrt(d) = ``logit``: scores of the s = +1 rows lie near
+    +logit and of the s = -1 rows near -logit in log2 units."""
+    rng = np.random.default_rng(SEED_BASE + 700 + seed)
+    T = int(sum(doc_lens))
+    d = head_dim
+    beta = float(np.sqrt(logit * np.sqrt(d) / (d * np.log2(np.e))))
+    sign = np.array([1.0, 0.0, -1.0, 0.0], dtype=np.float32)[(np.arange(T) // 32) % 4]
+    noise = lambda: rng.normal(0.0, 0.3, size=(T, heads, d)).astype(np.float32)
+    k = beta + noise()
+    q = sign[:, None, None] * beta + noise()
+    v = rng.standard_normal((T, heads, d), dtype=np.float32)
+    do = rng.standard_normal((T, heads, d), dtype=np.float32)
+    return Workload(f"extreme_rows_{'_'.join(map(str, doc_lens))}_h{heads}_d{d}", _bf16(q), _bf16(k), _bf16(v),
+                    _bf16(do), _cu(doc_lens), heads, d, notes={"logit": logit})
+
+
 def saved_forward_state(seed: int, T: int, H: int, d: int):
     """Stand-ins for the forward's saved outputs, for tests of the backward's
     preparation stage on its own: O bf16 ``[T, H, d]`` drawn N(0, 1), the

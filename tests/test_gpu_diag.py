@@ -33,6 +33,8 @@ CASES = {
     "hadamard_outliers_d128": lambda: W.small_packed(32, [300, 211], heads=2, head_dim=128,
                                                      outlier_scale=20.0, hadamard=True),
     "long_d128_h2": lambda: W.small_packed(95, [1500, 700], heads=2, head_dim=128),
+    # row maxima near +150 and -150 (both probability forms, both passes)
+    "extreme_rows_d128": lambda: W.extreme_rows(3, [230, 100], head_dim=128),
 }
 
 E4M3_VALUES = formats.e4m3_decode(np.arange(256, dtype=np.uint8))
@@ -94,7 +96,7 @@ def test_backward_replays_forward_codes(gpu_lib, case):
     assert checked > 0
 
 
-@pytest.mark.parametrize("case", ["ragged_d64_h3", "hadamard_outliers_d128"])
+@pytest.mark.parametrize("case", ["ragged_d64_h3", "hadamard_outliers_d128", "extreme_rows_d128"])
 def test_diag_calls_give_the_plain_results(gpu_lib, case):
     wl = CASES[case]()
     call, *_ = run_diag(gpu_lib, wl)

@@ -71,6 +71,9 @@ CASES = {
     "ragged_d128_h4": lambda: W.small_packed(33, [129, 64, 31, 250], heads=4, head_dim=128),
     # zero-length documents at the start, in the middle and at the end of the packed batch
     "empty_docs_d64": lambda: W.small_packed(37, [0, 45, 0, 0, 100, 33, 0], heads=2, head_dim=64),
+    # row maxima near +150 and -150 beside ordinary rows: both probability forms
+    "extreme_rows_d64": lambda: W.extreme_rows(1, [200, 97]),
+    "extreme_rows_d128": lambda: W.extreme_rows(2, [160, 130], head_dim=128),
 }
 
 
