@@ -290,28 +290,32 @@ attn_fwd_kernel(FwdArgs a) {
     const int j0 = kt * FWD_BK;
     bool act[2], dia[2];
     // interior tile: every key precedes every query of the wave (or, not
-    // causal, any key) and lies in the document
+    // causal, any key) and lies in the document; both blocks are then active
+    // (and, causal, neither is diagonal)
     const bool interior = (!CAUSAL || j0 + FWD_BK <= qw0) && j0 + FWD_BK <= L;
-    float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int KB = 2 * kt + kb;
       act[kb] = (!CAUSAL || KB <= QB) && j0 + 32 * kb < L;
       dia[kb] = KB == QB;
-      if (act[kb]) {
-        if (interior) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, st[kb][rr]);
-        } else {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            if ((!CAUSAL || j <= i) && j < L) tmax = fmaxf(tmax, st[kb][rr]);
-          }
-        }
-      }
     }
     if (!(act[0] || act[1])) return;
+    // the tile's maximum over the visible scores (all 64 on an interior tile)
+    float tmax = -INFINITY;
+    if (interior) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, st[kb][rr]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          if (act[kb] && (!CAUSAL || j <= i) && j < L) tmax = fmaxf(tmax, st[kb][rr]);
+        }
+    }
     {   // the other lane half holds the query's other 16 keys of each block
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -332,10 +336,12 @@ attn_fwd_kernel(FwdArgs a) {
     // every path (the fast form sums exp2(S') and scales the sum by 2^(8 - m~),
     // which gives the bits of the sum of the scaled terms)
     int pc[2][4];
+    if (fast && interior && !dia[0] && !dia[1]) {
+      // the common step, straight-line over both blocks (without the causal
+      // mask an interior tile may still hold the query's diagonal block)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float ls = 0.f;
-      if (fast && interior && !dia[kb]) {
+      for (int kb = 0; kb < 2; ++kb) {
+        float ls = 0.f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float e[4];
@@ -346,45 +352,51 @@ attn_fwd_kernel(FwdArgs a) {
           }
           pc[kb][g] = cvt_fp8x4_scaled(e[0], e[1], e[2], e[3], psc);
         }
-        ls = __builtin_amdgcn_ldexpf(ls, kofs);
-      } else if (interior && !dia[kb]) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // exact option: the fold of keys 8g + 4hh + r against the block's
-          // reference joins the power of two of P (four exponent bytes at once)
-          int fold4 = 0;
-          if constexpr (EXACT) fold4 = *reinterpret_cast<const int*>(&sVe[buf][32 * kb + 8 * g + 4 * hh]);
-          const int fref = EXACT ? (int)sVr[buf][kb] : 0;
-          float pv4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pr = p_scaled(st[kb][4 * g + r] * c, kofs);
-            ls += pr;
-            pv4[r] = EXACT ? __builtin_amdgcn_ldexpf(pr, ((fold4 >> (8 * r)) & 255) - fref) : pr;
-          }
-          pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float pv4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
-            const int j = j0 + 32 * kb + jj;
-            float pr = 0.f;
-            if (act[kb] && (!CAUSAL || j <= i) && j < L) pr = p_scaled(st[kb][4 * g + r] * c, kofs);
-            ls += pr;
-            if constexpr (EXACT)   // every block folds V's per-token exponent into P
-              pv4[r] = __builtin_amdgcn_ldexpf(pr, ((int)sVe[buf][32 * kb + jj] - E8M0_BIAS) -
-                                                       (dia[kb] ? vref : (int)sVr[buf][kb] - E8M0_BIAS));
-            else
-              pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
-          }
-          pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
-        }
+        l_run += __builtin_amdgcn_ldexpf(ls, kofs);
       }
-      l_run += ls;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float ls = 0.f;
+        if (interior && !dia[kb]) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            // exact option: the fold of keys 8g + 4hh + r against the block's
+            // reference joins the power of two of P (four exponent bytes at once)
+            int fold4 = 0;
+            if constexpr (EXACT) fold4 = *reinterpret_cast<const int*>(&sVe[buf][32 * kb + 8 * g + 4 * hh]);
+            const int fref = EXACT ? (int)sVr[buf][kb] : 0;
+            float pv4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float pr = p_scaled(st[kb][4 * g + r] * c, kofs);
+              ls += pr;
+              pv4[r] = EXACT ? __builtin_amdgcn_ldexpf(pr, ((fold4 >> (8 * r)) & 255) - fref) : pr;
+            }
+            pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float pv4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
+              const int j = j0 + 32 * kb + jj;
+              float pr = 0.f;
+              if (act[kb] && (!CAUSAL || j <= i) && j < L) pr = p_scaled(st[kb][4 * g + r] * c, kofs);
+              ls += pr;
+              if constexpr (EXACT)   // every block folds V's per-token exponent into P
+                pv4[r] = __builtin_amdgcn_ldexpf(pr, ((int)sVe[buf][32 * kb + jj] - E8M0_BIAS) -
+                                                         (dia[kb] ? vref : (int)sVr[buf][kb] - E8M0_BIAS));
+              else
+                pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
+            }
+            pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+          }
+        }
+        l_run += ls;
+      }
     }
     if (rescale) {
 #pragma unroll
