@@ -79,6 +79,7 @@ class Numerics:
     softmax_scale: float | None = None
     nvfp4_amax: tuple | None = None  # (Q, K) tensor max-abs when the inputs are a slice
     exact: bool = False              # the exact option (see exact_fold_reference, _ds_exact)
+    p_format: str = "e4m3"           # probability operand of O: e4m3 | nvfp4 (p4_quantize)
 
 
 def scale_constants(d: int, softmax_scale: float | None):
@@ -174,6 +175,44 @@ def _ds_exact(ds, valid, e_fold, rows: bool, rule: str):
     return out / (scale[None, :] if rows else scale[:, None])
 
 
+P4_GROUP = 16       # keys per group of the 4-bit probability operand
+
+
+def roundup_e2m1(a):
+    """Smallest integer e with a <= 6 * 2^e, for a > 0 (elementwise): the
+    round-up scale rule of the token-block exponent with E2M1's largest
+    magnitude 6 in place of E4M3's 448.  With a = M 2^k, M in [1, 2): since
+    6 * 2^e = 1.5 * 2^(e + 2), e = k - 2 when M <= 1.5, else k - 1."""
+    m, k = np.frexp(np.asarray(a, dtype=np.float64))     # a = m 2^k, m in [0.5, 1)
+    return np.where(2.0 * m <= 1.5, k - 3, k - 2).astype(np.int64)
+
+
+def p4_quantize(x, valid):
+    """4-bit probability operand, log-domain NVFP4 ([Summary, §3.5.2 Softmax
+    Throughput and MMA Scheduling]; [Reading, 4.4] second bullet): the pages
+    quantize P to NVFP4 by taking each group's largest exponent and
+    subtracting, so the group scale is a power of two and no element is
+    divided.  ``x``: [rows, keys] fp64, nonnegative (P 2^8 times the diagonal
+    fold); ``valid``: the visible pairs.  Groups are 16 consecutive keys from
+    the document start, per row.  Per group, e = roundup_e2m1 of the largest
+    visible x (a group with none, or only zeros, is all zero); each visible
+    element becomes E2M1_RNE(x 2^-e) 2^e (at most 6 2^e, so nothing saturates),
+    and that value enters the FP8 product as an E4M3 number (exact but below
+    E4M3's range).  Returns the values (0 where not visible)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    n = x.shape[1]
+    for g0 in range(0, n, P4_GROUP):
+        sl = slice(g0, min(g0 + P4_GROUP, n))
+        seg = np.where(valid[:, sl], x[:, sl], 0.0)
+        amax = seg.max(axis=1)
+        nz = amax > 0
+        e = np.where(nz, roundup_e2m1(np.where(nz, amax, 1.0)), 0)
+        q = formats.e2m1_round(np.ldexp(seg, -e[:, None]))
+        out[:, sl] = np.where(valid[:, sl], np.ldexp(q, e[:, None]), 0.0)
+    return formats.e4m3_round(out)
+
+
 def forward_doc(qd, kd, vblk, vkey, v_exp_blk, v_exp_key, c32, num: Numerics):
     """Forward of one (document, head).
 
@@ -207,9 +246,13 @@ def forward_doc(qd, kd, vblk, vkey, v_exp_blk, v_exp_key, c32, num: Numerics):
         e_ref2 = np.broadcast_to(e_ref[:, None], (L, L))
     if num.quantize_p:
         f = np.where(diag, np.ldexp(1.0, np.minimum(v_exp_key[None, :] - e_ref2, 0)), 1.0)
-        p_off = np.ldexp(formats.e4m3_round(np.ldexp(p, -P_EXP)), P_EXP)
-        p_dia = np.ldexp(formats.e4m3_round(np.ldexp(p * f, -P_EXP)), P_EXP) / f
-        peff = np.where(diag, p_dia, p_off)
+        if num.p_format == "nvfp4":
+            # one 4-bit operand over every visible pair (the fold applied first)
+            peff = np.ldexp(p4_quantize(np.ldexp(p * f, -P_EXP), valid), P_EXP) / f
+        else:
+            p_off = np.ldexp(formats.e4m3_round(np.ldexp(p, -P_EXP)), P_EXP)
+            p_dia = np.ldexp(formats.e4m3_round(np.ldexp(p * f, -P_EXP)), P_EXP) / f
+            peff = np.where(diag, p_dia, p_off)
     else:
         peff = p
     o = (np.where(diag, 0.0, peff) @ vblk + np.where(diag, peff, 0.0) @ vkey) / l[:, None]

@@ -33,7 +33,8 @@ Bounds used (per (document, head), vectorised; e = error, rel = relative):
   rel <= 2^(c e_S + 2u|S'|) (1 + 4 u) - 1; the integer row maximum is taken as
   equal on both sides (a different one scales every P of the row by an exact
   power of two, which leaves O and dS unchanged outside E4M3 subnormals);
-* P^: the code span of [x (1 - rel), x (1 + rel)], x = P 2^8 f;
+* P^: the code span of [x (1 - rel), x (1 + rel)], x = P 2^8 f (for the 4-bit
+  operand also over the group scales the group's interval maxima allow);
 * l = sum P: rel <= (1 + max rel(P) over the row)(1 + gamma_L) - 1;
 * O (before bf16): w = (1 + rel(l)) sum_j span(P^)_ij |V_j| / l_i
   + gamma_L (|P^| |V|)_i / l_i + (rel(l) + u) |O_i|; the bf16 span of
@@ -76,6 +77,33 @@ def _bf16_span(x, w):
     return _span(formats.bf16_round, x - w, x + w)
 
 
+def _p4_span(lo, hi, valid):
+    """Width of the values the 4-bit probability operand (p4_quantize) can
+    give an element whose value lies in [lo, hi] while every element of its
+    group lies in its own interval: the group scale is one of the round-up
+    exponents of the group's smallest and largest possible maxima, and under
+    each scale the E2M1 rounding (then the E4M3 carry) is monotone."""
+    from .attention import P4_GROUP, roundup_e2m1
+    out = np.zeros_like(lo)
+    n = lo.shape[1]
+    for g0 in range(0, n, P4_GROUP):
+        sl = slice(g0, min(g0 + P4_GROUP, n))
+        v = valid[:, sl]
+        a_lo = np.where(v, lo[:, sl], 0.0).max(axis=1)
+        a_hi = np.where(v, hi[:, sl], 0.0).max(axis=1)
+        qmin = np.full(lo[:, sl].shape, np.inf)
+        qmax = np.full(lo[:, sl].shape, -np.inf)
+        for a in (a_lo, a_hi):
+            nz = a > 0
+            e = np.where(nz, roundup_e2m1(np.where(nz, a, 1.0)), 0)[:, None]
+            q_lo = np.where(nz[:, None], formats.e4m3_round(np.ldexp(formats.e2m1_round(np.ldexp(lo[:, sl], -e)), e)), 0.0)
+            q_hi = np.where(nz[:, None], formats.e4m3_round(np.ldexp(formats.e2m1_round(np.ldexp(hi[:, sl], -e)), e)), 0.0)
+            qmin = np.minimum(qmin, q_lo)
+            qmax = np.maximum(qmax, q_hi)
+        out[:, sl] = np.where(v, qmax - qmin, 0.0)
+    return out
+
+
 def doc_head_allowances(fw, qs, ks, vblk, vkey, dod, num: Numerics, c32):
     """Allowances of one (document, head).  qs, ks: score operands; vblk,
     vkey, dod as for forward_doc/backward_doc.  Returns the O allowance
@@ -95,7 +123,10 @@ def doc_head_allowances(fw, qs, ks, vblk, vkey, dod, num: Numerics, c32):
     if num.quantize_p:
         f = fw["fold"]                      # the forward's fold factor of every pair (1 off the fold)
         x = np.ldexp(p * f, 8)
-        span_pe = np.where(valid, np.ldexp(_e4m3_span(x * (1 - rel_p), x * (1 + rel_p)), -8) / f, 0.0)
+        if num.p_format == "nvfp4":
+            span_pe = np.where(valid, np.ldexp(_p4_span(x * (1 - rel_p), x * (1 + rel_p), valid), -8) / f, 0.0)
+        else:
+            span_pe = np.where(valid, np.ldexp(_e4m3_span(x * (1 - rel_p), x * (1 + rel_p)), -8) / f, 0.0)
     else:
         span_pe = rel_p * p
     rel_l = (1 + np.max(rel_p, axis=1, initial=0.0)) * (1 + gamma(L)) - 1
