@@ -187,6 +187,35 @@ def graph_replay(call, torch, steps: int, warmup: int, flops: int):
         return {"error": str(e)[:200]}
 
 
+def p4_forward_timing(flamia, torch, wl, reps: int = 20):
+    """The forward with the 4-bit probability operand (flamia_attn_fwd_p4)
+    beside the plain forward on the same quantized operands: HIP events on the
+    launch stream around each launch, median of ``reps`` after 3 warm-ups."""
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
+    call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard)
+    call.quantize()
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return sorted(ms)[len(ms) // 2]
+
+    f8 = med(call.forward)
+    f4 = med(lambda: flamia.attn_fwd_p4(call.desc, call.qt, call.o, call.row_max, call.row_sum, call.fws))
+    del call
+    return {"workload": wl.name, "fwd_ms": f8, "fwd_p4_ms": f4, "p4_over_fp8": f4 / f8,
+            "note": "4-bit probability operand (log-domain NVFP4, groups of 16 keys) carried into the FP8 P^V product"}
+
+
 def worklist_build(flamia, torch, ndocs: int = 131072):
     """The GPU work-list build alone (flamia_plan_build) on the pages' stress
     case: ndocs single-token documents.  HIP events on the launch stream,
@@ -456,7 +485,7 @@ def main():
     if args.config == 3 and not args.no_extra and not (args.kv_heads or args.exact or args.non_causal
                                                        or args.deterministic or args.causal_dq_scale):
         wl4 = workloads.config(4)
-        extra = {}
+        extra = {"p4_forward": p4_forward_timing(flamia, torch, wl)}
         for tag, cds in (("long_context_32768", False), ("long_context_32768_causal_dq_scale", True)):
             m4 = measure(flamia, torch, wl4, args.steps, args.warmup, causal_dq_scale=cds)
             extra[tag] = {"workload": wl4.name, "causal_dq_scale": cds, "ms_per_step": m4["ms"],

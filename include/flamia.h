@@ -247,6 +247,25 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
                               int32_t* row_max, float* row_sum, void* ws, hipStream_t stream);
 
 /*
+ * flamia_attn_fwd_p4 -- the forward with the 4-bit probability operand,
+ * [Summary, §3.5.2 Softmax Throughput and MMA Scheduling] and [Reading, 4.4]
+ * second bullet: the probabilities of the NVFP4 path are quantized in the
+ * log domain.  Everything is flamia_attn_fwd's but for the operand of the
+ * P^V product: per query row and group of 16 consecutive keys (document-
+ * aligned), a power-of-two scale 2^e with e the smallest integer such that
+ * the group's largest P * 2^8 (times the diagonal fold) is at most 6 * 2^e,
+ * E2M1 codes of the values over 2^e (round to nearest even), and the products
+ * code x 2^e carried into the FP8 product as E4M3 values.  row_max and
+ * row_sum are flamia_attn_fwd's (l sums the unquantized P).  Arguments as for
+ * flamia_attn_fwd.  The backward is not defined for this forward's output
+ * (its dV would need the same 4-bit operand).
+ * Errors: FLAMIA_ERR_UNSUPPORTED on the mixed path or with the exact option;
+ * otherwise as flamia_attn_fwd.
+ */
+flamia_status flamia_attn_fwd_p4(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
+                                 int32_t* row_max, float* row_sum, void* ws, hipStream_t stream);
+
+/*
  * flamia_attn_bwd -- backward pass, [Summary, §3.3 Forward-Backward Numerical
  * Consistency] and [Reading, 4.3]/[Reading, 4.4] third bullet: dO is
  * token-block quantized and D = rowsum(dO~ * O) is built from that same

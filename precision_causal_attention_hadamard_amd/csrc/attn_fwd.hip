@@ -72,9 +72,12 @@ struct FwdArgs {
 // DIAG: also writes each P^ code and the running row maximum it was taken
 // against, for the check that the backward replays the forward's codes
 // ([Summary, §3.3 Forward-Backward Numerical Consistency]).
-template <int D, int PATH, bool EXACT, bool CAUSAL, bool DIAG = false>
+// P4: the 4-bit probability operand (log-domain NVFP4, p4_block) in place of
+// E4M3 P^ (MXFP8 path, without the exact option).
+template <int D, int PATH, bool EXACT, bool CAUSAL, bool DIAG = false, bool P4 = false>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(FwdArgs a) {
+  static_assert(!P4 || (PATH == 0 && !EXACT && !DIAG), "4-bit probability operand: MXFP8 path only");
   constexpr int KS = D + 16;          // token-major row stride (bytes)
   constexpr int KSB = 2 * D + 16;     // token-major bf16 row stride (bytes), mixed path K
   constexpr int NS = D / 64;          // K-steps of the FP8 S product
@@ -342,15 +345,25 @@ attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float ls = 0.f;
+        if constexpr (P4) {
+          float e[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float e[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            e[r] = __builtin_amdgcn_exp2f(st[kb][4 * g + r] * c);
-            ls += e[r];
+          for (int rr = 0; rr < 16; ++rr) {
+            e[rr] = __builtin_amdgcn_exp2f(st[kb][rr] * c);
+            ls += e[rr];
           }
-          pc[kb][g] = cvt_fp8x4_scaled(e[0], e[1], e[2], e[3], psc);
+          p4_block(e, psc, pc[kb]);
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float e[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              e[r] = __builtin_amdgcn_exp2f(st[kb][4 * g + r] * c);
+              ls += e[r];
+            }
+            pc[kb][g] = cvt_fp8x4_scaled(e[0], e[1], e[2], e[3], psc);
+          }
         }
         l_run += __builtin_amdgcn_ldexpf(ls, kofs);
       }
@@ -358,6 +371,7 @@ attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float ls = 0.f;
+        float pv16[16];          // 4-bit operand: the block's values before its group quantization
         if (interior && !dia[kb]) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -372,8 +386,9 @@ attn_fwd_kernel(FwdArgs a) {
               const float pr = p_scaled(st[kb][4 * g + r] * c, kofs);
               ls += pr;
               pv4[r] = EXACT ? __builtin_amdgcn_ldexpf(pr, ((fold4 >> (8 * r)) & 255) - fref) : pr;
+              pv16[4 * g + r] = pv4[r];
             }
-            pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+            if constexpr (!P4) pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
           }
         } else {
 #pragma unroll
@@ -391,10 +406,12 @@ attn_fwd_kernel(FwdArgs a) {
                                                          (dia[kb] ? vref : (int)sVr[buf][kb] - E8M0_BIAS));
               else
                 pv4[r] = dia[kb] ? __builtin_amdgcn_ldexpf(pr, ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref) : pr;
+              pv16[4 * g + r] = pv4[r];
             }
-            pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+            if constexpr (!P4) pc[kb][g] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
           }
         }
+        if constexpr (P4) p4_block(pv16, 1.0f, pc[kb]);
         l_run += ls;
       }
     }
@@ -492,7 +509,7 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
                            const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
                            const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
                            const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream,
-                           uint8_t* dump, int* dump_max, int dump_len) {
+                           uint8_t* dump, int* dump_max, int dump_len, bool p4) {
   if (p.T == 0) return hipSuccess;
   const char* base = static_cast<const char*>(plan);
   FwdArgs a{p, reinterpret_cast<const int*>(base), reinterpret_cast<const int2*>(base + pl.fwd_offset),
@@ -500,7 +517,15 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
             static_cast<uint16_t*>(o), row_max, row_sum, dump, dump_max, dump_len};
   dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(FWD_THREADS), 0, stream, a); };
-  if (dump_len > 0) {      // diagnostic instantiation: MXFP8 path, causal, no exact option
+  if (p4) {                // 4-bit probability operand: MXFP8 path, no exact option
+    if (p.causal) {
+      if (p.D == 64) go(attn_fwd_kernel<64, 0, false, true, false, true>);
+      else go(attn_fwd_kernel<128, 0, false, true, false, true>);
+    } else {
+      if (p.D == 64) go(attn_fwd_kernel<64, 0, false, false, false, true>);
+      else go(attn_fwd_kernel<128, 0, false, false, false, true>);
+    }
+  } else if (dump_len > 0) {      // diagnostic instantiation: MXFP8 path, causal, no exact option
     if (p.D == 64) go(attn_fwd_kernel<64, 0, false, true, true>); else go(attn_fwd_kernel<128, 0, false, true, true>);
   } else if (p.path == 1 && p.causal) {
     if (p.D == 64) go(attn_fwd_kernel<64, 1, false, true>); else go(attn_fwd_kernel<128, 1, false, true>);

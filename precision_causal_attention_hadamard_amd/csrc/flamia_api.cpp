@@ -298,6 +298,20 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
                                     qt->v_ref_exp, fp4_operands(qt), o, row_max, row_sum, stream));
 }
 
+flamia_status flamia_attn_fwd_p4(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
+                                 int32_t* row_max, float* row_sum, void* ws, hipStream_t stream) {
+  (void)ws;
+  const flamia_status s = validate(desc);
+  if (s != FLAMIA_OK) return s;
+  if (desc->path != 0 || desc->exact) return FLAMIA_ERR_UNSUPPORTED;
+  if (!qt_complete(desc, qt) || !tensors_ok(desc, {o, row_max, row_sum})) return FLAMIA_ERR_INVALID_ARG;
+  const Problem p = problem(desc);
+  return hip_status(launch_attn_fwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,
+                                    qt->v_key_codes, qt->q_exp, qt->k_exp, qt->v_exp, qt->v_key_exp,
+                                    qt->v_ref_exp, fp4_operands(qt), o, row_max, row_sum, stream, nullptr, nullptr,
+                                    0, true));
+}
+
 flamia_status flamia_attn_bwd_prep(const flamia_attn_desc* desc, const flamia_qtensors* qt, const void* o,
                                    const int32_t* row_max, const float* row_sum, const void* dout, void* ws,
                                    hipStream_t stream) {

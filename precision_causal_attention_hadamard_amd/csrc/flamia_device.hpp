@@ -334,6 +334,47 @@ __device__ __forceinline__ float p_scaled(float x, int kofs) {
 // branch for every visible score (S' <= m~ <= 120), with 2^(8 - m~) applied
 // inside the E4M3 convert (same codes as ldexp, then convert) and once to a
 // block's sum (sums of 64 such values stay finite).
+// ---------------------------------------------------------------- 4-bit probability operand
+// The lane's 16 nonnegative values of one 32-key block (register rr = 4g + r
+// holds key 8g + 4hh + r) in 4-bit form: groups of 16 consecutive keys are
+// registers 0-7 and 8-15 of the two lane halves.  Per group, e = the smallest
+// integer with max <= 6 2^e (the group maximum = M 2^k: e = k - 2 for M <= 1.5,
+// else k - 1), the E2M1 codes of v / 2^e by the hardware convert (round to
+// nearest even, dividing by its scale), and the values code x 2^e back as E4M3
+// codes of value / sc (the convert's scale again; exact but below E4M3's
+// range).  A group whose maximum is zero, subnormal or needs a scale below
+// 2^-126 becomes zero (its values are then far below E4M3's range at any
+// scale the callers pass).
+__device__ __forceinline__ void p4_block(const float (&v)[16], float sc, int (&pc)[4]) {
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    float gm = fmaxf(fmaxf(fmaxf(v[8 * h2], v[8 * h2 + 1]), fmaxf(v[8 * h2 + 2], v[8 * h2 + 3])),
+                     fmaxf(fmaxf(v[8 * h2 + 4], v[8 * h2 + 5]), fmaxf(v[8 * h2 + 6], v[8 * h2 + 7])));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gm), __float_as_uint(gm), false, false);
+    gm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const uint32_t b = __float_as_uint(gm);
+    const int be = (int)(b >> 23);
+    const int e = be - 127 - ((b & 0x7fffffu) <= 0x400000u ? 2 : 1);
+    if (be == 0 || e < -126) {
+      pc[2 * h2] = 0;
+      pc[2 * h2 + 1] = 0;
+      continue;
+    }
+    const float s2 = __builtin_amdgcn_ldexpf(1.0f, e);
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      const int g = 2 * h2 + g2;
+      uint32_t c4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[4 * g], v[4 * g + 1], s2, 0);
+      c4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c4, v[4 * g + 2], v[4 * g + 3], s2, 1);
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c4, s2, 0);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c4, s2, 1);
+      v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, lo[0], lo[1], sc, false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, hi[0], hi[1], sc, true);
+      pc[g] = __builtin_bit_cast(int, w);
+    }
+  }
+}
+
 // E4M3 codes of a / sc .. d / sc for a power of two sc: the convert's scale
 // divides exactly before its single rounding (the same codes as ldexp, then
 // convert).

@@ -84,7 +84,8 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
                            const uint8_t* v_key_codes, const uint8_t* q_exp, const uint8_t* k_exp,
                            const uint8_t* v_exp, const uint8_t* v_key_exp, const uint8_t* v_ref_exp,
                            const Fp4Operands& f4, void* o, int* row_max, float* row_sum, hipStream_t stream,
-                           uint8_t* dump = nullptr, int* dump_max = nullptr, int dump_len = 0);
+                           uint8_t* dump = nullptr, int* dump_max = nullptr, int dump_len = 0,
+                           bool p4 = false);
 
 // Everything the backward kernel reads and writes.
 struct BwdInputs {

@@ -49,7 +49,7 @@ class BwdWsOffsets(ctypes.Structure):
 
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_plan_build", "flamia_quantize", "flamia_attn_fwd",
-           "flamia_attn_bwd", "flamia_attn_bwd_noalloc", "flamia_attn_bwd_prep", "flamia_attn_bwd_main",
+           "flamia_attn_fwd_p4", "flamia_attn_bwd", "flamia_attn_bwd_noalloc", "flamia_attn_bwd_prep", "flamia_attn_bwd_main",
            "flamia_attn_bwd_finish", "flamia_attn_fwd_diag", "flamia_attn_bwd_main_diag", "flamia_bwd_ws_layout", "flamia_tile_config", "flamia_plan_view", "flamia_status_string")
 
 _lib = None
@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH):
         "flamia_plan_build": [dp, qp, P],
         "flamia_quantize": [dp, P, P, P, qp, P],
         "flamia_attn_fwd": [dp, qp, P, P, P, P, P],
+        "flamia_attn_fwd_p4": [dp, qp, P, P, P, P, P],
         "flamia_attn_bwd": [dp, qp, P, P, P, P, P, P, P, P, P],
         "flamia_attn_bwd_noalloc": [dp, qp, P, P, P, P, P, P, P, P],
         "flamia_attn_bwd_prep": [dp, qp, P, P, P, P, P, P],
@@ -143,6 +144,11 @@ def quantize(desc, q, k, v, qt: QTensors, stream=None):
 def attn_fwd(desc, qt: QTensors, o, row_max, row_sum, ws=None, stream=None):
     _check(load().flamia_attn_fwd(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
                                   _ptr(row_sum), _ptr(ws), _stream(stream)), "flamia_attn_fwd")
+
+
+def attn_fwd_p4(desc, qt: QTensors, o, row_max, row_sum, ws=None, stream=None):
+    _check(load().flamia_attn_fwd_p4(ctypes.byref(desc), ctypes.byref(qt), _ptr(o), _ptr(row_max),
+                                     _ptr(row_sum), _ptr(ws), _stream(stream)), "flamia_attn_fwd_p4")
 
 
 def attn_bwd(desc, qt: QTensors, o, row_max, row_sum, dout, dq, dk, dv, ws, stream=None):
