@@ -307,14 +307,15 @@ def cpu_baseline(wl, causal: bool = True, max_len: int = CPU_SAMPLE_MAX_LEN):
 
 
 def measure(flamia, torch, wl, steps, warmup, causal_dq_scale=False, deterministic=False, exact=False,
-            non_causal=False):
+            non_causal=False, exp2_fma=False):
     """Eager stage timing (HIP events between the entry points) over W + K
     steps, then the graph-replayed headline (median of 3 rounds of K)."""
     dev = torch.device("cuda:0")
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     call = flamia.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard,
                                causal_dq_scale=wl.causal_dq_scale or causal_dq_scale, path=wl.path,
-                               deterministic=deterministic, exact=exact, causal=not non_causal)
+                               deterministic=deterministic, exact=exact, causal=not non_causal,
+                               exp2_fma=exp2_fma)
     if non_causal:
         pairs = wl.heads * sum(L * L for L in wl.doc_lens)
     else:
@@ -366,6 +367,12 @@ def main():
                          "FLOPs then count every (query, key) pair of a document")
     ap.add_argument("--causal-dq-scale", action="store_true",
                     help="the optional causal dQ accumulator scale (prescale from causally visible key blocks only)")
+    ap.add_argument("--shape", default="",
+                    help="one of the pages' packed benchmark shapes instead of --config: "
+                         "equal_4x4096, equal_16x1024, equal_16x4096, equal_64x1024, "
+                         "skew_8192_32x256, skew_8192_224x256")
+    ap.add_argument("--exp2-fma", action="store_true",
+                    help="exponentials of half of the 32x32 blocks on the FMA-pipe polynomial (both passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the long-context workload's extra measurements on the default run")
@@ -393,13 +400,14 @@ def main():
 
     from precision_causal_attention_hadamard_amd import flamia, workloads
 
-    wl = workloads.config(args.config, kv_heads=args.kv_heads)
+    wl = (workloads.pages_shape(args.shape, kv_heads=args.kv_heads) if args.shape
+          else workloads.config(args.config, kv_heads=args.kv_heads))
     # the CPU baseline runs first, in forked workers, before anything touches the GPU
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, causal=not args.non_causal)
 
     flamia.load()
     m = measure(flamia, torch, wl, args.steps, args.warmup, args.causal_dq_scale, args.deterministic,
-                args.exact, args.non_causal)
+                args.exact, args.non_causal, args.exp2_fma)
     call, stage_ms, pairs, flops, ms_per_step = m["call"], m["stage_ms"], m["pairs"], m["flops"], m["ms"]
     if args.copy_calibration:
         dev = torch.device("cuda:0")
@@ -459,6 +467,7 @@ def main():
                    "doc_lens": wl.doc_lens if len(wl.doc_lens) <= 8 else f"{len(wl.doc_lens)} documents",
                    "hadamard": bool(wl.hadamard), "path": "mixed" if wl.path else "mxfp8",
                    "deterministic": bool(args.deterministic), "exact": bool(args.exact),
+                   "exp2_fma": bool(args.exp2_fma),
                    "causal": not args.non_causal,
                    "causal_dq_scale": bool(wl.causal_dq_scale or args.causal_dq_scale),
                    "causal_pairs": pairs, "flops_per_step": flops},
@@ -483,9 +492,15 @@ def main():
     out["graph"] = m["graph"]
     del call, m
     if args.config == 3 and not args.no_extra and not (args.kv_heads or args.exact or args.non_causal
-                                                       or args.deterministic or args.causal_dq_scale):
+                                                       or args.deterministic or args.causal_dq_scale
+                                                       or args.shape or args.exp2_fma):
         wl4 = workloads.config(4)
         extra = {"p4_forward": p4_forward_timing(flamia, torch, wl)}
+        m4 = measure(flamia, torch, wl, args.steps, args.warmup, exp2_fma=True)
+        extra["exp2_fma"] = {"workload": wl.name, "ms_per_step": m4["ms"],
+                             "TFLOP/s": m4["flops"] / (m4["ms"] * 1e-3) / 1e12, "stage_ms": m4["stage_ms"],
+                             "note": "exp2 of half of the 32x32 blocks on a degree-5 FMA-pipe polynomial, both passes"}
+        del m4
         for tag, cds in (("long_context_32768", False), ("long_context_32768_causal_dq_scale", True)):
             m4 = measure(flamia, torch, wl4, args.steps, args.warmup, causal_dq_scale=cds)
             extra[tag] = {"workload": wl4.name, "causal_dq_scale": cds, "ms_per_step": m4["ms"],
@@ -493,6 +508,14 @@ def main():
                           "pct_fp8_peak": 100.0 * m4["flops"] / (m4["ms"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
                           "timing": m4["timing"], "stage_ms": m4["stage_ms"], "flops_per_step": m4["flops"]}
             del m4
+        for shape in ("equal_4x4096", "skew_8192_32x256", "skew_8192_224x256"):
+            ws = workloads.pages_shape(shape)
+            m4 = measure(flamia, torch, ws, args.steps, args.warmup)
+            extra[shape] = {"workload": ws.name, "ms_per_step": m4["ms"],
+                            "TFLOP/s": m4["flops"] / (m4["ms"] * 1e-3) / 1e12,
+                            "pct_fp8_peak": 100.0 * m4["flops"] / (m4["ms"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+                            "stage_ms": m4["stage_ms"], "flops_per_step": m4["flops"]}
+            del m4, ws
         out["extra"] = extra
     out["worklist"] = worklist_build(flamia, torch)
     if cpu is not None:

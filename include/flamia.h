@@ -102,6 +102,15 @@ typedef struct flamia_attn_desc {
                                    per-token causal dQ prescale.  No output depends on a later
                                    position's inputs.  MXFP8 path only (path = 1:
                                    FLAMIA_ERR_UNSUPPORTED) */
+  int32_t exp2_fma;             /* 1: the exponentials of half of the 32 x 32 (query block, key
+                                   block) pairs -- those whose document-local block indices have
+                                   an odd sum -- on a degree-5 polynomial on the FMA pipe instead of
+                                   the transcendental unit ([Reading, 4.4] second bullet: part of
+                                   the exp work emulated on the FMA pipe).  Forward and backward
+                                   choose alike, so the backward still replays the forward's P^.
+                                   0 or 1; 1 needs path 0, causal, no exact option, one key/value
+                                   head per query head and atomic dQ (else
+                                   FLAMIA_ERR_UNSUPPORTED) */
 } flamia_attn_desc;
 
 /*

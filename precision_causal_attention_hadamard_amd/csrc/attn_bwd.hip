@@ -665,8 +665,9 @@ __device__ __forceinline__ float half_max32(float m) {
 // final row maximum, when the replay is exact: [Summary, §3.3
 // Forward-Backward Numerical Consistency]) and counts the nonzero dS and
 // those whose E4M3 code is zero ([Summary, §3.3] second bullet).
-template <int D, bool DET, bool GRP, bool EXACT, bool CAUSAL, bool DIAG = false>
+template <int D, bool DET, bool GRP, bool EXACT, bool CAUSAL, bool DIAG = false, bool POLY = false>
 __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
+  static_assert(!POLY || (!DET && !GRP && !EXACT && CAUSAL), "FMA-pipe exp2: the default call only");
   constexpr int NS = D / 64;
   constexpr int ND = D / 32;
   constexpr int NDK = ND / 2;                // dK d-blocks per wave
@@ -906,6 +907,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const int QB = 2 * qt + qh;
     const bool act = kb_active && (!CAUSAL || QB >= KB) && 32 * qh < nq;
     const bool dia = QB == KB;
+    const bool pol = POLY && poly_block(QB, KB);   // the forward's choice for this block
     // no mask (and, but for the exact option, no fold); without the causal
     // mask a block may also hold keys past the document end
     const bool fast = !dia && 32 * qh + 32 <= nq && (CAUSAL || k0 + 32 * kb + 32 <= L);
@@ -963,7 +965,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         const float ufd = __builtin_amdgcn_ldexpf(1.0f, -fd);
         // the block's rows as one straight-line body per probability form
         // (fast where every row of the query block allows it)
-        auto rows = [&](auto PW) {
+        auto rows = [&](auto PW, auto PL) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int r0 = 32 * qh + 8 * g + 4 * hh;
@@ -973,8 +975,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)        // P 2^8
             pf[r] = decltype(PW)::value
-                        ? __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(sacc[4 * g + r] * c), kov[r])
-                        : p_scaled(sacc[4 * g + r] * c, kov[r]);
+                        ? __builtin_amdgcn_ldexpf(exp2_p<decltype(PL)::value>(sacc[4 * g + r] * c), kov[r])
+                        : p_scaled<decltype(PL)::value>(sacc[4 * g + r] * c, kov[r]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int rr = 4 * g + r;
@@ -995,10 +997,14 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, EXACT ? ufd : 1.0f, true));
         }
         };
+        auto rows_pw = [&](auto PW) {
+          if (POLY && pol) rows(PW, std::integral_constant<bool, POLY>{});
+          else rows(PW, std::false_type{});
+        };
         if ((__builtin_amdgcn_readfirstlane(pqx[32 * qh]) >> 24) & 1)
-          rows(std::true_type{});
+          rows_pw(std::true_type{});
         else
-          rows(std::false_type{});
+          rows_pw(std::false_type{});
       } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -1012,7 +1018,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
             const int i = q0 + r0 + r;
             float dsr = 0.f, pev = 0.f;
             if (kv && (!CAUSAL || j <= i) && i < L) {
-              const float p8 = p_scaled(sacc[rr] * c, kov[r]);
+              const float x = sacc[rr] * c;
+              const float p8 = (POLY && pol) ? p_scaled<POLY>(x, kov[r]) : p_scaled(x, kov[r]);
               dsr = (p8 * ilv[r]) * pacc[rr];
               int code;
               if (EXACT || dia) {
@@ -1347,8 +1354,19 @@ hipError_t launch_attn_bwd(const Problem& p, const void* plan, const PlanLayout&
     if (in.ds_counts != nullptr)
       hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, stream, in.ds_counts, 2);
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
-    if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, false, true, true>);
-    else go8(attn_bwd8_kernel<128, false, false, false, true, true>);
+    if (p.exp2_fma) {
+      if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, false, true, true, true>);
+      else go8(attn_bwd8_kernel<128, false, false, false, true, true, true>);
+    } else {
+      if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, false, true, true>);
+      else go8(attn_bwd8_kernel<128, false, false, false, true, true>);
+    }
+  } else if (p.exp2_fma) {
+    // exp2 of half of the blocks on the FMA pipe: MXFP8, one head per item,
+    // causal, atomic dQ
+    auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
+    if (p.D == 64) go8(attn_bwd8_kernel<64, false, false, false, true, false, true>);
+    else go8(attn_bwd8_kernel<128, false, false, false, true, false, true>);
   } else {
     auto go8 = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(2 * BWD_THREADS), 0, stream, a); };
     // one instantiation per (determinism, grouped heads, exact option, causal);

@@ -74,10 +74,13 @@ struct FwdArgs {
 // ([Summary, §3.3 Forward-Backward Numerical Consistency]).
 // P4: the 4-bit probability operand (log-domain NVFP4, p4_block) in place of
 // E4M3 P^ (MXFP8 path, without the exact option).
-template <int D, int PATH, bool EXACT, bool CAUSAL, bool DIAG = false, bool P4 = false>
+// POLY: exp2 of the blocks poly_block selects on the FMA-pipe polynomial
+// (MXFP8 path, without the exact option or the 4-bit operand).
+template <int D, int PATH, bool EXACT, bool CAUSAL, bool DIAG = false, bool P4 = false, bool POLY = false>
 __global__ void __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(FwdArgs a) {
   static_assert(!P4 || (PATH == 0 && !EXACT && !DIAG), "4-bit probability operand: MXFP8 path only");
+  static_assert(!POLY || (PATH == 0 && !EXACT && !P4), "FMA-pipe exp2: MXFP8 path only");
   constexpr int KS = D + 16;          // token-major row stride (bytes)
   constexpr int KSB = 2 * D + 16;     // token-major bf16 row stride (bytes), mixed path K
   constexpr int NS = D / 64;          // K-steps of the FP8 S product
@@ -291,7 +294,7 @@ attn_fwd_kernel(FwdArgs a) {
   auto softmax_pv = [&](int kt, v16f (&st)[2]) {
     const int buf = kt & 1;
     const int j0 = kt * FWD_BK;
-    bool act[2], dia[2];
+    bool act[2], dia[2], pol[2];
     // interior tile: every key precedes every query of the wave (or, not
     // causal, any key) and lies in the document; both blocks are then active
     // (and, causal, neither is diagonal)
@@ -301,6 +304,7 @@ attn_fwd_kernel(FwdArgs a) {
       const int KB = 2 * kt + kb;
       act[kb] = (!CAUSAL || KB <= QB) && j0 + 32 * kb < L;
       dia[kb] = KB == QB;
+      pol[kb] = POLY && poly_block(QB, KB);
     }
     if (!(act[0] || act[1])) return;
     // the tile's maximum over the visible scores (all 64 on an interior tile)
@@ -354,16 +358,19 @@ attn_fwd_kernel(FwdArgs a) {
           }
           p4_block(e, psc, pc[kb]);
         } else {
+          auto block = [&](auto PB) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float e[4];
+            for (int g = 0; g < 4; ++g) {
+              float e[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              e[r] = __builtin_amdgcn_exp2f(st[kb][4 * g + r] * c);
-              ls += e[r];
+              for (int r = 0; r < 4; ++r) {
+                e[r] = exp2_p<decltype(PB)::value>(st[kb][4 * g + r] * c);
+                ls += e[r];
+              }
+              pc[kb][g] = cvt_fp8x4_scaled(e[0], e[1], e[2], e[3], psc);
             }
-            pc[kb][g] = cvt_fp8x4_scaled(e[0], e[1], e[2], e[3], psc);
-          }
+          };
+          if (POLY && pol[kb]) block(std::true_type{}); else block(std::false_type{});
         }
         l_run += __builtin_amdgcn_ldexpf(ls, kofs);
       }
@@ -383,7 +390,8 @@ attn_fwd_kernel(FwdArgs a) {
             float pv4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float pr = p_scaled(st[kb][4 * g + r] * c, kofs);
+              const float x = st[kb][4 * g + r] * c;
+              const float pr = (POLY && pol[kb]) ? p_scaled<POLY>(x, kofs) : p_scaled(x, kofs);
               ls += pr;
               pv4[r] = EXACT ? __builtin_amdgcn_ldexpf(pr, ((fold4 >> (8 * r)) & 255) - fref) : pr;
               pv16[4 * g + r] = pv4[r];
@@ -399,7 +407,10 @@ attn_fwd_kernel(FwdArgs a) {
               const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
               const int j = j0 + 32 * kb + jj;
               float pr = 0.f;
-              if (act[kb] && (!CAUSAL || j <= i) && j < L) pr = p_scaled(st[kb][4 * g + r] * c, kofs);
+              if (act[kb] && (!CAUSAL || j <= i) && j < L) {
+                const float x = st[kb][4 * g + r] * c;
+                pr = (POLY && pol[kb]) ? p_scaled<POLY>(x, kofs) : p_scaled(x, kofs);
+              }
               ls += pr;
               if constexpr (EXACT)   // every block folds V's per-token exponent into P
                 pv4[r] = __builtin_amdgcn_ldexpf(pr, ((int)sVe[buf][32 * kb + jj] - E8M0_BIAS) -
@@ -517,7 +528,15 @@ hipError_t launch_attn_fwd(const Problem& p, const void* plan, const PlanLayout&
             static_cast<uint16_t*>(o), row_max, row_sum, dump, dump_max, dump_len};
   dim3 grid((unsigned)pl.cap_fwd * (unsigned)p.H);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(FWD_THREADS), 0, stream, a); };
-  if (p4) {                // 4-bit probability operand: MXFP8 path, no exact option
+  if (p.exp2_fma) {        // FMA-pipe exp2 on half of the blocks: MXFP8 path, causal, no exact option
+    if (dump_len > 0) {
+      if (p.D == 64) go(attn_fwd_kernel<64, 0, false, true, true, false, true>);
+      else go(attn_fwd_kernel<128, 0, false, true, true, false, true>);
+    } else {
+      if (p.D == 64) go(attn_fwd_kernel<64, 0, false, true, false, false, true>);
+      else go(attn_fwd_kernel<128, 0, false, true, false, false, true>);
+    }
+  } else if (p4) {         // 4-bit probability operand: MXFP8 path, no exact option
     if (p.causal) {
       if (p.D == 64) go(attn_fwd_kernel<64, 0, false, true, false, true>);
       else go(attn_fwd_kernel<128, 0, false, true, false, true>);

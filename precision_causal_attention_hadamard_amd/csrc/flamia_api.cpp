@@ -49,6 +49,12 @@ flamia_status validate(const flamia_attn_desc* d) {
   if (!d->causal && (d->causal_dq_scale || d->exact)) return FLAMIA_ERR_INVALID_ARG;
   // the exact option is built for the MXFP8 path
   if (d->exact && d->path != 0) return FLAMIA_ERR_UNSUPPORTED;
+  // the FMA-pipe exp2: 0 or 1; built for the default MXFP8 call (causal, one
+  // key/value head per query head, atomic dQ, no exact option)
+  if (d->exp2_fma & ~1) return FLAMIA_ERR_INVALID_ARG;
+  if (d->exp2_fma && (d->path != 0 || d->exact || !d->causal || d->deterministic ||
+                      (d->num_kv_heads > 0 && d->num_kv_heads != d->num_heads)))
+    return FLAMIA_ERR_UNSUPPORTED;
   // index limits: documents and tiles are packed into 24 and 20 bits of the
   // sort key, costs into 20 bits; a launch's work-items (up to 512 per
   // workgroup, one workgroup per tile and head) must fit 32 bits
@@ -173,6 +179,7 @@ Problem problem(const flamia_attn_desc* d) {
   p.deterministic = d->deterministic;
   p.exact = d->exact;
   p.causal = d->causal;
+  p.exp2_fma = d->exp2_fma;
   // the exact option carries its own (per-token) causal dQ prescale
   if (p.exact) p.causal_dq_scale = 1;
   p.softmax_scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
@@ -303,7 +310,7 @@ flamia_status flamia_attn_fwd_p4(const flamia_attn_desc* desc, const flamia_qten
   (void)ws;
   const flamia_status s = validate(desc);
   if (s != FLAMIA_OK) return s;
-  if (desc->path != 0 || desc->exact) return FLAMIA_ERR_UNSUPPORTED;
+  if (desc->path != 0 || desc->exact || desc->exp2_fma) return FLAMIA_ERR_UNSUPPORTED;
   if (!qt_complete(desc, qt) || !tensors_ok(desc, {o, row_max, row_sum})) return FLAMIA_ERR_INVALID_ARG;
   const Problem p = problem(desc);
   return hip_status(launch_attn_fwd(p, qt->plan, plan_layout(desc), qt->q_codes, qt->k_codes, qt->v_codes,

@@ -325,11 +325,43 @@ __device__ __forceinline__ int cvt_floor_i32(float x) {
 // 2^floor(S') exp2(fract(S')).  `kofs` = 8 - m~.
 constexpr float P_X_LO = -126.f, P_X_HI = 120.f;
 constexpr int P_M_LO = -100, P_M_HI = 120;
+
+// exp2 on the FMA pipe (the optional polynomial evaluation of the pages'
+// softmax scheduling, [Reading, 4.4] second bullet): 2^f for f in [0, 1) as
+// q(f) = 1 + f (c1 + f (c2 + f (c3 + f (c4 + f c5)))), five FMAs in this
+// order.  The coefficients minimise the largest relative error of q against
+// 2^f on [0, 1] (8.3e-8; 2.4 ulp after fp32 rounding of the Horner steps), and
+// q(0) = 1 exactly, so integer arguments give exact powers of two.
+__device__ __forceinline__ float exp2_fma_frac(float f) {
+  float q = 0.001867053215391934f;
+  q = __builtin_fmaf(q, f, 0.00901719182729721f);
+  q = __builtin_fmaf(q, f, 0.05579979717731476f);
+  q = __builtin_fmaf(q, f, 0.24016447365283966f);
+  q = __builtin_fmaf(q, f, 0.6931512951850891f);
+  return __builtin_fmaf(q, f, 1.0f);
+}
+// 2^x = 2^floor(x) q(fract(x)) (rounded once where the result is subnormal)
+__device__ __forceinline__ float exp2_fma(float x) {
+  return __builtin_amdgcn_ldexpf(exp2_fma_frac(__builtin_amdgcn_fractf(x)), cvt_floor_i32(x));
+}
+// exp2 of the probability evaluation: the transcendental unit, or (POLY) the
+// FMA-pipe polynomial.  Which blocks take the polynomial is fixed per 32 x 32
+// (query block, key block) pair, so both passes make the same choice.
+template <bool POLY>
+__device__ __forceinline__ float exp2_p(float x) {
+  if constexpr (POLY) return exp2_fma(x);
+  else return __builtin_amdgcn_exp2f(x);
+}
+template <bool POLY = false>
 __device__ __forceinline__ float p_scaled(float x, int kofs) {
-  const float whole = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(x), kofs);
-  const float split = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x)), cvt_floor_i32(x) + kofs);
+  const float frac2 = POLY ? exp2_fma_frac(__builtin_amdgcn_fractf(x)) : __builtin_amdgcn_exp2f(__builtin_amdgcn_fractf(x));
+  const float whole = __builtin_amdgcn_ldexpf(exp2_p<POLY>(x), kofs);
+  const float split = __builtin_amdgcn_ldexpf(frac2, cvt_floor_i32(x) + kofs);
   return (x <= P_X_HI && (x >= P_X_LO || kofs <= 8 - P_M_LO)) ? whole : split;
 }
+// The polynomial takes the 32 x 32 blocks whose document-local query-block and
+// key-block indices have an odd sum (half of the blocks; none on the diagonal).
+__device__ __forceinline__ bool poly_block(int qb, int kb) { return ((qb + kb) & 1) != 0; }
 // Rows whose m~ lies in [P_M_LO, P_M_HI] take the fast form, p_scaled's whole
 // branch for every visible score (S' <= m~ <= 120), with 2^(8 - m~) applied
 // inside the E4M3 convert (same codes as ldexp, then convert) and once to a

@@ -41,6 +41,7 @@ struct Problem {
   int deterministic;       // dQ from per-step partials added in a fixed order
   int exact;               // the exact option: per-token scales, all-tile V fold, two dS payloads
   int causal;              // 1: key j visible to query i for j <= i; 0: every key of the document
+  int exp2_fma;            // 1: exp2 of the blocks poly_block selects on the FMA-pipe polynomial
   float softmax_scale;     // fp32 softmax scale
   float c_log2;            // fp32(softmax_scale * log2(e))
 };

@@ -34,7 +34,8 @@ class AttnDesc(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("hadamard", ctypes.c_int32), ("causal_dq_scale", ctypes.c_int32),
                 ("deterministic", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("num_kv_heads", ctypes.c_int32), ("exact", ctypes.c_int32)]
+                ("num_kv_heads", ctypes.c_int32), ("exact", ctypes.c_int32),
+                ("exp2_fma", ctypes.c_int32)]
 
 
 class QTensors(ctypes.Structure):
@@ -111,11 +112,11 @@ def _stream(stream=None):
 def make_desc(cu_seqlens_dev: torch.Tensor, total_tokens: int, num_docs: int, max_doc_len: int,
               num_heads: int, head_dim: int, hadamard: bool = False, causal_dq_scale: bool = False,
               softmax_scale: float = 0.0, path: int = 0, causal: int = 1, deterministic: int = 0,
-              num_kv_heads: int = 0, exact: int = 0) -> AttnDesc:
+              num_kv_heads: int = 0, exact: int = 0, exp2_fma: int = 0) -> AttnDesc:
     return AttnDesc(total_tokens, num_docs, max_doc_len,
                     cu_seqlens_dev.data_ptr() if cu_seqlens_dev is not None else None,
                     num_heads, head_dim, causal, path, int(hadamard), int(causal_dq_scale),
-                    deterministic, softmax_scale, num_kv_heads, exact)
+                    deterministic, softmax_scale, num_kv_heads, exact, exp2_fma)
 
 
 def buffer_sizes(desc: AttnDesc):
@@ -220,10 +221,13 @@ class TrainingCall:
     step (quantize, forward, backward).  Inputs are bf16 CUDA tensors, q and
     do ``[T, H, d]``, k and v ``[T, Hk, d]`` (Hk dividing H: grouped query
     attention when Hk < H); ``cu_seqlens`` a list of ints; ``causal`` False
-    drops the j <= i mask (every key of a document is visible)."""
+    drops the j <= i mask (every key of a document is visible); ``exp2_fma``
+    puts the exponentials of half of the 32 x 32 blocks on the FMA-pipe
+    polynomial in both passes."""
 
     def __init__(self, q, k, v, do, cu_seqlens, hadamard=False, causal_dq_scale=False,
-                 softmax_scale=0.0, path=0, deterministic=False, exact=False, causal=True, max_doc_len=None):
+                 softmax_scale=0.0, path=0, deterministic=False, exact=False, causal=True, max_doc_len=None,
+                 exp2_fma=False):
         dev = q.device
         self.q, self.k, self.v, self.do = q, k, v, do
         T, H, d = q.shape
@@ -235,7 +239,7 @@ class TrainingCall:
         self.desc = make_desc(self.cu, T, len(lens), mdl, H, d, hadamard,
                               causal_dq_scale, softmax_scale, path, causal=int(causal),
                               deterministic=int(deterministic),
-                              num_kv_heads=Hk, exact=int(exact))
+                              num_kv_heads=Hk, exact=int(exact), exp2_fma=int(exp2_fma))
         qb, fb, bb = buffer_sizes(self.desc)
         self.qbuf = torch.empty(qb, dtype=torch.uint8, device=dev)
         self.qt = qtensors_layout(self.desc, self.qbuf)

@@ -144,6 +144,29 @@ def config(k: int, seed: int | None = None, kv_heads: int = 0) -> Workload:
     raise ValueError(k)
 
 
+# The pages' packed kernel-benchmark shapes beside the five workloads above
+# (16 heads, head dim 128, N(0, 1), MXFP8, Hadamard off): equal-length batches
+# and the two skewed calls, one 8192-token document followed by 32 or 224
+# documents of 256 tokens.
+PAGES_SHAPES = {
+    "equal_4x4096": [4096] * 4,
+    "equal_16x1024": [1024] * 16,
+    "equal_16x4096": [4096] * 16,
+    "equal_64x1024": [1024] * 64,
+    "skew_8192_32x256": [8192] + [256] * 32,
+    "skew_8192_224x256": [8192] + [256] * 224,
+}
+
+
+def pages_shape(name: str, seed: int = SEED_BASE + 600, kv_heads: int = 0) -> Workload:
+    """One of ``PAGES_SHAPES`` with inputs drawn by the recipe above."""
+    lens = PAGES_SHAPES[name]
+    rng = np.random.default_rng(seed)
+    q, kk, v, do = draw_tensors(rng, int(sum(lens)), 16, 128, kv_heads=kv_heads)
+    kvs = f"_kv{kv_heads}" if kv_heads and kv_heads != 16 else ""
+    return Workload(f"{name}_h16{kvs}_d128", q, kk, v, do, _cu(lens), 16, 128)
+
+
 def small_packed(seed: int, doc_lens, heads: int = 2, head_dim: int = 64,
                  outlier_scale: float = 0.0, hadamard: bool = False, path: int = 0,
                  kv_heads: int = 0) -> Workload:

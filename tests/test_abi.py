@@ -243,6 +243,20 @@ def test_noncausal_descriptor_rules(lib):
     assert sizes_status(lib, base_desc(causal=0, path=1))[0] == 0
 
 
+def test_exp2_fma_descriptor_rules(lib):
+    """exp2_fma is 0 or 1; 1 is built for the default MXFP8 call only (causal,
+    one key/value head per query head, atomic dQ, no exact option)."""
+    assert sizes_status(lib, base_desc(exp2_fma=1))[0] == 0
+    assert sizes_status(lib, base_desc(exp2_fma=1, hadamard=1, causal_dq_scale=1))[0] == 0
+    assert sizes_status(lib, base_desc(exp2_fma=2))[0] == 1
+    assert sizes_status(lib, base_desc(exp2_fma=-1))[0] == 1
+    for kw in (dict(path=1), dict(exact=1), dict(causal=0), dict(deterministic=1),
+               dict(num_heads=4, num_kv_heads=2)):
+        assert sizes_status(lib, base_desc(exp2_fma=1, **kw))[0] == 2, kw
+    # the layouts do not depend on it
+    assert sizes_status(lib, base_desc(exp2_fma=1))[1:] == sizes_status(lib, base_desc())[1:]
+
+
 def noncausal_steps(L, bq=64, bk=128):
     """Every key tile of a document visits every query tile without the mask."""
     return (-(-L // bk)) * (-(-L // bq))

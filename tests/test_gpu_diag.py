@@ -40,10 +40,10 @@ CASES = {
 E4M3_VALUES = formats.e4m3_decode(np.arange(256, dtype=np.uint8))
 
 
-def run_diag(lib, wl):
+def run_diag(lib, wl, **kw):
     dev = torch.device("cuda")
     q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
-    call = lib.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard)
+    call = lib.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard, **kw)
     T, H, d = call.shape
     Lmax = max(wl.doc_lens)
     nkt = -(-Lmax // 64)
@@ -60,11 +60,10 @@ def run_diag(lib, wl):
     return call, fwd.cpu().numpy(), fmax.cpu().numpy(), bwd.cpu().numpy(), counts.cpu().numpy()
 
 
-@pytest.mark.parametrize("case", list(CASES))
-def test_backward_replays_forward_codes(gpu_lib, case):
-    wl = CASES[case]()
-    print(f"[diag] {case}", flush=True)
-    call, fwd, fmax, bwd, counts = run_diag(gpu_lib, wl)
+def check_replay(wl, call, fwd, fmax, bwd, case):
+    """Every visible pair written by both kernels, none of the masked ones;
+    the codes equal in E4M3's normal range.  Returns (checked, below,
+    differ_below)."""
     m_final = call.row_max.cpu().numpy().astype(np.int64)
     checked = below = differ_below = 0
     for s, e in zip(wl.cu_seqlens[:-1], wl.cu_seqlens[1:]):
@@ -91,6 +90,15 @@ def test_backward_replays_forward_codes(gpu_lib, case):
             sub = vis & ~normal
             below += int(sub.sum())
             differ_below += int(np.count_nonzero(vf[sub] != vb[sub]))
+    return checked, below, differ_below
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_backward_replays_forward_codes(gpu_lib, case):
+    wl = CASES[case]()
+    print(f"[diag] {case}", flush=True)
+    call, fwd, fmax, bwd, counts = run_diag(gpu_lib, wl)
+    checked, below, differ_below = check_replay(wl, call, fwd, fmax, bwd, case)
     print(f"[diag] {case}: {checked} codes in the normal range equal; {differ_below} of {below} below it differ",
           flush=True)
     assert checked > 0
