@@ -336,7 +336,7 @@ attn_fwd_kernel(FwdArgs a) {
     const int kofs = 8 - m_run;       // P 2^8 = 2^(S' + 8 - m~)
     // fast form (p_scaled's codes, see there): exp2(S') per score, the row's
     // 2^(8 - m~) applied inside the E4M3 convert and once to the tile's sum
-    const bool fast = !EXACT && __all(m_run >= P_M_LO && m_run <= P_M_HI);
+    const bool fast = __all(m_run >= P_M_LO && m_run <= P_M_HI);
     const float psc = __builtin_amdgcn_ldexpf(1.0f, fast ? m_run - 8 : 0);
 
     // l gains one partial sum per 32-key block, summed in the same order on
@@ -366,6 +366,15 @@ attn_fwd_kernel(FwdArgs a) {
               for (int r = 0; r < 4; ++r) {
                 e[r] = exp2_p<decltype(PB)::value>(st[kb][4 * g + r] * c);
                 ls += e[r];
+              }
+              if constexpr (EXACT) {
+                // the key's fold against its block's reference, exact before
+                // the scaled convert (a product that leaves fp32's normal range
+                // here is below 2^-18 after the row's scale: code 0 either way)
+                const int fold4 = *reinterpret_cast<const int*>(&sVe[buf][32 * kb + 8 * g + 4 * hh]);
+                const int fref = (int)sVr[buf][kb];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_ldexpf(e[r], ((fold4 >> (8 * r)) & 255) - fref);
               }
               pc[kb][g] = cvt_fp8x4_scaled(e[0], e[1], e[2], e[3], psc);
             }
