@@ -158,8 +158,9 @@ attn_fwd_kernel(FwdArgs a) {
   v16f oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = v16f{};
-  float l_run = 0.f;          // sum of P * 2^8
-  int m_run = M_NONE;
+  float l_run = 0.f;          // sum of P * 2^8, taken against m_acc
+  int m_run = M_NONE;         // running integer row maximum
+  int m_acc = M_NONE;         // the maximum oacc and l_run are taken against (<= m_run)
   const float c = p.c_log2;
 
   const int kt_last = ((CAUSAL ? min(q0 + FWD_BQ, L) : L) - 1) / FWD_BK;
@@ -328,11 +329,24 @@ attn_fwd_kernel(FwdArgs a) {
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     const int m_tile = tmax == -INFINITY ? M_NONE : (int)ceilf(tmax * c);
-    const int m_new = max(m_run, m_tile);
-    const int sh = m_run - m_new;     // <= 0: every online rescale is a power of two
-    const bool rescale = __any(sh != 0);
-    l_run = __builtin_amdgcn_ldexpf(l_run, sh);
-    m_run = m_new;
+    m_run = max(m_run, m_tile);
+    // The online rescale is deferred: oacc and l_run stay taken against m_acc
+    // while m_run - m_acc <= FWD_LAZY, the P^V product carrying the factor
+    // 2^(m_run - m_acc) in P^'s operand scale and the sums in their power of
+    // two.  Every factor is a power of two, so O is the same bit for bit as
+    // with a rescale at every change of m~; when any lane of the wave runs
+    // further ahead, all rebase.
+    int dl = m_run - m_acc;
+    if (__any(dl > FWD_LAZY)) {
+      const int sh = m_acc - m_run;   // <= 0
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) oacc[db][rr] = __builtin_amdgcn_ldexpf(oacc[db][rr], sh);
+      l_run = __builtin_amdgcn_ldexpf(l_run, sh);
+      m_acc = m_run;
+      dl = 0;
+    }
     const int kofs = 8 - m_run;       // P 2^8 = 2^(S' + 8 - m~)
     // fast form (p_scaled's codes, see there): exp2(S') per score, the row's
     // 2^(8 - m~) applied inside the E4M3 convert and once to the tile's sum
@@ -381,7 +395,7 @@ attn_fwd_kernel(FwdArgs a) {
           };
           if (POLY && pol[kb]) block(std::true_type{}); else block(std::false_type{});
         }
-        l_run += __builtin_amdgcn_ldexpf(ls, kofs);
+        l_run += __builtin_amdgcn_ldexpf(ls, kofs + dl);
       }
     } else {
 #pragma unroll
@@ -432,14 +446,8 @@ attn_fwd_kernel(FwdArgs a) {
           }
         }
         if constexpr (P4) p4_block(pv16, 1.0f, pc[kb]);
-        l_run += ls;
+        l_run += __builtin_amdgcn_ldexpf(ls, dl);
       }
-    }
-    if (rescale) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) oacc[db][rr] = __builtin_amdgcn_ldexpf(oacc[db][rr], sh);
     }
     const v8i pb = v8i{pc[0][0], pc[0][1], pc[0][2], pc[0][3], pc[1][0], pc[1][1], pc[1][2], pc[1][3]};
     if constexpr (DIAG) {
@@ -459,9 +467,10 @@ attn_fwd_kernel(FwdArgs a) {
         if (hh == 0 && kt < nkt) a.dump_max[row * nkt + kt] = m_run;
       }
     }
-    // lane half hh supplies the scales of key block hh
-    const int sb = EXACT ? (dia[hh] ? E8M0_BIAS + vref + P_EXP : (int)sVr[buf][hh] + P_EXP)
-                         : (dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP);
+    // lane half hh supplies the scales of key block hh (with the deferred
+    // rescale's 2^(m_run - m_acc) of the lane's query)
+    const int sb = dl + (EXACT ? (dia[hh] ? E8M0_BIAS + vref + P_EXP : (int)sVr[buf][hh] + P_EXP)
+                               : (dia[hh] ? E8M0_BIAS + vref + P_EXP : E8M0_BIAS + P_EXP));
     const int sa = (EXACT || dia[hh]) ? E8M0_BIAS : (int)sVe[buf][32 * hh];
     // exact option: V's codes are per token everywhere
     const uint8_t* v0 = (!EXACT && dia[0]) ? sVk[buf] : sV[buf];
@@ -518,7 +527,7 @@ attn_fwd_kernel(FwdArgs a) {
         }
       if (hh == 0) {
         a.row_max[hT + i] = m_run;
-        a.row_sum[hT + i] = l;
+        a.row_sum[hT + i] = __builtin_amdgcn_ldexpf(l, m_acc - m_run);   // l is taken against m_acc
       }
     }
   }

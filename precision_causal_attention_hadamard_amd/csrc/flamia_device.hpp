@@ -41,6 +41,10 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 constexpr int TOKEN_BLOCK = 32;   // tokens per scale block
 constexpr int FWD_BQ = 128;       // queries per forward work item
 constexpr int FWD_BK = 64;        // keys per forward inner step
+// Largest deferred rescale of the forward, in powers of two: P^'s operand
+// scale 2^(fold reference + P_EXP + FWD_LAZY) stays a finite E8M0 value (at
+// most 2^127) and the fp32 accumulators lose at most 2^8 of headroom.
+constexpr int FWD_LAZY = 8;
 constexpr int BWD_BQ = 64;        // queries per backward inner step
 constexpr int BWD_BK = 128;       // keys per backward work item
 constexpr int E8M0_BIAS = 127;
