@@ -171,16 +171,26 @@ attn_fwd_kernel(FwdArgs a) {
   uint8_t pke = 0, pve = 0, pvke = 0, pvr = 0;
   const uint8_t* k4doc = PATH ? a.f4.k_fp4 + ((size_t)s_d * rsk + (size_t)hk * D) / 2 : nullptr;
   const uint8_t* ksfdoc = PATH ? a.f4.k_sf + ((size_t)s_d * rsk + (size_t)hk * D) / 16 : nullptr;
+  // this thread's 16-byte chunks of a key tile: row, byte offset in the
+  // [T, Hk, d] codes from the tile's first key, LDS offset (loop-invariant;
+  // a step adds a uniform base)
+  int crow[NCH];
+  uint32_t cgl[NCH], clds[NCH];
+#pragma unroll
+  for (int c2 = 0; c2 < NCH; ++c2) {
+    const int ch = tid + FWD_THREADS * c2;
+    crow[c2] = ch / (D / 16);
+    cgl[c2] = (uint32_t)crow[c2] * (uint32_t)rsk + 16u * (uint32_t)(ch % (D / 16));
+    clds[c2] = (uint32_t)(crow[c2] * KS + 16 * (ch % (D / 16)));
+  }
   auto prefetch_k = [&](int kt) {
     const int j0 = kt * FWD_BK;
     const int nvalid = min(FWD_BK, L - j0);
     if constexpr (PATH == 0) {
+      const uint8_t* kt0 = kdoc + (size_t)j0 * rsk;
 #pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2) {
-        const int ch = tid + FWD_THREADS * c2;
-        const int r = ch / (D / 16), c16 = ch % (D / 16);
-        pk[c2] = r < nvalid ? ld16(kdoc + (size_t)(j0 + r) * rsk + 16 * c16) : v4i{0, 0, 0, 0};
-      }
+      for (int c2 = 0; c2 < NCH; ++c2)
+        pk[c2] = (nvalid == FWD_BK || crow[c2] < nvalid) ? ld16(kt0 + cgl[c2]) : v4i{0, 0, 0, 0};
     } else {
       // NVFP4 K: 16-byte chunk = 32 codes (d in [32 c, 32 c + 32)) of one key, 2 group scales
       constexpr int CPR = D / 32;       // 16-byte chunks (32 codes) per key row
@@ -197,14 +207,13 @@ attn_fwd_kernel(FwdArgs a) {
     const int j0 = kt * FWD_BK;
     const int nvalid = min(FWD_BK, L - j0);
     const bool diag_tile = (kt >> 1) == qt;   // holds the query tile's diagonal blocks
+    const uint8_t* vt0 = vdoc + (size_t)j0 * rsk;
+    const uint8_t* vkt0 = vkdoc + (size_t)j0 * rsk;
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
-      const int ch = tid + FWD_THREADS * c2;
-      const int r = ch / (D / 16), c16 = ch % (D / 16);
-      const bool ok = r < nvalid;
-      const size_t off = (size_t)(j0 + r) * rsk + 16 * c16;
-      pv[c2] = ok ? ld16(vdoc + off) : v4i{0, 0, 0, 0};
-      pvk[c2] = (ok && diag_tile) ? ld16(vkdoc + off) : v4i{0, 0, 0, 0};
+      const bool ok = nvalid == FWD_BK || crow[c2] < nvalid;
+      pv[c2] = ok ? ld16(vt0 + cgl[c2]) : v4i{0, 0, 0, 0};
+      pvk[c2] = (ok && diag_tile) ? ld16(vkt0 + cgl[c2]) : v4i{0, 0, 0, 0};
     }
     // exact option: the largest per-key exponent of each key block is the
     // in-block prefix maximum at its last token (only read for blocks that
@@ -219,11 +228,7 @@ attn_fwd_kernel(FwdArgs a) {
   auto commit_k = [&](int slot) {
     if constexpr (PATH == 0) {
 #pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2) {
-        const int ch = tid + FWD_THREADS * c2;
-        const int r = ch / (D / 16), c16 = ch % (D / 16);
-        st16(&sK[slot][r * KS + 16 * c16], pk[c2]);
-      }
+      for (int c2 = 0; c2 < NCH; ++c2) st16(&sK[slot][clds[c2]], pk[c2]);
     } else {
       constexpr int CPR = D / 32;
       if (tid < FWD_BK * CPR) {
@@ -239,10 +244,8 @@ attn_fwd_kernel(FwdArgs a) {
   auto commit_v = [&](int buf, bool diag_tile) {
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
-      const int ch = tid + FWD_THREADS * c2;
-      const int r = ch / (D / 16), c16 = ch % (D / 16);
-      st16(&sV[buf][r * KS + 16 * c16], pv[c2]);
-      if (diag_tile) st16(&sVk[buf][r * KS + 16 * c16], pvk[c2]);   // read on diagonal blocks only
+      st16(&sV[buf][clds[c2]], pv[c2]);
+      if (diag_tile) st16(&sVk[buf][clds[c2]], pvk[c2]);   // read on diagonal blocks only
     }
     if (EXACT && tid < 2) sVr[buf][tid] = pvr;
     if (tid < FWD_BK) {
@@ -379,7 +382,7 @@ attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 e[r] = exp2_p<decltype(PB)::value>(st[kb][4 * g + r] * c);
-                ls += e[r];
+                ls = (g == 0 && r == 0) ? e[r] : ls + e[r];    // exp2 >= +0: the same sum as from 0
               }
               if constexpr (EXACT) {
                 // the key's fold against its block's reference, exact before

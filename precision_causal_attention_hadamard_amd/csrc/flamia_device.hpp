@@ -415,7 +415,8 @@ __device__ __forceinline__ void p4_block(const float (&v)[16], float sc, int (&p
 // divides exactly before its single rounding (the same codes as ldexp, then
 // convert).
 __device__ __forceinline__ int cvt_fp8x4_scaled(float a, float b, float c, float d, float sc) {
-  v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, sc, false);
+  // (the first convert's upper half is overwritten by the second)
+  v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, a), a, b, sc, false);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, sc, true);
   return __builtin_bit_cast(int, w);
 }
