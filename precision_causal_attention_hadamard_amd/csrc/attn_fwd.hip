@@ -319,12 +319,19 @@ attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, st[kb][rr]);
     } else {
+      // key j0 + 32 kb + 8 g + 4 hh + r is visible when its offset 32 kb + 8 g + r
+      // (a constant per register) is at most lim
+      const int lim = (CAUSAL ? min(i, L - 1) : L - 1) - (j0 + 4 * hh);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
+        if (act[kb]) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int j = j0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          if (act[kb] && (!CAUSAL || j <= i) && j < L) tmax = fmaxf(tmax, st[kb][rr]);
+          for (int rr = 0; rr < 16; rr += 2) {
+            const int o0 = 32 * kb + 8 * (rr >> 2) + (rr & 3);
+            const float s0 = o0 <= lim ? st[kb][rr] : -INFINITY;
+            const float s1 = o0 + 1 <= lim ? st[kb][rr + 1] : -INFINITY;
+            tmax = fmaxf(tmax, fmaxf(s0, s1));
+          }
         }
     }
     {   // the other lane half holds the query's other 16 keys of each block
