@@ -71,6 +71,10 @@ CASES = {
     "ragged_d128_h4": lambda: W.small_packed(33, [129, 64, 31, 250], heads=4, head_dim=128),
     # zero-length documents at the start, in the middle and at the end of the packed batch
     "empty_docs_d64": lambda: W.small_packed(37, [0, 45, 0, 0, 100, 33, 0], heads=2, head_dim=64),
+    # documents on tile and block boundaries (multiples of 32, 64 and 128 tokens), one head
+    "aligned_d128_h1": lambda: W.small_packed(38, [128, 256, 64, 32, 384], heads=1, head_dim=128),
+    # one long document at d = 64 with the rotation: many key tiles per query tile
+    "long_d64_hadamard": lambda: W.small_packed(39, [1999], heads=2, head_dim=64, hadamard=True),
     # row maxima near +150 and -150 beside ordinary rows: both probability forms
     "extreme_rows_d64": lambda: W.extreme_rows(1, [200, 97]),
     "extreme_rows_d128": lambda: W.extreme_rows(2, [160, 130], head_dim=128),
