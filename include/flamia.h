@@ -268,8 +268,8 @@ flamia_status flamia_attn_fwd(const flamia_attn_desc* desc, const flamia_qtensor
  * row_sum are flamia_attn_fwd's (l sums the unquantized P).  Arguments as for
  * flamia_attn_fwd.  The backward is not defined for this forward's output
  * (its dV would need the same 4-bit operand).
- * Errors: FLAMIA_ERR_UNSUPPORTED on the mixed path or with the exact option;
- * otherwise as flamia_attn_fwd.
+ * Errors: FLAMIA_ERR_UNSUPPORTED on the mixed path, with the exact option or
+ * with exp2_fma = 1; otherwise as flamia_attn_fwd.
  */
 flamia_status flamia_attn_fwd_p4(const flamia_attn_desc* desc, const flamia_qtensors* qt, void* o,
                                  int32_t* row_max, float* row_sum, void* ws, hipStream_t stream);
