@@ -398,9 +398,12 @@ flamia_status flamia_attn_bwd_main_diag(const flamia_attn_desc* desc, const flam
  *              e_dO(i) + E_V + E_K + log2 d + 13, E_V and E_K the largest V
  *              and K exponents of the document (of its blocks up to i's with
  *              causal_dq_scale; of its tokens up to i with the exact option)
+ *   dq_acc     [T,H,d] fp16 dQ 2^-sigma_i, zeroed by the prep stage and summed
+ *              by the main stage (atomic mode); flamia_attn_bwd_finish writes
+ *              dq from it
  */
 typedef struct flamia_bwd_ws_offsets {
-  size_t do_codes, do_exp, neg_delta, inv_l, g, dq_sigma;
+  size_t do_codes, do_exp, neg_delta, inv_l, g, dq_sigma, dq_acc;
 } flamia_bwd_ws_offsets;
 flamia_status flamia_bwd_ws_layout(const flamia_attn_desc* desc, flamia_bwd_ws_offsets* out);
 

@@ -95,6 +95,49 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
   }
 }
 
+// dQ without the rotation, deterministic slots or dK: the same arithmetic as
+// finalize_kernel, with the accumulator read and dq written in whole 1 KB
+// pieces per wave instruction (16 bytes a lane, consecutive lanes on
+// consecutive bytes); FIN_FLAT pieces a thread, all loads issued first.
+constexpr int FIN_FLAT = 4;
+template <int D>
+__global__ void __launch_bounds__(FIN_THREADS)
+finalize_dq_flat_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __restrict__ dq_sigma,
+                        uint16_t* __restrict__ dq) {
+  const size_t n8 = (size_t)p.T * p.H * (D / 8);       // 16-byte pieces
+  const size_t first = (size_t)blockIdx.x * (FIN_THREADS * FIN_FLAT) + threadIdx.x;
+  v4i w[FIN_FLAT];
+  int sig[FIN_FLAT];
+#pragma unroll
+  for (int c = 0; c < FIN_FLAT; ++c) {
+    const size_t idx = first + (size_t)c * FIN_THREADS;
+    if (idx < n8) {
+      w[c] = ld16(dq_acc + idx * 8);
+      const size_t row = idx / (D / 8);                 // = t * H + h
+      const int t = (int)(row / p.H), h = (int)(row % p.H);
+      sig[c] = dq_sigma[(size_t)h * p.T + t];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < FIN_FLAT; ++c) {
+    const size_t idx = first + (size_t)c * FIN_THREADS;
+    if (idx < n8) {
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t u = (uint32_t)w[c][k];
+        _Float16 lo, hi;
+        uint16_t ul = (uint16_t)(u & 0xffffu), uh = (uint16_t)(u >> 16);
+        __builtin_memcpy(&lo, &ul, 2);
+        __builtin_memcpy(&hi, &uh, 2);
+        x[2 * k] = __builtin_amdgcn_ldexpf((float)lo, sig[c]) * p.softmax_scale;
+        x[2 * k + 1] = __builtin_amdgcn_ldexpf((float)hi, sig[c]) * p.softmax_scale;
+      }
+      store_bf16<8>(dq + idx * 8, x);
+    }
+  }
+}
+
 // Split groups (grouped query attention with the group spread over several
 // backward items): dK and dV of each (token, key/value head) row are the sums
 // of the gsplit fp32 partials, added in part order; dK is rotated back with the
@@ -151,6 +194,17 @@ hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_s
                            const int* det_base, int det_cap, hipStream_t stream) {
   const size_t rows = (size_t)p.T * p.H;
   if (rows == 0) return hipSuccess;
+  if (!p.hadamard && !p.deterministic && !with_dk) {
+    const size_t n8 = rows * (size_t)(p.D / 8);
+    dim3 gf((unsigned)((n8 + FIN_THREADS * FIN_FLAT - 1) / (FIN_THREADS * FIN_FLAT)));
+    if (p.D == 64)
+      hipLaunchKernelGGL(finalize_dq_flat_kernel<64>, gf, dim3(FIN_THREADS), 0, stream, p, (const uint16_t*)dq_acc,
+                         dq_sigma, (uint16_t*)dq);
+    else
+      hipLaunchKernelGGL(finalize_dq_flat_kernel<128>, gf, dim3(FIN_THREADS), 0, stream, p, (const uint16_t*)dq_acc,
+                         dq_sigma, (uint16_t*)dq);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((rows * FIN_PARTS + FIN_THREADS - 1) / FIN_THREADS));
   if (p.D == 64)
     hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(FIN_THREADS), 0, stream, p,

@@ -468,6 +468,7 @@ flamia_status flamia_bwd_ws_layout(const flamia_attn_desc* desc, flamia_bwd_ws_o
   out->inv_l = b.il8;
   out->g = b.g;
   out->dq_sigma = b.dq_sigma;
+  out->dq_acc = b.dq_acc;
   return FLAMIA_OK;
 }
 

@@ -46,7 +46,8 @@ class QTensors(ctypes.Structure):
 
 
 class BwdWsOffsets(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_size_t) for name in ("do_codes", "do_exp", "neg_delta", "inv_l", "g", "dq_sigma")]
+    _fields_ = [(name, ctypes.c_size_t) for name in ("do_codes", "do_exp", "neg_delta", "inv_l", "g", "dq_sigma",
+                                                     "dq_acc")]
 
 
 EXPORTS = ("flamia_buffer_sizes", "flamia_qtensors_layout", "flamia_plan_build", "flamia_quantize", "flamia_attn_fwd",
@@ -323,7 +324,8 @@ class TrainingCall:
     def bwd_payload(self):
         """What the backward's prep stage left in the workspace: dO codes
         [T,H,d], dO exponent bytes [H,T], D [H,T] (fp32), 2^-8 / l [H,T], G
-        [T,H,d] (bf16) and the dQ prescale exponent [H,T] (int32)."""
+        [T,H,d] (bf16), the dQ prescale exponent [H,T] (int32) and the fp16
+        dQ accumulator [T,H,d] (summed by the main stage)."""
         T, H, d = self.shape
         o = bwd_ws_layout(self.desc)
         w = self.bws
@@ -332,7 +334,8 @@ class TrainingCall:
                     D=-w[o.neg_delta:o.neg_delta + 4 * T * H].view(torch.float32).view(H, T),
                     inv_l=w[o.inv_l:o.inv_l + 4 * T * H].view(torch.float32).view(H, T),
                     g=w[o.g:o.g + 2 * T * H * d].view(torch.bfloat16).view(T, H, d),
-                    dq_sigma=w[o.dq_sigma:o.dq_sigma + 4 * T * H].view(torch.int32).view(H, T))
+                    dq_sigma=w[o.dq_sigma:o.dq_sigma + 4 * T * H].view(torch.int32).view(H, T),
+                    dq_acc=w[o.dq_acc:o.dq_acc + 2 * T * H * d].view(torch.float16).view(T, H, d))
 
     def plan_error_word(self) -> int:
         """Word 2 of the plan: 1 when deterministic mode ran out of dQ partial slots."""

@@ -7,6 +7,11 @@
   (bf16 of the fp32 product) bit for bit; D = sum_d dO~ O within the bound of
   an fp32 sum of d exact products ([Summary, §3.3]: D comes from the same
   quantized dO as dP).
+* The dQ finaliser (flamia_attn_bwd_finish, atomic mode): dq equals
+  bf16(acc 2^sigma * softmax_scale) bit for bit from the fp16 accumulator and
+  the prescale exponent the workspace holds after the main stage (with the
+  rotation: that value rotated back by the fp32 butterflies of the oracle's
+  transform, bit for bit).
 * The E4M3 conversion of the quantizer: every finite bf16 value times every
   power of two 2^k, k = -20..20, that lies in a block's E4M3 range, through
   flamia_quantize; the Q, K, V block codes and the per-key V codes and
@@ -100,3 +105,27 @@ def test_e4m3_conversion_sweep(gpu_lib):
     np.testing.assert_array_equal(call.exps("v_key_exp").cpu().numpy().astype(np.int64), ke + 127)
     # the sweep reaches every E4M3 code (both signs, subnormals, zero)
     assert len(np.unique(codes)) == 254
+
+
+@pytest.mark.parametrize("case", ["ragged_d64_h3", "noncausal_d64", "gqa_d128_h4_kv2", "config2_fullsize"])
+def test_dq_finaliser_applies_the_prescale(gpu_lib, case):
+    spec = CASES[case]
+    wl = spec["wl"]()
+    causal = spec.get("causal", True)
+    print(f"[finalise] {case}", flush=True)
+    dev = torch.device("cuda")
+    q, k, v, do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
+    call = gpu_lib.TrainingCall(q, k, v, do, wl.cu_seqlens, hadamard=wl.hadamard, causal=causal)
+    call.step()
+    torch.cuda.synchronize()
+    pay = call.bwd_payload()
+    sig = pay["dq_sigma"].t().contiguous().unsqueeze(-1).float()          # [T, H, 1]
+    scale = np.float32(1.0 / np.sqrt(wl.head_dim))
+    x = pay["dq_acc"].float() * torch.exp2(sig)                           # exact: a power of two
+    want = (x * torch.tensor(scale, device=dev)).to(torch.bfloat16)      # fp32 product, then RNE
+    if wl.hadamard:
+        # rotated back with the forward rotation's fp32 butterflies, in its order
+        from oracle.hadamard import fwht_fp32
+        xs = (x * torch.tensor(scale, device=dev)).cpu().numpy().astype(np.float32)
+        want = torch.from_numpy(fwht_fp32(xs)).to(torch.bfloat16).to(dev)
+    assert torch.equal(call.dq, want)
