@@ -375,7 +375,8 @@ def main():
                     help="exponentials of half of the 32x32 blocks on the FMA-pipe polynomial (both passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the long-context workload's extra measurements on the default run")
+                    help="skip the default run's extra measurements (config 4 both ways, the pages' equal and "
+                         "skewed shapes, the 4-bit forward, exp2 on the FMA pipe)")
     ap.add_argument("--deterministic", action="store_true",
                     help="ordered dQ reduction (per-step partials, fixed-order fp16 sum) instead of atomics")
     ap.add_argument("--copy-calibration", action="store_true",
