@@ -408,39 +408,48 @@ attn_fwd_kernel(FwdArgs a) {
         l_run += __builtin_amdgcn_ldexpf(ls, kofs + dl);
       }
     } else if (PATH == 0 && !EXACT && !P4 && fast) {
-      // a step with a diagonal or boundary block, rows in the fast range: the
-      // fast form with the mask (0 for a key the query does not see) and the
-      // fold as an exact ldexp before the scaled convert -- every fold is
-      // <= 0, and a product that leaves fp32's normal range here is below
-      // 2^-18 after the row's scale, so the codes are those of the forms below
+      // a step with a diagonal or boundary block, rows in the fast range.  Per
+      // 32-key block: one the wave sees none of gives codes 0 and adds 0 to l;
+      // one wholly before the wave's queries and inside the document takes
+      // the common form; the rest the fast form with the mask (0 for a key the
+      // query does not see) and, on the diagonal, the fold as an exact ldexp
+      // before the scaled convert -- every fold is <= 0, and a product that
+      // leaves fp32's normal range here is below 2^-18 after the row's scale,
+      // so the codes are those of the forms below
+      const int lim = (CAUSAL ? min(i, L - 1) : L - 1) - (j0 + 4 * hh);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        if (!act[kb]) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) pc[kb][g] = 0;
+          continue;
+        }
+        const bool whole = !dia[kb] && j0 + 32 * kb + 32 <= L && (!CAUSAL || 2 * kt + kb < QB);
         float ls = 0.f;
-        float pv16[16];
-        auto block = [&](auto PB) {
+        auto block = [&](auto PB, auto WB) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
+            // four per-key exponents of the diagonal block's V fold at once
+            const int f4 = (!decltype(WB)::value && dia[kb])
+                               ? *reinterpret_cast<const int*>(&sVke[buf][32 * kb + 8 * g + 4 * hh]) : 0;
             float e4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int jj = 8 * g + 4 * hh + r;           // key within the 32-block
-              const int j = j0 + 32 * kb + jj;
-              const bool vis = interior ? true : (act[kb] && (!CAUSAL || j <= i) && j < L);
+              // key j0 + 32 kb + 8 g + 4 hh + r is visible when 32 kb + 8 g + r <= lim
+              const bool vis = decltype(WB)::value || 32 * kb + 8 * g + r <= lim;
               const float ev = vis ? exp2_p<decltype(PB)::value>(st[kb][4 * g + r] * c) : 0.f;
               ls = (g == 0 && r == 0) ? ev : ls + ev;     // exp2 >= +0: the same sum as from 0
-              int fold = 0;
-              if constexpr (EXACT)
-                fold = ((int)sVe[buf][32 * kb + jj] - E8M0_BIAS) - (dia[kb] ? vref : (int)sVr[buf][kb] - E8M0_BIAS);
-              else if (dia[kb])
-                fold = ((int)sVke[buf][32 * kb + jj] - E8M0_BIAS) - vref;
-              e4[r] = __builtin_amdgcn_ldexpf(ev, fold);
-              pv16[4 * g + r] = e4[r];
+              e4[r] = (!decltype(WB)::value && dia[kb])
+                          ? __builtin_amdgcn_ldexpf(ev, ((f4 >> (8 * r)) & 255) - E8M0_BIAS - vref) : ev;
             }
-            if constexpr (!P4) pc[kb][g] = cvt_fp8x4_scaled(e4[0], e4[1], e4[2], e4[3], psc);
+            pc[kb][g] = cvt_fp8x4_scaled(e4[0], e4[1], e4[2], e4[3], psc);
           }
         };
-        if (POLY && pol[kb]) block(std::true_type{}); else block(std::false_type{});
-        if constexpr (P4) p4_block(pv16, psc, pc[kb]);
+        if (whole) {
+          if (POLY && pol[kb]) block(std::true_type{}, std::true_type{}); else block(std::false_type{}, std::true_type{});
+        } else {
+          if (POLY && pol[kb]) block(std::true_type{}, std::false_type{}); else block(std::false_type{}, std::false_type{});
+        }
         l_run += __builtin_amdgcn_ldexpf(ls, kofs + dl);
       }
     } else {
