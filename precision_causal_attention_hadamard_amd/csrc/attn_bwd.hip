@@ -1005,6 +1005,59 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
           rows_pw(std::true_type{});
         else
           rows_pw(std::false_type{});
+      } else if (!EXACT && ((__builtin_amdgcn_readfirstlane(pqx[32 * qh]) >> 24) & 1)) {
+        // a diagonal or ragged block whose rows all take the fast form: the
+        // mask as a select (0 for what the query does not see) and, on the
+        // diagonal, each row's V fold as exact ldexps around the convert --
+        // the values and codes of the per-score form below.  Row 8 g + r of
+        // the lane (query q0 + 32 qh + 8 g + 4 hh + r) sees the lane's key
+        // when lo <= 8 g + r < hi
+        const int qrow0 = q0 + 32 * qh + 4 * hh;
+        const int lo = CAUSAL ? j - qrow0 : 0;
+        const int hi = kv ? L - qrow0 : 0;
+        auto rows_m = [&](auto PL) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int r0 = 32 * qh + 8 * g + 4 * hh;
+            const v4i kov = *reinterpret_cast<const v4i*>(pko + r0);
+            const v4f ilv = *reinterpret_cast<const v4f*>(pil + r0);
+            const v4i qxv = *reinterpret_cast<const v4i*>(pqx + r0);
+            float xf[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int rr = 4 * g + r;
+              const bool vis = 8 * g + r >= lo && 8 * g + r < hi;
+              const float p8 = __builtin_amdgcn_ldexpf(exp2_p<decltype(PL)::value>(sacc[rr] * c), kov[r]);
+              const float dsr = vis ? (p8 * ilv[r]) * pacc[rr] : 0.f;
+              dsv[rr] = dsr;
+              amax = fmaxf(amax, fabsf(dsr));
+              const float pv = vis ? p8 : 0.f;
+              xf[r] = dia ? __builtin_amdgcn_ldexpf(pv, e_key - (((qxv[r] >> 16) & 255) - E8M0_BIAS)) : pv;
+            }
+            const int code = cvt_fp8x4(xf[0], xf[1], xf[2], xf[3]);
+            if constexpr (DIAG) {
+              if (a.dump != nullptr && j < a.dump_len) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (8 * g + r >= lo && 8 * g + r < hi)
+                    a.dump[((size_t)h * T + s_d + q0 + r0 + r) * a.dump_len + j] = (uint8_t)((code >> (8 * r)) & 255);
+              }
+            }
+            if (dia) {
+              float pf[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                pf[r] = __builtin_amdgcn_ldexpf(fp8_value(code, r), (((qxv[r] >> 16) & 255) - E8M0_BIAS) - e_key);
+              pe[2 * g] = (uint32_t)f32_to_bf16_bits(pf[0]) | ((uint32_t)f32_to_bf16_bits(pf[1]) << 16);
+              pe[2 * g + 1] = (uint32_t)f32_to_bf16_bits(pf[2]) | ((uint32_t)f32_to_bf16_bits(pf[3]) << 16);
+            } else {
+              pe[2 * g] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false));
+              pe[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, true));
+            }
+          }
+        };
+        if (POLY && pol) rows_m(std::integral_constant<bool, POLY>{});
+        else rows_m(std::false_type{});
       } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
