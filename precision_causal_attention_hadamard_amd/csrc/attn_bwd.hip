@@ -1302,16 +1302,19 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   // split groups: this item's part (recomputed here rather than kept live)
   const int GS = GRP ? a.gsplit : 1, part = GRP ? (int)(blockIdx.x % GS) : 0;
   // ---- item end: the two query-half dV partials of each key block meet in
-  // the (now free) bf16 tile buffers, key blocks 0-1 first, then 2-3; then dK
+  // the (now free) bf16 tile buffers, key blocks 0-1 first, then 2-3, the
+  // sums staying in the registers of the query-half-0 waves; then dK
   for (int round = 0; round < 2; ++round) {
     const bool mine = (kb >> 1) == round;
-    float* red = reinterpret_cast<float*>((kb & 1) ? sG1 : sG0) + lane * (ND * 16);
+    // chunk-major: chunk 4 db + q4 of every lane side by side (each
+    // instruction moves 1 KB without bank conflicts)
+    float* red = reinterpret_cast<float*>((kb & 1) ? sG1 : sG0) + 4 * lane;
     if (mine && qh == 1) {
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<v4f*>(red + 16 * db + 4 * q4) =
+          *reinterpret_cast<v4f*>(red + 256 * (4 * db + q4)) =
               v4f{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]};
     }
     __syncthreads();
@@ -1320,20 +1323,48 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const v4f o = *reinterpret_cast<const v4f*>(red + 16 * db + 4 * q4);
+          const v4f o = *reinterpret_cast<const v4f*>(red + 256 * (4 * db + q4));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int jk = k0 + 32 * kb + 8 * q4 + 4 * hh + r;
-            if (jk < L) {
-              const size_t oi = doc0k + (size_t)jk * rsk + 32 * db + n;
-              if (GS == 1) a.dv[oi] = f32_to_bf16_bits(dv[db][4 * q4 + r] + o[r]);
-              else a.dv_f32[(size_t)part * T * rsk + oi] = dv[db][4 * q4 + r] + o[r];
+          for (int r = 0; r < 4; ++r) dv[db][4 * q4 + r] = dv[db][4 * q4 + r] + o[r];
+          if (GS != 1) {     // split groups: fp32 partials of this part
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int jk = k0 + 32 * kb + 8 * q4 + 4 * hh + r;
+              if (jk < L)
+                a.dv_f32[(size_t)part * T * rsk + doc0k + (size_t)jk * rsk + 32 * db + n] = dv[db][4 * q4 + r];
             }
           }
         }
     }
     __syncthreads();
   }
+  // dV as bf16 into a key-major tile per key block (the free query code
+  // buffers, 2d bytes a row), its 16-byte chunks XOR-swizzled by row so that
+  // the column writes here and the row-quarter reads below are free of bank
+  // conflicts
+  auto dvt = [&](int b) { return b == 0 ? sQ0 : b == 1 ? sQ1 : b == 2 ? sO0 : sO1; };
+  static_assert(32 * 2 * D <= CT, "a key block of bf16 dV fits one query code buffer");
+  auto dv_off = [](int row, int dcol) {        // byte offset of (row, d) in a key block's tile
+    const int sw = D == 128 ? (row & 7) : (((row >> 1) & 1) | (((row >> 2) & 1) << 2));
+    return row * (2 * D) + (((dcol >> 3) ^ sw) << 4) + 2 * (dcol & 7);
+  };
+  if (GS == 1 && qh == 0 && kb_active) {
+    uint8_t* const t = dvt(kb);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        *reinterpret_cast<uint16_t*>(t + dv_off(8 * (rr >> 2) + 4 * hh + (rr & 3), 32 * db + n)) =
+            f32_to_bf16_bits(dv[db][rr]);
+  }
+  // fp32 dK tile index of (row, d): 16-byte chunks XOR-swizzled by row (and,
+  // d = 128, by the chunk's upper half) so that both the column writes below
+  // and the row-quarter reads are free of bank conflicts
+  auto dk_idx = [](int row, int col) {
+    const int ch = col >> 2;
+    const int sw = (row & 3) | (((row >> 2) & 1) << 3) | (D == 128 ? ((ch >> 4) & 1) << 2 : 0);
+    return row * D + ((ch ^ sw) << 2) + (col & 3);
+  };
   // dK times the softmax scale into a key-major fp32 tile (key block kb in
   // one free buffer, 32 rows of d), then four lanes per key row rotate it
   // back (Hadamard option) with the same butterflies as the dQ finaliser and
@@ -1346,7 +1377,7 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     for (int e = 0; e < NDK; ++e)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr)
-        tile[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * D + 32 * (NDK * qh + e) + n] = dk[e][rr] * sc;
+        tile[dk_idx(8 * (rr >> 2) + 4 * hh + (rr & 3), 32 * (NDK * qh + e) + n)] = dk[e][rr] * sc;
   }
   __syncthreads();
   {
@@ -1355,22 +1386,28 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     const int jk = k0 + row;
     if (jk < L) {                                     // whole quads leave together
       const int rb = row >> 5;
-      const float* const src = reinterpret_cast<const float*>(rb == 0 ? sK : rb == 1 ? sV : rb == 2 ? sG0 : sG1) +
-                               (row & 31) * D + q4p * E;
+      const float* const src = reinterpret_cast<const float*>(rb == 0 ? sK : rb == 1 ? sV : rb == 2 ? sG0 : sG1);
       if (GS == 1) {
         float x[E];
 #pragma unroll
         for (int c = 0; c < E / 4; ++c) {
-          const v4f w = *reinterpret_cast<const v4f*>(src + 4 * c);
+          const v4f w = *reinterpret_cast<const v4f*>(src + dk_idx(row & 31, q4p * E + 4 * c));
 #pragma unroll
           for (int k = 0; k < 4; ++k) x[4 * c + k] = w[k];
         }
         if (p.hadamard) fwht_quarter_row<D>(x, q4p);
         store_bf16<E>(a.dk + doc0k + (size_t)jk * rsk + q4p * E, x);
+        // this row quarter of dV: E bf16 = E / 8 chunks
+        const uint8_t* const vt = dvt(rb);
+#pragma unroll
+        for (int c = 0; c < E / 8; ++c)
+          st16(a.dv + doc0k + (size_t)jk * rsk + q4p * E + 8 * c,
+               *reinterpret_cast<const v4i*>(vt + dv_off(row & 31, q4p * E + 8 * c)));
       } else {
         float* dst = a.dk_f32 + (size_t)part * T * rsk + doc0k + (size_t)jk * rsk + q4p * E;
 #pragma unroll
-        for (int c = 0; c < E / 4; ++c) *reinterpret_cast<v4f*>(dst + 4 * c) = *reinterpret_cast<const v4f*>(src + 4 * c);
+        for (int c = 0; c < E / 4; ++c)
+          *reinterpret_cast<v4f*>(dst + 4 * c) = *reinterpret_cast<const v4f*>(src + dk_idx(row & 31, q4p * E + 4 * c));
       }
     }
   }
