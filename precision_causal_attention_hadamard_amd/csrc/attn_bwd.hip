@@ -808,11 +808,18 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 
   // per-lane LDS offsets (loop-invariant)
   const int ck = code_key<D>(n);
-  int offA[NS][2];                 // row n (of a 32-row block), chunks 4s + hh and 4s + 2 + hh
+  // row n of the wave's query block (Q~, dO~) and key block (K~, V~), chunks 4s + hh and
+  // 4s + 2 + hh, as byte offsets from the tile's start (the tile is then the read's
+  // constant offset)
+  int offQ2[NS][2], offK2[NS][2];
 #pragma unroll
   for (int s2 = 0; s2 < NS; ++s2)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) offA[s2][e] = n * D + (((4 * s2 + 2 * e + hh) ^ ck) << 4);
+    for (int e = 0; e < 2; ++e) {
+      const int o = n * D + (((4 * s2 + 2 * e + hh) ^ ck) << 4);
+      offQ2[s2][e] = 32 * qh * D + o;
+      offK2[s2][e] = 32 * kb * D + o;
+    }
   int offK[NDK];                   // 8-bit transpose reads of the Q~ tile (dK operand), this wave's half of d
   {
     const int pp = lane & 15, b = pp >> 1;
@@ -830,9 +837,6 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       offG[db][1] = wide_off<D>(t + 8, 2 * (32 * db + colg + 4 * s4));
     }
   }
-  // operands of this wave's key block: K~ and V~ rows 32 kb + n
-  const uint8_t* const kbase = sK + 32 * kb * D;
-  const uint8_t* const vbase = sV + 32 * kb * D;
 
   // dQ^T: wave -> (d slice, query block); d = 64 uses waves 0-3 only
   const bool dq_wave = D == 128 || wave < 4;
@@ -925,19 +929,17 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       // exact option: each row's own exponent (lane n supplies row n's scale)
       const int qx = pqx[32 * qh + (EXACT ? n : 0)];
       const int sqe = qx & 255, sdoe = (qx >> 8) & 255;
-      const uint8_t* qrow = tQ + 32 * qh * D;
-      const uint8_t* drow = tdO + 32 * qh * D;
       auto s_step = [&](int s) {
-        const v8i qa = cat8(ld16(qrow + offA[s][0]), ld16(qrow + offA[s][1]));
-        const v8i kb8 = cat8(ld16(kbase + offA[s][0]), ld16(kbase + offA[s][1]));
+        const v8i qa = cat8(ld16(tQ + offQ2[s][0]), ld16(tQ + offQ2[s][1]));
+        const v8i kb8 = cat8(ld16(sK + offK2[s][0]), ld16(sK + offK2[s][1]));
         sacc = s == 0 ? mfma_f8(qa, kb8, v16f{}, sqe, ke) : mfma_f8(qa, kb8, sacc, sqe, ke);
       };
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         s_step(s);
         // diagonal block: per-key V~ codes
-        pacc = mfma_f8(cat8(ld16(drow + offA[s][0]), ld16(drow + offA[s][1])),
-                       (!EXACT && dia) ? vkey(s) : cat8(ld16(vbase + offA[s][0]), ld16(vbase + offA[s][1])), pacc,
+        pacc = mfma_f8(cat8(ld16(tdO + offQ2[s][0]), ld16(tdO + offQ2[s][1])),
+                       (!EXACT && dia) ? vkey(s) : cat8(ld16(sV + offK2[s][0]), ld16(sV + offK2[s][1])), pacc,
                        sdoe, (!EXACT && dia) ? vke : ve);
       }
     }
