@@ -567,9 +567,14 @@ attn_fwd_kernel(FwdArgs a) {
   if (wave_active) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
     const float l = __builtin_amdgcn_ldexpf(l_run + (hh ? __uint_as_float(sw[0]) : __uint_as_float(sw[1])), P_EXP);
-    if (iv) {
-      const float inv = 1.0f / l;
-      uint16_t* orow = a.o + (size_t)(s_d + i) * rs + (size_t)head * D;
+    // O's 32 rows of the wave go through a free V buffer (the loop's last
+    // barrier is behind every wave): row n at 2d bytes, its 16-byte chunks
+    // XOR-swizzled by row, then whole rows out with 16-byte stores
+    constexpr int CPR = 2 * D / 16;                  // 16-byte chunks per row
+    uint8_t* const ot = (wave & 2) ? sVk[wave & 1] : sV[wave & 1];
+    static_assert(32 * 2 * D <= FWD_BK * KS, "a wave's O rows fit one V buffer");
+    {
+      const float inv = 1.0f / l;                    // rows past the document are not stored
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -578,8 +583,23 @@ attn_fwd_kernel(FwdArgs a) {
           const uint32_t b1 = f32_to_bf16_bits(oacc[db][4 * g + 1] * inv);
           const uint32_t b2 = f32_to_bf16_bits(oacc[db][4 * g + 2] * inv);
           const uint32_t b3 = f32_to_bf16_bits(oacc[db][4 * g + 3] * inv);
-          *reinterpret_cast<v2i*>(orow + 32 * db + 8 * g + 4 * hh) = v2i{(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
+          const int c = 4 * db + g;                  // d = 8c + 4hh .. 8c + 4hh + 3
+          *reinterpret_cast<v2i*>(ot + n * (2 * D) + ((c ^ (n & (CPR - 1))) << 4) + 8 * hh) =
+              v2i{(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
         }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    {
+      constexpr int RPI = 64 / CPR;                  // rows per store instruction
+#pragma unroll
+      for (int k = 0; k < 32 / RPI; ++k) {
+        const int r = RPI * k + lane / CPR, c = lane % CPR;
+        const v4i v = *reinterpret_cast<const v4i*>(ot + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
+        if (qw0 + r < L) st16(a.o + (size_t)(s_d + qw0 + r) * rs + (size_t)head * D + 8 * c, v);
+      }
+    }
+    if (iv) {
       if (hh == 0) {
         a.row_max[hT + i] = m_run;
         a.row_sum[hT + i] = __builtin_amdgcn_ldexpf(l, m_acc - m_run);   // l is taken against m_acc
