@@ -810,15 +810,18 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   const int ck = code_key<D>(n);
   // row n of the wave's query block (Q~, dO~) and key block (K~, V~), chunks 4s + hh and
   // 4s + 2 + hh, as byte offsets from the tile's start (the tile is then the read's
-  // constant offset)
+  // constant offset).  The FMA-pipe exp2 and exact instantiations have no registers to
+  // spare for the second array: there the block bases are added at each read
+  constexpr bool FOLD = !POLY && !EXACT;
+  const int qb0 = FOLD ? 0 : 32 * qh * D, kb0 = FOLD ? 0 : 32 * kb * D;
   int offQ2[NS][2], offK2[NS][2];
 #pragma unroll
   for (int s2 = 0; s2 < NS; ++s2)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int o = n * D + (((4 * s2 + 2 * e + hh) ^ ck) << 4);
-      offQ2[s2][e] = 32 * qh * D + o;
-      offK2[s2][e] = 32 * kb * D + o;
+      offQ2[s2][e] = (FOLD ? 32 * qh * D : 0) + o;
+      offK2[s2][e] = (FOLD ? 32 * kb * D : 0) + o;
     }
   int offK[NDK];                   // 8-bit transpose reads of the Q~ tile (dK operand), this wave's half of d
   {
@@ -930,16 +933,16 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
       const int qx = pqx[32 * qh + (EXACT ? n : 0)];
       const int sqe = qx & 255, sdoe = (qx >> 8) & 255;
       auto s_step = [&](int s) {
-        const v8i qa = cat8(ld16(tQ + offQ2[s][0]), ld16(tQ + offQ2[s][1]));
-        const v8i kb8 = cat8(ld16(sK + offK2[s][0]), ld16(sK + offK2[s][1]));
+        const v8i qa = cat8(ld16(tQ + qb0 + offQ2[s][0]), ld16(tQ + qb0 + offQ2[s][1]));
+        const v8i kb8 = cat8(ld16(sK + kb0 + offK2[s][0]), ld16(sK + kb0 + offK2[s][1]));
         sacc = s == 0 ? mfma_f8(qa, kb8, v16f{}, sqe, ke) : mfma_f8(qa, kb8, sacc, sqe, ke);
       };
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         s_step(s);
         // diagonal block: per-key V~ codes
-        pacc = mfma_f8(cat8(ld16(tdO + offQ2[s][0]), ld16(tdO + offQ2[s][1])),
-                       (!EXACT && dia) ? vkey(s) : cat8(ld16(sV + offK2[s][0]), ld16(sV + offK2[s][1])), pacc,
+        pacc = mfma_f8(cat8(ld16(tdO + qb0 + offQ2[s][0]), ld16(tdO + qb0 + offQ2[s][1])),
+                       (!EXACT && dia) ? vkey(s) : cat8(ld16(sV + kb0 + offK2[s][0]), ld16(sV + kb0 + offK2[s][1])), pacc,
                        sdoe, (!EXACT && dia) ? vke : ve);
       }
     }
