@@ -453,6 +453,13 @@ def main():
                 "frac_dtype_weighted": achieved / wpeak if bound == "mfma" else None,
                 "dtype_weighted_peak": wpeak if bound == "mfma" else None,
                 "algorithmic_work_per_launch": work, "avg_launch_ms": stage_ms[dom]}
+    # the forward's own fraction of the FP8 peak (the other matrix-core kernel of the call)
+    fname, _, fwork, fwpeak = kernels["attn_fwd"]
+    f_ach = fwork / (stage_ms["attn_fwd"] * 1e-3) / 1e12
+    roofline_fwd = {"bound": "mfma", "kernel": fname, "achieved": f_ach, "peak": FP8_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": f_ach / FP8_PEAK_TFLOPS,
+                    "frac_dtype_weighted": f_ach / fwpeak, "dtype_weighted_peak": fwpeak,
+                    "algorithmic_work_per_launch": fwork, "avg_launch_ms": stage_ms["attn_fwd"]}
     qk_ms = max(stage_ms["quantize"] - plan_ms, 1e-6)
     quant = {"quant_qkv_ms": qk_ms, "plan_ms": plan_ms, "launches": 3 if wl.path else 2,
              "GB/s": qbytes / (qk_ms * 1e-3) / 1e9,
@@ -479,6 +486,7 @@ def main():
         "kernel_only_ms": {"fwd": stage_ms["attn_fwd"], "bwd": stage_ms["attn_bwd"] + stage_ms["bwd_finish"]},
         "quantizer": quant,
         "roofline": roofline,
+        "roofline_fwd": roofline_fwd,
     }
     if not (wl.path or grouped or args.exact or args.deterministic or args.non_causal):
         # one untimed diagnostic backward on the state the timed steps left:
