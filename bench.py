@@ -101,6 +101,16 @@ def _pmc_rows(run_dir: str, counter: str):
     return rows
 
 
+def is_diag_instantiation(name: str) -> bool:
+    """The backward's diagnostic instantiation (DIAG, the sixth template
+    argument of attn_bwd8_kernel) writes extra counts; the bench launches it
+    once for the dS zero fraction, and it is no launch of the timed kernel."""
+    if "attn_bwd8_kernel<" not in name:
+        return False
+    args = name.split("attn_bwd8_kernel<", 1)[1].split(">", 1)[0].split(",")
+    return len(args) > 5 and args[5].strip() == "true"
+
+
 def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str, kernel: str):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, both with --copy-calibration) into the traffic record of the
@@ -116,7 +126,8 @@ def write_traffic(fetch_dir: str, write_dir: str, cfg: int, command: str, kernel
             raise SystemExit(f"{counter}: no device copy in {run_dir} (run with --copy-calibration)")
         copy_kib = max(copies)
         factor = (1 << 30) / 1024.0 / copy_kib
-        vals = [float(r["Counter_Value"]) for r in rows if f"flamia::{kernel}<" in r["Kernel_Name"]]
+        vals = [float(r["Counter_Value"]) for r in rows
+                if f"flamia::{kernel}<" in r["Kernel_Name"] and not is_diag_instantiation(r["Kernel_Name"])]
         if not vals:
             raise SystemExit(f"{counter}: no {kernel} dispatch in {run_dir}")
         kib = sum(vals) / len(vals)
