@@ -20,8 +20,7 @@ template <int D>
 __global__ void __launch_bounds__(FIN_THREADS)
 finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __restrict__ dq_sigma,
                 const float* __restrict__ dk_f32, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
-                bool with_dk, const uint16_t* __restrict__ dq_part, const int* __restrict__ det_base,
-                int det_cap) {
+                bool do_dq, bool with_dk) {
   constexpr int E = D / FIN_PARTS;
   const size_t rows = (size_t)p.T * p.H;
   const size_t row = ((size_t)blockIdx.x * FIN_THREADS + threadIdx.x) / FIN_PARTS;   // = t * H + h
@@ -30,37 +29,12 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
   if (row >= rows) return;
   const int t = (int)(row / p.H), h = (int)(row % p.H);
   const size_t off = row * D + (size_t)part * E;
-  {
+  if (do_dq) {
     float x[E];
     const int sig = dq_sigma[(size_t)h * p.T + t];
-    // deterministic mode: the fp16 accumulator is rebuilt here from the
-    // step partials of every key tile that sees this query, added in fp16 in
-    // ascending key-tile order; a row one of whose partials did not fit the
-    // workspace (max_doc_len under-promised) is written as NaN
     v4i acc[E / 8];
-    bool lost = false;
-    if (p.deterministic) {
-      const int d = find_doc(p.cu, p.ndocs, t);
-      const int s0 = p.cu[d], L = p.cu[d + 1] - s0, lp = t - s0;
-      const int qt = lp / BWD_BQ, r = lp % BWD_BQ;
-      const int nq = (L + BWD_BQ - 1) / BWD_BQ, nk = (L + BWD_BK - 1) / BWD_BK;
-      const int umax = p.causal ? min(qt / 2, nk - 1) : nk - 1;
-      v8h a8[E / 8];
 #pragma unroll
-      for (int c = 0; c < E / 8; ++c) a8[c] = v8h{};
-      for (int u = 0; u <= umax; ++u) {
-        const long long step = det_step(det_base[d], u, qt, nq, p.causal);
-        if (step >= det_cap) { lost = true; break; }    // the plan flags the overflow too
-        const uint16_t* src = dq_part + (((size_t)step * p.H + h) * BWD_BQ + r) * D + (size_t)part * E;
-#pragma unroll
-        for (int c = 0; c < E / 8; ++c) a8[c] = a8[c] + __builtin_bit_cast(v8h, ld16(src + 8 * c));
-      }
-#pragma unroll
-      for (int c = 0; c < E / 8; ++c) acc[c] = __builtin_bit_cast(v4i, a8[c]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < E / 8; ++c) acc[c] = ld16(dq_acc + off + 8 * c);
-    }
+    for (int c = 0; c < E / 8; ++c) acc[c] = ld16(dq_acc + off + 8 * c);
 #pragma unroll
     for (int c = 0; c < E / 8; ++c) {
       const v4i w = acc[c];
@@ -75,10 +49,6 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
         x[8 * c + 2 * k + 1] = __builtin_amdgcn_ldexpf((float)hi, sig) * p.softmax_scale;
       }
     }
-    if (lost) {
-#pragma unroll
-      for (int k = 0; k < E; ++k) x[k] = __builtin_nanf("");
-    }
     if (p.hadamard) fwht_quarter_row<D>(x, part);
     store_bf16<E>(dq + off, x);
   }
@@ -92,6 +62,92 @@ finalize_kernel(Problem p, const uint16_t* __restrict__ dq_acc, const int* __res
     }
     if (p.hadamard) fwht_quarter_row<D>(x, part);
     store_bf16<E>(dk + off, x);
+  }
+}
+
+// Deterministic mode: the fp16 accumulator of a query row is rebuilt from the
+// step partials of every key tile that sees the query, added in fp16 in
+// ascending key-tile order, then scaled, rotated back and rounded as in
+// finalize_kernel.  A block covers 64 consecutive tokens of one head, four
+// lanes a row.  Lane `part` holds the 16-byte chunks part, part + 4, ... of the
+// row, so the four lanes of a row read 64 contiguous bytes of a partial per
+// instruction and a wave's instruction covers 16 consecutive rows of one
+// slot.  The loop has no divergent branches, so the partials of DET_RING key
+// tiles stay in flight: its trip count is the wave's largest, a row's loads
+// past its last key tile re-read that tile and its adds there are masked.  A
+// row one of whose partials did not fit the workspace (max_doc_len
+// under-promised) is written as NaN; its loads read its own output row.
+constexpr int DET_ROWS = FIN_THREADS / FIN_PARTS;   // tokens per block
+constexpr int DET_RING = 4;                         // key tiles in flight per row
+
+template <int D>
+__global__ void __launch_bounds__(FIN_THREADS)
+finalize_dq_det_kernel(Problem p, const uint16_t* __restrict__ dq_part, const int* __restrict__ det_base,
+                       int det_cap, const int* __restrict__ dq_sigma, uint16_t* __restrict__ dq) {
+  constexpr int NC = D / 32;          // 16-byte chunks per lane
+  constexpr int E = D / 4;
+  // token blocks from the last to the first, so each document's longest rows
+  // (its last queries, which see the most key tiles) start first
+  const int h = (int)(blockIdx.x % (unsigned)p.H);
+  const int nblk = (p.T + DET_ROWS - 1) / DET_ROWS;
+  const int t_row = (nblk - 1 - (int)(blockIdx.x / (unsigned)p.H)) * DET_ROWS + (int)(threadIdx.x / FIN_PARTS);
+  const int part = threadIdx.x & (FIN_PARTS - 1);
+  // every lane stays to the end (the wave maximum and the row transform read
+  // other lanes); a row past the last token works on the last token and
+  // stores nothing
+  const bool live = t_row < p.T;
+  const int t = live ? t_row : p.T - 1;
+  const int d = find_doc(p.cu, p.ndocs, t);
+  const int s0 = p.cu[d], L = p.cu[d + 1] - s0, lp = t - s0;
+  const int qt = lp / BWD_BQ, r = lp % BWD_BQ;
+  const int nq = (L + BWD_BQ - 1) / BWD_BQ, nk = (L + BWD_BK - 1) / BWD_BK;
+  const int umax = p.causal ? min(qt / 2, nk - 1) : nk - 1;
+  const int base = det_base[d];
+  const int sig = dq_sigma[(size_t)h * p.T + t];
+  uint16_t* const dst = dq + ((size_t)t * p.H + h) * D + 8 * part;
+  // a row's step indices grow with the key tile, so the last one decides
+  const bool lost = det_step(base, umax, qt, nq, p.causal) >= det_cap;
+  const uint16_t* const row0 = dq_part + ((size_t)h * BWD_BQ + r) * D + 8 * part;
+  const size_t per_step = (size_t)p.H * BWD_BQ * D;
+  auto load = [&](v4i (&c4)[NC], int u) {
+    const uint16_t* src = lost ? dst : row0 + (size_t)det_step(base, min(u, umax), qt, nq, p.causal) * per_step;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) c4[c] = ld16(src + 32 * c);
+  };
+  v8h acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = v8h{};
+  const int uw = wave_max_i(umax);
+  v4i ring[DET_RING][NC];
+#pragma unroll
+  for (int i = 0; i < DET_RING; ++i) load(ring[i], i);
+  for (int u = 0; u <= uw; u += DET_RING) {
+#pragma unroll
+    for (int i = 0; i < DET_RING; ++i) {
+      const bool take = u + i <= umax;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const v8h s = acc[c] + __builtin_bit_cast(v8h, ring[i][c]);
+        acc[c] = take ? s : acc[c];
+      }
+      load(ring[i], u + i + DET_RING);
+    }
+  }
+  float x[E];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      x[8 * c + k] = lost ? __builtin_nanf("") : __builtin_amdgcn_ldexpf((float)acc[c][k], sig) * p.softmax_scale;
+  if (p.hadamard) fwht_chunked_row<D>(x, part);
+  if (!live) return;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    v4i w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (int)((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k]) | ((uint32_t)f32_to_bf16_bits(x[8 * c + 2 * k + 1]) << 16));
+    st16(dst + 32 * c, w);
   }
 }
 
@@ -205,15 +261,24 @@ hipError_t launch_finalize(const Problem& p, const void* dq_acc, const int* dq_s
                          dq_sigma, (uint16_t*)dq);
     return hipGetLastError();
   }
+  if (p.deterministic) {
+    dim3 gd((unsigned)(((size_t)p.T + DET_ROWS - 1) / DET_ROWS * p.H));
+    if (p.D == 64)
+      hipLaunchKernelGGL(finalize_dq_det_kernel<64>, gd, dim3(FIN_THREADS), 0, stream, p, (const uint16_t*)dq_part,
+                         det_base, det_cap, dq_sigma, (uint16_t*)dq);
+    else
+      hipLaunchKernelGGL(finalize_dq_det_kernel<128>, gd, dim3(FIN_THREADS), 0, stream, p, (const uint16_t*)dq_part,
+                         det_base, det_cap, dq_sigma, (uint16_t*)dq);
+    if (!with_dk) return hipGetLastError();
+  }
+  const bool do_dq = !p.deterministic;
   dim3 grid((unsigned)((rows * FIN_PARTS + FIN_THREADS - 1) / FIN_THREADS));
   if (p.D == 64)
     hipLaunchKernelGGL(finalize_kernel<64>, grid, dim3(FIN_THREADS), 0, stream, p,
-                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk,
-                       (const uint16_t*)dq_part, det_base, det_cap);
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, do_dq, with_dk);
   else
     hipLaunchKernelGGL(finalize_kernel<128>, grid, dim3(FIN_THREADS), 0, stream, p,
-                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, with_dk,
-                       (const uint16_t*)dq_part, det_base, det_cap);
+                       (const uint16_t*)dq_acc, dq_sigma, dk_f32, (uint16_t*)dq, (uint16_t*)dk, do_dq, with_dk);
   return hipGetLastError();
 }
 
