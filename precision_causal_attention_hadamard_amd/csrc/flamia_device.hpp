@@ -482,49 +482,6 @@ __device__ __forceinline__ void fwht_quarter_row(float (&x)[D / 4], int part) {
   for (int a = 0; a < E; ++a) x[a] = x[a] * inv_sqrt_d;
 }
 
-// The same transform with the row dealt out in 16-byte chunks: lane `part` of
-// the quad holds chunks part, part + 4, ..., so element 32 c + 8 part + k sits
-// in x[8 c + k].  The butterflies run in the same order h = 1, 2, ..., d/2 with
-// the same sums and differences as fwht_quarter_row, so the results are the
-// same bit for bit; only which of them cross lanes (h = 8, 16) differs.
-template <int D>
-__device__ __forceinline__ void fwht_chunked_row(float (&x)[D / 4], int part) {
-  constexpr int E = D / 4, NC = D / 32;
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-    for (int a = 0; a < E; ++a)
-      if ((a & h) == 0) {
-        const float lo = x[a], hi = x[a + h];
-        x[a] = lo + hi;
-        x[a + h] = lo - hi;
-      }
-#pragma unroll
-  for (int a = 0; a < E; ++a) {      // h = 8: partner lane part ^ 1
-    const float other = __int_as_float(dpp_move<0xb1>(__float_as_int(x[a])));
-    x[a] = (part & 1) ? other - x[a] : x[a] + other;
-  }
-#pragma unroll
-  for (int a = 0; a < E; ++a) {      // h = 16: partner lane part ^ 2
-    const float other = __int_as_float(dpp_move<0x4e>(__float_as_int(x[a])));
-    x[a] = (part & 2) ? other - x[a] : x[a] + other;
-  }
-#pragma unroll
-  for (int hc = 1; hc < NC; hc <<= 1)  // h = 32 (and 64 at d = 128): across the lane's chunks
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if ((c & hc) == 0)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float lo = x[8 * c + k], hi = x[8 * (c + hc) + k];
-          x[8 * c + k] = lo + hi;
-          x[8 * (c + hc) + k] = lo - hi;
-        }
-  const float inv_sqrt_d = D == 64 ? 0.125f : __uint_as_float(0x3db504f3u);
-#pragma unroll
-  for (int a = 0; a < E; ++a) x[a] = x[a] * inv_sqrt_d;
-}
-
 template <int N>
 __device__ __forceinline__ void store_bf16(uint16_t* __restrict__ dst, const float (&x)[N]) {
 #pragma unroll
