@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "attn_bwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_bwd.hip",    # mixed path
     "attn_fwd_kernel": "precision_causal_attention_hadamard_amd/csrc/attn_fwd.hip",
     "quant_qkv_kernel": "precision_causal_attention_hadamard_amd/csrc/quant.hip",
+    "finalize_dq_det_kernel": "precision_causal_attention_hadamard_amd/csrc/finalize.hip",   # deterministic dQ
 }
 
 
