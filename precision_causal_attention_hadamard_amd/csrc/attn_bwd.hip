@@ -885,7 +885,10 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 #pragma unroll
       for (int t2 = 0; t2 < NIT; ++t2) {
         const int row0 = RPI * (wave + 8 * t2);
-        *reinterpret_cast<v2h*>(slot + (row0 + frow) * (D * 2) + 4 * fpair) = hv[t2];
+        // non-temporal: the partials are read back only by the finaliser, so
+        // they must not evict the query tiles later items re-read from L2
+        __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, hv[t2]),
+                                    reinterpret_cast<uint32_t*>(slot + (row0 + frow) * (D * 2) + 4 * fpair));
       }
       return;
     }
