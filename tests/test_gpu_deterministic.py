@@ -25,6 +25,9 @@ DET_CASES = {
     "hadamard_outliers_d128": CASES["hadamard_outliers_d128"],
     "ragged_d128_h4": CASES["ragged_d128_h4"],
     "mixed_d128_h2": lambda: W.small_packed(42, [256, 100], heads=2, head_dim=128, path=1),
+    # the finaliser's rotation at d = 64 (one butterfly stage across a lane's chunks)
+    "hadamard_ragged_d64_h3": lambda: W.small_packed(43, [1, 17, 45, 100, 33, 64, 130, 2, 200], heads=3,
+                                                     head_dim=64, hadamard=True),
 }
 
 
