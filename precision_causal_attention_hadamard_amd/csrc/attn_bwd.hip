@@ -679,6 +679,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
 
   __shared__ __attribute__((aligned(1024))) uint8_t sK[BWD_BK * D];         // K~ tile of the item
   __shared__ __attribute__((aligned(1024))) uint8_t sV[BWD_BK * D];         // V~ block codes of the item
+  // per-key V~ codes of the item (the diagonal blocks' dP operand), same layout
+  __shared__ __attribute__((aligned(1024))) uint8_t sVk[EXACT ? 16 : BWD_BK * D];
   // query-tile double buffers (distinct arrays, so reads of one buffer never
   // wait for the loads into the other); after the last step the bf16 pair
   // holds the dV partial sums
@@ -737,15 +739,19 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
   const uint8_t* g_doc = reinterpret_cast<const uint8_t*>(a.g + docq);
   uint8_t* dq_doc = reinterpret_cast<uint8_t*>(a.dq_acc + docq);
 
-  // ---- item start: K~ and V~ tiles (128 rows), swizzled code layout
+  // ---- item start: K~ and V~ tiles (128 rows), swizzled code layout; the
+  // per-key V~ codes too (rows past the document end repeat its last row, as
+  // in the other tiles: their P and dS are masked to zero)
   {
     constexpr int NI = BWD_BK * D / 1024;
-    for (int i = wave; i < 2 * NI; i += 8) {
-      const int ii = i % NI;
+    constexpr int NTILE = EXACT ? 2 : 3;
+    for (int i = wave; i < NTILE * NI; i += 8) {
+      const int ti = i / NI, ii = i % NI;
       const int o = ii * 1024 + 16 * lane;
       const int r = o / D, slot = (o % D) >> 4;
       const uint32_t off = (uint32_t)min(k0 + r, L - 1) * rsk32 + 16u * (uint32_t)(slot ^ code_key<D>(r));
-      dma16((i < NI ? a.k_codes : a.v_codes) + doc0k + off, (i < NI ? sK : sV) + ii * 1024);
+      dma16((ti == 0 ? a.k_codes : ti == 1 ? a.v_codes : a.v_key_codes) + doc0k + off,
+            (ti == 0 ? sK : ti == 1 ? sV : sVk) + ii * 1024);
     }
   }
   // ---- query tiles: code instruction `wave` (if any), bf16 instructions wave + 8 k, plane `wave`
@@ -800,10 +806,6 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
     vke = a.v_key_exp[mi];
   }
   const int e_key = vke - E8M0_BIAS;
-  auto vkey = [&](int s2) {
-    const uint8_t* vr = a.v_key_codes + doc0k + (size_t)min(j, L - 1) * rsk + 64 * s2 + 16 * hh;
-    return kv ? cat8(ld16(vr), ld16(vr + 32)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  };
   full_barrier();
 
   // per-lane LDS offsets (loop-invariant)
@@ -945,7 +947,8 @@ __global__ void __launch_bounds__(2 * BWD_THREADS) attn_bwd8_kernel(BwdArgs a) {
         s_step(s);
         // diagonal block: per-key V~ codes
         pacc = mfma_f8(cat8(ld16(tdO + qb0 + offQ2[s][0]), ld16(tdO + qb0 + offQ2[s][1])),
-                       (!EXACT && dia) ? vkey(s) : cat8(ld16(sV + kb0 + offK2[s][0]), ld16(sV + kb0 + offK2[s][1])), pacc,
+                       (!EXACT && dia) ? cat8(ld16(sVk + kb0 + offK2[s][0]), ld16(sVk + kb0 + offK2[s][1]))
+                                       : cat8(ld16(sV + kb0 + offK2[s][0]), ld16(sV + kb0 + offK2[s][1])), pacc,
                        sdoe, (!EXACT && dia) ? vke : ve);
       }
     }
